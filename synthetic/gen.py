@@ -1,0 +1,188 @@
+"""Seeded input generators (numpy PCG64), one stream per tensor slice.
+
+Every tensor slice is drawn from ``PCG64(SeedSequence([cfg_seed, tensor_id,
+*index]))`` so any slice can be regenerated alone.  bfloat16 tensors are
+produced as uint16 bit patterns by round-to-nearest-even from float32; int4
+tensors as packed bytes (two codes per byte, even channel in the low nibble)
+with binary16 scales/zeros as uint16 bit patterns.
+
+Workload recipes (shapes follow the configurations the library is measured
+on; the value distributions are stated per function).
+"""
+import numpy as np
+
+__all__ = [
+    "rng", "f32_to_bf16_bits", "normal_bf16", "normal_f32", "tiny_weights",
+    "tiny_prompt", "kept_random", "degrees", "int4_grid", "pack_codes",
+    "planted_accept", "planted_logits", "TINY_WEIGHT_ORDER", "TID",
+]
+
+# Tensor ids used in SeedSequence keys.
+TID = dict(q=1, k=2, v=3, tail_k=4, tail_v=5, blk_k=6, blk_v=7, kept=8,
+           degree=9, kcode=10, vcode=11, kscale=12, vscale=13, logits=14,
+           accept=15, hidden=16, lm=17)
+
+
+def rng(cfg_seed, tensor_id, *index):
+    return np.random.Generator(np.random.PCG64(
+        np.random.SeedSequence([int(cfg_seed), int(tensor_id)] + [int(i) for i in index])))
+
+
+def f32_to_bf16_bits(x):
+    """float32 values -> uint16 bfloat16 bit patterns, round to nearest even."""
+    u = np.asarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    r = (u + np.uint64(0x7FFF) + ((u >> np.uint64(16)) & np.uint64(1))) >> np.uint64(16)
+    return r.astype(np.uint16)
+
+
+def normal_f32(shape, cfg_seed, tensor_id, std=1.0, slice_dims=2):
+    """float32 N(0, std^2) of ``shape``; the first ``slice_dims`` axes index
+    independent streams (e.g. (b, kv head))."""
+    shape = tuple(int(s) for s in shape)
+    out = np.empty(shape, dtype=np.float32)
+    lead = shape[:slice_dims]
+    for idx in np.ndindex(*lead):
+        g = rng(cfg_seed, tensor_id, *idx)
+        out[idx] = (g.standard_normal(shape[slice_dims:], dtype=np.float32) * np.float32(std))
+    return out
+
+
+def normal_bf16(shape, cfg_seed, tensor_id, std=1.0, slice_dims=2):
+    """bf16 bit patterns of :func:`normal_f32` draws."""
+    return f32_to_bf16_bits(normal_f32(shape, cfg_seed, tensor_id, std, slice_dims))
+
+
+# --------------------------------------------------------------------------
+# Tiny decoder (2 layers, d_model 256, 4 q heads / 2 KV heads, head_dim 64,
+# MLP width 1024, vocab 512): float32 weights N(0, 0.02^2) drawn in this
+# order from one PCG64(seed) stream.
+TINY_WEIGHT_ORDER = ("wq", "wk", "wv", "wo", "wg", "wu", "wd")
+
+
+def tiny_weights(seed=0, n_layers=2, d_model=256, n_q_heads=4, n_kv_heads=2,
+                 head_dim=64, ffn=1024, vocab=512, std=0.02):
+    g = np.random.Generator(np.random.PCG64(seed))
+    draw = lambda *s: (g.standard_normal(s, dtype=np.float64) * std).astype(np.float32)
+    w = {"emb": draw(vocab, d_model)}
+    shapes = {"wq": (d_model, n_q_heads * head_dim), "wk": (d_model, n_kv_heads * head_dim),
+              "wv": (d_model, n_kv_heads * head_dim), "wo": (n_q_heads * head_dim, d_model),
+              "wg": (d_model, ffn), "wu": (d_model, ffn), "wd": (ffn, d_model)}
+    for l in range(n_layers):
+        for name in TINY_WEIGHT_ORDER:
+            w[f"l{l}.{name}"] = draw(*shapes[name])
+    w["w_lm"] = draw(d_model, vocab)
+    return w
+
+
+def tiny_prompt(seed=1, length=1024, vocab=512):
+    return np.random.Generator(np.random.PCG64(seed)).integers(0, vocab, length).astype(np.int32)
+
+
+# --------------------------------------------------------------------------
+# Compressed-cache metadata (variant A: kept token subset with degrees).
+def kept_random(n_ctx, n_keep, cfg_seed, b, sinks=4, recent=1024):
+    """Ascending kept positions: sinks, the last ``recent`` tokens, and the
+    rest drawn uniformly without replacement from the range between them."""
+    rest = n_keep - sinks - recent
+    if rest < 0 or rest > n_ctx - sinks - recent:
+        raise ValueError("kept budget does not fit the context")
+    g = rng(cfg_seed, TID["kept"], b)
+    mid = g.choice(np.arange(sinks, n_ctx - recent), size=rest, replace=False)
+    return np.sort(np.concatenate([np.arange(sinks), mid,
+                                   np.arange(n_ctx - recent, n_ctx)])).astype(np.int32)
+
+
+def degrees(shape, cfg_seed, lo=1, hi=4):
+    """float32 merge degrees n_t drawn uniformly from {lo..hi}; the first axis
+    (batch) indexes independent streams."""
+    shape = tuple(int(s) for s in shape)
+    out = np.empty(shape, dtype=np.float32)
+    for b in range(shape[0]):
+        out[b] = rng(cfg_seed, TID["degree"], b).integers(lo, hi + 1, shape[1:]).astype(np.float32)
+    return out
+
+
+# --------------------------------------------------------------------------
+# Int4 compressed cache (variant B), drawn directly on the quantization grid.
+def pack_codes(codes):
+    """int codes 0..15 ``[..., D]`` -> uint8 ``[..., D/2]``, even channel low."""
+    codes = np.asarray(codes).astype(np.uint8)
+    return (codes[..., 0::2] | (codes[..., 1::2] << 4)).astype(np.uint8)
+
+
+def int4_grid(B, Hkv, cap, D, cfg_seed, smin=0.3, smax=0.5):
+    """Codes uniform on 0..15 and binary16 scales ``s ~ U[smin, smax]``,
+    zeros ``z = -7.5 s`` (so reconstructions span about +-3.75).
+
+    Returns dict of uint8 ``k_codes/v_codes [B][Hkv][cap][D/2]`` and uint16
+    (binary16 bits) ``k_scale/k_zero [B][Hkv][cap/32][D]``,
+    ``v_scale/v_zero [B][Hkv][cap][D/32]``, plus the unpacked int codes
+    ``k_c/v_c`` for the oracle side.
+    """
+    assert cap % 32 == 0 and D % 32 == 0
+    shp = dict(k_c=(B, Hkv, cap, D), v_c=(B, Hkv, cap, D),
+               k_scale=(B, Hkv, cap // 32, D), v_scale=(B, Hkv, cap, D // 32))
+    res = {"k_c": np.empty(shp["k_c"], np.uint8), "v_c": np.empty(shp["v_c"], np.uint8),
+           "k_scale": np.empty(shp["k_scale"], np.uint16), "k_zero": np.empty(shp["k_scale"], np.uint16),
+           "v_scale": np.empty(shp["v_scale"], np.uint16), "v_zero": np.empty(shp["v_scale"], np.uint16)}
+    for b in range(B):
+        for h in range(Hkv):
+            gk = rng(cfg_seed, TID["kcode"], b, h)
+            gv = rng(cfg_seed, TID["vcode"], b, h)
+            res["k_c"][b, h] = gk.integers(0, 16, (cap, D))
+            res["v_c"][b, h] = gv.integers(0, 16, (cap, D))
+            gs = rng(cfg_seed, TID["kscale"], b, h)
+            ks = gs.uniform(smin, smax, (cap // 32, D)).astype(np.float16)
+            res["k_scale"][b, h] = ks.view(np.uint16)
+            res["k_zero"][b, h] = (ks.astype(np.float32) * np.float32(-7.5)).astype(np.float16).view(np.uint16)
+            gs = rng(cfg_seed, TID["vscale"], b, h)
+            vs = gs.uniform(smin, smax, (cap, D // 32)).astype(np.float16)
+            res["v_scale"][b, h] = vs.view(np.uint16)
+            res["v_zero"][b, h] = (vs.astype(np.float32) * np.float32(-7.5)).astype(np.float16).view(np.uint16)
+    res["k_codes"] = pack_codes(res["k_c"])
+    res["v_codes"] = pack_codes(res["v_c"])
+    return res
+
+
+# --------------------------------------------------------------------------
+# Acceptance patterns for workloads without a trained model.
+def planted_accept(B, k, vocab, cfg_seed, n_lo, n_hi, force=()):
+    """Per request a target sequence ``y_1..y_{k+1}`` and drafts ``d_1..d_k``
+    that copy ``y`` for the first ``n`` positions and then differ, with
+    ``n ~ U{n_lo..n_hi}``; ``force`` maps request index -> fixed n.
+
+    Returns ``(y [B][k+1], d [B][k], n [B])`` int32.
+    """
+    y = np.empty((B, k + 1), np.int32)
+    d = np.empty((B, k), np.int32)
+    n = np.empty(B, np.int32)
+    force = dict(force)
+    for b in range(B):
+        g = rng(cfg_seed, TID["accept"], b)
+        n[b] = force.get(b, g.integers(n_lo, n_hi + 1))
+        y[b] = g.integers(0, vocab, k + 1)
+        d[b] = g.integers(0, vocab, k)
+        d[b, :n[b]] = y[b, :n[b]]
+        if n[b] < k and d[b, n[b]] == y[b, n[b]]:
+            d[b, n[b]] = (y[b, n[b]] + 1) % vocab
+    return y, d, n
+
+
+def planted_logits(y, vocab, cfg_seed, margin=4.0, ties=0):
+    """float32 logits ``[B][M][V]`` N(0,1) whose row argmax is ``y`` (the
+    planted entry is the row maximum plus ``margin``).  ``ties > 0`` plants
+    that many extra copies of the maximum at higher indices than ``y``."""
+    B, M = y.shape
+    out = np.empty((B, M, vocab), np.float32)
+    for b in range(B):
+        g = rng(cfg_seed, TID["logits"], b)
+        out[b] = g.standard_normal((M, vocab), dtype=np.float32)
+        for j in range(M):
+            top = out[b, j].max() + np.float32(margin)
+            out[b, j, y[b, j]] = top
+            if ties:
+                higher = np.arange(y[b, j] + 1, vocab)
+                if higher.size:
+                    for t in g.choice(higher, size=min(ties, higher.size), replace=False):
+                        out[b, j, t] = top
+    return out
