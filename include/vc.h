@@ -1,0 +1,153 @@
+/*
+ * vc.h -- C ABI of the VeriCache draft-then-verify hot path on MI355X (gfx950).
+ *
+ * The method ("Riepilogo Tecnico: VeriCache", gist.science paper 2605.17613,
+ * section "Algoritmo Principale"): the target model drafts candidate tokens
+ * over a compressed KV cache (KV_comp), one forward pass over the full cache
+ * (KV_full) verifies all drafted tokens at once, and tokens are accepted up to
+ * the first mismatch, plus one bonus token when every draft matches.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Tensor pointers are DEVICE pointers unless stated otherwise; arrays are
+ *    dense, row-major, in the index order written ([B][Hkv][cap][D] means D
+ *    fastest).  Base pointers of bf16/fp32 tensors must be 16-byte aligned.
+ *  - K is token-major ([..][tokens][D]); V is CHANNEL-major ([..][D][tokens]).
+ *    Both contractions of attention (q.k over channels, p.v over tokens)
+ *    then reduce along the contiguous axis.
+ *  - The caller owns every buffer (e.g. allocated by torch).  These calls
+ *    never allocate device memory, never synchronize, never modify inputs;
+ *    work is enqueued on `stream` (a hipStream_t; NULL = null stream) and the
+ *    call returns.  Calls on distinct streams with distinct outputs may run
+ *    concurrently.
+ *  - Lengths that live in device memory (main_len, tail_len, ctx_len) are
+ *    clamped by the kernels to their capacities, so out-of-range values can
+ *    not cause out-of-bounds accesses.  A query whose key set is empty gets
+ *    NaN output and -inf lse.
+ *  - Return: VC_OK, or VC_EINVAL (bad pointer/shape/alignment), VC_ENOTSUP
+ *    (a head_dim / dtype / format combination that is not compiled),
+ *    VC_EHIP (a HIP launch error).  On a non-OK status nothing was enqueued
+ *    (except for VC_EHIP), and vc_last_error() returns a message for the
+ *    calling thread.
+ */
+#ifndef VC_H
+#define VC_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { VC_OK = 0, VC_EINVAL = 1, VC_ENOTSUP = 2, VC_EHIP = 3 } vc_status;
+typedef enum { VC_BF16 = 0, VC_FP32 = 1 } vc_dtype;
+typedef enum { VC_KV_DENSE = 0, VC_KV_INT4 = 1 } vc_kv_format;
+
+/* ------------------------------------------------------------------------ */
+/* Draft decode attention ("Algoritmo Principale", step 1: drafting over the
+ * compressed cache).  One query token per request; for query head h (KV head
+ * g = h / (Hq/Hkv)) the output is
+ *   o = sum_t softmax_t(scale * q.k_t + beta_t) v_t
+ * over the main (compressed) segment t < main_len[b][g] followed by the tail
+ * segment t < tail_len[b] (beta = 0).  beta_t = ln(degree_t) when degrees are
+ * given: a centroid that merged n_t tokens enters the softmax with the
+ * logarithm of its degree ("Riassunto Tecnico: CentroidKV", gist.science paper
+ * 2506.11418, "Componenti Chiave", item 4 "Aggregazione"); otherwise 0.
+ * The main segment is either dense (bf16/fp32) or int4 group-quantized
+ * (the quantizing drafters of "Supporto Architetturale"):
+ *   K_hat[t][d] = ck[t][d] * k_scale[t/32][d] + k_zero[t/32][d]
+ *   V_hat[d][t] = cv[d][t] * v_scale[d/32][t] + v_zero[d/32][t]
+ * (one K group = one channel over 32 tokens, one V group = one token over 32
+ * channels; codes 0..15, scales/zeros binary16).                            */
+typedef struct vc_draft_args {
+  int32_t B, Hq, Hkv, D;          /* D in {64, 128}; Hq % Hkv == 0, Hq/Hkv <= 16   */
+  int32_t dtype;                  /* vc_dtype of q, dense K/V, tail K/V and out    */
+  int32_t fmt;                    /* vc_kv_format of the main segment              */
+  float   scale;                  /* softmax scale, normally 1/sqrt(D)             */
+  int32_t num_splits;             /* token splits per (b, KV head); 0 = automatic  */
+  int64_t cap;                    /* main capacity per (b, KV head); multiple of 64 */
+  int64_t tcap;                   /* tail capacity (0 when no tail)                */
+  const void    *q;               /* [B][Hq][D]                                    */
+  const int32_t *main_len;        /* [B][Hkv] valid main tokens                    */
+  const void    *k;               /* DENSE [B][Hkv][cap][D]; INT4 u8 [B][Hkv][cap][D/2],
+                                     two channels per byte, even channel low nibble */
+  const void    *v;               /* DENSE [B][Hkv][D][cap]; INT4 u8 [B][Hkv][D][cap/2],
+                                     two tokens per byte, even token low nibble    */
+  const uint16_t *k_scale, *k_zero; /* INT4 only: fp16 [B][Hkv][cap/32][D]         */
+  const uint16_t *v_scale, *v_zero; /* INT4 only: fp16 [B][Hkv][D/32][cap]         */
+  const float   *degree;          /* optional [B][Hd][cap] merge degrees n_t >= 1  */
+  int64_t degree_h_stride;        /* 0: one row per request shared by all KV heads;
+                                     cap: one row per KV head                      */
+  const void    *tail_k;          /* optional [B][Hkv][tcap][D] (dtype)            */
+  const void    *tail_v;          /* optional [B][Hkv][D][tcap] (dtype)            */
+  const int32_t *tail_len;        /* optional [B]; NULL means 0                    */
+  void  *out;                     /* [B][Hq][D] (dtype)                            */
+  float *out_lse;                 /* optional [B][Hq], natural log                 */
+  void  *workspace;               /* split partials; >= vc_draft_workspace_size()  */
+  size_t workspace_bytes;
+} vc_draft_args;
+
+vc_status vc_draft_attn(const vc_draft_args *a, void *stream);
+size_t    vc_draft_workspace_size(const vc_draft_args *a);
+
+/* ------------------------------------------------------------------------ */
+/* Verify block attention ("Algoritmo Principale", step 2: one forward pass
+ * with the full cache checks every drafted token in parallel).  Each request
+ * has a block of M query rows (the last accepted token followed by the k
+ * drafts, M = k + 1).  Row i of request b sees every context key
+ * t < ctx_len[b] and the block keys 0..i (causal inside the block):
+ *   o[b][i][h] = sum_t softmax_t(scale * q.k_t) v_t.
+ * With ctx_len = 0 and the prompt as the block this is causal prefill.     */
+typedef struct vc_verify_args {
+  int32_t B, Hq, Hkv, D, M;       /* D in {64, 128}; M >= 1; Hq % Hkv == 0         */
+  int32_t dtype;                  /* vc_dtype of every tensor below                */
+  float   scale;
+  int32_t num_splits;             /* key splits per (b, KV head); 0 = automatic    */
+  int64_t ccap;                   /* context capacity; multiple of 64              */
+  const void    *q;               /* [B][M][Hq][D]                                 */
+  const void    *ctx_k;           /* [B][Hkv][ccap][D]                             */
+  const void    *ctx_v;           /* [B][Hkv][D][ccap]                             */
+  const int32_t *ctx_len;         /* [B]                                           */
+  const void    *blk_k;           /* [B][Hkv][M][D]                                */
+  const void    *blk_v;           /* [B][Hkv][D][M]                                */
+  void  *out;                     /* [B][M][Hq][D]                                 */
+  float *out_lse;                 /* optional [B][M][Hq], natural log              */
+  void  *workspace;               /* >= vc_verify_workspace_size()                 */
+  size_t workspace_bytes;
+} vc_verify_args;
+
+vc_status vc_verify_attn(const vc_verify_args *a, void *stream);
+size_t    vc_verify_workspace_size(const vc_verify_args *a);
+
+/* ------------------------------------------------------------------------ */
+/* Greedy acceptance ("Algoritmo Principale", step 3).  For each request the
+ * M = k + 1 logit rows are the full-cache predictions after x0, d_1..d_k:
+ *   y_{j+1} = argmax(logits[b][j])   (lowest index among equal maxima;
+ *                                     logits must be finite)
+ *   n       = number of leading j with d_j == y_j          (0..k)
+ *   emitted = d_1..d_n, y_{n+1}      (y_{k+1} is the bonus when n = k)
+ * Outputs: argmax [B][M], accept_len [B] = n, out_tokens [B][M] = emitted
+ * then -1 padding, n_out [B] = n + 1.  Any M >= 1 is accepted.              */
+typedef struct vc_accept_args {
+  int32_t B, M, V;
+  int32_t logit_dtype;            /* VC_BF16 or VC_FP32                            */
+  const void    *logits;          /* [B][M][V]                                     */
+  const int32_t *draft;           /* [B][M-1] (may be NULL when M == 1)            */
+  int32_t *argmax;                /* [B][M]                                        */
+  int32_t *accept_len;            /* [B]                                           */
+  int32_t *out_tokens;            /* [B][M]                                        */
+  int32_t *n_out;                 /* [B]                                           */
+} vc_accept_args;
+
+vc_status vc_accept(const vc_accept_args *a, void *stream);
+
+/* ------------------------------------------------------------------------ */
+const char *vc_status_string(vc_status s);
+const char *vc_last_error(void);   /* thread-local message of the last failure */
+const char *vc_build_info(void);   /* target, compile flags                    */
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* VC_H */

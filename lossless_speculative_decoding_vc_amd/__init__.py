@@ -1,0 +1,267 @@
+"""Python binding of libvc, the MI355X (gfx950) VeriCache hot path.
+
+Argument marshalling only: every computation runs in the HIP kernels of
+``libvc.so`` (built in-tree by :mod:`lossless_speculative_decoding_vc_amd.build`).
+torch supplies device memory and the current HIP stream.  There is no CPU
+fallback: if the library is missing or fails to load, every call raises.
+
+Tensor layouts follow ``include/vc.h``: K token-major ``[..][tokens][D]``,
+V channel-major ``[..][D][tokens]``.
+"""
+import ctypes
+import os
+
+import torch
+
+__all__ = [
+    "VcError", "lib", "library_path", "draft_attn", "verify_attn", "accept",
+    "draft_workspace_size", "verify_workspace_size", "declared_symbols",
+    "VC_BF16", "VC_FP32", "VC_KV_DENSE", "VC_KV_INT4",
+]
+
+VC_OK, VC_EINVAL, VC_ENOTSUP, VC_EHIP = 0, 1, 2, 3
+VC_BF16, VC_FP32 = 0, 1
+VC_KV_DENSE, VC_KV_INT4 = 0, 1
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+library_path = os.path.join(_HERE, "libvc.so")
+_HEADERS = [os.path.join(os.path.dirname(_HERE), "include", f) for f in ("vc.h",)]
+
+
+class VcError(RuntimeError):
+    def __init__(self, status, msg):
+        super().__init__(f"{_STATUS.get(status, status)}: {msg}")
+        self.status = status
+
+
+_STATUS = {VC_OK: "VC_OK", VC_EINVAL: "VC_EINVAL", VC_ENOTSUP: "VC_ENOTSUP", VC_EHIP: "VC_EHIP"}
+
+_p = ctypes.c_void_p
+_i32 = ctypes.c_int32
+_i64 = ctypes.c_int64
+
+
+class DraftArgs(ctypes.Structure):
+    _fields_ = [("B", _i32), ("Hq", _i32), ("Hkv", _i32), ("D", _i32),
+                ("dtype", _i32), ("fmt", _i32), ("scale", ctypes.c_float), ("num_splits", _i32),
+                ("cap", _i64), ("tcap", _i64),
+                ("q", _p), ("main_len", _p), ("k", _p), ("v", _p),
+                ("k_scale", _p), ("k_zero", _p), ("v_scale", _p), ("v_zero", _p),
+                ("degree", _p), ("degree_h_stride", _i64),
+                ("tail_k", _p), ("tail_v", _p), ("tail_len", _p),
+                ("out", _p), ("out_lse", _p), ("workspace", _p), ("workspace_bytes", ctypes.c_size_t)]
+
+
+class VerifyArgs(ctypes.Structure):
+    _fields_ = [("B", _i32), ("Hq", _i32), ("Hkv", _i32), ("D", _i32), ("M", _i32),
+                ("dtype", _i32), ("scale", ctypes.c_float), ("num_splits", _i32),
+                ("ccap", _i64),
+                ("q", _p), ("ctx_k", _p), ("ctx_v", _p), ("ctx_len", _p),
+                ("blk_k", _p), ("blk_v", _p), ("out", _p), ("out_lse", _p),
+                ("workspace", _p), ("workspace_bytes", ctypes.c_size_t)]
+
+
+class AcceptArgs(ctypes.Structure):
+    _fields_ = [("B", _i32), ("M", _i32), ("V", _i32), ("logit_dtype", _i32),
+                ("logits", _p), ("draft", _p), ("argmax", _p), ("accept_len", _p),
+                ("out_tokens", _p), ("n_out", _p)]
+
+
+_lib = None
+
+
+def lib():
+    """The loaded ``libvc.so`` (raises if it is missing: there is no fallback)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(library_path):
+            raise ImportError(f"libvc.so not built at {library_path}; run "
+                              "python -m lossless_speculative_decoding_vc_amd.build")
+        L = ctypes.CDLL(library_path)
+        for name, argt in (("vc_draft_attn", [ctypes.POINTER(DraftArgs), _p]),
+                           ("vc_verify_attn", [ctypes.POINTER(VerifyArgs), _p]),
+                           ("vc_accept", [ctypes.POINTER(AcceptArgs), _p])):
+            fn = getattr(L, name)
+            fn.argtypes = argt
+            fn.restype = ctypes.c_int
+        L.vc_draft_workspace_size.argtypes = [ctypes.POINTER(DraftArgs)]
+        L.vc_draft_workspace_size.restype = ctypes.c_size_t
+        L.vc_verify_workspace_size.argtypes = [ctypes.POINTER(VerifyArgs)]
+        L.vc_verify_workspace_size.restype = ctypes.c_size_t
+        L.vc_last_error.restype = ctypes.c_char_p
+        L.vc_status_string.restype = ctypes.c_char_p
+        L.vc_status_string.argtypes = [ctypes.c_int]
+        L.vc_build_info.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def declared_symbols():
+    """Function names declared by the public headers."""
+    import re
+    names = []
+    for h in _HEADERS:
+        with open(h) as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        names += re.findall(r"^\s*[A-Za-z_][\w\s\*]*?\b(vc_\w+)\s*\(", text, flags=re.M)
+    return sorted(set(names))
+
+
+def _check(status):
+    if status != VC_OK:
+        raise VcError(status, lib().vc_last_error().decode())
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def _dev(t, name, dtype=None):
+    if t is None:
+        return
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+
+
+def _vc_dtype(t):
+    if t.dtype == torch.bfloat16:
+        return VC_BF16
+    if t.dtype == torch.float32:
+        return VC_FP32
+    raise ValueError(f"unsupported dtype {t.dtype}")
+
+
+def _draft_struct(q, k, v, main_len, degree, tail_k, tail_v, tail_len, out, out_lse,
+                  scale, num_splits, fmt, k_scale, k_zero, v_scale, v_zero, Hkv, cap):
+    B, Hq, D = q.shape
+    a = DraftArgs()
+    a.B, a.Hq, a.Hkv, a.D = B, Hq, Hkv, D
+    a.dtype = _vc_dtype(q)
+    a.fmt = fmt
+    a.scale = D ** -0.5 if scale is None else scale
+    a.num_splits = num_splits
+    a.cap = cap
+    a.tcap = 0 if tail_k is None else tail_k.shape[2]
+    a.q, a.main_len, a.k, a.v = _ptr(q), _ptr(main_len), _ptr(k), _ptr(v)
+    a.k_scale, a.k_zero, a.v_scale, a.v_zero = map(_ptr, (k_scale, k_zero, v_scale, v_zero))
+    a.degree = _ptr(degree)
+    a.degree_h_stride = 0 if degree is None or degree.shape[1] == 1 else cap
+    a.tail_k, a.tail_v, a.tail_len = _ptr(tail_k), _ptr(tail_v), _ptr(tail_len)
+    a.out, a.out_lse = _ptr(out), _ptr(out_lse)
+    return a
+
+
+def draft_attn(q, k, v, main_len, degree=None, tail_k=None, tail_v=None, tail_len=None,
+               out=None, out_lse=None, scale=None, num_splits=0, workspace=None,
+               fmt=VC_KV_DENSE, k_scale=None, k_zero=None, v_scale=None, v_zero=None,
+               stream=None):
+    """Draft decode attention (``vc_draft_attn``).
+
+    ``q [B][Hq][D]``; dense ``k [B][Hkv][cap][D]``, ``v [B][Hkv][D][cap]``;
+    ``main_len`` int32 ``[B][Hkv]``; ``degree`` fp32 ``[B][1 or Hkv][cap]``;
+    ``tail_k [B][Hkv][tcap][D]``, ``tail_v [B][Hkv][D][tcap]``, ``tail_len``
+    int32 ``[B]``.  Returns ``out [B][Hq][D]`` (and fills ``out_lse``).
+    """
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (tail_k, "tail_k"), (tail_v, "tail_v"),
+                 (out, "out"), (degree, "degree"), (out_lse, "out_lse"), (k_scale, "k_scale"),
+                 (k_zero, "k_zero"), (v_scale, "v_scale"), (v_zero, "v_zero")):
+        _dev(t, n)
+    _dev(main_len, "main_len", torch.int32)
+    _dev(tail_len, "tail_len", torch.int32)
+    B, Hq, D = q.shape
+    Hkv = k.shape[1]
+    cap = k.shape[2]
+    if out is None:
+        out = torch.empty_like(q)
+    a = _draft_struct(q, k, v, main_len, degree, tail_k, tail_v, tail_len, out, out_lse,
+                      scale, num_splits, fmt, k_scale, k_zero, v_scale, v_zero, Hkv, cap)
+    need = lib().vc_draft_workspace_size(ctypes.byref(a))
+    if need:
+        if workspace is None or workspace.numel() * workspace.element_size() < need:
+            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        a.workspace, a.workspace_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    _check(lib().vc_draft_attn(ctypes.byref(a), _stream(stream)))
+    return out
+
+
+def draft_workspace_size(**kw):
+    a = DraftArgs()
+    for key, val in kw.items():
+        setattr(a, key, val)
+    return lib().vc_draft_workspace_size(ctypes.byref(a))
+
+
+def verify_attn(q, ctx_k, ctx_v, ctx_len, blk_k, blk_v, out=None, out_lse=None, scale=None,
+                num_splits=0, workspace=None, stream=None):
+    """Verify block attention (``vc_verify_attn``).
+
+    ``q [B][M][Hq][D]``; ``ctx_k [B][Hkv][ccap][D]``, ``ctx_v [B][Hkv][D][ccap]``;
+    ``ctx_len`` int32 ``[B]``; ``blk_k [B][Hkv][M][D]``, ``blk_v [B][Hkv][D][M]``.
+    Returns ``out [B][M][Hq][D]``.
+    """
+    for t, n in ((q, "q"), (ctx_k, "ctx_k"), (ctx_v, "ctx_v"), (blk_k, "blk_k"),
+                 (blk_v, "blk_v"), (out, "out"), (out_lse, "out_lse")):
+        _dev(t, n)
+    _dev(ctx_len, "ctx_len", torch.int32)
+    B, M, Hq, D = q.shape
+    Hkv = blk_k.shape[1]
+    if out is None:
+        out = torch.empty_like(q)
+    a = VerifyArgs()
+    a.B, a.Hq, a.Hkv, a.D, a.M = B, Hq, Hkv, D, M
+    a.dtype = _vc_dtype(q)
+    a.scale = D ** -0.5 if scale is None else scale
+    a.num_splits = num_splits
+    a.ccap = 0 if ctx_k is None else ctx_k.shape[2]
+    a.q, a.ctx_k, a.ctx_v, a.ctx_len = _ptr(q), _ptr(ctx_k), _ptr(ctx_v), _ptr(ctx_len)
+    a.blk_k, a.blk_v, a.out, a.out_lse = _ptr(blk_k), _ptr(blk_v), _ptr(out), _ptr(out_lse)
+    need = lib().vc_verify_workspace_size(ctypes.byref(a))
+    if need:
+        if workspace is None or workspace.numel() * workspace.element_size() < need:
+            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        a.workspace, a.workspace_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    _check(lib().vc_verify_attn(ctypes.byref(a), _stream(stream)))
+    return out
+
+
+def verify_workspace_size(**kw):
+    a = VerifyArgs()
+    for key, val in kw.items():
+        setattr(a, key, val)
+    return lib().vc_verify_workspace_size(ctypes.byref(a))
+
+
+def accept(logits, draft, argmax=None, accept_len=None, out_tokens=None, n_out=None, stream=None):
+    """Greedy argmax + accept-until-first-mismatch (``vc_accept``).
+
+    ``logits [B][M][V]`` (bf16 or fp32); ``draft`` int32 ``[B][M-1]``.
+    Returns ``(argmax [B][M], accept_len [B], out_tokens [B][M], n_out [B])``.
+    """
+    _dev(logits, "logits")
+    _dev(draft, "draft", torch.int32)
+    B, M, V = logits.shape
+    dev = logits.device
+    argmax = torch.empty((B, M), dtype=torch.int32, device=dev) if argmax is None else argmax
+    accept_len = torch.empty(B, dtype=torch.int32, device=dev) if accept_len is None else accept_len
+    out_tokens = torch.empty((B, M), dtype=torch.int32, device=dev) if out_tokens is None else out_tokens
+    n_out = torch.empty(B, dtype=torch.int32, device=dev) if n_out is None else n_out
+    for t, n in ((argmax, "argmax"), (accept_len, "accept_len"), (out_tokens, "out_tokens"), (n_out, "n_out")):
+        _dev(t, n, torch.int32)
+    a = AcceptArgs()
+    a.B, a.M, a.V = B, M, V
+    a.logit_dtype = _vc_dtype(logits)
+    a.logits, a.draft = _ptr(logits), _ptr(draft)
+    a.argmax, a.accept_len, a.out_tokens, a.n_out = map(_ptr, (argmax, accept_len, out_tokens, n_out))
+    _check(lib().vc_accept(ctypes.byref(a), _stream(stream)))
+    return argmax, accept_len, out_tokens, n_out

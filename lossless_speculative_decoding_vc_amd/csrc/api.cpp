@@ -1,0 +1,168 @@
+// C ABI of libvc: argument validation, split planning and dispatch.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "../../include/vc.h"
+#include "launch.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+vc_status fail(vc_status s, const char *fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return s;
+}
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+vc_status hip_status(hipError_t e, const char *what) {
+  if (e == hipSuccess) return VC_OK;
+  return fail(VC_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+#define REQ(cond, ...) \
+  do {                 \
+    if (!(cond)) return fail(VC_EINVAL, __VA_ARGS__); \
+  } while (0)
+
+vc_status check_heads(int B, int Hq, int Hkv, int D) {
+  REQ(B >= 0 && Hq > 0 && Hkv > 0, "B, Hq, Hkv must be positive (B may be 0)");
+  REQ(Hq % Hkv == 0, "Hq (%d) must be a multiple of Hkv (%d)", Hq, Hkv);
+  REQ(Hq / Hkv <= 16, "at most 16 query heads per KV head (got %d)", Hq / Hkv);
+  if (D != 64 && D != 128) return fail(VC_ENOTSUP, "head_dim %d not compiled (64 or 128)", D);
+  return VC_OK;
+}
+
+vc_status check_draft_shape(const vc_draft_args *a) {
+  REQ(a, "null argument struct");
+  vc_status st = check_heads(a->B, a->Hq, a->Hkv, a->D);
+  if (st != VC_OK) return st;
+  REQ(a->dtype == VC_BF16 || a->dtype == VC_FP32, "unknown dtype %d", a->dtype);
+  REQ(a->fmt == VC_KV_DENSE || a->fmt == VC_KV_INT4, "unknown kv format %d", a->fmt);
+  if (a->fmt == VC_KV_INT4 && a->dtype != VC_BF16)
+    return fail(VC_ENOTSUP, "int4 main segment is compiled for bf16 queries only");
+  if (a->fmt == VC_KV_INT4) return fail(VC_ENOTSUP, "int4 main segment not compiled in this build");
+  REQ(a->cap >= 0 && a->cap % 64 == 0, "cap (%lld) must be a non-negative multiple of 64", (long long)a->cap);
+  REQ(a->tcap >= 0, "tcap must be non-negative");
+  return VC_OK;
+}
+
+vc_status check_draft(const vc_draft_args *a) {
+  vc_status st = check_draft_shape(a);
+  if (st != VC_OK || a->B == 0) return st;
+  REQ(a->q && a->out && a->main_len, "q, out and main_len are required");
+  REQ(a->cap == 0 || (a->k && a->v), "k and v are required when cap > 0");
+  REQ(aligned16(a->q) && aligned16(a->out) && aligned16(a->k) && aligned16(a->v),
+      "q, k, v and out must be 16-byte aligned");
+  if (a->tail_len) {
+    REQ(a->tcap > 0 && a->tail_k && a->tail_v, "tail_len given without tail_k/tail_v/tcap");
+    REQ(aligned16(a->tail_k) && aligned16(a->tail_v), "tail_k and tail_v must be 16-byte aligned");
+  }
+  if (a->degree) {
+    REQ(aligned16(a->degree), "degree must be 16-byte aligned");
+    REQ(a->degree_h_stride == 0 || a->degree_h_stride == a->cap,
+        "degree_h_stride must be 0 (shared) or cap (per KV head)");
+  }
+  REQ(a->scale > 0.f && a->scale == a->scale, "scale must be positive and finite");
+  return VC_OK;
+}
+
+vc_status check_verify_shape(const vc_verify_args *a) {
+  REQ(a, "null argument struct");
+  vc_status st = check_heads(a->B, a->Hq, a->Hkv, a->D);
+  if (st != VC_OK) return st;
+  REQ(a->dtype == VC_BF16 || a->dtype == VC_FP32, "unknown dtype %d", a->dtype);
+  REQ(a->M >= 1, "M must be >= 1");
+  REQ(a->ccap >= 0 && a->ccap % 64 == 0, "ccap (%lld) must be a non-negative multiple of 64", (long long)a->ccap);
+  return VC_OK;
+}
+
+vc_status check_verify(const vc_verify_args *a) {
+  vc_status st = check_verify_shape(a);
+  if (st != VC_OK || a->B == 0) return st;
+  REQ(a->q && a->out && a->ctx_len && a->blk_k && a->blk_v, "q, out, ctx_len, blk_k and blk_v are required");
+  REQ(a->ccap == 0 || (a->ctx_k && a->ctx_v), "ctx_k and ctx_v are required when ccap > 0");
+  REQ(aligned16(a->q) && aligned16(a->out) && aligned16(a->ctx_k) && aligned16(a->ctx_v) &&
+          aligned16(a->blk_k) && aligned16(a->blk_v),
+      "tensor pointers must be 16-byte aligned");
+  REQ(a->scale > 0.f && a->scale == a->scale, "scale must be positive and finite");
+  return VC_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *vc_status_string(vc_status s) {
+  switch (s) {
+    case VC_OK: return "VC_OK";
+    case VC_EINVAL: return "VC_EINVAL";
+    case VC_ENOTSUP: return "VC_ENOTSUP";
+    case VC_EHIP: return "VC_EHIP";
+  }
+  return "unknown vc_status";
+}
+
+const char *vc_last_error(void) { return g_err.c_str(); }
+
+const char *vc_build_info(void) {
+  return "libvc gfx950 (HIP " HIP_VERSION_GITHASH "), MFMA bf16 draft/verify, fp32 VALU draft/verify";
+}
+
+size_t vc_draft_workspace_size(const vc_draft_args *a) {
+  if (check_draft_shape(a) != VC_OK) return 0;
+  return vc::plan_draft(*a).ws_bytes;
+}
+
+size_t vc_verify_workspace_size(const vc_verify_args *a) {
+  if (check_verify_shape(a) != VC_OK) return 0;
+  return vc::plan_verify(*a).ws_bytes;
+}
+
+vc_status vc_draft_attn(const vc_draft_args *a, void *stream) {
+  vc_status st = check_draft(a);
+  if (st != VC_OK) return st;
+  if (a->B == 0) return VC_OK;
+  const vc::SplitPlan pl = vc::plan_draft(*a);
+  if (pl.ws_bytes) {
+    if (!a->workspace || a->workspace_bytes < pl.ws_bytes)
+      return fail(VC_EINVAL, "workspace of %zu bytes required (got %zu)", pl.ws_bytes, a->workspace_bytes);
+    if (!aligned16(a->workspace)) return fail(VC_EINVAL, "workspace must be 16-byte aligned");
+  }
+  return hip_status(vc::launch_draft(*a, pl, (hipStream_t)stream), "vc_draft_attn launch");
+}
+
+vc_status vc_verify_attn(const vc_verify_args *a, void *stream) {
+  vc_status st = check_verify(a);
+  if (st != VC_OK) return st;
+  if (a->B == 0) return VC_OK;
+  const vc::SplitPlan pl = vc::plan_verify(*a);
+  if (pl.ws_bytes) {
+    if (!a->workspace || a->workspace_bytes < pl.ws_bytes)
+      return fail(VC_EINVAL, "workspace of %zu bytes required (got %zu)", pl.ws_bytes, a->workspace_bytes);
+    if (!aligned16(a->workspace)) return fail(VC_EINVAL, "workspace must be 16-byte aligned");
+  }
+  return hip_status(vc::launch_verify(*a, pl, (hipStream_t)stream), "vc_verify_attn launch");
+}
+
+vc_status vc_accept(const vc_accept_args *a, void *stream) {
+  if (!a) return fail(VC_EINVAL, "null argument struct");
+  REQ(a->B >= 0 && a->M >= 1 && a->V >= 1, "B >= 0, M >= 1 and V >= 1 required");
+  REQ(a->logit_dtype == VC_BF16 || a->logit_dtype == VC_FP32, "unknown logit dtype %d", a->logit_dtype);
+  if (a->B == 0) return VC_OK;
+  REQ(a->logits && a->argmax && a->accept_len && a->out_tokens && a->n_out, "null output or logits pointer");
+  REQ(a->M == 1 || a->draft, "draft is required when M > 1");
+  REQ(aligned16(a->logits), "logits must be 16-byte aligned");
+  return hip_status(vc::launch_accept(*a, (hipStream_t)stream), "vc_accept launch");
+}
+
+}  // extern "C"

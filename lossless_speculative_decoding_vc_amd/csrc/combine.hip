@@ -1,0 +1,65 @@
+// Log-sum-exp merge of split attention partials.
+//
+// A split covers a contiguous range of the key sequence and stores its
+// softmax-normalised output o_s and its log-sum-exp lse_s (base 2).  The
+// attention over the union of the ranges is
+//   o = sum_s 2^(lse_s - L) o_s,   L = log2 sum_s 2^lse_s,
+// the standard flash-decoding reduction.  One wave per (row, head); reads
+// splits x (D + 1) floats, writes D outputs.
+#include "common.h"
+#include "launch.h"
+
+namespace vc {
+namespace {
+
+template <int D, bool kBf16>
+__global__ __launch_bounds__(64) void combine_splits(const float *__restrict__ part_o,
+                                                     const float *__restrict__ part_lse,
+                                                     int splits, int rows, void *__restrict__ out,
+                                                     float *__restrict__ out_lse) {
+  const int row = blockIdx.x;
+  const int lane = threadIdx.x;
+  float mx = kNegInf;
+  for (int s = 0; s < splits; ++s) mx = fmaxf(mx, part_lse[(size_t)s * rows + row]);
+  constexpr int kPer = D / 64;
+  float acc[kPer];
+#pragma unroll
+  for (int e = 0; e < kPer; ++e) acc[e] = 0.f;
+  float wsum = 0.f;
+  if (mx != kNegInf) {
+    for (int s = 0; s < splits; ++s) {
+      const float l = part_lse[(size_t)s * rows + row];
+      const float w = fast_exp2(l - mx);   // 0 for empty splits (l = -inf)
+      wsum += w;
+      const float *po = part_o + ((size_t)s * rows + row) * D;
+#pragma unroll
+      for (int e = 0; e < kPer; ++e) acc[e] += w * po[lane * kPer + e];
+    }
+  }
+  const float inv = 1.f / wsum;   // wsum == 0 only for an empty key set -> NaN output
+#pragma unroll
+  for (int e = 0; e < kPer; ++e) {
+    const float v = acc[e] * inv;
+    if constexpr (kBf16) reinterpret_cast<uint16_t *>(out)[(size_t)row * D + lane * kPer + e] = f32_to_bf16(v);
+    else reinterpret_cast<float *>(out)[(size_t)row * D + lane * kPer + e] = v;
+  }
+  if (out_lse && lane == 0) out_lse[row] = (mx + fast_log2(wsum)) * kLn2;
+}
+
+}  // namespace
+
+hipError_t launch_combine(const float *part_o, const float *part_lse, int splits, int rows, int D,
+                          int dtype, void *out, float *out_lse, hipStream_t s) {
+  if (rows == 0) return hipSuccess;
+  const bool bf = dtype == VC_BF16;
+  if (D == 128) {
+    if (bf) combine_splits<128, true><<<rows, 64, 0, s>>>(part_o, part_lse, splits, rows, out, out_lse);
+    else combine_splits<128, false><<<rows, 64, 0, s>>>(part_o, part_lse, splits, rows, out, out_lse);
+  } else {
+    if (bf) combine_splits<64, true><<<rows, 64, 0, s>>>(part_o, part_lse, splits, rows, out, out_lse);
+    else combine_splits<64, false><<<rows, 64, 0, s>>>(part_o, part_lse, splits, rows, out, out_lse);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace vc

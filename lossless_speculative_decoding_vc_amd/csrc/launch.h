@@ -1,0 +1,29 @@
+// Kernel launchers (internal).  Arguments were validated by api.cpp.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "../../include/vc.h"
+
+namespace vc {
+
+// Launch plan of a split attention call: `splits` partial results per
+// (row, head) are merged by the combine kernel when splits > 1.
+struct SplitPlan {
+  int splits;
+  size_t ws_bytes;
+};
+
+SplitPlan plan_draft(const vc_draft_args &a);
+SplitPlan plan_verify(const vc_verify_args &a);
+
+hipError_t launch_accept(const vc_accept_args &a, hipStream_t s);
+hipError_t launch_draft(const vc_draft_args &a, const SplitPlan &p, hipStream_t s);
+hipError_t launch_verify(const vc_verify_args &a, const SplitPlan &p, hipStream_t s);
+
+// Merge `splits` partials (o normalised per split, lse in log2 units) of
+// `rows` (row, head) pairs into out (bf16 or fp32) and optional lse (ln).
+hipError_t launch_combine(const float *part_o, const float *part_lse, int splits, int rows, int D,
+                          int dtype, void *out, float *out_lse, hipStream_t s);
+
+}  // namespace vc

@@ -14,7 +14,8 @@ import numpy as np
 __all__ = [
     "rng", "f32_to_bf16_bits", "normal_bf16", "normal_f32", "tiny_weights",
     "tiny_prompt", "kept_random", "degrees", "int4_grid", "pack_codes",
-    "planted_accept", "planted_logits", "TINY_WEIGHT_ORDER", "TID",
+    "planted_accept", "planted_logits", "TINY_WEIGHT_ORDER", "TID", "torch_normal",
+    "torch_randint",
 ]
 
 # Tensor ids used in SeedSequence keys.
@@ -186,3 +187,22 @@ def planted_logits(y, vocab, cfg_seed, margin=4.0, ties=0):
                     for t in g.choice(higher, size=min(ties, higher.size), replace=False):
                         out[b, j, t] = top
     return out
+
+
+# --------------------------------------------------------------------------
+# Bulk device-side draws for the full-size workloads (torch's seeded Philox
+# generator on the GPU; only random numbers, no method arithmetic).
+def torch_normal(shape, seed, device, dtype, std=1.0):
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(int(seed))
+    t = torch.empty(tuple(shape), dtype=dtype, device=device)
+    t.normal_(0.0, std, generator=g)
+    return t
+
+
+def torch_randint(shape, lo, hi, seed, device, dtype):
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(int(seed))
+    return torch.randint(lo, hi, tuple(shape), generator=g, device=device, dtype=dtype)

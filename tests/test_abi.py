@@ -1,0 +1,88 @@
+"""CPU checks of the C ABI: the library loads and exports every function the
+public header declares, the ctypes structs match the C layout (compiled with
+gcc from include/vc.h), and argument validation rejects bad calls before
+any GPU work."""
+import ctypes
+import os
+import subprocess
+import tempfile
+
+import pytest
+
+import lossless_speculative_decoding_vc_amd as vcb
+from lossless_speculative_decoding_vc_amd import build as vbuild
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(vbuild.LIB):
+        vbuild.build()
+    return vcb.lib()
+
+
+def test_exports_every_declared_symbol(L):
+    names = vcb.declared_symbols()
+    assert {"vc_draft_attn", "vc_verify_attn", "vc_accept"} <= set(names)
+    missing = [n for n in names if not hasattr(L, n)]
+    assert not missing, missing
+
+
+def _c_layout(struct, fields):
+    src = "#include <stdio.h>\n#include <stddef.h>\n#include \"vc.h\"\nint main(void){\n"
+    src += f'printf("%zu\\n", sizeof({struct}));\n'
+    for f in fields:
+        src += f'printf("%zu\\n", offsetof({struct}, {f}));\n'
+    src += "return 0;}\n"
+    with tempfile.TemporaryDirectory() as d:
+        c = os.path.join(d, "l.c")
+        exe = os.path.join(d, "l")
+        with open(c, "w") as fh:
+            fh.write(src)
+        subprocess.run(["gcc", "-std=c11", "-I", os.path.join(ROOT, "include"), c, "-o", exe], check=True)
+        out = subprocess.run([exe], check=True, capture_output=True, text=True).stdout.split()
+    return [int(x) for x in out]
+
+
+@pytest.mark.parametrize("cls,cname", [(vcb.DraftArgs, "vc_draft_args"),
+                                       (vcb.VerifyArgs, "vc_verify_args"),
+                                       (vcb.AcceptArgs, "vc_accept_args")])
+def test_struct_layout_matches_header(cls, cname):
+    fields = [f[0] for f in cls._fields_]
+    got = [ctypes.sizeof(cls)] + [getattr(cls, f).offset for f in fields]
+    assert got == _c_layout(cname, fields)
+
+
+def _draft(**kw):
+    a = vcb.DraftArgs()
+    a.B, a.Hq, a.Hkv, a.D, a.dtype, a.fmt, a.scale, a.cap = 2, 8, 2, 128, 0, 0, 0.088, 1024
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+def test_validation_rejects_before_launch(L):
+    # every one of these fails host-side validation; nothing reaches the GPU
+    cases = [_draft(Hq=7), _draft(D=96), _draft(cap=1000), _draft(scale=0.0), _draft(dtype=5)]
+    codes = [L.vc_draft_attn(ctypes.byref(a), None) for a in cases]
+    assert codes == [vcb.VC_EINVAL, vcb.VC_ENOTSUP, vcb.VC_EINVAL, vcb.VC_EINVAL, vcb.VC_EINVAL]
+    # missing pointers with a non-empty batch
+    assert L.vc_draft_attn(ctypes.byref(_draft()), None) == vcb.VC_EINVAL
+    assert b"required" in L.vc_last_error()
+    v = vcb.VerifyArgs()
+    v.B, v.Hq, v.Hkv, v.D, v.M, v.scale, v.ccap = 1, 64, 8, 128, 0, 0.088, 64
+    assert L.vc_verify_attn(ctypes.byref(v), None) == vcb.VC_EINVAL
+    acc = vcb.AcceptArgs()
+    acc.B, acc.M, acc.V = 1, 0, 10
+    assert L.vc_accept(ctypes.byref(acc), None) == vcb.VC_EINVAL
+    assert L.vc_status_string(2) == b"VC_ENOTSUP"
+
+
+def test_workspace_plan_is_host_only(L):
+    # c3 draft shape: 32 x 8 KV heads, 32768 compressed tokens -> split partials
+    a = _draft(B=32, Hq=32, Hkv=8, cap=32768)
+    ws = L.vc_draft_workspace_size(ctypes.byref(a))
+    assert ws > 0 and ws % (32 * 32 * 129 * 4) == 0
+    # fp32 mode runs unsplit
+    assert L.vc_draft_workspace_size(ctypes.byref(_draft(dtype=1))) == 0

@@ -1,0 +1,98 @@
+"""GPU parity of vc_draft_attn against the oracle (bf16 2e-2, fp32 1e-4),
+over head groupings, ragged lengths, merge degrees, the draft tail, forced
+split counts and the degenerate cases (empty main segment, tail only)."""
+import numpy as np
+import pytest
+
+import synthetic as S
+from oracle import attention as A
+from oracle.formats import bf16_to_f64
+
+from .helpers import TOL, assert_close, bf16_dev_to_f64, rel_l2, to_dev, to_dev_bf16
+
+pytestmark = pytest.mark.gpu
+
+
+def _case(B, Hq, Hkv, D, cap, main_len, tcap, tail_len, dtype, deg_mode, seed, qstd=1.0):
+    """Seeded inputs in both layouts: oracle side float64 [.., tokens, D]."""
+    qf = S.normal_f32((B, Hq, D), seed, S.TID["q"], std=qstd, slice_dims=1)
+    kf = S.normal_f32((B, Hkv, cap, D), seed, S.TID["k"])
+    vf = S.normal_f32((B, Hkv, cap, D), seed, S.TID["v"])
+    tkf = S.normal_f32((B, Hkv, tcap, D), seed, S.TID["tail_k"]) if tcap else None
+    tvf = S.normal_f32((B, Hkv, tcap, D), seed, S.TID["tail_v"]) if tcap else None
+    deg = None
+    if deg_mode == "shared":
+        deg = S.degrees((B, 1, cap), seed)
+    elif deg_mode == "per_head":
+        deg = S.degrees((B, Hkv, cap), seed)
+    dev, ref = {}, {}
+    for name, arr, chan_major in (("q", qf, False), ("k", kf, False), ("v", vf, True),
+                                  ("tail_k", tkf, False), ("tail_v", tvf, True)):
+        if arr is None:
+            dev[name] = ref[name] = None
+            continue
+        if dtype == "bf16":
+            bits = S.f32_to_bf16_bits(arr)
+            ref[name] = bf16_to_f64(bits)
+            dbits = np.swapaxes(bits, -1, -2) if chan_major else bits
+            dev[name] = to_dev_bf16(np.ascontiguousarray(dbits))
+        else:
+            ref[name] = arr.astype(np.float64)
+            darr = np.swapaxes(arr, -1, -2) if chan_major else arr
+            dev[name] = to_dev(np.ascontiguousarray(darr))
+    ml = np.asarray(main_len, np.int32).reshape(B, Hkv)
+    tl = None if tcap == 0 else np.asarray(tail_len, np.int32).reshape(B)
+    return dev, ref, ml, tl, deg
+
+
+def _check(B, Hq, Hkv, D, cap, main_len, tcap=0, tail_len=None, dtype="bf16", deg_mode=None,
+           seed=0, splits=0, qstd=1.0, min_rel_l2=None):
+    import torch
+    import lossless_speculative_decoding_vc_amd as vc
+    dev, ref, ml, tl, deg = _case(B, Hq, Hkv, D, cap, main_len, tcap, tail_len, dtype, deg_mode, seed, qstd)
+    lse = torch.empty((B, Hq), dtype=torch.float32, device="cuda")
+    out = vc.draft_attn(dev["q"], dev["k"], dev["v"], to_dev(ml),
+                        degree=None if deg is None else to_dev(deg),
+                        tail_k=dev["tail_k"], tail_v=dev["tail_v"],
+                        tail_len=None if tl is None else to_dev(tl),
+                        out_lse=lse, num_splits=splits)
+    torch.cuda.synchronize()
+    got = bf16_dev_to_f64(out) if dtype == "bf16" else out.cpu().numpy().astype(np.float64)
+    o_ref, lse_ref = A.draft_attn(ref["q"], ref["k"], ref["v"], ml, deg, ref["tail_k"], ref["tail_v"], tl)
+    assert_close(got, o_ref, TOL[dtype], "out")
+    assert_close(lse.cpu().numpy(), lse_ref, TOL[dtype] * 0.1, "lse")
+    if min_rel_l2 is not None:
+        assert rel_l2(got, o_ref) <= min_rel_l2
+    return got, o_ref
+
+
+@pytest.mark.parametrize("G", [1, 4, 5, 8, 16])
+@pytest.mark.parametrize("D", [64, 128])
+def test_groupings_ragged(G, D):
+    Hkv = 2
+    _check(2, G * Hkv, Hkv, D, 1024, [[1000, 777], [1024, 65]], 16, [5, 0],
+           deg_mode="shared", seed=G * 10 + D)
+
+
+@pytest.mark.parametrize("deg_mode", [None, "shared", "per_head"])
+@pytest.mark.parametrize("splits", [0, 1, 3, 7])
+def test_degrees_and_splits_peaked(deg_mode, splits):
+    # q std 4: scores spread widely, outputs O(0.1-1), so the tolerance bites
+    got, ref = _check(3, 12, 3, 128, 2048, [[2048, 1999, 1500], [700, 64, 1], [0, 33, 2047]], 40,
+                      [40, 7, 1], deg_mode=deg_mode, seed=7, splits=splits, qstd=4.0, min_rel_l2=2e-2)
+    assert np.abs(ref).mean() > 0.05        # non-vacuous comparison
+
+
+def test_tail_only_and_main_only():
+    # main_len 0 everywhere for request 0: keys come from the tail alone
+    _check(2, 8, 2, 128, 512, [[0, 0], [512, 100]], 24, [24, 0], deg_mode="shared", seed=3)
+
+
+@pytest.mark.parametrize("G", [2, 4])
+def test_fp32_mode(G):
+    _check(2, 2 * G, 2, 64, 320, [[300, 257], [1, 320]], 9, [9, 3], dtype="fp32",
+           deg_mode="shared", seed=21, qstd=3.0)
+
+
+def test_fp32_no_tail_no_degree():
+    _check(1, 4, 2, 64, 256, [[243, 200]], 0, None, dtype="fp32", seed=22)

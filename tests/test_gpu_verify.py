@@ -1,0 +1,91 @@
+"""GPU parity of vc_verify_attn against the oracle: block rows causal among
+themselves, full context visible, ragged context lengths, head groupings,
+forced split counts, causal prefill (empty context), bf16 and fp32."""
+import numpy as np
+import pytest
+
+import synthetic as S
+from oracle import attention as A
+from oracle.formats import bf16_to_f64
+
+from .helpers import TOL, assert_close, bf16_dev_to_f64, rel_l2, to_dev, to_dev_bf16
+
+pytestmark = pytest.mark.gpu
+
+
+def _inputs(B, M, Hq, Hkv, D, ccap, dtype, seed, qstd):
+    arrs = {
+        "q": (S.normal_f32((B, M, Hq, D), seed, S.TID["q"], std=qstd, slice_dims=1), False),
+        "ctx_k": (S.normal_f32((B, Hkv, ccap, D), seed, S.TID["k"]), False),
+        "ctx_v": (S.normal_f32((B, Hkv, ccap, D), seed, S.TID["v"]), True),
+        "blk_k": (S.normal_f32((B, Hkv, M, D), seed, S.TID["blk_k"]), False),
+        "blk_v": (S.normal_f32((B, Hkv, M, D), seed, S.TID["blk_v"]), True),
+    }
+    dev, ref = {}, {}
+    for name, (arr, chan_major) in arrs.items():
+        if dtype == "bf16":
+            bits = S.f32_to_bf16_bits(arr)
+            ref[name] = bf16_to_f64(bits)
+            dev[name] = to_dev_bf16(np.ascontiguousarray(np.swapaxes(bits, -1, -2) if chan_major else bits))
+        else:
+            ref[name] = arr.astype(np.float64)
+            dev[name] = to_dev(np.ascontiguousarray(np.swapaxes(arr, -1, -2) if chan_major else arr))
+    return dev, ref
+
+
+def _check(B, M, Hq, Hkv, D, ccap, ctx_len, dtype="bf16", seed=0, splits=0, qstd=1.0, rows=None):
+    import torch
+    import lossless_speculative_decoding_vc_amd as vc
+    dev, ref = _inputs(B, M, Hq, Hkv, D, ccap, dtype, seed, qstd)
+    cl = np.asarray(ctx_len, np.int32)
+    lse = torch.empty((B, M, Hq), dtype=torch.float32, device="cuda")
+    out = vc.verify_attn(dev["q"], dev["ctx_k"], dev["ctx_v"], to_dev(cl), dev["blk_k"], dev["blk_v"],
+                         out_lse=lse, num_splits=splits)
+    torch.cuda.synchronize()
+    got = bf16_dev_to_f64(out) if dtype == "bf16" else out.cpu().numpy().astype(np.float64)
+    o_ref, lse_ref = A.verify_attn(ref["q"], ref["ctx_k"], ref["ctx_v"], cl, ref["blk_k"], ref["blk_v"],
+                                   rows=rows)
+    if rows is not None:
+        sel = tuple(np.array(rows).T)
+        got, o_ref = got[sel], o_ref[sel]
+        lse_got, lse_ref = lse.cpu().numpy()[sel], lse_ref[sel]
+    else:
+        lse_got = lse.cpu().numpy()
+    assert_close(got, o_ref, TOL[dtype], "out")
+    assert_close(lse_got, lse_ref, TOL[dtype] * 0.1, "lse")
+    return got, o_ref
+
+
+@pytest.mark.parametrize("M", [1, 9, 32, 33, 41])
+@pytest.mark.parametrize("G", [2, 4, 5, 8])
+def test_blocks_and_groupings(M, G):
+    Hkv = 2
+    _check(2, M, G * Hkv, Hkv, 128, 1280, [1100, 1234], seed=M * 100 + G, qstd=2.0)
+
+
+@pytest.mark.parametrize("splits", [1, 2, 5, 16])
+def test_forced_splits_peaked(splits):
+    got, ref = _check(2, 33, 10, 2, 128, 2048, [2048, 1537], seed=5, splits=splits, qstd=4.0)
+    assert rel_l2(got, ref) <= 2e-2 and np.abs(ref).mean() > 0.05
+
+
+def test_head_dim_64_and_many_rows():
+    # R = M*G = 400 packed rows -> several row tiles
+    _check(1, 50, 16, 2, 64, 640, [600], seed=9, qstd=2.0)
+
+
+def test_causal_prefill_empty_context():
+    _check(2, 100, 8, 2, 128, 0, [0, 0], seed=11, qstd=2.0)
+
+
+def test_short_context_and_zero_for_one_request():
+    _check(2, 9, 4, 2, 128, 64, [3, 0], seed=12)
+
+
+@pytest.mark.parametrize("G", [2, 5])
+def test_fp32_mode(G):
+    _check(1, 9, 2 * G, 2, 64, 1152, [1087], dtype="fp32", seed=13, qstd=3.0)
+
+
+def test_fp32_prefill():
+    _check(1, 130, 4, 2, 64, 0, [0], dtype="fp32", seed=14)
