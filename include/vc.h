@@ -143,6 +143,70 @@ typedef struct vc_accept_args {
 vc_status vc_accept(const vc_accept_args *a, void *stream);
 
 /* ------------------------------------------------------------------------ */
+/* Greedy token choice of the drafter (the draft step's argmax): for each of
+ * R rows of logits[R][V], out[r * out_stride] = lowest index of the row
+ * maximum (same rule as vc_accept).  out_stride >= 1 lets a caller write the
+ * i-th draft of every request straight into draft[B][k] (stride k).        */
+vc_status vc_argmax(int32_t R, int32_t V, int32_t logit_dtype, const void *logits,
+                    int32_t *out, int32_t out_stride, void *stream);
+
+/* Logits of hidden rows: logits[R][V] (fp32) = h[R][Dm] (bf16) x W[Dm][V]
+ * (bf16), row-major.  A plain library GEMM (rocBLAS, fp32 accumulate) on
+ * `stream`; the rocBLAS handle is created on first use and kept for the
+ * process (it owns rocBLAS's own workspace).                                */
+vc_status vc_lm_head(int32_t R, int32_t Dm, int32_t V, const void *h, const void *w,
+                     float *logits, void *stream);
+
+/* Commit after acceptance ("Algoritmo Principale", step 3: the process
+ * restarts from the last accepted token): append the verified K/V rows of
+ * x0, d_1..d_n -- the first n_out[b] rows of the block -- to a cache at its
+ * current length, and advance the length.
+ *   blk_k [B][Hkv][M][D], blk_v [B][Hkv][D][M]        (dtype)
+ *   dst_k [B][Hkv][cap][D], dst_v [B][Hkv][D][cap]    (dtype)
+ *   len [B][Hkv] (in/out), n_out [B]
+ *   degree: optional [B][Hd][cap] (Hd = 1 when degree_h_stride = 0, else
+ *   Hkv); appended rows get degree 1.
+ * Rows past cap are dropped (the length saturates at cap).                 */
+vc_status vc_commit_rows(int32_t B, int32_t Hkv, int32_t D, int32_t M, int32_t dtype, int64_t cap,
+                         const void *blk_k, const void *blk_v, const int32_t *n_out,
+                         void *dst_k, void *dst_v, int32_t *len, float *degree,
+                         int64_t degree_h_stride, void *stream);
+
+/* ------------------------------------------------------------------------ */
+/* Cross-resource staggering ("Innovazioni Chiave del Sistema", P1): while
+ * some requests draft from HBM, the full cache of the requests that verify
+ * is loaded from host memory over PCIe, so transfer overlaps compute.  The
+ * stagger object owns a host-to-device copy stream and a device-to-host
+ * write-back stream (both non-blocking, default priority) and the events of
+ * a ring of `nslots` device staging slots:
+ *   vc_stagger_stream_layer(l)  copy stream: wait until slot l % nslots is
+ *                               released, copy `bytes` from pinned host
+ *                               memory into it, mark layer l copied;
+ *   vc_stagger_acquire(l)       `stream` waits for layer l's copy; returns
+ *                               the slot holding it;
+ *   vc_stagger_release(l)       marks (in `stream` order) that the slot of
+ *                               layer l may be overwritten;
+ *   vc_stagger_writeback        device-to-host copy on the write-back
+ *                               stream, ordered after the work already
+ *                               enqueued on `after` (commit of verified rows
+ *                               to the host-resident full cache);
+ *   vc_stagger_copy_ms          duration of layer l's last host-to-device
+ *                               copy (valid after vc_stagger_sync).
+ * Slots are caller-owned device buffers; host sources must be pinned
+ * (hipHostMalloc) for the copies to run on the DMA engines.               */
+typedef struct vc_stagger vc_stagger;
+vc_status vc_stagger_create(vc_stagger **out, void *const *slots, int32_t nslots, size_t slot_bytes,
+                            int32_t max_layers);
+vc_status vc_stagger_stream_layer(vc_stagger *s, int32_t layer, const void *host_src, size_t bytes);
+vc_status vc_stagger_acquire(vc_stagger *s, int32_t layer, void *stream, void **slot);
+vc_status vc_stagger_release(vc_stagger *s, int32_t layer, void *stream);
+vc_status vc_stagger_writeback(vc_stagger *s, void *host_dst, const void *dev_src, size_t bytes, void *after);
+vc_status vc_stagger_after(vc_stagger *s, void *stream);   /* copy stream waits for `stream` */
+vc_status vc_stagger_sync(vc_stagger *s);
+vc_status vc_stagger_copy_ms(vc_stagger *s, int32_t layer, float *ms);
+vc_status vc_stagger_destroy(vc_stagger *s);
+
+/* ------------------------------------------------------------------------ */
 const char *vc_status_string(vc_status s);
 const char *vc_last_error(void);   /* thread-local message of the last failure */
 const char *vc_build_info(void);   /* target, compile flags                    */

@@ -16,6 +16,7 @@ import torch
 __all__ = [
     "VcError", "lib", "library_path", "draft_attn", "verify_attn", "accept",
     "draft_workspace_size", "verify_workspace_size", "declared_symbols",
+    "argmax", "lm_head", "commit_rows", "Stagger",
     "VC_BF16", "VC_FP32", "VC_KV_DENSE", "VC_KV_INT4",
 ]
 
@@ -88,6 +89,25 @@ def lib():
         L.vc_draft_workspace_size.restype = ctypes.c_size_t
         L.vc_verify_workspace_size.argtypes = [ctypes.POINTER(VerifyArgs)]
         L.vc_verify_workspace_size.restype = ctypes.c_size_t
+        L.vc_argmax.argtypes = [_i32, _i32, _i32, _p, _p, _i32, _p]
+        L.vc_argmax.restype = ctypes.c_int
+        L.vc_lm_head.argtypes = [_i32, _i32, _i32, _p, _p, _p, _p]
+        L.vc_lm_head.restype = ctypes.c_int
+        L.vc_commit_rows.argtypes = [_i32, _i32, _i32, _i32, _i32, _i64, _p, _p, _p, _p, _p, _p, _p, _i64, _p]
+        L.vc_commit_rows.restype = ctypes.c_int
+        L.vc_stagger_create.argtypes = [ctypes.POINTER(_p), ctypes.POINTER(_p), _i32, ctypes.c_size_t, _i32]
+        L.vc_stagger_stream_layer.argtypes = [_p, _i32, _p, ctypes.c_size_t]
+        L.vc_stagger_acquire.argtypes = [_p, _i32, _p, ctypes.POINTER(_p)]
+        L.vc_stagger_release.argtypes = [_p, _i32, _p]
+        L.vc_stagger_writeback.argtypes = [_p, _p, _p, ctypes.c_size_t, _p]
+        L.vc_stagger_after.argtypes = [_p, _p]
+        L.vc_stagger_sync.argtypes = [_p]
+        L.vc_stagger_copy_ms.argtypes = [_p, _i32, ctypes.POINTER(ctypes.c_float)]
+        L.vc_stagger_destroy.argtypes = [_p]
+        for n in ("vc_stagger_create", "vc_stagger_stream_layer", "vc_stagger_acquire", "vc_stagger_release",
+                  "vc_stagger_writeback", "vc_stagger_after", "vc_stagger_sync", "vc_stagger_copy_ms",
+                  "vc_stagger_destroy"):
+            getattr(L, n).restype = ctypes.c_int
         L.vc_last_error.restype = ctypes.c_char_p
         L.vc_status_string.restype = ctypes.c_char_p
         L.vc_status_string.argtypes = [ctypes.c_int]
@@ -265,3 +285,92 @@ def accept(logits, draft, argmax=None, accept_len=None, out_tokens=None, n_out=N
     a.argmax, a.accept_len, a.out_tokens, a.n_out = map(_ptr, (argmax, accept_len, out_tokens, n_out))
     _check(lib().vc_accept(ctypes.byref(a), _stream(stream)))
     return argmax, accept_len, out_tokens, n_out
+
+
+def argmax(logits, out=None, out_stride=1, stream=None):
+    """Drafter token choice (``vc_argmax``): row argmax of ``logits [R][V]``,
+    lowest index on ties, written to ``out[r * out_stride]`` (int32)."""
+    _dev(logits, "logits")
+    R, V = logits.shape[0], logits.shape[-1]
+    R = logits.numel() // V
+    if out is None:
+        out = torch.empty(R * out_stride, dtype=torch.int32, device=logits.device)
+    _check(lib().vc_argmax(R, V, _vc_dtype(logits), _ptr(logits), _ptr(out), out_stride, _stream(stream)))
+    return out
+
+
+def lm_head(h, w, logits=None, stream=None):
+    """``logits [R][V] (fp32) = h [R][Dm] (bf16) @ w [Dm][V] (bf16)`` (``vc_lm_head``)."""
+    _dev(h, "h", torch.bfloat16)
+    _dev(w, "w", torch.bfloat16)
+    R, Dm = h.shape
+    V = w.shape[1]
+    if logits is None:
+        logits = torch.empty((R, V), dtype=torch.float32, device=h.device)
+    _dev(logits, "logits", torch.float32)
+    _check(lib().vc_lm_head(R, Dm, V, _ptr(h), _ptr(w), _ptr(logits), _stream(stream)))
+    return logits
+
+
+def commit_rows(blk_k, blk_v, n_out, dst_k, dst_v, length, degree=None, stream=None):
+    """Append the first ``n_out[b]`` block rows to a cache (``vc_commit_rows``).
+
+    ``blk_k [B][Hkv][M][D]``, ``blk_v [B][Hkv][D][M]``, ``dst_k [B][Hkv][cap][D]``,
+    ``dst_v [B][Hkv][D][cap]``, ``length`` int32 ``[B][Hkv]`` (updated in place).
+    """
+    for t, n in ((blk_k, "blk_k"), (blk_v, "blk_v"), (dst_k, "dst_k"), (dst_v, "dst_v"), (degree, "degree")):
+        _dev(t, n)
+    _dev(n_out, "n_out", torch.int32)
+    _dev(length, "length", torch.int32)
+    B, Hkv, M, D = blk_k.shape
+    cap = dst_k.shape[2]
+    hstride = 0 if degree is None or degree.shape[1] == 1 else cap
+    _check(lib().vc_commit_rows(B, Hkv, D, M, _vc_dtype(blk_k), cap, _ptr(blk_k), _ptr(blk_v), _ptr(n_out),
+                                _ptr(dst_k), _ptr(dst_v), _ptr(length), _ptr(degree), hstride, _stream(stream)))
+
+
+class Stagger:
+    """Owner of the ``vc_stagger`` runtime object (copy streams, slot ring, events)."""
+
+    def __init__(self, slots, slot_bytes, max_layers):
+        arr = (_p * len(slots))(*[t.data_ptr() for t in slots])
+        self._slots = slots
+        h = _p()
+        _check(lib().vc_stagger_create(ctypes.byref(h), arr, len(slots), slot_bytes, max_layers))
+        self.h = h
+
+    def stream_layer(self, layer, host_src, nbytes):
+        _check(lib().vc_stagger_stream_layer(self.h, layer, _ptr(host_src), nbytes))
+
+    def acquire(self, layer, stream):
+        out = _p()
+        _check(lib().vc_stagger_acquire(self.h, layer, _stream(stream), ctypes.byref(out)))
+        return out.value
+
+    def release(self, layer, stream):
+        _check(lib().vc_stagger_release(self.h, layer, _stream(stream)))
+
+    def writeback(self, host_dst, dev_src, nbytes, after):
+        _check(lib().vc_stagger_writeback(self.h, _ptr(host_dst), _ptr(dev_src), nbytes, _stream(after)))
+
+    def after(self, stream):
+        _check(lib().vc_stagger_after(self.h, _stream(stream)))
+
+    def sync(self):
+        _check(lib().vc_stagger_sync(self.h))
+
+    def copy_ms(self, layer):
+        ms = ctypes.c_float()
+        _check(lib().vc_stagger_copy_ms(self.h, layer, ctypes.byref(ms)))
+        return ms.value
+
+    def close(self):
+        if self.h:
+            lib().vc_stagger_destroy(self.h)
+            self.h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

@@ -27,7 +27,8 @@ VC_DEVICE void better(float &bv, int &bi, float v, int i) {
 
 template <typename T, bool kVec>
 __global__ __launch_bounds__(kArgmaxThreads) void argmax_rows(const T *__restrict__ logits,
-                                                              int V, int *__restrict__ out) {
+                                                              int V, int *__restrict__ out,
+                                                              int out_stride) {
   const int row = blockIdx.x;
   const T *p = logits + (size_t)row * V;
   float bv = kNegInf;
@@ -72,7 +73,7 @@ __global__ __launch_bounds__(kArgmaxThreads) void argmax_rows(const T *__restric
   __syncthreads();
   if (tid == 0) {
     for (int w = 1; w < kArgmaxThreads / 64; ++w) better(bv, bi, sv[w], si[w]);
-    out[row] = (bi < V) ? bi : 0;
+    out[(size_t)row * out_stride] = (bi < V) ? bi : 0;
   }
 }
 
@@ -100,20 +101,25 @@ __global__ __launch_bounds__(64) void accept_rows(const int *__restrict__ draft,
 
 }  // namespace
 
-hipError_t launch_accept(const vc_accept_args &a, hipStream_t s) {
-  const int rows = a.B * a.M;
-  if (a.logit_dtype == VC_BF16) {
-    if (a.V % 8 == 0)
-      argmax_rows<uint16_t, true><<<rows, kArgmaxThreads, 0, s>>>((const uint16_t *)a.logits, a.V, a.argmax);
+hipError_t launch_argmax(int rows, int V, int dtype, const void *logits, int *out, int out_stride,
+                         hipStream_t s) {
+  if (rows == 0) return hipSuccess;
+  if (dtype == VC_BF16) {
+    if (V % 8 == 0)
+      argmax_rows<uint16_t, true><<<rows, kArgmaxThreads, 0, s>>>((const uint16_t *)logits, V, out, out_stride);
     else
-      argmax_rows<uint16_t, false><<<rows, kArgmaxThreads, 0, s>>>((const uint16_t *)a.logits, a.V, a.argmax);
+      argmax_rows<uint16_t, false><<<rows, kArgmaxThreads, 0, s>>>((const uint16_t *)logits, V, out, out_stride);
   } else {
-    if (a.V % 4 == 0)
-      argmax_rows<float, true><<<rows, kArgmaxThreads, 0, s>>>((const float *)a.logits, a.V, a.argmax);
+    if (V % 4 == 0)
+      argmax_rows<float, true><<<rows, kArgmaxThreads, 0, s>>>((const float *)logits, V, out, out_stride);
     else
-      argmax_rows<float, false><<<rows, kArgmaxThreads, 0, s>>>((const float *)a.logits, a.V, a.argmax);
+      argmax_rows<float, false><<<rows, kArgmaxThreads, 0, s>>>((const float *)logits, V, out, out_stride);
   }
-  hipError_t e = hipGetLastError();
+  return hipGetLastError();
+}
+
+hipError_t launch_accept(const vc_accept_args &a, hipStream_t s) {
+  hipError_t e = launch_argmax(a.B * a.M, a.V, a.logit_dtype, a.logits, a.argmax, 1, s);
   if (e != hipSuccess) return e;
   accept_rows<<<a.B, 64, 0, s>>>(a.draft, a.argmax, a.M, a.accept_len, a.out_tokens, a.n_out);
   return hipGetLastError();

@@ -100,6 +100,11 @@ vc_status check_verify(const vc_verify_args *a) {
 
 }  // namespace
 
+namespace vc {
+int lm_head(int R, int Dm, int V, const void *h, const void *w, float *logits, hipStream_t s, const char **err);
+vc_status set_error(vc_status s, const char *msg) { return fail(s, "%s", msg); }
+}  // namespace vc
+
 extern "C" {
 
 const char *vc_status_string(vc_status s) {
@@ -163,6 +168,41 @@ vc_status vc_accept(const vc_accept_args *a, void *stream) {
   REQ(a->M == 1 || a->draft, "draft is required when M > 1");
   REQ(aligned16(a->logits), "logits must be 16-byte aligned");
   return hip_status(vc::launch_accept(*a, (hipStream_t)stream), "vc_accept launch");
+}
+
+vc_status vc_argmax(int32_t R, int32_t V, int32_t logit_dtype, const void *logits, int32_t *out,
+                    int32_t out_stride, void *stream) {
+  REQ(R >= 0 && V >= 1 && out_stride >= 1, "R >= 0, V >= 1, out_stride >= 1 required");
+  REQ(logit_dtype == VC_BF16 || logit_dtype == VC_FP32, "unknown logit dtype %d", logit_dtype);
+  if (R == 0) return VC_OK;
+  REQ(logits && out, "null logits or output");
+  REQ(aligned16(logits), "logits must be 16-byte aligned");
+  return hip_status(vc::launch_argmax(R, V, logit_dtype, logits, out, out_stride, (hipStream_t)stream),
+                    "vc_argmax launch");
+}
+
+vc_status vc_lm_head(int32_t R, int32_t Dm, int32_t V, const void *h, const void *w, float *logits,
+                     void *stream) {
+  REQ(R >= 0 && Dm >= 1 && V >= 1, "R >= 0, Dm >= 1, V >= 1 required");
+  if (R == 0) return VC_OK;
+  REQ(h && w && logits, "null pointer");
+  const char *err = nullptr;
+  if (vc::lm_head(R, Dm, V, h, w, logits, (hipStream_t)stream, &err)) return fail(VC_EHIP, "vc_lm_head: %s", err);
+  return VC_OK;
+}
+
+vc_status vc_commit_rows(int32_t B, int32_t Hkv, int32_t D, int32_t M, int32_t dtype, int64_t cap,
+                         const void *blk_k, const void *blk_v, const int32_t *n_out, void *dst_k, void *dst_v,
+                         int32_t *len, float *degree, int64_t degree_h_stride, void *stream) {
+  REQ(B >= 0 && Hkv >= 1 && D >= 1 && M >= 1 && cap >= 0, "bad commit shape");
+  REQ(dtype == VC_BF16 || dtype == VC_FP32, "unknown dtype %d", dtype);
+  if (B == 0) return VC_OK;
+  REQ(blk_k && blk_v && n_out && dst_k && dst_v && len, "null pointer");
+  REQ(!degree || degree_h_stride == 0 || degree_h_stride == cap, "degree_h_stride must be 0 or cap");
+  const int64_t deg_b = degree_h_stride ? degree_h_stride * Hkv : cap;
+  return hip_status(vc::launch_commit(B, Hkv, D, M, dtype == VC_BF16 ? 2 : 4, cap, blk_k, blk_v, n_out, dst_k,
+                                      dst_v, len, degree, deg_b, degree_h_stride, (hipStream_t)stream),
+                    "vc_commit_rows launch");
 }
 
 }  // extern "C"

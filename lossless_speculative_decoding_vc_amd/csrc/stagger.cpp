@@ -1,0 +1,150 @@
+// Cross-resource staggering: streaming the full cache of the verifying
+// requests from pinned host memory while other requests draft from HBM.
+//
+// "Riepilogo Tecnico: VeriCache", "Innovazioni Chiave del Sistema", P1: draft
+// is bound by GPU HBM bandwidth, verify by the interconnect that brings the
+// full cache from CPU memory; the runtime staggers requests so that both
+// resources stay busy.  "Supporto Architetturale": for long-context decoding
+// the full cache lives in CPU memory and verification loads it over PCIe.
+//
+// The object below is the runtime half of that schedule: a host-to-device
+// copy stream feeding a ring of device staging slots layer by layer, a
+// write-back stream for committed rows, and the events that order them
+// against the compute streams (verify waits for its layer's copy; a slot is
+// refilled only after the verify that read it has finished).  Which kernels
+// run on which compute stream is the caller's choice; the draft work of the
+// other cohort goes on a stream that never waits for a copy.
+#include <hip/hip_runtime.h>
+
+#include <string>
+#include <vector>
+
+#include "../../include/vc.h"
+
+struct vc_stagger {
+  std::vector<void *> slots;
+  size_t slot_bytes = 0;
+  hipStream_t h2d = nullptr, d2h = nullptr;
+  std::vector<hipEvent_t> slot_free;             // per slot
+  std::vector<hipEvent_t> copy_start, copied;    // per layer
+  std::vector<char> copy_recorded;
+};
+
+namespace vc {
+vc_status set_error(vc_status s, const char *msg);
+}
+
+namespace {
+
+vc_status hipfail(hipError_t e, const char *what) {
+  return vc::set_error(VC_EHIP, (std::string(what) + ": " + hipGetErrorString(e)).c_str());
+}
+
+#define HIPCHK(x)                            \
+  do {                                       \
+    hipError_t e_ = (x);                     \
+    if (e_ != hipSuccess) return hipfail(e_, #x); \
+  } while (0)
+
+}  // namespace
+
+extern "C" {
+
+vc_status vc_stagger_create(vc_stagger **out, void *const *slots, int32_t nslots, size_t slot_bytes,
+                            int32_t max_layers) {
+  if (!out || !slots || nslots < 1 || max_layers < 1) return vc::set_error(VC_EINVAL, "bad stagger arguments");
+  for (int i = 0; i < nslots; ++i)
+    if (!slots[i]) return vc::set_error(VC_EINVAL, "null staging slot");
+  vc_stagger *s = new vc_stagger;
+  s->slots.assign(slots, slots + nslots);
+  s->slot_bytes = slot_bytes;
+  HIPCHK(hipStreamCreateWithFlags(&s->h2d, hipStreamNonBlocking));
+  HIPCHK(hipStreamCreateWithFlags(&s->d2h, hipStreamNonBlocking));
+  s->slot_free.resize(nslots);
+  for (auto &e : s->slot_free) HIPCHK(hipEventCreateWithFlags(&e, hipEventDisableTiming));
+  s->copy_start.resize(max_layers);
+  s->copied.resize(max_layers);
+  s->copy_recorded.assign(max_layers, 0);
+  for (int l = 0; l < max_layers; ++l) {
+    HIPCHK(hipEventCreate(&s->copy_start[l]));
+    HIPCHK(hipEventCreate(&s->copied[l]));
+  }
+  *out = s;
+  return VC_OK;
+}
+
+vc_status vc_stagger_stream_layer(vc_stagger *s, int32_t layer, const void *host_src, size_t bytes) {
+  if (!s || layer < 0 || layer >= (int)s->copied.size() || !host_src || bytes > s->slot_bytes)
+    return vc::set_error(VC_EINVAL, "bad stream_layer arguments");
+  const int slot = layer % (int)s->slots.size();
+  HIPCHK(hipStreamWaitEvent(s->h2d, s->slot_free[slot], 0));
+  HIPCHK(hipEventRecord(s->copy_start[layer], s->h2d));
+  HIPCHK(hipMemcpyAsync(s->slots[slot], host_src, bytes, hipMemcpyHostToDevice, s->h2d));
+  HIPCHK(hipEventRecord(s->copied[layer], s->h2d));
+  s->copy_recorded[layer] = 1;
+  return VC_OK;
+}
+
+vc_status vc_stagger_acquire(vc_stagger *s, int32_t layer, void *stream, void **slot) {
+  if (!s || layer < 0 || layer >= (int)s->copied.size() || !slot || !s->copy_recorded[layer])
+    return vc::set_error(VC_EINVAL, "acquire of a layer that was not streamed");
+  HIPCHK(hipStreamWaitEvent((hipStream_t)stream, s->copied[layer], 0));
+  *slot = s->slots[layer % (int)s->slots.size()];
+  return VC_OK;
+}
+
+vc_status vc_stagger_release(vc_stagger *s, int32_t layer, void *stream) {
+  if (!s || layer < 0 || layer >= (int)s->copied.size()) return vc::set_error(VC_EINVAL, "bad release");
+  HIPCHK(hipEventRecord(s->slot_free[layer % (int)s->slots.size()], (hipStream_t)stream));
+  return VC_OK;
+}
+
+vc_status vc_stagger_writeback(vc_stagger *s, void *host_dst, const void *dev_src, size_t bytes, void *after) {
+  if (!s || !host_dst || !dev_src) return vc::set_error(VC_EINVAL, "bad writeback arguments");
+  hipEvent_t ev;
+  HIPCHK(hipEventCreateWithFlags(&ev, hipEventDisableTiming));
+  HIPCHK(hipEventRecord(ev, (hipStream_t)after));
+  HIPCHK(hipStreamWaitEvent(s->d2h, ev, 0));
+  HIPCHK(hipEventDestroy(ev));
+  HIPCHK(hipMemcpyAsync(host_dst, dev_src, bytes, hipMemcpyDeviceToHost, s->d2h));
+  return VC_OK;
+}
+
+vc_status vc_stagger_after(vc_stagger *s, void *stream) {
+  if (!s) return vc::set_error(VC_EINVAL, "null stagger");
+  hipEvent_t ev;
+  HIPCHK(hipEventCreateWithFlags(&ev, hipEventDisableTiming));
+  HIPCHK(hipEventRecord(ev, (hipStream_t)stream));
+  HIPCHK(hipStreamWaitEvent(s->h2d, ev, 0));
+  HIPCHK(hipEventDestroy(ev));
+  return VC_OK;
+}
+
+vc_status vc_stagger_sync(vc_stagger *s) {
+  if (!s) return vc::set_error(VC_EINVAL, "null stagger");
+  HIPCHK(hipStreamSynchronize(s->h2d));
+  HIPCHK(hipStreamSynchronize(s->d2h));
+  return VC_OK;
+}
+
+vc_status vc_stagger_copy_ms(vc_stagger *s, int32_t layer, float *ms) {
+  if (!s || layer < 0 || layer >= (int)s->copied.size() || !ms || !s->copy_recorded[layer])
+    return vc::set_error(VC_EINVAL, "no copy recorded for this layer");
+  HIPCHK(hipEventElapsedTime(ms, s->copy_start[layer], s->copied[layer]));
+  return VC_OK;
+}
+
+vc_status vc_stagger_destroy(vc_stagger *s) {
+  if (!s) return VC_OK;
+  if (s->h2d) (void)hipStreamSynchronize(s->h2d);
+  if (s->d2h) (void)hipStreamSynchronize(s->d2h);
+  for (auto e : s->slot_free) (void)hipEventDestroy(e);
+  for (auto e : s->copy_start) (void)hipEventDestroy(e);
+  for (auto e : s->copied) (void)hipEventDestroy(e);
+  if (s->h2d) (void)hipStreamDestroy(s->h2d);
+  if (s->d2h) (void)hipStreamDestroy(s->d2h);
+  delete s;
+  return VC_OK;
+}
+
+}  // extern "C"
