@@ -4,8 +4,10 @@
 // softmax-normalised output o_s and its log-sum-exp lse_s (base 2).  The
 // attention over the union of the ranges is
 //   o = sum_s 2^(lse_s - L) o_s,   L = log2 sum_s 2^lse_s,
-// the standard flash-decoding reduction.  One wave per (row, head); reads
-// splits x (D + 1) floats, writes D outputs.
+// the standard flash-decoding reduction.  One wave per (row, head): the
+// lanes first read all split weights in one coalesced pass, then every lane
+// accumulates its D/64 channels over the splits with the weight broadcast
+// from the lane that read it (8 splits in flight).
 #include "common.h"
 #include "launch.h"
 
@@ -17,25 +19,39 @@ __global__ __launch_bounds__(64) void combine_splits(const float *__restrict__ p
                                                      const float *__restrict__ part_lse,
                                                      int splits, int rows, void *__restrict__ out,
                                                      float *__restrict__ out_lse) {
+  constexpr int kPer = D / 64;
   const int row = blockIdx.x;
   const int lane = threadIdx.x;
   float mx = kNegInf;
-  for (int s = 0; s < splits; ++s) mx = fmaxf(mx, part_lse[(size_t)s * rows + row]);
-  constexpr int kPer = D / 64;
+  for (int s = lane; s < splits; s += 64) mx = fmaxf(mx, part_lse[(size_t)s * rows + row]);
+  mx = wave_max(mx);
+  const float mu = (mx == kNegInf) ? 0.f : mx;
   float acc[kPer];
 #pragma unroll
   for (int e = 0; e < kPer; ++e) acc[e] = 0.f;
   float wsum = 0.f;
-  if (mx != kNegInf) {
-    for (int s = 0; s < splits; ++s) {
-      const float l = part_lse[(size_t)s * rows + row];
-      const float w = fast_exp2(l - mx);   // 0 for empty splits (l = -inf)
-      wsum += w;
-      const float *po = part_o + ((size_t)s * rows + row) * D;
+  for (int s0 = 0; s0 < splits; s0 += 64) {
+    const int sl = s0 + lane;
+    const float w_mine = (sl < splits) ? fast_exp2(part_lse[(size_t)sl * rows + row] - mu) : 0.f;
+    wsum += w_mine;
+    const int n = min(64, splits - s0);
+    for (int j0 = 0; j0 < n; j0 += 8) {
+      float w[8], v[8][kPer];
 #pragma unroll
-      for (int e = 0; e < kPer; ++e) acc[e] += w * po[lane * kPer + e];
+      for (int u = 0; u < 8; ++u) {
+        const int j = j0 + u;
+        w[u] = __shfl(w_mine, j < n ? j : 0, 64);
+        const float *po = part_o + ((size_t)(s0 + (j < n ? j : 0)) * rows + row) * D + lane * kPer;
+#pragma unroll
+        for (int e = 0; e < kPer; ++e) v[u][e] = (j < n) ? po[e] : 0.f;
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+#pragma unroll
+        for (int e = 0; e < kPer; ++e) acc[e] += w[u] * v[u][e];
     }
   }
+  wsum = wave_sum(wsum);
   const float inv = 1.f / wsum;   // wsum == 0 only for an empty key set -> NaN output
 #pragma unroll
   for (int e = 0; e < kPer; ++e) {
@@ -43,7 +59,7 @@ __global__ __launch_bounds__(64) void combine_splits(const float *__restrict__ p
     if constexpr (kBf16) reinterpret_cast<uint16_t *>(out)[(size_t)row * D + lane * kPer + e] = f32_to_bf16(v);
     else reinterpret_cast<float *>(out)[(size_t)row * D + lane * kPer + e] = v;
   }
-  if (out_lse && lane == 0) out_lse[row] = (mx + fast_log2(wsum)) * kLn2;
+  if (out_lse && lane == 0) out_lse[row] = (wsum > 0.f) ? (mx + fast_log2(wsum)) * kLn2 : kNegInf;
 }
 
 }  // namespace

@@ -10,14 +10,15 @@
 //  * grid (splits, B*Hkv); 4 waves per workgroup; every wave serves ALL
 //    G = Hq/Hkv query heads of its KV head, so each K/V byte is read from
 //    HBM exactly once per call.
-//  * a wave walks 64-token chunks.  Both contractions run on
+//  * a wave walks 32-token chunks, the next chunk's loads in flight while
+//    the current one is computed.  Both contractions run on
 //    v_mfma_f32_16x16x32_bf16 with operands loaded straight from HBM into
 //    registers (no LDS): S^T = K Q^T (A = 16 token rows of K, 16 bytes per
 //    lane; B = Q^T, one column per query head) and O^T = V^T P^T (A = 16
 //    channel rows of the channel-major V, 16 bytes = 8 consecutive tokens
 //    per lane; B = the probabilities, already in the lanes that produced
 //    them).  Token rows of the S^T tiles are permuted so that each lane's
-//    four score registers of two neighbouring tiles are 8 consecutive
+//    four score registers of the two S^T tiles are 8 consecutive
 //    tokens -- exactly the k-slots the PV MFMA needs; no data moves between
 //    lanes except two max-shuffles per chunk.
 //  * online softmax in base 2 (scores pre-multiplied by log2 e; the degree
@@ -31,7 +32,7 @@ namespace vc {
 namespace {
 
 constexpr int kDraftWaves = 4;
-constexpr int kChunk = 64;
+constexpr int kChunk = 32;   // tokens per wave step
 
 struct DraftParams {
   int B, Hq, Hkv, G, splits;
@@ -50,6 +51,15 @@ struct DraftParams {
 };
 
 VC_DEVICE u32x4 ld16(const uint16_t *p) { return *reinterpret_cast<const u32x4 *>(p); }
+
+// Registers of one 32-token chunk: K A-operands of the two S^T tiles, V^T
+// A-operands of the PV k-step, log2 degrees of the lane's 8 tokens.
+template <int D>
+struct DraftChunk {
+  u32x4 ka[2][D / 32];
+  u32x4 va[D / 16];
+  float lg[8];
+};
 
 template <int D>
 __global__ __launch_bounds__(kDraftWaves * 64) void draft_bf16_dense(DraftParams p) {
@@ -91,106 +101,93 @@ __global__ __launch_bounds__(kDraftWaves * 64) void draft_bf16_dense(DraftParams
   const uint16_t *tvb = p.tail_v ? p.tail_v + (size_t)bh * D * p.tcap : nullptr;
   const float *db = p.degree ? p.degree + b * p.deg_b_stride + kvh * p.deg_h_stride : nullptr;
 
-  float m_run = kNegInf, l_run = 0.f;
-  f32x4 o[DT];
-#pragma unroll
-  for (int dt = 0; dt < DT; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  for (int c = c0 + wave; c < c1; c += kDraftWaves) {
+  // S^T tile tau, row m (= lane col) holds token base + 8*(m>>2) + 4*tau + (m&3),
+  // so the lane's 4+4 score registers are tokens base + 8*grp + 0..7.
+  auto fetch = [&](int c, DraftChunk<D> &ch) __attribute__((always_inline)) {
     const int base = c * kChunk;
-    u32x4 ka[4][KS];
-    u32x4 va[DT][2];
-    float lg[16];   // log2 degree of the lane's 16 tokens (kappa-major)
-    const bool fast = base + kChunk <= mlen;
-    if (fast) {
+    if (base + kChunk <= mlen) {
 #pragma unroll
-      for (int tau = 0; tau < 4; ++tau) {
-        const int t = base + 32 * (tau >> 1) + 8 * (col >> 2) + 4 * (tau & 1) + (col & 3);
+      for (int tau = 0; tau < 2; ++tau) {
+        const int t = base + 8 * (col >> 2) + 4 * tau + (col & 3);
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) ka[tau][ks] = ld16(kb + (size_t)t * D + 32 * ks + 8 * grp);
+        for (int ks = 0; ks < KS; ++ks) ch.ka[tau][ks] = ld16(kb + (size_t)t * D + 32 * ks + 8 * grp);
       }
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-        for (int kp = 0; kp < 2; ++kp)
-          va[dt][kp] = ld16(vb + (size_t)(16 * dt + col) * p.cap + base + 32 * kp + 8 * grp);
+      for (int dt = 0; dt < DT; ++dt) ch.va[dt] = ld16(vb + (size_t)(16 * dt + col) * p.cap + base + 8 * grp);
       if (db) {
+        const f32x4 *dp = reinterpret_cast<const f32x4 *>(db + base + 8 * grp);
+        const f32x4 d0 = dp[0], d1 = dp[1];
 #pragma unroll
-        for (int kp = 0; kp < 2; ++kp) {
-          const f32x4 *dp = reinterpret_cast<const f32x4 *>(db + base + 32 * kp + 8 * grp);
-          const f32x4 d0 = dp[0], d1 = dp[1];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            lg[8 * kp + e] = fast_log2(d0[e]);
-            lg[8 * kp + 4 + e] = fast_log2(d1[e]);
-          }
+        for (int e = 0; e < 4; ++e) {
+          ch.lg[e] = fast_log2(d0[e]);
+          ch.lg[4 + e] = fast_log2(d1[e]);
         }
       } else {
 #pragma unroll
-        for (int e = 0; e < 16; ++e) lg[e] = 0.f;
+        for (int e = 0; e < 8; ++e) ch.lg[e] = 0.f;
       }
     } else {
       // Chunk crossing the end of the main segment: per-row source select
       // for K, per-element select for V (tail tokens, zero past the end).
 #pragma unroll
-      for (int tau = 0; tau < 4; ++tau) {
-        const int t = base + 32 * (tau >> 1) + 8 * (col >> 2) + 4 * (tau & 1) + (col & 3);
+      for (int tau = 0; tau < 2; ++tau) {
+        const int t = base + 8 * (col >> 2) + 4 * tau + (col & 3);
         const uint16_t *row = nullptr;
         if (t < mlen) row = kb + (size_t)t * D;
         else if (t < total) row = tkb + (size_t)(t - mlen) * D;
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-          ka[tau][ks] = row ? ld16(row + 32 * ks + 8 * grp) : u32x4{0, 0, 0, 0};
+        for (int ks = 0; ks < KS; ++ks) ch.ka[tau][ks] = row ? ld16(row + 32 * ks + 8 * grp) : u32x4{0, 0, 0, 0};
       }
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
         const int d = 16 * dt + col;
+        uint32_t w[4];
 #pragma unroll
-        for (int kp = 0; kp < 2; ++kp) {
-          uint32_t w[4];
+        for (int e2 = 0; e2 < 4; ++e2) {
+          uint32_t h[2];
 #pragma unroll
-          for (int e2 = 0; e2 < 4; ++e2) {
-            uint32_t h[2];
-#pragma unroll
-            for (int u = 0; u < 2; ++u) {
-              const int t = base + 32 * kp + 8 * grp + 2 * e2 + u;
-              uint16_t x = 0;
-              if (t < mlen) x = vb[(size_t)d * p.cap + t];
-              else if (t < total) x = tvb[(size_t)d * p.tcap + (t - mlen)];
-              h[u] = x;
-            }
-            w[e2] = h[0] | (h[1] << 16);
+          for (int u = 0; u < 2; ++u) {
+            const int t = base + 8 * grp + 2 * e2 + u;
+            uint16_t x = 0;
+            if (t < mlen) x = vb[(size_t)d * p.cap + t];
+            else if (t < total) x = tvb[(size_t)d * p.tcap + (t - mlen)];
+            h[u] = x;
           }
-          va[dt][kp] = u32x4{w[0], w[1], w[2], w[3]};
+          w[e2] = h[0] | (h[1] << 16);
         }
+        ch.va[dt] = u32x4{w[0], w[1], w[2], w[3]};
       }
 #pragma unroll
-      for (int kp = 0; kp < 2; ++kp)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int t = base + 32 * kp + 8 * grp + e;
-          lg[8 * kp + e] = (db && t < mlen) ? fast_log2(db[t]) : 0.f;
-        }
+      for (int e = 0; e < 8; ++e) {
+        const int t = base + 8 * grp + e;
+        ch.lg[e] = (db && t < mlen) ? fast_log2(db[t]) : 0.f;
+      }
     }
+  };
 
-    // S^T tiles: lane holds head `col`, tokens base + 32*(tau>>1) + 8*grp + 4*(tau&1) + i.
-    f32x4 s[4];
+  float m_run = kNegInf, l_run = 0.f;
+  f32x4 o[DT];
 #pragma unroll
-    for (int tau = 0; tau < 4; ++tau) {
+  for (int dt = 0; dt < DT; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  auto compute = [&](int c, const DraftChunk<D> &ch) __attribute__((always_inline)) {
+    const int base = c * kChunk;
+    f32x4 s[2];
+#pragma unroll
+    for (int tau = 0; tau < 2; ++tau) {
       s[tau] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) s[tau] = mfma16x16x32(as_bf16x8(ka[tau][ks]), qb[ks], s[tau]);
+      for (int ks = 0; ks < KS; ++ks) s[tau] = mfma16x16x32(as_bf16x8(ch.ka[tau][ks]), qb[ks], s[tau]);
     }
-    float sc[16];
+    float sc[8];
     float cmax = kNegInf;
 #pragma unroll
-    for (int tau = 0; tau < 4; ++tau)
+    for (int tau = 0; tau < 2; ++tau)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int e = 8 * (tau >> 1) + 4 * (tau & 1) + i;   // kappa-major token slot
-        const int t = base + 32 * (tau >> 1) + 8 * grp + 4 * (tau & 1) + i;
-        float x = s[tau][i] * p.qk_scale + lg[e];
-        x = (t < total) ? x : kNegInf;
+        const int e = 4 * tau + i;
+        float x = s[tau][i] * p.qk_scale + ch.lg[e];
+        x = (base + 8 * grp + e < total) ? x : kNegInf;
         sc[e] = x;
         cmax = fmaxf(cmax, x);
       }
@@ -199,26 +196,37 @@ __global__ __launch_bounds__(kDraftWaves * 64) void draft_bf16_dense(DraftParams
     const float m_new = fmaxf(m_run, cmax);
     const float m_use = (m_new == kNegInf) ? 0.f : m_new;
     const float alpha = fast_exp2(m_run - m_use);
-    float pr[16];
+    float pr[8];
     float psum = 0.f;
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
+    for (int e = 0; e < 8; ++e) {
       pr[e] = fast_exp2(sc[e] - m_use);
       psum += pr[e];
     }
     l_run = l_run * alpha + psum;
+    if (__any(m_new != m_run)) {
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) o[dt] *= alpha;
+    }
     m_run = m_new;
+    const bf16x8 pb = as_bf16x8(u32x4{pack_bf16x2(pr[0], pr[1]), pack_bf16x2(pr[2], pr[3]),
+                                      pack_bf16x2(pr[4], pr[5]), pack_bf16x2(pr[6], pr[7])});
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) o[dt] *= alpha;
-    bf16x8 pb[2];
-#pragma unroll
-    for (int kp = 0; kp < 2; ++kp)
-      pb[kp] = as_bf16x8(u32x4{pack_bf16x2(pr[8 * kp + 0], pr[8 * kp + 1]), pack_bf16x2(pr[8 * kp + 2], pr[8 * kp + 3]),
-                               pack_bf16x2(pr[8 * kp + 4], pr[8 * kp + 5]), pack_bf16x2(pr[8 * kp + 6], pr[8 * kp + 7])});
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-      for (int kp = 0; kp < 2; ++kp) o[dt] = mfma16x16x32(as_bf16x8(va[dt][kp]), pb[kp], o[dt]);
+    for (int dt = 0; dt < DT; ++dt) o[dt] = mfma16x16x32(as_bf16x8(ch.va[dt]), pb, o[dt]);
+  };
+
+  // Software pipeline: the next chunk's loads are in flight while the
+  // current one is computed (unrolled by two so the buffers stay static).
+  DraftChunk<D> ca, cb;
+  int c = c0 + wave;
+  if (c < c1) fetch(c, ca);
+  for (; c < c1; c += 2 * kDraftWaves) {
+    const int cn = c + kDraftWaves;
+    if (cn < c1) fetch(cn, cb);
+    compute(c, ca);
+    if (cn >= c1) break;
+    if (cn + kDraftWaves < c1) fetch(cn + kDraftWaves, ca);
+    compute(cn, cb);
   }
 
   // Merge the lane groups' partial sums, then the 4 waves through LDS.
@@ -272,7 +280,7 @@ SplitPlan plan_draft(const vc_draft_args &a) {
   int s = a.num_splits;
   if (s <= 0) {
     s = 1;
-    while (pairs * s < 1024 && chunks / (s * 2) >= 8) s *= 2;
+    while (pairs * s < 1024 && chunks / (s * 2) >= 16) s *= 2;
   }
   if (s > chunks && chunks > 0) s = (int)chunks;
   if (s < 1) s = 1;

@@ -10,23 +10,33 @@
 //  * the M block rows times the G = Hq/Hkv query heads that share a KV head
 //    are packed into R = M*G query rows, so one pass over a KV head's keys
 //    serves all of them (the contraction that makes verify dense).
-//  * grid (splits, row tiles, B*Hkv); W waves per workgroup, 32 rows per
-//    wave; the workgroup streams 32-token tiles of K (token-major) and V
-//    (channel-major) through double-buffered LDS, every wave reading the
-//    same tile, so K/V leave HBM once per row tile.
+//  * grid (splits, row groups, B*Hkv); up to 8 waves per workgroup (two per
+//    SIMD, so one wave's LDS latency hides behind the other's MFMAs), each
+//    wave owns two column tiles of 16 packed rows, so a row group covers up
+//    to 256 rows and K/V leave HBM once per row group.
+//  * the workgroup streams 64-token tiles of K (token-major) and V
+//    (channel-major) through a ring of 4 LDS stages filled by direct
+//    global->LDS loads (global_load_lds_dwordx4): three tiles stay in flight
+//    (96 KB per CU at head_dim 128) without holding any of them in
+//    registers.  Each wave-wide load lands as 1 KB of contiguous LDS, so bank
+//    conflicts are avoided by XOR-swizzling which 16-byte piece a lane
+//    fetches instead of padding rows.  Tiles that reach the block keys or
+//    the end of the key sequence are staged through registers.
 //  * S^T = K Q^T and O^T = V^T P^T on v_mfma_f32_16x16x32_bf16; the token
-//    rows of the two S^T tiles are permuted so that each lane's scores are
-//    the 8 consecutive tokens the PV MFMA consumes as its k-slots: P never
-//    leaves the registers it was computed in.
+//    rows of the S^T tiles are permuted so each lane's scores are the 8
+//    consecutive tokens the PV MFMA consumes as its k-slots: P never leaves
+//    the registers it was computed in.
 //  * fp32 online softmax in base 2, one running max per packed row; causal
-//    masking only in tiles that reach the block.
+//    masking only in tiles that reach the block; the output rescale is
+//    skipped when no row's max moved.
 #include "common.h"
 #include "launch.h"
 
 namespace vc {
 namespace {
 
-constexpr int kTile = 32;   // tokens per LDS tile
+constexpr int kTile = 64;      // tokens per LDS tile
+constexpr int kStages = 4;     // LDS ring depth
 
 struct VerifyParams {
   int B, Hq, Hkv, G, M, R, splits;
@@ -42,31 +52,92 @@ struct VerifyParams {
 };
 
 template <int D>
-struct VerifyLds {
-  static constexpr int kKStride = D * 2 + 16;   // bytes per K row (padded)
-  static constexpr int kVStride = kTile * 2 + 16;   // bytes per V channel row (padded)
-  static constexpr int kKBytes = kTile * kKStride;
-  static constexpr int kVBytes = D * kVStride;
-  static constexpr int kBuf = kKBytes + kVBytes;
+struct Lds {
+  static constexpr int kKRow = D * 2;                   // bytes per K token row
+  static constexpr int kKBytes = kTile * kKRow;
+  static constexpr int kVRow = kTile * 2;               // bytes per V channel row (128)
+  static constexpr int kVBytes = D * kVRow;
+  static constexpr int kStage = kKBytes + kVBytes;      // 256 * D bytes
+  static constexpr int kBlocks = kStage / 1024;         // 1 KB per wave-wide load
+  static constexpr int kKBlocks = kKBytes / 1024;
+  static constexpr int kSlots = kKRow / 16;             // 16-byte slots per K row
+  static constexpr int kRowsPerBlock = 1024 / kKRow;
 };
 
-template <int D, int W>
+// LDS row r of a K tile holds token ktok(r) of S^T tile r/16, row r%16, so
+// the 16 lanes of one operand read hit 16 consecutive rows.
+VC_DEVICE int ktok(int r) {
+  const int tau = r >> 4, m = r & 15;
+  return 32 * (tau >> 1) + 8 * (m >> 2) + 4 * (tau & 1) + (m & 3);
+}
+// XOR swizzle of 16-byte slots (an involution: maps logical <-> physical).
+template <int D>
+VC_DEVICE int kswz(int r, int slot) {
+  return (D == 128) ? (slot ^ (r & 15)) : (slot ^ ((r >> 1) & 7));
+}
+VC_DEVICE int vswz(int d, int slot) { return slot ^ ((d >> 1) & 7); }
+
+// One 16-byte direct global->LDS load per lane: lane i's piece lands at
+// LDS byte address lds_addr + 16*i.  Issued through inline assembly so the
+// compiler does not serialise it against later LDS accesses; completion is
+// tracked explicitly with s_waitcnt vmcnt and a workgroup barrier.
+VC_DEVICE void load_lds16(const void *gptr, uint32_t lds_addr) {
+  __asm__ volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gptr), "s"(lds_addr) : "memory", "m0");
+}
+
+// Tile that reaches the block keys or the end of the key sequence: staged
+// through registers with the same swizzled layout (zero past the end).
+template <int D>
+__device__ __noinline__ void stage_slow(uint8_t *st, int base, int cl, int total, int M, int64_t ccap,
+                                        const uint16_t *ckb, const uint16_t *cvb, const uint16_t *bkb,
+                                        const uint16_t *bvb, int tid, int nthreads) {
+  using L = Lds<D>;
+  for (int pc = tid; pc < L::kBlocks * 64; pc += nthreads) {
+    const int q = pc >> 6, ln = pc & 63;
+    u32x4 v = u32x4{0, 0, 0, 0};
+    if (q < L::kKBlocks) {
+      const int r = q * L::kRowsPerBlock + ln / L::kSlots;
+      const int seg = kswz<D>(r, ln % L::kSlots);
+      const int j = base + ktok(r);
+      if (j < cl) v = *reinterpret_cast<const u32x4 *>(ckb + (size_t)j * D + 8 * seg);
+      else if (j < total) v = *reinterpret_cast<const u32x4 *>(bkb + (size_t)(j - cl) * D + 8 * seg);
+    } else {
+      const int d = (q - L::kKBlocks) * 8 + ln / 8;
+      const int j0 = base + 8 * vswz(d, ln % 8);
+      uint32_t w[4];
+      for (int e2 = 0; e2 < 4; ++e2) {
+        uint32_t h[2];
+        for (int uu = 0; uu < 2; ++uu) {
+          const int j = j0 + 2 * e2 + uu;
+          uint16_t x = 0;
+          if (j < cl) x = cvb[(size_t)d * ccap + j];
+          else if (j < total) x = bvb[(size_t)d * M + (j - cl)];
+          h[uu] = x;
+        }
+        w[e2] = h[0] | (h[1] << 16);
+      }
+      v = u32x4{w[0], w[1], w[2], w[3]};
+    }
+    *reinterpret_cast<u32x4 *>(st + q * 1024 + ln * 16) = v;
+  }
+}
+
+template <int D, int W, int CT>
 __global__ __launch_bounds__(W * 64) void verify_bf16(VerifyParams p) {
-  using L = VerifyLds<D>;
+  using L = Lds<D>;
   constexpr int KS = D / 32, DT = D / 16;
-  constexpr int kPieces = 8 * D;   // 16-byte pieces per tile: K 4D + V 4D
   constexpr int kThreads = W * 64;
-  constexpr int kPer = (kPieces + kThreads - 1) / kThreads;
-  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * L::kBuf];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[kStages * L::kStage];
 
   const int bh = blockIdx.z;
   const int b = bh / p.Hkv, kvh = bh % p.Hkv;
   const int split = blockIdx.x;
   const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
   const int col = lane & 15, grp = lane >> 4;
   const int G = p.G, M = p.M;
-  const int r0 = blockIdx.y * (32 * W) + 32 * wave;
+  const int r0 = blockIdx.y * (16 * CT * W) + 16 * CT * wave;   // first packed row of this wave
 
   int cl = p.ctx_len[b];
   cl = cl < 0 ? 0 : (cl > p.ccap ? (int)p.ccap : cl);
@@ -77,20 +148,20 @@ __global__ __launch_bounds__(W * 64) void verify_bf16(VerifyParams p) {
   const int c1 = min(c0 + cps, nchunks);
 
   // Q^T operands: column = packed row r = i*G + g.
-  bf16x8 qb[2][KS];
-  int row_i[2];
+  bf16x8 qb[CT][KS];
+  int row_lim[CT];   // row r sees key j iff j < row_lim = cl + i + 1
 #pragma unroll
-  for (int c = 0; c < 2; ++c) {
-    const int r = r0 + 16 * c + col;
-    row_i[c] = r / G;
+  for (int ct = 0; ct < CT; ++ct) {
+    const int r = r0 + 16 * ct + col;
+    row_lim[ct] = cl + r / G + 1;
     if (r < p.R) {
       const int i = r / G, g = r % G;
       const uint16_t *qp = p.q + (((size_t)b * M + i) * p.Hq + kvh * G + g) * D;
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) qb[c][ks] = as_bf16x8(*reinterpret_cast<const u32x4 *>(qp + 32 * ks + 8 * grp));
+      for (int ks = 0; ks < KS; ++ks) qb[ct][ks] = as_bf16x8(*reinterpret_cast<const u32x4 *>(qp + 32 * ks + 8 * grp));
     } else {
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) qb[c][ks] = as_bf16x8(u32x4{0, 0, 0, 0});
+      for (int ks = 0; ks < KS; ++ks) qb[ct][ks] = as_bf16x8(u32x4{0, 0, 0, 0});
     }
   }
 
@@ -98,202 +169,220 @@ __global__ __launch_bounds__(W * 64) void verify_bf16(VerifyParams p) {
   const uint16_t *cvb = p.cv + (size_t)bh * D * p.ccap;
   const uint16_t *bkb = p.bk + (size_t)bh * M * D;
   const uint16_t *bvb = p.bv + (size_t)bh * D * M;
+  const uint32_t lds_base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t *)lds;
 
-  auto fetch = [&](int c, u32x4 *reg) {
+  // A tile is "full" when all 64 tokens are context tokens: then each wave
+  // fetches whole 1 KB blocks straight into LDS (block q: 4 K rows or 8 V
+  // channel rows, lanes ordered by physical slot).
+  auto full = [&](int c) __attribute__((always_inline)) { return c * kTile + kTile <= cl; };
+  auto issue = [&](int c) __attribute__((always_inline)) {
+    if (c >= c1) return;
+    const int stage = c & (kStages - 1);
     const int base = c * kTile;
-#pragma unroll
-    for (int u = 0; u < kPer; ++u) {
-      const int pc = tid + u * kThreads;
-      u32x4 v = u32x4{0, 0, 0, 0};
-      if (pc < 4 * D) {   // K piece: row, 16-byte segment
-        const int row = pc / (D / 8), seg = pc % (D / 8);
-        const int j = base + row;
-        if (j < cl) v = *reinterpret_cast<const u32x4 *>(ckb + (size_t)j * D + 8 * seg);
-        else if (j < total) v = *reinterpret_cast<const u32x4 *>(bkb + (size_t)(j - cl) * D + 8 * seg);
-      } else if (pc < kPieces) {   // V piece: channel, 8 tokens
-        const int pv = pc - 4 * D;
-        const int d = pv >> 2, q4 = pv & 3;
-        const int j0 = base + 8 * q4;
-        if (j0 + 8 <= cl) {
-          v = *reinterpret_cast<const u32x4 *>(cvb + (size_t)d * p.ccap + j0);
+    if (full(c)) {
+      for (int q = wave; q < L::kBlocks; q += W) {
+        const uint16_t *src;
+        if (q < L::kKBlocks) {
+          const int r = q * L::kRowsPerBlock + lane / L::kSlots;
+          src = ckb + (size_t)(base + ktok(r)) * D + 8 * kswz<D>(r, lane % L::kSlots);
         } else {
-          uint32_t w[4];
-#pragma unroll
-          for (int e2 = 0; e2 < 4; ++e2) {
-            uint32_t h[2];
-#pragma unroll
-            for (int uu = 0; uu < 2; ++uu) {
-              const int j = j0 + 2 * e2 + uu;
-              uint16_t x = 0;
-              if (j < cl) x = cvb[(size_t)d * p.ccap + j];
-              else if (j < total) x = bvb[(size_t)d * M + (j - cl)];
-              h[uu] = x;
-            }
-            w[e2] = h[0] | (h[1] << 16);
-          }
-          v = u32x4{w[0], w[1], w[2], w[3]};
+          const int d = (q - L::kKBlocks) * 8 + lane / 8;
+          src = cvb + (size_t)d * p.ccap + base + 8 * vswz(d, lane % 8);
         }
+        load_lds16(src, lds_base + (uint32_t)(stage * L::kStage + q * 1024));
       }
-      reg[u] = v;
-    }
-  };
-  auto stash = [&](int buf, const u32x4 *reg) {
-    uint8_t *base = lds + buf * L::kBuf;
-#pragma unroll
-    for (int u = 0; u < kPer; ++u) {
-      const int pc = tid + u * kThreads;
-      if (pc < 4 * D) {
-        const int row = pc / (D / 8), seg = pc % (D / 8);
-        *reinterpret_cast<u32x4 *>(base + row * L::kKStride + 16 * seg) = reg[u];
-      } else if (pc < kPieces) {
-        const int pv = pc - 4 * D;
-        const int d = pv >> 2, q4 = pv & 3;
-        *reinterpret_cast<u32x4 *>(base + L::kKBytes + d * L::kVStride + 16 * q4) = reg[u];
-      }
+    } else {
+      stage_slow<D>(lds + stage * L::kStage, base, cl, total, M, p.ccap, ckb, cvb, bkb, bvb, tid, kThreads);
     }
   };
 
-  float m_run[2] = {kNegInf, kNegInf}, l_run[2] = {0.f, 0.f};
-  f32x4 o[2][DT];
+  float m_run[CT], l_run[CT];
+  f32x4 o[CT][DT];
 #pragma unroll
-  for (int c = 0; c < 2; ++c)
+  for (int ct = 0; ct < CT; ++ct) {
+    m_run[ct] = kNegInf;
+    l_run[ct] = 0.f;
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) o[c][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  u32x4 pre[kPer];
-  if (c0 < c1) {
-    fetch(c0, pre);
-    stash(0, pre);
+    for (int dt = 0; dt < DT; ++dt) o[ct][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
-  __syncthreads();
-  for (int c = c0; c < c1; ++c) {
-    const int buf = (c - c0) & 1;
-    if (c + 1 < c1) fetch(c + 1, pre);
-    const uint8_t *kt = lds + buf * L::kBuf;
-    const uint8_t *vt = kt + L::kKBytes;
-    const int base = c * kTile;
 
-    f32x4 s[2][2];
+  // One 32-token half h of the 64-token tile: S^T tiles tau = 2h, 2h+1,
+  // online softmax, then the PV k-step h.  The K operands of the half are
+  // read before its first MFMA.
+  auto compute_half = [&](const uint8_t *kt, int base, int h, bool masked) __attribute__((always_inline)) {
+    const uint8_t *vt = kt + L::kKBytes;
+    u32x4 ka[2][KS];
 #pragma unroll
-    for (int cc = 0; cc < 2; ++cc)
+    for (int t2 = 0; t2 < 2; ++t2) {
+      const int kr = 16 * (2 * h + t2) + col;   // token base + 8*(col>>2) + 4*t2 + (col&3)
 #pragma unroll
-      for (int tau = 0; tau < 2; ++tau) s[cc][tau] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int tau = 0; tau < 2; ++tau) {
-      const int kr = 8 * (col >> 2) + 4 * tau + (col & 3);
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const bf16x8 ka = as_bf16x8(*reinterpret_cast<const u32x4 *>(kt + kr * L::kKStride + (32 * ks + 8 * grp) * 2));
-#pragma unroll
-        for (int cc = 0; cc < 2; ++cc) s[cc][tau] = mfma16x16x32(ka, qb[cc][ks], s[cc][tau]);
-      }
+      for (int ks = 0; ks < KS; ++ks)
+        ka[t2][ks] = *reinterpret_cast<const u32x4 *>(kt + kr * L::kKRow + 16 * kswz<D>(kr, 4 * ks + grp));
     }
-    const bool need_mask = base + kTile > cl;
-    bf16x8 pb[2];
+    f32x4 s[CT][2];
 #pragma unroll
-    for (int cc = 0; cc < 2; ++cc) {
+    for (int ct = 0; ct < CT; ++ct) s[ct][0] = s[ct][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+      for (int t2 = 0; t2 < 2; ++t2)
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) s[ct][t2] = mfma16x16x32(as_bf16x8(ka[t2][ks]), qb[ct][ks], s[ct][t2]);
+    bf16x8 pb[CT];
+    bool moved = false;
+    float alpha[CT];
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) {
       float sc[8];
       float cmax = kNegInf;
 #pragma unroll
-      for (int tau = 0; tau < 2; ++tau)
+      for (int t2 = 0; t2 < 2; ++t2)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          float x = s[cc][tau][i] * p.qk_scale;
-          if (need_mask) {
-            const int j = base + 8 * grp + 4 * tau + i;
-            if (j >= cl + row_i[cc] + 1) x = kNegInf;
-          }
-          sc[4 * tau + i] = x;
+          float x = s[ct][t2][i] * p.qk_scale;
+          if (masked && base + 32 * h + 8 * grp + 4 * t2 + i >= row_lim[ct]) x = kNegInf;
+          sc[4 * t2 + i] = x;
           cmax = fmaxf(cmax, x);
         }
       cmax = fmaxf(cmax, __shfl_xor(cmax, 16, 64));
       cmax = fmaxf(cmax, __shfl_xor(cmax, 32, 64));
-      const float m_new = fmaxf(m_run[cc], cmax);
+      const float m_new = fmaxf(m_run[ct], cmax);
       const float m_use = (m_new == kNegInf) ? 0.f : m_new;
-      const float alpha = fast_exp2(m_run[cc] - m_use);
+      alpha[ct] = fast_exp2(m_run[ct] - m_use);
+      moved |= (m_new != m_run[ct]);
       float pr[8], psum = 0.f;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         pr[e] = fast_exp2(sc[e] - m_use);
         psum += pr[e];
       }
-      l_run[cc] = l_run[cc] * alpha + psum;
-      m_run[cc] = m_new;
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) o[cc][dt] *= alpha;
-      pb[cc] = as_bf16x8(u32x4{pack_bf16x2(pr[0], pr[1]), pack_bf16x2(pr[2], pr[3]),
+      l_run[ct] = l_run[ct] * alpha[ct] + psum;
+      m_run[ct] = m_new;
+      pb[ct] = as_bf16x8(u32x4{pack_bf16x2(pr[0], pr[1]), pack_bf16x2(pr[2], pr[3]),
                                pack_bf16x2(pr[4], pr[5]), pack_bf16x2(pr[6], pr[7])});
+    }
+    if (__any(moved)) {
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) o[ct][dt] *= alpha[ct];
     }
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
-      const bf16x8 va = as_bf16x8(*reinterpret_cast<const u32x4 *>(vt + (16 * dt + col) * L::kVStride + 16 * grp));
+      const int d = 16 * dt + col;
+      const bf16x8 va = as_bf16x8(*reinterpret_cast<const u32x4 *>(vt + d * L::kVRow + 16 * vswz(d, 4 * h + grp)));
 #pragma unroll
-      for (int cc = 0; cc < 2; ++cc) o[cc][dt] = mfma16x16x32(va, pb[cc], o[cc][dt]);
+      for (int ct = 0; ct < CT; ++ct) o[ct][dt] = mfma16x16x32(va, pb[ct], o[ct][dt]);
     }
-    if (c + 1 < c1) stash(buf ^ 1, pre);
-    __syncthreads();
+  };
+
+  // Ring of kStages stages: tiles c+1..c+3 in flight while tile c is
+  // computed.  Direct loads complete in issue order per wave, so "tile c
+  // landed" is vmcnt <= (direct loads issued after it); the barrier then
+  // publishes all waves' pieces and guarantees stage (c-1)%4 is no longer
+  // being read when tile c+3 is issued into it.
+  constexpr int kNI = (L::kBlocks + W - 1) / W;   // direct loads per lane per tile (upper bound)
+  static_assert(L::kBlocks % W == 0 || W == 6, "uneven block split only for 6 waves");
+  for (int it = c0 - (kStages - 1); it < c1; ++it) {
+    if (it >= c0) {
+      const int n1 = (it + 1 < c1 && full(it + 1)) ? 1 : 0;
+      const int n2 = (it + 2 < c1 && full(it + 2)) ? 1 : 0;
+      // loads issued by this wave for tiles it+1, it+2 (uniform per wave)
+      const int mine = (L::kBlocks - wave + W - 1) / W;
+      const int after = (n1 + n2) * mine;
+      if (after >= 2 * kNI) __asm__ volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * kNI) : "memory");
+      else if (after >= 2 * kNI - 2) __asm__ volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * kNI - 2) : "memory");
+      else if (after >= kNI) __asm__ volatile("s_waitcnt vmcnt(%0)" ::"n"(kNI) : "memory");
+      else if (after >= kNI - 1) __asm__ volatile("s_waitcnt vmcnt(%0)" ::"n"(kNI - 1) : "memory");
+      else __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+    }
+    issue(it + kStages - 1);
+    if (it >= c0) {
+      const uint8_t *kt = lds + (it & (kStages - 1)) * L::kStage;
+      const int base = it * kTile;
+      if (base + kTile <= cl) {
+        compute_half(kt, base, 0, false);
+        compute_half(kt, base, 1, false);
+      } else {
+        compute_half(kt, base, 0, true);
+        compute_half(kt, base, 1, true);
+      }
+    }
   }
 
   const int rows = p.B * M * p.Hq;
 #pragma unroll
-  for (int cc = 0; cc < 2; ++cc) {
-    float l = l_run[cc];
+  for (int ct = 0; ct < CT; ++ct) {
+    float l = l_run[ct];
     l += __shfl_xor(l, 16, 64);
     l += __shfl_xor(l, 32, 64);
-    const int r = r0 + 16 * cc + col;
+    const int r = r0 + 16 * ct + col;
     if (r >= p.R) continue;
     const int i = r / G, g = r % G;
     const int orow = (b * M + i) * p.Hq + kvh * G + g;
-    const float inv = (l > 0.f) ? 1.f / l : 0.f;
     if (p.splits == 1) {
       const float invo = 1.f / l;   // NaN for an empty key set
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
         const int d = 16 * dt + 4 * grp;
-        u32x2 w = u32x2{pack_bf16x2(o[cc][dt][0] * invo, o[cc][dt][1] * invo),
-                        pack_bf16x2(o[cc][dt][2] * invo, o[cc][dt][3] * invo)};
+        u32x2 w = u32x2{pack_bf16x2(o[ct][dt][0] * invo, o[ct][dt][1] * invo),
+                        pack_bf16x2(o[ct][dt][2] * invo, o[ct][dt][3] * invo)};
         *reinterpret_cast<u32x2 *>(p.out + (size_t)orow * D + d) = w;
       }
-      if (p.out_lse && grp == 0) p.out_lse[orow] = (l > 0.f) ? (m_run[cc] + fast_log2(l)) * kLn2 : kNegInf;
+      if (p.out_lse && grp == 0) p.out_lse[orow] = (l > 0.f) ? (m_run[ct] + fast_log2(l)) * kLn2 : kNegInf;
     } else {
+      const float inv = (l > 0.f) ? 1.f / l : 0.f;
       float *po = p.part_o + ((size_t)split * rows + orow) * D;
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
         const int d = 16 * dt + 4 * grp;
-        *reinterpret_cast<f32x4 *>(po + d) = o[cc][dt] * inv;
+        *reinterpret_cast<f32x4 *>(po + d) = o[ct][dt] * inv;
       }
-      if (grp == 0) p.part_lse[(size_t)split * rows + orow] = (l > 0.f) ? m_run[cc] + fast_log2(l) : kNegInf;
+      if (grp == 0) p.part_lse[(size_t)split * rows + orow] = (l > 0.f) ? m_run[ct] + fast_log2(l) : kNegInf;
     }
   }
 }
 
-int verify_waves(int R) { return R <= 64 ? 2 : (R <= 128 ? 4 : (R <= 192 ? 6 : 8)); }
+// Waves and 16-row column tiles per wave for R packed rows: up to 256 rows
+// per workgroup (8 waves x 2 tiles), two waves per SIMD.
+struct VerifyShape {
+  int W, CT;
+};
+VerifyShape verify_shape(int R) {
+  if (R <= 64) return {4, 1};
+  if (R <= 128) return {4, 2};
+  if (R <= 192) return {6, 2};
+  return {8, 2};
+}
 
 template <int D>
-void launch_verify_d(const VerifyParams &p, int W, int row_tiles, hipStream_t s) {
-  dim3 grid(p.splits, row_tiles, p.B * p.Hkv);
-  switch (W) {
-    case 2: verify_bf16<D, 2><<<grid, 128, 0, s>>>(p); break;
-    case 4: verify_bf16<D, 4><<<grid, 256, 0, s>>>(p); break;
-    case 6: verify_bf16<D, 6><<<grid, 384, 0, s>>>(p); break;
-    default: verify_bf16<D, 8><<<grid, 512, 0, s>>>(p); break;
-  }
+void launch_verify_d(const VerifyParams &p, VerifyShape sh, int row_groups, hipStream_t s) {
+  dim3 grid(p.splits, row_groups, p.B * p.Hkv);
+  if (sh.W == 4 && sh.CT == 1) verify_bf16<D, 4, 1><<<grid, 256, 0, s>>>(p);
+  else if (sh.W == 4) verify_bf16<D, 4, 2><<<grid, 256, 0, s>>>(p);
+  else if (sh.W == 6) verify_bf16<D, 6, 2><<<grid, 384, 0, s>>>(p);
+  else verify_bf16<D, 8, 2><<<grid, 512, 0, s>>>(p);
 }
 
 }  // namespace
 
+// One workgroup per CU (its LDS ring): pick the split count so that the grid
+// is about one full wave of workgroups over the 256 CUs, with every split at
+// least 8 tiles long.
 SplitPlan plan_verify(const vc_verify_args &a) {
   SplitPlan p{1, 0};
   if (a.dtype == VC_FP32) return p;
   const int R = a.M * (a.Hq / a.Hkv);
-  const int W = verify_waves(R);
-  const int64_t row_tiles = (R + 32 * W - 1) / (32 * W);
-  const int64_t wgs = (int64_t)a.B * a.Hkv * row_tiles;
+  const VerifyShape sh = verify_shape(R);
+  const int64_t row_groups = (R + 16 * sh.CT * sh.W - 1) / (16 * sh.CT * sh.W);
+  const int64_t wgs = (int64_t)a.B * a.Hkv * row_groups;
   const int64_t chunks = (a.ccap + a.M + kTile - 1) / kTile;
   int s = a.num_splits;
   if (s <= 0) {
-    s = 1;
-    while (wgs * s < 512 && chunks / (s * 2) >= 16) s *= 2;
+    s = (int)((256 + wgs - 1) / wgs);
+    const int64_t max_s = chunks / 8 > 0 ? chunks / 8 : 1;
+    if (s > max_s) s = (int)max_s;
   }
   if (s > chunks && chunks > 0) s = (int)chunks;
   if (s < 1) s = 1;
@@ -318,10 +407,10 @@ hipError_t launch_verify(const vc_verify_args &a, const SplitPlan &pl, hipStream
   const size_t rows = (size_t)a.B * a.M * a.Hq;
   p.part_o = (float *)a.workspace;
   p.part_lse = p.part_o ? p.part_o + (size_t)pl.splits * rows * a.D : nullptr;
-  const int W = verify_waves(p.R);
-  const int row_tiles = (p.R + 32 * W - 1) / (32 * W);
-  if (a.D == 128) launch_verify_d<128>(p, W, row_tiles, s);
-  else launch_verify_d<64>(p, W, row_tiles, s);
+  const VerifyShape sh = verify_shape(p.R);
+  const int row_groups = (p.R + 16 * sh.CT * sh.W - 1) / (16 * sh.CT * sh.W);
+  if (a.D == 128) launch_verify_d<128>(p, sh, row_groups, s);
+  else launch_verify_d<64>(p, sh, row_groups, s);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || pl.splits == 1) return e;
   return launch_combine(p.part_o, p.part_lse, pl.splits, (int)rows, a.D, a.dtype, a.out, a.out_lse, s);
