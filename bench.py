@@ -50,7 +50,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=2)
     ap.add_argument("--warmup", type=int, default=1)
     ap.add_argument("--workload", default="stagger128k",
-                    choices=["stagger128k", "verify32k", "draft128k"])
+                    choices=["stagger128k", "verify32k", "draft128k", "draft128k_int4"])
     ap.add_argument("--layers", type=int, default=64)
     ap.add_argument("--distinct-layers", type=int, default=16,
                     help="distinct compressed-cache buffers per cohort (layers rotate over them)")
@@ -318,6 +318,30 @@ def kernel_alone(args):
             vc.verify_attn(st["q"], st["k"], st["v"], cl, st["bk"], st["bv"], out=out, workspace=ws)
         flops = 4.0 * D * Hq * B * sum(N + i + 1 for i in range(M))
         nbytes = B * Hkv * (N + M) * D * 4 + 2 * B * M * Hq * D * 2
+    elif args.workload == "draft128k_int4":
+        # batch 32, int4 K/V over all 131072 tokens (4 of 16 bits = 25%)
+        B, Hq, Hkv, D, cap = 32, 32, 8, 128, 131072
+        import synthetic as S
+        kq = S.torch_randint((B, Hkv, cap, D // 2), 0, 256, 5, dev, torch.int32).to(torch.uint8)
+        vq = S.torch_randint((B, Hkv, D, cap // 2), 0, 256, 6, dev, torch.int32).to(torch.uint8)
+
+        def scales(shape, seed):
+            g = torch.Generator(device=dev)
+            g.manual_seed(seed)
+            sc = (torch.rand(shape, generator=g, device=dev) * 0.2 + 0.3).half()
+            return sc, (sc.float() * -7.5).half()
+        ks, kz = scales((B, Hkv, cap // 32, D), 7)
+        vs, vz = scales((B, Hkv, D // 32, cap), 8)
+        q = _bf16_randn((B, Hq, D), 3, dev)
+        ml = torch.full((B, Hkv), cap, dtype=torch.int32, device=dev)
+        out = torch.empty((B, Hq, D), dtype=torch.bfloat16, device=dev)
+        ws = torch.empty(1 << 26, dtype=torch.uint8, device=dev)
+
+        def call(i):
+            vc.draft_attn(q, kq, vq, ml, out=out, workspace=ws, fmt=vc.VC_KV_INT4,
+                          k_scale=ks, k_zero=kz, v_scale=vs, v_zero=vz)
+        flops = 4.0 * D * Hq * B * cap
+        nbytes = B * Hkv * cap * 160 + 2 * B * Hq * D * 2
     else:
         B, Hq, Hkv, D, cap = 32, 32, 8, 128, 32768
         nset = 1   # 4.3 GB per set >> MALL

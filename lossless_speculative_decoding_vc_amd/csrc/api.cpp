@@ -50,7 +50,7 @@ vc_status check_draft_shape(const vc_draft_args *a) {
   REQ(a->fmt == VC_KV_DENSE || a->fmt == VC_KV_INT4, "unknown kv format %d", a->fmt);
   if (a->fmt == VC_KV_INT4 && a->dtype != VC_BF16)
     return fail(VC_ENOTSUP, "int4 main segment is compiled for bf16 queries only");
-  if (a->fmt == VC_KV_INT4) return fail(VC_ENOTSUP, "int4 main segment not compiled in this build");
+  if (a->fmt == VC_KV_INT4 && a->D != 128) return fail(VC_ENOTSUP, "int4 main segment is compiled for head_dim 128");
   REQ(a->cap >= 0 && a->cap % 64 == 0, "cap (%lld) must be a non-negative multiple of 64", (long long)a->cap);
   REQ(a->tcap >= 0, "tcap must be non-negative");
   return VC_OK;
@@ -63,6 +63,12 @@ vc_status check_draft(const vc_draft_args *a) {
   REQ(a->cap == 0 || (a->k && a->v), "k and v are required when cap > 0");
   REQ(aligned16(a->q) && aligned16(a->out) && aligned16(a->k) && aligned16(a->v),
       "q, k, v and out must be 16-byte aligned");
+  if (a->fmt == VC_KV_INT4) {
+    REQ(a->cap == 0 || (a->k_scale && a->k_zero && a->v_scale && a->v_zero),
+        "int4 main segment needs k_scale, k_zero, v_scale and v_zero");
+    REQ(aligned16(a->k_scale) && aligned16(a->k_zero) && aligned16(a->v_scale) && aligned16(a->v_zero),
+        "int4 scales and zeros must be 16-byte aligned");
+  }
   if (a->tail_len) {
     REQ(a->tcap > 0 && a->tail_k && a->tail_v, "tail_len given without tail_k/tail_v/tcap");
     REQ(aligned16(a->tail_k) && aligned16(a->tail_v), "tail_k and tail_v must be 16-byte aligned");

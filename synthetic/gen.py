@@ -115,33 +115,32 @@ def int4_grid(B, Hkv, cap, D, cfg_seed, smin=0.3, smax=0.5):
     """Codes uniform on 0..15 and binary16 scales ``s ~ U[smin, smax]``,
     zeros ``z = -7.5 s`` (so reconstructions span about +-3.75).
 
-    Returns dict of uint8 ``k_codes/v_codes [B][Hkv][cap][D/2]`` and uint16
-    (binary16 bits) ``k_scale/k_zero [B][Hkv][cap/32][D]``,
-    ``v_scale/v_zero [B][Hkv][cap][D/32]``, plus the unpacked int codes
-    ``k_c/v_c`` for the oracle side.
+    Library layouts (uint8 codes, uint16 binary16 bits):
+      ``k_codes [B][Hkv][cap][D/2]`` (two channels per byte, even channel low),
+      ``k_scale/k_zero [B][Hkv][cap/32][D]``,
+      ``v_codes [B][Hkv][D][cap/2]`` (channel-major, two tokens per byte,
+      even token low), ``v_scale/v_zero [B][Hkv][D/32][cap]``.
+    Also the unpacked codes ``k_c/v_c [B][Hkv][cap][D]`` (token-major) for
+    the oracle side.
     """
     assert cap % 32 == 0 and D % 32 == 0
-    shp = dict(k_c=(B, Hkv, cap, D), v_c=(B, Hkv, cap, D),
-               k_scale=(B, Hkv, cap // 32, D), v_scale=(B, Hkv, cap, D // 32))
-    res = {"k_c": np.empty(shp["k_c"], np.uint8), "v_c": np.empty(shp["v_c"], np.uint8),
-           "k_scale": np.empty(shp["k_scale"], np.uint16), "k_zero": np.empty(shp["k_scale"], np.uint16),
-           "v_scale": np.empty(shp["v_scale"], np.uint16), "v_zero": np.empty(shp["v_scale"], np.uint16)}
+    res = {"k_c": np.empty((B, Hkv, cap, D), np.uint8), "v_c": np.empty((B, Hkv, cap, D), np.uint8),
+           "k_scale": np.empty((B, Hkv, cap // 32, D), np.uint16),
+           "k_zero": np.empty((B, Hkv, cap // 32, D), np.uint16),
+           "v_scale": np.empty((B, Hkv, D // 32, cap), np.uint16),
+           "v_zero": np.empty((B, Hkv, D // 32, cap), np.uint16)}
     for b in range(B):
         for h in range(Hkv):
-            gk = rng(cfg_seed, TID["kcode"], b, h)
-            gv = rng(cfg_seed, TID["vcode"], b, h)
-            res["k_c"][b, h] = gk.integers(0, 16, (cap, D))
-            res["v_c"][b, h] = gv.integers(0, 16, (cap, D))
-            gs = rng(cfg_seed, TID["kscale"], b, h)
-            ks = gs.uniform(smin, smax, (cap // 32, D)).astype(np.float16)
+            res["k_c"][b, h] = rng(cfg_seed, TID["kcode"], b, h).integers(0, 16, (cap, D))
+            res["v_c"][b, h] = rng(cfg_seed, TID["vcode"], b, h).integers(0, 16, (cap, D))
+            ks = rng(cfg_seed, TID["kscale"], b, h).uniform(smin, smax, (cap // 32, D)).astype(np.float16)
             res["k_scale"][b, h] = ks.view(np.uint16)
             res["k_zero"][b, h] = (ks.astype(np.float32) * np.float32(-7.5)).astype(np.float16).view(np.uint16)
-            gs = rng(cfg_seed, TID["vscale"], b, h)
-            vs = gs.uniform(smin, smax, (cap, D // 32)).astype(np.float16)
+            vs = rng(cfg_seed, TID["vscale"], b, h).uniform(smin, smax, (D // 32, cap)).astype(np.float16)
             res["v_scale"][b, h] = vs.view(np.uint16)
             res["v_zero"][b, h] = (vs.astype(np.float32) * np.float32(-7.5)).astype(np.float16).view(np.uint16)
     res["k_codes"] = pack_codes(res["k_c"])
-    res["v_codes"] = pack_codes(res["v_c"])
+    res["v_codes"] = pack_codes(np.ascontiguousarray(np.swapaxes(res["v_c"], -1, -2)))
     return res
 
 

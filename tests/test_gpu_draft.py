@@ -96,3 +96,65 @@ def test_fp32_mode(G):
 
 def test_fp32_no_tail_no_degree():
     _check(1, 4, 2, 64, 256, [[243, 200]], 0, None, dtype="fp32", seed=22)
+
+
+# ---------------------------------------------------------------------------
+# int4 main segment (the quantizing drafter): the oracle reconstructs
+# x = c * s + z in fp64 and runs dense attention over the reconstruction.
+def _int4_check(B, Hq, Hkv, cap, main_len, tcap, tail_len, deg_mode, seed, splits=0, qstd=1.0):
+    import torch
+    import lossless_speculative_decoding_vc_amd as vc
+    from oracle import quant as Q
+    from oracle.formats import f16_to_f64
+    D = 128
+    g = S.int4_grid(B, Hkv, cap, D, seed)
+    qf = S.normal_f32((B, Hq, D), seed, S.TID["q"], std=qstd, slice_dims=1)
+    qbits = S.f32_to_bf16_bits(qf)
+    tkf = S.normal_f32((B, Hkv, tcap, D), seed, S.TID["tail_k"]) if tcap else None
+    tvf = S.normal_f32((B, Hkv, tcap, D), seed, S.TID["tail_v"]) if tcap else None
+    deg = None
+    if deg_mode == "shared":
+        deg = S.degrees((B, 1, cap), seed)
+    k_ref = np.empty((B, Hkv, cap, D))
+    v_ref = np.empty((B, Hkv, cap, D))
+    for b in range(B):
+        for h in range(Hkv):
+            k_ref[b, h] = Q.dequantize_k(g["k_c"][b, h], f16_to_f64(g["k_scale"][b, h]), f16_to_f64(g["k_zero"][b, h]))
+            v_ref[b, h] = Q.dequantize_v(g["v_c"][b, h], f16_to_f64(g["v_scale"][b, h]).T,
+                                         f16_to_f64(g["v_zero"][b, h]).T)
+    tk_ref = tv_ref = tk_dev = tv_dev = None
+    if tcap:
+        tkb, tvb = S.f32_to_bf16_bits(tkf), S.f32_to_bf16_bits(tvf)
+        tk_ref, tv_ref = bf16_to_f64(tkb), bf16_to_f64(tvb)
+        tk_dev = to_dev_bf16(tkb)
+        tv_dev = to_dev_bf16(np.ascontiguousarray(np.swapaxes(tvb, -1, -2)))
+    ml = np.asarray(main_len, np.int32).reshape(B, Hkv)
+    tl = None if tcap == 0 else np.asarray(tail_len, np.int32)
+    lse = torch.empty((B, Hq), dtype=torch.float32, device="cuda")
+    as_dev16 = lambda a: to_dev(np.ascontiguousarray(a).view(np.int16))
+    out = vc.draft_attn(to_dev_bf16(qbits), to_dev(g["k_codes"]), to_dev(g["v_codes"]), to_dev(ml),
+                        degree=None if deg is None else to_dev(deg), tail_k=tk_dev, tail_v=tv_dev,
+                        tail_len=None if tl is None else to_dev(tl), out_lse=lse, num_splits=splits,
+                        fmt=vc.VC_KV_INT4, k_scale=as_dev16(g["k_scale"]), k_zero=as_dev16(g["k_zero"]),
+                        v_scale=as_dev16(g["v_scale"]), v_zero=as_dev16(g["v_zero"]))
+    torch.cuda.synchronize()
+    got = bf16_dev_to_f64(out)
+    o_ref, lse_ref = A.draft_attn(bf16_to_f64(qbits), k_ref, v_ref, ml, deg, tk_ref, tv_ref, tl)
+    assert_close(got, o_ref, TOL["bf16"], "out")
+    assert_close(lse.cpu().numpy(), lse_ref, TOL["bf16"] * 0.1, "lse")
+    return got, o_ref
+
+
+@pytest.mark.parametrize("splits", [0, 1, 5])
+def test_int4_main_segment(splits):
+    _int4_check(2, 8, 2, 1024, [[1024, 1000], [64, 333]], 12, [12, 3], "shared", seed=31, splits=splits)
+
+
+def test_int4_peaked_no_tail():
+    got, ref = _int4_check(2, 16, 4, 512, [[512, 480, 96, 1], [200, 511, 32, 256]], 0, None, None,
+                           seed=32, qstd=1.0)
+    assert rel_l2(got, ref) <= 2e-2
+
+
+def test_int4_tail_only():
+    _int4_check(1, 4, 1, 256, [[0]], 20, [20], "shared", seed=33)
