@@ -26,7 +26,8 @@ VC_KV_DENSE, VC_KV_INT4 = 0, 1
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 library_path = os.path.join(_HERE, "libvc.so")
-_HEADERS = [os.path.join(os.path.dirname(_HERE), "include", f) for f in ("vc.h",)]
+_INCLUDE = os.path.join(os.path.dirname(_HERE), "include")
+_HEADERS = sorted(os.path.join(_INCLUDE, f) for f in os.listdir(_INCLUDE) if f.endswith(".h"))
 
 
 class VcError(RuntimeError):

@@ -30,7 +30,7 @@ def test_exports_every_declared_symbol(L):
 
 
 def _c_layout(struct, fields):
-    src = "#include <stdio.h>\n#include <stddef.h>\n#include \"vc.h\"\nint main(void){\n"
+    src = "#include <stdio.h>\n#include <stddef.h>\n#include \"vc_tiny.h\"\nint main(void){\n"
     src += f'printf("%zu\\n", sizeof({struct}));\n'
     for f in fields:
         src += f'printf("%zu\\n", offsetof({struct}, {f}));\n'
@@ -47,8 +47,13 @@ def _c_layout(struct, fields):
 
 @pytest.mark.parametrize("cls,cname", [(vcb.DraftArgs, "vc_draft_args"),
                                        (vcb.VerifyArgs, "vc_verify_args"),
-                                       (vcb.AcceptArgs, "vc_accept_args")])
+                                       (vcb.AcceptArgs, "vc_accept_args"),
+                                       ("TinyModelArgs", "vc_tiny_model"),
+                                       ("TinyAttnArgs", "vc_tiny_attn")])
 def test_struct_layout_matches_header(cls, cname):
+    if isinstance(cls, str):
+        import lossless_speculative_decoding_vc_amd.tiny_loop as tl
+        cls = getattr(tl, cls)
     fields = [f[0] for f in cls._fields_]
     got = [ctypes.sizeof(cls)] + [getattr(cls, f).offset for f in fields]
     assert got == _c_layout(cname, fields)

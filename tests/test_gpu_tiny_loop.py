@@ -1,0 +1,51 @@
+"""End-to-end GPU draft-then-verify loop on the tiny fp32 decoder, compared
+with the oracle run step by step: identical output tokens (== full-KV greedy
+decoding), identical drafts and accept lengths in every round, and the
+identity compressor accepting every draft plus the bonus token."""
+import numpy as np
+import pytest
+
+from oracle import tiny
+
+pytestmark = pytest.mark.gpu
+
+
+def _gpu_loop(arrays, prompt, n_new, k, compressor, recent=128):
+    from lossless_speculative_decoding_vc_amd.tiny_loop import TinyDecoder, TinyVeriCache
+    model = TinyDecoder(arrays, max_pos=len(prompt) + n_new + k + 64)
+    loop = TinyVeriCache(model, max_tokens=len(prompt) + n_new + k, k=k, compressor=compressor, recent=recent)
+    return loop.generate(prompt, n_new)
+
+
+def test_short_prompt_matches_oracle(tiny_setup):
+    spec, arrays, W, prompt = tiny_setup
+    p = prompt[:200]
+    rule = lambda T: tiny.kept_positions(T, 4, 32, 8)
+    ref, ref_rounds = tiny.vericache_decode(W, p, 24, 4, rule)
+    toks, rounds = _gpu_loop(arrays, p, 24, 4, "evict", recent=32)
+    assert toks == ref
+    assert [r[2] for r in rounds] == [r.n for r in ref_rounds]
+    assert [r[0] for r in rounds] == [r.drafts for r in ref_rounds]
+
+
+def test_measured_tiny_config_matches_oracle_and_greedy(tiny_setup):
+    # prompt 1024, 64 new tokens, k = 8, sinks 4 + last 128 + every 8th older token
+    spec, arrays, W, prompt = tiny_setup
+    ref, ref_rounds = tiny.vericache_decode(W, prompt, 64, 8)
+    greedy = tiny.greedy_decode(W, prompt, 64)
+    toks, rounds = _gpu_loop(arrays, prompt, 64, 8, "evict")
+    margin = min(min(r.draft_margin, r.verify_margin) for r in ref_rounds)
+    print(f"min top-2 logit margin in the oracle run: {margin:.3e}; rounds {len(rounds)}; "
+          f"accept lengths {[r[2] for r in rounds]}")
+    assert toks == ref == greedy
+    assert [r[2] for r in rounds] == [r.n for r in ref_rounds]
+    assert [r[0] for r in rounds] == [r.drafts for r in ref_rounds]
+    assert [r[1] for r in rounds] == [r.predictions for r in ref_rounds]
+
+
+def test_identity_compressor_full_acceptance(tiny_setup):
+    spec, arrays, W, prompt = tiny_setup
+    p = prompt[:300]
+    toks, rounds = _gpu_loop(arrays, p, 30, 6, "identity")
+    assert toks == tiny.greedy_decode(W, p, 30)
+    assert all(r[2] == 6 and len(r[3]) == 7 for r in rounds)    # every draft + the bonus
