@@ -57,6 +57,7 @@ def parse():
     ap.add_argument("--no-bulk", action="store_true", help="skip the bulk-synchronous comparison round")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--iters", type=int, default=50, help="kernel-alone iterations")
+    ap.add_argument("--splits", type=int, default=0, help="kernel-alone split count (0 = library default)")
     return ap.parse_args()
 
 
@@ -332,7 +333,8 @@ def kernel_alone(args):
 
         def call(i):
             st = sets[i % nset]
-            vc.verify_attn(st["q"], st["k"], st["v"], cl, st["bk"], st["bv"], out=out, workspace=ws)
+            vc.verify_attn(st["q"], st["k"], st["v"], cl, st["bk"], st["bv"], out=out, workspace=ws,
+                           num_splits=args.splits)
         flops = 4.0 * D * Hq * B * sum(N + i + 1 for i in range(M))
         nbytes = B * Hkv * (N + M) * D * 4 + 2 * B * M * Hq * D * 2
     elif args.workload == "copy1g":
@@ -357,7 +359,7 @@ def kernel_alone(args):
         ws = torch.empty(1 << 26, dtype=torch.uint8, device=dev)
 
         def call(i):
-            vc.draft_attn(q, kq, vq, ml, out=out, workspace=ws, fmt=vc.VC_KV_INT4,
+            vc.draft_attn(q, kq, vq, ml, out=out, workspace=ws, fmt=vc.VC_KV_INT4, num_splits=args.splits,
                           k_scale=ks, k_zero=kz, v_scale=vs, v_zero=vz)
         flops = 4.0 * D * Hq * B * cap
         nbytes = B * Hkv * cap * 160 + 2 * B * Hq * D * 2
@@ -374,7 +376,7 @@ def kernel_alone(args):
         ws = torch.empty(1 << 26, dtype=torch.uint8, device=dev)
 
         def call(i):
-            vc.draft_attn(q, K, Vt, ml, degree=deg, out=out, workspace=ws)
+            vc.draft_attn(q, K, Vt, ml, degree=deg, out=out, workspace=ws, num_splits=args.splits)
         flops = 4.0 * D * Hq * B * cap
         nbytes = B * Hkv * cap * D * 4 + B * cap * 4 + 2 * B * Hq * D * 2
     if args.workload == "copy1g":
@@ -467,7 +469,7 @@ def main():
                             "frac": r["gbs"] / HBM_PEAK_GBS, "traffic": None},
                "mfma": {"achieved": r["tflops"], "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                         "frac": r["tflops"] / MFMA_BF16_PEAK_TFLOPS},
-               "config": {"workload": args.workload}}
+               "config": {"workload": args.workload, "splits": args.splits}}
         print(json.dumps(out))
         return
 

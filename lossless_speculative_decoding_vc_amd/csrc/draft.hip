@@ -33,6 +33,7 @@ namespace {
 
 constexpr int kDraftWaves = 4;
 constexpr int kChunk = 32;   // tokens per wave step
+constexpr float kSlack = 8.f;  // lazy-rescale threshold (base 2)
 
 struct DraftParams {
   int B, Hq, Hkv, G, splits;
@@ -189,16 +190,25 @@ __global__ __launch_bounds__(kDraftWaves * 64) void draft_bf16_dense(DraftParams
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int e = 4 * tau + i;
-        float x = s[tau][i] * p.qk_scale + ch.lg[e];
+        float x = fmaf(s[tau][i], p.qk_scale, ch.lg[e]);
         x = (base + 8 * grp + e < total) ? x : kNegInf;
         sc[e] = x;
         cmax = fmaxf(cmax, x);
       }
-    cmax = fmaxf(cmax, __shfl_xor(cmax, 16, 64));
-    cmax = fmaxf(cmax, __shfl_xor(cmax, 32, 64));
-    const float m_new = fmaxf(m_run, cmax);
-    const float m_use = (m_new == kNegInf) ? 0.f : m_new;
-    const float alpha = fast_exp2(m_run - m_use);
+    // Lazy reference max: the lane groups exchange maxima (two cross-lane
+    // shuffles) and rescale only when some score in the wave exceeds the
+    // reference by more than kSlack; probabilities stay <= 2^kSlack.
+    if (__any(cmax - m_run > kSlack)) {   // false when both are -inf
+      cmax = fmaxf(cmax, __shfl_xor(cmax, 16, 64));
+      cmax = fmaxf(cmax, __shfl_xor(cmax, 32, 64));
+      const float m_new = fmaxf(m_run, cmax);
+      const float alpha = (m_new == kNegInf) ? 1.f : fast_exp2(m_run - m_new);
+      l_run *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) o[dt] *= alpha;
+      m_run = m_new;
+    }
+    const float m_use = (m_run == kNegInf) ? 0.f : m_run;
     float pr[8];
     float psum = 0.f;
 #pragma unroll
@@ -206,12 +216,7 @@ __global__ __launch_bounds__(kDraftWaves * 64) void draft_bf16_dense(DraftParams
       pr[e] = fast_exp2(sc[e] - m_use);
       psum += pr[e];
     }
-    l_run = l_run * alpha + psum;
-    if (__any(m_new != m_run)) {
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) o[dt] *= alpha;
-    }
-    m_run = m_new;
+    l_run += psum;
     const bf16x8 pb = as_bf16x8(u32x4{pack_bf16x2(pr[0], pr[1]), pack_bf16x2(pr[2], pr[3]),
                                       pack_bf16x2(pr[4], pr[5]), pack_bf16x2(pr[6], pr[7])});
 #pragma unroll
@@ -514,16 +519,25 @@ __global__ __launch_bounds__(kDraftWaves * 64) void draft_bf16_int4(DraftParams 
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int e = 4 * tau + i;
-        float x = s[tau][i] * p.qk_scale + lg[e];
+        float x = fmaf(s[tau][i], p.qk_scale, lg[e]);
         x = (base + 8 * grp + e < total) ? x : kNegInf;
         sc[e] = x;
         cmax = fmaxf(cmax, x);
       }
-    cmax = fmaxf(cmax, __shfl_xor(cmax, 16, 64));
-    cmax = fmaxf(cmax, __shfl_xor(cmax, 32, 64));
-    const float m_new = fmaxf(m_run, cmax);
-    const float m_use = (m_new == kNegInf) ? 0.f : m_new;
-    const float alpha = fast_exp2(m_run - m_use);
+    // Lazy reference max: the lane groups exchange maxima (two cross-lane
+    // shuffles) and rescale only when some score in the wave exceeds the
+    // reference by more than kSlack; probabilities stay <= 2^kSlack.
+    if (__any(cmax - m_run > kSlack)) {   // false when both are -inf
+      cmax = fmaxf(cmax, __shfl_xor(cmax, 16, 64));
+      cmax = fmaxf(cmax, __shfl_xor(cmax, 32, 64));
+      const float m_new = fmaxf(m_run, cmax);
+      const float alpha = (m_new == kNegInf) ? 1.f : fast_exp2(m_run - m_new);
+      l_run *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) o[dt] *= alpha;
+      m_run = m_new;
+    }
+    const float m_use = (m_run == kNegInf) ? 0.f : m_run;
     float pr[8];
     float psum = 0.f;
 #pragma unroll
@@ -531,12 +545,7 @@ __global__ __launch_bounds__(kDraftWaves * 64) void draft_bf16_int4(DraftParams 
       pr[e] = fast_exp2(sc[e] - m_use);
       psum += pr[e];
     }
-    l_run = l_run * alpha + psum;
-    if (__any(m_new != m_run)) {
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) o[dt] *= alpha;
-    }
-    m_run = m_new;
+    l_run += psum;
     const bf16x8 pb = as_bf16x8(u32x4{pack_bf16x2(pr[0], pr[1]), pack_bf16x2(pr[2], pr[3]),
                                       pack_bf16x2(pr[4], pr[5]), pack_bf16x2(pr[6], pr[7])});
 #pragma unroll

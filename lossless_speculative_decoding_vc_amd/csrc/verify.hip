@@ -37,6 +37,7 @@ namespace {
 
 constexpr int kTile = 64;      // tokens per LDS tile
 constexpr int kStages = 4;     // LDS ring depth
+constexpr float kSlack = 8.f;  // lazy-rescale threshold (base 2)
 
 struct VerifyParams {
   int B, Hq, Hkv, G, M, R, splits;
@@ -228,44 +229,57 @@ __global__ __launch_bounds__(W * 64) void verify_bf16(VerifyParams p) {
       for (int t2 = 0; t2 < 2; ++t2)
 #pragma unroll
         for (int ct = 0; ct < CT; ++ct) s[ct][t2] = mfma16x16x32(as_bf16x8(ka[t2][ks]), qb[ct][ks], s[ct][t2]);
-    bf16x8 pb[CT];
-    bool moved = false;
-    float alpha[CT];
+    // Lazy reference max per packed row: each lane first compares its own 8
+    // scores with the row's reference; only when some score in the wave
+    // exceeds it by more than kSlack (base 2) do the lane groups exchange
+    // their maxima (two cross-lane shuffles) and rescale -- after the first
+    // tiles that branch is rarely taken, and probabilities stay <= 2^kSlack.
+    const float qs = p.qk_scale;
+    float sc[CT][8];
+    bool need = false;
 #pragma unroll
     for (int ct = 0; ct < CT; ++ct) {
-      float sc[8];
-      float cmax = kNegInf;
+      float lmax = kNegInf;
 #pragma unroll
       for (int t2 = 0; t2 < 2; ++t2)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          float x = s[ct][t2][i] * p.qk_scale;
+          float x = s[ct][t2][i];
           if (masked && base + 32 * h + 8 * grp + 4 * t2 + i >= row_lim[ct]) x = kNegInf;
-          sc[4 * t2 + i] = x;
-          cmax = fmaxf(cmax, x);
+          sc[ct][4 * t2 + i] = x;
+          lmax = fmaxf(lmax, x);
         }
-      cmax = fmaxf(cmax, __shfl_xor(cmax, 16, 64));
-      cmax = fmaxf(cmax, __shfl_xor(cmax, 32, 64));
-      const float m_new = fmaxf(m_run[ct], cmax);
-      const float m_use = (m_new == kNegInf) ? 0.f : m_new;
-      alpha[ct] = fast_exp2(m_run[ct] - m_use);
-      moved |= (m_new != m_run[ct]);
+      need |= (lmax - m_run[ct]) * qs > kSlack;   // false when both are -inf
+    }
+    if (__any(need)) {
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct) {
+        float cmax = kNegInf;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) cmax = fmaxf(cmax, sc[ct][e]);
+        cmax = fmaxf(cmax, __shfl_xor(cmax, 16, 64));
+        cmax = fmaxf(cmax, __shfl_xor(cmax, 32, 64));
+        const float m_new = fmaxf(m_run[ct], cmax);
+        const float alpha = (m_new == kNegInf) ? 1.f : fast_exp2((m_run[ct] - m_new) * qs);
+        l_run[ct] *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) o[ct][dt] *= alpha;
+        m_run[ct] = m_new;
+      }
+    }
+    bf16x8 pb[CT];
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) {
+      const float mc = (m_run[ct] == kNegInf) ? 0.f : m_run[ct] * qs;
       float pr[8], psum = 0.f;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        pr[e] = fast_exp2(sc[e] - m_use);
+        pr[e] = fast_exp2(fmaf(sc[ct][e], qs, -mc));
         psum += pr[e];
       }
-      l_run[ct] = l_run[ct] * alpha[ct] + psum;
-      m_run[ct] = m_new;
+      l_run[ct] += psum;
       pb[ct] = as_bf16x8(u32x4{pack_bf16x2(pr[0], pr[1]), pack_bf16x2(pr[2], pr[3]),
                                pack_bf16x2(pr[4], pr[5]), pack_bf16x2(pr[6], pr[7])});
-    }
-    if (__any(moved)) {
-#pragma unroll
-      for (int ct = 0; ct < CT; ++ct)
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) o[ct][dt] *= alpha[ct];
     }
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
@@ -330,7 +344,7 @@ __global__ __launch_bounds__(W * 64) void verify_bf16(VerifyParams p) {
                         pack_bf16x2(o[ct][dt][2] * invo, o[ct][dt][3] * invo)};
         *reinterpret_cast<u32x2 *>(p.out + (size_t)orow * D + d) = w;
       }
-      if (p.out_lse && grp == 0) p.out_lse[orow] = (l > 0.f) ? (m_run[ct] + fast_log2(l)) * kLn2 : kNegInf;
+      if (p.out_lse && grp == 0) p.out_lse[orow] = (l > 0.f) ? (m_run[ct] * p.qk_scale + fast_log2(l)) * kLn2 : kNegInf;
     } else {
       const float inv = (l > 0.f) ? 1.f / l : 0.f;
       float *po = p.part_o + ((size_t)split * rows + orow) * D;
@@ -339,7 +353,7 @@ __global__ __launch_bounds__(W * 64) void verify_bf16(VerifyParams p) {
         const int d = 16 * dt + 4 * grp;
         *reinterpret_cast<f32x4 *>(po + d) = o[ct][dt] * inv;
       }
-      if (grp == 0) p.part_lse[(size_t)split * rows + orow] = (l > 0.f) ? m_run[ct] + fast_log2(l) : kNegInf;
+      if (grp == 0) p.part_lse[(size_t)split * rows + orow] = (l > 0.f) ? m_run[ct] * p.qk_scale + fast_log2(l) : kNegInf;
     }
   }
 }
