@@ -89,7 +89,7 @@ VC_DEVICE void load_lds16(const void *gptr, uint32_t lds_addr) {
 // Tile that reaches the block keys or the end of the key sequence: staged
 // through registers with the same swizzled layout (zero past the end).
 template <int D>
-__device__ __noinline__ void stage_slow(uint8_t *st, int base, int cl, int total, int M, int64_t ccap,
+VC_DEVICE void stage_slow(uint8_t *st, int base, int cl, int total, int M, int64_t ccap,
                                         const uint16_t *ckb, const uint16_t *cvb, const uint16_t *bkb,
                                         const uint16_t *bvb, int tid, int nthreads) {
   using L = Lds<D>;
@@ -166,34 +166,39 @@ __global__ __launch_bounds__(W * 64) void verify_bf16(VerifyParams p) {
     }
   }
 
+  // The direct loads below are invisible to the compiler's wait-count
+  // tracking: if a Q load were still outstanding inside the main loop, the
+  // compiler's wait for it would count the tile prefetches too and drain the
+  // ring.  Consuming Q in an empty asm makes it wait here, once.
+#pragma unroll
+  for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) __asm__ volatile("" ::"v"(qb[ct][ks]));
+
   const uint16_t *ckb = p.ck + (size_t)bh * p.ccap * D;
   const uint16_t *cvb = p.cv + (size_t)bh * D * p.ccap;
   const uint16_t *bkb = p.bk + (size_t)bh * M * D;
   const uint16_t *bvb = p.bv + (size_t)bh * D * M;
   const uint32_t lds_base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t *)lds;
 
-  // A tile is "full" when all 64 tokens are context tokens: then each wave
-  // fetches whole 1 KB blocks straight into LDS (block q: 4 K rows or 8 V
-  // channel rows, lanes ordered by physical slot).
-  auto full = [&](int c) __attribute__((always_inline)) { return c * kTile + kTile <= cl; };
+  // Tiles [c0, cf) hold only context tokens ("full"): each wave fetches whole
+  // 1 KB blocks of them straight into LDS (block q: 4 K rows or 8 V channel
+  // rows, lanes ordered by physical slot).  Tiles [cf, c1) reach the block
+  // keys or the end of the key sequence; they are staged after the main loop.
+  const int cf = max(c0, min(c1, cl / kTile));
   auto issue = [&](int c) __attribute__((always_inline)) {
-    if (c >= c1) return;
     const int stage = c & (kStages - 1);
     const int base = c * kTile;
-    if (full(c)) {
-      for (int q = wave; q < L::kBlocks; q += W) {
-        const uint16_t *src;
-        if (q < L::kKBlocks) {
-          const int r = q * L::kRowsPerBlock + lane / L::kSlots;
-          src = ckb + (size_t)(base + ktok(r)) * D + 8 * kswz<D>(r, lane % L::kSlots);
-        } else {
-          const int d = (q - L::kKBlocks) * 8 + lane / 8;
-          src = cvb + (size_t)d * p.ccap + base + 8 * vswz(d, lane % 8);
-        }
-        load_lds16(src, lds_base + (uint32_t)(stage * L::kStage + q * 1024));
+    for (int q = wave; q < L::kBlocks; q += W) {
+      const uint16_t *src;
+      if (q < L::kKBlocks) {
+        const int r = q * L::kRowsPerBlock + lane / L::kSlots;
+        src = ckb + (size_t)(base + ktok(r)) * D + 8 * kswz<D>(r, lane % L::kSlots);
+      } else {
+        const int d = (q - L::kKBlocks) * 8 + lane / 8;
+        src = cvb + (size_t)d * p.ccap + base + 8 * vswz(d, lane % 8);
       }
-    } else {
-      stage_slow<D>(lds + stage * L::kStage, base, cl, total, M, p.ccap, ckb, cvb, bkb, bvb, tid, kThreads);
+      load_lds16(src, lds_base + (uint32_t)(stage * L::kStage + q * 1024));
     }
   };
 
@@ -294,35 +299,29 @@ __global__ __launch_bounds__(W * 64) void verify_bf16(VerifyParams p) {
   // computed.  Direct loads complete in issue order per wave, so "tile c
   // landed" is vmcnt <= (direct loads issued after it); the barrier then
   // publishes all waves' pieces and guarantees stage (c-1)%4 is no longer
-  // being read when tile c+3 is issued into it.
-  constexpr int kNI = (L::kBlocks + W - 1) / W;   // direct loads per lane per tile (upper bound)
-  static_assert(L::kBlocks % W == 0 || W == 6, "uneven block split only for 6 waves");
-  for (int it = c0 - (kStages - 1); it < c1; ++it) {
-    if (it >= c0) {
-      const int n1 = (it + 1 < c1 && full(it + 1)) ? 1 : 0;
-      const int n2 = (it + 2 < c1 && full(it + 2)) ? 1 : 0;
-      // loads issued by this wave for tiles it+1, it+2 (uniform per wave)
-      const int mine = (L::kBlocks - wave + W - 1) / W;
-      const int after = (n1 + n2) * mine;
-      if (after >= 2 * kNI) __asm__ volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * kNI) : "memory");
-      else if (after >= 2 * kNI - 2) __asm__ volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * kNI - 2) : "memory");
-      else if (after >= kNI) __asm__ volatile("s_waitcnt vmcnt(%0)" ::"n"(kNI) : "memory");
-      else if (after >= kNI - 1) __asm__ volatile("s_waitcnt vmcnt(%0)" ::"n"(kNI - 1) : "memory");
-      else __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      __syncthreads();
-    }
-    issue(it + kStages - 1);
-    if (it >= c0) {
-      const uint8_t *kt = lds + (it & (kStages - 1)) * L::kStage;
-      const int base = it * kTile;
-      if (base + kTile <= cl) {
-        compute_half(kt, base, 0, false);
-        compute_half(kt, base, 1, false);
-      } else {
-        compute_half(kt, base, 0, true);
-        compute_half(kt, base, 1, true);
-      }
-    }
+  // being read when tile c+3 is issued into it.  The loop body holds no
+  // call and no other memory load, so nothing else moves vmcnt.
+  constexpr int kMine = L::kBlocks / W;   // fewest direct loads per wave per tile
+  for (int c = c0; c < min(c0 + kStages - 1, cf); ++c) issue(c);
+  for (int it = c0; it < cf; ++it) {
+    const int ahead = min(cf - 1 - it, kStages - 2);   // tiles issued after this one (0..2)
+    if (ahead >= 2) __asm__ volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * kMine) : "memory");
+    else if (ahead == 1) __asm__ volatile("s_waitcnt vmcnt(%0)" ::"n"(kMine) : "memory");
+    else __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (it + kStages - 1 < cf) issue(it + kStages - 1);
+    const uint8_t *kt = lds + (it & (kStages - 1)) * L::kStage;
+    compute_half(kt, it * kTile, 0, false);
+    compute_half(kt, it * kTile, 1, false);
+  }
+  // Tiles with block keys or past the end: staged through registers.
+  for (int it = cf; it < c1; ++it) {
+    uint8_t *st = lds + (it & (kStages - 1)) * L::kStage;
+    __syncthreads();
+    stage_slow<D>(st, it * kTile, cl, total, M, p.ccap, ckb, cvb, bkb, bvb, tid, kThreads);
+    __syncthreads();
+    compute_half(st, it * kTile, 0, true);
+    compute_half(st, it * kTile, 1, true);
   }
 
   const int rows = p.B * M * p.Hq;
