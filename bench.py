@@ -50,7 +50,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=2)
     ap.add_argument("--warmup", type=int, default=1)
     ap.add_argument("--workload", default="stagger128k",
-                    choices=["stagger128k", "verify32k", "draft128k", "draft128k_int4", "copy1g"])
+                    choices=["stagger128k", "verify32k", "verify128k", "draft128k", "draft128k_int4", "copy1g"])
     ap.add_argument("--layers", type=int, default=64)
     ap.add_argument("--distinct-layers", type=int, default=16,
                     help="distinct compressed-cache buffers per cohort (layers rotate over them)")
@@ -321,9 +321,13 @@ def kernel_alone(args):
     import lossless_speculative_decoding_vc_amd as vc
     dev = "cuda"
     s = torch.cuda.current_stream()
-    if args.workload == "verify32k":
-        B, Hq, Hkv, D, N, M = 1, 64, 8, 128, 32768, 32
-        nset = 5
+    if args.workload in ("verify32k", "verify128k"):
+        if args.workload == "verify32k":   # Llama-70B layer shape, one request, k = 32
+            B, Hq, Hkv, D, N, M = 1, 64, 8, 128, 32768, 32
+            nset = 5
+        else:   # verifying cohort of the staggered batch: Qwen-32B layer shape, 16 requests, k = 32
+            B, Hq, Hkv, D, N, M = 16, 40, 8, 128, 131072, 33
+            nset = 2
         sets = [dict(q=_bf16_randn((B, M, Hq, D), 10 + i, dev), k=_bf16_randn((B, Hkv, N, D), 20 + i, dev),
                      v=_bf16_randn((B, Hkv, D, N), 30 + i, dev), bk=_bf16_randn((B, Hkv, M, D), 40 + i, dev),
                      bv=_bf16_randn((B, Hkv, D, M), 50 + i, dev)) for i in range(nset)]

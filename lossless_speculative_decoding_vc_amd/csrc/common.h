@@ -28,12 +28,22 @@ VC_DEVICE float u32_as_f32(uint32_t w) { return __builtin_bit_cast(float, w); }
 VC_DEVICE float bf16_lo(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
 VC_DEVICE float bf16_hi(uint32_t w) { return __builtin_bit_cast(float, w & 0xffff0000u); }
 VC_DEVICE float bf16_to_f32(uint16_t h) { return __builtin_bit_cast(float, uint32_t(h) << 16); }
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+// Two floats -> one packed bf16 pair (RNE) in a single v_cvt_pk_bf16_f32.
 VC_DEVICE uint32_t pack_bf16x2(float lo, float hi) {
-  __bf16 a = (__bf16)lo, b = (__bf16)hi;
-  return uint32_t(__builtin_bit_cast(uint16_t, a)) | (uint32_t(__builtin_bit_cast(uint16_t, b)) << 16);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{lo, hi}), bf16x2));
+}
+// acc + lo + hi of a packed bf16 pair, in one v_dot2 against (1, 1).
+VC_DEVICE float sum_bf16x2(uint32_t w, float acc) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w), bf16x2{(__bf16)1.0f, (__bf16)1.0f}, acc, false);
 }
 VC_DEVICE uint16_t f32_to_bf16(float x) { return __builtin_bit_cast(uint16_t, (__bf16)x); }
 VC_DEVICE float f16_to_f32(uint16_t h) { return (float)__builtin_bit_cast(_Float16, h); }
+
+// IEEE maximum (NaN-propagating): lowers to v_maximum3_f32 without the
+// canonicalising v_max that fmaxf needs on MFMA results.
+VC_DEVICE float vmax(float a, float b) { return __builtin_elementwise_maximum(a, b); }
 
 VC_DEVICE float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 VC_DEVICE float fast_log2(float x) { return __builtin_amdgcn_logf(x); }

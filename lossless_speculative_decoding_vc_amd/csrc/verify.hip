@@ -10,25 +10,30 @@
 //  * the M block rows times the G = Hq/Hkv query heads that share a KV head
 //    are packed into R = M*G query rows, so one pass over a KV head's keys
 //    serves all of them (the contraction that makes verify dense).
-//  * grid (splits, row groups, B*Hkv); up to 8 waves per workgroup (two per
-//    SIMD, so one wave's LDS latency hides behind the other's MFMAs), each
-//    wave owns two column tiles of 16 packed rows, so a row group covers up
-//    to 256 rows and K/V leave HBM once per row group.
+//  * grid (splits, row groups, B*Hkv).  A row group is up to 256 packed
+//    rows and K/V leave HBM once per row group: up to 192 rows it is four
+//    waves (one per SIMD) of up to three 16-row column tiles each, beyond
+//    that eight waves of two tiles (two per SIMD).
 //  * the workgroup streams 64-token tiles of K (token-major) and V
 //    (channel-major) through a ring of 4 LDS stages filled by direct
-//    global->LDS loads (global_load_lds_dwordx4): three tiles stay in flight
-//    (96 KB per CU at head_dim 128) without holding any of them in
-//    registers.  Each wave-wide load lands as 1 KB of contiguous LDS, so bank
-//    conflicts are avoided by XOR-swizzling which 16-byte piece a lane
+//    global->LDS loads (global_load_lds_dwordx4), two to three tiles in
+//    flight (64-96 KB per CU at head_dim 128) without holding any of them
+//    in registers.  Each wave-wide load lands as 1 KB of contiguous LDS, so
+//    bank conflicts are avoided by XOR-swizzling which 16-byte piece a lane
 //    fetches instead of padding rows.  Tiles that reach the block keys or
-//    the end of the key sequence are staged through registers.
+//    the end of the key sequence are staged through registers after the
+//    main loop.
 //  * S^T = K Q^T and O^T = V^T P^T on v_mfma_f32_16x16x32_bf16; the token
 //    rows of the S^T tiles are permuted so each lane's scores are the 8
 //    consecutive tokens the PV MFMA consumes as its k-slots: P never leaves
 //    the registers it was computed in.
-//  * fp32 online softmax in base 2, one running max per packed row; causal
-//    masking only in tiles that reach the block; the output rescale is
-//    skipped when no row's max moved.
+//  * the main loop is software-pipelined by 32-token halves: the QK MFMAs
+//    of the next half overlap the probabilities of the current one, the PV
+//    MFMAs overlap the next half's maxima, and K/V operands are read from
+//    LDS a half-step ahead.
+//  * fp32 online softmax in base 2 with a lazily updated reference max per
+//    packed row (rescale only when a score exceeds it by more than 2^8);
+//    causal masking only in tiles that reach the block.
 #include "common.h"
 #include "launch.h"
 
@@ -189,7 +194,10 @@ __global__ __launch_bounds__(W * 64) void verify_bf16(VerifyParams p) {
   auto issue = [&](int c) __attribute__((always_inline)) {
     const int stage = c & (kStages - 1);
     const int base = c * kTile;
-    for (int q = wave; q < L::kBlocks; q += W) {
+#pragma unroll
+    for (int j = 0; j < (L::kBlocks + W - 1) / W; ++j) {
+      const int q = wave + j * W;
+      if (q >= L::kBlocks) break;
       const uint16_t *src;
       if (q < L::kKBlocks) {
         const int r = q * L::kRowsPerBlock + lane / L::kSlots;
@@ -202,66 +210,62 @@ __global__ __launch_bounds__(W * 64) void verify_bf16(VerifyParams p) {
     }
   };
 
-  float m_run[CT], l_run[CT];
+  float m_run[CT], l_run[CT], mq[CT];   // mq = scaled reference (0 while it is -inf)
   f32x4 o[CT][DT];
 #pragma unroll
   for (int ct = 0; ct < CT; ++ct) {
     m_run[ct] = kNegInf;
+    mq[ct] = 0.f;
     l_run[ct] = 0.f;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) o[ct][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-  // One 32-token half h of the 64-token tile: S^T tiles tau = 2h, 2h+1,
-  // online softmax, then the PV k-step h.  The K operands of the half are
-  // read before its first MFMA.
-  auto compute_half = [&](const uint8_t *kt, int base, int h, bool masked) __attribute__((always_inline)) {
-    const uint8_t *vt = kt + L::kKBytes;
-    u32x4 ka[2][KS];
+  // Pieces of one 32-token half h of a 64-token tile (S^T tiles tau = 2h,
+  // 2h+1, then the PV k-step h).
+  const float qs = p.qk_scale;
+  using KOps = u32x4[2][KS];
+  using Scores = f32x4[CT][2];
+  // K operands of half h (16 token rows per S^T tile, 32 channels per k-step).
+  auto load_k = [&](const uint8_t *kt, int h, KOps &ka) __attribute__((always_inline)) {
 #pragma unroll
     for (int t2 = 0; t2 < 2; ++t2) {
-      const int kr = 16 * (2 * h + t2) + col;   // token base + 8*(col>>2) + 4*t2 + (col&3)
+      const int kr = 16 * (2 * h + t2) + col;   // token 8*(col>>2) + 4*t2 + (col&3) of the half
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks)
         ka[t2][ks] = *reinterpret_cast<const u32x4 *>(kt + kr * L::kKRow + 16 * kswz<D>(kr, 4 * ks + grp));
     }
-    f32x4 s[CT][2];
+  };
+  auto qk = [&](const KOps &ka, Scores &sc) __attribute__((always_inline)) {
 #pragma unroll
-    for (int ct = 0; ct < CT; ++ct) s[ct][0] = s[ct][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int ct = 0; ct < CT; ++ct) sc[ct][0] = sc[ct][1] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
       for (int t2 = 0; t2 < 2; ++t2)
 #pragma unroll
-        for (int ct = 0; ct < CT; ++ct) s[ct][t2] = mfma16x16x32(as_bf16x8(ka[t2][ks]), qb[ct][ks], s[ct][t2]);
-    // Lazy reference max per packed row: each lane first compares its own 8
-    // scores with the row's reference; only when some score in the wave
-    // exceeds it by more than kSlack (base 2) do the lane groups exchange
-    // their maxima (two cross-lane shuffles) and rescale -- after the first
-    // tiles that branch is rarely taken, and probabilities stay <= 2^kSlack.
-    const float qs = p.qk_scale;
-    float sc[CT][8];
+        for (int ct = 0; ct < CT; ++ct) sc[ct][t2] = mfma16x16x32(as_bf16x8(ka[t2][ks]), qb[ct][ks], sc[ct][t2]);
+  };
+  // Lazy reference max per packed row: each lane compares its own 8 scores
+  // with the row's reference; only when some score in the wave exceeds it by
+  // more than kSlack (base 2) do the lane groups exchange their maxima (two
+  // cross-lane shuffles) and rescale.  After the first tiles that branch is
+  // rarely taken, and probabilities stay <= 2^kSlack.
+  auto row_max = [&](const Scores &sc, float (&lmax)[CT]) __attribute__((always_inline)) {
     bool need = false;
 #pragma unroll
     for (int ct = 0; ct < CT; ++ct) {
-      float lmax = kNegInf;
-#pragma unroll
-      for (int t2 = 0; t2 < 2; ++t2)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          float x = s[ct][t2][i];
-          if (masked && base + 32 * h + 8 * grp + 4 * t2 + i >= row_lim[ct]) x = kNegInf;
-          sc[ct][4 * t2 + i] = x;
-          lmax = fmaxf(lmax, x);
-        }
-      need |= (lmax - m_run[ct]) * qs > kSlack;   // false when both are -inf
+      lmax[ct] = vmax(vmax(vmax(sc[ct][0][0], sc[ct][0][1]), vmax(sc[ct][0][2], sc[ct][0][3])),
+                      vmax(vmax(sc[ct][1][0], sc[ct][1][1]), vmax(sc[ct][1][2], sc[ct][1][3])));
+      need |= (lmax[ct] - m_run[ct]) * qs > kSlack;   // false when both are -inf
     }
+    return need;
+  };
+  auto rescale = [&](bool need, const float (&lmax)[CT]) __attribute__((always_inline)) {
     if (__any(need)) {
 #pragma unroll
       for (int ct = 0; ct < CT; ++ct) {
-        float cmax = kNegInf;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) cmax = fmaxf(cmax, sc[ct][e]);
+        float cmax = lmax[ct];
         cmax = fmaxf(cmax, __shfl_xor(cmax, 16, 64));
         cmax = fmaxf(cmax, __shfl_xor(cmax, 32, 64));
         const float m_new = fmaxf(m_run[ct], cmax);
@@ -270,58 +274,145 @@ __global__ __launch_bounds__(W * 64) void verify_bf16(VerifyParams p) {
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) o[ct][dt] *= alpha;
         m_run[ct] = m_new;
+        mq[ct] = (m_new == kNegInf) ? 0.f : m_new * qs;
       }
     }
-    bf16x8 pb[CT];
+  };
+  auto update_max = [&](const Scores &sc) __attribute__((always_inline)) {
+    float lmax[CT];
+    rescale(row_max(sc, lmax), lmax);
+  };
+  // Probabilities relative to the reference, packed to bf16 as the B operand
+  // of the PV MFMA (k-slot e of lane group grp = token 8*grp + e of the half).
+  // The row sum accumulates the bf16-rounded probabilities, i.e. exactly the
+  // weights the PV MFMA applies.
+  auto exp_pack = [&](const Scores &sc, bf16x8 (&pb)[CT]) __attribute__((always_inline)) {
 #pragma unroll
     for (int ct = 0; ct < CT; ++ct) {
-      const float mc = (m_run[ct] == kNegInf) ? 0.f : m_run[ct] * qs;
-      float pr[8], psum = 0.f;
+      float pr[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        pr[e] = fast_exp2(fmaf(sc[ct][e], qs, -mc));
-        psum += pr[e];
-      }
-      l_run[ct] += psum;
-      pb[ct] = as_bf16x8(u32x4{pack_bf16x2(pr[0], pr[1]), pack_bf16x2(pr[2], pr[3]),
-                               pack_bf16x2(pr[4], pr[5]), pack_bf16x2(pr[6], pr[7])});
+      for (int e = 0; e < 8; ++e) pr[e] = fast_exp2(fmaf(sc[ct][e >> 2][e & 3], qs, -mq[ct]));
+      const u32x4 w = u32x4{pack_bf16x2(pr[0], pr[1]), pack_bf16x2(pr[2], pr[3]),
+                            pack_bf16x2(pr[4], pr[5]), pack_bf16x2(pr[6], pr[7])};
+      l_run[ct] = sum_bf16x2(w[3], sum_bf16x2(w[2], sum_bf16x2(w[1], sum_bf16x2(w[0], l_run[ct]))));
+      pb[ct] = as_bf16x8(w);
     }
+  };
+  // V^T operands of half h (16 channels per output tile, 32 tokens).
+  using VOps = u32x4[DT];
+  auto load_v = [&](const uint8_t *kt, int h, VOps &va) __attribute__((always_inline)) {
+    const uint8_t *vt = kt + L::kKBytes;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
       const int d = 16 * dt + col;
-      const bf16x8 va = as_bf16x8(*reinterpret_cast<const u32x4 *>(vt + d * L::kVRow + 16 * vswz(d, 4 * h + grp)));
-#pragma unroll
-      for (int ct = 0; ct < CT; ++ct) o[ct][dt] = mfma16x16x32(va, pb[ct], o[ct][dt]);
+      va[dt] = *reinterpret_cast<const u32x4 *>(vt + d * L::kVRow + 16 * vswz(d, 4 * h + grp));
     }
   };
+  auto pv = [&](const VOps &va, const bf16x8 (&pb)[CT]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct) o[ct][dt] = mfma16x16x32(as_bf16x8(va[dt]), pb[ct], o[ct][dt]);
+  };
+  auto stage_ptr = [&](int c) __attribute__((always_inline)) { return lds + (c & (kStages - 1)) * L::kStage; };
 
-  // Ring of kStages stages: tiles c+1..c+3 in flight while tile c is
-  // computed.  Direct loads complete in issue order per wave, so "tile c
-  // landed" is vmcnt <= (direct loads issued after it); the barrier then
-  // publishes all waves' pieces and guarantees stage (c-1)%4 is no longer
-  // being read when tile c+3 is issued into it.  The loop body holds no
-  // call and no other memory load, so nothing else moves vmcnt.
+  // Main loop over the full tiles, software-pipelined by halves: while the
+  // QK MFMAs of half n+1 run, the VALU computes the probabilities of half n;
+  // while the PV MFMAs of half n run, it takes the maxima of half n+1.  K
+  // and V operands are read from LDS one half-step before their MFMAs.
+  //
+  // Ring of kStages LDS stages filled by direct loads.  At the top of tile
+  // c the wave waits for tile c+1 (direct loads complete in issue order per
+  // wave, so "landed" is vmcnt <= the loads issued after it), and a barrier
+  // publishes all waves' pieces and guarantees that tile c-1's stage is no
+  // longer read, so tile c+3 can be issued into it.  The loop holds no call
+  // and no other memory load, so nothing else moves vmcnt.
   constexpr int kMine = L::kBlocks / W;   // fewest direct loads per wave per tile
-  for (int c = c0; c < min(c0 + kStages - 1, cf); ++c) issue(c);
-  for (int it = c0; it < cf; ++it) {
-    const int ahead = min(cf - 1 - it, kStages - 2);   // tiles issued after this one (0..2)
-    if (ahead >= 2) __asm__ volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * kMine) : "memory");
-    else if (ahead == 1) __asm__ volatile("s_waitcnt vmcnt(%0)" ::"n"(kMine) : "memory");
+  auto wait_tiles_after = [&](int n) __attribute__((always_inline)) {   // n = 0, 1, 2 tiles may stay in flight
+    if (n >= 2) __asm__ volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * kMine) : "memory");
+    else if (n == 1) __asm__ volatile("s_waitcnt vmcnt(%0)" ::"n"(kMine) : "memory");
     else __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  };
+  if (c0 < cf) {
+    for (int c = c0; c < min(c0 + kStages - 1, cf); ++c) issue(c);
+    wait_tiles_after(min(cf - 1 - c0, kStages - 2));
     __syncthreads();
-    if (it + kStages - 1 < cf) issue(it + kStages - 1);
-    const uint8_t *kt = lds + (it & (kStages - 1)) * L::kStage;
-    compute_half(kt, it * kTile, 0, false);
-    compute_half(kt, it * kTile, 1, false);
+    KOps ka;
+    VOps va;
+    Scores s_cur, s_nxt;
+    bf16x8 pb[CT];
+    load_k(stage_ptr(c0), 0, ka);
+    qk(ka, s_cur);
+    load_k(stage_ptr(c0), 1, ka);
+    load_v(stage_ptr(c0), 0, va);
+    update_max(s_cur);
+    for (int it = c0; it + 1 < cf; ++it) {
+      wait_tiles_after(it + 2 < cf ? 1 : 0);
+      __syncthreads();
+      if (it + kStages - 1 < cf) issue(it + kStages - 1);
+      const uint8_t *kt = stage_ptr(it), *kn = stage_ptr(it + 1);
+      // half 2*it: S(2it+1) = QK, P(2it) -> PV.  The scheduling fences keep
+      // each operand refill after the MFMAs that still read the old one, so
+      // only one copy of the K and V operands is live.
+      float lmax[CT];
+      qk(ka, s_nxt);
+      exp_pack(s_cur, pb);
+      __builtin_amdgcn_sched_barrier(0);
+      load_k(kn, 0, ka);
+      pv(va, pb);
+      bool need = row_max(s_nxt, lmax);
+      __builtin_amdgcn_sched_barrier(0);
+      load_v(kt, 1, va);
+      rescale(need, lmax);
+      // half 2*it+1: S(2it+2) = QK, P(2it+1) -> PV
+      qk(ka, s_cur);
+      exp_pack(s_nxt, pb);
+      __builtin_amdgcn_sched_barrier(0);
+      load_k(kn, 1, ka);
+      pv(va, pb);
+      need = row_max(s_cur, lmax);
+      __builtin_amdgcn_sched_barrier(0);
+      load_v(kn, 0, va);
+      rescale(need, lmax);
+    }
+    const uint8_t *kt = stage_ptr(cf - 1);
+    qk(ka, s_nxt);
+    exp_pack(s_cur, pb);
+    pv(va, pb);
+    load_v(kt, 1, va);
+    update_max(s_nxt);
+    exp_pack(s_nxt, pb);
+    pv(va, pb);
   }
-  // Tiles with block keys or past the end: staged through registers.
+
+  // Tiles with block keys or past the end: staged through registers, causal
+  // mask applied to the scores, not pipelined.
   for (int it = cf; it < c1; ++it) {
-    uint8_t *st = lds + (it & (kStages - 1)) * L::kStage;
+    uint8_t *st = stage_ptr(it);
     __syncthreads();
     stage_slow<D>(st, it * kTile, cl, total, M, p.ccap, ckb, cvb, bkb, bvb, tid, kThreads);
     __syncthreads();
-    compute_half(st, it * kTile, 0, true);
-    compute_half(st, it * kTile, 1, true);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      KOps ka;
+      Scores sc;
+      bf16x8 pb[CT];
+      load_k(st, h, ka);
+      qk(ka, sc);
+      const int jb = it * kTile + 32 * h + 8 * grp;   // key index of score (t2, i): jb + 4*t2 + i
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+        for (int t2 = 0; t2 < 2; ++t2)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (jb + 4 * t2 + i >= row_lim[ct]) sc[ct][t2][i] = kNegInf;
+      VOps va;
+      load_v(st, h, va);
+      update_max(sc);
+      exp_pack(sc, pb);
+      pv(va, pb);
+    }
   }
 
   const int rows = p.B * M * p.Hq;
@@ -357,25 +448,28 @@ __global__ __launch_bounds__(W * 64) void verify_bf16(VerifyParams p) {
   }
 }
 
-// Waves and 16-row column tiles per wave for R packed rows: up to 256 rows
-// per workgroup (8 waves x 2 tiles), two waves per SIMD.
+// Waves and 16-row column tiles per wave for R packed rows.  Up to 192
+// rows: four waves (one per SIMD) of up to 48 rows; more rows per wave means
+// fewer LDS bytes per MFMA (each K/V operand read from LDS feeds CT MFMAs).
+// Up to 256 rows: eight waves of 32 rows (64 rows per wave would not fit
+// the register file at head_dim 128).
 struct VerifyShape {
   int W, CT;
 };
 VerifyShape verify_shape(int R) {
   if (R <= 64) return {4, 1};
   if (R <= 128) return {4, 2};
-  if (R <= 192) return {6, 2};
+  if (R <= 192) return {4, 3};
   return {8, 2};
 }
 
 template <int D>
 void launch_verify_d(const VerifyParams &p, VerifyShape sh, int row_groups, hipStream_t s) {
   dim3 grid(p.splits, row_groups, p.B * p.Hkv);
-  if (sh.W == 4 && sh.CT == 1) verify_bf16<D, 4, 1><<<grid, 256, 0, s>>>(p);
-  else if (sh.W == 4) verify_bf16<D, 4, 2><<<grid, 256, 0, s>>>(p);
-  else if (sh.W == 6) verify_bf16<D, 6, 2><<<grid, 384, 0, s>>>(p);
-  else verify_bf16<D, 8, 2><<<grid, 512, 0, s>>>(p);
+  if (sh.W == 8) verify_bf16<D, 8, 2><<<grid, 512, 0, s>>>(p);
+  else if (sh.CT == 1) verify_bf16<D, 4, 1><<<grid, 256, 0, s>>>(p);
+  else if (sh.CT == 2) verify_bf16<D, 4, 2><<<grid, 256, 0, s>>>(p);
+  else verify_bf16<D, 4, 3><<<grid, 256, 0, s>>>(p);
 }
 
 }  // namespace
