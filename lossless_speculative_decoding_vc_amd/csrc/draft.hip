@@ -276,52 +276,77 @@ __global__ __launch_bounds__(kDraftWaves * 64) void draft_bf16_dense(DraftParams
 
 // ---------------------------------------------------------------------------
 // Int4 main segment ("Supporto Architetturale": quantizing drafters plug into
-// the same interface).  Same MFMA pipeline as the dense kernel; each lane
-// dequantises its own operands in registers right before the MFMAs:
-//  * K: the lane's S^T row is a token; its 16-byte code load covers channels
-//    32*grp .. 32*grp+31 (k-step ks takes 8*ks..8*ks+7 of them), with the
-//    chunk's per-channel scales/zeros (the chunk is exactly one 32-token
-//    group);
-//  * V: the lane's row is a channel; its 4-byte code load covers the 8 tokens
-//    of its k-slots, with their per-token scales/zeros of the channel's
-//    32-channel group.
-// x = code * scale + zero in fp32, rounded to bf16 for the MFMA.
-VC_DEVICE void unpack8(uint32_t w, float *out) {
-  // byte i of w holds element 2i (low nibble) and 2i+1 (high nibble)
-  const uint32_t lo = w & 0x0F0F0F0Fu, hi = (w >> 4) & 0x0F0F0F0Fu;
-  // (float)(byte k) compiles to v_cvt_f32_ubyte<k>
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    out[2 * k] = (float)((lo >> (8 * k)) & 0xffu);
-    out[2 * k + 1] = (float)((hi >> (8 * k)) & 0xffu);
-  }
+// the same interface).  K codes are grouped per channel over 32 tokens -- one
+// group is exactly one 32-token chunk -- and V codes per token over 32
+// channels.  Design:
+//  * every wave streams its own chunks through a private ring of kI4Stages
+//    LDS stages filled by direct global->LDS loads: per chunk 2 KB of K
+//    codes, 2 KB of V codes and 1 KB of scales/zeros (plus 128 B of merge
+//    degrees when present), four chunks in flight per wave.  No barrier is
+//    needed: a wave only reads what it loaded itself.
+//  * the quantisation is folded into the other MFMA operand, so the VALU
+//    never multiplies an individual code by its scale:
+//      S_t   = sum_d (q_d s_d) c_td + sum_d q_d z_d
+//      O_d  += sum_t (p_t s_tg) c_td + sum_t p_t z_tg
+//    with c read as an exact fp16 "magic" value (1024 + c or 64 + c, one
+//    v_perm + one OR per pair of codes) and the magic offsets removed by an
+//    extra MFMA against the constant -1024/-64 operand; the zero-point terms
+//    are MFMAs whose A operand repeats z along the rows.  All operands are
+//    fp16 (v_mfma_f32_16x16x32_f16) with fp32 accumulation; Q is brought
+//    into fp16 range with an exact per-head power-of-two scale.
+//  * chunks that reach the bf16 tail or the end of the sequence are
+//    dequantised element-wise after the main loop.
+constexpr int kI4Stages = 5;
+constexpr int kI4Stage = 6 * 1024;   // K codes, V codes, scales/zeros, degree (bytes)
+
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+
+VC_DEVICE f16x8 as_f16x8(const u32x4 &u) { return __builtin_bit_cast(f16x8, u); }
+VC_DEVICE f32x4 mfma_f16(const u32x4 &a, const u32x4 &b, const f32x4 &c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(as_f16x8(a), as_f16x8(b), c, 0, 0, 0);
 }
-VC_DEVICE void f16x8(const u32x4 &w, float *out) {
+VC_DEVICE uint32_t pk_mul_f16(uint32_t a, uint32_t b) {
+  return __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, a) * __builtin_bit_cast(f16x2, b));
+}
+// acc + lo + hi of a packed fp16 pair (the word is taken by value: a bit
+// cast applied to an ext_vector element would read element 0).
+VC_DEVICE float sum_f16x2(uint32_t w, float acc) {
+  return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, w), f16x2{(_Float16)1.0f, (_Float16)1.0f}, acc, false);
+}
+VC_DEVICE uint32_t pack_f16x2(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{lo, hi}), f16x2));
+}
+// Eight 4-bit codes (byte j = codes 2j, 2j+1 in its low, high nibble) as four
+// fp16 pairs (1024 + c_2j, 64 + c_2j+1): the low nibble lands in the low
+// mantissa bits of an fp16 whose ulp is 1, the high nibble in bits 4..7 of
+// one whose ulp is 1/16 -- both exact.
+VC_DEVICE u32x4 magic_codes(uint32_t w) {
+  const uint32_t lo = w & 0x0F0F0F0Fu, hi = w & 0xF0F0F0F0u;
+  u32x4 r;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const uint32_t u = w[i];
-    out[2 * i] = f16_to_f32((uint16_t)(u & 0xffffu));
-    out[2 * i + 1] = f16_to_f32((uint16_t)(u >> 16));
-  }
+  for (int j = 0; j < 4; ++j)
+    r[j] = __builtin_amdgcn_perm(hi, lo, 0x0C000C00u | ((4u + j) << 16) | (uint32_t)j) | 0x54006400u;
+  return r;
+}
+constexpr uint32_t kNegMagic = 0xD400E400u;   // fp16 pair (-1024, -64)
+
+// Direct global->LDS load of 16 bytes per lane (lane i lands at lds + 16 i).
+VC_DEVICE void dma16(const void *gptr, uint32_t lds_addr) {
+  __asm__ volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gptr), "s"(lds_addr) : "memory", "m0");
 }
 
-template <int D>
-struct Int4Raw {
-  u32x4 kc[2];          // K codes of the two S^T tiles (32 channels each)
-  u32x4 ks[4], kz[4];   // K scales / zeros of channels 32*grp .. +31
-  uint32_t vc[D / 16];  // V codes: 8 tokens of channel 16*dt + col
-  u32x4 vs[D / 32], vz[D / 32];   // V scales / zeros of the lane's 8 tokens per channel group
-  float lg[8];
-};
-
-template <int D>
-__global__ __launch_bounds__(kDraftWaves * 64) void draft_bf16_int4(DraftParams p) {
+template <int D, bool DEG>
+__global__ __launch_bounds__(kDraftWaves * 64) void draft_int4(DraftParams p) {
   constexpr int KS = D / 32, DT = D / 16, NG = D / 32;
   static_assert(D == 128, "int4 draft is compiled for head_dim 128");
+  constexpr int kBlk = DEG ? 6 : 5;   // direct loads per chunk per wave
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[kDraftWaves * kI4Stages * kI4Stage];
+
   const int bh = blockIdx.y;
   const int b = bh / p.Hkv, kvh = bh % p.Hkv;
   const int split = blockIdx.x;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int col = lane & 15, grp = lane >> 4;
   const int G = p.G;
 
@@ -332,22 +357,54 @@ __global__ __launch_bounds__(kDraftWaves * 64) void draft_bf16_int4(DraftParams 
     tlen = p.tail_len[b];
     tlen = tlen < 0 ? 0 : (tlen > p.tcap ? (int)p.tcap : tlen);
   }
-  const int total = mlen + tlen;
-  const int nchunks = (total + kChunk - 1) / kChunk;
+  // Chunks 0 .. nmain-1 cover the int4 segment (the last one masked at
+  // mlen), chunks nmain .. nmain+ntail-1 the bf16 tail from token mlen on.
+  const int nmain = (mlen + kChunk - 1) / kChunk;
+  const int nchunks = nmain + (tlen + kChunk - 1) / kChunk;
   const int cps = (nchunks + p.splits - 1) / p.splits;
   const int c0 = split * cps;
   const int c1 = min(c0 + cps, nchunks);
+  const int cf = max(c0, min(c1, nmain));   // [c0, cf): int4 chunks of this split
 
-  // Q^T operand, channel order d = 32*grp + 8*ks + e (the K code layout).
-  bf16x8 qb[KS];
+  // Q^T operand in fp16, channel order d = 32*grp + 8*ks + e (the K code
+  // layout), scaled per head by 2^-E so that max |q| lies in [0.5, 1).
+  float qf[KS][8];
+  float qmax = 0.f;
   if (col < G) {
     const uint16_t *qp = p.q + ((size_t)b * p.Hq + kvh * G + col) * D;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) qb[ks] = as_bf16x8(ld16(qp + 32 * grp + 8 * ks));
+    for (int ks = 0; ks < KS; ++ks) {
+      const u32x4 w = ld16(qp + 32 * grp + 8 * ks);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        qf[ks][2 * j] = bf16_lo(w[j]);
+        qf[ks][2 * j + 1] = bf16_hi(w[j]);
+      }
+    }
   } else {
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) qb[ks] = as_bf16x8(u32x4{0, 0, 0, 0});
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) qf[ks][e] = 0.f;
   }
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) qmax = fmaxf(qmax, fabsf(qf[ks][e]));
+  qmax = fmaxf(qmax, __shfl_xor(qmax, 16, 64));
+  qmax = fmaxf(qmax, __shfl_xor(qmax, 32, 64));
+  const int qexp = (qmax > 0.f) ? __builtin_amdgcn_frexp_expf(qmax) : 0;
+  const float qs = ldexpf(p.qk_scale, qexp);   // score scale of this lane's head (base 2)
+  u32x4 qh[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      qh[ks][j] = pack_f16x2(ldexpf(qf[ks][2 * j], -qexp), ldexpf(qf[ks][2 * j + 1], -qexp));
+  // Make the compiler wait for the Q loads here: its wait counts do not see
+  // the direct loads below and would otherwise count them.
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) __asm__ volatile("" ::"v"(qh[ks]));
 
   const uint8_t *kqb = p.kq + (size_t)bh * p.cap * (D / 2);
   const uint8_t *vqb = p.vq + (size_t)bh * D * (p.cap / 2);
@@ -364,169 +421,12 @@ __global__ __launch_bounds__(kDraftWaves * 64) void draft_bf16_int4(DraftParams 
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  auto fetch = [&](int c, Int4Raw<D> &r) __attribute__((always_inline)) {
-    const int base = c * kChunk;
-    const int g32 = base / 32;
-#pragma unroll
-    for (int tau = 0; tau < 2; ++tau) {
-      const int t = base + 8 * (col >> 2) + 4 * tau + (col & 3);
-      r.kc[tau] = *reinterpret_cast<const u32x4 *>(kqb + (size_t)t * (D / 2) + 16 * grp);
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      r.ks[i] = ld16(ksb + (size_t)g32 * D + 32 * grp + 8 * i);
-      r.kz[i] = ld16(kzb + (size_t)g32 * D + 32 * grp + 8 * i);
-    }
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
-      r.vc[dt] = *reinterpret_cast<const uint32_t *>(vqb + (size_t)(16 * dt + col) * (p.cap / 2) + (base + 8 * grp) / 2);
-#pragma unroll
-    for (int j = 0; j < NG; ++j) {
-      r.vs[j] = ld16(vsb + (size_t)j * p.cap + base + 8 * grp);
-      r.vz[j] = ld16(vzb + (size_t)j * p.cap + base + 8 * grp);
-    }
-    if (db) {
-      const f32x4 *dp = reinterpret_cast<const f32x4 *>(db + base + 8 * grp);
-      const f32x4 d0 = dp[0], d1 = dp[1];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        r.lg[e] = fast_log2(d0[e]);
-        r.lg[4 + e] = fast_log2(d1[e]);
-      }
-    } else {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) r.lg[e] = 0.f;
-    }
-  };
-
-  // Dequantise into MFMA operands (main chunk) -- full chunks only.
-  auto decode = [&](const Int4Raw<D> &r, u32x4 (&ka)[2][KS], u32x4 (&va)[DT]) __attribute__((always_inline)) {
-    float sf[32], zf[32];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      f16x8(r.ks[i], sf + 8 * i);
-      f16x8(r.kz[i], zf + 8 * i);
-    }
-#pragma unroll
-    for (int tau = 0; tau < 2; ++tau)
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        float cv[8];
-        unpack8(r.kc[tau][ks], cv);
-        uint32_t w[4];
-#pragma unroll
-        for (int e2 = 0; e2 < 4; ++e2)
-          w[e2] = pack_bf16x2(fmaf(cv[2 * e2], sf[8 * ks + 2 * e2], zf[8 * ks + 2 * e2]),
-                              fmaf(cv[2 * e2 + 1], sf[8 * ks + 2 * e2 + 1], zf[8 * ks + 2 * e2 + 1]));
-        ka[tau][ks] = u32x4{w[0], w[1], w[2], w[3]};
-      }
-    float vsf[NG][8], vzf[NG][8];
-#pragma unroll
-    for (int j = 0; j < NG; ++j) {
-      f16x8(r.vs[j], vsf[j]);
-      f16x8(r.vz[j], vzf[j]);
-    }
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
-      const int j = dt >> 1;
-      float cv[8];
-      unpack8(r.vc[dt], cv);
-      uint32_t w[4];
-#pragma unroll
-      for (int e2 = 0; e2 < 4; ++e2)
-        w[e2] = pack_bf16x2(fmaf(cv[2 * e2], vsf[j][2 * e2], vzf[j][2 * e2]),
-                            fmaf(cv[2 * e2 + 1], vsf[j][2 * e2 + 1], vzf[j][2 * e2 + 1]));
-      va[dt] = u32x4{w[0], w[1], w[2], w[3]};
-    }
-  };
-
-  // Chunk that reaches the tail or the end: element-wise, from the int4 main
-  // segment, the bf16 tail, or zero.
-  auto slow_ops = [&](int c, u32x4 (&ka)[2][KS], u32x4 (&va)[DT], float (&lg)[8]) __attribute__((always_inline)) {
-    const int base = c * kChunk;
-#pragma unroll
-    for (int tau = 0; tau < 2; ++tau) {
-      const int t = base + 8 * (col >> 2) + 4 * tau + (col & 3);
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        uint32_t w[4];
-#pragma unroll
-        for (int e2 = 0; e2 < 4; ++e2) {
-          float x[2];
-#pragma unroll
-          for (int u = 0; u < 2; ++u) {
-            const int d = 32 * grp + 8 * ks + 2 * e2 + u;
-            float v = 0.f;
-            if (t < mlen) {
-              const uint8_t byte = kqb[(size_t)t * (D / 2) + d / 2];
-              const float code = (float)((d & 1) ? (byte >> 4) : (byte & 15));
-              v = fmaf(code, f16_to_f32(ksb[(size_t)(t / 32) * D + d]), f16_to_f32(kzb[(size_t)(t / 32) * D + d]));
-            } else if (t < total) {
-              v = bf16_to_f32(tkb[(size_t)(t - mlen) * D + d]);
-            }
-            x[u] = v;
-          }
-          w[e2] = pack_bf16x2(x[0], x[1]);
-        }
-        ka[tau][ks] = u32x4{w[0], w[1], w[2], w[3]};
-      }
-    }
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
-      const int d = 16 * dt + col, j = d / 32;
-      uint32_t w[4];
-#pragma unroll
-      for (int e2 = 0; e2 < 4; ++e2) {
-        float x[2];
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          const int t = base + 8 * grp + 2 * e2 + u;
-          float v = 0.f;
-          if (t < mlen) {
-            const uint8_t byte = vqb[(size_t)d * (p.cap / 2) + t / 2];
-            const float code = (float)((t & 1) ? (byte >> 4) : (byte & 15));
-            v = fmaf(code, f16_to_f32(vsb[(size_t)j * p.cap + t]), f16_to_f32(vzb[(size_t)j * p.cap + t]));
-          } else if (t < total) {
-            v = bf16_to_f32(tvb[(size_t)d * p.tcap + (t - mlen)]);
-          }
-          x[u] = v;
-        }
-        w[e2] = pack_bf16x2(x[0], x[1]);
-      }
-      va[dt] = u32x4{w[0], w[1], w[2], w[3]};
-    }
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int t = base + 8 * grp + e;
-      lg[e] = (db && t < mlen) ? fast_log2(db[t]) : 0.f;
-    }
-  };
-
-  auto compute = [&](int c, const u32x4 (&ka)[2][KS], const u32x4 (&va)[DT], const float (&lg)[8])
-      __attribute__((always_inline)) {
-    const int base = c * kChunk;
-    f32x4 s[2];
-#pragma unroll
-    for (int tau = 0; tau < 2; ++tau) {
-      s[tau] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) s[tau] = mfma16x16x32(as_bf16x8(ka[tau][ks]), qb[ks], s[tau]);
-    }
-    float sc[8];
-    float cmax = kNegInf;
-#pragma unroll
-    for (int tau = 0; tau < 2; ++tau)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int e = 4 * tau + i;
-        float x = fmaf(s[tau][i], p.qk_scale, lg[e]);
-        x = (base + 8 * grp + e < total) ? x : kNegInf;
-        sc[e] = x;
-        cmax = fmaxf(cmax, x);
-      }
-    // Lazy reference max: the lane groups exchange maxima (two cross-lane
-    // shuffles) and rescale only when some score in the wave exceeds the
-    // reference by more than kSlack; probabilities stay <= 2^kSlack.
+  // Online softmax of one chunk's 8 scores per lane (token 8*grp + e).
+  // Returns the probabilities relative to the lane's reference max.  Lazy
+  // reference: the lane groups exchange maxima and rescale only when some
+  // score in the wave exceeds it by more than kSlack.
+  auto softmax = [&](float (&sc)[8], float (&pr)[8]) __attribute__((always_inline)) {
+    float cmax = vmax(vmax(vmax(sc[0], sc[1]), vmax(sc[2], sc[3])), vmax(vmax(sc[4], sc[5]), vmax(sc[6], sc[7])));
     if (__any(cmax - m_run > kSlack)) {   // false when both are -inf
       cmax = fmaxf(cmax, __shfl_xor(cmax, 16, 64));
       cmax = fmaxf(cmax, __shfl_xor(cmax, 32, 64));
@@ -538,51 +438,199 @@ __global__ __launch_bounds__(kDraftWaves * 64) void draft_bf16_int4(DraftParams 
       m_run = m_new;
     }
     const float m_use = (m_run == kNegInf) ? 0.f : m_run;
-    float pr[8];
-    float psum = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) pr[e] = fast_exp2(sc[e] - m_use);
+  };
+
+  // ---- main loop: whole int4 chunks through the wave's LDS ring ----------
+  uint8_t *ring = lds + wave * (kI4Stages * kI4Stage);
+  const uint32_t ring_addr = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t *)ring;
+  const int first = c0 + wave;
+  const int nmine = (cf > first) ? (cf - first + kDraftWaves - 1) / kDraftWaves : 0;
+  // Direct loads of chunk c into stage st (lane i writes 16 bytes at 16 i):
+  //  blocks 0-1: K codes, token row t at 64 t, its 16-byte slot s holding
+  //              global slot s ^ ((t >> 3) & 3) (bank-conflict-free reads);
+  //  blocks 2-3: V codes, channel d at 2048 + 16 d (the chunk's 32 tokens);
+  //  block 4:    K scales (4096 + 2 ch), K zeros (4352 + 2 ch), V scales
+  //              (4608 + 64 g + 2 t), V zeros (4864 + 64 g + 2 t);
+  //  block 5:    merge degrees (5120 + 4 t), lanes 0..7 only.
+  auto issue = [&](int k) __attribute__((always_inline)) {
+    const int c = first + kDraftWaves * k;
+    const int base = c * kChunk;
+    const uint32_t st = ring_addr + (uint32_t)((k % kI4Stages) * kI4Stage);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int t = 16 * h + (lane >> 2);
+      dma16(kqb + (size_t)(base + t) * (D / 2) + 16 * ((lane & 3) ^ ((t >> 3) & 3)), st + 1024 * h);
+    }
+#pragma unroll
+    for (int h = 0; h < 2; ++h) dma16(vqb + (size_t)(64 * h + lane) * (p.cap / 2) + base / 2, st + 2048 + 1024 * h);
+    const uint16_t *src;
+    const int q = lane & 15;
+    if (lane < 16) src = ksb + (size_t)(base / 32) * D + 8 * q;
+    else if (lane < 32) src = kzb + (size_t)(base / 32) * D + 8 * q;
+    else if (lane < 48) src = vsb + (size_t)(q >> 2) * p.cap + base + 8 * (q & 3);
+    else src = vzb + (size_t)(q >> 2) * p.cap + base + 8 * (q & 3);
+    dma16(src, st + 4096);
+    if (DEG) {
+      if (lane < 8) dma16(db + base + 4 * lane, st + 5120);
+    }
+  };
+  auto wait_chunks_after = [&](int n) __attribute__((always_inline)) {   // n = 0..kI4Stages-2
+    if (n >= 3) __asm__ volatile("s_waitcnt vmcnt(%0)" ::"n"(3 * kBlk) : "memory");
+    else if (n == 2) __asm__ volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * kBlk) : "memory");
+    else if (n == 1) __asm__ volatile("s_waitcnt vmcnt(%0)" ::"n"(kBlk) : "memory");
+    else __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  };
+  static_assert(kI4Stages == 5, "wait_chunks_after covers up to 3 chunks in flight");
+  const u32x4 negm = u32x4{kNegMagic, kNegMagic, kNegMagic, kNegMagic};
+
+  // One int4 chunk from its LDS stage; `masked` drops tokens at or past mlen.
+  auto main_chunk = [&](const uint8_t *st, int c, bool masked) __attribute__((always_inline)) {
+    // operands of this chunk
+    u32x4 kc[2], ksc[KS], kzr[KS], vsc[NG], vzr[NG];
+    uint32_t vc[DT];
+#pragma unroll
+    for (int tau = 0; tau < 2; ++tau) {
+      const int t = 8 * (col >> 2) + 4 * tau + (col & 3);
+      kc[tau] = *reinterpret_cast<const u32x4 *>(st + 64 * t + 16 * (grp ^ ((t >> 3) & 3)));
+    }
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      ksc[ks] = *reinterpret_cast<const u32x4 *>(st + 4096 + 2 * (32 * grp + 8 * ks));
+      kzr[ks] = *reinterpret_cast<const u32x4 *>(st + 4352 + 2 * (32 * grp + 8 * ks));
+    }
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) vc[dt] = *reinterpret_cast<const uint32_t *>(st + 2048 + 16 * (16 * dt + col) + 4 * grp);
+#pragma unroll
+    for (int g = 0; g < NG; ++g) {
+      vsc[g] = *reinterpret_cast<const u32x4 *>(st + 4608 + 64 * g + 16 * grp);
+      vzr[g] = *reinterpret_cast<const u32x4 *>(st + 4864 + 64 * g + 16 * grp);
+    }
+    float lg[8];
+    if (DEG) {
+      const f32x4 d0 = *reinterpret_cast<const f32x4 *>(st + 5120 + 32 * grp);
+      const f32x4 d1 = *reinterpret_cast<const f32x4 *>(st + 5120 + 32 * grp + 16);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        lg[e] = fast_log2(d0[e]);
+        lg[4 + e] = fast_log2(d1[e]);
+      }
+    }
+    // scores: S = C + codes . q' with q' = q s and the row-constant
+    // C = sum_d q_d z_d - (magic offsets) . q'
+    u32x4 qp[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) qp[ks][j] = pk_mul_f16(qh[ks][j], ksc[ks][j]);
+    f32x4 cst = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      cst = mfma_f16(negm, qp[ks], cst);
+      cst = mfma_f16(kzr[ks], qh[ks], cst);
+    }
+    f32x4 s[2];
+#pragma unroll
+    for (int tau = 0; tau < 2; ++tau) {
+      s[tau] = cst;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) s[tau] = mfma_f16(magic_codes(kc[tau][ks]), qp[ks], s[tau]);
+    }
+    float sc[8], pr[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      pr[e] = fast_exp2(sc[e] - m_use);
-      psum += pr[e];
+      sc[e] = DEG ? fmaf(s[e >> 2][e & 3], qs, lg[e]) : s[e >> 2][e & 3] * qs;
+      if (masked && c * kChunk + 8 * grp + e >= mlen) sc[e] = kNegInf;
     }
-    l_run += psum;
-    const bf16x8 pb = as_bf16x8(u32x4{pack_bf16x2(pr[0], pr[1]), pack_bf16x2(pr[2], pr[3]),
-                                      pack_bf16x2(pr[4], pr[5]), pack_bf16x2(pr[6], pr[7])});
+    softmax(sc, pr);
+    // O += codes . (p s) + z . p, per 32-channel group g of the V scales
+    u32x4 pp;
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) o[dt] = mfma16x16x32(as_bf16x8(va[dt]), pb, o[dt]);
+    for (int j = 0; j < 4; ++j) pp[j] = pack_f16x2(pr[2 * j], pr[2 * j + 1]);
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      l_run = sum_f16x2(pp[j], l_run);
+#pragma unroll
+    for (int g = 0; g < NG; ++g) {
+      u32x4 pg;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) pg[j] = pk_mul_f16(pp[j], vsc[g][j]);
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int dt = 2 * g + h;
+        o[dt] = mfma_f16(magic_codes(vc[dt]), pg, o[dt]);
+        o[dt] = mfma_f16(negm, pg, o[dt]);
+        o[dt] = mfma_f16(vzr[g], pp, o[dt]);
+      }
+    }
   };
 
-  // Pipeline: raw loads of the next chunk in flight while the current
-  // chunk's dequantised operands go through the MFMAs.
-  Int4Raw<D> raw;
-  u32x4 ka[2][KS], va[DT];
-  float lg[8];
-  int c = c0 + wave;
-  auto prepare = [&](int cc) __attribute__((always_inline)) {
-    if (cc * kChunk + kChunk <= mlen) {
-      decode(raw, ka, va);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) lg[e] = raw.lg[e];
-    } else {
-      slow_ops(cc, ka, va, lg);
-    }
-  };
-  if (c < c1) {
-    if (c * kChunk + kChunk <= mlen) fetch(c, raw);
-    prepare(c);
-  }
-  for (; c < c1; c += kDraftWaves) {
-    const int cn = c + kDraftWaves;
-    const bool have_next = cn < c1;
-    if (have_next && cn * kChunk + kChunk <= mlen) fetch(cn, raw);
-    compute(c, ka, va, lg);
-    if (have_next) prepare(cn);
+  for (int k = 0; k < min(kI4Stages - 1, nmine); ++k) issue(k);
+  for (int k = 0; k < nmine; ++k) {
+    wait_chunks_after(min(nmine - 1 - k, kI4Stages - 2));
+    if (k + kI4Stages - 1 < nmine) issue(k + kI4Stages - 1);
+    const uint8_t *st = ring + (k % kI4Stages) * kI4Stage;
+    const int c = first + kDraftWaves * k;
+    if ((c + 1) * kChunk <= mlen) main_chunk(st, c, false);
+    else main_chunk(st, c, true);
   }
 
+  // ---- bf16 tail chunks (tokens mlen + 32 j ...): loads clamped in range and
+  // masked afterwards, so they issue back to back ---------------------------
+  // (The wave's chunks are first + 4 k; those past its int4 ones all lie in
+  // [nmain, c1).)
+  for (int c = first + kDraftWaves * nmine; c < c1; c += kDraftWaves) {
+    const int tb = kChunk * (c - nmain);   // first tail index of this chunk
+    u32x4 ka[2][KS], va[DT];
+#pragma unroll
+    for (int tau = 0; tau < 2; ++tau) {
+      const int t = tb + 8 * (col >> 2) + 4 * tau + (col & 3);
+      const int tc = min(t, tlen - 1);
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const u32x4 w = ld16(tkb + (size_t)tc * D + 32 * grp + 8 * ks);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) ka[tau][ks][j] = pack_f16x2(bf16_lo(w[j]), bf16_hi(w[j]));
+      }
+    }
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      const int d = 16 * dt + col;
+      float x[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[e] = bf16_to_f32(tvb[(size_t)d * p.tcap + min(tb + 8 * grp + e, tlen - 1)]);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) va[dt][j] = pack_f16x2(x[2 * j], x[2 * j + 1]);
+    }
+    f32x4 s[2];
+#pragma unroll
+    for (int tau = 0; tau < 2; ++tau) {
+      s[tau] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) s[tau] = mfma_f16(ka[tau][ks], qh[ks], s[tau]);
+    }
+    float sc[8], pr[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) sc[e] = (tb + 8 * grp + e < tlen) ? s[e >> 2][e & 3] * qs : kNegInf;
+    softmax(sc, pr);
+    u32x4 pp;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) pp[j] = pack_f16x2(pr[2 * j], pr[2 * j + 1]);
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      l_run = sum_f16x2(pp[j], l_run);
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) o[dt] = mfma_f16(va[dt], pp, o[dt]);
+  }
+
+  // ---- merge the 4 waves through LDS (reusing the ring) ------------------
   l_run += __shfl_xor(l_run, 16, 64);
   l_run += __shfl_xor(l_run, 32, 64);
-  __shared__ float sm[kDraftWaves][16], sl[kDraftWaves][16];
-  __shared__ float so[kDraftWaves][D][17];
+  __syncthreads();   // every wave is done with its ring
+  float (*sm)[16] = reinterpret_cast<float (*)[16]>(lds);
+  float (*sl)[16] = reinterpret_cast<float (*)[16]>(lds + kDraftWaves * 16 * sizeof(float));
+  float (*so)[D][17] = reinterpret_cast<float (*)[D][17]>(lds + 2 * kDraftWaves * 16 * sizeof(float));
   if (grp == 0) { sm[wave][col] = m_run; sl[wave][col] = l_run; }
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt)
@@ -659,7 +707,8 @@ hipError_t launch_draft(const vc_draft_args &a, const SplitPlan &pl, hipStream_t
   p.kq = (const uint8_t *)a.k; p.vq = (const uint8_t *)a.v;
   p.ks = a.k_scale; p.kz = a.k_zero; p.vs = a.v_scale; p.vz = a.v_zero;
   dim3 grid(pl.splits, a.B * a.Hkv);
-  if (a.fmt == VC_KV_INT4) draft_bf16_int4<128><<<grid, kDraftWaves * 64, 0, s>>>(p);
+  if (a.fmt == VC_KV_INT4 && a.degree) draft_int4<128, true><<<grid, kDraftWaves * 64, 0, s>>>(p);
+  else if (a.fmt == VC_KV_INT4) draft_int4<128, false><<<grid, kDraftWaves * 64, 0, s>>>(p);
   else if (a.D == 128) draft_bf16_dense<128><<<grid, kDraftWaves * 64, 0, s>>>(p);
   else draft_bf16_dense<64><<<grid, kDraftWaves * 64, 0, s>>>(p);
   hipError_t e = hipGetLastError();
