@@ -348,7 +348,7 @@ def kernel_alone(args):
         B, Hq, Hkv, D, cap = 32, 32, 8, 128, 131072
         import synthetic as S
         kq = S.torch_randint((B, Hkv, cap, D // 2), 0, 256, 5, dev, torch.int32).to(torch.uint8)
-        vq = S.torch_randint((B, Hkv, D, cap // 2), 0, 256, 6, dev, torch.int32).to(torch.uint8)
+        vq = S.torch_randint((B, Hkv, cap // 32, D, 16), 0, 256, 6, dev, torch.int32).to(torch.uint8)
 
         def scales(shape, seed):
             g = torch.Generator(device=dev)
@@ -356,7 +356,7 @@ def kernel_alone(args):
             sc = (torch.rand(shape, generator=g, device=dev) * 0.2 + 0.3).half()
             return sc, (sc.float() * -7.5).half()
         ks, kz = scales((B, Hkv, cap // 32, D), 7)
-        vs, vz = scales((B, Hkv, D // 32, cap), 8)
+        vs, vz = scales((B, Hkv, cap // 32, D // 32, 32), 8)
         q = _bf16_randn((B, Hq, D), 3, dev)
         ml = torch.full((B, Hkv), cap, dtype=torch.int32, device=dev)
         out = torch.empty((B, Hq, D), dtype=torch.bfloat16, device=dev)

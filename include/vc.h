@@ -57,9 +57,10 @@ typedef enum { VC_KV_DENSE = 0, VC_KV_INT4 = 1 } vc_kv_format;
  * The main segment is either dense (bf16/fp32) or int4 group-quantized
  * (the quantizing drafters of "Supporto Architetturale"):
  *   K_hat[t][d] = ck[t][d] * k_scale[t/32][d] + k_zero[t/32][d]
- *   V_hat[d][t] = cv[d][t] * v_scale[d/32][t] + v_zero[d/32][t]
+ *   V_hat[t][d] = cv[t][d] * v_scale[t/32][d/32][t%32] + v_zero[t/32][d/32][t%32]
  * (one K group = one channel over 32 tokens, one V group = one token over 32
- * channels; codes 0..15, scales/zeros binary16).                            */
+ * channels; codes 0..15, scales/zeros binary16).  Everything int4 is laid out
+ * in 32-token blocks, so one block's codes and parameters are contiguous.  */
 typedef struct vc_draft_args {
   int32_t B, Hq, Hkv, D;          /* D in {64, 128}; Hq % Hkv == 0, Hq/Hkv <= 16   */
   int32_t dtype;                  /* vc_dtype of q, dense K/V, tail K/V and out    */
@@ -72,10 +73,12 @@ typedef struct vc_draft_args {
   const int32_t *main_len;        /* [B][Hkv] valid main tokens                    */
   const void    *k;               /* DENSE [B][Hkv][cap][D]; INT4 u8 [B][Hkv][cap][D/2],
                                      two channels per byte, even channel low nibble */
-  const void    *v;               /* DENSE [B][Hkv][D][cap]; INT4 u8 [B][Hkv][D][cap/2],
-                                     two tokens per byte, even token low nibble    */
+  const void    *v;               /* DENSE [B][Hkv][D][cap]; INT4 u8
+                                     [B][Hkv][cap/32][D][16]: per 32-token block,
+                                     channel d's 32 codes, two tokens per byte,
+                                     even token low nibble                         */
   const uint16_t *k_scale, *k_zero; /* INT4 only: fp16 [B][Hkv][cap/32][D]         */
-  const uint16_t *v_scale, *v_zero; /* INT4 only: fp16 [B][Hkv][D/32][cap]         */
+  const uint16_t *v_scale, *v_zero; /* INT4 only: fp16 [B][Hkv][cap/32][D/32][32]  */
   const float   *degree;          /* optional [B][Hd][cap] merge degrees n_t >= 1  */
   int64_t degree_h_stride;        /* 0: one row per request shared by all KV heads;
                                      cap: one row per KV head                      */

@@ -282,8 +282,10 @@ __global__ __launch_bounds__(kDraftWaves * 64) void draft_bf16_dense(DraftParams
 //  * every wave streams its own chunks through a private ring of kI4Stages
 //    LDS stages filled by direct global->LDS loads: per chunk 2 KB of K
 //    codes, 2 KB of V codes and 1 KB of scales/zeros (plus 128 B of merge
-//    degrees when present), four chunks in flight per wave.  No barrier is
-//    needed: a wave only reads what it loaded itself.
+//    degrees when present), two chunks in flight per wave.  No barrier is
+//    needed: a wave only reads what it loaded itself.  Two workgroups share
+//    a CU (63 KB of LDS each, at most 256 registers per lane), so every SIMD
+//    interleaves two waves and 16 chunks (80 KB) per CU are in flight.
 //  * the quantisation is folded into the other MFMA operand, so the VALU
 //    never multiplies an individual code by its scale:
 //      S_t   = sum_d (q_d s_d) c_td + sum_d q_d z_d
@@ -296,8 +298,8 @@ __global__ __launch_bounds__(kDraftWaves * 64) void draft_bf16_dense(DraftParams
 //    into fp16 range with an exact per-head power-of-two scale.
 //  * chunks that reach the bf16 tail or the end of the sequence are
 //    dequantised element-wise after the main loop.
-constexpr int kI4Stages = 5;
-constexpr int kI4Stage = 6 * 1024;   // K codes, V codes, scales/zeros, degree (bytes)
+constexpr int kI4Stages = 3;
+constexpr int kI4Stage = 5 * 1024 + 256;   // K codes, V codes, scales/zeros, degree (bytes)
 
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
@@ -337,7 +339,7 @@ VC_DEVICE void dma16(const void *gptr, uint32_t lds_addr) {
 }
 
 template <int D, bool DEG>
-__global__ __launch_bounds__(kDraftWaves * 64) void draft_int4(DraftParams p) {
+__global__ __launch_bounds__(kDraftWaves * 64, 2) void draft_int4(DraftParams p) {
   constexpr int KS = D / 32, DT = D / 16, NG = D / 32;
   static_assert(D == 128, "int4 draft is compiled for head_dim 128");
   constexpr int kBlk = DEG ? 6 : 5;   // direct loads per chunk per wave
@@ -454,6 +456,8 @@ __global__ __launch_bounds__(kDraftWaves * 64) void draft_int4(DraftParams p) {
   //  block 4:    K scales (4096 + 2 ch), K zeros (4352 + 2 ch), V scales
   //              (4608 + 64 g + 2 t), V zeros (4864 + 64 g + 2 t);
   //  block 5:    merge degrees (5120 + 4 t), lanes 0..7 only.
+  // Every piece is a contiguous run of the 32-token-blocked int4 layout, so
+  // each load uses whole cache lines.
   auto issue = [&](int k) __attribute__((always_inline)) {
     const int c = first + kDraftWaves * k;
     const int base = c * kChunk;
@@ -464,13 +468,13 @@ __global__ __launch_bounds__(kDraftWaves * 64) void draft_int4(DraftParams p) {
       dma16(kqb + (size_t)(base + t) * (D / 2) + 16 * ((lane & 3) ^ ((t >> 3) & 3)), st + 1024 * h);
     }
 #pragma unroll
-    for (int h = 0; h < 2; ++h) dma16(vqb + (size_t)(64 * h + lane) * (p.cap / 2) + base / 2, st + 2048 + 1024 * h);
+    for (int h = 0; h < 2; ++h) dma16(vqb + (size_t)base * (D / 2) + 1024 * h + 16 * lane, st + 2048 + 1024 * h);
     const uint16_t *src;
     const int q = lane & 15;
     if (lane < 16) src = ksb + (size_t)(base / 32) * D + 8 * q;
     else if (lane < 32) src = kzb + (size_t)(base / 32) * D + 8 * q;
-    else if (lane < 48) src = vsb + (size_t)(q >> 2) * p.cap + base + 8 * (q & 3);
-    else src = vzb + (size_t)(q >> 2) * p.cap + base + 8 * (q & 3);
+    else if (lane < 48) src = vsb + (size_t)base * NG + 8 * q;
+    else src = vzb + (size_t)base * NG + 8 * q;
     dma16(src, st + 4096);
     if (DEG) {
       if (lane < 8) dma16(db + base + 4 * lane, st + 5120);
@@ -482,7 +486,7 @@ __global__ __launch_bounds__(kDraftWaves * 64) void draft_int4(DraftParams p) {
     else if (n == 1) __asm__ volatile("s_waitcnt vmcnt(%0)" ::"n"(kBlk) : "memory");
     else __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
   };
-  static_assert(kI4Stages == 5, "wait_chunks_after covers up to 3 chunks in flight");
+  static_assert(kI4Stages <= 5, "wait_chunks_after covers up to 3 chunks in flight");
   const u32x4 negm = u32x4{kNegMagic, kNegMagic, kNegMagic, kNegMagic};
 
   // One int4 chunk from its LDS stage; `masked` drops tokens at or past mlen.

@@ -115,32 +115,40 @@ def int4_grid(B, Hkv, cap, D, cfg_seed, smin=0.3, smax=0.5):
     """Codes uniform on 0..15 and binary16 scales ``s ~ U[smin, smax]``,
     zeros ``z = -7.5 s`` (so reconstructions span about +-3.75).
 
-    Library layouts (uint8 codes, uint16 binary16 bits):
+    Library layouts (uint8 codes, uint16 binary16 bits), all in 32-token
+    blocks:
       ``k_codes [B][Hkv][cap][D/2]`` (two channels per byte, even channel low),
       ``k_scale/k_zero [B][Hkv][cap/32][D]``,
-      ``v_codes [B][Hkv][D][cap/2]`` (channel-major, two tokens per byte,
-      even token low), ``v_scale/v_zero [B][Hkv][D/32][cap]``.
-    Also the unpacked codes ``k_c/v_c [B][Hkv][cap][D]`` (token-major) for
-    the oracle side.
+      ``v_codes [B][Hkv][cap/32][D][16]`` (per block, channel d's 32 tokens,
+      two tokens per byte, even token low),
+      ``v_scale/v_zero [B][Hkv][cap/32][D/32][32]``.
+    Also the token-major forms for the oracle side: unpacked codes
+    ``k_c/v_c [B][Hkv][cap][D]`` and ``v_scale_td/v_zero_td [B][Hkv][cap][D/32]``.
     """
     assert cap % 32 == 0 and D % 32 == 0
+    nb, ng = cap // 32, D // 32
     res = {"k_c": np.empty((B, Hkv, cap, D), np.uint8), "v_c": np.empty((B, Hkv, cap, D), np.uint8),
-           "k_scale": np.empty((B, Hkv, cap // 32, D), np.uint16),
-           "k_zero": np.empty((B, Hkv, cap // 32, D), np.uint16),
-           "v_scale": np.empty((B, Hkv, D // 32, cap), np.uint16),
-           "v_zero": np.empty((B, Hkv, D // 32, cap), np.uint16)}
+           "k_scale": np.empty((B, Hkv, nb, D), np.uint16),
+           "k_zero": np.empty((B, Hkv, nb, D), np.uint16),
+           "v_scale_td": np.empty((B, Hkv, cap, ng), np.uint16),
+           "v_zero_td": np.empty((B, Hkv, cap, ng), np.uint16)}
     for b in range(B):
         for h in range(Hkv):
             res["k_c"][b, h] = rng(cfg_seed, TID["kcode"], b, h).integers(0, 16, (cap, D))
             res["v_c"][b, h] = rng(cfg_seed, TID["vcode"], b, h).integers(0, 16, (cap, D))
-            ks = rng(cfg_seed, TID["kscale"], b, h).uniform(smin, smax, (cap // 32, D)).astype(np.float16)
+            ks = rng(cfg_seed, TID["kscale"], b, h).uniform(smin, smax, (nb, D)).astype(np.float16)
             res["k_scale"][b, h] = ks.view(np.uint16)
             res["k_zero"][b, h] = (ks.astype(np.float32) * np.float32(-7.5)).astype(np.float16).view(np.uint16)
-            vs = rng(cfg_seed, TID["vscale"], b, h).uniform(smin, smax, (D // 32, cap)).astype(np.float16)
-            res["v_scale"][b, h] = vs.view(np.uint16)
-            res["v_zero"][b, h] = (vs.astype(np.float32) * np.float32(-7.5)).astype(np.float16).view(np.uint16)
+            vs = rng(cfg_seed, TID["vscale"], b, h).uniform(smin, smax, (cap, ng)).astype(np.float16)
+            res["v_scale_td"][b, h] = vs.view(np.uint16)
+            res["v_zero_td"][b, h] = (vs.astype(np.float32) * np.float32(-7.5)).astype(np.float16).view(np.uint16)
     res["k_codes"] = pack_codes(res["k_c"])
-    res["v_codes"] = pack_codes(np.ascontiguousarray(np.swapaxes(res["v_c"], -1, -2)))
+    # [cap][D] -> [cap/32][32][D] -> [cap/32][D][32] -> pack token pairs -> [cap/32][D][16]
+    vblk = res["v_c"].reshape(B, Hkv, nb, 32, D).transpose(0, 1, 2, 4, 3)
+    res["v_codes"] = pack_codes(np.ascontiguousarray(vblk))
+    for key in ("v_scale", "v_zero"):
+        td = res[key + "_td"].reshape(B, Hkv, nb, 32, ng).transpose(0, 1, 2, 4, 3)
+        res[key] = np.ascontiguousarray(td)
     return res
 
 

@@ -120,8 +120,8 @@ def _int4_check(B, Hq, Hkv, cap, main_len, tcap, tail_len, deg_mode, seed, split
     for b in range(B):
         for h in range(Hkv):
             k_ref[b, h] = Q.dequantize_k(g["k_c"][b, h], f16_to_f64(g["k_scale"][b, h]), f16_to_f64(g["k_zero"][b, h]))
-            v_ref[b, h] = Q.dequantize_v(g["v_c"][b, h], f16_to_f64(g["v_scale"][b, h]).T,
-                                         f16_to_f64(g["v_zero"][b, h]).T)
+            v_ref[b, h] = Q.dequantize_v(g["v_c"][b, h], f16_to_f64(g["v_scale_td"][b, h]),
+                                         f16_to_f64(g["v_zero_td"][b, h]))
     tk_ref = tv_ref = tk_dev = tv_dev = None
     if tcap:
         tkb, tvb = S.f32_to_bf16_bits(tkf), S.f32_to_bf16_bits(tvf)
