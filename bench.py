@@ -113,7 +113,7 @@ class Cohort:
         self.NLD = NLD
         # compressed cache (draft role), one buffer per distinct layer
         self.K = [_bf16_randn((B, Hkv, c.cap, D), seed + 10 + i, dev) for i in range(NLD)]
-        self.Vt = [_bf16_randn((B, Hkv, D, c.cap), seed + 40 + i, dev) for i in range(NLD)]
+        self.Vt = [_bf16_randn((B, Hkv, c.cap // 32, D, 32), seed + 40 + i, dev) for i in range(NLD)]   # blocked
         self.deg = [S.torch_randint((B, 1, c.cap), 1, 5, seed + 70 + i, dev, torch.int32).float() for i in range(NLD)]
         self.len = torch.full((L, B, Hkv), c.Lc, dtype=torch.int32, device=dev)
         self.tail_k = _bf16_randn((B, Hkv, c.k, D), seed + 100, dev)
@@ -243,7 +243,7 @@ def run_stagger(args, t_start):
         for l in range(L):
             j = l % NLD
             vc.commit_rows(Xc.bk[j], Xc.bv[j], n_out, Xc.K[j], Xc.Vt[j], Xc.len[l], degree=Xc.deg[j],
-                           stream=ver_s)
+                           v_blocked=True, stream=ver_s)
             stg.writeback(host_commit[l, 0], Xc.bk[j], blk_bytes, ver_s)
             stg.writeback(host_commit[l, 1], Xc.bv[j], blk_bytes, ver_s)
         torch.cuda.synchronize()
@@ -371,7 +371,7 @@ def kernel_alone(args):
         B, Hq, Hkv, D, cap = 32, 32, 8, 128, 32768
         nset = 1   # 4.3 GB per set >> MALL
         K = _bf16_randn((B, Hkv, cap, D), 1, dev)
-        Vt = _bf16_randn((B, Hkv, D, cap), 2, dev)
+        Vt = _bf16_randn((B, Hkv, cap // 32, D, 32), 2, dev)   # 32-token blocks
         q = _bf16_randn((B, Hq, D), 3, dev)
         import synthetic as S
         deg = S.torch_randint((B, 1, cap), 1, 5, 4, dev, torch.int32).float()

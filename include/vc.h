@@ -73,7 +73,8 @@ typedef struct vc_draft_args {
   const int32_t *main_len;        /* [B][Hkv] valid main tokens                    */
   const void    *k;               /* DENSE [B][Hkv][cap][D]; INT4 u8 [B][Hkv][cap][D/2],
                                      two channels per byte, even channel low nibble */
-  const void    *v;               /* DENSE [B][Hkv][D][cap]; INT4 u8
+  const void    *v;               /* DENSE [B][Hkv][cap/32][D][32]: 32-token
+                                     blocks, channel-major inside a block; INT4 u8
                                      [B][Hkv][cap/32][D][16]: per 32-token block,
                                      channel d's 32 codes, two tokens per byte,
                                      even token low nibble                         */
@@ -165,13 +166,16 @@ vc_status vc_lm_head(int32_t R, int32_t Dm, int32_t V, const void *h, const void
  * x0, d_1..d_n -- the first n_out[b] rows of the block -- to a cache at its
  * current length, and advance the length.
  *   blk_k [B][Hkv][M][D], blk_v [B][Hkv][D][M]        (dtype)
- *   dst_k [B][Hkv][cap][D], dst_v [B][Hkv][D][cap]    (dtype)
+ *   dst_k [B][Hkv][cap][D]                            (dtype)
+ *   dst_v [B][Hkv][D][cap] when dst_v_blocked = 0 (a full cache, as
+ *         vc_verify_attn reads it), [B][Hkv][cap/32][D][32] when it is 1 (a
+ *         compressed main segment, as vc_draft_attn reads it; cap % 32 == 0)
  *   len [B][Hkv] (in/out), n_out [B]
  *   degree: optional [B][Hd][cap] (Hd = 1 when degree_h_stride = 0, else
  *   Hkv); appended rows get degree 1.
  * Rows past cap are dropped (the length saturates at cap).                 */
 vc_status vc_commit_rows(int32_t B, int32_t Hkv, int32_t D, int32_t M, int32_t dtype, int64_t cap,
-                         const void *blk_k, const void *blk_v, const int32_t *n_out,
+                         int32_t dst_v_blocked, const void *blk_k, const void *blk_v, const int32_t *n_out,
                          void *dst_k, void *dst_v, int32_t *len, float *degree,
                          int64_t degree_h_stride, void *stream);
 

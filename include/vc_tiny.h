@@ -86,9 +86,11 @@ vc_status vc_tiny_forward(const vc_tiny_model *m, int32_t R, const int32_t *toke
 
 /* Compressed-cache construction for a token-eviction compressor: copy the
  * rows at positions idx[0..n-1] (device, ascending) of a cache into a
- * compacted cache, per KV head: dst_k[h][j] = src_k[h][idx[j]],
- * dst_v[h][:][j] = src_v[h][:][idx[j]]; sets dst_len[h] = n (device [Hkv]).
- * K token-major [Hkv][cap][D], V channel-major [Hkv][D][cap]; fp32.        */
+ * compacted cache, per KV head: dst_k[h][j] = src_k[h][idx[j]], dst_v of
+ * row j = column idx[j] of src_v; sets dst_len[h] = n (device [Hkv]).
+ * K token-major [Hkv][cap][D]; source V channel-major [Hkv][D][src_cap]
+ * (a full cache), destination V in the draft main-segment layout
+ * [Hkv][dst_cap/32][D][32] (dst_cap % 32 == 0); fp32.                       */
 vc_status vc_gather_rows(int32_t Hkv, int32_t D, int32_t n, const int32_t *idx, const float *src_k,
                          const float *src_v, int64_t src_cap, float *dst_k, float *dst_v, int64_t dst_cap,
                          int32_t *dst_len, void *stream);

@@ -94,7 +94,7 @@ def lib():
         L.vc_argmax.restype = ctypes.c_int
         L.vc_lm_head.argtypes = [_i32, _i32, _i32, _p, _p, _p, _p]
         L.vc_lm_head.restype = ctypes.c_int
-        L.vc_commit_rows.argtypes = [_i32, _i32, _i32, _i32, _i32, _i64, _p, _p, _p, _p, _p, _p, _p, _i64, _p]
+        L.vc_commit_rows.argtypes = [_i32, _i32, _i32, _i32, _i32, _i64, _i32, _p, _p, _p, _p, _p, _p, _p, _i64, _p]
         L.vc_commit_rows.restype = ctypes.c_int
         L.vc_stagger_create.argtypes = [ctypes.POINTER(_p), ctypes.POINTER(_p), _i32, ctypes.c_size_t, _i32]
         L.vc_stagger_stream_layer.argtypes = [_p, _i32, _p, ctypes.c_size_t]
@@ -189,7 +189,8 @@ def draft_attn(q, k, v, main_len, degree=None, tail_k=None, tail_v=None, tail_le
                stream=None):
     """Draft decode attention (``vc_draft_attn``).
 
-    ``q [B][Hq][D]``; dense ``k [B][Hkv][cap][D]``, ``v [B][Hkv][D][cap]``;
+    ``q [B][Hq][D]``; dense ``k [B][Hkv][cap][D]``, ``v [B][Hkv][cap/32][D][32]``
+    (32-token blocks, channel-major inside a block);
     ``main_len`` int32 ``[B][Hkv]``; ``degree`` fp32 ``[B][1 or Hkv][cap]``;
     ``tail_k [B][Hkv][tcap][D]``, ``tail_v [B][Hkv][D][tcap]``, ``tail_len``
     int32 ``[B]``.  Returns ``out [B][Hq][D]`` (and fills ``out_lse``).
@@ -313,11 +314,13 @@ def lm_head(h, w, logits=None, stream=None):
     return logits
 
 
-def commit_rows(blk_k, blk_v, n_out, dst_k, dst_v, length, degree=None, stream=None):
+def commit_rows(blk_k, blk_v, n_out, dst_k, dst_v, length, degree=None, v_blocked=False, stream=None):
     """Append the first ``n_out[b]`` block rows to a cache (``vc_commit_rows``).
 
     ``blk_k [B][Hkv][M][D]``, ``blk_v [B][Hkv][D][M]``, ``dst_k [B][Hkv][cap][D]``,
-    ``dst_v [B][Hkv][D][cap]``, ``length`` int32 ``[B][Hkv]`` (updated in place).
+    ``dst_v [B][Hkv][D][cap]`` (a full cache) or, with ``v_blocked``,
+    ``[B][Hkv][cap/32][D][32]`` (a compressed main segment), ``length`` int32
+    ``[B][Hkv]`` (updated in place).
     """
     for t, n in ((blk_k, "blk_k"), (blk_v, "blk_v"), (dst_k, "dst_k"), (dst_v, "dst_v"), (degree, "degree")):
         _dev(t, n)
@@ -326,7 +329,7 @@ def commit_rows(blk_k, blk_v, n_out, dst_k, dst_v, length, degree=None, stream=N
     B, Hkv, M, D = blk_k.shape
     cap = dst_k.shape[2]
     hstride = 0 if degree is None or degree.shape[1] == 1 else cap
-    _check(lib().vc_commit_rows(B, Hkv, D, M, _vc_dtype(blk_k), cap, _ptr(blk_k), _ptr(blk_v), _ptr(n_out),
+    _check(lib().vc_commit_rows(B, Hkv, D, M, _vc_dtype(blk_k), cap, 1 if v_blocked else 0, _ptr(blk_k), _ptr(blk_v), _ptr(n_out),
                                 _ptr(dst_k), _ptr(dst_v), _ptr(length), _ptr(degree), hstride, _stream(stream)))
 
 

@@ -198,15 +198,18 @@ vc_status vc_lm_head(int32_t R, int32_t Dm, int32_t V, const void *h, const void
 }
 
 vc_status vc_commit_rows(int32_t B, int32_t Hkv, int32_t D, int32_t M, int32_t dtype, int64_t cap,
-                         const void *blk_k, const void *blk_v, const int32_t *n_out, void *dst_k, void *dst_v,
+                         int32_t dst_v_blocked, const void *blk_k, const void *blk_v, const int32_t *n_out,
+                         void *dst_k, void *dst_v,
                          int32_t *len, float *degree, int64_t degree_h_stride, void *stream) {
   REQ(B >= 0 && Hkv >= 1 && D >= 1 && M >= 1 && cap >= 0, "bad commit shape");
   REQ(dtype == VC_BF16 || dtype == VC_FP32, "unknown dtype %d", dtype);
+  REQ(dst_v_blocked == 0 || dst_v_blocked == 1, "dst_v_blocked must be 0 or 1");
+  REQ(!dst_v_blocked || cap % 32 == 0, "a blocked V cache needs cap %% 32 == 0");
   if (B == 0) return VC_OK;
   REQ(blk_k && blk_v && n_out && dst_k && dst_v && len, "null pointer");
   REQ(!degree || degree_h_stride == 0 || degree_h_stride == cap, "degree_h_stride must be 0 or cap");
   const int64_t deg_b = degree_h_stride ? degree_h_stride * Hkv : cap;
-  return hip_status(vc::launch_commit(B, Hkv, D, M, dtype == VC_BF16 ? 2 : 4, cap, blk_k, blk_v, n_out, dst_k,
+  return hip_status(vc::launch_commit(B, Hkv, D, M, dtype == VC_BF16 ? 2 : 4, cap, dst_v_blocked, blk_k, blk_v, n_out, dst_k,
                                       dst_v, len, degree, deg_b, degree_h_stride, (hipStream_t)stream),
                     "vc_commit_rows launch");
 }

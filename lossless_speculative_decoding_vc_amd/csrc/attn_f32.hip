@@ -18,8 +18,9 @@ struct F32Params {
   int Hq, Hkv, G, M, D;
   float qk_scale;
   const float *q;                    // [B][M][Hq][D]
-  const float *ak, *av;              // segment A: K [acap][D], V [D][acap] per (b, kvh)
-  int64_t acap;
+  const float *ak, *av;              // segment A: K [acap][D] per (b, kvh); V [D][acap] (verify
+  int64_t acap;                      // context) or [acap/32][D][32] (draft main segment)
+  int av_blocked;
   const int32_t *alen;               // per (b, kvh) if alen_per_head else per b
   int alen_per_head;
   const float *deg;                  // optional, per token of segment A
@@ -86,7 +87,9 @@ __global__ __launch_bounds__(64) void attn_f32(F32Params p) {
       float a2 = acc[e] * alpha;
       for (int j = 0; j < n; ++j) {
         const int tt = t0 + j;
-        const float v = (tt < la) ? av[(size_t)d * p.acap + tt] : bv[(size_t)d * p.bcap + (tt - la)];
+        const float v = (tt < la) ? av[p.av_blocked ? (size_t)(tt >> 5) * D * 32 + d * 32 + (tt & 31)
+                                                   : (size_t)d * p.acap + tt]
+                                  : bv[(size_t)d * p.bcap + (tt - la)];
         a2 = fmaf(ps[j], v, a2);
       }
       acc[e] = a2;
@@ -109,7 +112,7 @@ hipError_t launch_draft_f32(const vc_draft_args &a, hipStream_t s) {
   p.Hq = a.Hq; p.Hkv = a.Hkv; p.G = a.Hq / a.Hkv; p.M = 1; p.D = a.D;
   p.qk_scale = a.scale * kLog2e;
   p.q = (const float *)a.q;
-  p.ak = (const float *)a.k; p.av = (const float *)a.v; p.acap = a.cap;
+  p.ak = (const float *)a.k; p.av = (const float *)a.v; p.acap = a.cap; p.av_blocked = 1;
   p.alen = a.main_len; p.alen_per_head = 1;
   p.deg = a.degree;
   p.deg_h_stride = a.degree_h_stride;

@@ -4,7 +4,8 @@
 // restarts from the last accepted token, so the verified K/V rows of the
 // accepted block prefix (x0, d_1..d_n: n_out = n + 1 rows) join the cache.
 // One workgroup per (request, KV head): it reads the current length, copies
-// the rows (K token-major, V channel-major) and advances the length.  Rows
+// the rows (K token-major; V channel-major for a full cache, or in 32-token
+// blocks for a compressed main segment) and advances the length.  Rows
 // beyond the capacity are dropped.  Reads n_out from device memory, so no
 // host synchronisation sits between acceptance and commit.
 #include "common.h"
@@ -14,7 +15,7 @@ namespace vc {
 namespace {
 
 template <typename T>
-__global__ __launch_bounds__(256) void commit_rows(int Hkv, int D, int M, int64_t cap,
+__global__ __launch_bounds__(256) void commit_rows(int Hkv, int D, int M, int64_t cap, int v_blocked,
                                                    const T *__restrict__ blk_k, const T *__restrict__ blk_v,
                                                    const int32_t *__restrict__ n_out, T *__restrict__ dst_k,
                                                    T *__restrict__ dst_v, int32_t *__restrict__ len,
@@ -30,11 +31,12 @@ __global__ __launch_bounds__(256) void commit_rows(int Hkv, int D, int M, int64_
   const T *sk = blk_k + (size_t)bh * M * D;
   const T *sv = blk_v + (size_t)bh * D * M;
   T *dk = dst_k + ((size_t)bh * cap + L) * D;
-  T *dv = dst_v + (size_t)bh * D * cap + L;
+  T *dv = dst_v + (size_t)bh * D * cap;
   for (int e = threadIdx.x; e < n * D; e += blockDim.x) dk[e] = sk[e];
   for (int e = threadIdx.x; e < n * D; e += blockDim.x) {
-    const int d = e / n, r = e % n;
-    dv[(size_t)d * cap + r] = sv[(size_t)d * M + r];
+    const int d = e / n, r = e % n, t = L + r;
+    const size_t at = v_blocked ? (size_t)(t >> 5) * D * 32 + d * 32 + (t & 31) : (size_t)d * cap + t;
+    dv[at] = sv[(size_t)d * M + r];
   }
   if (degree) {
     float *dg = degree + b * deg_b_stride + h * deg_h_stride + L;
@@ -46,16 +48,16 @@ __global__ __launch_bounds__(256) void commit_rows(int Hkv, int D, int M, int64_
 
 }  // namespace
 
-hipError_t launch_commit(int B, int Hkv, int D, int M, int elem_bytes, int64_t cap, const void *blk_k,
+hipError_t launch_commit(int B, int Hkv, int D, int M, int elem_bytes, int64_t cap, int v_blocked, const void *blk_k,
                          const void *blk_v, const int32_t *n_out, void *dst_k, void *dst_v, int32_t *len,
                          float *degree, int64_t deg_b_stride, int64_t deg_h_stride, hipStream_t s) {
   if (B == 0) return hipSuccess;
   if (elem_bytes == 2)
-    commit_rows<uint16_t><<<B * Hkv, 256, 0, s>>>(Hkv, D, M, cap, (const uint16_t *)blk_k, (const uint16_t *)blk_v,
+    commit_rows<uint16_t><<<B * Hkv, 256, 0, s>>>(Hkv, D, M, cap, v_blocked, (const uint16_t *)blk_k, (const uint16_t *)blk_v,
                                                   n_out, (uint16_t *)dst_k, (uint16_t *)dst_v, len, degree,
                                                   deg_b_stride, deg_h_stride);
   else
-    commit_rows<float><<<B * Hkv, 256, 0, s>>>(Hkv, D, M, cap, (const float *)blk_k, (const float *)blk_v, n_out,
+    commit_rows<float><<<B * Hkv, 256, 0, s>>>(Hkv, D, M, cap, v_blocked, (const float *)blk_k, (const float *)blk_v, n_out,
                                                (float *)dst_k, (float *)dst_v, len, degree, deg_b_stride,
                                                deg_h_stride);
   return hipGetLastError();

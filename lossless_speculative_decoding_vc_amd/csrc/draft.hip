@@ -10,6 +10,8 @@
 //  * grid (splits, B*Hkv); 4 waves per workgroup; every wave serves ALL
 //    G = Hq/Hkv query heads of its KV head, so each K/V byte is read from
 //    HBM exactly once per call.
+//  * the main segment's V is stored in 32-token blocks (channel-major inside
+//    a block), so one chunk's V is a contiguous 8 KB run at head_dim 128.
 //  * a wave walks 32-token chunks, the next chunk's loads in flight while
 //    the current one is computed.  Both contractions run on
 //    v_mfma_f32_16x16x32_bf16 with operands loaded straight from HBM into
@@ -117,7 +119,7 @@ __global__ __launch_bounds__(kDraftWaves * 64) void draft_bf16_dense(DraftParams
         for (int ks = 0; ks < KS; ++ks) ch.ka[tau][ks] = ld16(kb + (size_t)t * D + 32 * ks + 8 * grp);
       }
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) ch.va[dt] = ld16(vb + (size_t)(16 * dt + col) * p.cap + base + 8 * grp);
+      for (int dt = 0; dt < DT; ++dt) ch.va[dt] = ld16(vb + (size_t)base * D + (16 * dt + col) * kChunk + 8 * grp);
       if (db) {
         const f32x4 *dp = reinterpret_cast<const f32x4 *>(db + base + 8 * grp);
         const f32x4 d0 = dp[0], d1 = dp[1];
@@ -153,7 +155,7 @@ __global__ __launch_bounds__(kDraftWaves * 64) void draft_bf16_dense(DraftParams
           for (int u = 0; u < 2; ++u) {
             const int t = base + 8 * grp + 2 * e2 + u;
             uint16_t x = 0;
-            if (t < mlen) x = vb[(size_t)d * p.cap + t];
+            if (t < mlen) x = vb[(size_t)(t / kChunk) * D * kChunk + d * kChunk + (t % kChunk)];
             else if (t < total) x = tvb[(size_t)d * p.tcap + (t - mlen)];
             h[u] = x;
           }

@@ -20,7 +20,7 @@ SplitPlan plan_verify(const vc_verify_args &a);
 hipError_t launch_accept(const vc_accept_args &a, hipStream_t s);
 hipError_t launch_argmax(int rows, int V, int dtype, const void *logits, int *out, int out_stride,
                          hipStream_t s);
-hipError_t launch_commit(int B, int Hkv, int D, int M, int elem_bytes, int64_t cap, const void *blk_k,
+hipError_t launch_commit(int B, int Hkv, int D, int M, int elem_bytes, int64_t cap, int v_blocked, const void *blk_k,
                          const void *blk_v, const int32_t *n_out, void *dst_k, void *dst_v, int32_t *len,
                          float *degree, int64_t deg_b_stride, int64_t deg_h_stride, hipStream_t s);
 hipError_t launch_draft(const vc_draft_args &a, const SplitPlan &p, hipStream_t s);

@@ -123,7 +123,7 @@ __global__ __launch_bounds__(256) void gather_rows(int D, int n, const int32_t *
     int p = idx[j];
     p = p < 0 ? 0 : (p >= scap ? (int)scap - 1 : p);
     dkh[(size_t)j * D + d] = skh[(size_t)p * D + d];
-    dvh[(size_t)d * dcap + j] = svh[(size_t)d * scap + p];
+    dvh[(size_t)(j >> 5) * D * 32 + d * 32 + (j & 31)] = svh[(size_t)d * scap + p];
   }
   if (threadIdx.x == 0) dlen[h] = n;
 }
@@ -265,8 +265,8 @@ vc_status vc_tiny_forward(const vc_tiny_model *m, int32_t R, const int32_t *toke
 vc_status vc_gather_rows(int32_t Hkv, int32_t D, int32_t n, const int32_t *idx, const float *src_k,
                          const float *src_v, int64_t src_cap, float *dst_k, float *dst_v, int64_t dst_cap,
                          int32_t *dst_len, void *stream) {
-  if (Hkv < 1 || D < 1 || n < 0 || n > dst_cap || src_cap < 1 || !idx || !src_k || !src_v || !dst_k || !dst_v ||
-      !dst_len)
+  if (Hkv < 1 || D < 1 || n < 0 || n > dst_cap || dst_cap % 32 != 0 || src_cap < 1 || !idx || !src_k || !src_v ||
+      !dst_k || !dst_v || !dst_len)
     return vc::set_error(VC_EINVAL, "bad gather arguments");
   vc::gather_rows<<<Hkv, 256, 0, (hipStream_t)stream>>>(D, n, idx, src_k, src_v, src_cap, dst_k, dst_v, dst_cap,
                                                         dst_len);

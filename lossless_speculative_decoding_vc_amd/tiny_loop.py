@@ -132,7 +132,7 @@ class TinyVeriCache:
         self.full_len = [torch.zeros((1, Hkv), dtype=torch.int32, device=dev) for _ in range(self.nl)]
         self.ccap = self.cap if compressor == "identity" else _ceil64(sinks + recent + max_tokens // stride + 1)
         self.comp_k = [z(1, Hkv, self.ccap, D) for _ in range(self.nl)]
-        self.comp_v = [z(1, Hkv, D, self.ccap) for _ in range(self.nl)]
+        self.comp_v = [z(1, Hkv, self.ccap // 32, D, 32) for _ in range(self.nl)]   # 32-token blocks
         self.comp_len = torch.zeros((1, Hkv), dtype=torch.int32, device=dev)
         self.tail_k = [z(1, Hkv, max(k, 1), D) for _ in range(self.nl)]
         self.tail_v = [z(1, Hkv, D, max(k, 1)) for _ in range(self.nl)]

@@ -42,3 +42,12 @@ def rel_l2(got, ref):
     got = np.asarray(got, dtype=np.float64)
     ref = np.asarray(ref, dtype=np.float64)
     return float(np.linalg.norm(got - ref) / max(np.linalg.norm(ref), 1e-300))
+
+
+def blocked32(x):
+    """Token-major ``[..., cap, D]`` -> the draft main-segment V layout
+    ``[..., cap/32, D, 32]`` (32-token blocks, channel-major inside)."""
+    x = np.asarray(x)
+    *lead, cap, D = x.shape
+    assert cap % 32 == 0
+    return np.ascontiguousarray(x.reshape(*lead, cap // 32, 32, D).swapaxes(-1, -2))

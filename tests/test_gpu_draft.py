@@ -8,7 +8,7 @@ import synthetic as S
 from oracle import attention as A
 from oracle.formats import bf16_to_f64
 
-from .helpers import TOL, assert_close, bf16_dev_to_f64, rel_l2, to_dev, to_dev_bf16
+from .helpers import TOL, assert_close, bf16_dev_to_f64, blocked32, rel_l2, to_dev, to_dev_bf16
 
 pytestmark = pytest.mark.gpu
 
@@ -26,19 +26,20 @@ def _case(B, Hq, Hkv, D, cap, main_len, tcap, tail_len, dtype, deg_mode, seed, q
     elif deg_mode == "per_head":
         deg = S.degrees((B, Hkv, cap), seed)
     dev, ref = {}, {}
-    for name, arr, chan_major in (("q", qf, False), ("k", kf, False), ("v", vf, True),
-                                  ("tail_k", tkf, False), ("tail_v", tvf, True)):
+    # main V in 32-token blocks, tail V channel-major
+    for name, arr, lay in (("q", qf, None), ("k", kf, None), ("v", vf, "blocked"),
+                           ("tail_k", tkf, None), ("tail_v", tvf, "chan")):
         if arr is None:
             dev[name] = ref[name] = None
             continue
         if dtype == "bf16":
             bits = S.f32_to_bf16_bits(arr)
             ref[name] = bf16_to_f64(bits)
-            dbits = np.swapaxes(bits, -1, -2) if chan_major else bits
+            dbits = blocked32(bits) if lay == "blocked" else (np.swapaxes(bits, -1, -2) if lay == "chan" else bits)
             dev[name] = to_dev_bf16(np.ascontiguousarray(dbits))
         else:
             ref[name] = arr.astype(np.float64)
-            darr = np.swapaxes(arr, -1, -2) if chan_major else arr
+            darr = blocked32(arr) if lay == "blocked" else (np.swapaxes(arr, -1, -2) if lay == "chan" else arr)
             dev[name] = to_dev(np.ascontiguousarray(darr))
     ml = np.asarray(main_len, np.int32).reshape(B, Hkv)
     tl = None if tcap == 0 else np.asarray(tail_len, np.int32).reshape(B)

@@ -41,8 +41,8 @@ def test_lm_head_matches_fp64():
     assert_close(out.cpu().numpy(), ref, 1e-4, "logits")
 
 
-@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
-def test_commit_rows(dtype):
+@pytest.mark.parametrize("dtype,v_blocked", [("bf16", False), ("fp32", False), ("bf16", True), ("fp32", True)])
+def test_commit_rows(dtype, v_blocked):
     import torch
     import lossless_speculative_decoding_vc_amd as vc
     B, Hkv, M, D, cap = 3, 2, 9, 64, 128
@@ -52,13 +52,19 @@ def test_commit_rows(dtype):
     bv = torch.randn((B, Hkv, D, M), device="cuda").to(tdt)
     K = torch.randn((B, Hkv, cap, D), device="cuda").to(tdt)
     Vt = torch.randn((B, Hkv, D, cap), device="cuda").to(tdt)
+    if v_blocked:   # [cap/32][D][32]; Vt stays the channel-major view of the same values
+        Vdst = Vt.reshape(B, Hkv, D, cap // 32, 32).permute(0, 1, 3, 2, 4).contiguous()
+    else:
+        Vdst = Vt
     deg = torch.full((B, 1, cap), 3.0, device="cuda")
     L0 = np.array([[10, 10], [120, 120], [0, 0]], np.int32)
     n_out = np.array([4, 9, 1], np.int32)
     length = to_dev(L0)
     K0, V0, D0 = K.cpu().clone(), Vt.cpu().clone(), deg.cpu().clone()
-    vc.commit_rows(bk, bv, to_dev(n_out), K, Vt, length, degree=deg)
+    vc.commit_rows(bk, bv, to_dev(n_out), K, Vdst, length, degree=deg, v_blocked=v_blocked)
     torch.cuda.synchronize()
+    if v_blocked:
+        Vt = Vdst.permute(0, 1, 3, 2, 4).reshape(B, Hkv, D, cap)
     exp_len = np.minimum(L0 + n_out[:, None], cap)
     np.testing.assert_array_equal(length.cpu().numpy(), exp_len)
     Kh, Vh, Dh = K.cpu(), Vt.cpu(), deg.cpu()
