@@ -75,21 +75,36 @@ class Cfg:
     Dm = 5120
 
 
+KERNEL_OF = {
+    "draft128k": "vc_draft_attn: draft_bf16_dense + combine_splits",
+    "draft128k_int4": "vc_draft_attn: draft_int4 + combine_splits",
+    "verify32k": "vc_verify_attn: verify_bf16 + combine_splits",
+    "verify128k": "vc_verify_attn: verify_bf16 + combine_splits",
+    "copy1g": "torch copy_ (1 GiB device to device)",
+}
+
+
 def measured_traffic(key):
-    """HBM bytes per launch from the committed PMC summary, if it was taken
-    on the current draft kernel source (else None)."""
+    """HBM bytes per launch from the committed PMC summaries under profiles/
+    (``*_hbm_traffic.txt``), if the summary holding ``key`` was taken on the
+    current source of its kernel (else None)."""
+    import glob
     import hashlib
     root = os.path.dirname(os.path.abspath(__file__))
-    prof = os.path.join(root, "profiles", "draft_attn_hbm_traffic.txt")
-    src = os.path.join(root, "lossless_speculative_decoding_vc_amd", "csrc", "draft.hip")
-    try:
-        kv = dict(l.split(": ", 1) for l in open(prof).read().splitlines() if ": " in l and not l.startswith("#"))
-        sha = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
-        if kv.get("kernel_source_sha256_16", "").strip() != sha:
+    for prof in sorted(glob.glob(os.path.join(root, "profiles", "*_hbm_traffic.txt"))):
+        try:
+            kv = dict(l.split(": ", 1) for l in open(prof).read().splitlines()
+                      if ": " in l and not l.startswith("#"))
+            if key not in kv:
+                continue
+            src = os.path.join(root, kv["kernel_source"].strip())
+            sha = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+            if kv.get("kernel_source_sha256_16", "").strip() != sha:
+                return None
+            return float(kv[key])
+        except (OSError, KeyError, ValueError):
             return None
-        return float(kv[key])
-    except (OSError, KeyError, ValueError):
-        return None
+    return None
 
 
 def log(msg):
@@ -470,7 +485,10 @@ def main():
                "higher_is_better": False, "n_gpus": 1, "steps": args.iters, "warmup": 5,
                "dtype": "bf16", "data": "synthetic",
                "roofline": {"bound": "hbm", "achieved": r["gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                            "frac": r["gbs"] / HBM_PEAK_GBS, "traffic": None},
+                            "frac": r["gbs"] / HBM_PEAK_GBS,
+                            "traffic": measured_traffic(f"{args.workload}_traffic_bytes_per_launch"),
+                            "kernel": KERNEL_OF.get(args.workload), "bytes_per_launch": r["nbytes"],
+                            "avg_us": r["avg_us"]},
                "mfma": {"achieved": r["tflops"], "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                         "frac": r["tflops"] / MFMA_BF16_PEAK_TFLOPS},
                "config": {"workload": args.workload, "splits": args.splits}}
