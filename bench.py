@@ -27,9 +27,15 @@ kernel's roofline (draft attention, HBM-bound), the verify kernel's MFMA
 utilisation, PCIe GB/s, the staggered-vs-bulk-synchronous comparison and the
 CPU oracle timed on a bounded sample of the same workload.
 
-``--workload verify32k`` / ``draft128k`` time the attention kernels alone
-(Llama-70B verify layer at 32K context; batch-32 draft over a 25% compressed
-128K context).
+``--workload <leg>`` times one attention call alone, inputs resident in HBM
+(at least two rotating input sets, each larger than the 256 MB MALL):
+  verify32k      Llama-70B verify layer at 32K context, block of 32
+  verify128k     the staggered batch's verifying cohort (16 requests, 131072)
+  verify1m       one layer of the 1M-token configuration (block of 41)
+  draft128k      batch-32 draft over a 25% compressed 128K context + degrees
+  draft128k_int4 batch-32 draft over int4 K/V of all 131072 tokens
+  draft1m_int4   the 1M-token configuration's int4 drafter
+  copy1g         a 1 GiB device copy (reference for the HBM byte counters)
 """
 import argparse
 import json
@@ -50,7 +56,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=2)
     ap.add_argument("--warmup", type=int, default=1)
     ap.add_argument("--workload", default="stagger128k",
-                    choices=["stagger128k", "verify32k", "verify128k", "draft128k", "draft128k_int4", "copy1g"])
+                    choices=["stagger128k", "verify32k", "verify128k", "verify1m", "draft128k", "draft128k_int4",
+                             "draft1m_int4", "copy1g"])
     ap.add_argument("--layers", type=int, default=64)
     ap.add_argument("--distinct-layers", type=int, default=16,
                     help="distinct compressed-cache buffers per cohort (layers rotate over them)")
@@ -78,6 +85,8 @@ class Cfg:
 KERNEL_OF = {
     "draft128k": "vc_draft_attn: draft_bf16_dense + combine_splits",
     "draft128k_int4": "vc_draft_attn: draft_int4 + combine_splits",
+    "draft1m_int4": "vc_draft_attn: draft_int4 + combine_splits",
+    "verify1m": "vc_verify_attn: verify_bf16 + combine_splits",
     "verify32k": "vc_verify_attn: verify_bf16 + combine_splits",
     "verify128k": "vc_verify_attn: verify_bf16 + combine_splits",
     "copy1g": "torch copy_ (1 GiB device to device)",
@@ -336,12 +345,15 @@ def kernel_alone(args):
     import lossless_speculative_decoding_vc_amd as vc
     dev = "cuda"
     s = torch.cuda.current_stream()
-    if args.workload in ("verify32k", "verify128k"):
+    if args.workload in ("verify32k", "verify128k", "verify1m"):
         if args.workload == "verify32k":   # Llama-70B layer shape, one request, k = 32
             B, Hq, Hkv, D, N, M = 1, 64, 8, 128, 32768, 32
             nset = 5
-        else:   # verifying cohort of the staggered batch: Qwen-32B layer shape, 16 requests, k = 32
+        elif args.workload == "verify128k":   # verifying cohort of the staggered batch: Qwen-32B layer, 16 requests
             B, Hq, Hkv, D, N, M = 16, 40, 8, 128, 131072, 33
+            nset = 2
+        else:   # one layer of the 1M-token configuration: Mistral-24B layer shape, one request, k = 40
+            B, Hq, Hkv, D, N, M = 1, 32, 8, 128, 1048576, 41
             nset = 2
         sets = [dict(q=_bf16_randn((B, M, Hq, D), 10 + i, dev), k=_bf16_randn((B, Hkv, N, D), 20 + i, dev),
                      v=_bf16_randn((B, Hkv, D, N), 30 + i, dev), bk=_bf16_randn((B, Hkv, M, D), 40 + i, dev),
@@ -358,9 +370,11 @@ def kernel_alone(args):
         nbytes = B * Hkv * (N + M) * D * 4 + 2 * B * M * Hq * D * 2
     elif args.workload == "copy1g":
         pass
-    elif args.workload == "draft128k_int4":
-        # batch 32, int4 K/V over all 131072 tokens (4 of 16 bits = 25%)
-        B, Hq, Hkv, D, cap = 32, 32, 8, 128, 131072
+    elif args.workload in ("draft128k_int4", "draft1m_int4"):
+        if args.workload == "draft128k_int4":   # batch 32, int4 K/V over all 131072 tokens (4 of 16 bits = 25%)
+            B, Hq, Hkv, D, cap = 32, 32, 8, 128, 131072
+        else:   # drafter of the 1M-token configuration: one request, int4 over 1048576 tokens
+            B, Hq, Hkv, D, cap = 1, 32, 8, 128, 1048576
         import synthetic as S
         kq = S.torch_randint((B, Hkv, cap, D // 2), 0, 256, 5, dev, torch.int32).to(torch.uint8)
         vq = S.torch_randint((B, Hkv, cap // 32, D, 16), 0, 256, 6, dev, torch.int32).to(torch.uint8)

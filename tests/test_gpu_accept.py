@@ -77,3 +77,15 @@ def test_negative_zero_equals_positive_zero():
     logits[0, 0, 3] = -0.0
     logits[0, 0, 5] = 0.0
     _run(logits, np.array([[3]], np.int32), "fp32")
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+def test_planted_patterns_1m_config(dtype):
+    # the 1M-token configuration's block: k = 40 drafts (M = 41) over a 131072-token vocabulary;
+    # the full-accept + bonus and the first-position-mismatch patterns and one n ~ U{24..40}
+    B, k, V = 3, 40, 131072
+    y, d, n = S.planted_accept(B, k, V, cfg_seed=5, n_lo=24, n_hi=40, force={0: k, 1: 0})
+    got = _run(S.planted_logits(y, V, cfg_seed=5), d, dtype)
+    np.testing.assert_array_equal(got[1], n)
+    assert got[1][0] == k and got[3][0] == k + 1
+    assert got[1][1] == 0 and got[3][1] == 1

@@ -1,0 +1,183 @@
+"""Parity at the full benchmark sizes, in the launch configuration bench.py
+times (library-chosen splits), on sampled outputs the oracle computes one by
+one.  Inputs come from the seeded device generators of ``synthetic``; the
+sampled (request, KV head) slices are copied to the host and decoded exactly
+for the oracle.  Query scales are raised (std 2-4) so that softmax weights
+concentrate on a few keys and the outputs are O(0.1-1): with N(0,1) queries
+over 10^5 keys the outputs would sit far below the absolute tolerance."""
+import numpy as np
+import pytest
+
+import synthetic as S
+from oracle import attention as A
+from oracle import quant as Q
+from oracle.formats import f16_to_f64, unpack_int4
+
+from .helpers import TOL, assert_close, bf16_dev_to_f64, rel_l2
+
+pytestmark = pytest.mark.gpu
+
+
+def _bf16(shape, seed, std=1.0):
+    import torch
+    return S.torch_normal(shape, seed, "cuda", torch.bfloat16, std)
+
+
+def _free():
+    import gc
+    import torch
+    gc.collect()
+    torch.cuda.empty_cache()
+
+
+def _verify_case(B, Hq, Hkv, N, M, seed, samples):
+    import torch
+    import lossless_speculative_decoding_vc_amd as vc
+    D, G = 128, Hq // Hkv
+    q = _bf16((B, M, Hq, D), seed, std=4.0)
+    k = _bf16((B, Hkv, N, D), seed + 1)
+    vt = _bf16((B, Hkv, D, N), seed + 2)          # channel-major full cache
+    bk = _bf16((B, Hkv, M, D), seed + 3)
+    bvt = _bf16((B, Hkv, D, M), seed + 4)
+    cl = torch.full((B,), N, dtype=torch.int32, device="cuda")
+    out = vc.verify_attn(q, k, vt, cl, bk, bvt)
+    torch.cuda.synchronize()
+    got, ref = [], []
+    for b, kvh, rows in samples:
+        kk = bf16_dev_to_f64(k[b, kvh])
+        vv = bf16_dev_to_f64(vt[b, kvh]).T
+        bkk = bf16_dev_to_f64(bk[b, kvh])
+        bvv = bf16_dev_to_f64(bvt[b, kvh]).T
+        for i, g in rows:
+            h = kvh * G + g
+            o, _ = A.verify_attn_row(bf16_dev_to_f64(q[b, i, h]), kk, vv, N, bkk, bvv, i)
+            ref.append(o)
+            got.append(bf16_dev_to_f64(out[b, i, h]))
+        del kk, vv
+    del q, k, vt, bk, bvt, out
+    _free()
+    got, ref = np.array(got), np.array(ref)
+    assert_close(got, ref, TOL["bf16"], "verify out")
+    assert rel_l2(got, ref) <= 2e-2
+
+
+def test_verify_32k_llama70b_layer():
+    # Llama-70B layer shape: 64 q / 8 KV heads, context 32768, block k + 1 = 32
+    _verify_case(1, 64, 8, 32768, 32, 1100,
+                 [(0, 0, [(0, 0), (17, 3), (31, 7)]), (0, 5, [(9, 1), (31, 0)]), (0, 7, [(30, 6)])])
+
+
+def test_verify_128k_qwen32b_cohort():
+    # verifying cohort of the staggered batch: 16 requests, 40 q / 8 KV heads, 131072 context, M = 33
+    _verify_case(16, 40, 8, 131072, 33, 1200,
+                 [(0, 0, [(0, 0), (32, 4)]), (11, 6, [(16, 2), (32, 0)]), (15, 7, [(5, 3)])])
+
+
+def test_verify_1m_mistral24b_layer():
+    # 1M-token context: 32 q / 8 KV heads, 1048576 context, block k + 1 = 41
+    _verify_case(1, 32, 8, 1048576, 41, 1300, [(0, 2, [(0, 1), (40, 3)]), (0, 7, [(20, 0)])])
+
+
+def _draft_dense_case(B, Hq, Hkv, cap, tcap, tlen, seed, samples, qstd):
+    import torch
+    import lossless_speculative_decoding_vc_amd as vc
+    D, G = 128, Hq // Hkv
+    q = _bf16((B, Hq, D), seed, std=qstd)
+    k = _bf16((B, Hkv, cap, D), seed + 1)
+    vb = _bf16((B, Hkv, cap // 32, D, 32), seed + 2)     # 32-token blocks
+    deg = S.torch_randint((B, 1, cap), 1, 5, seed + 3, "cuda", torch.int32).float()
+    ml = torch.full((B, Hkv), cap, dtype=torch.int32, device="cuda")
+    tk = tv = tl = None
+    if tcap:
+        tk = _bf16((B, Hkv, tcap, D), seed + 4)
+        tv = _bf16((B, Hkv, D, tcap), seed + 5)
+        tl = torch.full((B,), tlen, dtype=torch.int32, device="cuda")
+    out = vc.draft_attn(q, k, vb, ml, degree=deg, tail_k=tk, tail_v=tv, tail_len=tl)
+    torch.cuda.synchronize()
+    got, ref = [], []
+    for b, kvh, gs in samples:
+        kk = bf16_dev_to_f64(k[b, kvh])
+        vv = bf16_dev_to_f64(vb[b, kvh]).transpose(0, 2, 1).reshape(cap, D)
+        dd = deg[b, 0].cpu().numpy().astype(np.float64)
+        tkk = bf16_dev_to_f64(tk[b, kvh]) if tcap else None
+        tvv = bf16_dev_to_f64(tv[b, kvh]).T if tcap else None
+        for g in gs:
+            h = kvh * G + g
+            o, _ = A.draft_attn_one(bf16_dev_to_f64(q[b, h]), kk, vv, cap, dd, tkk, tvv, tlen if tcap else 0)
+            ref.append(o)
+            got.append(bf16_dev_to_f64(out[b, h]))
+    del q, k, vb, deg, out, tk, tv
+    _free()
+    got, ref = np.array(got), np.array(ref)
+    assert_close(got, ref, TOL["bf16"], "draft out")
+    assert rel_l2(got, ref) <= 2e-2
+
+
+def test_draft_128k_compacted_with_degrees():
+    # batch 32, 32 q / 8 KV heads, 131072 tokens compressed to 32768 with merge degrees
+    _draft_dense_case(32, 32, 8, 32768, 0, 0, 1400, [(0, 0, [0, 3]), (13, 5, [1]), (31, 7, [2, 3])], qstd=3.0)
+
+
+def test_draft_qwen32b_cohort_with_tail():
+    # drafting cohort of the staggered batch: 16 requests, 40 q / 8 KV heads, 32768 compressed + 32 tail tokens
+    _draft_dense_case(16, 40, 8, 32768, 32, 32, 1500, [(0, 0, [0, 4]), (9, 3, [2]), (15, 7, [1, 3])], qstd=3.0)
+
+
+def _int4_device(B, Hkv, cap, D, seed):
+    import torch
+    kq = S.torch_randint((B, Hkv, cap, D // 2), 0, 256, seed, "cuda", torch.int32).to(torch.uint8)
+    vq = S.torch_randint((B, Hkv, cap // 32, D, 16), 0, 256, seed + 1, "cuda", torch.int32).to(torch.uint8)
+
+    def scales(shape, s):
+        g = torch.Generator(device="cuda")
+        g.manual_seed(s)
+        sc = (torch.rand(shape, generator=g, device="cuda") * 0.2 + 0.3).half()
+        return sc, (sc.float() * -7.5).half()
+    ks, kz = scales((B, Hkv, cap // 32, D), seed + 2)
+    vs, vz = scales((B, Hkv, cap // 32, D // 32, 32), seed + 3)
+    return kq, vq, ks, kz, vs, vz
+
+
+def _f16_host(t):
+    import torch
+    return f16_to_f64(t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16))
+
+
+def _int4_case(B, Hq, Hkv, cap, seed, samples, qstd):
+    import torch
+    import lossless_speculative_decoding_vc_amd as vc
+    D, G = 128, Hq // Hkv
+    q = _bf16((B, Hq, D), seed, std=qstd)
+    kq, vq, ks, kz, vs, vz = _int4_device(B, Hkv, cap, D, seed + 10)
+    ml = torch.full((B, Hkv), cap, dtype=torch.int32, device="cuda")
+    out = vc.draft_attn(q, kq, vq, ml, fmt=vc.VC_KV_INT4, k_scale=ks, k_zero=kz, v_scale=vs, v_zero=vz)
+    torch.cuda.synchronize()
+    got, ref = [], []
+    for b, kvh, gs in samples:
+        kc = unpack_int4(kq[b, kvh].cpu().numpy())                              # [cap][D]
+        vc_blk = unpack_int4(vq[b, kvh].cpu().numpy())                          # [cap/32][D][32]
+        vcodes = vc_blk.transpose(0, 2, 1).reshape(cap, D)
+        kk = Q.dequantize_k(kc, _f16_host(ks[b, kvh]), _f16_host(kz[b, kvh]))
+        vsc = _f16_host(vs[b, kvh]).transpose(0, 2, 1).reshape(cap, D // 32)    # [cap][D/32]
+        vzr = _f16_host(vz[b, kvh]).transpose(0, 2, 1).reshape(cap, D // 32)
+        vv = Q.dequantize_v(vcodes, vsc, vzr)
+        for g in gs:
+            h = kvh * G + g
+            o, _ = A.draft_attn_one(bf16_dev_to_f64(q[b, h]), kk, vv, cap)
+            ref.append(o)
+            got.append(bf16_dev_to_f64(out[b, h]))
+    del q, kq, vq, ks, kz, vs, vz, out
+    _free()
+    got, ref = np.array(got), np.array(ref)
+    assert_close(got, ref, TOL["bf16"], "int4 draft out")
+    assert rel_l2(got, ref) <= 2e-2
+
+
+def test_draft_int4_128k():
+    # batch 32, 32 q / 8 KV heads, int4 K/V over all 131072 tokens
+    _int4_case(32, 32, 8, 131072, 1600, [(0, 0, [0]), (20, 4, [1, 3]), (31, 7, [2])], qstd=2.0)
+
+
+def test_draft_int4_1m():
+    # the drafter of the 1M-token configuration: one request, 32 q / 8 KV heads, int4 over 1048576 tokens
+    _int4_case(1, 32, 8, 1048576, 1700, [(0, 1, [0, 3]), (0, 6, [2])], qstd=2.0)
