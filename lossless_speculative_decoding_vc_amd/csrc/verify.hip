@@ -91,6 +91,11 @@ VC_DEVICE void load_lds16(const void *gptr, uint32_t lds_addr) {
   __asm__ volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gptr), "s"(lds_addr) : "memory", "m0");
 }
 
+// The same load with a scalar 64-bit base and a 32-bit per-lane byte offset.
+VC_DEVICE void load_lds16_s(uint32_t voff, const void *sbase, uint32_t lds_addr) {
+  __asm__ volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "s"(lds_addr) : "memory", "m0");
+}
+
 // Tile that reaches the block keys or the end of the key sequence: staged
 // through registers with the same swizzled layout (zero past the end).
 template <int D>
@@ -448,26 +453,398 @@ __global__ __launch_bounds__(W * 64) void verify_bf16(VerifyParams p) {
   }
 }
 
-// Waves and 16-row column tiles per wave for R packed rows.  Up to 192
-// rows: four waves (one per SIMD) of up to 48 rows; more rows per wave means
-// fewer LDS bytes per MFMA (each K/V operand read from LDS feeds CT MFMAs).
-// Up to 256 rows: eight waves of 32 rows (64 rows per wave would not fit
-// the register file at head_dim 128).
+// The rows [r0, r0 + 16*CT) of one workgroup of verify_pp, run by one wave
+// of eight (two per SIMD); the two waves of a SIMD may hold different CT.
+template <int D, int CT>
+VC_DEVICE void pp_rows(const VerifyParams &p, uint8_t *lds, const int wave, const int r0) {
+  constexpr int W = 8;
+  using L = Lds<D>;
+  constexpr int KS = D / 32, DT = D / 16;
+  constexpr int kThreads = W * 64;
+
+  const int bh = blockIdx.z;
+  const int b = bh / p.Hkv, kvh = bh % p.Hkv;
+  const int split = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int col = lane & 15, grp = lane >> 4;
+  const int G = p.G, M = p.M;
+
+  int cl = p.ctx_len[b];
+  cl = cl < 0 ? 0 : (cl > p.ccap ? (int)p.ccap : cl);
+  const int total = cl + M;
+  const int nchunks = (total + kTile - 1) / kTile;
+  const int cps = (nchunks + p.splits - 1) / p.splits;
+  const int c0 = split * cps;
+  const int c1 = min(c0 + cps, nchunks);
+
+  // Q^T operands: column = packed row r = i*G + g.
+  bf16x8 qb[CT][KS];
+  int row_lim[CT];   // row r sees key j iff j < row_lim = cl + i + 1
+#pragma unroll
+  for (int ct = 0; ct < CT; ++ct) {
+    const int r = r0 + 16 * ct + col;
+    row_lim[ct] = cl + r / G + 1;
+    if (r < p.R) {
+      const int i = r / G, g = r % G;
+      const uint16_t *qp = p.q + (((size_t)b * M + i) * p.Hq + kvh * G + g) * D;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) qb[ct][ks] = as_bf16x8(*reinterpret_cast<const u32x4 *>(qp + 32 * ks + 8 * grp));
+    } else {
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) qb[ct][ks] = as_bf16x8(u32x4{0, 0, 0, 0});
+    }
+  }
+
+  // The direct loads below are invisible to the compiler's wait-count
+  // tracking: if a Q load were still outstanding inside the main loop, the
+  // compiler's wait for it would count the tile prefetches too and drain the
+  // ring.  Consuming Q in an empty asm makes it wait here, once.
+#pragma unroll
+  for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) __asm__ volatile("" ::"v"(qb[ct][ks]));
+
+  const uint16_t *ckb = p.ck + (size_t)bh * p.ccap * D;
+  const uint16_t *cvb = p.cv + (size_t)bh * D * p.ccap;
+  const uint16_t *bkb = p.bk + (size_t)bh * M * D;
+  const uint16_t *bvb = p.bv + (size_t)bh * D * M;
+  const uint32_t lds_base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t *)lds;
+
+  // Tiles [c0, cf) hold only context tokens ("full"): each wave fetches whole
+  // 1 KB blocks of them straight into LDS (block q: 4 K rows or 8 V channel
+  // rows, lanes ordered by physical slot).  Tiles [cf, c1) reach the block
+  // keys or the end of the key sequence; they are staged after the main loop.
+  const int cf = max(c0, min(c1, cl / kTile));
+  // Per-lane byte offsets of this wave's direct loads, relative to the
+  // tile's first K row / first V column (scalar bases, so each load holds one
+  // 32-bit VGPR).  K blocks come first: W divides the K block count.
+  constexpr int kJobs = L::kBlocks / W, kKJobs = L::kKBlocks / W;
+  static_assert(L::kBlocks % W == 0 && L::kKBlocks % W == 0, "even split of a tile's loads");
+  uint32_t doff[kJobs];
+#pragma unroll
+  for (int j = 0; j < kJobs; ++j) {
+    const int q = wave + j * W;
+    if (j < kKJobs) {
+      const int r = q * L::kRowsPerBlock + lane / L::kSlots;
+      doff[j] = (uint32_t)(ktok(r) * D + 8 * kswz<D>(r, lane % L::kSlots)) * 2u;
+    } else {
+      const int d = (q - L::kKBlocks) * 8 + lane / 8;
+      doff[j] = (uint32_t)((size_t)d * p.ccap + 8 * vswz(d, lane % 8)) * 2u;
+    }
+  }
+  auto issue = [&](int c) __attribute__((always_inline)) {
+    const uint32_t st = lds_base + (uint32_t)((c & (kStages - 1)) * L::kStage);
+    const uint16_t *kb = ckb + (size_t)c * kTile * D, *vb = cvb + (size_t)c * kTile;
+#pragma unroll
+    for (int j = 0; j < kJobs; ++j)
+      load_lds16_s(doff[j], j < kKJobs ? kb : vb, st + (uint32_t)((wave + j * W) * 1024));
+  };
+
+  float m_run[CT], l_run[CT], mq[CT];   // mq = scaled reference (0 while it is -inf)
+  f32x4 o[CT][DT];
+#pragma unroll
+  for (int ct = 0; ct < CT; ++ct) {
+    m_run[ct] = kNegInf;
+    mq[ct] = 0.f;
+    l_run[ct] = 0.f;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) o[ct][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  // Pieces of one 32-token half h of a 64-token tile (S^T tiles tau = 2h,
+  // 2h+1, then the PV k-step h).
+  const float qs = p.qk_scale;
+  using KOps = u32x4[2][KS];
+  using Scores = f32x4[CT][2];
+  // K operands of half h (16 token rows per S^T tile, 32 channels per k-step).
+  auto load_k = [&](const uint8_t *kt, int h, KOps &ka) __attribute__((always_inline)) {
+#pragma unroll
+    for (int t2 = 0; t2 < 2; ++t2) {
+      const int kr = 16 * (2 * h + t2) + col;   // token 8*(col>>2) + 4*t2 + (col&3) of the half
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        ka[t2][ks] = *reinterpret_cast<const u32x4 *>(kt + kr * L::kKRow + 16 * kswz<D>(kr, 4 * ks + grp));
+    }
+  };
+  auto qk = [&](const KOps &ka, Scores &sc) __attribute__((always_inline)) {
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) sc[ct][0] = sc[ct][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+      for (int t2 = 0; t2 < 2; ++t2)
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) sc[ct][t2] = mfma16x16x32(as_bf16x8(ka[t2][ks]), qb[ct][ks], sc[ct][t2]);
+  };
+  // Lazy reference max per packed row: each lane compares its own 8 scores
+  // with the row's reference; only when some score in the wave exceeds it by
+  // more than kSlack (base 2) do the lane groups exchange their maxima (two
+  // cross-lane shuffles) and rescale.  After the first tiles that branch is
+  // rarely taken, and probabilities stay <= 2^kSlack.
+  auto row_max = [&](const Scores &sc, float (&lmax)[CT]) __attribute__((always_inline)) {
+    bool need = false;
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) {
+      lmax[ct] = vmax(vmax(vmax(sc[ct][0][0], sc[ct][0][1]), vmax(sc[ct][0][2], sc[ct][0][3])),
+                      vmax(vmax(sc[ct][1][0], sc[ct][1][1]), vmax(sc[ct][1][2], sc[ct][1][3])));
+      need |= (lmax[ct] - m_run[ct]) * qs > kSlack;   // false when both are -inf
+    }
+    return need;
+  };
+  auto rescale = [&](bool need, const float (&lmax)[CT]) __attribute__((always_inline)) {
+    if (__any(need)) {
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct) {
+        float cmax = lmax[ct];
+        cmax = fmaxf(cmax, __shfl_xor(cmax, 16, 64));
+        cmax = fmaxf(cmax, __shfl_xor(cmax, 32, 64));
+        const float m_new = fmaxf(m_run[ct], cmax);
+        const float alpha = (m_new == kNegInf) ? 1.f : fast_exp2((m_run[ct] - m_new) * qs);
+        l_run[ct] *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) o[ct][dt] *= alpha;
+        m_run[ct] = m_new;
+        mq[ct] = (m_new == kNegInf) ? 0.f : m_new * qs;
+      }
+    }
+  };
+  auto update_max = [&](const Scores &sc) __attribute__((always_inline)) {
+    float lmax[CT];
+    rescale(row_max(sc, lmax), lmax);
+  };
+  // Probabilities relative to the reference, packed to bf16 as the B operand
+  // of the PV MFMA (k-slot e of lane group grp = token 8*grp + e of the half).
+  // The row sum accumulates the bf16-rounded probabilities, i.e. exactly the
+  // weights the PV MFMA applies.
+  auto exp_pack = [&](const Scores &sc, bf16x8 (&pb)[CT]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) {
+      float pr[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) pr[e] = fast_exp2(fmaf(sc[ct][e >> 2][e & 3], qs, -mq[ct]));
+      const u32x4 w = u32x4{pack_bf16x2(pr[0], pr[1]), pack_bf16x2(pr[2], pr[3]),
+                            pack_bf16x2(pr[4], pr[5]), pack_bf16x2(pr[6], pr[7])};
+      l_run[ct] = sum_bf16x2(w[3], sum_bf16x2(w[2], sum_bf16x2(w[1], sum_bf16x2(w[0], l_run[ct]))));
+      pb[ct] = as_bf16x8(w);
+    }
+  };
+  // V^T operands of half h (16 channels per output tile, 32 tokens).
+  using VOps = u32x4[DT];
+  auto load_v = [&](const uint8_t *kt, int h, VOps &va) __attribute__((always_inline)) {
+    const uint8_t *vt = kt + L::kKBytes;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      const int d = 16 * dt + col;
+      va[dt] = *reinterpret_cast<const u32x4 *>(vt + d * L::kVRow + 16 * vswz(d, 4 * h + grp));
+    }
+  };
+  auto pv = [&](const VOps &va, const bf16x8 (&pb)[CT]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct) o[ct][dt] = mfma16x16x32(as_bf16x8(va[dt]), pb[ct], o[ct][dt]);
+  };
+  auto stage_ptr = [&](int c) __attribute__((always_inline)) { return lds + (c & (kStages - 1)) * L::kStage; };
+
+  // Main loop over the full tiles as a two-group ping-pong.  Each 32-token
+  // half n is an MFMA cluster M_n (O += PV of half n-1, then S_n = QK of
+  // half n; between the two it reads the V operands of half n from LDS)
+  // followed by a VALU cluster V_n (softmax of S_n into P_n; it reads the K
+  // operands of half n+1).  The two waves that share a SIMD (w and w+4) run
+  // the same sequence one cluster apart, separated by a workgroup barrier
+  // after every cluster, so one of them issues MFMAs while the other runs
+  // the softmax on the VALU (a single wave cannot overlap the two: an MFMA
+  // blocks its own issue for its whole duration), and both read LDS in every
+  // phase.
+  //
+  // Ring: in global phase f (wave group g runs its cluster f - g), relative
+  // tile u is read from phase 4u-1 to 4u+3 and is waited for (each wave its
+  // own direct loads, vmcnt) at the end of phase 4u-2; tile v is issued at
+  // the start of phase 4v-11 into the stage of tile v-4, whose last reads
+  // completed before the barrier ending phase 4v-13 (the barrier waits for
+  // outstanding LDS reads).  Two tiles stay in flight behind the one waited
+  // for.
+  constexpr int kMine = kJobs;   // direct loads per wave per tile
+  auto wait_tiles_after = [&](int n) __attribute__((always_inline)) {   // n = 0, 1, 2 tiles may stay in flight
+    if (n >= 2) __asm__ volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * kMine) : "memory");
+    else if (n == 1) __asm__ volatile("s_waitcnt vmcnt(%0)" ::"n"(kMine) : "memory");
+    else __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  };
+  auto bar = [&]() __attribute__((always_inline)) {
+    __builtin_amdgcn_sched_barrier(0);
+    __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  const int grp2 = wave >> 2;   // 0 leads, 1 lags by one cluster
+  // A wave whose rows are all past R (row-group padding) keeps to the
+  // barrier and load schedule but skips its arithmetic.
+  const bool active = r0 < p.R;
+  if (c0 < cf) {
+    const int T = cf - c0;
+    for (int t = 0; t < min(3, T); ++t) issue(c0 + t);
+    wait_tiles_after(min(T - 1, 2));
+    __syncthreads();
+    KOps ka;
+    VOps va;
+    Scores sc;
+    bf16x8 pb[CT];
+    load_k(stage_ptr(c0), 0, ka);
+    if (grp2 == 1) bar();
+    // M_0
+    if (grp2 == 1 && 3 < T) issue(c0 + 3);
+    __builtin_amdgcn_sched_barrier(0);
+    load_v(stage_ptr(c0), 0, va);
+    if (active) qk(ka, sc);
+    bar();
+    for (int t = 0; t < T; ++t) {
+      const uint8_t *st = stage_ptr(c0 + t);
+      const uint8_t *sn = stage_ptr(c0 + min(t + 1, T - 1));
+      // V_2t: P of half 0; K operands of half 1
+      if (grp2 == 0 && t + 3 < T) issue(c0 + t + 3);
+      load_k(st, 1, ka);
+      __builtin_amdgcn_sched_barrier(0);
+      if (active) {
+        update_max(sc);
+        exp_pack(sc, pb);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      if (grp2 == 1 && t + 1 < T) wait_tiles_after(min(2, T - 2 - t));
+      bar();
+      // M_2t+1: PV of half 0; V operands of half 1; S of half 1
+      if (active) pv(va, pb);
+      __builtin_amdgcn_sched_barrier(0);
+      load_v(st, 1, va);
+      if (active) qk(ka, sc);
+      __builtin_amdgcn_sched_barrier(0);
+      if (grp2 == 0 && t + 1 < T) wait_tiles_after(min(2, T - 2 - t));
+      bar();
+      // V_2t+1: P of half 1; K operands of half 0 of tile t+1 (after the
+      // last tile these repeat tile t and the scores they give are unused)
+      load_k(sn, 0, ka);
+      __builtin_amdgcn_sched_barrier(0);
+      if (active) {
+        update_max(sc);
+        exp_pack(sc, pb);
+      }
+      bar();
+      // M_2t+2: PV of half 1; V operands and S of half 0 of tile t+1
+      if (grp2 == 1 && t + 4 < T) issue(c0 + t + 4);
+      __builtin_amdgcn_sched_barrier(0);
+      if (active) pv(va, pb);
+      __builtin_amdgcn_sched_barrier(0);
+      load_v(sn, 0, va);
+      if (active) qk(ka, sc);
+      bar();
+    }
+    if (grp2 == 0) bar();
+  }
+
+  // Tiles with block keys or past the end: staged through registers, causal
+  // mask applied to the scores, not pipelined.
+  for (int it = cf; it < c1; ++it) {
+    uint8_t *st = stage_ptr(it);
+    __syncthreads();
+    stage_slow<D>(st, it * kTile, cl, total, M, p.ccap, ckb, cvb, bkb, bvb, tid, kThreads);
+    __syncthreads();
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      KOps ka;
+      Scores sc;
+      bf16x8 pb[CT];
+      load_k(st, h, ka);
+      qk(ka, sc);
+      const int jb = it * kTile + 32 * h + 8 * grp;   // key index of score (t2, i): jb + 4*t2 + i
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+        for (int t2 = 0; t2 < 2; ++t2)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (jb + 4 * t2 + i >= row_lim[ct]) sc[ct][t2][i] = kNegInf;
+      VOps va;
+      load_v(st, h, va);
+      update_max(sc);
+      exp_pack(sc, pb);
+      pv(va, pb);
+    }
+  }
+
+  const int rows = p.B * M * p.Hq;
+#pragma unroll
+  for (int ct = 0; ct < CT; ++ct) {
+    float l = l_run[ct];
+    l += __shfl_xor(l, 16, 64);
+    l += __shfl_xor(l, 32, 64);
+    const int r = r0 + 16 * ct + col;
+    if (r >= p.R) continue;
+    const int i = r / G, g = r % G;
+    const int orow = (b * M + i) * p.Hq + kvh * G + g;
+    if (p.splits == 1) {
+      const float invo = 1.f / l;   // NaN for an empty key set
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        const int d = 16 * dt + 4 * grp;
+        u32x2 w = u32x2{pack_bf16x2(o[ct][dt][0] * invo, o[ct][dt][1] * invo),
+                        pack_bf16x2(o[ct][dt][2] * invo, o[ct][dt][3] * invo)};
+        *reinterpret_cast<u32x2 *>(p.out + (size_t)orow * D + d) = w;
+      }
+      if (p.out_lse && grp == 0) p.out_lse[orow] = (l > 0.f) ? (m_run[ct] * p.qk_scale + fast_log2(l)) * kLn2 : kNegInf;
+    } else {
+      const float inv = (l > 0.f) ? 1.f / l : 0.f;
+      float *po = p.part_o + ((size_t)split * rows + orow) * D;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        const int d = 16 * dt + 4 * grp;
+        *reinterpret_cast<f32x4 *>(po + d) = o[ct][dt] * inv;
+      }
+      if (grp == 0) p.part_lse[(size_t)split * rows + orow] = (l > 0.f) ? m_run[ct] * p.qk_scale + fast_log2(l) : kNegInf;
+    }
+  }
+}
+
+
+// Eight waves, two per SIMD (waves w and w+4), in the ping-pong schedule of
+// pp_rows.  A row group is 64*(CTA+CTB) packed rows: waves 0-3 take 16*CTA
+// rows each, waves 4-7 the next 16*CTB each.
+template <int D, int CTA, int CTB>
+__global__ __launch_bounds__(512) void verify_pp(VerifyParams p) {
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[kStages * Lds<D>::kStage];
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int rg = blockIdx.y * 64 * (CTA + CTB);
+  if (wave < 4) pp_rows<D, CTA>(p, lds, wave, rg + 16 * CTA * wave);
+  else pp_rows<D, CTB>(p, lds, wave, rg + 64 * CTA + 16 * CTB * (wave - 4));
+}
+
+// Kernel and row split for R packed rows.  Up to 64 rows: verify_bf16 with
+// four waves of one 16-row column tile.  Beyond that the ping-pong kernel:
+// 128-row groups as 16 + 16 rows per SIMD, 192 as 32 + 16, 256 as 32 + 32
+// (two waves per SIMD cap a wave at 256 registers, i.e. 32 rows at head_dim
+// 128).  The ping-pong kernel addresses a V row through a 32-bit byte offset,
+// so a context capacity of 2^31 bytes per channel row and beyond uses
+// verify_bf16 with 48-row waves.
 struct VerifyShape {
-  int W, CT;
+  bool pp;
+  int W, CT;      // verify_bf16
+  int CTA, CTB;   // verify_pp
+  int rows() const { return pp ? 64 * (CTA + CTB) : 16 * CT * W; }
 };
-VerifyShape verify_shape(int R) {
-  if (R <= 64) return {4, 1};
-  if (R <= 128) return {4, 2};
-  if (R <= 192) return {4, 3};
-  return {8, 2};
+VerifyShape verify_shape(int R, int64_t ccap) {
+  if (R <= 64) return {false, 4, 1, 0, 0};
+  if ((int64_t)2 * ccap * 128 >= ((int64_t)1 << 31)) return {false, 4, R <= 128 ? 2 : 3, 0, 0};
+  if (R <= 128) return {true, 0, 0, 1, 1};
+  if (R <= 192) return {true, 0, 0, 2, 1};
+  return {true, 0, 0, 2, 2};
 }
 
 template <int D>
 void launch_verify_d(const VerifyParams &p, VerifyShape sh, int row_groups, hipStream_t s) {
   dim3 grid(p.splits, row_groups, p.B * p.Hkv);
-  if (sh.W == 8) verify_bf16<D, 8, 2><<<grid, 512, 0, s>>>(p);
-  else if (sh.CT == 1) verify_bf16<D, 4, 1><<<grid, 256, 0, s>>>(p);
+  if (sh.pp) {
+    if (sh.CTA == 1) verify_pp<D, 1, 1><<<grid, 512, 0, s>>>(p);
+    else if (sh.CTB == 1) verify_pp<D, 2, 1><<<grid, 512, 0, s>>>(p);
+    else verify_pp<D, 2, 2><<<grid, 512, 0, s>>>(p);
+  } else if (sh.CT == 1) verify_bf16<D, 4, 1><<<grid, 256, 0, s>>>(p);
   else if (sh.CT == 2) verify_bf16<D, 4, 2><<<grid, 256, 0, s>>>(p);
   else verify_bf16<D, 4, 3><<<grid, 256, 0, s>>>(p);
 }
@@ -481,8 +858,8 @@ SplitPlan plan_verify(const vc_verify_args &a) {
   SplitPlan p{1, 0};
   if (a.dtype == VC_FP32) return p;
   const int R = a.M * (a.Hq / a.Hkv);
-  const VerifyShape sh = verify_shape(R);
-  const int64_t row_groups = (R + 16 * sh.CT * sh.W - 1) / (16 * sh.CT * sh.W);
+  const VerifyShape sh = verify_shape(R, a.ccap);
+  const int64_t row_groups = (R + sh.rows() - 1) / sh.rows();
   const int64_t wgs = (int64_t)a.B * a.Hkv * row_groups;
   const int64_t chunks = (a.ccap + a.M + kTile - 1) / kTile;
   int s = a.num_splits;
@@ -514,8 +891,8 @@ hipError_t launch_verify(const vc_verify_args &a, const SplitPlan &pl, hipStream
   const size_t rows = (size_t)a.B * a.M * a.Hq;
   p.part_o = (float *)a.workspace;
   p.part_lse = p.part_o ? p.part_o + (size_t)pl.splits * rows * a.D : nullptr;
-  const VerifyShape sh = verify_shape(p.R);
-  const int row_groups = (p.R + 16 * sh.CT * sh.W - 1) / (16 * sh.CT * sh.W);
+  const VerifyShape sh = verify_shape(p.R, p.ccap);
+  const int row_groups = (p.R + sh.rows() - 1) / sh.rows();
   if (a.D == 128) launch_verify_d<128>(p, sh, row_groups, s);
   else launch_verify_d<64>(p, sh, row_groups, s);
   hipError_t e = hipGetLastError();
