@@ -71,13 +71,17 @@ typedef struct vc_draft_args {
   int64_t tcap;                   /* tail capacity (0 when no tail)                */
   const void    *q;               /* [B][Hq][D]                                    */
   const int32_t *main_len;        /* [B][Hkv] valid main tokens                    */
-  const void    *k;               /* DENSE [B][Hkv][cap][D]; INT4 u8 [B][Hkv][cap][D/2],
-                                     two channels per byte, even channel low nibble */
+  const void    *k;               /* DENSE [B][Hkv][cap][D]; INT4 u8 [B][Hkv][cap][D/2]:
+                                     a token's D codes in channel order, packed
+                                     eight per 32-bit word (see below)             */
   const void    *v;               /* DENSE [B][Hkv][cap/32][D][32]: 32-token
                                      blocks, channel-major inside a block; INT4 u8
                                      [B][Hkv][cap/32][D][16]: per 32-token block,
-                                     channel d's 32 codes, two tokens per byte,
-                                     even token low nibble                         */
+                                     channel d's 32 codes in token order, packed
+                                     eight per 32-bit word (see below)             */
+  /* INT4 code words: eight consecutive 4-bit codes c0..c7 per little-endian
+     32-bit word, c_2j in bits 4j..4j+3 and c_2j+1 in bits 16+4j..16+4j+3
+     (j = 0..3): bytes c0|c2<<4, c4|c6<<4, c1|c3<<4, c5|c7<<4.               */
   const uint16_t *k_scale, *k_zero; /* INT4 only: fp16 [B][Hkv][cap/32][D]         */
   const uint16_t *v_scale, *v_zero; /* INT4 only: fp16 [B][Hkv][cap/32][D/32][32]  */
   const float   *degree;          /* optional [B][Hd][cap] merge degrees n_t >= 1  */

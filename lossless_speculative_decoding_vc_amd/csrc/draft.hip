@@ -321,19 +321,29 @@ VC_DEVICE float sum_f16x2(uint32_t w, float acc) {
 VC_DEVICE uint32_t pack_f16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{lo, hi}), f16x2));
 }
-// Eight 4-bit codes (byte j = codes 2j, 2j+1 in its low, high nibble) as four
-// fp16 pairs (1024 + c_2j, 64 + c_2j+1): the low nibble lands in the low
-// mantissa bits of an fp16 whose ulp is 1, the high nibble in bits 4..7 of
-// one whose ulp is 1/16 -- both exact.
-VC_DEVICE u32x4 magic_codes(uint32_t w) {
-  const uint32_t lo = w & 0x0F0F0F0Fu, hi = w & 0xF0F0F0F0u;
-  u32x4 r;
-#pragma unroll
-  for (int j = 0; j < 4; ++j)
-    r[j] = __builtin_amdgcn_perm(hi, lo, 0x0C000C00u | ((4u + j) << 16) | (uint32_t)j) | 0x54006400u;
+// (x & m) | c in one v_and_or_b32.  A three-operand instruction takes no
+// 32-bit literal here and at most one scalar operand, so the mask comes from
+// an SGPR and the magic from a VGPR; written out because the compiler splits
+// the expression into two two-operand instructions with literals.
+VC_DEVICE uint32_t and_or(uint32_t x, uint32_t m, uint32_t c) {
+  uint32_t r;
+  __asm__("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(x), "s"(m), "v"(c));
   return r;
 }
-constexpr uint32_t kNegMagic = 0xD400E400u;   // fp16 pair (-1024, -64)
+// One 32-bit word of eight 4-bit codes (code 2j in bits 4j..4j+3, code 2j+1
+// in bits 16+4j..16+4j+3) as four fp16 pairs in code order:
+//   (1024 + c0, 1024 + c1), (64 + c2, 64 + c3), (1024 + c4, 1024 + c5),
+//   (64 + c6, 64 + c7).
+// A code in bits 0..3 of a half lands in the low mantissa bits of an fp16
+// whose ulp is 1, one in bits 4..7 in those of an fp16 whose ulp is 1/16:
+// both exact.  One shift and four and-or per eight codes.
+VC_DEVICE u32x4 magic_codes(uint32_t w, uint32_t m1024, uint32_t m64) {
+  const uint32_t w8 = w >> 8;
+  return u32x4{and_or(w, 0x000F000Fu, m1024), and_or(w, 0x00F000F0u, m64),
+               and_or(w8, 0x000F000Fu, m1024), and_or(w8, 0x00F000F0u, m64)};
+}
+// The magic offsets of magic_codes, negated (fp16 pairs, same slot order).
+constexpr uint32_t kNegMagic1024 = 0xE400E400u, kNegMagic64 = 0xD400D400u;
 
 // Direct global->LDS load of 16 bytes per lane (lane i lands at lds + 16 i).
 VC_DEVICE void dma16(const void *gptr, uint32_t lds_addr) {
@@ -489,7 +499,9 @@ __global__ __launch_bounds__(kDraftWaves * 64, 2) void draft_int4(DraftParams p)
     else __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
   };
   static_assert(kI4Stages <= 5, "wait_chunks_after covers up to 3 chunks in flight");
-  const u32x4 negm = u32x4{kNegMagic, kNegMagic, kNegMagic, kNegMagic};
+  const u32x4 negm = u32x4{kNegMagic1024, kNegMagic64, kNegMagic1024, kNegMagic64};
+  uint32_t m1024 = 0x64006400u, m64 = 0x54005400u;
+  __asm__ volatile("" : "+v"(m1024), "+v"(m64));   // the magics stay in VGPRs
 
   // One int4 chunk from its LDS stage; `masked` drops tokens at or past mlen.
   auto main_chunk = [&](const uint8_t *st, int c, bool masked) __attribute__((always_inline)) {
@@ -541,7 +553,7 @@ __global__ __launch_bounds__(kDraftWaves * 64, 2) void draft_int4(DraftParams p)
     for (int tau = 0; tau < 2; ++tau) {
       s[tau] = cst;
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) s[tau] = mfma_f16(magic_codes(kc[tau][ks]), qp[ks], s[tau]);
+      for (int ks = 0; ks < KS; ++ks) s[tau] = mfma_f16(magic_codes(kc[tau][ks], m1024, m64), qp[ks], s[tau]);
     }
     float sc[8], pr[8];
 #pragma unroll
@@ -565,7 +577,7 @@ __global__ __launch_bounds__(kDraftWaves * 64, 2) void draft_int4(DraftParams p)
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         const int dt = 2 * g + h;
-        o[dt] = mfma_f16(magic_codes(vc[dt]), pg, o[dt]);
+        o[dt] = mfma_f16(magic_codes(vc[dt], m1024, m64), pg, o[dt]);
         o[dt] = mfma_f16(negm, pg, o[dt]);
         o[dt] = mfma_f16(vzr[g], pp, o[dt]);
       }

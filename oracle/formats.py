@@ -5,9 +5,10 @@ Test infrastructure only (see :mod:`oracle`).
 Every stored value is widened exactly to float64: a bfloat16 is the upper
 half of an IEEE binary32, so shifting its 16 bits left by 16 and reading the
 word as binary32 reproduces its value; binary16 widens exactly through
-numpy's ``float16``.  Packed int4 codes hold two 4-bit unsigned codes per
-byte, the even channel in the low nibble (the layout of the quantized
-compressed cache this library reads).
+numpy's ``float16``.  Packed int4 codes (the layout of the quantized
+compressed cache this library reads) hold eight 4-bit unsigned codes per
+little-endian 32-bit word: code i of the word sits in nibble (i // 2) + 4 (i % 2),
+i.e. the even codes fill the low 16 bits and the odd codes the high 16 bits.
 """
 import numpy as np
 
@@ -25,11 +26,19 @@ def f16_to_f64(bits):
 
 
 def unpack_int4(packed):
-    """uint8 ``[..., D/2]`` -> int64 codes ``[..., D]``; low nibble = even channel."""
+    """uint8 ``[..., N/2]`` -> int64 codes ``[..., N]`` (N a multiple of 8).
+
+    Four bytes form one little-endian word w; code i of its group of eight is
+    ``(w >> 4 k) & 15`` with nibble index ``k = i // 2 + 4 (i % 2)``.
+    """
     packed = np.asarray(packed, dtype=np.uint8)
-    lo = (packed & 0x0F).astype(np.int64)
-    hi = (packed >> 4).astype(np.int64)
-    out = np.empty(packed.shape[:-1] + (packed.shape[-1] * 2,), dtype=np.int64)
-    out[..., 0::2] = lo
-    out[..., 1::2] = hi
-    return out
+    nb = packed.shape[-1]
+    if nb % 4:
+        raise ValueError("int4 codes are packed in whole 32-bit words")
+    b = packed.reshape(packed.shape[:-1] + (nb // 4, 4)).astype(np.int64)
+    w = b[..., 0] | (b[..., 1] << 8) | (b[..., 2] << 16) | (b[..., 3] << 24)
+    out = np.empty(packed.shape[:-1] + (nb // 4, 8), dtype=np.int64)
+    for i in range(8):
+        k = i // 2 + 4 * (i % 2)
+        out[..., i] = (w >> (4 * k)) & 15
+    return out.reshape(packed.shape[:-1] + (nb * 2,))

@@ -16,7 +16,8 @@ this module fixes one asymmetric min/max scheme (a reading, not a page fact):
 * code ``c = clip(rint((x - z16) / s16), 0, 15)`` (ties to even), ``c = 0``
   when ``s16 == 0``;
 * reconstruction ``x_hat = c * s16 + z16``;
-* storage two codes per byte, even channel in the low nibble.
+* storage eight codes per little-endian 32-bit word, code i in nibble
+  i // 2 + 4 (i % 2) (the compressed-cache layout the library reads).
 
 Parity: pinned by the half-step error bound, exactness on constant groups and
 on values that already lie on the grid, and by reduction of quantized
@@ -80,8 +81,18 @@ def dequantize_v(codes, scale, zero):
 
 
 def pack_int4(codes):
-    """``codes [..., D]`` in 0..15 -> ``uint8 [..., D/2]``, even channel low."""
+    """``codes [..., N]`` in 0..15 (N a multiple of 8) -> ``uint8 [..., N/2]``:
+    code i of each group of eight in nibble i // 2 + 4 (i % 2) of a
+    little-endian 32-bit word."""
     codes = np.asarray(codes, dtype=np.int64)
     if codes.min(initial=0) < 0 or codes.max(initial=0) > 15:
         raise ValueError("int4 codes must lie in 0..15")
-    return (codes[..., 0::2] | (codes[..., 1::2] << 4)).astype(np.uint8)
+    n = codes.shape[-1]
+    if n % 8:
+        raise ValueError("int4 codes are packed eight per 32-bit word")
+    g = codes.reshape(codes.shape[:-1] + (n // 8, 8))
+    w = np.zeros(g.shape[:-1], dtype=np.int64)
+    for i in range(8):
+        w |= g[..., i] << (4 * (i // 2 + 4 * (i % 2)))
+    out = np.stack([(w >> (8 * j)) & 255 for j in range(4)], axis=-1).astype(np.uint8)
+    return out.reshape(codes.shape[:-1] + (n // 2,))

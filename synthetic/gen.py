@@ -3,8 +3,9 @@
 Every tensor slice is drawn from ``PCG64(SeedSequence([cfg_seed, tensor_id,
 *index]))`` so any slice can be regenerated alone.  bfloat16 tensors are
 produced as uint16 bit patterns by round-to-nearest-even from float32; int4
-tensors as packed bytes (two codes per byte, even channel in the low nibble)
-with binary16 scales/zeros as uint16 bit patterns.
+tensors as packed bytes (eight codes per little-endian 32-bit word, the even
+codes of the word in its low half) with binary16 scales/zeros as uint16 bit
+patterns.
 
 Workload recipes (shapes follow the configurations the library is measured
 on; the value distributions are stated per function).
@@ -106,9 +107,20 @@ def degrees(shape, cfg_seed, lo=1, hi=4):
 # --------------------------------------------------------------------------
 # Int4 compressed cache (variant B), drawn directly on the quantization grid.
 def pack_codes(codes):
-    """int codes 0..15 ``[..., D]`` -> uint8 ``[..., D/2]``, even channel low."""
-    codes = np.asarray(codes).astype(np.uint8)
-    return (codes[..., 0::2] | (codes[..., 1::2] << 4)).astype(np.uint8)
+    """int codes 0..15 ``[..., N]`` (N a multiple of 8) -> uint8 ``[..., N/2]``.
+
+    Each group of eight consecutive codes c0..c7 becomes one little-endian
+    32-bit word with c_2j in bits 4j..4j+3 and c_2j+1 in bits 16+4j..16+4j+3.
+    """
+    c = np.asarray(codes).astype(np.uint32)
+    n = c.shape[-1]
+    assert n % 8 == 0
+    c = c.reshape(c.shape[:-1] + (n // 8, 8))
+    w = np.zeros(c.shape[:-1], np.uint32)
+    for j in range(4):
+        w |= c[..., 2 * j] << np.uint32(4 * j)
+        w |= c[..., 2 * j + 1] << np.uint32(16 + 4 * j)
+    return np.ascontiguousarray(w.astype("<u4")).view(np.uint8).reshape(c.shape[:-2] + (n // 2,))
 
 
 def int4_grid(B, Hkv, cap, D, cfg_seed, smin=0.3, smax=0.5):
@@ -117,10 +129,11 @@ def int4_grid(B, Hkv, cap, D, cfg_seed, smin=0.3, smax=0.5):
 
     Library layouts (uint8 codes, uint16 binary16 bits), all in 32-token
     blocks:
-      ``k_codes [B][Hkv][cap][D/2]`` (two channels per byte, even channel low),
+      ``k_codes [B][Hkv][cap][D/2]`` (a token's codes in channel order, packed
+      as :func:`pack_codes` does),
       ``k_scale/k_zero [B][Hkv][cap/32][D]``,
-      ``v_codes [B][Hkv][cap/32][D][16]`` (per block, channel d's 32 tokens,
-      two tokens per byte, even token low),
+      ``v_codes [B][Hkv][cap/32][D][16]`` (per block, channel d's 32 codes in
+      token order, packed as :func:`pack_codes` does),
       ``v_scale/v_zero [B][Hkv][cap/32][D/32][32]``.
     Also the token-major forms for the oracle side: unpacked codes
     ``k_c/v_c [B][Hkv][cap][D]`` and ``v_scale_td/v_zero_td [B][Hkv][cap][D/32]``.
@@ -143,7 +156,7 @@ def int4_grid(B, Hkv, cap, D, cfg_seed, smin=0.3, smax=0.5):
             res["v_scale_td"][b, h] = vs.view(np.uint16)
             res["v_zero_td"][b, h] = (vs.astype(np.float32) * np.float32(-7.5)).astype(np.float16).view(np.uint16)
     res["k_codes"] = pack_codes(res["k_c"])
-    # [cap][D] -> [cap/32][32][D] -> [cap/32][D][32] -> pack token pairs -> [cap/32][D][16]
+    # [cap][D] -> [cap/32][32][D] -> [cap/32][D][32] -> pack each channel's 32 tokens -> [cap/32][D][16]
     vblk = res["v_c"].reshape(B, Hkv, nb, 32, D).transpose(0, 1, 2, 4, 3)
     res["v_codes"] = pack_codes(np.ascontiguousarray(vblk))
     for key in ("v_scale", "v_zero"):

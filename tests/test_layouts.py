@@ -6,6 +6,21 @@ import numpy as np
 import synthetic as S
 
 
+def code_at(row, i):
+    """Code i of a packed uint8 row: word i // 8, nibble k = (i % 8) // 2 +
+    4 ((i % 8) % 2) of that little-endian word (byte k // 2, half k % 2)."""
+    j = i % 8
+    k = j // 2 + 4 * (j % 2)
+    byte = int(row[4 * (i // 8) + k // 2])
+    return (byte >> (4 * (k % 2))) & 15
+
+
+def test_code_word_example():
+    # codes 1..8 of one word: bytes c0|c2<<4, c4|c6<<4, c1|c3<<4, c5|c7<<4
+    packed = S.pack_codes(np.arange(1, 9))
+    assert packed.tolist() == [0x31, 0x75, 0x42, 0x86]
+
+
 def test_int4_blocked_layouts():
     B, Hkv, cap, D = 2, 2, 96, 64
     g = S.int4_grid(B, Hkv, cap, D, cfg_seed=5)
@@ -14,12 +29,10 @@ def test_int4_blocked_layouts():
     for _ in range(400):
         b, h = rng.integers(B), rng.integers(Hkv)
         t, d = int(rng.integers(cap)), int(rng.integers(D))
-        # k: [cap][D/2], two channels per byte, even channel in the low nibble
-        byte = int(g["k_codes"][b, h, t, d // 2])
-        assert (byte >> (4 * (d & 1))) & 15 == kc[b, h, t, d]
-        # v: [cap/32][D][16], per block channel d's 32 tokens, even token low
-        byte = int(g["v_codes"][b, h, t // 32, d, (t % 32) // 2])
-        assert (byte >> (4 * (t & 1))) & 15 == vc[b, h, t, d]
+        # k: [cap][D/2], a token's codes in channel order, eight per word
+        assert code_at(g["k_codes"][b, h, t], d) == kc[b, h, t, d]
+        # v: [cap/32][D][16], per block channel d's 32 codes in token order
+        assert code_at(g["v_codes"][b, h, t // 32, d], t % 32) == vc[b, h, t, d]
         # v scale / zero: [cap/32][D/32][32]
         assert g["v_scale"][b, h, t // 32, d // 32, t % 32] == g["v_scale_td"][b, h, t, d // 32]
         assert g["v_zero"][b, h, t // 32, d // 32, t % 32] == g["v_zero_td"][b, h, t, d // 32]

@@ -1,6 +1,6 @@
 """Pins of the oracle's int4 group quantizer: the half-step error bound,
 exactness on constant groups and on values already on the grid, and the
-packing layout (even channel in the low nibble)."""
+packing layout (eight codes per 32-bit word, even codes in the low half)."""
 import numpy as np
 import pytest
 
@@ -78,7 +78,9 @@ def test_pack_unpack_layout():
     codes = RNG.integers(0, 16, (5, 64))
     packed = Q.pack_int4(codes)
     assert packed.shape == (5, 32) and packed.dtype == np.uint8
-    assert packed[0, 0] == codes[0, 0] | (codes[0, 1] << 4)
+    # worked by hand: codes 1..8 -> word 0x86427531, bytes 31 75 42 86
+    assert Q.pack_int4(np.arange(1, 9)).tolist() == [0x31, 0x75, 0x42, 0x86]
+    assert unpack_int4(np.array([0x31, 0x75, 0x42, 0x86], np.uint8)).tolist() == list(range(1, 9))
     np.testing.assert_array_equal(unpack_int4(packed), codes)
     with pytest.raises(ValueError):
-        Q.pack_int4(np.array([[16, 0]]))
+        Q.pack_int4(np.array([[16, 0, 0, 0, 0, 0, 0, 0]]))
