@@ -86,9 +86,9 @@ KERNEL_OF = {
     "draft128k": "vc_draft_attn: draft_bf16_dense + combine_splits",
     "draft128k_int4": "vc_draft_attn: draft_int4 + combine_splits",
     "draft1m_int4": "vc_draft_attn: draft_int4 + combine_splits",
-    "verify1m": "vc_verify_attn: verify_bf16 + combine_splits",
-    "verify32k": "vc_verify_attn: verify_bf16 + combine_splits",
-    "verify128k": "vc_verify_attn: verify_bf16 + combine_splits",
+    "verify1m": "vc_verify_attn: verify_pp + combine_splits",
+    "verify32k": "vc_verify_attn: verify_pp + combine_splits",
+    "verify128k": "vc_verify_attn: verify_pp + combine_splits",
     "copy1g": "torch copy_ (1 GiB device to device)",
 }
 

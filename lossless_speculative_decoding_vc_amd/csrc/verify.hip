@@ -678,7 +678,7 @@ VC_DEVICE void pp_rows(const VerifyParams &p, uint8_t *lds, const int wave, cons
   };
   const int grp2 = wave >> 2;   // 0 leads, 1 lags by one cluster
   // A wave whose rows are all past R (row-group padding) keeps to the
-  // barrier and load schedule but skips its arithmetic.
+  // barrier and load schedule but skips its LDS reads and arithmetic.
   const bool active = r0 < p.R;
   if (c0 < cf) {
     const int T = cf - c0;
@@ -694,7 +694,7 @@ VC_DEVICE void pp_rows(const VerifyParams &p, uint8_t *lds, const int wave, cons
     // M_0
     if (grp2 == 1 && 3 < T) issue(c0 + 3);
     __builtin_amdgcn_sched_barrier(0);
-    load_v(stage_ptr(c0), 0, va);
+    if (active) load_v(stage_ptr(c0), 0, va);
     if (active) qk(ka, sc);
     bar();
     for (int t = 0; t < T; ++t) {
@@ -702,7 +702,7 @@ VC_DEVICE void pp_rows(const VerifyParams &p, uint8_t *lds, const int wave, cons
       const uint8_t *sn = stage_ptr(c0 + min(t + 1, T - 1));
       // V_2t: P of half 0; K operands of half 1
       if (grp2 == 0 && t + 3 < T) issue(c0 + t + 3);
-      load_k(st, 1, ka);
+      if (active) load_k(st, 1, ka);
       __builtin_amdgcn_sched_barrier(0);
       if (active) {
         update_max(sc);
@@ -714,14 +714,14 @@ VC_DEVICE void pp_rows(const VerifyParams &p, uint8_t *lds, const int wave, cons
       // M_2t+1: PV of half 0; V operands of half 1; S of half 1
       if (active) pv(va, pb);
       __builtin_amdgcn_sched_barrier(0);
-      load_v(st, 1, va);
+      if (active) load_v(st, 1, va);
       if (active) qk(ka, sc);
       __builtin_amdgcn_sched_barrier(0);
       if (grp2 == 0 && t + 1 < T) wait_tiles_after(min(2, T - 2 - t));
       bar();
       // V_2t+1: P of half 1; K operands of half 0 of tile t+1 (after the
       // last tile these repeat tile t and the scores they give are unused)
-      load_k(sn, 0, ka);
+      if (active) load_k(sn, 0, ka);
       __builtin_amdgcn_sched_barrier(0);
       if (active) {
         update_max(sc);
@@ -733,7 +733,7 @@ VC_DEVICE void pp_rows(const VerifyParams &p, uint8_t *lds, const int wave, cons
       __builtin_amdgcn_sched_barrier(0);
       if (active) pv(va, pb);
       __builtin_amdgcn_sched_barrier(0);
-      load_v(sn, 0, va);
+      if (active) load_v(sn, 0, va);
       if (active) qk(ka, sc);
       bar();
     }
