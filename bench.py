@@ -35,6 +35,8 @@ CPU oracle timed on a bounded sample of the same workload.
   draft128k      batch-32 draft over a 25% compressed 128K context + degrees
   draft128k_int4 batch-32 draft over int4 K/V of all 131072 tokens
   draft1m_int4   the 1M-token configuration's int4 drafter
+  quant128k_int4 building that int4 cache from bf16 K/V (vc_quantize_int4 over
+                 batch 32 x 8 KV heads x 131072 tokens)
   copy1g         a 1 GiB device copy (reference for the HBM byte counters)
 """
 import argparse
@@ -57,7 +59,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=1)
     ap.add_argument("--workload", default="stagger128k",
                     choices=["stagger128k", "verify32k", "verify128k", "verify1m", "draft128k", "draft128k_int4",
-                             "draft1m_int4", "copy1g"])
+                             "draft1m_int4", "quant128k_int4", "copy1g"])
     ap.add_argument("--layers", type=int, default=64)
     ap.add_argument("--distinct-layers", type=int, default=16,
                     help="distinct compressed-cache buffers per cohort (layers rotate over them)")
@@ -89,6 +91,7 @@ KERNEL_OF = {
     "verify1m": "vc_verify_attn: verify_pp + combine_splits",
     "verify32k": "vc_verify_attn: verify_pp + combine_splits",
     "verify128k": "vc_verify_attn: verify_pp + combine_splits",
+    "quant128k_int4": "vc_quantize_int4: quantize_int4",
     "copy1g": "torch copy_ (1 GiB device to device)",
 }
 
@@ -370,6 +373,23 @@ def kernel_alone(args):
         nbytes = B * Hkv * (N + M) * D * 4 + 2 * B * M * Hq * D * 2
     elif args.workload == "copy1g":
         pass
+    elif args.workload == "quant128k_int4":
+        # the int4 cache of the 128K draft leg built from bf16 K/V: 32 requests x 8 KV heads x 131072 tokens
+        B, Hkv, D, cap = 32, 8, 128, 131072
+        K = _bf16_randn((B, Hkv, cap, D), 11, dev)
+        Vt = _bf16_randn((B, Hkv, D, cap), 12, dev)
+        zero = torch.zeros((B, Hkv), dtype=torch.int32, device=dev)
+        qd = dict(k_codes=torch.empty((B, Hkv, cap, D // 2), dtype=torch.uint8, device=dev),
+                  k_scale=torch.empty((B, Hkv, cap // 32, D), dtype=torch.float16, device=dev),
+                  k_zero=torch.empty((B, Hkv, cap // 32, D), dtype=torch.float16, device=dev),
+                  v_codes=torch.empty((B, Hkv, cap // 32, D, 16), dtype=torch.uint8, device=dev),
+                  v_scale=torch.empty((B, Hkv, cap // 32, D // 32, 32), dtype=torch.float16, device=dev),
+                  v_zero=torch.empty((B, Hkv, cap // 32, D // 32, 32), dtype=torch.float16, device=dev))
+
+        def call(i):
+            vc.quantize_int4(K, Vt, zero, cap // 32, zero, **qd)
+        flops = 0.0
+        nbytes = B * Hkv * cap * D * 2 * 2 + B * Hkv * cap * 160
     elif args.workload in ("draft128k_int4", "draft1m_int4"):
         if args.workload == "draft128k_int4":   # batch 32, int4 K/V over all 131072 tokens (4 of 16 bits = 25%)
             B, Hq, Hkv, D, cap = 32, 32, 8, 128, 131072

@@ -184,6 +184,35 @@ vc_status vc_commit_rows(int32_t B, int32_t Hkv, int32_t D, int32_t M, int32_t d
                          int64_t degree_h_stride, void *stream);
 
 /* ------------------------------------------------------------------------ */
+/* Int4 group quantization into the compressed-cache format vc_draft_attn
+ * reads with fmt = VC_KV_INT4 ("Riepilogo Tecnico: VeriCache", "Supporto
+ * Architetturale": the drafter's cache may come from a quantizer behind the
+ * same interface as eviction; the pages fix no scheme, this library reads it
+ * as asymmetric min/max over 32-element groups).  For every (b, KV head) and
+ * group j < n_groups, the 32 bf16 tokens src_start[bh] + 32 j .. + 31 of the
+ * source are quantized into tokens dst_start[bh] + 32 j .. of the cache:
+ *   K: one group = one channel over the 32 tokens; V: one group = one token
+ *   over 32 channels;  s = (max - min) / 15 and z = min, each rounded to
+ *   binary16 (nearest even);  code = clip(rint((x - z) / s), 0, 15), ties to
+ *   even, 0 when s == 0 (exactly, as an exact evaluation decides).
+ *   src_k [B][Hkv][src_cap][D], src_v [B][Hkv][D][src_cap]  bf16 (the tail
+ *         layouts of vc_draft_attn)
+ *   src_start, dst_start [B][Hkv] int32 (device); dst_start % 32 == 0; a
+ *         (b, KV head) whose groups would leave [0, src_cap) or [0, cap), or
+ *         whose dst_start is negative or not a multiple of 32, is skipped
+ *   k_codes, k_scale, k_zero, v_codes, v_scale, v_zero: the INT4 layouts of
+ *         vc_draft_args with capacity cap (a multiple of 32); only the
+ *         written groups' bytes change.
+ * D = 128; n_groups <= 65535; inputs finite with |x| <= 65504; src_k, src_v
+ * and the code buffers 16-byte aligned.  Appending
+ * verified tokens to an int4 cache (flushing full 32-token groups of the bf16
+ * tail) and building the cache from a full bf16 cache are both this call.    */
+vc_status vc_quantize_int4(int32_t B, int32_t Hkv, int32_t D, const void *src_k, const void *src_v,
+                           int64_t src_cap, const int32_t *src_start, int32_t n_groups, int64_t cap,
+                           const int32_t *dst_start, void *k_codes, void *k_scale, void *k_zero, void *v_codes,
+                           void *v_scale, void *v_zero, void *stream);
+
+/* ------------------------------------------------------------------------ */
 /* Cross-resource staggering ("Innovazioni Chiave del Sistema", P1): while
  * some requests draft from HBM, the full cache of the requests that verify
  * is loaded from host memory over PCIe, so transfer overlaps compute.  The

@@ -16,7 +16,7 @@ import torch
 __all__ = [
     "VcError", "lib", "library_path", "draft_attn", "verify_attn", "accept",
     "draft_workspace_size", "verify_workspace_size", "declared_symbols",
-    "argmax", "lm_head", "commit_rows", "Stagger",
+    "argmax", "lm_head", "commit_rows", "quantize_int4", "Stagger",
     "VC_BF16", "VC_FP32", "VC_KV_DENSE", "VC_KV_INT4",
 ]
 
@@ -96,6 +96,8 @@ def lib():
         L.vc_lm_head.restype = ctypes.c_int
         L.vc_commit_rows.argtypes = [_i32, _i32, _i32, _i32, _i32, _i64, _i32, _p, _p, _p, _p, _p, _p, _p, _i64, _p]
         L.vc_commit_rows.restype = ctypes.c_int
+        L.vc_quantize_int4.argtypes = [_i32, _i32, _i32, _p, _p, _i64, _p, _i32, _i64, _p, _p, _p, _p, _p, _p, _p, _p]
+        L.vc_quantize_int4.restype = ctypes.c_int
         L.vc_stagger_create.argtypes = [ctypes.POINTER(_p), ctypes.POINTER(_p), _i32, ctypes.c_size_t, _i32]
         L.vc_stagger_stream_layer.argtypes = [_p, _i32, _p, ctypes.c_size_t]
         L.vc_stagger_acquire.argtypes = [_p, _i32, _p, ctypes.POINTER(_p)]
@@ -331,6 +333,33 @@ def commit_rows(blk_k, blk_v, n_out, dst_k, dst_v, length, degree=None, v_blocke
     hstride = 0 if degree is None or degree.shape[1] == 1 else cap
     _check(lib().vc_commit_rows(B, Hkv, D, M, _vc_dtype(blk_k), cap, 1 if v_blocked else 0, _ptr(blk_k), _ptr(blk_v), _ptr(n_out),
                                 _ptr(dst_k), _ptr(dst_v), _ptr(length), _ptr(degree), hstride, _stream(stream)))
+
+
+def quantize_int4(src_k, src_v, src_start, n_groups, dst_start, k_codes, k_scale, k_zero, v_codes, v_scale,
+                  v_zero, stream=None):
+    """Quantize 32-token groups of bf16 rows into an int4 cache (``vc_quantize_int4``).
+
+    ``src_k [B][Hkv][src_cap][D]``, ``src_v [B][Hkv][D][src_cap]`` bf16;
+    ``src_start``/``dst_start`` int32 ``[B][Hkv]``; the cache tensors have the
+    int4 layouts :func:`draft_attn` takes (``k_codes [B][Hkv][cap][D/2]`` uint8,
+    ``k_scale/k_zero [B][Hkv][cap/32][D]``, ``v_codes [B][Hkv][cap/32][D][16]``,
+    ``v_scale/v_zero [B][Hkv][cap/32][D/32][32]``, binary16 as float16 or int16).
+    """
+    _dev(src_k, "src_k", torch.bfloat16)
+    _dev(src_v, "src_v", torch.bfloat16)
+    _dev(src_start, "src_start", torch.int32)
+    _dev(dst_start, "dst_start", torch.int32)
+    for t, n in ((k_codes, "k_codes"), (v_codes, "v_codes")):
+        _dev(t, n, torch.uint8)
+    for t, n in ((k_scale, "k_scale"), (k_zero, "k_zero"), (v_scale, "v_scale"), (v_zero, "v_zero")):
+        _dev(t, n)
+        if t.element_size() != 2:
+            raise ValueError(f"{n} must hold binary16 values (float16 or int16)")
+    B, Hkv, src_cap, D = src_k.shape
+    cap = k_codes.shape[2]
+    _check(lib().vc_quantize_int4(B, Hkv, D, _ptr(src_k), _ptr(src_v), src_cap, _ptr(src_start), int(n_groups), cap,
+                                  _ptr(dst_start), _ptr(k_codes), _ptr(k_scale), _ptr(k_zero), _ptr(v_codes),
+                                  _ptr(v_scale), _ptr(v_zero), _stream(stream)))
 
 
 class Stagger:

@@ -214,4 +214,34 @@ vc_status vc_commit_rows(int32_t B, int32_t Hkv, int32_t D, int32_t M, int32_t d
                     "vc_commit_rows launch");
 }
 
+vc_status vc_quantize_int4(int32_t B, int32_t Hkv, int32_t D, const void *src_k, const void *src_v,
+                           int64_t src_cap, const int32_t *src_start, int32_t n_groups, int64_t cap,
+                           const int32_t *dst_start, void *k_codes, void *k_scale, void *k_zero, void *v_codes,
+                           void *v_scale, void *v_zero, void *stream) {
+  REQ(B >= 0 && Hkv >= 1 && n_groups >= 0 && src_cap >= 0 && cap >= 0, "bad quantize shape");
+  if (D != 128) return fail(VC_ENOTSUP, "the int4 cache is compiled for head_dim 128 (got %d)", D);
+  REQ(cap % 32 == 0, "cap (%lld) must be a multiple of 32", (long long)cap);
+  REQ(n_groups <= 65535, "at most 65535 groups per call (got %d)", n_groups);
+  if (B == 0 || n_groups == 0) return VC_OK;
+  REQ(src_k && src_v && src_start && dst_start && k_codes && k_scale && k_zero && v_codes && v_scale && v_zero,
+      "null pointer");
+  REQ(aligned16(k_codes) && aligned16(v_codes) && aligned16(src_k) && aligned16(src_v),
+      "source and int4 code buffers must be 16-byte aligned");
+  vc::QuantParams p;
+  p.BH = B * Hkv;
+  p.src_cap = src_cap;
+  p.cap = cap;
+  p.src_k = static_cast<const uint16_t *>(src_k);
+  p.src_v = static_cast<const uint16_t *>(src_v);
+  p.src_start = src_start;
+  p.dst_start = dst_start;
+  p.k_codes = static_cast<uint8_t *>(k_codes);
+  p.v_codes = static_cast<uint8_t *>(v_codes);
+  p.k_scale = static_cast<uint16_t *>(k_scale);
+  p.k_zero = static_cast<uint16_t *>(k_zero);
+  p.v_scale = static_cast<uint16_t *>(v_scale);
+  p.v_zero = static_cast<uint16_t *>(v_zero);
+  return hip_status(vc::launch_quantize_int4(p, n_groups, (hipStream_t)stream), "vc_quantize_int4 launch");
+}
+
 }  // extern "C"

@@ -26,6 +26,17 @@ hipError_t launch_commit(int B, int Hkv, int D, int M, int elem_bytes, int64_t c
 hipError_t launch_draft(const vc_draft_args &a, const SplitPlan &p, hipStream_t s);
 hipError_t launch_verify(const vc_verify_args &a, const SplitPlan &p, hipStream_t s);
 
+// Int4 group quantization (see quant.hip): BH = B * Hkv slices.
+struct QuantParams {
+  int BH;
+  int64_t src_cap, cap;
+  const uint16_t *src_k, *src_v;
+  const int32_t *src_start, *dst_start;
+  uint8_t *k_codes, *v_codes;
+  uint16_t *k_scale, *k_zero, *v_scale, *v_zero;
+};
+hipError_t launch_quantize_int4(const QuantParams &p, int n_groups, hipStream_t s);
+
 // Merge `splits` partials (o normalised per split, lse in log2 units) of
 // `rows` (row, head) pairs into out (bf16 or fp32) and optional lse (ln).
 hipError_t launch_combine(const float *part_o, const float *part_lse, int splits, int rows, int D,
