@@ -17,8 +17,10 @@ Sources (web pages, cited by title and section):
   compressors behind one interface).
 * "Riassunto Tecnico: CentroidKV" (gist.science, paper 2506.11418) --
   section "Componenti Chiave", item 4 "Aggregazione" (attention over merged
-  centroids adds the cluster degree as a logarithmic term in the softmax),
-  item 2 "Pipeline di Inferenza" (attention sinks and recent tokens are kept).
+  centroids adds the cluster degree as a logarithmic term in the softmax;
+  centroids are degree-weighted means), item 2 "Pipeline di Inferenza"
+  (attention sinks and recent tokens are kept), item 3 "Chunked Soft
+  Matching" (chunks, alternating A/B sets, top-r merging of matched pairs).
 
 Modules:
 
@@ -27,6 +29,8 @@ Modules:
   causal) attention, written as the softmax definition.
 * :mod:`oracle.accept`    -- greedy argmax and accept-until-first-mismatch.
 * :mod:`oracle.quant`     -- the int4 group quantizer of the compressed cache.
+* :mod:`oracle.csm`       -- one Chunked Soft Matching clustering round
+  (CentroidKV, "Componenti Chiave" items 1-4).
 * :mod:`oracle.tiny`      -- the tiny random-weight decoder, full-KV greedy
   decoding and the VeriCache loop run step by step.
 
