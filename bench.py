@@ -37,6 +37,8 @@ CPU oracle timed on a bounded sample of the same workload.
   draft1m_int4   the 1M-token configuration's int4 drafter
   quant128k_int4 building that int4 cache from bf16 K/V (vc_quantize_int4 over
                  batch 32 x 8 KV heads x 131072 tokens)
+  csm128k        one Chunked Soft Matching round (vc_csm_round, r = 1, chunks of
+                 64) over the cohort's 131072-token caches (16 x 8 KV heads)
   copy1g         a 1 GiB device copy (reference for the HBM byte counters)
 """
 import argparse
@@ -59,7 +61,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=1)
     ap.add_argument("--workload", default="stagger128k",
                     choices=["stagger128k", "verify32k", "verify128k", "verify1m", "draft128k", "draft128k_int4",
-                             "draft1m_int4", "quant128k_int4", "copy1g"])
+                             "draft1m_int4", "quant128k_int4", "csm128k", "copy1g"])
     ap.add_argument("--layers", type=int, default=64)
     ap.add_argument("--distinct-layers", type=int, default=16,
                     help="distinct compressed-cache buffers per cohort (layers rotate over them)")
@@ -92,6 +94,7 @@ KERNEL_OF = {
     "verify32k": "vc_verify_attn: verify_pp + combine_splits",
     "verify128k": "vc_verify_attn: verify_pp + combine_splits",
     "quant128k_int4": "vc_quantize_int4: quantize_int4",
+    "csm128k": "vc_csm_round: csm_round_kernel",
     "copy1g": "torch copy_ (1 GiB device to device)",
 }
 
@@ -373,6 +376,21 @@ def kernel_alone(args):
         nbytes = B * Hkv * (N + M) * D * 4 + 2 * B * M * Hq * D * 2
     elif args.workload == "copy1g":
         pass
+    elif args.workload == "csm128k":
+        # one clustering round over the staggered cohort's caches: 16 requests x 8 KV heads x 131072 tokens
+        B, Hkv, D, cap = 16, 8, 128, 131072
+        K = _bf16_randn((B, Hkv, cap, D), 13, dev)
+        Vb = _bf16_randn((B, Hkv, cap // 32, D, 32), 14, dev)
+        cap_out = cap // 2 + 1024
+        ok = torch.empty((B, Hkv, cap_out, D), dtype=torch.bfloat16, device=dev)
+        ov = torch.empty((B, Hkv, cap_out // 32, D, 32), dtype=torch.bfloat16, device=dev)
+        od = torch.empty((B, Hkv, cap_out), dtype=torch.float32, device=dev)
+        n_keep = []
+
+        def call(i):
+            n_keep.append(vc.csm_round(K, Vb, cap, 4, 1024, 64, 1.0, ok, ov, od))
+        flops = 0.0
+        nbytes = B * Hkv * cap * D * 2 * 2 + B * Hkv * (cap // 2 + 514) * (D * 2 * 2 + 4)
     elif args.workload == "quant128k_int4":
         # the int4 cache of the 128K draft leg built from bf16 K/V: 32 requests x 8 KV heads x 131072 tokens
         B, Hkv, D, cap = 32, 8, 128, 131072

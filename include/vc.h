@@ -213,6 +213,37 @@ vc_status vc_quantize_int4(int32_t B, int32_t Hkv, int32_t D, const void *src_k,
                            void *v_scale, void *v_zero, void *stream);
 
 /* ------------------------------------------------------------------------ */
+/* One clustering round of Chunked Soft Matching ("Riassunto Tecnico:
+ * CentroidKV", "Componenti Chiave" items 1-4) over a compressed cache in the
+ * dense main-segment layout of vc_draft_args, producing the merged subset and
+ * its degrees n_t for the log-degree term of vc_draft_attn.  Per (b, KV head)
+ * over the first n_in tokens:
+ *   tokens [0, n_sink) and [n_in - n_recent, n_in) pass through unchanged;
+ *   the rest is cut into chunks of `chunk` tokens (the last may be shorter);
+ *   in a chunk, A = even positions, B = odd positions; each A token's match
+ *   is the B token of its chunk with the largest key cosine (lowest index on
+ *   equal values); the floor(r * |A|) A tokens with the largest cosine
+ *   (lower index first on equal values) merge into their matches;
+ *   a cluster's key and value are the degree-weighted means of its members
+ *   (fp32, rounded to bf16), its degree the sum; unmerged tokens are copied
+ *   bit-exactly; survivors keep ascending position.
+ * The decaying ratio schedule r = r_init - j * delta_r is the caller's (one
+ * call per round).  The survivor count, the same for every (b, KV head), is
+ * returned in *n_out (host) before launch; output tokens past it are not
+ * written.
+ *   in_k [B][Hkv][cap_in][D], in_v [B][Hkv][cap_in/32][D][32]   bf16
+ *   in_deg [B][Hkv][cap_in] fp32 (NULL: every degree 1)
+ *   out_k [B][Hkv][cap_out][D], out_v [B][Hkv][cap_out/32][D][32]   bf16
+ *   out_deg [B][Hkv][cap_out] fp32 (feed vc_draft_attn with
+ *           degree_h_stride = cap_out; the drafter takes cap_out % 64 == 0)
+ * D = 128; 2 <= chunk <= 128; 0 <= r <= 1; caps multiples of 32; K buffers
+ * 16-byte aligned; in and out must not overlap.                              */
+vc_status vc_csm_round(int32_t B, int32_t Hkv, int32_t D, int32_t n_in, int32_t n_sink, int32_t n_recent,
+                       int32_t chunk, float r, const void *in_k, const void *in_v, const float *in_deg,
+                       int64_t cap_in, void *out_k, void *out_v, float *out_deg, int64_t cap_out, int32_t *n_out,
+                       void *stream);
+
+/* ------------------------------------------------------------------------ */
 /* Cross-resource staggering ("Innovazioni Chiave del Sistema", P1): while
  * some requests draft from HBM, the full cache of the requests that verify
  * is loaded from host memory over PCIe, so transfer overlaps compute.  The

@@ -16,7 +16,7 @@ import torch
 __all__ = [
     "VcError", "lib", "library_path", "draft_attn", "verify_attn", "accept",
     "draft_workspace_size", "verify_workspace_size", "declared_symbols",
-    "argmax", "lm_head", "commit_rows", "quantize_int4", "Stagger",
+    "argmax", "lm_head", "commit_rows", "quantize_int4", "csm_round", "Stagger",
     "VC_BF16", "VC_FP32", "VC_KV_DENSE", "VC_KV_INT4",
 ]
 
@@ -98,6 +98,9 @@ def lib():
         L.vc_commit_rows.restype = ctypes.c_int
         L.vc_quantize_int4.argtypes = [_i32, _i32, _i32, _p, _p, _i64, _p, _i32, _i64, _p, _p, _p, _p, _p, _p, _p, _p]
         L.vc_quantize_int4.restype = ctypes.c_int
+        L.vc_csm_round.argtypes = [_i32, _i32, _i32, _i32, _i32, _i32, _i32, ctypes.c_float, _p, _p, _p, _i64,
+                                   _p, _p, _p, _i64, ctypes.POINTER(_i32), _p]
+        L.vc_csm_round.restype = ctypes.c_int
         L.vc_stagger_create.argtypes = [ctypes.POINTER(_p), ctypes.POINTER(_p), _i32, ctypes.c_size_t, _i32]
         L.vc_stagger_stream_layer.argtypes = [_p, _i32, _p, ctypes.c_size_t]
         L.vc_stagger_acquire.argtypes = [_p, _i32, _p, ctypes.POINTER(_p)]
@@ -360,6 +363,27 @@ def quantize_int4(src_k, src_v, src_start, n_groups, dst_start, k_codes, k_scale
     _check(lib().vc_quantize_int4(B, Hkv, D, _ptr(src_k), _ptr(src_v), src_cap, _ptr(src_start), int(n_groups), cap,
                                   _ptr(dst_start), _ptr(k_codes), _ptr(k_scale), _ptr(k_zero), _ptr(v_codes),
                                   _ptr(v_scale), _ptr(v_zero), _stream(stream)))
+
+
+def csm_round(in_k, in_v, n_in, n_sink, n_recent, chunk, r, out_k, out_v, out_deg, in_deg=None, stream=None):
+    """One Chunked Soft Matching round (``vc_csm_round``); returns the survivor count.
+
+    ``in_k [B][Hkv][cap_in][D]``, ``in_v [B][Hkv][cap_in/32][D][32]`` bf16,
+    ``in_deg [B][Hkv][cap_in]`` float32 or None; outputs in the same layouts with
+    ``cap_out``; ``out_deg [B][Hkv][cap_out]`` float32.
+    """
+    _dev(in_k, "in_k", torch.bfloat16)
+    _dev(in_v, "in_v", torch.bfloat16)
+    _dev(out_k, "out_k", torch.bfloat16)
+    _dev(out_v, "out_v", torch.bfloat16)
+    _dev(out_deg, "out_deg", torch.float32)
+    _dev(in_deg, "in_deg", torch.float32)
+    B, Hkv, cap_in, D = in_k.shape
+    n_out = _i32()
+    _check(lib().vc_csm_round(B, Hkv, D, int(n_in), int(n_sink), int(n_recent), int(chunk), float(r), _ptr(in_k),
+                              _ptr(in_v), _ptr(in_deg), cap_in, _ptr(out_k), _ptr(out_v), _ptr(out_deg),
+                              out_k.shape[2], ctypes.byref(n_out), _stream(stream)))
+    return n_out.value
 
 
 class Stagger:

@@ -244,4 +244,34 @@ vc_status vc_quantize_int4(int32_t B, int32_t Hkv, int32_t D, const void *src_k,
   return hip_status(vc::launch_quantize_int4(p, n_groups, (hipStream_t)stream), "vc_quantize_int4 launch");
 }
 
+vc_status vc_csm_round(int32_t B, int32_t Hkv, int32_t D, int32_t n_in, int32_t n_sink, int32_t n_recent,
+                       int32_t chunk, float r, const void *in_k, const void *in_v, const float *in_deg,
+                       int64_t cap_in, void *out_k, void *out_v, float *out_deg, int64_t cap_out, int32_t *n_out,
+                       void *stream) {
+  REQ(n_out, "null n_out");
+  REQ(B >= 0 && Hkv >= 1 && n_in >= 0 && n_sink >= 0 && n_recent >= 0, "bad CSM shape");
+  if (D != 128) return fail(VC_ENOTSUP, "the CSM round is compiled for head_dim 128 (got %d)", D);
+  REQ(chunk >= 2 && chunk <= 128, "chunk must lie in 2..128 (got %d)", chunk);
+  REQ(r >= 0.f && r <= 1.f, "r must lie in [0, 1]");
+  REQ(n_sink + n_recent <= n_in, "sinks + recent tokens (%d) exceed n_in (%d)", n_sink + n_recent, n_in);
+  REQ(n_in <= cap_in && cap_in % 32 == 0 && cap_out % 32 == 0, "n_in <= cap_in; caps multiples of 32");
+  const int out = vc::csm_survivors(n_in, n_sink, n_recent, chunk, r);
+  REQ(out <= cap_out, "the round keeps %d tokens; cap_out is %lld", out, (long long)cap_out);
+  REQ((int64_t)(n_in - n_sink - n_recent + chunk - 1) / chunk + 2 <= 2147483647, "too many chunks");
+  *n_out = out;
+  if (B == 0) return VC_OK;
+  REQ(in_k && in_v && out_k && out_v && out_deg, "null pointer");
+  REQ(aligned16(in_k) && aligned16(out_k), "K buffers must be 16-byte aligned");
+  vc::CsmParams p;
+  p.n_in = n_in; p.n_sink = n_sink; p.n_recent = n_recent; p.chunk = chunk; p.n_out = out; p.r = r;
+  p.cap_in = cap_in; p.cap_out = cap_out;
+  p.in_k = static_cast<const uint16_t *>(in_k);
+  p.in_v = static_cast<const uint16_t *>(in_v);
+  p.in_deg = in_deg;
+  p.out_k = static_cast<uint16_t *>(out_k);
+  p.out_v = static_cast<uint16_t *>(out_v);
+  p.out_deg = out_deg;
+  return hip_status(vc::launch_csm_round(p, B * Hkv, (hipStream_t)stream), "vc_csm_round launch");
+}
+
 }  // extern "C"

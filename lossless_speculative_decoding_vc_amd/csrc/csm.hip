@@ -1,0 +1,325 @@
+// One clustering round of Chunked Soft Matching over the compressed cache.
+//
+// "Riassunto Tecnico: CentroidKV", "Componenti Chiave": attention sinks and
+// recent tokens stay out of the partition (item 2); the rest is cut into
+// chunks, each chunk's tokens are split alternately into sets A and B, each
+// token is paired with a highly similar token of the other set, the pairs are
+// ranked by similarity and only the top fraction r is merged (item 3); the
+// similarity is the cosine of the key states (item 1); a cluster's key and
+// value are the degree-weighted mean of its members and its degree their sum
+// (item 4).  Readings where the page is silent: A = even positions of the
+// chunk, B = odd; an A token's match is the B token of its chunk with the
+// largest key cosine (lowest index on equal values); the floor(r |A|) A
+// tokens with the largest cosine (lower index first on equal values) merge;
+// survivors keep ascending position.
+//
+// Layouts are those of vc_draft_attn's dense main segment: K [cap][D]
+// token-major, V in 32-token blocks [cap/32][D][32], degrees [cap] (fp32, one
+// row per KV head), so rounds compose and the output feeds the drafter.
+//
+// One workgroup of 256 threads per (chunk, b, KV head), plus two per (b, KV
+// head) that copy the sinks and the recent tokens; chunks up to 64 tokens use
+// a 37 KB LDS footprint, up to 128 an 81 KB one.  A chunk's keys and values
+// are staged in LDS (bf16); the |A| x |B| key dot products run on MFMA
+// (exact bf16 products, fp32 sums) and are divided by the fp32 norms; each A token's argmax and rank are found by a plain
+// scan; each survivor is written once: unmerged tokens bit-exactly, clusters
+// as the fp32 degree-weighted mean rounded to bf16, V by (channel, survivor)
+// so the blocked writes coalesce.  Every chunk before the
+// last is full, so a chunk's output offset follows from its index alone.
+#include "common.h"
+#include "launch.h"
+
+namespace vc {
+namespace {
+
+constexpr int kD = 128;
+
+VC_DEVICE float dot8(const u32x4 &a, const u32x4 &b, float acc) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    acc = fmaf(bf16_lo(a[j]), bf16_lo(b[j]), acc);
+    acc = fmaf(bf16_hi(a[j]), bf16_hi(b[j]), acc);
+  }
+  return acc;
+}
+
+template <int kMaxChunk>
+__global__ __launch_bounds__(256) void csm_round_kernel(CsmParams p) {
+  __shared__ __attribute__((aligned(16))) uint16_t ks[kMaxChunk][kD + 8];   // rows padded by 16 B: lanes reading different rows spread over the banks
+  __shared__ __attribute__((aligned(16))) uint16_t vs[kD][kMaxChunk];   // channel-major, as in the source
+  __shared__ float nrm[kMaxChunk], dg[kMaxChunk];
+  __shared__ float sim[kMaxChunk / 2][kMaxChunk / 2];
+  __shared__ float score[kMaxChunk / 2];
+  __shared__ int match[kMaxChunk / 2], mergedA[kMaxChunk / 2];
+  __shared__ int surv[kMaxChunk], nmem[kMaxChunk / 2];
+  __shared__ uint8_t mem[kMaxChunk / 2][kMaxChunk / 2];
+  const int bh = blockIdx.y, tid = threadIdx.x;
+  const int nchunks = (int)gridDim.x - 2;
+  const int c = (int)blockIdx.x - 1;   // -1: sinks, nchunks: recent tokens
+  const uint16_t *ik = p.in_k + (size_t)bh * p.cap_in * kD;
+  const uint16_t *iv = p.in_v + (size_t)bh * p.cap_in * kD;
+  const float *idg = p.in_deg ? p.in_deg + (size_t)bh * p.cap_in : nullptr;
+  uint16_t *ok = p.out_k + (size_t)bh * p.cap_out * kD;
+  uint16_t *ov = p.out_v + (size_t)bh * p.cap_out * kD;
+  float *odg = p.out_deg + (size_t)bh * p.cap_out;
+  auto vidx = [](int64_t t, int d) { return (size_t)(t >> 5) * kD * 32 + (size_t)d * 32 + (t & 31); };
+
+  if (c < 0 || c >= nchunks) {
+    // pass-through of the sinks (to the front) or the recent tokens (to the end)
+    const int n = c < 0 ? p.n_sink : p.n_recent;
+    const int64_t src0 = c < 0 ? 0 : p.n_in - p.n_recent, dst0 = c < 0 ? 0 : p.n_out - p.n_recent;
+    for (int e = tid; e < n * kD; e += 256) {
+      const int t = e / kD, d = e % kD;
+      ok[(size_t)(dst0 + t) * kD + d] = ik[(size_t)(src0 + t) * kD + d];
+      ov[vidx(dst0 + t, d)] = iv[vidx(src0 + t, d)];
+    }
+    for (int t = tid; t < n; t += 256) odg[dst0 + t] = idg ? idg[src0 + t] : 1.f;
+    return;
+  }
+
+  const int64_t s0 = (int64_t)p.n_sink + (int64_t)c * p.chunk;
+  const int L = (int)min((int64_t)p.chunk, p.n_in - p.n_recent - s0);
+  const int nA = (L + 1) / 2, nB = L / 2;
+  const int m = nB > 0 ? (int)floor((double)p.r * nA) : 0;
+  const int m_full = (int)floor((double)p.r * ((p.chunk + 1) / 2));
+  const int64_t base = (int64_t)p.n_sink + (int64_t)c * (p.chunk - m_full);   // earlier chunks are full
+
+  // stage the chunk: K rows in 16-byte pieces, V from its 32-token blocks
+  for (int e = tid; e < L * (kD / 8); e += 256) {
+    const int t = e / (kD / 8), q = e % (kD / 8);
+    *reinterpret_cast<u32x4 *>(&ks[t][8 * q]) = *reinterpret_cast<const u32x4 *>(ik + (size_t)(s0 + t) * kD + 8 * q);
+  }
+  // V: four tokens (8 bytes) at a time when the chunk starts on a multiple of
+  // 4 (four such tokens never straddle a 32-token block), else one by one
+  if ((s0 & 3) == 0) {
+    const int ng = (L + 3) / 4;
+    for (int e = tid; e < ng * kD; e += 256) {
+      const int d = e / ng, g = e % ng, t = 4 * g;
+      if (t + 3 < L) {
+        const u32x2 w = *reinterpret_cast<const u32x2 *>(iv + vidx(s0 + t, d));
+        *reinterpret_cast<u32x2 *>(&vs[d][t]) = w;
+      } else {
+        for (int u = t; u < L; ++u) vs[d][u] = iv[vidx(s0 + u, d)];
+      }
+    }
+  } else {
+    for (int e = tid; e < L * kD; e += 256) {
+      const int d = e / L, t = e % L;
+      vs[d][t] = iv[vidx(s0 + t, d)];
+    }
+  }
+  for (int t = tid; t < L; t += 256) dg[t] = idg ? idg[s0 + t] : 1.f;
+  __syncthreads();
+  for (int t = tid; t < L; t += 256) {
+    float acc = 0.f;
+#pragma unroll 4
+    for (int q = 0; q < kD / 8; ++q) {
+      const u32x4 w = *reinterpret_cast<const u32x4 *>(&ks[t][8 * q]);
+      acc = dot8(w, w, acc);
+    }
+    nrm[t] = sqrtf(acc);
+  }
+  __syncthreads();
+  // cosines of A token i (position 2i) with B token j (position 2j+1): the
+  // dot products as 16x16 tiles of v_mfma_f32_16x16x32_bf16 (bf16 products
+  // are exact in its fp32 accumulation), one tile per wave in turn; rows past
+  // nA / nB read row 0 and are not stored
+  {
+    const int wave = tid >> 6, lane = tid & 63, col = lane & 15, grp = lane >> 4;
+    const int tA = (nA + 15) / 16, tB = (nB + 15) / 16;
+    for (int tile = wave; tile < tA * tB; tile += 4) {
+      const int ti = tile / tB, tj = tile % tB;
+      const int ia = 16 * ti + col, jb = 16 * tj + col;
+      const int ra = ia < nA ? 2 * ia : 0, rb = jb < nB ? 2 * jb + 1 : 0;
+      f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int k = 0; k < kD / 32; ++k) {
+        const u32x4 a = *reinterpret_cast<const u32x4 *>(&ks[ra][32 * k + 8 * grp]);
+        const u32x4 b = *reinterpret_cast<const u32x4 *>(&ks[rb][32 * k + 8 * grp]);
+        acc = mfma16x16x32(as_bf16x8(a), as_bf16x8(b), acc);
+      }
+      // lane holds S[16 ti + 4 grp + i][16 tj + col]
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int ii = 16 * ti + 4 * grp + i, jj = 16 * tj + col;
+        if (ii < nA && jj < nB) sim[ii][jj] = acc[i] / (nrm[2 * ii] * nrm[2 * jj + 1]);
+      }
+    }
+  }
+  __syncthreads();
+  // argmax (lowest B index on equal values) and rank of every A token, eight
+  // lanes per A token and a shuffle reduction
+  for (int base_i = 0; base_i < nA; base_i += 32) {
+    const int i = base_i + (tid >> 3), sub = tid & 7;
+    float bs = -2.f;
+    int best = 0x7fffffff;
+    if (i < nA)
+      for (int j = sub; j < nB; j += 8)
+        if (sim[i][j] > bs) { bs = sim[i][j]; best = j; }
+#pragma unroll
+    for (int o = 1; o < 8; o <<= 1) {
+      const float ob = __shfl_xor(bs, o, 64);
+      const int oj = __shfl_xor(best, o, 64);
+      if (ob > bs || (ob == bs && oj < best)) { bs = ob; best = oj; }
+    }
+    if (i < nA && sub == 0) {
+      match[i] = nB > 0 ? best : 0;
+      score[i] = bs;
+    }
+  }
+  __syncthreads();
+  for (int base_i = 0; base_i < nA; base_i += 32) {
+    const int i = base_i + (tid >> 3), sub = tid & 7;
+    int rank = 0;
+    if (i < nA) {
+      const float si = score[i];
+      for (int k = sub; k < nA; k += 8) rank += (score[k] > si) || (score[k] == si && k < i);
+    }
+#pragma unroll
+    for (int o = 1; o < 8; o <<= 1) rank += __shfl_xor(rank, o, 64);
+    if (i < nA && sub == 0) mergedA[i] = rank < m;
+  }
+  __syncthreads();
+  // survivors (B tokens and unmerged A tokens) in position order: surv[k] is
+  // the chunk position of output slot base + k; mem[j] lists, in ascending
+  // order, the A tokens merged into B token j
+  if (tid < L) {
+    const int t = tid;
+    if ((t & 1) || !mergedA[t >> 1]) {
+      int below = 0;
+      for (int i = 0; 2 * i < t; ++i) below += mergedA[i];
+      surv[t - below] = t;
+    }
+  }
+  if (tid < nB) {
+    int n = 0;
+    for (int i = 0; i < nA; ++i)
+      if (mergedA[i] && match[i] == tid) mem[tid][n++] = (uint8_t)i;
+    nmem[tid] = n;
+  }
+  __syncthreads();
+  const int ns = L - m;
+  // Output: survivor k (chunk position surv[k]) goes to slot base + k; its
+  // members are itself and, for a B token, the A tokens merged into it (the
+  // first kRegMem read into registers, any further ones from LDS).
+  constexpr int kRegMem = 8;
+  auto members = [&](int t, int (&mb)[kRegMem], float (&wm)[kRegMem], int &nm) __attribute__((always_inline)) {
+    nm = (t & 1) ? nmem[t >> 1] : 0;
+    float w = dg[t];
+#pragma unroll
+    for (int u = 0; u < kRegMem; ++u) {
+      mb[u] = u < nm ? 2 * mem[t >> 1][u] : t;
+      wm[u] = u < nm ? dg[mb[u]] : 0.f;
+      w += wm[u];
+    }
+    for (int u = kRegMem; u < nm; ++u) w += dg[2 * mem[t >> 1][u]];
+    return w;
+  };
+  // K rows and degrees: four lanes share a token row (32 channels each,
+  // 16-byte stores)
+  for (int k0 = 0; k0 < ns; k0 += 64) {
+    const int k = k0 + (tid & 63), quarter = tid >> 6;
+    if (k >= ns) continue;
+    const int t = surv[k];
+    int mb[kRegMem], nm;
+    float wm[kRegMem];
+    const float w = members(t, mb, wm, nm), inv = 1.f / w;
+    if (quarter == 0) odg[base + k] = w;
+#pragma unroll
+    for (int q = 4 * quarter; q < 4 * quarter + 4; ++q) {
+      uint16_t *dst = ok + (size_t)(base + k) * kD + 8 * q;
+      if (nm == 0) {
+        *reinterpret_cast<u32x4 *>(dst) = *reinterpret_cast<const u32x4 *>(&ks[t][8 * q]);
+        continue;
+      }
+      float acc[8];
+#pragma unroll
+      for (int e2 = 0; e2 < 8; ++e2) acc[e2] = dg[t] * bf16_to_f32(ks[t][8 * q + e2]);
+#pragma unroll
+      for (int u = 0; u < kRegMem; ++u)
+        if (u < nm)
+#pragma unroll
+          for (int e2 = 0; e2 < 8; ++e2) acc[e2] = fmaf(wm[u], bf16_to_f32(ks[mb[u]][8 * q + e2]), acc[e2]);
+      for (int u = kRegMem; u < nm; ++u) {
+        const int a2 = 2 * mem[t >> 1][u];
+#pragma unroll
+        for (int e2 = 0; e2 < 8; ++e2) acc[e2] = fmaf(dg[a2], bf16_to_f32(ks[a2][8 * q + e2]), acc[e2]);
+      }
+      u32x4 kw;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) kw[j] = pack_bf16x2(acc[2 * j] * inv, acc[2 * j + 1] * inv);
+      *reinterpret_cast<u32x4 *>(dst) = kw;
+    }
+  }
+  __syncthreads();
+  // V: the output tile [channel][survivor] is formed in LDS (over the key
+  // buffer, no longer read), then leaves in pieces of four consecutive tokens
+  // (8 bytes, never straddling a 32-token block) when the first output slot
+  // is a multiple of 4, else element by element.
+  static_assert(sizeof(ks) >= sizeof(uint16_t) * kD * kMaxChunk, "V tile fits over the key buffer");
+  uint16_t (*vo)[kMaxChunk] = reinterpret_cast<uint16_t (*)[kMaxChunk]>(&ks[0][0]);
+  for (int k0 = 0; k0 < ns; k0 += 64) {
+    const int k = k0 + (tid & 63), quarter = tid >> 6;
+    if (k >= ns) continue;
+    const int t = surv[k];
+    int mb[kRegMem], nm;
+    float wm[kRegMem];
+    const float inv = 1.f / members(t, mb, wm, nm);
+    for (int d = 32 * quarter; d < 32 * quarter + 32; ++d) {
+      uint16_t val = vs[d][t];
+      if (nm > 0) {
+        float acc = dg[t] * bf16_to_f32(val);
+#pragma unroll
+        for (int u = 0; u < kRegMem; ++u)
+          if (u < nm) acc = fmaf(wm[u], bf16_to_f32(vs[d][mb[u]]), acc);
+        for (int u = kRegMem; u < nm; ++u) {
+          const int a2 = 2 * mem[t >> 1][u];
+          acc = fmaf(dg[a2], bf16_to_f32(vs[d][a2]), acc);
+        }
+        val = f32_to_bf16(acc * inv);
+      }
+      vo[d][k] = val;
+    }
+  }
+  __syncthreads();
+  if ((base & 3) == 0) {
+    constexpr int G4 = kMaxChunk / 4, CPP = 256 / G4;   // 4-token groups per channel, channels per pass
+    const int g = tid % G4;
+    if (4 * g < ns)
+      for (int d = tid / G4; d < kD; d += CPP) {
+        if (4 * g + 3 < ns) {
+          *reinterpret_cast<u32x2 *>(ov + vidx(base + 4 * g, d)) = *reinterpret_cast<const u32x2 *>(&vo[d][4 * g]);
+        } else {
+          for (int u = 4 * g; u < ns; ++u) ov[vidx(base + u, d)] = vo[d][u];
+        }
+      }
+  } else {
+    for (int k0 = 0; k0 < ns; k0 += 64) {
+      const int k = k0 + (tid & 63);
+      if (k < ns)
+        for (int d = tid >> 6; d < kD; d += 4) ov[vidx(base + k, d)] = vo[d][k];
+    }
+  }
+}
+
+}  // namespace
+
+int csm_survivors(int n_in, int n_sink, int n_recent, int chunk, float r) {
+  int out = n_in;
+  for (int s = n_sink; s < n_in - n_recent; s += chunk) {
+    const int L = min(chunk, n_in - n_recent - s);
+    if (L > 1) out -= (int)floor((double)r * ((L + 1) / 2));
+  }
+  return out;
+}
+
+hipError_t launch_csm_round(const CsmParams &p, int BH, hipStream_t s) {
+  const int mid = p.n_in - p.n_recent - p.n_sink;
+  const int nchunks = mid > 0 ? (mid + p.chunk - 1) / p.chunk : 0;
+  if (BH == 0) return hipSuccess;
+  if (p.chunk <= 64) csm_round_kernel<64><<<dim3(nchunks + 2, BH), 256, 0, s>>>(p);
+  else csm_round_kernel<128><<<dim3(nchunks + 2, BH), 256, 0, s>>>(p);
+  return hipGetLastError();
+}
+
+}  // namespace vc

@@ -37,6 +37,19 @@ struct QuantParams {
 };
 hipError_t launch_quantize_int4(const QuantParams &p, int n_groups, hipStream_t s);
 
+// One Chunked Soft Matching round (see csm.hip).
+struct CsmParams {
+  int n_in, n_sink, n_recent, chunk, n_out;
+  float r;
+  int64_t cap_in, cap_out;
+  const uint16_t *in_k, *in_v;
+  const float *in_deg;
+  uint16_t *out_k, *out_v;
+  float *out_deg;
+};
+int csm_survivors(int n_in, int n_sink, int n_recent, int chunk, float r);
+hipError_t launch_csm_round(const CsmParams &p, int BH, hipStream_t s);
+
 // Merge `splits` partials (o normalised per split, lse in log2 units) of
 // `rows` (row, head) pairs into out (bf16 or fp32) and optional lse (ln).
 hipError_t launch_combine(const float *part_o, const float *part_lse, int splits, int rows, int D,

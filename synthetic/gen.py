@@ -15,14 +15,14 @@ import numpy as np
 __all__ = [
     "rng", "f32_to_bf16_bits", "normal_bf16", "normal_f32", "tiny_weights",
     "tiny_prompt", "kept_random", "degrees", "int4_grid", "pack_codes",
-    "planted_accept", "planted_logits", "TINY_WEIGHT_ORDER", "TID", "torch_normal",
+    "planted_accept", "planted_logits", "csm_planted", "TINY_WEIGHT_ORDER", "TID", "torch_normal",
     "torch_randint",
 ]
 
 # Tensor ids used in SeedSequence keys.
 TID = dict(q=1, k=2, v=3, tail_k=4, tail_v=5, blk_k=6, blk_v=7, kept=8,
            degree=9, kcode=10, vcode=11, kscale=12, vscale=13, logits=14,
-           accept=15, hidden=16, lm=17)
+           accept=15, hidden=16, lm=17, csm=18)
 
 
 def rng(cfg_seed, tensor_id, *index):
@@ -163,6 +163,37 @@ def int4_grid(B, Hkv, cap, D, cfg_seed, smin=0.3, smax=0.5):
         td = res[key + "_td"].reshape(B, Hkv, nb, 32, ng).transpose(0, 1, 2, 4, 3)
         res[key] = np.ascontiguousarray(td)
     return res
+
+
+# --------------------------------------------------------------------------
+# Key sets with planted near-duplicates for the chunked clustering round.
+def csm_planted(B, Hkv, n, D, n_sink, n_recent, chunk, n_plant, cfg_seed, noise=0.02):
+    """float32 ``k, v [B][Hkv][n][D]``, N(0,1), where in every chunk of the
+    middle segment ``[n_sink, n - n_recent)`` (cut every ``chunk`` tokens,
+    positions counted from the chunk start) ``n_plant(L)`` of the even
+    positions are copies of a randomly chosen odd position of the same chunk
+    plus ``noise`` times N(0,1) (``L`` = chunk length); several may copy the
+    same odd position.  Returns ``(k, v, planted)`` with ``planted`` a list of
+    ``(b, h, even position, odd position)``.
+    """
+    k = np.empty((B, Hkv, n, D), np.float32)
+    v = np.empty((B, Hkv, n, D), np.float32)
+    planted = []
+    for b in range(B):
+        for h in range(Hkv):
+            g = rng(cfg_seed, TID["csm"], b, h)
+            k[b, h] = g.standard_normal((n, D), dtype=np.float32)
+            v[b, h] = g.standard_normal((n, D), dtype=np.float32)
+            for s in range(n_sink, n - n_recent, chunk):
+                L = min(chunk, n - n_recent - s)
+                n_even, n_odd = (L + 1) // 2, L // 2
+                if n_odd == 0:
+                    continue
+                for i in g.choice(n_even, size=min(n_plant(L), n_even), replace=False):
+                    j = int(g.integers(0, n_odd))
+                    k[b, h, s + 2 * i] = k[b, h, s + 2 * j + 1] + noise * g.standard_normal(D, dtype=np.float32)
+                    planted.append((b, h, s + 2 * int(i), s + 2 * j + 1))
+    return k, v, planted
 
 
 # --------------------------------------------------------------------------
