@@ -19,12 +19,13 @@
 //
 // One workgroup of 256 threads per (chunk, b, KV head), plus two per (b, KV
 // head) that copy the sinks and the recent tokens; chunks up to 64 tokens use
-// a 37 KB LDS footprint, up to 128 an 81 KB one.  A chunk's keys and values
-// are staged in LDS (bf16); the |A| x |B| key dot products run on MFMA
-// (exact bf16 products, fp32 sums) and are divided by the fp32 norms; each A token's argmax and rank are found by a plain
-// scan; each survivor is written once: unmerged tokens bit-exactly, clusters
-// as the fp32 degree-weighted mean rounded to bf16, V by (channel, survivor)
-// so the blocked writes coalesce.  Every chunk before the
+// a 40 KB LDS footprint, up to 128 an 89 KB one.  A chunk's keys and values
+// are staged in LDS (bf16).  The |A| x |B| key dot products run on MFMA
+// (exact bf16 products, fp32 sums) and are divided by the fp32 norms; each A
+// token's argmax and rank come from eight lanes and a shuffle reduction.
+// Each survivor is written once: unmerged tokens bit-exactly, clusters as the
+// fp32 degree-weighted mean rounded to bf16, V through an LDS tile
+// [channel][survivor] so the blocked writes coalesce.  Every chunk before the
 // last is full, so a chunk's output offset follows from its index alone.
 #include "common.h"
 #include "launch.h"
@@ -68,11 +69,13 @@ __global__ __launch_bounds__(256) void csm_round_kernel(CsmParams p) {
     // pass-through of the sinks (to the front) or the recent tokens (to the end)
     const int n = c < 0 ? p.n_sink : p.n_recent;
     const int64_t src0 = c < 0 ? 0 : p.n_in - p.n_recent, dst0 = c < 0 ? 0 : p.n_out - p.n_recent;
-    for (int e = tid; e < n * kD; e += 256) {
-      const int t = e / kD, d = e % kD;
-      ok[(size_t)(dst0 + t) * kD + d] = ik[(size_t)(src0 + t) * kD + d];
-      ov[vidx(dst0 + t, d)] = iv[vidx(src0 + t, d)];
+    for (int e = tid; e < n * (kD / 8); e += 256) {   // K rows in 16-byte pieces
+      const int t = e / (kD / 8), q = e % (kD / 8);
+      *reinterpret_cast<u32x4 *>(ok + (size_t)(dst0 + t) * kD + 8 * q) =
+          *reinterpret_cast<const u32x4 *>(ik + (size_t)(src0 + t) * kD + 8 * q);
     }
+    for (int d = 0; d < kD; ++d)                      // V: consecutive lanes, consecutive tokens
+      for (int t = tid; t < n; t += 256) ov[vidx(dst0 + t, d)] = iv[vidx(src0 + t, d)];
     for (int t = tid; t < n; t += 256) odg[dst0 + t] = idg ? idg[src0 + t] : 1.f;
     return;
   }
@@ -92,16 +95,17 @@ __global__ __launch_bounds__(256) void csm_round_kernel(CsmParams p) {
   // V: four tokens (8 bytes) at a time when the chunk starts on a multiple of
   // 4 (four such tokens never straddle a 32-token block), else one by one
   if ((s0 & 3) == 0) {
-    const int ng = (L + 3) / 4;
-    for (int e = tid; e < ng * kD; e += 256) {
-      const int d = e / ng, g = e % ng, t = 4 * g;
-      if (t + 3 < L) {
-        const u32x2 w = *reinterpret_cast<const u32x2 *>(iv + vidx(s0 + t, d));
-        *reinterpret_cast<u32x2 *>(&vs[d][t]) = w;
-      } else {
-        for (int u = t; u < L; ++u) vs[d][u] = iv[vidx(s0 + u, d)];
+    // lane -> (4-token group g, channels d, d + 256/G4, ...): no division
+    constexpr int G4 = kMaxChunk / 4;
+    const int g = tid % G4, t = 4 * g;
+    if (t < L)
+      for (int d = tid / G4; d < kD; d += 256 / G4) {
+        if (t + 3 < L) {
+          *reinterpret_cast<u32x2 *>(&vs[d][t]) = *reinterpret_cast<const u32x2 *>(iv + vidx(s0 + t, d));
+        } else {
+          for (int u = t; u < L; ++u) vs[d][u] = iv[vidx(s0 + u, d)];
+        }
       }
-    }
   } else {
     for (int e = tid; e < L * kD; e += 256) {
       const int d = e / L, t = e % L;
