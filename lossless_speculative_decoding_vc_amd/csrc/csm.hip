@@ -87,29 +87,45 @@ __global__ __launch_bounds__(256) void csm_round_kernel(CsmParams p) {
   const int m_full = (int)floor((double)p.r * ((p.chunk + 1) / 2));
   const int64_t base = (int64_t)p.n_sink + (int64_t)c * (p.chunk - m_full);   // earlier chunks are full
 
-  // stage the chunk: K rows in 16-byte pieces, V from its 32-token blocks
-  for (int e = tid; e < L * (kD / 8); e += 256) {
-    const int t = e / (kD / 8), q = e % (kD / 8);
-    *reinterpret_cast<u32x4 *>(&ks[t][8 * q]) = *reinterpret_cast<const u32x4 *>(ik + (size_t)(s0 + t) * kD + 8 * q);
-  }
-  // V: four tokens (8 bytes) at a time when the chunk starts on a multiple of
-  // 4 (four such tokens never straddle a 32-token block), else one by one
-  if ((s0 & 3) == 0) {
-    // lane -> (4-token group g, channels d, d + 256/G4, ...): no division
-    constexpr int G4 = kMaxChunk / 4;
-    const int g = tid % G4, t = 4 * g;
-    if (t < L)
-      for (int d = tid / G4; d < kD; d += 256 / G4) {
-        if (t + 3 < L) {
-          *reinterpret_cast<u32x2 *>(&vs[d][t]) = *reinterpret_cast<const u32x2 *>(iv + vidx(s0 + t, d));
-        } else {
-          for (int u = t; u < L; ++u) vs[d][u] = iv[vidx(s0 + u, d)];
-        }
+  // stage the chunk: every load of a thread is issued before any of them is
+  // written to LDS (compile-time trip counts, predicated on the chunk length),
+  // so the loads overlap instead of each waiting for its own round trip.
+  // K rows in 16-byte pieces; V in 8-byte pieces of four tokens (which never
+  // straddle a 32-token block) when the chunk starts on a multiple of 4.
+  {
+    constexpr int KP = kMaxChunk * (kD / 8) / 256;   // K pieces per thread
+    u32x4 kr[KP];
+#pragma unroll
+    for (int j = 0; j < KP; ++j) {
+      const int e = tid + 256 * j, t = e / (kD / 8), q = e % (kD / 8);
+      kr[j] = t < L ? *reinterpret_cast<const u32x4 *>(ik + (size_t)(s0 + t) * kD + 8 * q) : u32x4{0, 0, 0, 0};
+    }
+    if ((s0 & 3) == 0) {
+      constexpr int G4 = kMaxChunk / 4, VP = kD / (256 / G4);   // 4-token groups per channel, pieces per thread
+      const int g = tid % G4, t = 4 * g;
+      u32x2 vr[VP];
+#pragma unroll
+      for (int j = 0; j < VP; ++j) {
+        const int d = tid / G4 + (256 / G4) * j;
+        vr[j] = t + 3 < L ? *reinterpret_cast<const u32x2 *>(iv + vidx(s0 + t, d)) : u32x2{0, 0};
       }
-  } else {
-    for (int e = tid; e < L * kD; e += 256) {
-      const int d = e / L, t = e % L;
-      vs[d][t] = iv[vidx(s0 + t, d)];
+#pragma unroll
+      for (int j = 0; j < VP; ++j) {
+        const int d = tid / G4 + (256 / G4) * j;
+        if (t + 3 < L) *reinterpret_cast<u32x2 *>(&vs[d][t]) = vr[j];
+        else
+          for (int u = t; u < L; ++u) vs[d][u] = iv[vidx(s0 + u, d)];
+      }
+    } else {
+      for (int e = tid; e < L * kD; e += 256) {
+        const int d = e / L, t = e % L;
+        vs[d][t] = iv[vidx(s0 + t, d)];
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < KP; ++j) {
+      const int e = tid + 256 * j, t = e / (kD / 8), q = e % (kD / 8);
+      if (t < L) *reinterpret_cast<u32x4 *>(&ks[t][8 * q]) = kr[j];
     }
   }
   for (int t = tid; t < L; t += 256) dg[t] = idg ? idg[s0 + t] : 1.f;
@@ -187,19 +203,36 @@ __global__ __launch_bounds__(256) void csm_round_kernel(CsmParams p) {
   // survivors (B tokens and unmerged A tokens) in position order: surv[k] is
   // the chunk position of output slot base + k; mem[j] lists, in ascending
   // order, the A tokens merged into B token j
-  if (tid < L) {
-    const int t = tid;
-    if ((t & 1) || !mergedA[t >> 1]) {
-      int below = 0;
-      for (int i = 0; 2 * i < t; ++i) below += mergedA[i];
-      surv[t - below] = t;
+  {
+    // merge flags of the A tokens as bit masks (A token i = bit i), one 64-bit
+    // word per 64 A tokens, so survivor slots are popcounts
+    __shared__ unsigned long long mmask[kMaxChunk / 128 + 1];
+    if (tid < 64 * ((nA + 63) / 64)) {
+      const unsigned long long bal = __ballot(tid < nA && mergedA[tid]);
+      if ((tid & 63) == 0) mmask[tid >> 6] = bal;
     }
-  }
-  if (tid < nB) {
-    int n = 0;
-    for (int i = 0; i < nA; ++i)
-      if (mergedA[i] && match[i] == tid) mem[tid][n++] = (uint8_t)i;
-    nmem[tid] = n;
+    __syncthreads();
+    if (tid < L) {
+      const int t = tid;
+      if ((t & 1) || !mergedA[t >> 1]) {
+        const int na_below = (t + 1) >> 1;   // A tokens at positions below t
+        int below = 0;
+#pragma unroll
+        for (int w = 0; w * 64 < kMaxChunk / 2; ++w) {
+          const int bits = min(64, max(0, na_below - 64 * w));
+          const unsigned long long msk = bits >= 64 ? ~0ull : ((1ull << bits) - 1);
+          below += __popcll(mmask[w] & msk);
+        }
+        surv[t - below] = t;
+      }
+    }
+    if (tid < nB) {
+      int n = 0;
+#pragma unroll
+      for (int i = 0; i < kMaxChunk / 2; ++i)
+        if (i < nA && mergedA[i] && match[i] == tid) mem[tid][n++] = (uint8_t)i;
+      nmem[tid] = n;
+    }
   }
   __syncthreads();
   const int ns = L - m;
