@@ -61,7 +61,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=1)
     ap.add_argument("--workload", default="stagger128k",
                     choices=["stagger128k", "verify32k", "verify128k", "verify1m", "draft128k", "draft128k_int4",
-                             "draft1m_int4", "quant128k_int4", "csm128k", "copy1g"])
+                             "draft1m_int4", "quant128k_int4", "csm128k", "lmhead_verify", "lmhead_draft",
+                             "copy1g"])
     ap.add_argument("--layers", type=int, default=64)
     ap.add_argument("--distinct-layers", type=int, default=16,
                     help="distinct compressed-cache buffers per cohort (layers rotate over them)")
@@ -95,6 +96,8 @@ KERNEL_OF = {
     "verify128k": "vc_verify_attn: verify_pp + combine_splits",
     "quant128k_int4": "vc_quantize_int4: quantize_int4",
     "csm128k": "vc_csm_round: csm_round_kernel",
+    "lmhead_verify": "vc_lm_head_accept: lm_argmax + argmax_partials + accept_rows",
+    "lmhead_draft": "vc_lm_head_argmax: lm_argmax + argmax_partials",
     "copy1g": "torch copy_ (1 GiB device to device)",
 }
 
@@ -345,12 +348,29 @@ def run_stagger(args, t_start):
 
 
 # ---------------------------------------------------------------------------
+def _time_calls(call, iters, s):
+    """Mean microseconds per call over `iters` calls after 5 warm-ups (HIP events on stream s)."""
+    import torch
+    for i in range(5):
+        call(i)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(s)
+    for i in range(iters):
+        call(i)
+    e1.record(s)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / iters
+
+
 def kernel_alone(args):
-    """Attention kernels alone, with >= 4 rotating buffer sets (> 256 MB MALL)."""
+    """Kernels alone, with rotating buffer sets larger than the 256 MB MALL."""
     import torch
     import lossless_speculative_decoding_vc_amd as vc
     dev = "cuda"
     s = torch.cuda.current_stream()
+    extra = {}
+    bound = "hbm"
     if args.workload in ("verify32k", "verify128k", "verify1m"):
         if args.workload == "verify32k":   # Llama-70B layer shape, one request, k = 32
             B, Hq, Hkv, D, N, M = 1, 64, 8, 128, 32768, 32
@@ -376,6 +396,45 @@ def kernel_alone(args):
         nbytes = B * Hkv * (N + M) * D * 4 + 2 * B * M * Hq * D * 2
     elif args.workload == "copy1g":
         pass
+    elif args.workload in ("lmhead_verify", "lmhead_draft"):
+        # LM head of the staggered batch (Dm 5120, vocabulary 32768) fused with the greedy choice: the
+        # verifying cohort's 16 x 33 block rows with acceptance, or the drafting cohort's 16 rows
+        c = Cfg
+        R = c.B * c.M if args.workload == "lmhead_verify" else c.B
+        nset = 2   # 2 x 335 MB of weights > 256 MB MALL
+        Ws = [_bf16_randn((c.V, c.Dm), 60 + i, dev, std=0.02) for i in range(nset)]
+        Wt = [w.t().contiguous() for w in Ws]     # [Dm][V] for the library GEMM
+        hs = [_bf16_randn((R, c.Dm), 70 + i, dev) for i in range(nset)]
+        ws = vc.lm_head_argmax_workspace(R, c.V, dev)
+        drafts = torch.zeros((c.B, c.k), dtype=torch.int32, device=dev)
+        outs = [torch.empty(R, dtype=torch.int32, device=dev) for _ in range(4)]
+        logits = torch.empty((R, c.V), dtype=torch.float32, device=dev)
+
+        if args.workload == "lmhead_verify":
+            def call(i):
+                vc.lm_head_accept(hs[i % nset].view(c.B, c.M, c.Dm), Ws[i % nset], drafts, workspace=ws)
+
+            def call_unfused(i):
+                vc.lm_head(hs[i % nset], Wt[i % nset], logits)
+                vc.accept(logits.view(c.B, c.M, c.V), drafts)
+        else:
+            def call(i):
+                vc.lm_head_argmax(hs[i % nset], Ws[i % nset], out=outs[0], workspace=ws)
+
+            def call_unfused(i):
+                vc.lm_head(hs[i % nset], Wt[i % nset], logits)
+                vc.argmax(logits, out=outs[1])
+        # rows on which the fused path and the library GEMM + argmax pick the same token (they sum in
+        # different orders, so only near ties may differ)
+        vc.lm_head(hs[0], Wt[0], logits)
+        ref_am = vc.argmax(logits)
+        got_am = vc.lm_head_argmax(hs[0], Ws[0], workspace=ws)
+        extra["rows_agreeing_with_library_gemm"] = int((ref_am == got_am).sum().item())
+        flops = 2.0 * R * c.Dm * c.V
+        nbytes = c.V * c.Dm * 2 + R * c.Dm * 2
+        extra["unfused_us"] = _time_calls(call_unfused, args.iters, s)
+        extra["rows"] = R
+        bound = "mfma" if args.workload == "lmhead_verify" else "hbm"
     elif args.workload == "csm128k":
         # one clustering round over the staggered cohort's caches: 16 requests x 8 KV heads x 131072 tokens
         B, Hkv, D, cap = 16, 8, 128, 131072
@@ -458,17 +517,9 @@ def kernel_alone(args):
 
         def call(i):
             dst.copy_(src)
-    for i in range(5):
-        call(i)
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(s)
-    for i in range(args.iters):
-        call(i)
-    e1.record(s)
-    torch.cuda.synchronize()
-    t = e0.elapsed_time(e1) * 1e-3 / args.iters
-    return dict(avg_us=t * 1e6, gbs=nbytes / t / 1e9, tflops=flops / t / 1e12, nbytes=nbytes, flops=flops)
+    t = _time_calls(call, args.iters, s) * 1e-6
+    return dict(avg_us=t * 1e6, gbs=nbytes / t / 1e9, tflops=flops / t / 1e12, nbytes=nbytes, flops=flops,
+                bound=bound, extra=extra)
 
 
 # ---------------------------------------------------------------------------
@@ -533,14 +584,19 @@ def main():
 
     if args.workload != "stagger128k":
         r = kernel_alone(args)
+        if r["bound"] == "mfma":
+            roof = {"bound": "mfma", "achieved": r["tflops"], "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                    "frac": r["tflops"] / MFMA_BF16_PEAK_TFLOPS, "flops_per_launch": r["flops"]}
+        else:
+            roof = {"bound": "hbm", "achieved": r["gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": r["gbs"] / HBM_PEAK_GBS}
+        roof.update({"traffic": measured_traffic(f"{args.workload}_traffic_bytes_per_launch"),
+                     "kernel": KERNEL_OF.get(args.workload), "bytes_per_launch": r["nbytes"],
+                     "avg_us": r["avg_us"]})
         out = {"metric": f"{args.workload} kernel alone", "value": r["avg_us"], "unit": "us",
                "higher_is_better": False, "n_gpus": 1, "steps": args.iters, "warmup": 5,
                "dtype": "bf16", "data": "synthetic",
-               "roofline": {"bound": "hbm", "achieved": r["gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                            "frac": r["gbs"] / HBM_PEAK_GBS,
-                            "traffic": measured_traffic(f"{args.workload}_traffic_bytes_per_launch"),
-                            "kernel": KERNEL_OF.get(args.workload), "bytes_per_launch": r["nbytes"],
-                            "avg_us": r["avg_us"]},
+               "roofline": roof, **r["extra"],
                "mfma": {"achieved": r["tflops"], "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                         "frac": r["tflops"] / MFMA_BF16_PEAK_TFLOPS},
                "config": {"workload": args.workload, "splits": args.splits}}

@@ -165,6 +165,35 @@ vc_status vc_argmax(int32_t R, int32_t V, int32_t logit_dtype, const void *logit
 vc_status vc_lm_head(int32_t R, int32_t Dm, int32_t V, const void *h, const void *w,
                      float *logits, void *stream);
 
+/* LM head fused with the greedy choice ("Algoritmo Principale", steps 1
+ * and 3: the drafter and the verifier keep only the argmax of each logit
+ * row): out[r * out_stride] = lowest index of the maximum over v of
+ *   logit[r][v] = sum_k h[r][k] * w[v][k]
+ * computed in fp32 from bf16 products (MFMA) without writing the logits.
+ *   h [R][Dm] bf16, w [V][Dm] bf16 (vocab-major: a linear layer's weight),
+ *   both 16-byte aligned; Dm % 32 == 0; out int32 (device).
+ * NaN logits never win (a row of NaN gives 0).  The summation order differs
+ * from vc_lm_head + vc_argmax, so at a near tie (logits equal to fp32
+ * rounding) the two may pick different maxima.  workspace: device buffer of
+ * at least vc_lm_head_argmax_workspace_size(R, V) bytes (per-tile maxima),
+ * 16-byte aligned, owned by the caller and not read across calls.
+ * VC_EINVAL on bad shapes, null or misaligned pointers or a short
+ * workspace; nothing is enqueued then.                                     */
+size_t    vc_lm_head_argmax_workspace_size(int32_t R, int32_t V);
+vc_status vc_lm_head_argmax(int32_t R, int32_t Dm, int32_t V, const void *h, const void *w,
+                            int32_t *out, int32_t out_stride, void *workspace,
+                            size_t workspace_bytes, void *stream);
+
+/* The verify step's logits, greedy acceptance and emitted tokens in one
+ * call: vc_lm_head_argmax over the B*M block rows h [B][M][Dm] into
+ * argmax [B][M], then the acceptance of vc_accept (same outputs, same rule)
+ * against draft [B][M-1].  The workspace is that of
+ * vc_lm_head_argmax_workspace_size(B * M, V).                              */
+vc_status vc_lm_head_accept(int32_t B, int32_t M, int32_t Dm, int32_t V, const void *h, const void *w,
+                            const int32_t *draft, int32_t *argmax, int32_t *accept_len,
+                            int32_t *out_tokens, int32_t *n_out, void *workspace,
+                            size_t workspace_bytes, void *stream);
+
 /* Commit after acceptance ("Algoritmo Principale", step 3: the process
  * restarts from the last accepted token): append the verified K/V rows of
  * x0, d_1..d_n -- the first n_out[b] rows of the block -- to a cache at its

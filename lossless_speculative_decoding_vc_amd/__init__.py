@@ -94,6 +94,12 @@ def lib():
         L.vc_argmax.restype = ctypes.c_int
         L.vc_lm_head.argtypes = [_i32, _i32, _i32, _p, _p, _p, _p]
         L.vc_lm_head.restype = ctypes.c_int
+        L.vc_lm_head_argmax_workspace_size.argtypes = [_i32, _i32]
+        L.vc_lm_head_argmax_workspace_size.restype = ctypes.c_size_t
+        L.vc_lm_head_argmax.argtypes = [_i32, _i32, _i32, _p, _p, _p, _i32, _p, ctypes.c_size_t, _p]
+        L.vc_lm_head_argmax.restype = ctypes.c_int
+        L.vc_lm_head_accept.argtypes = [_i32, _i32, _i32, _i32, _p, _p, _p, _p, _p, _p, _p, _p, ctypes.c_size_t, _p]
+        L.vc_lm_head_accept.restype = ctypes.c_int
         L.vc_commit_rows.argtypes = [_i32, _i32, _i32, _i32, _i32, _i64, _i32, _p, _p, _p, _p, _p, _p, _p, _i64, _p]
         L.vc_commit_rows.restype = ctypes.c_int
         L.vc_quantize_int4.argtypes = [_i32, _i32, _i32, _p, _p, _i64, _p, _i32, _i64, _p, _p, _p, _p, _p, _p, _p, _p]
@@ -317,6 +323,61 @@ def lm_head(h, w, logits=None, stream=None):
     _dev(logits, "logits", torch.float32)
     _check(lib().vc_lm_head(R, Dm, V, _ptr(h), _ptr(w), _ptr(logits), _stream(stream)))
     return logits
+
+
+def lm_head_argmax_workspace(R, V, device):
+    """Workspace tensor (uint8) for :func:`lm_head_argmax` over R rows."""
+    n = lib().vc_lm_head_argmax_workspace_size(R, V)
+    return torch.empty(max(n, 16), dtype=torch.uint8, device=device)
+
+
+def lm_head_argmax(h, w, out=None, out_stride=1, workspace=None, stream=None):
+    """Greedy token of each hidden row without writing logits
+    (``vc_lm_head_argmax``): ``out[r * out_stride] = argmax_v h[r] . w[v]``
+    for ``h [R][Dm]`` and vocab-major ``w [V][Dm]`` (bf16)."""
+    _dev(h, "h", torch.bfloat16)
+    _dev(w, "w", torch.bfloat16)
+    Dm = h.shape[-1]
+    R = h.numel() // Dm
+    V = w.shape[0]
+    if w.shape[1] != Dm:
+        raise ValueError("w must be [V][Dm]")
+    if out is None:
+        out = torch.empty(R * out_stride, dtype=torch.int32, device=h.device)
+    _dev(out, "out", torch.int32)
+    if workspace is None:
+        workspace = lm_head_argmax_workspace(R, V, h.device)
+    _check(lib().vc_lm_head_argmax(R, Dm, V, _ptr(h), _ptr(w), _ptr(out), out_stride, _ptr(workspace),
+                                   workspace.numel() * workspace.element_size(), _stream(stream)))
+    return out
+
+
+def lm_head_accept(h, w, draft, argmax=None, accept_len=None, out_tokens=None, n_out=None, workspace=None,
+                   stream=None):
+    """Verify logits, greedy acceptance and emitted tokens in one call
+    (``vc_lm_head_accept``): ``h [B][M][Dm]``, vocab-major ``w [V][Dm]``
+    (bf16), ``draft`` int32 ``[B][M-1]``.  Returns
+    ``(argmax [B][M], accept_len [B], out_tokens [B][M], n_out [B])``."""
+    _dev(h, "h", torch.bfloat16)
+    _dev(w, "w", torch.bfloat16)
+    _dev(draft, "draft", torch.int32)
+    B, M, Dm = h.shape
+    V = w.shape[0]
+    if w.shape[1] != Dm:
+        raise ValueError("w must be [V][Dm]")
+    dev = h.device
+    argmax = torch.empty((B, M), dtype=torch.int32, device=dev) if argmax is None else argmax
+    accept_len = torch.empty(B, dtype=torch.int32, device=dev) if accept_len is None else accept_len
+    out_tokens = torch.empty((B, M), dtype=torch.int32, device=dev) if out_tokens is None else out_tokens
+    n_out = torch.empty(B, dtype=torch.int32, device=dev) if n_out is None else n_out
+    for t, n in ((argmax, "argmax"), (accept_len, "accept_len"), (out_tokens, "out_tokens"), (n_out, "n_out")):
+        _dev(t, n, torch.int32)
+    if workspace is None:
+        workspace = lm_head_argmax_workspace(B * M, V, dev)
+    _check(lib().vc_lm_head_accept(B, M, Dm, V, _ptr(h), _ptr(w), _ptr(draft), _ptr(argmax), _ptr(accept_len),
+                                   _ptr(out_tokens), _ptr(n_out), _ptr(workspace),
+                                   workspace.numel() * workspace.element_size(), _stream(stream)))
+    return argmax, accept_len, out_tokens, n_out
 
 
 def commit_rows(blk_k, blk_v, n_out, dst_k, dst_v, length, degree=None, v_blocked=False, stream=None):

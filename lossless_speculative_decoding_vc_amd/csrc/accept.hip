@@ -121,7 +121,13 @@ hipError_t launch_argmax(int rows, int V, int dtype, const void *logits, int *ou
 hipError_t launch_accept(const vc_accept_args &a, hipStream_t s) {
   hipError_t e = launch_argmax(a.B * a.M, a.V, a.logit_dtype, a.logits, a.argmax, 1, s);
   if (e != hipSuccess) return e;
-  accept_rows<<<a.B, 64, 0, s>>>(a.draft, a.argmax, a.M, a.accept_len, a.out_tokens, a.n_out);
+  return launch_accept_rows(a.B, a.M, a.draft, a.argmax, a.accept_len, a.out_tokens, a.n_out, s);
+}
+
+hipError_t launch_accept_rows(int B, int M, const int32_t *draft, const int32_t *argmax, int32_t *accept_len,
+                              int32_t *out_tokens, int32_t *n_out, hipStream_t s) {
+  if (B == 0) return hipSuccess;
+  accept_rows<<<B, 64, 0, s>>>(draft, argmax, M, accept_len, out_tokens, n_out);
   return hipGetLastError();
 }
 

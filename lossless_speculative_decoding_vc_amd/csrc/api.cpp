@@ -197,6 +197,51 @@ vc_status vc_lm_head(int32_t R, int32_t Dm, int32_t V, const void *h, const void
   return VC_OK;
 }
 
+size_t vc_lm_head_argmax_workspace_size(int32_t R, int32_t V) {
+  if (R <= 0 || V <= 0) return 0;
+  return vc::lm_argmax_workspace(R, V);
+}
+
+namespace {
+vc_status check_lm_argmax(int32_t R, int32_t Dm, int32_t V, const void *h, const void *w, const void *out,
+                          void *ws, size_t ws_bytes) {
+  REQ(R >= 0 && V >= 1 && Dm >= 32, "R >= 0, V >= 1 and Dm >= 32 required");
+  if (Dm % 32) return fail(VC_ENOTSUP, "Dm (%d) must be a multiple of 32", Dm);
+  REQ(Dm <= (1 << 20), "Dm (%d) above 2^20", Dm);
+  if (R == 0) return VC_OK;
+  REQ(h && w && out && ws, "null h, w, output or workspace");
+  REQ(aligned16(h) && aligned16(w) && aligned16(ws), "h, w and workspace must be 16-byte aligned");
+  REQ(ws_bytes >= vc::lm_argmax_workspace(R, V), "workspace of %zu bytes is below the %zu required", ws_bytes,
+      vc::lm_argmax_workspace(R, V));
+  return VC_OK;
+}
+}  // namespace
+
+vc_status vc_lm_head_argmax(int32_t R, int32_t Dm, int32_t V, const void *h, const void *w, int32_t *out,
+                            int32_t out_stride, void *workspace, size_t workspace_bytes, void *stream) {
+  REQ(out_stride >= 1, "out_stride must be >= 1");
+  vc_status st = check_lm_argmax(R, Dm, V, h, w, out, workspace, workspace_bytes);
+  if (st != VC_OK || R == 0) return st;
+  return hip_status(vc::launch_lm_argmax(R, Dm, V, h, w, out, out_stride, workspace, (hipStream_t)stream),
+                    "vc_lm_head_argmax launch");
+}
+
+vc_status vc_lm_head_accept(int32_t B, int32_t M, int32_t Dm, int32_t V, const void *h, const void *w,
+                            const int32_t *draft, int32_t *argmax, int32_t *accept_len, int32_t *out_tokens,
+                            int32_t *n_out, void *workspace, size_t workspace_bytes, void *stream) {
+  REQ(B >= 0 && M >= 1, "B >= 0 and M >= 1 required");
+  REQ((int64_t)B * M <= 0x7fffffff, "B * M overflows");
+  vc_status st = check_lm_argmax(B * M, Dm, V, h, w, argmax, workspace, workspace_bytes);
+  if (st != VC_OK || B == 0) return st;
+  REQ(accept_len && out_tokens && n_out, "null accept output");
+  REQ(M == 1 || draft, "draft is required when M > 1");
+  hipStream_t s = (hipStream_t)stream;
+  st = hip_status(vc::launch_lm_argmax(B * M, Dm, V, h, w, argmax, 1, workspace, s), "vc_lm_head_accept launch");
+  if (st != VC_OK) return st;
+  return hip_status(vc::launch_accept_rows(B, M, draft, argmax, accept_len, out_tokens, n_out, s),
+                    "vc_lm_head_accept launch");
+}
+
 vc_status vc_commit_rows(int32_t B, int32_t Hkv, int32_t D, int32_t M, int32_t dtype, int64_t cap,
                          int32_t dst_v_blocked, const void *blk_k, const void *blk_v, const int32_t *n_out,
                          void *dst_k, void *dst_v,

@@ -20,6 +20,13 @@ SplitPlan plan_verify(const vc_verify_args &a);
 hipError_t launch_accept(const vc_accept_args &a, hipStream_t s);
 hipError_t launch_argmax(int rows, int V, int dtype, const void *logits, int *out, int out_stride,
                          hipStream_t s);
+// Acceptance over precomputed argmax rows (argmax [B][M], draft [B][M-1]).
+hipError_t launch_accept_rows(int B, int M, const int32_t *draft, const int32_t *argmax, int32_t *accept_len,
+                              int32_t *out_tokens, int32_t *n_out, hipStream_t s);
+// LM head fused with the argmax (see lmhead_argmax.hip).
+size_t lm_argmax_workspace(int R, int V);
+hipError_t launch_lm_argmax(int R, int Dm, int V, const void *h, const void *w, int *out, int out_stride,
+                            void *ws, hipStream_t s);
 hipError_t launch_commit(int B, int Hkv, int D, int M, int elem_bytes, int64_t cap, int v_blocked, const void *blk_k,
                          const void *blk_v, const int32_t *n_out, void *dst_k, void *dst_v, int32_t *len,
                          float *degree, int64_t deg_b_stride, int64_t deg_h_stride, hipStream_t s);

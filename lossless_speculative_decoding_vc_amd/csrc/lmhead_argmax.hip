@@ -1,0 +1,240 @@
+// LM head fused with the greedy choice: for every hidden row, the argmax over
+// the vocabulary of h W^T, without writing the logits.
+//
+// "Riepilogo Tecnico: VeriCache", "Algoritmo Principale": the drafter picks
+// each draft token greedily (step 1) and the verify pass takes the full-cache
+// greedy prediction at every block row (steps 2-3).  Both only need the
+// index of the largest logit, so the [rows][vocab] logit matrix (69 MB at
+// 528 rows x 32768 fp32) never has to reach HBM.
+//
+// Design (gfx950):
+//  * W is vocab-major [V][Dm] (a linear layer's weight) and h is [R][Dm], so
+//    both MFMA operands reduce along their contiguous axis and load as 16-byte
+//    vectors: logits^T tile = W_tile (A, 16 vocab x 32 k) x h_tile^T (B,
+//    32 k x 16 rows) on v_mfma_f32_16x16x32_bf16, fp32 accumulation.
+//  * a workgroup owns a tile of BV vocab entries x BR hidden rows and walks
+//    the whole Dm axis in 32-wide k-steps through a ring of S LDS stages
+//    filled by direct global->LDS loads (global_load_lds_dwordx4: no
+//    registers held for prefetch).  One wave-wide load moves 16 rows x 64 B
+//    into 1 KB of contiguous LDS; which 16-byte piece a lane fetches is
+//    XOR-swizzled by row so the operand reads are free of bank conflicts.
+//  * verify-sized row counts (R > 64) use 8 waves (two per SIMD, so one
+//    wave's LDS reads overlap the other's MFMAs), 4 along vocab x 2 along
+//    rows, each wave 64 vocab x 144 rows (36 accumulator tiles): BV = 256,
+//    BR = 288.  At 528 rows x 32768 vocab that is 2 x 128 = 256 workgroups,
+//    one per CU; the two row tiles of a vocab tile sit on the same XCD so W
+//    leaves HBM once and the second read hits that XCD's L2.
+//  * drafter-sized row counts (R <= 64) stream W once with one row tile:
+//    4 waves of 16*NV vocab x R rows and an 8-deep ring (HBM-bound).
+//  * epilogue: each lane scans its accumulators in vocab order, lanes and
+//    waves that share a row meet by shuffles and LDS, and the tile writes
+//    one (max, index) pair per row; a second kernel reduces the pairs of a
+//    row over the vocab tiles.  Ties go to the lowest vocab index and NaN
+//    logits never win, as in the unfused argmax.
+#include "common.h"
+#include "launch.h"
+
+namespace vc {
+namespace {
+
+struct Best {
+  float v;
+  int i;
+};
+
+struct LmParams {
+  int R, Dm, V, n_vt;
+  const uint16_t *h, *w;   // h [R][Dm], w [V][Dm]
+  Best *part;              // [R][n_vt]
+};
+
+VC_DEVICE void better(float &bv, int &bi, float v, int i) {
+  if (v > bv || (v == bv && i < bi)) { bv = v; bi = i; }
+}
+
+// One 16-byte direct global->LDS load per lane with a scalar 64-bit base and
+// a 32-bit per-lane byte offset: lane i's piece lands at lds_addr + 16*i.
+// Completion is tracked with s_waitcnt vmcnt and a workgroup barrier.
+VC_DEVICE void lds_load16(uint32_t voff, const void *sbase, uint32_t lds_addr) {
+  __asm__ volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "s"(lds_addr)
+                   : "memory", "m0");
+}
+
+// Physical 16-byte slot of logical slot s (k = 8s..8s+7) in LDS row r.
+VC_DEVICE int swz(int r, int s) { return s ^ ((r >> 2) & 3); }
+
+template <int NV, int NR, int WV, int WR, int S>
+__global__ __launch_bounds__(WV *WR * 64) void lm_argmax(LmParams p) {
+  constexpr int W = WV * WR;
+  constexpr int BV = 16 * NV * WV, BR = 16 * NR * WR;
+  constexpr int kBlkW = BV / 16, kBlk = kBlkW + BR / 16;   // 1 KB blocks per stage
+  constexpr int kStage = kBlk * 1024;
+  constexpr int kMine = (kBlk + W - 1) / W;                 // load slots per wave per stage
+  constexpr int kMinLoads = kBlk / W;                       // loads every wave issues per stage
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[S * kStage];
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, col = lane & 15, grp = lane >> 4;
+  const int wv = wave % WV, wr = wave / WV;
+
+  // Tile of this workgroup.  Workgroups are dealt round-robin to the 8 XCDs;
+  // when the grid divides evenly, XCD x takes a contiguous run of tiles in
+  // (vocab tile, row tile) order, so the row tiles sharing a vocab tile
+  // share that XCD's L2.
+  const int n_rt = (p.R + BR - 1) / BR;
+  const int nb = gridDim.x;
+  int t = blockIdx.x;
+  if ((nb & 7) == 0) t = (t & 7) * (nb >> 3) + (t >> 3);
+  const int vt = t / n_rt, rt = t % n_rt;
+  const int v0 = vt * BV, r0 = rt * BR;
+
+  // Per-lane byte offsets of this wave's load slots (fixed across k-steps);
+  // rows past the end are clamped to the last row (loaded, never used).
+  const char *wtile = reinterpret_cast<const char *>(p.w + (size_t)v0 * p.Dm);
+  const char *htile = reinterpret_cast<const char *>(p.h + (size_t)r0 * p.Dm);
+  uint32_t voff[kMine];
+#pragma unroll
+  for (int j = 0; j < kMine; ++j) {
+    const int q = wave + j * W;
+    const int r = 16 * (q < kBlkW ? q : q - kBlkW) + (lane >> 2);   // row within its tile
+    const int lim = q < kBlkW ? p.V - v0 : p.R - r0;
+    const int rc = r < lim ? r : lim - 1;
+    voff[j] = (uint32_t)(rc * p.Dm * 2 + 16 * swz(r, lane & 3));
+  }
+  const uint32_t lds_base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t *)lds;
+  const int T = p.Dm / 32;
+
+  auto issue = [&](int ks) __attribute__((always_inline)) {
+    const uint32_t st = lds_base + (uint32_t)((ks % S) * kStage);
+    const char *wb = wtile + ks * 64, *hb = htile + ks * 64;
+#pragma unroll
+    for (int j = 0; j < kMine; ++j) {
+      const int q = wave + j * W;
+      if (q < kBlk) lds_load16(voff[j], q < kBlkW ? wb : hb, st + q * 1024);
+    }
+  };
+
+  f32x4 acc[NV][NR];
+#pragma unroll
+  for (int a = 0; a < NV; ++a)
+#pragma unroll
+    for (int b = 0; b < NR; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+#pragma unroll
+  for (int ks = 0; ks < S - 1; ++ks)
+    if (ks < T) issue(ks);
+
+  for (int ks = 0; ks < T; ++ks) {
+    // This wave's loads of step ks are done once at most the loads of the
+    // later steps already issued (ks+1 .. ks+S-2) are outstanding; counting
+    // the fewest loads a wave issues per step only waits longer.
+    if (ks + S - 2 < T) __asm__ volatile("s_waitcnt vmcnt(%0)" ::"n"((S - 2) * kMinLoads) : "memory");
+    else __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();   // every wave's loads of step ks have landed; step ks-1's stage is free
+    if (ks + S - 1 < T) issue(ks + S - 1);
+    const uint8_t *st = lds + (ks % S) * kStage;
+    bf16x8 a[NV], b[NR];
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int r = 16 * (wv * NV + i) + col;
+      a[i] = as_bf16x8(*reinterpret_cast<const u32x4 *>(st + r * 64 + 16 * swz(r, grp)));
+    }
+#pragma unroll
+    for (int i = 0; i < NR; ++i) {
+      const int r = 16 * (wr * NR + i) + col;
+      b[i] = as_bf16x8(*reinterpret_cast<const u32x4 *>(st + kBlkW * 1024 + r * 64 + 16 * swz(r, grp)));
+    }
+#pragma unroll
+    for (int i = 0; i < NV; ++i)
+#pragma unroll
+      for (int j = 0; j < NR; ++j) acc[i][j] = mfma16x16x32(a[i], b[j], acc[i][j]);
+  }
+
+  // Epilogue.  acc[i][j][e] is the logit of vocab v0 + 16*(wv*NV + i) +
+  // 4*grp + e at row r0 + 16*(wr*NR + j) + col.
+  __syncthreads();   // the ring is reused for the cross-wave exchange
+  Best *xch = reinterpret_cast<Best *>(lds);   // [BR][WV]
+#pragma unroll
+  for (int j = 0; j < NR; ++j) {
+    float bv = kNegInf;
+    int bi = 0x7fffffff;
+#pragma unroll
+    for (int i = 0; i < NV; ++i)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int v = v0 + 16 * (wv * NV + i) + 4 * grp + e;
+        if (v < p.V) better(bv, bi, acc[i][j][e], v);
+      }
+    better(bv, bi, __shfl_xor(bv, 16, 64), __shfl_xor(bi, 16, 64));
+    better(bv, bi, __shfl_xor(bv, 32, 64), __shfl_xor(bi, 32, 64));
+    if (grp == 0) xch[(16 * (wr * NR + j) + col) * WV + wv] = Best{bv, bi};
+  }
+  __syncthreads();
+  for (int rr = tid; rr < BR; rr += W * 64) {
+    if (r0 + rr >= p.R) break;
+    float bv = kNegInf;
+    int bi = 0x7fffffff;
+#pragma unroll
+    for (int x = 0; x < WV; ++x) better(bv, bi, xch[rr * WV + x].v, xch[rr * WV + x].i);
+    p.part[(size_t)(r0 + rr) * p.n_vt + vt] = Best{bv, bi};
+  }
+}
+
+// Row argmax from the per-tile pairs: one wave per row.
+__global__ __launch_bounds__(256) void argmax_partials(const Best *__restrict__ part, int n_vt, int R, int V,
+                                                       int *__restrict__ out, int out_stride) {
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (row >= R) return;
+  float bv = kNegInf;
+  int bi = 0x7fffffff;
+  for (int j = lane; j < n_vt; j += 64) {
+    const Best b = part[(size_t)row * n_vt + j];
+    better(bv, bi, b.v, b.i);
+  }
+  for (int o = 32; o > 0; o >>= 1) better(bv, bi, __shfl_xor(bv, o, 64), __shfl_xor(bi, o, 64));
+  if (lane == 0) out[(size_t)row * out_stride] = (bi < V) ? bi : 0;
+}
+
+// Configurations: verify-sized (R > 64) and drafter-sized (R <= 64, NR rows
+// blocks of 16).
+constexpr int kBigNV = 4, kBigNR = 9, kBigWV = 4, kBigWR = 2, kBigS = 4;
+constexpr int kSmallNV = 2, kSmallWV = 4, kSmallS = 8;
+
+template <int NV, int NR, int WV, int WR, int S>
+hipError_t launch_cfg(const LmParams &p0, hipStream_t s) {
+  constexpr int BV = 16 * NV * WV, BR = 16 * NR * WR;
+  LmParams p = p0;
+  p.n_vt = (p.V + BV - 1) / BV;
+  const int n_rt = (p.R + BR - 1) / BR;
+  lm_argmax<NV, NR, WV, WR, S><<<p.n_vt * n_rt, WV * WR * 64, 0, s>>>(p);
+  return hipGetLastError();
+}
+
+int vocab_tile(int R) { return R > 64 ? 16 * kBigNV * kBigWV : 16 * kSmallNV * kSmallWV; }
+
+}  // namespace
+
+size_t lm_argmax_workspace(int R, int V) {
+  const int bv = vocab_tile(R);
+  return (size_t)R * ((V + bv - 1) / bv) * sizeof(Best);
+}
+
+hipError_t launch_lm_argmax(int R, int Dm, int V, const void *h, const void *w, int *out, int out_stride,
+                            void *ws, hipStream_t s) {
+  if (R == 0) return hipSuccess;
+  LmParams p{R, Dm, V, 0, (const uint16_t *)h, (const uint16_t *)w, (Best *)ws};
+  hipError_t e;
+  if (R > 64) e = launch_cfg<kBigNV, kBigNR, kBigWV, kBigWR, kBigS>(p, s);
+  else if (R > 48) e = launch_cfg<kSmallNV, 4, kSmallWV, 1, kSmallS>(p, s);
+  else if (R > 32) e = launch_cfg<kSmallNV, 3, kSmallWV, 1, kSmallS>(p, s);
+  else if (R > 16) e = launch_cfg<kSmallNV, 2, kSmallWV, 1, kSmallS>(p, s);
+  else e = launch_cfg<kSmallNV, 1, kSmallWV, 1, kSmallS>(p, s);
+  if (e != hipSuccess) return e;
+  const int bv = vocab_tile(R);
+  argmax_partials<<<(R + 3) / 4, 256, 0, s>>>((const Best *)ws, (V + bv - 1) / bv, R, V, out, out_stride);
+  return hipGetLastError();
+}
+
+}  // namespace vc

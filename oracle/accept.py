@@ -20,9 +20,13 @@ Readings where the pages are silent:
 
 Parity: pinned by brute force over every match/mismatch pattern for small k,
 by hand-derived cases under ``tests/golden/`` and by ``numpy.argmax``'s
-first-occurrence rule.
+first-occurrence rule.  The LM-head argmax (:func:`lm_head_argmax`) is pinned
+by exact integer arithmetic on integer-valued inputs and by the
+Cauchy-Schwarz maximum of planted equal-norm rows.
 """
 import numpy as np
+
+from .formats import bf16_to_f64
 
 
 def greedy_argmax(row):
@@ -78,3 +82,33 @@ def accept_batch(logits, drafts):
         toks[b, :len(emitted)] = emitted
         n_out[b] = len(emitted)
     return am, n_acc, toks, n_out
+
+
+def lm_head_logits(h_bits, w_bits):
+    """Logits of bf16 hidden rows through a vocab-major bf16 LM head:
+    ``logit[r][v] = sum_k h[r][k] * w[v][k]`` with ``h [R][Dm]`` and
+    ``w [V][Dm]`` given as bf16 bit patterns.  Products of bf16 values are
+    exact in fp64 and the sum is accumulated in fp64."""
+    h = bf16_to_f64(np.asarray(h_bits))
+    w = bf16_to_f64(np.asarray(w_bits))
+    return h @ w.T
+
+
+def lm_head_argmax(h_bits, w_bits):
+    """Greedy token of each hidden row ("Algoritmo Principale", steps 1 and
+    3): :func:`greedy_argmax` of every row of :func:`lm_head_logits`."""
+    return np.array([greedy_argmax(r) for r in lm_head_logits(h_bits, w_bits)], dtype=np.int32)
+
+
+def fp32_sum_bound(h_bits, w_bits):
+    """Per-row bound on how far any fp32 evaluation of a logit (exact
+    products, fp32 additions in any order) can lie from the exact value:
+    ``gamma_Dm * max_v sum_k |h[r][k] w[v][k]|`` with ``gamma_n = n u / (1 - n u)``
+    and ``u = 2^-24`` (the standard bound for recursive summation).
+    Returns ``[R]``."""
+    h = np.abs(bf16_to_f64(np.asarray(h_bits)))
+    w = np.abs(bf16_to_f64(np.asarray(w_bits)))
+    n = h.shape[1]
+    u = 2.0 ** -24
+    gamma = n * u / (1 - n * u)
+    return gamma * (h @ w.T).max(axis=1)

@@ -15,14 +15,14 @@ import numpy as np
 __all__ = [
     "rng", "f32_to_bf16_bits", "normal_bf16", "normal_f32", "tiny_weights",
     "tiny_prompt", "kept_random", "degrees", "int4_grid", "pack_codes",
-    "planted_accept", "planted_logits", "csm_planted", "TINY_WEIGHT_ORDER", "TID", "torch_normal",
+    "planted_accept", "planted_logits", "csm_planted", "lm_planted", "TINY_WEIGHT_ORDER", "TID", "torch_normal",
     "torch_randint",
 ]
 
 # Tensor ids used in SeedSequence keys.
 TID = dict(q=1, k=2, v=3, tail_k=4, tail_v=5, blk_k=6, blk_v=7, kept=8,
            degree=9, kcode=10, vcode=11, kscale=12, vscale=13, logits=14,
-           accept=15, hidden=16, lm=17, csm=18)
+           accept=15, hidden=16, lm=17, csm=18, lm_head=19)
 
 
 def rng(cfg_seed, tensor_id, *index):
@@ -243,6 +243,20 @@ def planted_logits(y, vocab, cfg_seed, margin=4.0, ties=0):
 # --------------------------------------------------------------------------
 # Bulk device-side draws for the full-size workloads (torch's seeded Philox
 # generator on the GPU; only random numbers, no method arithmetic).
+def lm_planted(V, Dm, targets, cfg_seed, scale_exp=-4):
+    """A vocab-major LM head ``w [V][Dm]`` of random +-2^scale_exp entries
+    (distinct rows, all of the same norm) and hidden rows ``h = w[targets]``,
+    as bf16 bit patterns ``(h [R][Dm], w [V][Dm])``."""
+    g = rng(cfg_seed, TID["lm_head"], 0)
+    while True:
+        signs = g.integers(0, 2, size=(V, Dm), dtype=np.int8)
+        if len(np.unique(signs, axis=0)) == V:
+            break
+    w = np.where(signs == 1, 1.0, -1.0).astype(np.float32) * np.float32(2.0 ** scale_exp)
+    wb = f32_to_bf16_bits(w)
+    return wb[np.asarray(targets).reshape(-1)], wb
+
+
 def torch_normal(shape, seed, device, dtype, std=1.0):
     import torch
     g = torch.Generator(device=device)

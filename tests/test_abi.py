@@ -91,3 +91,22 @@ def test_workspace_plan_is_host_only(L):
     assert ws > 0 and ws % (32 * 32 * 129 * 4) == 0
     # fp32 mode runs unsplit
     assert L.vc_draft_workspace_size(ctypes.byref(_draft(dtype=1))) == 0
+
+
+def test_lm_head_argmax_validation_is_host_only(L):
+    # the fused LM head + argmax: bad shapes, null pointers and a short
+    # workspace are rejected before any GPU work
+    fake = ctypes.c_void_p(1 << 20)   # aligned, never dereferenced on these paths
+    ws_need = L.vc_lm_head_argmax_workspace_size(528, 32768)
+    assert ws_need == 528 * 128 * 8   # one (max, index) pair per row and 256-entry vocabulary tile
+    assert L.vc_lm_head_argmax_workspace_size(16, 32768) == 16 * 256 * 8
+    assert L.vc_lm_head_argmax(4, 48, 100, fake, fake, fake, 1, fake, 1 << 20, None) == vcb.VC_ENOTSUP
+    assert L.vc_lm_head_argmax(4, 64, 100, fake, fake, fake, 1, fake, 8, None) == vcb.VC_EINVAL
+    assert b"workspace" in L.vc_last_error()
+    assert L.vc_lm_head_argmax(4, 64, 100, None, fake, fake, 1, fake, 1 << 20, None) == vcb.VC_EINVAL
+    assert L.vc_lm_head_argmax(4, 64, 100, fake, fake, fake, 0, fake, 1 << 20, None) == vcb.VC_EINVAL
+    assert L.vc_lm_head_argmax(0, 64, 100, None, None, None, 1, None, 0, None) == vcb.VC_OK
+    assert L.vc_lm_head_accept(2, 3, 64, 100, fake, fake, None, fake, fake, fake, fake, fake, 1 << 20,
+                               None) == vcb.VC_EINVAL   # M > 1 needs drafts
+    assert L.vc_lm_head_accept(0, 3, 64, 100, None, None, None, None, None, None, None, None, 0,
+                               None) == vcb.VC_OK

@@ -1,0 +1,147 @@
+"""GPU parity of the LM head fused with the greedy choice (vc_lm_head_argmax,
+vc_lm_head_accept) against the oracle.
+
+The kernel sums exact bf16 products in fp32, the oracle in fp64.  Where a
+row's two largest exact logits are further apart than twice the fp32
+summation bound, the argmax is unique and must match exactly; on the few
+rows closer than that, the kernel's choice must be a logit within that
+distance of the maximum (several answers are correct there).  Planted
+equal-norm rows (Cauchy-Schwarz) give inputs whose argmax is known exactly.
+"""
+import numpy as np
+import pytest
+
+import synthetic as S
+from oracle.accept import accept_batch, fp32_sum_bound, lm_head_logits
+
+from .helpers import to_dev, to_dev_bf16
+
+pytestmark = pytest.mark.gpu
+
+
+def _check_rows(got, h_bits, w_bits, rows=None, min_clear=0.9):
+    rows = np.arange(h_bits.shape[0]) if rows is None else np.asarray(rows)
+    lg = lm_head_logits(h_bits[rows], w_bits)
+    bound = fp32_sum_bound(h_bits[rows], w_bits)
+    srt = np.sort(lg, axis=1)
+    top = srt[:, -1]
+    margin = top - srt[:, -2] if lg.shape[1] > 1 else np.full(len(rows), np.inf)
+    ref = np.array([int(np.flatnonzero(r == r.max())[0]) for r in lg])
+    clear = margin > 2 * bound
+    assert clear.mean() >= min_clear, "inputs without clear maxima test nothing"
+    np.testing.assert_array_equal(got[rows][clear], ref[clear])
+    for i in np.flatnonzero(~clear):
+        assert lg[i, got[rows[i]]] >= top[i] - 2 * bound[i], (rows[i], got[rows[i]], ref[i])
+
+
+def _inputs(R, Dm, V, seed):
+    rng = np.random.default_rng(seed)
+    h = S.f32_to_bf16_bits(rng.standard_normal((R, Dm), dtype=np.float32))
+    w = S.f32_to_bf16_bits(rng.standard_normal((V, Dm), dtype=np.float32) * np.float32(0.02))
+    return h, w
+
+
+@pytest.mark.parametrize("R,Dm,V", [(1, 256, 512), (5, 96, 513), (16, 256, 1000), (33, 128, 4096),
+                                    (64, 64, 700), (65, 256, 2000), (300, 96, 1500), (528, 256, 1031)])
+def test_argmax_random(R, Dm, V):
+    import torch
+    import lossless_speculative_decoding_vc_amd as vc
+    h, w = _inputs(R, Dm, V, seed=R * 7 + V)
+    out = vc.lm_head_argmax(to_dev_bf16(h), to_dev_bf16(w))
+    torch.cuda.synchronize()
+    _check_rows(out.cpu().numpy(), h, w)
+
+
+@pytest.mark.parametrize("R", [16, 528])
+def test_argmax_full_size_sampled(R):
+    # the staggered batch's LM head (Dm 5120, vocabulary 32768): drafting rows and verify block rows;
+    # the oracle evaluates 40 sampled rows; at Dm 5120 the worst-case fp32 bound leaves about one row in
+    # five without a provably unique maximum (those are checked for validity)
+    import torch
+    import lossless_speculative_decoding_vc_amd as vc
+    Dm, V = 5120, 32768
+    h, w = _inputs(R, Dm, V, seed=99 + R)
+    out = vc.lm_head_argmax(to_dev_bf16(h), to_dev_bf16(w)).cpu().numpy()
+    torch.cuda.synchronize()
+    rows = np.unique(np.concatenate([[0, R - 1], np.random.default_rng(R).integers(0, R, 38)]))
+    _check_rows(out, h, w, rows, min_clear=0.6)
+
+
+@pytest.mark.parametrize("R,Dm,V", [(528, 512, 32768), (16, 5120, 4096), (100, 64, 300)])
+def test_argmax_planted_exact(R, Dm, V):
+    import torch
+    import lossless_speculative_decoding_vc_amd as vc
+    targets = np.random.default_rng(R + Dm).integers(0, V, R)
+    targets[:3] = [0, V - 1, V // 2]
+    h, w = S.lm_planted(V, Dm, targets, cfg_seed=R)
+    out = vc.lm_head_argmax(to_dev_bf16(h), to_dev_bf16(w))
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(out.cpu().numpy(), targets)
+
+
+def test_argmax_ties_pick_lowest_index():
+    # exact ties: duplicated rows of w give bit-identical fp32 logits
+    import torch
+    import lossless_speculative_decoding_vc_amd as vc
+    V, Dm = 2048, 256
+    targets = np.array([1500, 7, 300, 2047, 1024, 600] * 3)
+    h, w = S.lm_planted(V, Dm, targets, cfg_seed=8)
+    w = w.copy()
+    lower = {1500: 3, 300: 299, 2047: 1023, 1024: 256, 600: 599}   # duplicates at lower indices
+    for hi, lo in lower.items():
+        w[lo] = w[hi]
+    w[2000] = w[7]   # a duplicate at a higher index does not win
+    out = vc.lm_head_argmax(to_dev_bf16(h), to_dev_bf16(w))
+    torch.cuda.synchronize()
+    expect = [lower.get(int(t), int(t)) for t in targets]
+    np.testing.assert_array_equal(out.cpu().numpy(), expect)
+
+
+def test_out_stride_writes_draft_columns():
+    import torch
+    import lossless_speculative_decoding_vc_amd as vc
+    R, V, Dm, k = 16, 1000, 128, 32
+    targets = np.random.default_rng(1).integers(0, V, R)
+    h, w = S.lm_planted(V, Dm, targets, cfg_seed=9)
+    drafts = torch.full((R, k), -5, dtype=torch.int32, device="cuda")
+    vc.lm_head_argmax(to_dev_bf16(h), to_dev_bf16(w), out=drafts.view(-1)[3:], out_stride=k)
+    torch.cuda.synchronize()
+    d = drafts.cpu().numpy()
+    np.testing.assert_array_equal(d[:, 3], targets)
+    assert np.all(np.delete(d, 3, axis=1) == -5)
+
+
+@pytest.mark.parametrize("B,k,V,Dm", [(16, 32, 32768, 512), (3, 8, 512, 256), (2, 0, 300, 64)])
+def test_lm_head_accept_planted(B, k, V, Dm):
+    import torch
+    import lossless_speculative_decoding_vc_amd as vc
+    M = k + 1
+    force = {0: 0, 1: k} if B >= 2 else {}
+    y, d, n = S.planted_accept(B, k, V, cfg_seed=4, n_lo=min(24, k), n_hi=k, force=force)
+    h, w = S.lm_planted(V, Dm, y.reshape(-1), cfg_seed=B + k)
+    dd = to_dev(d.astype(np.int32).reshape(B, k)) if k else torch.zeros((B, 0), dtype=torch.int32, device="cuda")
+    got = vc.lm_head_accept(to_dev_bf16(h).view(B, M, Dm), to_dev_bf16(w), dd)
+    torch.cuda.synchronize()
+    ref = accept_batch(lm_head_logits(h, w).reshape(B, M, V), d.reshape(B, k))
+    for g, r, name in zip(got, ref, ("argmax", "accept_len", "out_tokens", "n_out")):
+        np.testing.assert_array_equal(g.cpu().numpy(), r, err_msg=name)
+    np.testing.assert_array_equal(got[1].cpu().numpy(), n)
+
+
+def test_errors_and_empty():
+    import torch
+    import lossless_speculative_decoding_vc_amd as vc
+    h = torch.zeros((4, 48), dtype=torch.bfloat16, device="cuda")
+    w = torch.zeros((100, 48), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(vc.VcError):   # Dm not a multiple of 32
+        vc.lm_head_argmax(h, w)
+    h = torch.zeros((4, 64), dtype=torch.bfloat16, device="cuda")
+    w = torch.zeros((100, 64), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(vc.VcError):   # workspace too small
+        vc.lm_head_argmax(h, w, workspace=torch.empty(16, dtype=torch.uint8, device="cuda"))
+    out = vc.lm_head_argmax(h[:0], w)
+    assert out.numel() == 0
+    # all-zero logits: every entry ties, the lowest index wins
+    out = vc.lm_head_argmax(h, w)
+    torch.cuda.synchronize()
+    assert out.cpu().tolist() == [0, 0, 0, 0]
