@@ -18,6 +18,8 @@
 //    registers held for prefetch).  One wave-wide load moves 16 rows x 64 B
 //    into 1 KB of contiguous LDS; which 16-byte piece a lane fetches is
 //    XOR-swizzled by row so the operand reads are free of bank conflicts.
+//    Each wave reads the next step's MFMA operands from LDS between the
+//    current step's MFMAs.
 //  * verify-sized row counts (R > 64) use 8 waves (two per SIMD, so one
 //    wave's LDS reads overlap the other's MFMAs), 4 along vocab x 2 along
 //    rows, each wave 64 vocab x 144 rows (36 accumulator tiles): BV = 256,
@@ -121,34 +123,72 @@ __global__ __launch_bounds__(WV *WR * 64) void lm_argmax(LmParams p) {
 #pragma unroll
     for (int b = 0; b < NR; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+  // Ring protocol.  The operands of step ks are read from LDS into
+  // registers during step ks-1's MFMAs, so a step's slot is free once every
+  // wave has passed the barrier at the top of step ks; step ks+S reuses it.
+  // LDS read latency thus stays off the critical path: after the barrier a
+  // wave starts its MFMAs at once, and each row block's MFMAs are followed
+  // by the read of that block's next operand into the registers they free.
 #pragma unroll
-  for (int ks = 0; ks < S - 1; ++ks)
+  for (int ks = 0; ks < S; ++ks)
     if (ks < T) issue(ks);
+  if (S <= T) __asm__ volatile("s_waitcnt vmcnt(%0)" ::"n"((S - 1) * kMinLoads) : "memory");
+  else __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  bf16x8 a[NV], b[NR];
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int r = 16 * (wv * NV + i) + col;
+    a[i] = as_bf16x8(*reinterpret_cast<const u32x4 *>(lds + r * 64 + 16 * swz(r, grp)));
+  }
+#pragma unroll
+  for (int j = 0; j < NR; ++j) {
+    const int r = 16 * (wr * NR + j) + col;
+    b[j] = as_bf16x8(*reinterpret_cast<const u32x4 *>(lds + kBlkW * 1024 + r * 64 + 16 * swz(r, grp)));
+  }
 
   for (int ks = 0; ks < T; ++ks) {
-    // This wave's loads of step ks are done once at most the loads of the
-    // later steps already issued (ks+1 .. ks+S-2) are outstanding; counting
-    // the fewest loads a wave issues per step only waits longer.
-    if (ks + S - 2 < T) __asm__ volatile("s_waitcnt vmcnt(%0)" ::"n"((S - 2) * kMinLoads) : "memory");
-    else __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();   // every wave's loads of step ks have landed; step ks-1's stage is free
-    if (ks + S - 1 < T) issue(ks + S - 1);
-    const uint8_t *st = lds + (ks % S) * kStage;
-    bf16x8 a[NV], b[NR];
+    // Step ks+1 has landed once at most the later steps issued so far
+    // (ks+2 .. ks+S-1) are outstanding (counting the fewest loads a wave
+    // issues per step only waits longer); this wave's reads of step ks are
+    // complete, so after the barrier its slot may be refilled.
+    if (ks + S <= T) __asm__ volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"((S - 2) * kMinLoads) : "memory");
+    else __asm__ volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (ks + S < T) issue(ks + S);
+    // Operands of step ks+1 (on the last step a stale in-bounds slot whose
+    // values are never used).
+    const uint8_t *nst = lds + ((ks + 1) % S) * kStage;
+    bf16x8 na[NV], nb[NR];
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
       const int r = 16 * (wv * NV + i) + col;
-      a[i] = as_bf16x8(*reinterpret_cast<const u32x4 *>(st + r * 64 + 16 * swz(r, grp)));
+      na[i] = as_bf16x8(*reinterpret_cast<const u32x4 *>(nst + r * 64 + 16 * swz(r, grp)));
     }
 #pragma unroll
-    for (int i = 0; i < NR; ++i) {
-      const int r = 16 * (wr * NR + i) + col;
-      b[i] = as_bf16x8(*reinterpret_cast<const u32x4 *>(st + kBlkW * 1024 + r * 64 + 16 * swz(r, grp)));
+    for (int j = 0; j < NR; ++j) {
+#pragma unroll
+      for (int i = 0; i < NV; ++i) acc[i][j] = mfma16x16x32(a[i], b[j], acc[i][j]);
+      const int r = 16 * (wr * NR + j) + col;
+      nb[j] = as_bf16x8(*reinterpret_cast<const u32x4 *>(nst + kBlkW * 1024 + r * 64 + 16 * swz(r, grp)));
+    }
+    // Issue order: the NV reads of na between the first row block's MFMAs,
+    // then one nb read after each row block's NV MFMAs.
+#pragma unroll
+    for (int g = 0; g < NV; ++g) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // DS read
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+    }
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+#pragma unroll
+    for (int j = 1; j < NR; ++j) {
+      __builtin_amdgcn_sched_group_barrier(0x008, NV, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
 #pragma unroll
-    for (int i = 0; i < NV; ++i)
+    for (int i = 0; i < NV; ++i) a[i] = na[i];
 #pragma unroll
-      for (int j = 0; j < NR; ++j) acc[i][j] = mfma16x16x32(a[i], b[j], acc[i][j]);
+    for (int j = 0; j < NR; ++j) b[j] = nb[j];
   }
 
   // Epilogue.  acc[i][j][e] is the logit of vocab v0 + 16*(wv*NV + i) +
