@@ -27,7 +27,11 @@
 //    one per CU; the two row tiles of a vocab tile sit on the same XCD so W
 //    leaves HBM once and the second read hits that XCD's L2.
 //  * drafter-sized row counts (R <= 64) stream W once with one row tile:
-//    4 waves of 16*NV vocab x R rows and an 8-deep ring (HBM-bound).
+//    4 waves of 32 vocab x R rows (HBM-bound).  A ring stage there spans
+//    four k-steps, i.e. 256 contiguous bytes of every weight row (3 stages
+//    in flight), which reads HBM faster than 64-byte pieces of more rows.
+//    Verify-sized tiles keep one k-step per stage: their 34 KB stages
+//    would leave a ring of only two.
 //  * epilogue: each lane scans its accumulators in vocab order, lanes and
 //    waves that share a row meet by shuffles and LDS, and the tile writes
 //    one (max, index) pair per row; a second kernel reduces the pairs of a
@@ -62,17 +66,29 @@ VC_DEVICE void lds_load16(uint32_t voff, const void *sbase, uint32_t lds_addr) {
                    : "memory", "m0");
 }
 
-// Physical 16-byte slot of logical slot s (k = 8s..8s+7) in LDS row r.
-VC_DEVICE int swz(int r, int s) { return s ^ ((r >> 2) & 3); }
+// Physical 16-byte slot of logical slot s in LDS row r when a row holds KS
+// k-steps (4*KS slots of 8 k): the 16 rows one operand read touches land on
+// distinct bank groups.
+template <int KS>
+VC_DEVICE int swz(int r, int s) {
+  constexpr int kShift = KS == 1 ? 2 : (KS == 2 ? 1 : 0);
+  return s ^ ((r >> kShift) & (4 * KS - 1));
+}
 
-template <int NV, int NR, int WV, int WR, int S>
+// Tile of NV x NR 16x16 logit blocks per wave, WV x WR waves, a ring of S
+// LDS stages of KS 32-wide k-steps each.
+template <int NV, int NR, int WV, int WR, int S, int KS>
 __global__ __launch_bounds__(WV *WR * 64) void lm_argmax(LmParams p) {
   constexpr int W = WV * WR;
   constexpr int BV = 16 * NV * WV, BR = 16 * NR * WR;
-  constexpr int kBlkW = BV / 16, kBlk = kBlkW + BR / 16;   // 1 KB blocks per stage
+  constexpr int kRowB = 64 * KS;                            // bytes of a row in one stage
+  constexpr int kRpb = 1024 / kRowB;                        // rows per 1 KB load block
+  constexpr int kSlots = 4 * KS;                            // 16-byte slots per row
+  constexpr int kBlkW = BV / kRpb, kBlk = kBlkW + BR / kRpb;   // 1 KB blocks per stage
   constexpr int kStage = kBlk * 1024;
   constexpr int kMine = (kBlk + W - 1) / W;                 // load slots per wave per stage
   constexpr int kMinLoads = kBlk / W;                       // loads every wave issues per stage
+  static_assert(S * kStage <= 160 * 1024, "ring exceeds LDS");
   __shared__ __attribute__((aligned(1024))) uint8_t lds[S * kStage];
 
   const int tid = threadIdx.x;
@@ -91,7 +107,7 @@ __global__ __launch_bounds__(WV *WR * 64) void lm_argmax(LmParams p) {
   const int vt = t / n_rt, rt = t % n_rt;
   const int v0 = vt * BV, r0 = rt * BR;
 
-  // Per-lane byte offsets of this wave's load slots (fixed across k-steps);
+  // Per-lane byte offsets of this wave's load slots (fixed across stages);
   // rows past the end are clamped to the last row (loaded, never used).
   const char *wtile = reinterpret_cast<const char *>(p.w + (size_t)v0 * p.Dm);
   const char *htile = reinterpret_cast<const char *>(p.h + (size_t)r0 * p.Dm);
@@ -99,96 +115,105 @@ __global__ __launch_bounds__(WV *WR * 64) void lm_argmax(LmParams p) {
 #pragma unroll
   for (int j = 0; j < kMine; ++j) {
     const int q = wave + j * W;
-    const int r = 16 * (q < kBlkW ? q : q - kBlkW) + (lane >> 2);   // row within its tile
+    const int r = kRpb * (q < kBlkW ? q : q - kBlkW) + lane / kSlots;   // row within its tile
     const int lim = q < kBlkW ? p.V - v0 : p.R - r0;
     const int rc = r < lim ? r : lim - 1;
-    voff[j] = (uint32_t)(rc * p.Dm * 2 + 16 * swz(r, lane & 3));
+    voff[j] = (uint32_t)(rc * p.Dm * 2 + 16 * swz<KS>(r, lane % kSlots));
   }
   const uint32_t lds_base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t *)lds;
-  const int T = p.Dm / 32;
+  const int NSt = p.Dm / (32 * KS);   // stages
 
-  auto issue = [&](int ks) __attribute__((always_inline)) {
-    const uint32_t st = lds_base + (uint32_t)((ks % S) * kStage);
-    const char *wb = wtile + ks * 64, *hb = htile + ks * 64;
+  auto issue = [&](int u) __attribute__((always_inline)) {
+    const uint32_t st = lds_base + (uint32_t)((u % S) * kStage);
+    const char *wb = wtile + u * kRowB, *hb = htile + u * kRowB;
 #pragma unroll
     for (int j = 0; j < kMine; ++j) {
       const int q = wave + j * W;
       if (q < kBlk) lds_load16(voff[j], q < kBlkW ? wb : hb, st + q * 1024);
     }
   };
+  // MFMA operands of k-step kk of the stage at st.
+  auto read_a = [&](const uint8_t *st, int kk, int i) __attribute__((always_inline)) {
+    const int r = 16 * (wv * NV + i) + col;
+    return as_bf16x8(*reinterpret_cast<const u32x4 *>(st + r * kRowB + 16 * swz<KS>(r, 4 * kk + grp)));
+  };
+  auto read_b = [&](const uint8_t *st, int kk, int j) __attribute__((always_inline)) {
+    const int r = 16 * (wr * NR + j) + col;
+    return as_bf16x8(
+        *reinterpret_cast<const u32x4 *>(st + BV * kRowB + r * kRowB + 16 * swz<KS>(r, 4 * kk + grp)));
+  };
 
   f32x4 acc[NV][NR];
 #pragma unroll
-  for (int a = 0; a < NV; ++a)
+  for (int i = 0; i < NV; ++i)
 #pragma unroll
-    for (int b = 0; b < NR; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < NR; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // Ring protocol.  The operands of step ks are read from LDS into
-  // registers during step ks-1's MFMAs, so a step's slot is free once every
-  // wave has passed the barrier at the top of step ks; step ks+S reuses it.
-  // LDS read latency thus stays off the critical path: after the barrier a
-  // wave starts its MFMAs at once, and each row block's MFMAs are followed
-  // by the read of that block's next operand into the registers they free.
+  // Ring protocol.  The operands of each k-step are read from LDS into
+  // registers during the previous k-step's MFMAs.  Stage u's last operands
+  // are read while its second-to-last k-step computes, so at the top of its
+  // last k-step every wave waits for stage u+1, passes a barrier, and stage
+  // u+S refills u's slot.  LDS read latency thus stays off the critical
+  // path: after a barrier a wave starts its MFMAs at once, and each row
+  // block's MFMAs are followed by the read of that block's next operand
+  // into the registers they free.
 #pragma unroll
-  for (int ks = 0; ks < S; ++ks)
-    if (ks < T) issue(ks);
-  if (S <= T) __asm__ volatile("s_waitcnt vmcnt(%0)" ::"n"((S - 1) * kMinLoads) : "memory");
+  for (int u = 0; u < S; ++u)
+    if (u < NSt) issue(u);
+  if (S <= NSt) __asm__ volatile("s_waitcnt vmcnt(%0)" ::"n"((S - 1) * kMinLoads) : "memory");
   else __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
   bf16x8 a[NV], b[NR];
 #pragma unroll
-  for (int i = 0; i < NV; ++i) {
-    const int r = 16 * (wv * NV + i) + col;
-    a[i] = as_bf16x8(*reinterpret_cast<const u32x4 *>(lds + r * 64 + 16 * swz(r, grp)));
-  }
+  for (int i = 0; i < NV; ++i) a[i] = read_a(lds, 0, i);
 #pragma unroll
-  for (int j = 0; j < NR; ++j) {
-    const int r = 16 * (wr * NR + j) + col;
-    b[j] = as_bf16x8(*reinterpret_cast<const u32x4 *>(lds + kBlkW * 1024 + r * 64 + 16 * swz(r, grp)));
-  }
+  for (int j = 0; j < NR; ++j) b[j] = read_b(lds, 0, j);
 
-  for (int ks = 0; ks < T; ++ks) {
-    // Step ks+1 has landed once at most the later steps issued so far
-    // (ks+2 .. ks+S-1) are outstanding (counting the fewest loads a wave
-    // issues per step only waits longer); this wave's reads of step ks are
-    // complete, so after the barrier its slot may be refilled.
-    if (ks + S <= T) __asm__ volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"((S - 2) * kMinLoads) : "memory");
-    else __asm__ volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
-    __syncthreads();
-    if (ks + S < T) issue(ks + S);
-    // Operands of step ks+1 (on the last step a stale in-bounds slot whose
-    // values are never used).
-    const uint8_t *nst = lds + ((ks + 1) % S) * kStage;
-    bf16x8 na[NV], nb[NR];
+  for (int u = 0; u < NSt; ++u) {
+    const uint8_t *cur = lds + (u % S) * kStage;
+    // on the last stage a stale in-bounds slot whose values are never used
+    const uint8_t *nxt = lds + ((u + 1) % S) * kStage;
 #pragma unroll
-    for (int i = 0; i < NV; ++i) {
-      const int r = 16 * (wv * NV + i) + col;
-      na[i] = as_bf16x8(*reinterpret_cast<const u32x4 *>(nst + r * 64 + 16 * swz(r, grp)));
-    }
+    for (int kk = 0; kk < KS; ++kk) {
+      if (kk == KS - 1) {
+        // Stage u+1 has landed once at most the later stages issued so far
+        // (u+2 .. u+S-1) are outstanding (counting the fewest loads a wave
+        // issues per stage only waits longer); this wave's reads of stage
+        // u are complete, so after the barrier its slot may be refilled.
+        if (u + S <= NSt) __asm__ volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"((S - 2) * kMinLoads) : "memory");
+        else __asm__ volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+        __syncthreads();
+        if (u + S < NSt) issue(u + S);
+      }
+      const uint8_t *pst = kk == KS - 1 ? nxt : cur;
+      const int pk = kk == KS - 1 ? 0 : kk + 1;
+      bf16x8 na[NV], nb[NR];
 #pragma unroll
-    for (int j = 0; j < NR; ++j) {
+      for (int i = 0; i < NV; ++i) na[i] = read_a(pst, pk, i);
 #pragma unroll
-      for (int i = 0; i < NV; ++i) acc[i][j] = mfma16x16x32(a[i], b[j], acc[i][j]);
-      const int r = 16 * (wr * NR + j) + col;
-      nb[j] = as_bf16x8(*reinterpret_cast<const u32x4 *>(nst + kBlkW * 1024 + r * 64 + 16 * swz(r, grp)));
-    }
-    // Issue order: the NV reads of na between the first row block's MFMAs,
-    // then one nb read after each row block's NV MFMAs.
+      for (int j = 0; j < NR; ++j) {
 #pragma unroll
-    for (int g = 0; g < NV; ++g) {
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // DS read
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
-    }
-    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        for (int i = 0; i < NV; ++i) acc[i][j] = mfma16x16x32(a[i], b[j], acc[i][j]);
+        nb[j] = read_b(pst, pk, j);
+      }
+      // Issue order: the NV reads of na between the first row block's
+      // MFMAs, then one nb read after each row block's NV MFMAs.
 #pragma unroll
-    for (int j = 1; j < NR; ++j) {
-      __builtin_amdgcn_sched_group_barrier(0x008, NV, 0);
+      for (int g = 0; g < NV; ++g) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // DS read
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+      }
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+#pragma unroll
+      for (int j = 1; j < NR; ++j) {
+        __builtin_amdgcn_sched_group_barrier(0x008, NV, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+#pragma unroll
+      for (int i = 0; i < NV; ++i) a[i] = na[i];
+#pragma unroll
+      for (int j = 0; j < NR; ++j) b[j] = nb[j];
     }
-#pragma unroll
-    for (int i = 0; i < NV; ++i) a[i] = na[i];
-#pragma unroll
-    for (int j = 0; j < NR; ++j) b[j] = nb[j];
   }
 
   // Epilogue.  acc[i][j][e] is the logit of vocab v0 + 16*(wv*NV + i) +
@@ -237,19 +262,26 @@ __global__ __launch_bounds__(256) void argmax_partials(const Best *__restrict__ 
   if (lane == 0) out[(size_t)row * out_stride] = (bi < V) ? bi : 0;
 }
 
-// Configurations: verify-sized (R > 64) and drafter-sized (R <= 64, NR rows
-// blocks of 16).
+// Configurations: verify-sized (R > 64) and drafter-sized (R <= 64, NR row
+// blocks of 16).  A stage spans KS k-steps (64*KS contiguous bytes of every
+// row) when Dm allows it, else one.
 constexpr int kBigNV = 4, kBigNR = 9, kBigWV = 4, kBigWR = 2, kBigS = 4;
-constexpr int kSmallNV = 2, kSmallWV = 4, kSmallS = 8;
+constexpr int kSmallNV = 2, kSmallWV = 4, kSmallKS = 4, kSmallS = 3;
 
-template <int NV, int NR, int WV, int WR, int S>
+template <int NV, int NR, int WV, int WR, int S, int KS>
 hipError_t launch_cfg(const LmParams &p0, hipStream_t s) {
   constexpr int BV = 16 * NV * WV, BR = 16 * NR * WR;
   LmParams p = p0;
   p.n_vt = (p.V + BV - 1) / BV;
   const int n_rt = (p.R + BR - 1) / BR;
-  lm_argmax<NV, NR, WV, WR, S><<<p.n_vt * n_rt, WV * WR * 64, 0, s>>>(p);
+  lm_argmax<NV, NR, WV, WR, S, KS><<<p.n_vt * n_rt, WV * WR * 64, 0, s>>>(p);
   return hipGetLastError();
+}
+
+template <int NR>
+hipError_t launch_small(const LmParams &p, hipStream_t s) {
+  if ((p.Dm / 32) % kSmallKS == 0) return launch_cfg<kSmallNV, NR, kSmallWV, 1, kSmallS, kSmallKS>(p, s);
+  return launch_cfg<kSmallNV, NR, kSmallWV, 1, 8, 1>(p, s);
 }
 
 int vocab_tile(int R) { return R > 64 ? 16 * kBigNV * kBigWV : 16 * kSmallNV * kSmallWV; }
@@ -266,11 +298,11 @@ hipError_t launch_lm_argmax(int R, int Dm, int V, const void *h, const void *w, 
   if (R == 0) return hipSuccess;
   LmParams p{R, Dm, V, 0, (const uint16_t *)h, (const uint16_t *)w, (Best *)ws};
   hipError_t e;
-  if (R > 64) e = launch_cfg<kBigNV, kBigNR, kBigWV, kBigWR, kBigS>(p, s);
-  else if (R > 48) e = launch_cfg<kSmallNV, 4, kSmallWV, 1, kSmallS>(p, s);
-  else if (R > 32) e = launch_cfg<kSmallNV, 3, kSmallWV, 1, kSmallS>(p, s);
-  else if (R > 16) e = launch_cfg<kSmallNV, 2, kSmallWV, 1, kSmallS>(p, s);
-  else e = launch_cfg<kSmallNV, 1, kSmallWV, 1, kSmallS>(p, s);
+  if (R > 64) e = launch_cfg<kBigNV, kBigNR, kBigWV, kBigWR, kBigS, 1>(p, s);
+  else if (R > 48) e = launch_small<4>(p, s);
+  else if (R > 32) e = launch_small<3>(p, s);
+  else if (R > 16) e = launch_small<2>(p, s);
+  else e = launch_small<1>(p, s);
   if (e != hipSuccess) return e;
   const int bv = vocab_tile(R);
   argmax_partials<<<(R + 3) / 4, 256, 0, s>>>((const Best *)ws, (V + bv - 1) / bv, R, V, out, out_stride);
