@@ -7,13 +7,14 @@ Default workload -- the staggered mixed batch at Qwen-32B layer shape
 * cohort X (16 requests) VERIFIES a k = 32 block (M = 33 rows) against its
   full 131072-token cache, which is streamed layer by layer from pinned host
   memory over PCIe into a ring of two 8 GiB HBM slots (``vc_stagger``), then
-  takes the block's logits through a 5120 x 32768 bf16 LM head, accepts up to
-  the first mismatch (+ bonus) and commits the verified rows (device append +
-  host write-back);
+  takes the block rows through a 5120 x 32768 bf16 LM head fused with the
+  greedy argmax and the acceptance (``vc_lm_head_accept``: no logits reach
+  HBM), accepts up to the first mismatch (+ bonus) and commits the verified
+  rows (device append + host write-back);
 * cohort Y (16 requests) meanwhile DRAFTS its next 32 tokens: per step and
   layer, decode attention over its 25%-compressed cache (32768 kept tokens
   with log-degree bias, plus the draft tail) in HBM, then per step the LM head
-  and the argmax.
+  fused with the argmax (``vc_lm_head_argmax``).
 The cohorts swap roles every round ("Riepilogo Tecnico: VeriCache",
 "Innovazioni Chiave del Sistema", P1).  One bench step = one round.  Inputs
 are synthetic (seeded): random-normal K/V/q, merge degrees uniform in
@@ -39,6 +40,9 @@ CPU oracle timed on a bounded sample of the same workload.
                  batch 32 x 8 KV heads x 131072 tokens)
   csm128k        one Chunked Soft Matching round (vc_csm_round, r = 1, chunks of
                  64) over the cohort's 131072-token caches (16 x 8 KV heads)
+  lmhead_verify  the verifying cohort's LM head fused with argmax + acceptance
+                 (528 rows x 5120 x 32768), next to the library GEMM + argmax
+  lmhead_draft   the drafting cohort's LM head fused with the argmax (16 rows)
   copy1g         a 1 GiB device copy (reference for the HBM byte counters)
 """
 import argparse
@@ -140,6 +144,7 @@ class Cohort:
 
     def __init__(self, c, tag, L, NLD, W, seed):
         import torch
+        import lossless_speculative_decoding_vc_amd as vc
         import synthetic as S
         dev = "cuda"
         B, Hq, Hkv, D = c.B, c.Hq, c.Hkv, c.D
@@ -153,13 +158,13 @@ class Cohort:
         self.tail_v = _bf16_randn((B, Hkv, D, c.k), seed + 101, dev)
         self.dq = [_bf16_randn((B, Hq, D), seed + 110 + i, dev) for i in range(NLD)]
         self.dout = torch.empty((B, Hq, D), dtype=torch.bfloat16, device=dev)
-        self.dlogits = torch.empty((B, c.V), dtype=torch.float32, device=dev)
+        self.lws_d = vc.lm_head_argmax_workspace(B, c.V, dev)      # LM-head tile maxima, drafting role
         # verify role
         self.vq = [_bf16_randn((B, c.M, Hq, D), seed + 150 + i, dev) for i in range(NLD)]
         self.bk = [_bf16_randn((B, Hkv, c.M, D), seed + 180 + i, dev) for i in range(NLD)]
         self.bv = [_bf16_randn((B, Hkv, D, c.M), seed + 210 + i, dev) for i in range(NLD)]
         self.vout = torch.empty((B, c.M, Hq, D), dtype=torch.bfloat16, device=dev)
-        self.vlogits = torch.empty((B * c.M, c.V), dtype=torch.float32, device=dev)
+        self.lws_v = vc.lm_head_argmax_workspace(B * c.M, c.V, dev)  # LM-head tile maxima, verifying role
         self.ctx_len = torch.full((B,), c.N, dtype=torch.int32, device=dev)
         # planted acceptance: drafts copy the full-cache prediction for n steps
         y, d, n = S.planted_accept(B, c.k, c.V, cfg_seed=seed, n_lo=24, n_hi=32)
@@ -167,9 +172,9 @@ class Cohort:
         self.planted_d = d
         yt = torch.from_numpy(y.astype(np.int64)).to(dev)
         dt_ = torch.from_numpy(d.astype(np.int64)).to(dev)
-        Wt = W.t()   # [V][Dm] view: row t is the LM-head column of token t
-        self.hv = Wt[yt.reshape(-1)].contiguous()                 # [B*M][Dm]
-        self.hd = [Wt[dt_[:, i]].contiguous() for i in range(c.k)]  # per step [B][Dm]
+        # W is vocab-major [V][Dm]: hidden row = W[t] makes t the row's argmax (largest norm-squared)
+        self.hv = W[yt.reshape(-1)].contiguous().view(B, c.M, c.Dm)   # [B][M][Dm]
+        self.hd = [W[dt_[:, i]].contiguous() for i in range(c.k)]    # per step [B][Dm]
         self.drafts = torch.from_numpy(d).to(dev)                 # [B][k] int32 (previous round's)
         self.taillen = [torch.full((B,), i, dtype=torch.int32, device=dev) for i in range(c.k + 1)]
         self.dws = None
@@ -183,7 +188,7 @@ def run_stagger(args, t_start):
     L, NLD = args.layers, args.distinct_layers
     dev = "cuda"
     torch.manual_seed(0)
-    W = _bf16_randn((c.Dm, c.V), 3, dev, std=0.02)
+    W = _bf16_randn((c.V, c.Dm), 3, dev, std=0.02)   # LM head, vocab-major
     X = Cohort(c, "A", L, NLD, W, seed=4)
     Y = Cohort(c, "B", L, NLD, W, seed=40)
     for co in (X, Y):
@@ -232,8 +237,8 @@ def run_stagger(args, t_start):
             if ev is not None:
                 ev[1].record(dr_s)
                 timers["draft"].append((ev, l))
-        vc.lm_head(Yc.hd[i], W, Yc.dlogits, stream=dr_s)
-        vc.argmax(Yc.dlogits, out=Yc.drafts.view(-1)[i:], out_stride=c.k, stream=dr_s)
+        vc.lm_head_argmax(Yc.hd[i], W, out=Yc.drafts.view(-1)[i:], out_stride=c.k, workspace=Yc.lws_d,
+                          stream=dr_s)
 
     def run_round(Xc, Yc, mode, timers=None):
         """Cohort Xc verifies, Yc drafts.  Returns verified tokens."""
@@ -270,9 +275,8 @@ def run_stagger(args, t_start):
             for _ in range(nsteps_per_layer[l]):
                 enqueue_draft_step(Yc, step, timers)
                 step += 1
-        # verify logits, greedy acceptance, commit
-        vc.lm_head(Xc.hv, W, Xc.vlogits, stream=ver_s)
-        am, n_acc, toks, n_out = vc.accept(Xc.vlogits.view(c.B, c.M, c.V), Xc.drafts, stream=ver_s)
+        # verify LM head fused with the greedy argmax and the acceptance, then commit
+        am, n_acc, toks, n_out = vc.lm_head_accept(Xc.hv, W, Xc.drafts, workspace=Xc.lws_v, stream=ver_s)
         for l in range(L):
             j = l % NLD
             vc.commit_rows(Xc.bk[j], Xc.bv[j], n_out, Xc.K[j], Xc.Vt[j], Xc.len[l], degree=Xc.deg[j],
@@ -548,10 +552,12 @@ def cpu_baseline(verified_per_round, layers):
     for g in range(G):
         A.draft_attn_one(q[0, g], dk, dv, c.Lc, deg, bk, bv, c.k)
     t_dhead = (time.time() - t) / G
-    W = rng.standard_normal((c.Dm, c.V)).astype(np.float64) * 0.02
-    h = rng.standard_normal((4, c.Dm))
+    import synthetic as S
+    from oracle.accept import lm_head_logits
+    W = S.f32_to_bf16_bits(rng.standard_normal((c.V, c.Dm), dtype=np.float32) * np.float32(0.02))
+    h = S.f32_to_bf16_bits(rng.standard_normal((4, c.Dm), dtype=np.float32))
     t = time.time()
-    lg = h @ W
+    lg = lm_head_logits(h, W)
     t_lm_row = (time.time() - t) / 4
     t = time.time()
     accept(np.concatenate([lg] * 9)[:c.M], rng.integers(0, c.V, c.k))
