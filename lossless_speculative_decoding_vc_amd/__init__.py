@@ -149,6 +149,13 @@ def _ptr(t):
     return None if t is None else t.data_ptr()
 
 
+def _check_out(out, rows, stride):
+    """The kernels write out[r * stride] for r < rows: the tensor must reach that far."""
+    if rows > 0 and out.numel() < (rows - 1) * stride + 1:
+        raise ValueError(f"out holds {out.numel()} entries; {rows} rows at stride {stride} need "
+                         f"{(rows - 1) * stride + 1}")
+
+
 def _stream(stream):
     if stream is None:
         stream = torch.cuda.current_stream()
@@ -289,8 +296,13 @@ def accept(logits, draft, argmax=None, accept_len=None, out_tokens=None, n_out=N
     accept_len = torch.empty(B, dtype=torch.int32, device=dev) if accept_len is None else accept_len
     out_tokens = torch.empty((B, M), dtype=torch.int32, device=dev) if out_tokens is None else out_tokens
     n_out = torch.empty(B, dtype=torch.int32, device=dev) if n_out is None else n_out
-    for t, n in ((argmax, "argmax"), (accept_len, "accept_len"), (out_tokens, "out_tokens"), (n_out, "n_out")):
+    for t, n, numel in ((argmax, "argmax", B * M), (accept_len, "accept_len", B), (out_tokens, "out_tokens", B * M),
+                        (n_out, "n_out", B)):
         _dev(t, n, torch.int32)
+        if t.numel() < numel:
+            raise ValueError(f"{n} holds {t.numel()} entries, {numel} needed")
+    if draft.numel() < B * (M - 1):
+        raise ValueError(f"draft must be [B][M-1] = [{B}][{M - 1}]")
     a = AcceptArgs()
     a.B, a.M, a.V = B, M, V
     a.logit_dtype = _vc_dtype(logits)
@@ -308,6 +320,8 @@ def argmax(logits, out=None, out_stride=1, stream=None):
     R = logits.numel() // V
     if out is None:
         out = torch.empty(R * out_stride, dtype=torch.int32, device=logits.device)
+    _dev(out, "out", torch.int32)
+    _check_out(out, R, out_stride)
     _check(lib().vc_argmax(R, V, _vc_dtype(logits), _ptr(logits), _ptr(out), out_stride, _stream(stream)))
     return out
 
@@ -345,6 +359,7 @@ def lm_head_argmax(h, w, out=None, out_stride=1, workspace=None, stream=None):
     if out is None:
         out = torch.empty(R * out_stride, dtype=torch.int32, device=h.device)
     _dev(out, "out", torch.int32)
+    _check_out(out, R, out_stride)
     if workspace is None:
         workspace = lm_head_argmax_workspace(R, V, h.device)
     _check(lib().vc_lm_head_argmax(R, Dm, V, _ptr(h), _ptr(w), _ptr(out), out_stride, _ptr(workspace),
@@ -370,8 +385,13 @@ def lm_head_accept(h, w, draft, argmax=None, accept_len=None, out_tokens=None, n
     accept_len = torch.empty(B, dtype=torch.int32, device=dev) if accept_len is None else accept_len
     out_tokens = torch.empty((B, M), dtype=torch.int32, device=dev) if out_tokens is None else out_tokens
     n_out = torch.empty(B, dtype=torch.int32, device=dev) if n_out is None else n_out
-    for t, n in ((argmax, "argmax"), (accept_len, "accept_len"), (out_tokens, "out_tokens"), (n_out, "n_out")):
+    for t, n, numel in ((argmax, "argmax", B * M), (accept_len, "accept_len", B), (out_tokens, "out_tokens", B * M),
+                        (n_out, "n_out", B)):
         _dev(t, n, torch.int32)
+        if t.numel() < numel:
+            raise ValueError(f"{n} holds {t.numel()} entries, {numel} needed")
+    if draft.numel() < B * (M - 1):
+        raise ValueError(f"draft must be [B][M-1] = [{B}][{M - 1}]")
     if workspace is None:
         workspace = lm_head_argmax_workspace(B * M, V, dev)
     _check(lib().vc_lm_head_accept(B, M, Dm, V, _ptr(h), _ptr(w), _ptr(draft), _ptr(argmax), _ptr(accept_len),

@@ -139,6 +139,10 @@ def test_errors_and_empty():
     w = torch.zeros((100, 64), dtype=torch.bfloat16, device="cuda")
     with pytest.raises(vc.VcError):   # workspace too small
         vc.lm_head_argmax(h, w, workspace=torch.empty(16, dtype=torch.uint8, device="cuda"))
+    with pytest.raises(ValueError):   # strided output too short for 4 rows at stride 8
+        vc.lm_head_argmax(h, w, out=torch.empty(20, dtype=torch.int32, device="cuda"), out_stride=8)
+    with pytest.raises(ValueError):   # drafts of the wrong length
+        vc.lm_head_accept(h.view(2, 2, 64), w, torch.zeros((2, 0), dtype=torch.int32, device="cuda"))
     out = vc.lm_head_argmax(h[:0], w)
     assert out.numel() == 0
     # all-zero logits: every entry ties, the lowest index wins
