@@ -38,6 +38,9 @@ CPU oracle timed on a bounded sample of the same workload.
   draft1m_int4   the 1M-token configuration's int4 drafter
   quant128k_int4 building that int4 cache from bf16 K/V (vc_quantize_int4 over
                  batch 32 x 8 KV heads x 131072 tokens)
+  draft128k_int4p, draft1m_int4p, quant128k_int4p
+                 the same int4 legs in the packed layout (VC_KV_INT4_PACKED: one
+                 interleaved 5120-byte block per 32 tokens)
   csm128k        one Chunked Soft Matching round (vc_csm_round, r = 1, chunks of
                  64) over the cohort's 131072-token caches (16 x 8 KV heads)
   lmhead_verify  the verifying cohort's LM head fused with argmax + acceptance
@@ -65,7 +68,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=1)
     ap.add_argument("--workload", default="stagger128k",
                     choices=["stagger128k", "verify32k", "verify128k", "verify1m", "draft128k", "draft128k_int4",
-                             "draft1m_int4", "quant128k_int4", "csm128k", "lmhead_verify", "lmhead_draft",
+                             "draft1m_int4", "draft128k_int4p", "draft1m_int4p", "quant128k_int4", "quant128k_int4p", "csm128k", "lmhead_verify", "lmhead_draft",
                              "copy1g"])
     ap.add_argument("--layers", type=int, default=64)
     ap.add_argument("--distinct-layers", type=int, default=16,
@@ -95,10 +98,13 @@ KERNEL_OF = {
     "draft128k": "vc_draft_attn: draft_bf16_dense + combine_splits",
     "draft128k_int4": "vc_draft_attn: draft_int4 + combine_splits",
     "draft1m_int4": "vc_draft_attn: draft_int4 + combine_splits",
+    "draft128k_int4p": "vc_draft_attn (packed int4 blocks): draft_int4 + combine_splits",
+    "draft1m_int4p": "vc_draft_attn (packed int4 blocks): draft_int4 + combine_splits",
     "verify1m": "vc_verify_attn: verify_pp + combine_splits",
     "verify32k": "vc_verify_attn: verify_pp + combine_splits",
     "verify128k": "vc_verify_attn: verify_pp + combine_splits",
     "quant128k_int4": "vc_quantize_int4: quantize_int4",
+    "quant128k_int4p": "vc_quantize_int4_packed: quantize_int4",
     "csm128k": "vc_csm_round: csm_round_kernel",
     "lmhead_verify": "vc_lm_head_accept: lm_argmax + argmax_partials + accept_rows",
     "lmhead_draft": "vc_lm_head_argmax: lm_argmax + argmax_partials",
@@ -454,6 +460,18 @@ def kernel_alone(args):
             n_keep.append(vc.csm_round(K, Vb, cap, 4, 1024, 64, 1.0, ok, ov, od))
         flops = 0.0
         nbytes = B * Hkv * cap * D * 2 * 2 + B * Hkv * (cap // 2 + 514) * (D * 2 * 2 + 4)
+    elif args.workload == "quant128k_int4p":
+        # the same int4 cache built in the packed layout (one 5120-byte block per 32 tokens)
+        B, Hkv, D, cap = 32, 8, 128, 131072
+        K = _bf16_randn((B, Hkv, cap, D), 11, dev)
+        Vt = _bf16_randn((B, Hkv, D, cap), 12, dev)
+        zero = torch.zeros((B, Hkv), dtype=torch.int32, device=dev)
+        blk = torch.empty((B, Hkv, cap // 32, vc.INT4_PACKED_BLOCK), dtype=torch.uint8, device=dev)
+
+        def call(i):
+            vc.quantize_int4_packed(K, Vt, zero, cap // 32, zero, blk)
+        flops = 0.0
+        nbytes = B * Hkv * cap * D * 2 * 2 + B * Hkv * cap * 160
     elif args.workload == "quant128k_int4":
         # the int4 cache of the 128K draft leg built from bf16 K/V: 32 requests x 8 KV heads x 131072 tokens
         B, Hkv, D, cap = 32, 8, 128, 131072
@@ -471,8 +489,9 @@ def kernel_alone(args):
             vc.quantize_int4(K, Vt, zero, cap // 32, zero, **qd)
         flops = 0.0
         nbytes = B * Hkv * cap * D * 2 * 2 + B * Hkv * cap * 160
-    elif args.workload in ("draft128k_int4", "draft1m_int4"):
-        if args.workload == "draft128k_int4":   # batch 32, int4 K/V over all 131072 tokens (4 of 16 bits = 25%)
+    elif args.workload in ("draft128k_int4", "draft1m_int4", "draft128k_int4p", "draft1m_int4p"):
+        packed = args.workload.endswith("p")
+        if args.workload.startswith("draft128k"):   # batch 32, int4 K/V over all 131072 tokens (4 of 16 bits = 25%)
             B, Hq, Hkv, D, cap = 32, 32, 8, 128, 131072
         else:   # drafter of the 1M-token configuration: one request, int4 over 1048576 tokens
             B, Hq, Hkv, D, cap = 1, 32, 8, 128, 1048576
@@ -492,9 +511,22 @@ def kernel_alone(args):
         out = torch.empty((B, Hq, D), dtype=torch.bfloat16, device=dev)
         ws = torch.empty(1 << 26, dtype=torch.uint8, device=dev)
 
-        def call(i):
-            vc.draft_attn(q, kq, vq, ml, out=out, workspace=ws, fmt=vc.VC_KV_INT4, num_splits=args.splits,
-                          k_scale=ks, k_zero=kz, v_scale=vs, v_zero=vz)
+        if packed:   # the same codes and parameters, one interleaved 5120-byte block per 32 tokens
+            nb = cap // 32
+            blk = torch.empty((B, Hkv, nb, vc.INT4_PACKED_BLOCK), dtype=torch.uint8, device=dev)
+            blk[..., 0:2048] = kq.view(B, Hkv, nb, 2048)
+            blk[..., 2048:4096] = vq.view(B, Hkv, nb, 2048)
+            for j, t in enumerate((ks, kz, vs, vz)):
+                blk[..., 4096 + 256 * j:4352 + 256 * j] = t.contiguous().view(torch.uint8).view(B, Hkv, nb, 256)
+            del kq, vq, ks, kz, vs, vz
+
+            def call(i):
+                vc.draft_attn(q, blk, None, ml, out=out, workspace=ws, fmt=vc.VC_KV_INT4_PACKED,
+                              num_splits=args.splits)
+        else:
+            def call(i):
+                vc.draft_attn(q, kq, vq, ml, out=out, workspace=ws, fmt=vc.VC_KV_INT4, num_splits=args.splits,
+                              k_scale=ks, k_zero=kz, v_scale=vs, v_zero=vz)
         flops = 4.0 * D * Hq * B * cap
         nbytes = B * Hkv * cap * 160 + 2 * B * Hq * D * 2
     else:

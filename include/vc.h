@@ -42,7 +42,7 @@ extern "C" {
 
 typedef enum { VC_OK = 0, VC_EINVAL = 1, VC_ENOTSUP = 2, VC_EHIP = 3 } vc_status;
 typedef enum { VC_BF16 = 0, VC_FP32 = 1 } vc_dtype;
-typedef enum { VC_KV_DENSE = 0, VC_KV_INT4 = 1 } vc_kv_format;
+typedef enum { VC_KV_DENSE = 0, VC_KV_INT4 = 1, VC_KV_INT4_PACKED = 2 } vc_kv_format;
 
 /* ------------------------------------------------------------------------ */
 /* Draft decode attention ("Algoritmo Principale", step 1: drafting over the
@@ -84,6 +84,12 @@ typedef struct vc_draft_args {
      (j = 0..3): bytes c0|c2<<4, c4|c6<<4, c1|c3<<4, c5|c7<<4.               */
   const uint16_t *k_scale, *k_zero; /* INT4 only: fp16 [B][Hkv][cap/32][D]         */
   const uint16_t *v_scale, *v_zero; /* INT4 only: fp16 [B][Hkv][cap/32][D/32][32]  */
+  /* INT4_PACKED: the same codes and parameters with each 32-token block's six
+     pieces interleaved into one 5120-byte block, k = u8 [B][Hkv][cap/32][5120]:
+     bytes 0..2047 K codes (as INT4 k), 2048..4095 V codes (as INT4 v),
+     4096..4351 K scales, 4352..4607 K zeros, 4608..4863 V scales, 4864..5119
+     V zeros (each as the INT4 arrays' block); v and the four scale/zero
+     pointers must be NULL.  One block is then one contiguous read.          */
   const float   *degree;          /* optional [B][Hd][cap] merge degrees n_t >= 1  */
   int64_t degree_h_stride;        /* 0: one row per request shared by all KV heads;
                                      cap: one row per KV head                      */
@@ -240,6 +246,13 @@ vc_status vc_quantize_int4(int32_t B, int32_t Hkv, int32_t D, const void *src_k,
                            int64_t src_cap, const int32_t *src_start, int32_t n_groups, int64_t cap,
                            const int32_t *dst_start, void *k_codes, void *k_scale, void *k_zero, void *v_codes,
                            void *v_scale, void *v_zero, void *stream);
+
+/* The same quantization into the interleaved fmt = VC_KV_INT4_PACKED cache:
+ * packed u8 [B][Hkv][cap/32][5120] (block layout as in vc_draft_args).
+ * Arguments, decisions and errors as vc_quantize_int4.                      */
+vc_status vc_quantize_int4_packed(int32_t B, int32_t Hkv, int32_t D, const void *src_k, const void *src_v,
+                                  int64_t src_cap, const int32_t *src_start, int32_t n_groups, int64_t cap,
+                                  const int32_t *dst_start, void *packed, void *stream);
 
 /* ------------------------------------------------------------------------ */
 /* One clustering round of Chunked Soft Matching ("Riassunto Tecnico:

@@ -17,12 +17,13 @@ __all__ = [
     "VcError", "lib", "library_path", "draft_attn", "verify_attn", "accept",
     "draft_workspace_size", "verify_workspace_size", "declared_symbols",
     "argmax", "lm_head", "commit_rows", "quantize_int4", "csm_round", "Stagger",
-    "VC_BF16", "VC_FP32", "VC_KV_DENSE", "VC_KV_INT4",
+    "VC_BF16", "VC_FP32", "VC_KV_DENSE", "VC_KV_INT4", "VC_KV_INT4_PACKED",
 ]
 
 VC_OK, VC_EINVAL, VC_ENOTSUP, VC_EHIP = 0, 1, 2, 3
 VC_BF16, VC_FP32 = 0, 1
-VC_KV_DENSE, VC_KV_INT4 = 0, 1
+VC_KV_DENSE, VC_KV_INT4, VC_KV_INT4_PACKED = 0, 1, 2
+INT4_PACKED_BLOCK = 5120   # bytes per 32-token block of a packed int4 cache (head_dim 128)
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 library_path = os.path.join(_HERE, "libvc.so")
@@ -104,6 +105,8 @@ def lib():
         L.vc_commit_rows.restype = ctypes.c_int
         L.vc_quantize_int4.argtypes = [_i32, _i32, _i32, _p, _p, _i64, _p, _i32, _i64, _p, _p, _p, _p, _p, _p, _p, _p]
         L.vc_quantize_int4.restype = ctypes.c_int
+        L.vc_quantize_int4_packed.argtypes = [_i32, _i32, _i32, _p, _p, _i64, _p, _i32, _i64, _p, _p, _p]
+        L.vc_quantize_int4_packed.restype = ctypes.c_int
         L.vc_csm_round.argtypes = [_i32, _i32, _i32, _i32, _i32, _i32, _i32, ctypes.c_float, _p, _p, _p, _i64,
                                    _p, _p, _p, _i64, ctypes.POINTER(_i32), _p]
         L.vc_csm_round.restype = ctypes.c_int
@@ -222,6 +225,10 @@ def draft_attn(q, k, v, main_len, degree=None, tail_k=None, tail_v=None, tail_le
     B, Hq, D = q.shape
     Hkv = k.shape[1]
     cap = k.shape[2]
+    if fmt == VC_KV_INT4_PACKED:   # k is [B][Hkv][cap/32][5120] uint8
+        if k.dim() != 4 or k.shape[3] != INT4_PACKED_BLOCK:
+            raise ValueError("a packed int4 cache is [B][Hkv][cap/32][5120] uint8")
+        cap = k.shape[2] * 32
     if out is None:
         out = torch.empty_like(q)
     a = _draft_struct(q, k, v, main_len, degree, tail_k, tail_v, tail_len, out, out_lse,
@@ -444,6 +451,23 @@ def quantize_int4(src_k, src_v, src_start, n_groups, dst_start, k_codes, k_scale
     _check(lib().vc_quantize_int4(B, Hkv, D, _ptr(src_k), _ptr(src_v), src_cap, _ptr(src_start), int(n_groups), cap,
                                   _ptr(dst_start), _ptr(k_codes), _ptr(k_scale), _ptr(k_zero), _ptr(v_codes),
                                   _ptr(v_scale), _ptr(v_zero), _stream(stream)))
+
+
+def quantize_int4_packed(src_k, src_v, src_start, n_groups, dst_start, packed, stream=None):
+    """:func:`quantize_int4` into a packed int4 cache (``vc_quantize_int4_packed``):
+    ``packed [B][Hkv][cap/32][5120]`` uint8, one interleaved block per 32 tokens
+    (K codes, V codes, K scales, K zeros, V scales, V zeros)."""
+    _dev(src_k, "src_k", torch.bfloat16)
+    _dev(src_v, "src_v", torch.bfloat16)
+    _dev(src_start, "src_start", torch.int32)
+    _dev(dst_start, "dst_start", torch.int32)
+    _dev(packed, "packed", torch.uint8)
+    if packed.dim() != 4 or packed.shape[3] != INT4_PACKED_BLOCK:
+        raise ValueError("a packed int4 cache is [B][Hkv][cap/32][5120] uint8")
+    B, Hkv, src_cap, D = src_k.shape
+    cap = packed.shape[2] * 32
+    _check(lib().vc_quantize_int4_packed(B, Hkv, D, _ptr(src_k), _ptr(src_v), src_cap, _ptr(src_start),
+                                         int(n_groups), cap, _ptr(dst_start), _ptr(packed), _stream(stream)))
 
 
 def csm_round(in_k, in_v, n_in, n_sink, n_recent, chunk, r, out_k, out_v, out_deg, in_deg=None, stream=None):

@@ -47,10 +47,10 @@ vc_status check_draft_shape(const vc_draft_args *a) {
   vc_status st = check_heads(a->B, a->Hq, a->Hkv, a->D);
   if (st != VC_OK) return st;
   REQ(a->dtype == VC_BF16 || a->dtype == VC_FP32, "unknown dtype %d", a->dtype);
-  REQ(a->fmt == VC_KV_DENSE || a->fmt == VC_KV_INT4, "unknown kv format %d", a->fmt);
-  if (a->fmt == VC_KV_INT4 && a->dtype != VC_BF16)
-    return fail(VC_ENOTSUP, "int4 main segment is compiled for bf16 queries only");
-  if (a->fmt == VC_KV_INT4 && a->D != 128) return fail(VC_ENOTSUP, "int4 main segment is compiled for head_dim 128");
+  REQ(a->fmt == VC_KV_DENSE || a->fmt == VC_KV_INT4 || a->fmt == VC_KV_INT4_PACKED, "unknown kv format %d", a->fmt);
+  const bool i4 = a->fmt != VC_KV_DENSE;
+  if (i4 && a->dtype != VC_BF16) return fail(VC_ENOTSUP, "int4 main segment is compiled for bf16 queries only");
+  if (i4 && a->D != 128) return fail(VC_ENOTSUP, "int4 main segment is compiled for head_dim 128");
   REQ(a->cap >= 0 && a->cap % 64 == 0, "cap (%lld) must be a non-negative multiple of 64", (long long)a->cap);
   REQ(a->tcap >= 0, "tcap must be non-negative");
   return VC_OK;
@@ -60,7 +60,13 @@ vc_status check_draft(const vc_draft_args *a) {
   vc_status st = check_draft_shape(a);
   if (st != VC_OK || a->B == 0) return st;
   REQ(a->q && a->out && a->main_len, "q, out and main_len are required");
-  REQ(a->cap == 0 || (a->k && a->v), "k and v are required when cap > 0");
+  if (a->fmt == VC_KV_INT4_PACKED) {
+    REQ(a->cap == 0 || a->k, "k (the packed int4 blocks) is required when cap > 0");
+    REQ(!a->v && !a->k_scale && !a->k_zero && !a->v_scale && !a->v_zero,
+        "a packed int4 main segment lives in k alone: v and the scale/zero pointers must be NULL");
+  } else {
+    REQ(a->cap == 0 || (a->k && a->v), "k and v are required when cap > 0");
+  }
   REQ(aligned16(a->q) && aligned16(a->out) && aligned16(a->k) && aligned16(a->v),
       "q, k, v and out must be 16-byte aligned");
   if (a->fmt == VC_KV_INT4) {
@@ -272,7 +278,11 @@ vc_status vc_quantize_int4(int32_t B, int32_t Hkv, int32_t D, const void *src_k,
       "null pointer");
   REQ(aligned16(k_codes) && aligned16(v_codes) && aligned16(src_k) && aligned16(src_v),
       "source and int4 code buffers must be 16-byte aligned");
+  REQ(aligned16(k_scale) && aligned16(k_zero) && aligned16(v_scale) && aligned16(v_zero),
+      "int4 scale and zero buffers must be 16-byte aligned");
   vc::QuantParams p;
+  p.code_bs = 32 * D / 2;   // 2048 bytes of codes per 32-token block
+  p.par_bs = 2 * D;         // 256 bytes of binary16 per block
   p.BH = B * Hkv;
   p.src_cap = src_cap;
   p.cap = cap;
@@ -287,6 +297,35 @@ vc_status vc_quantize_int4(int32_t B, int32_t Hkv, int32_t D, const void *src_k,
   p.v_scale = static_cast<uint16_t *>(v_scale);
   p.v_zero = static_cast<uint16_t *>(v_zero);
   return hip_status(vc::launch_quantize_int4(p, n_groups, (hipStream_t)stream), "vc_quantize_int4 launch");
+}
+
+vc_status vc_quantize_int4_packed(int32_t B, int32_t Hkv, int32_t D, const void *src_k, const void *src_v,
+                                  int64_t src_cap, const int32_t *src_start, int32_t n_groups, int64_t cap,
+                                  const int32_t *dst_start, void *packed, void *stream) {
+  REQ(B >= 0 && Hkv >= 1 && n_groups >= 0 && src_cap >= 0 && cap >= 0, "bad quantize shape");
+  if (D != 128) return fail(VC_ENOTSUP, "the int4 cache is compiled for head_dim 128 (got %d)", D);
+  REQ(cap % 32 == 0, "cap (%lld) must be a multiple of 32", (long long)cap);
+  REQ(n_groups <= 65535, "at most 65535 groups per call (got %d)", n_groups);
+  if (B == 0 || n_groups == 0) return VC_OK;
+  REQ(src_k && src_v && src_start && dst_start && packed, "null pointer");
+  REQ(aligned16(packed) && aligned16(src_k) && aligned16(src_v), "source and packed buffers must be 16-byte aligned");
+  uint8_t *blk = static_cast<uint8_t *>(packed);
+  vc::QuantParams p;
+  p.BH = B * Hkv;
+  p.src_cap = src_cap;
+  p.cap = cap;
+  p.src_k = static_cast<const uint16_t *>(src_k);
+  p.src_v = static_cast<const uint16_t *>(src_v);
+  p.src_start = src_start;
+  p.dst_start = dst_start;
+  p.k_codes = blk + vc::kPackedKCodes;
+  p.v_codes = blk + vc::kPackedVCodes;
+  p.k_scale = reinterpret_cast<uint16_t *>(blk + vc::kPackedKScale);
+  p.k_zero = reinterpret_cast<uint16_t *>(blk + vc::kPackedKZero);
+  p.v_scale = reinterpret_cast<uint16_t *>(blk + vc::kPackedVScale);
+  p.v_zero = reinterpret_cast<uint16_t *>(blk + vc::kPackedVZero);
+  p.code_bs = p.par_bs = vc::kPackedBlock;
+  return hip_status(vc::launch_quantize_int4(p, n_groups, (hipStream_t)stream), "vc_quantize_int4_packed launch");
 }
 
 vc_status vc_csm_round(int32_t B, int32_t Hkv, int32_t D, int32_t n_in, int32_t n_sink, int32_t n_recent,

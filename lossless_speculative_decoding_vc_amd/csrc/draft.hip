@@ -51,7 +51,7 @@ struct DraftParams {
   uint16_t *out;
   float *out_lse;
   float *part_o, *part_lse;
-  // int4 main segment
+  // int4 main segment (packed: kq is the array of 5120-byte blocks)
   const uint8_t *kq, *vq;                    // codes
   const uint16_t *ks, *kz, *vs, *vz;         // binary16 scales / zeros
 };
@@ -350,7 +350,7 @@ VC_DEVICE void dma16(const void *gptr, uint32_t lds_addr) {
   __asm__ volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gptr), "s"(lds_addr) : "memory", "m0");
 }
 
-template <int D, bool DEG>
+template <int D, bool DEG, bool PACKED>
 __global__ __launch_bounds__(kDraftWaves * 64, 2) void draft_int4(DraftParams p) {
   constexpr int KS = D / 32, DT = D / 16, NG = D / 32;
   static_assert(D == 128, "int4 draft is compiled for head_dim 128");
@@ -426,6 +426,8 @@ __global__ __launch_bounds__(kDraftWaves * 64, 2) void draft_int4(DraftParams p)
   const uint16_t *kzb = p.kz + (size_t)bh * (p.cap / 32) * D;
   const uint16_t *vsb = p.vs + (size_t)bh * NG * p.cap;
   const uint16_t *vzb = p.vz + (size_t)bh * NG * p.cap;
+  // packed: one 5120-byte block per 32 tokens (p.kq is the block array)
+  const uint8_t *pkb = p.kq + (size_t)bh * (p.cap / kChunk) * kPackedBlock;
   const uint16_t *tkb = p.tail_k ? p.tail_k + (size_t)bh * p.tcap * D : nullptr;
   const uint16_t *tvb = p.tail_v ? p.tail_v + (size_t)bh * D * p.tcap : nullptr;
   const float *db = p.degree ? p.degree + b * p.deg_b_stride + kvh * p.deg_h_stride : nullptr;
@@ -474,20 +476,34 @@ __global__ __launch_bounds__(kDraftWaves * 64, 2) void draft_int4(DraftParams p)
     const int c = first + kDraftWaves * k;
     const int base = c * kChunk;
     const uint32_t st = ring_addr + (uint32_t)((k % kI4Stages) * kI4Stage);
+    if constexpr (PACKED) {
+      // the block's K codes, V codes and its four 256-byte parameter pieces
+      // are one contiguous 5120-byte run
+      const uint8_t *blk = pkb + (size_t)c * kPackedBlock;
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int t = 16 * h + (lane >> 2);
-      dma16(kqb + (size_t)(base + t) * (D / 2) + 16 * ((lane & 3) ^ ((t >> 3) & 3)), st + 1024 * h);
+      for (int h = 0; h < 2; ++h) {
+        const int t = 16 * h + (lane >> 2);
+        dma16(blk + t * (D / 2) + 16 * ((lane & 3) ^ ((t >> 3) & 3)), st + 1024 * h);
+      }
+#pragma unroll
+      for (int h = 0; h < 2; ++h) dma16(blk + kPackedVCodes + 1024 * h + 16 * lane, st + 2048 + 1024 * h);
+      dma16(blk + kPackedKScale + 16 * lane, st + 4096);
+    } else {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int t = 16 * h + (lane >> 2);
+        dma16(kqb + (size_t)(base + t) * (D / 2) + 16 * ((lane & 3) ^ ((t >> 3) & 3)), st + 1024 * h);
+      }
+#pragma unroll
+      for (int h = 0; h < 2; ++h) dma16(vqb + (size_t)base * (D / 2) + 1024 * h + 16 * lane, st + 2048 + 1024 * h);
+      const uint16_t *src;
+      const int q = lane & 15;
+      if (lane < 16) src = ksb + (size_t)(base / 32) * D + 8 * q;
+      else if (lane < 32) src = kzb + (size_t)(base / 32) * D + 8 * q;
+      else if (lane < 48) src = vsb + (size_t)base * NG + 8 * q;
+      else src = vzb + (size_t)base * NG + 8 * q;
+      dma16(src, st + 4096);
     }
-#pragma unroll
-    for (int h = 0; h < 2; ++h) dma16(vqb + (size_t)base * (D / 2) + 1024 * h + 16 * lane, st + 2048 + 1024 * h);
-    const uint16_t *src;
-    const int q = lane & 15;
-    if (lane < 16) src = ksb + (size_t)(base / 32) * D + 8 * q;
-    else if (lane < 32) src = kzb + (size_t)(base / 32) * D + 8 * q;
-    else if (lane < 48) src = vsb + (size_t)base * NG + 8 * q;
-    else src = vzb + (size_t)base * NG + 8 * q;
-    dma16(src, st + 4096);
     if (DEG) {
       if (lane < 8) dma16(db + base + 4 * lane, st + 5120);
     }
@@ -722,13 +738,20 @@ hipError_t launch_draft(const vc_draft_args &a, const SplitPlan &pl, hipStream_t
   const size_t rows = (size_t)a.B * a.Hq;
   p.part_o = (float *)a.workspace;
   p.part_lse = p.part_o ? p.part_o + (size_t)pl.splits * rows * a.D : nullptr;
-  p.kq = (const uint8_t *)a.k; p.vq = (const uint8_t *)a.v;
+  p.kq = (const uint8_t *)a.k; p.vq = (const uint8_t *)a.v;   // packed: k holds the blocks
   p.ks = a.k_scale; p.kz = a.k_zero; p.vs = a.v_scale; p.vz = a.v_zero;
+  const bool pk = a.fmt == VC_KV_INT4_PACKED;
   dim3 grid(pl.splits, a.B * a.Hkv);
-  if (a.fmt == VC_KV_INT4 && a.degree) draft_int4<128, true><<<grid, kDraftWaves * 64, 0, s>>>(p);
-  else if (a.fmt == VC_KV_INT4) draft_int4<128, false><<<grid, kDraftWaves * 64, 0, s>>>(p);
-  else if (a.D == 128) draft_bf16_dense<128><<<grid, kDraftWaves * 64, 0, s>>>(p);
-  else draft_bf16_dense<64><<<grid, kDraftWaves * 64, 0, s>>>(p);
+  if (a.fmt != VC_KV_DENSE) {
+    if (pk && a.degree) draft_int4<128, true, true><<<grid, kDraftWaves * 64, 0, s>>>(p);
+    else if (pk) draft_int4<128, false, true><<<grid, kDraftWaves * 64, 0, s>>>(p);
+    else if (a.degree) draft_int4<128, true, false><<<grid, kDraftWaves * 64, 0, s>>>(p);
+    else draft_int4<128, false, false><<<grid, kDraftWaves * 64, 0, s>>>(p);
+  } else if (a.D == 128) {
+    draft_bf16_dense<128><<<grid, kDraftWaves * 64, 0, s>>>(p);
+  } else {
+    draft_bf16_dense<64><<<grid, kDraftWaves * 64, 0, s>>>(p);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || pl.splits == 1) return e;
   return launch_combine(p.part_o, p.part_lse, pl.splits, (int)rows, a.D, a.dtype, a.out, a.out_lse, s);

@@ -33,7 +33,13 @@ hipError_t launch_commit(int B, int Hkv, int D, int M, int elem_bytes, int64_t c
 hipError_t launch_draft(const vc_draft_args &a, const SplitPlan &p, hipStream_t s);
 hipError_t launch_verify(const vc_verify_args &a, const SplitPlan &p, hipStream_t s);
 
-// Int4 group quantization (see quant.hip): BH = B * Hkv slices.
+// The interleaved int4 block (fmt = VC_KV_INT4_PACKED, head_dim 128): byte
+// offsets of a 32-token block's six pieces and the block size.
+constexpr int kPackedKCodes = 0, kPackedVCodes = 2048, kPackedKScale = 4096, kPackedKZero = 4352,
+              kPackedVScale = 4608, kPackedVZero = 4864, kPackedBlock = 5120;
+
+// Int4 group quantization (see quant.hip): BH = B * Hkv slices.  Block j of
+// slice bh of a piece starts at base + (bh * cap/32 + j) * stride bytes.
 struct QuantParams {
   int BH;
   int64_t src_cap, cap;
@@ -41,6 +47,7 @@ struct QuantParams {
   const int32_t *src_start, *dst_start;
   uint8_t *k_codes, *v_codes;
   uint16_t *k_scale, *k_zero, *v_scale, *v_zero;
+  int code_bs, par_bs;   // bytes per block: codes, scales/zeros
 };
 hipError_t launch_quantize_int4(const QuantParams &p, int n_groups, hipStream_t s);
 

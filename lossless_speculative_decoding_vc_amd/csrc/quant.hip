@@ -1,5 +1,6 @@
 // Int4 group quantization of bf16 K/V rows into the compressed-cache format
-// vc_draft_attn reads with fmt = VC_KV_INT4.
+// vc_draft_attn reads with fmt = VC_KV_INT4 (six arrays) or VC_KV_INT4_PACKED
+// (one interleaved 5120-byte block per 32 tokens).
 //
 // "Riepilogo Tecnico: VeriCache", "Supporto Architetturale": the drafter's
 // compressed cache may come from a quantizer, behind the same interface as
@@ -95,6 +96,7 @@ __global__ __launch_bounds__(256) void quantize_int4(QuantParams p) {
   if (s0 < 0 || d0 < 0 || (d0 % kGroup) != 0 || s0 + span > p.src_cap || d0 + span > p.cap) return;
   const int64_t st = (int64_t)s0 + (int64_t)grp * kGroup, dt = (int64_t)d0 + (int64_t)grp * kGroup;
   const int64_t blk = dt / kGroup;
+  const size_t gblk = (size_t)bh * (p.cap / kGroup) + blk;   // block index over all slices
 
   // The K tile is 8 KB contiguous and read in 16-byte pieces; the V tile is
   // 128 channel runs of 64 B, read in 16-byte pieces when the first token and
@@ -132,9 +134,9 @@ __global__ __launch_bounds__(256) void quantize_int4(QuantParams p) {
     const float s = f16_to_f32(s16), z = f16_to_f32(z16), rs = __builtin_amdgcn_rcpf(s);
 #pragma unroll
     for (int t = 0; t < kGroup; ++t) kcode[t][d] = (uint8_t)code_of(x[t], z, s, rs);
-    const size_t o = ((size_t)bh * (p.cap / kGroup) + blk) * D + d;
-    p.k_scale[o] = s16;
-    p.k_zero[o] = z16;
+    const size_t o = gblk * p.par_bs + 2 * d;   // bytes
+    *reinterpret_cast<uint16_t *>(reinterpret_cast<uint8_t *>(p.k_scale) + o) = s16;
+    *reinterpret_cast<uint16_t *>(reinterpret_cast<uint8_t *>(p.k_zero) + o) = z16;
   } else {
     // V token t, channel group g
     const int t = (tid - D) % kGroup, g = (tid - D) / kGroup;
@@ -150,14 +152,14 @@ __global__ __launch_bounds__(256) void quantize_int4(QuantParams p) {
     const float s = f16_to_f32(s16), z = f16_to_f32(z16), rs = __builtin_amdgcn_rcpf(s);
 #pragma unroll
     for (int j = 0; j < kGroup; ++j) vcode[kGroup * g + j][t] = (uint8_t)code_of(x[j], z, s, rs);
-    const size_t o = (((size_t)bh * (p.cap / kGroup) + blk) * NG + g) * kGroup + t;
-    p.v_scale[o] = s16;
-    p.v_zero[o] = z16;
+    const size_t o = gblk * p.par_bs + 2 * (g * kGroup + t);   // bytes
+    *reinterpret_cast<uint16_t *>(reinterpret_cast<uint8_t *>(p.v_scale) + o) = s16;
+    *reinterpret_cast<uint16_t *>(reinterpret_cast<uint8_t *>(p.v_zero) + o) = z16;
   }
   __syncthreads();
   // K codes: token row t of the group, D/8 words; V codes: channel d's 32 tokens, 4 words
-  uint32_t *kq = reinterpret_cast<uint32_t *>(p.k_codes + ((size_t)bh * p.cap + dt) * (D / 2));
-  uint32_t *vq = reinterpret_cast<uint32_t *>(p.v_codes + (((size_t)bh * (p.cap / kGroup) + blk) * D) * (kGroup / 2));
+  uint32_t *kq = reinterpret_cast<uint32_t *>(p.k_codes + gblk * p.code_bs);
+  uint32_t *vq = reinterpret_cast<uint32_t *>(p.v_codes + gblk * p.code_bs);
   for (int w = tid; w < kGroup * D / 8; w += 256) {
     const int t = w / (D / 8), c = w % (D / 8);
     kq[w] = pack8(&kcode[t][8 * c]);

@@ -15,7 +15,7 @@ import numpy as np
 __all__ = [
     "rng", "f32_to_bf16_bits", "normal_bf16", "normal_f32", "tiny_weights",
     "tiny_prompt", "kept_random", "degrees", "int4_grid", "pack_codes",
-    "planted_accept", "planted_logits", "csm_planted", "lm_planted", "TINY_WEIGHT_ORDER", "TID", "torch_normal",
+    "planted_accept", "planted_logits", "csm_planted", "lm_planted", "pack_int4_blocks", "TINY_WEIGHT_ORDER", "TID", "torch_normal",
     "torch_randint",
 ]
 
@@ -121,6 +121,20 @@ def pack_codes(codes):
         w |= c[..., 2 * j] << np.uint32(4 * j)
         w |= c[..., 2 * j + 1] << np.uint32(16 + 4 * j)
     return np.ascontiguousarray(w.astype("<u4")).view(np.uint8).reshape(c.shape[:-2] + (n // 2,))
+
+
+def pack_int4_blocks(k_codes, v_codes, k_scale, k_zero, v_scale, v_zero):
+    """The six int4 arrays of :func:`int4_grid` (library layouts) interleaved
+    per 32-token block: uint8 ``[B][Hkv][cap/32][5120]`` holding K codes
+    (2048 B), V codes (2048 B), K scales, K zeros, V scales, V zeros (256 B
+    each, little-endian binary16).  Storage layout only."""
+    k_codes, v_codes = np.asarray(k_codes), np.asarray(v_codes)
+    B, Hkv, cap = k_codes.shape[:3]
+    nb = cap // 32
+    parts = [k_codes.reshape(B, Hkv, nb, 2048), v_codes.reshape(B, Hkv, nb, 2048)]
+    for a in (k_scale, k_zero, v_scale, v_zero):
+        parts.append(np.ascontiguousarray(np.asarray(a).astype("<u2")).view(np.uint8).reshape(B, Hkv, nb, 256))
+    return np.ascontiguousarray(np.concatenate(parts, axis=-1))
 
 
 def int4_grid(B, Hkv, cap, D, cfg_seed, smin=0.3, smax=0.5):

@@ -82,6 +82,14 @@ def test_validation_rejects_before_launch(L):
     acc.B, acc.M, acc.V = 1, 0, 10
     assert L.vc_accept(ctypes.byref(acc), None) == vcb.VC_EINVAL
     assert L.vc_status_string(2) == b"VC_ENOTSUP"
+    # packed int4: bf16 queries and head_dim 128 only; the cache lives in k alone
+    assert L.vc_draft_attn(ctypes.byref(_draft(fmt=2, dtype=1)), None) == vcb.VC_ENOTSUP
+    assert L.vc_draft_attn(ctypes.byref(_draft(fmt=2, D=64)), None) == vcb.VC_ENOTSUP
+    assert L.vc_draft_attn(ctypes.byref(_draft(fmt=3)), None) == vcb.VC_EINVAL
+    fake = 1 << 20
+    a = _draft(fmt=2, q=fake, out=fake, main_len=fake, k=fake, v=fake)
+    assert L.vc_draft_attn(ctypes.byref(a), None) == vcb.VC_EINVAL
+    assert b"NULL" in L.vc_last_error()
 
 
 def test_workspace_plan_is_host_only(L):

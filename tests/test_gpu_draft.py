@@ -102,7 +102,7 @@ def test_fp32_no_tail_no_degree():
 # ---------------------------------------------------------------------------
 # int4 main segment (the quantizing drafter): the oracle reconstructs
 # x = c * s + z in fp64 and runs dense attention over the reconstruction.
-def _int4_check(B, Hq, Hkv, cap, main_len, tcap, tail_len, deg_mode, seed, splits=0, qstd=1.0):
+def _int4_check(B, Hq, Hkv, cap, main_len, tcap, tail_len, deg_mode, seed, splits=0, qstd=1.0, packed=False):
     import torch
     import lossless_speculative_decoding_vc_amd as vc
     from oracle import quant as Q
@@ -133,11 +133,15 @@ def _int4_check(B, Hq, Hkv, cap, main_len, tcap, tail_len, deg_mode, seed, split
     tl = None if tcap == 0 else np.asarray(tail_len, np.int32)
     lse = torch.empty((B, Hq), dtype=torch.float32, device="cuda")
     as_dev16 = lambda a: to_dev(np.ascontiguousarray(a).view(np.int16))
-    out = vc.draft_attn(to_dev_bf16(qbits), to_dev(g["k_codes"]), to_dev(g["v_codes"]), to_dev(ml),
-                        degree=None if deg is None else to_dev(deg), tail_k=tk_dev, tail_v=tv_dev,
-                        tail_len=None if tl is None else to_dev(tl), out_lse=lse, num_splits=splits,
-                        fmt=vc.VC_KV_INT4, k_scale=as_dev16(g["k_scale"]), k_zero=as_dev16(g["k_zero"]),
-                        v_scale=as_dev16(g["v_scale"]), v_zero=as_dev16(g["v_zero"]))
+    common = dict(degree=None if deg is None else to_dev(deg), tail_k=tk_dev, tail_v=tv_dev,
+                  tail_len=None if tl is None else to_dev(tl), out_lse=lse, num_splits=splits)
+    if packed:   # the same cache, one interleaved 5120-byte block per 32 tokens
+        blk = S.pack_int4_blocks(g["k_codes"], g["v_codes"], g["k_scale"], g["k_zero"], g["v_scale"], g["v_zero"])
+        out = vc.draft_attn(to_dev_bf16(qbits), to_dev(blk), None, to_dev(ml), fmt=vc.VC_KV_INT4_PACKED, **common)
+    else:
+        out = vc.draft_attn(to_dev_bf16(qbits), to_dev(g["k_codes"]), to_dev(g["v_codes"]), to_dev(ml),
+                            fmt=vc.VC_KV_INT4, k_scale=as_dev16(g["k_scale"]), k_zero=as_dev16(g["k_zero"]),
+                            v_scale=as_dev16(g["v_scale"]), v_zero=as_dev16(g["v_zero"]), **common)
     torch.cuda.synchronize()
     got = bf16_dev_to_f64(out)
     o_ref, lse_ref = A.draft_attn(bf16_to_f64(qbits), k_ref, v_ref, ml, deg, tk_ref, tv_ref, tl)
@@ -159,3 +163,13 @@ def test_int4_peaked_no_tail():
 
 def test_int4_tail_only():
     _int4_check(1, 4, 1, 256, [[0]], 20, [20], "shared", seed=33)
+
+
+@pytest.mark.parametrize("splits", [0, 3])
+def test_int4_packed_main_segment(splits):
+    # the packed layout: same codes and parameters, one contiguous block per 32 tokens
+    _int4_check(2, 8, 2, 1024, [[1024, 1000], [64, 333]], 12, [12, 3], "shared", seed=31, splits=splits,
+                packed=True)
+    got, ref = _int4_check(2, 16, 4, 512, [[512, 480, 96, 1], [200, 511, 32, 256]], 0, None, None, seed=32,
+                           packed=True)
+    assert rel_l2(got, ref) <= 2e-2

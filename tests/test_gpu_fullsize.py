@@ -151,7 +151,17 @@ def _int4_case(B, Hq, Hkv, cap, seed, samples, qstd):
     kq, vq, ks, kz, vs, vz = _int4_device(B, Hkv, cap, D, seed + 10)
     ml = torch.full((B, Hkv), cap, dtype=torch.int32, device="cuda")
     out = vc.draft_attn(q, kq, vq, ml, fmt=vc.VC_KV_INT4, k_scale=ks, k_zero=kz, v_scale=vs, v_zero=vz)
+    # the same cache in the packed layout (one 5120-byte block per 32 tokens) gives the same bits
+    nb = cap // 32
+    blk = torch.empty((B, Hkv, nb, vc.INT4_PACKED_BLOCK), dtype=torch.uint8, device="cuda")
+    blk[..., 0:2048] = kq.view(B, Hkv, nb, 2048)
+    blk[..., 2048:4096] = vq.view(B, Hkv, nb, 2048)
+    for j, t in enumerate((ks, kz, vs, vz)):
+        blk[..., 4096 + 256 * j:4352 + 256 * j] = t.contiguous().view(torch.uint8).view(B, Hkv, nb, 256)
+    out_p = vc.draft_attn(q, blk, None, ml, fmt=vc.VC_KV_INT4_PACKED)
     torch.cuda.synchronize()
+    assert torch.equal(out_p.view(torch.int16), out.view(torch.int16)), "packed and separate int4 layouts differ"
+    del blk, out_p
     got, ref = [], []
     for b, kvh, gs in samples:
         kc = unpack_int4(kq[b, kvh].cpu().numpy())                              # [cap][D]

@@ -141,3 +141,31 @@ def test_quantized_cache_feeds_draft_attention():
     torch.cuda.synchronize()
     o_ref, _ = A.draft_attn(bf16_to_f64(qbits), k_ref, v_ref, ml)
     assert_close(bf16_dev_to_f64(out), o_ref, TOL["bf16"], "draft over the device-quantized cache")
+
+
+def test_quantize_packed_matches_separate_arrays():
+    # vc_quantize_int4_packed writes exactly the six arrays' bytes, interleaved per block, and leaves
+    # blocks outside the call untouched
+    import torch
+    import lossless_speculative_decoding_vc_amd as vc
+    B, Hkv, src_cap, cap, n = 2, 3, 160, 256, 3
+    kbits = S.f32_to_bf16_bits(S.normal_f32((B, Hkv, src_cap, D), 44, S.TID["k"], std=1.5))
+    vbits = S.f32_to_bf16_bits(S.normal_f32((B, Hkv, src_cap, D), 44, S.TID["v"], std=0.7))
+    src = [[0, 7, 64], [31, 0, 64]]
+    dst = [[0, 96, 160], [64, 160, 32]]
+    sep, _ = _run(kbits, vbits, src, dst, n, cap)
+    packed = torch.full((B, Hkv, cap // 32, 5120), SENT8, dtype=torch.uint8, device="cuda")
+    vc.quantize_int4_packed(to_dev_bf16(kbits), to_dev_bf16(np.ascontiguousarray(np.swapaxes(vbits, -1, -2))),
+                            to_dev(np.asarray(src, np.int32)), n, to_dev(np.asarray(dst, np.int32)), packed)
+    torch.cuda.synchronize()
+    got = packed.cpu().numpy()
+    ref = S.pack_int4_blocks(sep["k_codes"], sep["v_codes"], sep["k_scale"].view(np.uint16),
+                             sep["k_zero"].view(np.uint16), sep["v_scale"].view(np.uint16),
+                             sep["v_zero"].view(np.uint16))
+    for b in range(B):
+        for h in range(Hkv):
+            blk = slice(dst[b][h] // 32, dst[b][h] // 32 + n)
+            np.testing.assert_array_equal(got[b, h, blk], ref[b, h, blk])
+            untouched = np.ones(cap // 32, bool)
+            untouched[blk] = False
+            assert np.all(got[b, h, untouched] == SENT8)

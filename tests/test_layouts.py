@@ -40,3 +40,23 @@ def test_int4_blocked_layouts():
         assert g["k_scale"].shape == (B, Hkv, cap // 32, D)
     assert g["v_codes"].shape == (B, Hkv, cap // 32, D, 16)
     assert g["v_scale"].shape == (B, Hkv, cap // 32, D // 32, 32)
+
+
+def test_int4_packed_block_layout():
+    # one 5120-byte block per 32 tokens: K codes, V codes, K scales, K zeros, V scales, V zeros
+    B, Hkv, cap, D = 2, 1, 96, 128
+    g = S.int4_grid(B, Hkv, cap, D, cfg_seed=6)
+    blk = S.pack_int4_blocks(g["k_codes"], g["v_codes"], g["k_scale"], g["k_zero"], g["v_scale"], g["v_zero"])
+    assert blk.shape == (B, Hkv, cap // 32, 5120) and blk.dtype == np.uint8
+    u16 = lambda row, off: int(row[off]) | (int(row[off + 1]) << 8)
+    rng = np.random.default_rng(1)
+    for _ in range(400):
+        b, t, d = int(rng.integers(B)), int(rng.integers(cap)), int(rng.integers(D))
+        row = blk[b, 0, t // 32]
+        j, g32 = t % 32, d // 32
+        assert code_at(row[64 * j:64 * j + 64], d) == g["k_c"][b, 0, t, d]
+        assert code_at(row[2048 + 16 * d:2048 + 16 * d + 16], j) == g["v_c"][b, 0, t, d]
+        assert u16(row, 4096 + 2 * d) == g["k_scale"][b, 0, t // 32, d]
+        assert u16(row, 4352 + 2 * d) == g["k_zero"][b, 0, t // 32, d]
+        assert u16(row, 4608 + 2 * (32 * g32 + j)) == g["v_scale_td"][b, 0, t, g32]
+        assert u16(row, 4864 + 2 * (32 * g32 + j)) == g["v_zero_td"][b, 0, t, g32]
