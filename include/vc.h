@@ -219,6 +219,27 @@ vc_status vc_commit_rows(int32_t B, int32_t Hkv, int32_t D, int32_t M, int32_t d
                          int64_t degree_h_stride, void *stream);
 
 /* ------------------------------------------------------------------------ */
+/* Compressed-cache construction for a token-eviction compressor ("Riepilogo
+ * Tecnico: VeriCache", "Supporto Architetturale": eviction policies sit
+ * behind the same compression interface; the kept set is per token, shared
+ * by a request's KV heads).  For request b, KV head h and j < n_kept[b]:
+ *   dst_k[b][h][j] = src_k[b][h][idx[b][j]]
+ *   token j of dst_v[b][h] = token idx[b][j] of src_v[b][h]
+ *   src_k [B][Hkv][src_cap][D], src_v [B][Hkv][D][src_cap]   (a full cache,
+ *         as vc_verify_attn reads it)
+ *   dst_k [B][Hkv][cap][D], dst_v [B][Hkv][cap/32][D][32]    (the main segment
+ *         of vc_draft_attn)
+ *   idx int32 [B][idx_stride] (device; any order, ascending keeps positions in
+ *   order), n_kept int32 [B] (device, clamped to [0, min(cap, idx_stride)]),
+ *   dst_len int32 [B][Hkv] (device, optional) set to the clamped n_kept.
+ * dtype VC_BF16 or VC_FP32; D in {64, 128}; cap % 32 == 0; all K/V buffers
+ * 16-byte aligned.  An index outside [0, src_cap) writes a zero row; rows at
+ * or past n_kept are not written.  Source and destination must not overlap.*/
+vc_status vc_compact_kv(int32_t B, int32_t Hkv, int32_t D, int32_t dtype, const void *src_k, const void *src_v,
+                        int64_t src_cap, const int32_t *idx, int64_t idx_stride, const int32_t *n_kept,
+                        void *dst_k, void *dst_v, int64_t cap, int32_t *dst_len, void *stream);
+
+/* ------------------------------------------------------------------------ */
 /* Int4 group quantization into the compressed-cache format vc_draft_attn
  * reads with fmt = VC_KV_INT4 ("Riepilogo Tecnico: VeriCache", "Supporto
  * Architetturale": the drafter's cache may come from a quantizer behind the

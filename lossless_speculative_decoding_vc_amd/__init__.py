@@ -105,6 +105,8 @@ def lib():
         L.vc_commit_rows.restype = ctypes.c_int
         L.vc_quantize_int4.argtypes = [_i32, _i32, _i32, _p, _p, _i64, _p, _i32, _i64, _p, _p, _p, _p, _p, _p, _p, _p]
         L.vc_quantize_int4.restype = ctypes.c_int
+        L.vc_compact_kv.argtypes = [_i32, _i32, _i32, _i32, _p, _p, _i64, _p, _i64, _p, _p, _p, _i64, _p, _p]
+        L.vc_compact_kv.restype = ctypes.c_int
         L.vc_quantize_int4_packed.argtypes = [_i32, _i32, _i32, _p, _p, _i64, _p, _i32, _i64, _p, _p, _p]
         L.vc_quantize_int4_packed.restype = ctypes.c_int
         L.vc_csm_round.argtypes = [_i32, _i32, _i32, _i32, _i32, _i32, _i32, ctypes.c_float, _p, _p, _p, _i64,
@@ -451,6 +453,33 @@ def quantize_int4(src_k, src_v, src_start, n_groups, dst_start, k_codes, k_scale
     _check(lib().vc_quantize_int4(B, Hkv, D, _ptr(src_k), _ptr(src_v), src_cap, _ptr(src_start), int(n_groups), cap,
                                   _ptr(dst_start), _ptr(k_codes), _ptr(k_scale), _ptr(k_zero), _ptr(v_codes),
                                   _ptr(v_scale), _ptr(v_zero), _stream(stream)))
+
+
+def compact_kv(src_k, src_v, idx, n_kept, dst_k, dst_v, dst_len=None, stream=None):
+    """Eviction compaction (``vc_compact_kv``): row j < n_kept[b] of the
+    compacted cache is row ``idx[b][j]`` of the full cache, for every KV head.
+
+    ``src_k [B][Hkv][src_cap][D]``, ``src_v [B][Hkv][D][src_cap]`` (a full
+    cache); ``idx`` int32 ``[B][stride]``, ``n_kept`` int32 ``[B]``;
+    ``dst_k [B][Hkv][cap][D]``, ``dst_v [B][Hkv][cap/32][D][32]`` (the draft
+    main segment); ``dst_len`` int32 ``[B][Hkv]`` or None.
+    """
+    for t, n in ((src_k, "src_k"), (src_v, "src_v"), (dst_k, "dst_k"), (dst_v, "dst_v")):
+        _dev(t, n, src_k.dtype)
+    _dev(idx, "idx", torch.int32)
+    _dev(n_kept, "n_kept", torch.int32)
+    _dev(dst_len, "dst_len", torch.int32)
+    B, Hkv, src_cap, D = src_k.shape
+    cap = dst_k.shape[2]
+    if tuple(src_v.shape) != (B, Hkv, D, src_cap) or tuple(dst_v.shape) != (B, Hkv, cap // 32, D, 32):
+        raise ValueError("src_v must be [B][Hkv][D][src_cap] and dst_v [B][Hkv][cap/32][D][32]")
+    if idx.dim() != 2 or idx.shape[0] != B or n_kept.numel() < B:
+        raise ValueError("idx must be [B][stride] and n_kept [B]")
+    if dst_len is not None and dst_len.numel() < B * Hkv:
+        raise ValueError("dst_len must hold B * Hkv entries")
+    _check(lib().vc_compact_kv(B, Hkv, D, _vc_dtype(src_k), _ptr(src_k), _ptr(src_v), src_cap, _ptr(idx),
+                               idx.shape[1], _ptr(n_kept), _ptr(dst_k), _ptr(dst_v), cap, _ptr(dst_len),
+                               _stream(stream)))
 
 
 def quantize_int4_packed(src_k, src_v, src_start, n_groups, dst_start, packed, stream=None):

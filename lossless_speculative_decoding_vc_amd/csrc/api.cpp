@@ -265,6 +265,24 @@ vc_status vc_commit_rows(int32_t B, int32_t Hkv, int32_t D, int32_t M, int32_t d
                     "vc_commit_rows launch");
 }
 
+vc_status vc_compact_kv(int32_t B, int32_t Hkv, int32_t D, int32_t dtype, const void *src_k, const void *src_v,
+                        int64_t src_cap, const int32_t *idx, int64_t idx_stride, const int32_t *n_kept,
+                        void *dst_k, void *dst_v, int64_t cap, int32_t *dst_len, void *stream) {
+  REQ(B >= 0 && Hkv >= 1 && src_cap >= 0 && cap >= 0 && idx_stride >= 0, "bad compaction shape");
+  REQ(dtype == VC_BF16 || dtype == VC_FP32, "unknown dtype %d", dtype);
+  if (D != 64 && D != 128) return fail(VC_ENOTSUP, "head_dim %d not compiled (64 or 128)", D);
+  REQ(cap % 32 == 0, "cap (%lld) must be a multiple of 32", (long long)cap);
+  REQ(cap / 32 <= 0x7fffffff, "cap too large");
+  if (B == 0 || cap == 0) return VC_OK;
+  REQ(idx_stride >= 1, "idx_stride must be >= 1");
+  REQ(src_k && src_v && idx && n_kept && dst_k && dst_v, "null pointer");
+  REQ(aligned16(src_k) && aligned16(src_v) && aligned16(dst_k) && aligned16(dst_v),
+      "K/V buffers must be 16-byte aligned");
+  return hip_status(vc::launch_compact_kv(B, Hkv, D, dtype == VC_BF16 ? 2 : 4, src_k, src_v, src_cap, idx, idx_stride,
+                                          n_kept, dst_k, dst_v, cap, dst_len, (hipStream_t)stream),
+                    "vc_compact_kv launch");
+}
+
 vc_status vc_quantize_int4(int32_t B, int32_t Hkv, int32_t D, const void *src_k, const void *src_v,
                            int64_t src_cap, const int32_t *src_start, int32_t n_groups, int64_t cap,
                            const int32_t *dst_start, void *k_codes, void *k_scale, void *k_zero, void *v_codes,

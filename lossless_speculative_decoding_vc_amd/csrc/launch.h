@@ -30,6 +30,9 @@ hipError_t launch_lm_argmax(int R, int Dm, int V, const void *h, const void *w, 
 hipError_t launch_commit(int B, int Hkv, int D, int M, int elem_bytes, int64_t cap, int v_blocked, const void *blk_k,
                          const void *blk_v, const int32_t *n_out, void *dst_k, void *dst_v, int32_t *len,
                          float *degree, int64_t deg_b_stride, int64_t deg_h_stride, hipStream_t s);
+hipError_t launch_compact_kv(int B, int Hkv, int D, int elem_bytes, const void *src_k, const void *src_v,
+                             int64_t src_cap, const int32_t *idx, int64_t idx_stride, const int32_t *n_kept,
+                             void *dst_k, void *dst_v, int64_t cap, int32_t *dst_len, hipStream_t s);
 hipError_t launch_draft(const vc_draft_args &a, const SplitPlan &p, hipStream_t s);
 hipError_t launch_verify(const vc_verify_args &a, const SplitPlan &p, hipStream_t s);
 

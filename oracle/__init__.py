@@ -29,6 +29,7 @@ Modules:
   causal) attention, written as the softmax definition.
 * :mod:`oracle.accept`    -- greedy argmax and accept-until-first-mismatch.
 * :mod:`oracle.quant`     -- the int4 group quantizer of the compressed cache.
+* :mod:`oracle.compress`  -- eviction compaction (the kept rows of a cache).
 * :mod:`oracle.csm`       -- one Chunked Soft Matching clustering round
   (CentroidKV, "Componenti Chiave" items 1-4).
 * :mod:`oracle.tiny`      -- the tiny random-weight decoder, full-KV greedy

@@ -118,3 +118,17 @@ def test_lm_head_argmax_validation_is_host_only(L):
                                None) == vcb.VC_EINVAL   # M > 1 needs drafts
     assert L.vc_lm_head_accept(0, 3, 64, 100, None, None, None, None, None, None, None, None, 0,
                                None) == vcb.VC_OK
+
+
+def test_compact_kv_validation_is_host_only(L):
+    fake = ctypes.c_void_p(1 << 20)
+    args = lambda **kw: [kw.get(k, d) for k, d in (("B", 2), ("Hkv", 2), ("D", 128), ("dtype", 0), ("sk", fake),
+                                                    ("sv", fake), ("src_cap", 256), ("idx", fake), ("stride", 64),
+                                                    ("n", fake), ("dk", fake), ("dv", fake), ("cap", 64),
+                                                    ("dl", None), ("s", None))]
+    assert L.vc_compact_kv(*args(dtype=5)) == vcb.VC_EINVAL
+    assert L.vc_compact_kv(*args(D=96)) == vcb.VC_ENOTSUP
+    assert L.vc_compact_kv(*args(cap=40)) == vcb.VC_EINVAL
+    assert L.vc_compact_kv(*args(idx=None)) == vcb.VC_EINVAL
+    assert L.vc_compact_kv(*args(stride=0)) == vcb.VC_EINVAL
+    assert L.vc_compact_kv(*args(B=0, sk=None)) == vcb.VC_OK
