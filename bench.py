@@ -43,6 +43,8 @@ CPU oracle timed on a bounded sample of the same workload.
                  interleaved 5120-byte block per 32 tokens)
   csm128k        one Chunked Soft Matching round (vc_csm_round, r = 1, chunks of
                  64) over the cohort's 131072-token caches (16 x 8 KV heads)
+  draft_cohort   one layer-step of the staggered batch's drafting cohort (16 requests,
+                 40 q / 8 KV heads, 32768 tokens + degrees + 32 tail tokens), alone
   lmhead_verify  the verifying cohort's LM head fused with argmax + acceptance
                  (528 rows x 5120 x 32768), next to the library GEMM + argmax
   lmhead_draft   the drafting cohort's LM head fused with the argmax (16 rows)
@@ -68,7 +70,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=1)
     ap.add_argument("--workload", default="stagger128k",
                     choices=["stagger128k", "verify32k", "verify128k", "verify1m", "draft128k", "draft128k_int4",
-                             "draft1m_int4", "draft128k_int4p", "draft1m_int4p", "quant128k_int4", "quant128k_int4p", "csm128k", "lmhead_verify", "lmhead_draft",
+                             "draft1m_int4", "draft128k_int4p", "draft1m_int4p", "draft_cohort", "quant128k_int4", "quant128k_int4p", "csm128k", "lmhead_verify", "lmhead_draft",
                              "copy1g"])
     ap.add_argument("--layers", type=int, default=64)
     ap.add_argument("--distinct-layers", type=int, default=16,
@@ -77,6 +79,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--iters", type=int, default=50, help="kernel-alone iterations")
     ap.add_argument("--splits", type=int, default=0, help="kernel-alone split count (0 = library default)")
+    ap.add_argument("--sets", type=int, default=4, help="draft_cohort: rotating compressed caches")
     return ap.parse_args()
 
 
@@ -98,6 +101,7 @@ KERNEL_OF = {
     "draft128k": "vc_draft_attn: draft_bf16_dense + combine_splits",
     "draft128k_int4": "vc_draft_attn: draft_int4 + combine_splits",
     "draft1m_int4": "vc_draft_attn: draft_int4 + combine_splits",
+    "draft_cohort": "vc_draft_attn: draft_bf16_dense + combine_splits",
     "draft128k_int4p": "vc_draft_attn (packed int4 blocks): draft_int4 + combine_splits",
     "draft1m_int4p": "vc_draft_attn (packed int4 blocks): draft_int4 + combine_splits",
     "verify1m": "vc_verify_attn: verify_pp + combine_splits",
@@ -529,6 +533,30 @@ def kernel_alone(args):
                               k_scale=ks, k_zero=kz, v_scale=vs, v_zero=vz)
         flops = 4.0 * D * Hq * B * cap
         nbytes = B * Hkv * cap * 160 + 2 * B * Hq * D * 2
+    elif args.workload == "draft_cohort":
+        # one layer-step of the staggered batch's drafting cohort: 16 requests, 40 q / 8 KV heads, 32768
+        # compressed tokens with degrees (capacity 34816) and a 32-token draft tail; --sets rotating layers
+        c = Cfg
+        B, Hq, Hkv, D = c.B, c.Hq, c.Hkv, c.D
+        import synthetic as S
+        sets = [dict(K=_bf16_randn((B, Hkv, c.cap, D), 80 + i, dev),
+                     V=_bf16_randn((B, Hkv, c.cap // 32, D, 32), 90 + i, dev),
+                     deg=S.torch_randint((B, 1, c.cap), 1, 5, 100 + i, dev, torch.int32).float())
+                for i in range(args.sets)]
+        q = _bf16_randn((B, Hq, D), 3, dev)
+        tk = _bf16_randn((B, Hkv, c.k, D), 4, dev)
+        tv = _bf16_randn((B, Hkv, D, c.k), 5, dev)
+        tl = torch.full((B,), c.k, dtype=torch.int32, device=dev)
+        ml = torch.full((B, Hkv), c.Lc, dtype=torch.int32, device=dev)
+        out = torch.empty((B, Hq, D), dtype=torch.bfloat16, device=dev)
+        ws = torch.empty(1 << 26, dtype=torch.uint8, device=dev)
+
+        def call(i):
+            st = sets[i % len(sets)]
+            vc.draft_attn(q, st["K"], st["V"], ml, degree=st["deg"], tail_k=tk, tail_v=tv, tail_len=tl, out=out,
+                          workspace=ws, num_splits=args.splits)
+        flops = 4.0 * D * Hq * B * (c.Lc + c.k)
+        nbytes = B * Hkv * (c.Lc + c.k) * D * 4 + B * c.Lc * 4 + 2 * B * Hq * D * 2
     else:
         B, Hq, Hkv, D, cap = 32, 32, 8, 128, 32768
         nset = 1   # 4.3 GB per set >> MALL
