@@ -122,3 +122,53 @@ def test_stagger_streams_layers_and_matches_direct_verify():
         torch.cuda.synchronize()
         assert torch.equal(outs[l], direct), l
     stg.close()
+
+
+@pytest.mark.parametrize("delayed", [(0, 2), (1, 3, 4), (0, 1, 2, 3, 4)])
+def test_stagger_slot_reuse_under_forced_delays(delayed):
+    """The two-slot ring under forced reorderings: the verify stream stalls
+    (a bounded spin kernel) before the chosen layers, so the copy engine is
+    ready to run ahead.  A copy into a slot must still wait for the release of
+    the layer that last read it: every layer's output stays bit-identical to
+    verify over a resident copy of that layer."""
+    import torch
+    import lossless_speculative_decoding_vc_amd as vc
+    B, M, Hq, Hkv, D, N, L = 1, 9, 8, 2, 128, 4096, 5
+    half = B * Hkv * N * D * 2
+    host = [torch.empty(2 * half, dtype=torch.uint8, pin_memory=True) for _ in range(L)]
+    res = []
+    for l in range(L):
+        k = S.normal_bf16((B, Hkv, N, D), 200 + l, 2)
+        v = S.normal_bf16((B, Hkv, D, N), 200 + l, 3)
+        host[l][:half].copy_(torch.from_numpy(k.view(np.uint8).reshape(-1)))
+        host[l][half:].copy_(torch.from_numpy(v.view(np.uint8).reshape(-1)))
+        res.append((to_dev_bf16(k), to_dev_bf16(v)))
+    q = to_dev_bf16(S.normal_bf16((B, M, Hq, D), 8, 1, std=3.0, slice_dims=1))
+    bk = to_dev_bf16(S.normal_bf16((B, Hkv, M, D), 8, 6))
+    bv = to_dev_bf16(S.normal_bf16((B, Hkv, D, M), 8, 7))
+    cl = to_dev(np.array([N], np.int32))
+    slots = [torch.empty(2 * half, dtype=torch.uint8, device="cuda") for _ in range(2)]
+    stg = vc.Stagger(slots, 2 * half, L)
+    vs = torch.cuda.Stream()
+    outs = [torch.empty((B, M, Hq, D), dtype=torch.bfloat16, device="cuda") for _ in range(L)]
+    stg.stream_layer(0, host[0], 2 * half)
+    stg.stream_layer(1, host[1], 2 * half)
+    for l in range(L):
+        ptr = stg.acquire(l, vs)
+        if l in delayed:
+            with torch.cuda.stream(vs):
+                torch.cuda._sleep(20_000_000)   # a few milliseconds of spinning, then it exits
+        base = slots[0] if ptr == slots[0].data_ptr() else slots[1]
+        kk = base[:half].view(torch.bfloat16).view(B, Hkv, N, D)
+        vv = base[half:].view(torch.bfloat16).view(B, Hkv, D, N)
+        vc.verify_attn(q, kk, vv, cl, bk, bv, out=outs[l], stream=vs)
+        stg.release(l, vs)
+        if l + 2 < L:
+            stg.stream_layer(l + 2, host[l + 2], 2 * half)
+    torch.cuda.synchronize()
+    stg.sync()
+    for l in range(L):
+        direct = vc.verify_attn(q, res[l][0], res[l][1], cl, bk, bv)
+        torch.cuda.synchronize()
+        assert torch.equal(outs[l], direct), l
+    stg.close()
