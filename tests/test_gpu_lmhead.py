@@ -42,7 +42,8 @@ def _inputs(R, Dm, V, seed):
 
 
 @pytest.mark.parametrize("R,Dm,V", [(1, 256, 512), (5, 96, 513), (16, 256, 1000), (33, 128, 4096),
-                                    (64, 64, 700), (65, 256, 2000), (300, 96, 1500), (528, 256, 1031)])
+                                    (64, 64, 700), (65, 256, 2000), (300, 96, 1500), (528, 256, 1031),
+                                    (1, 32, 1), (600, 64, 3000), (528, 128, 151936)])
 def test_argmax_random(R, Dm, V):
     import torch
     import lossless_speculative_decoding_vc_amd as vc
