@@ -587,6 +587,39 @@ def kernel_alone(args):
 
 
 # ---------------------------------------------------------------------------
+def measured_peaks():
+    """What this machine reaches on plain reference operations (context for the roofline fractions, which use the
+    published peaks): a 1 GiB device copy (HBM read + write), a 1 GiB pinned host-to-device copy (PCIe) and an
+    8192^3 bf16 library GEMM (MFMA)."""
+    import torch
+    dev = "cuda"
+    s = torch.cuda.current_stream()
+
+    def t_us(fn, n):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(s)
+        for _ in range(n):
+            fn()
+        e1.record(s)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / n
+    src = torch.empty(GiB, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    hbm = 2 * GiB / t_us(lambda: dst.copy_(src), 10) / 1e3
+    host = torch.empty(GiB, dtype=torch.uint8, pin_memory=True)
+    h2d = GiB / t_us(lambda: dst.copy_(host, non_blocking=True), 5) / 1e3
+    del src, dst, host
+    n = 8192
+    a = torch.randn((n, n), device=dev, dtype=torch.bfloat16)
+    b = torch.randn((n, n), device=dev, dtype=torch.bfloat16)
+    gemm = 2.0 * n ** 3 / t_us(lambda: torch.matmul(a, b), 20) / 1e6
+    return {"hbm_device_copy_gbs": hbm, "pcie_h2d_pinned_gbs": h2d, "bf16_gemm_tflops": gemm,
+            "what": "1 GiB device copy, 1 GiB pinned host-to-device copy, 8192^3 bf16 torch.matmul"}
+
+
+# ---------------------------------------------------------------------------
 def cpu_baseline(verified_per_round, layers):
     """The oracle (fp64 numpy) on a bounded sample of the round, extrapolated."""
     from threadpoolctl import threadpool_info
@@ -670,6 +703,7 @@ def main():
         return
 
     r = run_stagger(args, t_start)
+    peaks = measured_peaks()
     cpu = None
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample")
@@ -694,6 +728,9 @@ def main():
                    "mfma_frac": r["verify_tflops"] / MFMA_BF16_PEAK_TFLOPS, "hbm_gbs": r["verify_gbs"],
                    "hbm_frac": r["verify_gbs"] / HBM_PEAK_GBS, "flops_per_launch": r["v_flops"]},
         "pcie_h2d_gbs": r["pcie_h2d_gbs"],
+        "measured_peaks": dict(peaks, draft_frac_of_copy=r["draft_gbs"] / peaks["hbm_device_copy_gbs"],
+                               verify_frac_of_gemm=r["verify_tflops"] / peaks["bf16_gemm_tflops"],
+                               pcie_frac_of_pinned_copy=r["pcie_h2d_gbs"] / peaks["pcie_h2d_pinned_gbs"]),
         "bulk_sync_round_ms": None if r["bulk_sync_s"] is None else r["bulk_sync_s"] * 1e3,
         "verified_tokens_per_round": r["verified_per_round"],
         "parity_planted_accept": r["parity_ok"],
