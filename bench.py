@@ -49,6 +49,10 @@ CPU oracle timed on a bounded sample of the same workload.
                  (528 rows x 5120 x 32768), next to the library GEMM + argmax
   lmhead_draft   the drafting cohort's LM head fused with the argmax (16 rows)
   copy1g         a 1 GiB device copy (reference for the HBM byte counters)
+
+``--workload long1m`` runs rounds of the 1M-token configuration instead (one
+request, k = 40, int4 drafting resident in HBM, the full cache streamed per
+layer; ``--layers`` defaults to 40).
 """
 import argparse
 import json
@@ -70,9 +74,10 @@ def parse():
     ap.add_argument("--warmup", type=int, default=1)
     ap.add_argument("--workload", default="stagger128k",
                     choices=["stagger128k", "verify32k", "verify128k", "verify1m", "draft128k", "draft128k_int4",
-                             "draft1m_int4", "draft128k_int4p", "draft1m_int4p", "draft_cohort", "quant128k_int4", "quant128k_int4p", "csm128k", "lmhead_verify", "lmhead_draft",
+                             "draft1m_int4", "draft128k_int4p", "draft1m_int4p", "draft_cohort", "long1m", "quant128k_int4", "quant128k_int4p", "csm128k", "lmhead_verify", "lmhead_draft",
                              "copy1g"])
-    ap.add_argument("--layers", type=int, default=64)
+    ap.add_argument("--layers", type=int, default=None,
+                    help="model layers per round (default 64 for stagger128k, 40 for long1m)")
     ap.add_argument("--distinct-layers", type=int, default=16,
                     help="distinct compressed-cache buffers per cohort (layers rotate over them)")
     ap.add_argument("--no-bulk", action="store_true", help="skip the bulk-synchronous comparison round")
@@ -80,7 +85,10 @@ def parse():
     ap.add_argument("--iters", type=int, default=50, help="kernel-alone iterations")
     ap.add_argument("--splits", type=int, default=0, help="kernel-alone split count (0 = library default)")
     ap.add_argument("--sets", type=int, default=4, help="draft_cohort: rotating compressed caches")
-    return ap.parse_args()
+    args = ap.parse_args()
+    if args.layers is None:
+        args.layers = 40 if args.workload == "long1m" else 64
+    return args
 
 
 # ---------------------------------------------------------------------------
@@ -359,6 +367,144 @@ def run_stagger(args, t_start):
     }
     stg.close()
     return res
+
+
+# ---------------------------------------------------------------------------
+# One request at 1M tokens (Mistral-24B layer shape), k = 40
+def run_long1m(args, t_start):
+    """Rounds of the 1M-token configuration: one request drafts k = 40 tokens over its int4 compressed cache
+    (packed blocks, resident in HBM) through every layer, then verifies the 41-row block layer by layer against
+    the full 1048576-token cache, each layer's 4 GiB streamed from pinned host memory through a two-slot ring
+    (the first two layers' copies overlap the drafting), then takes the LM head fused with the argmax and the
+    acceptance.  Acceptance is planted per round: full acceptance with the bonus, a first-position mismatch,
+    then n ~ U{24..40}."""
+    import torch
+    import lossless_speculative_decoding_vc_amd as vc
+    import synthetic as S
+    dev = "cuda"
+    B, Hq, Hkv, D, N, k = 1, 32, 8, 128, 1048576, 40
+    M, V, Dm = k + 1, 131072, 5120
+    L, NLD = args.layers, min(args.distinct_layers, 4)
+    nb = N // 32
+    # int4 compressed caches (packed), NLD distinct layers
+    blks = []
+    for i in range(NLD):
+        blk = torch.empty((B, Hkv, nb, vc.INT4_PACKED_BLOCK), dtype=torch.uint8, device=dev)
+        blk[..., :4096] = S.torch_randint((B, Hkv, nb, 4096), 0, 256, 300 + i, dev, torch.int32).to(torch.uint8)
+        g = torch.Generator(device=dev)
+        g.manual_seed(310 + i)
+        for j in range(2):   # K and V scale/zero pairs
+            sc = (torch.rand((B, Hkv, nb, 128), generator=g, device=dev) * 0.2 + 0.3).half()
+            blk[..., 4096 + 512 * j:4352 + 512 * j] = sc.view(torch.uint8)
+            blk[..., 4352 + 512 * j:4608 + 512 * j] = (sc.float() * -7.5).half().view(torch.uint8)
+        blks.append(blk)
+    dq = [_bf16_randn((B, Hq, D), 320 + i, dev) for i in range(NLD)]
+    tail_k = _bf16_randn((B, Hkv, k, D), 330, dev)
+    tail_v = _bf16_randn((B, Hkv, D, k), 331, dev)
+    taillen = [torch.full((B,), i, dtype=torch.int32, device=dev) for i in range(k + 1)]
+    ml = torch.full((B, Hkv), N, dtype=torch.int32, device=dev)
+    dout = torch.empty((B, Hq, D), dtype=torch.bfloat16, device=dev)
+    dws = torch.empty(1 << 26, dtype=torch.uint8, device=dev)
+    vq = [_bf16_randn((B, M, Hq, D), 340 + i, dev) for i in range(NLD)]
+    bk = _bf16_randn((B, Hkv, M, D), 350, dev)
+    bv = _bf16_randn((B, Hkv, D, M), 351, dev)
+    vout = torch.empty((B, M, Hq, D), dtype=torch.bfloat16, device=dev)
+    vws = torch.empty(1 << 26, dtype=torch.uint8, device=dev)
+    ctx_len = torch.full((B,), N, dtype=torch.int32, device=dev)
+    W = _bf16_randn((V, Dm), 352, dev, std=0.02)   # LM head, vocab-major
+    lws_d = vc.lm_head_argmax_workspace(B, V, dev)
+    lws_v = vc.lm_head_argmax_workspace(B * M, V, dev)
+    drafts = torch.zeros((B, k), dtype=torch.int32, device=dev)
+    half = B * Hkv * N * D * 2
+    slot_bytes = 2 * half   # 4 GiB: K then channel-major V
+    slots = [torch.empty(slot_bytes, dtype=torch.uint8, device=dev) for _ in range(2)]
+    g = torch.Generator(device=dev)
+    g.manual_seed(353)
+    slots[0].view(torch.bfloat16).normal_(0.0, 1.0, generator=g)
+    pool = [torch.empty(slot_bytes, dtype=torch.uint8, pin_memory=True) for _ in range(2)]
+    for pbuf in pool:
+        pbuf.copy_(slots[0])
+    stg = vc.Stagger(slots, slot_bytes, L)
+    ds, vs = torch.cuda.Stream(), torch.cuda.Stream()
+    torch.cuda.synchronize()
+    log(f"long1m setup done in {time.time() - t_start:.1f} s ({L} layers)")
+
+    def views(ptr):
+        base = slots[0] if ptr == slots[0].data_ptr() else slots[1]
+        return (base[:half].view(torch.bfloat16).view(B, Hkv, N, D),
+                base[half:].view(torch.bfloat16).view(B, Hkv, D, N))
+
+    timers = {"draft": [], "verify": []}
+
+    def run_round(r, timed):
+        force = {0: k} if r % 3 == 0 else ({0: 0} if r % 3 == 1 else {})
+        y, d, n = S.planted_accept(B, k, V, cfg_seed=400 + r, n_lo=24, n_hi=k, force=force)
+        yt = torch.from_numpy(y.astype(np.int64)).to(dev)
+        dt_ = torch.from_numpy(d.astype(np.int64)).to(dev)
+        hv = W[yt.reshape(-1)].contiguous().view(B, M, Dm)
+        hd = [W[dt_[:, i]].contiguous() for i in range(k)]
+        torch.cuda.synchronize()
+        t0 = time.time()
+        stg.stream_layer(0, pool[0], slot_bytes)
+        if L > 1:
+            stg.stream_layer(1, pool[1], slot_bytes)
+        for i in range(k):
+            for l in range(L):
+                ev = None
+                if timed and l == 0:
+                    ev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                    ev[0].record(ds)
+                vc.draft_attn(dq[l % NLD], blks[l % NLD], None, ml, tail_k=tail_k, tail_v=tail_v,
+                              tail_len=taillen[i + 1], out=dout, workspace=dws, fmt=vc.VC_KV_INT4_PACKED, stream=ds)
+                if ev is not None:
+                    ev[1].record(ds)
+                    timers["draft"].append(ev)
+            vc.lm_head_argmax(hd[i], W, out=drafts.view(-1)[i:], out_stride=k, workspace=lws_d, stream=ds)
+        vs.wait_stream(ds)   # the block holds the drafted tokens
+        for l in range(L):
+            ptr = stg.acquire(l, vs)
+            kk, vv = views(ptr)
+            ev = None
+            if timed:
+                ev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                ev[0].record(vs)
+            vc.verify_attn(vq[l % NLD], kk, vv, ctx_len, bk, bv, out=vout, workspace=vws, stream=vs)
+            if ev is not None:
+                ev[1].record(vs)
+                timers["verify"].append(ev)
+            stg.release(l, vs)
+            if l + 2 < L:
+                stg.stream_layer(l + 2, pool[l % 2], slot_bytes)
+        am, n_acc, toks, n_out = vc.lm_head_accept(hv, W, drafts, workspace=lws_v, stream=vs)
+        torch.cuda.synchronize()
+        stg.sync()
+        dt = time.time() - t0
+        ok = bool(np.array_equal(n_acc.cpu().numpy(), n)) and bool(np.array_equal(drafts.cpu().numpy(), d))
+        return int(n_out.sum().item()), dt, ok, int(n[0])
+
+    for w in range(args.warmup):
+        run_round(w, False)
+    verified, total_s, parity_ok, pattern = 0, 0.0, True, []
+    for s_ in range(args.steps):
+        v, dt, ok, n0 = run_round(args.warmup + s_, True)
+        verified += v
+        total_s += dt
+        parity_ok &= ok
+        pattern.append(n0)
+        log(f"long1m round {s_}: {dt:.2f} s, accepted {n0}, emitted {v}, parity {ok}")
+    copy_ms = [stg.copy_ms(l) for l in range(L)]
+    stg.close()
+    d_us = float(np.mean([e[0].elapsed_time(e[1]) for e in timers["draft"]])) * 1e3
+    v_us = float(np.mean([e[0].elapsed_time(e[1]) for e in timers["verify"]])) * 1e3
+    d_bytes = B * Hkv * N * 160 + B * Hkv * k / 2 * D * 4 + 2 * B * Hq * D * 2
+    v_bytes = B * Hkv * (N + M) * D * 4 + 2 * B * M * Hq * D * 2
+    v_flops = 4.0 * D * Hq * B * sum(N + i + 1 for i in range(M))
+    return {"value": verified / total_s, "ms_per_step": total_s / args.steps * 1e3, "parity_ok": parity_ok,
+            "accepted_per_round": pattern, "layers": L,
+            "pcie_h2d_gbs": slot_bytes / (np.mean(copy_ms) * 1e-3) / 1e9,
+            "draft_avg_us": d_us, "draft_gbs": d_bytes / d_us / 1e3, "verify_avg_us": v_us,
+            "verify_tflops": v_flops / v_us / 1e6, "verify_gbs": v_bytes / v_us / 1e3,
+            "d_bytes": d_bytes, "v_flops": v_flops}
 
 
 # ---------------------------------------------------------------------------
@@ -680,6 +826,32 @@ def main():
     if not torch.cuda.is_available():
         print(json.dumps({"error": "no GPU visible"}))
         sys.exit(2)
+
+    if args.workload == "long1m":
+        r = run_long1m(args, t_start)
+        out = {
+            "metric": f"verified tokens/sec, 1M context, k=40 ({r['layers']} layers)", "value": r["value"],
+            "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+            "ms_per_step": r["ms_per_step"], "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+            "dtype": "bf16", "data": "synthetic",
+            "config": {"workload": "1M-token long context, Mistral-24B layer shape: one request, 32 q / 8 KV heads, "
+                                   "head_dim 128; drafts k=40 over int4 (packed) compressed KV of 1048576 tokens in "
+                                   "HBM, verifies the 41-row block against the full bf16 cache streamed per layer "
+                                   "(4 GiB) from pinned host memory; 5120x131072 LM head; planted acceptance",
+                       "layers": r["layers"], "context": 1048576, "k": 40,
+                       "step": "one round (k draft steps through every layer, then the verify pass)"},
+            "roofline": {"bound": "hbm", "achieved": r["draft_gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": r["draft_gbs"] / HBM_PEAK_GBS, "traffic": None,
+                         "kernel": "int4 draft attention (vc_draft_attn: draft_int4 packed + combine_splits)",
+                         "avg_us": r["draft_avg_us"], "bytes_per_launch": r["d_bytes"]},
+            "verify": {"avg_us": r["verify_avg_us"], "tflops": r["verify_tflops"],
+                       "mfma_frac": r["verify_tflops"] / MFMA_BF16_PEAK_TFLOPS, "hbm_gbs": r["verify_gbs"],
+                       "hbm_frac": r["verify_gbs"] / HBM_PEAK_GBS, "flops_per_launch": r["v_flops"]},
+            "pcie_h2d_gbs": r["pcie_h2d_gbs"], "accepted_per_round": r["accepted_per_round"],
+            "parity_planted_accept": r["parity_ok"],
+        }
+        print(json.dumps(out))
+        return
 
     if args.workload != "stagger128k":
         r = kernel_alone(args)
