@@ -50,6 +50,9 @@ CPU oracle timed on a bounded sample of the same workload.
   lmhead_draft   the drafting cohort's LM head fused with the argmax (16 rows)
   copy1g         a 1 GiB device copy (reference for the HBM byte counters)
 
+``--workload tiny`` runs the small decoder's end-to-end loop (tokens/s next to
+full-KV greedy decoding on the GPU and the oracle's loop on the host).
+
 ``--workload long1m`` runs rounds of the 1M-token configuration instead (one
 request, k = 40, int4 drafting resident in HBM, the full cache streamed per
 layer; ``--layers`` defaults to 40).
@@ -74,7 +77,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=1)
     ap.add_argument("--workload", default="stagger128k",
                     choices=["stagger128k", "verify32k", "verify128k", "verify1m", "draft128k", "draft128k_int4",
-                             "draft1m_int4", "draft128k_int4p", "draft1m_int4p", "draft_cohort", "long1m", "quant128k_int4", "quant128k_int4p", "csm128k", "lmhead_verify", "lmhead_draft",
+                             "draft1m_int4", "draft128k_int4p", "draft1m_int4p", "draft_cohort", "long1m", "tiny", "quant128k_int4", "quant128k_int4p", "csm128k", "lmhead_verify", "lmhead_draft",
                              "copy1g"])
     ap.add_argument("--layers", type=int, default=None,
                     help="model layers per round (default 64 for stagger128k, 40 for long1m)")
@@ -367,6 +370,59 @@ def run_stagger(args, t_start):
     }
     stg.close()
     return res
+
+
+# ---------------------------------------------------------------------------
+# The tiny end-to-end loop (2-layer random decoder, prompt 1024, 64 new tokens, k = 8)
+def run_tiny(args):
+    """The draft-then-verify loop of the small fp32 decoder on the GPU (eviction compressor: 4 sinks + the last
+    128 tokens + every 8th older one), next to full-KV greedy decoding on the GPU (the same loop with k = 0) and the
+    oracle's loop on the host cores.  Decode phase timed apart from the prefill."""
+    import torch
+    import synthetic as S
+    from lossless_speculative_decoding_vc_amd.tiny_loop import TinyDecoder, TinyVeriCache
+    from oracle import tiny
+    arrays = S.tiny_weights(seed=0)
+    prompt = S.tiny_prompt(seed=1)
+    n_new, k = 64, 8
+    model = TinyDecoder(arrays, max_pos=len(prompt) + n_new + k + 64)
+
+    def run(kk):
+        loop = TinyVeriCache(model, max_tokens=len(prompt) + n_new + kk, k=kk, compressor="evict")
+        torch.cuda.synchronize()
+        t0 = time.time()
+        out = [loop.prefill(prompt)]
+        torch.cuda.synchronize()
+        t1 = time.time()
+        rounds = []
+        while len(out) < n_new:
+            r = loop.round()
+            rounds.append(r)
+            out.extend(r[3])
+        torch.cuda.synchronize()
+        return out[:n_new], rounds, t1 - t0, time.time() - t1
+    run(k)   # warm-up (library load, first launches)
+    times, greedy_times = [], []
+    for _ in range(args.steps):
+        toks, rounds, _, t_dec = run(k)
+        times.append(t_dec)
+        gtoks, _, _, g_dec = run(0)
+        greedy_times.append(g_dec)
+    spec = tiny.TinySpec()
+    W = tiny.TinyWeights.from_arrays(spec, arrays)
+    t = time.time()
+    ref, ref_rounds = tiny.vericache_decode(W, prompt, n_new, k)
+    t_oracle = time.time() - t
+    from threadpoolctl import threadpool_info
+    threads = max([x.get("num_threads", 1) for x in threadpool_info()] or [1])
+    dec = float(np.median(times))
+    return {"value": (n_new - 1) / dec, "ms_per_step": dec * 1e3,
+            "greedy_tokens_per_s": (n_new - 1) / float(np.median(greedy_times)),
+            "accept_lengths": [int(r[2]) for r in rounds], "rounds": len(rounds),
+            "tokens_equal_oracle": toks == ref, "tokens_equal_gpu_greedy": toks == gtoks,
+            "accept_lengths_equal_oracle": [int(r[2]) for r in rounds] == [r.n for r in ref_rounds],
+            "cpu_baseline": {"value": n_new / t_oracle, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+                             "sample": "the whole loop (prefill of 1024 tokens and 64 new tokens), fp64 numpy"}}
 
 
 # ---------------------------------------------------------------------------
@@ -826,6 +882,21 @@ def main():
     if not torch.cuda.is_available():
         print(json.dumps({"error": "no GPU visible"}))
         sys.exit(2)
+
+    if args.workload == "tiny":
+        r = run_tiny(args)
+        out = {"metric": "tiny loop decode tokens/sec (k=8)", "value": r["value"], "unit": "tokens/s", "n_gpus": 1,
+               "steps": args.steps, "warmup": 1, "ms_per_step": r["ms_per_step"], "higher_is_better": True,
+               "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+               "config": {"workload": "tiny end-to-end loop: 2-layer random decoder (d_model 256, 4 q / 2 KV heads, "
+                                      "head_dim 64, vocab 512, fp32), prompt 1024, 64 new tokens, k=8, eviction "
+                                      "compressor (4 sinks + last 128 + every 8th older token)",
+                          "step": "the decode phase of one generation (prefill timed apart)"},
+               **{key: r[key] for key in ("greedy_tokens_per_s", "accept_lengths", "rounds", "tokens_equal_oracle",
+                                          "tokens_equal_gpu_greedy", "accept_lengths_equal_oracle",
+                                          "cpu_baseline")}}
+        print(json.dumps(out))
+        return
 
     if args.workload == "long1m":
         r = run_long1m(args, t_start)
