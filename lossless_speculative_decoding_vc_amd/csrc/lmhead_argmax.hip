@@ -15,9 +15,10 @@
 //  * a workgroup owns a tile of BV vocab entries x BR hidden rows and walks
 //    the whole Dm axis in 32-wide k-steps through a ring of S LDS stages
 //    filled by direct global->LDS loads (global_load_lds_dwordx4: no
-//    registers held for prefetch).  One wave-wide load moves 16 rows x 64 B
-//    into 1 KB of contiguous LDS; which 16-byte piece a lane fetches is
-//    XOR-swizzled by row so the operand reads are free of bank conflicts.
+//    registers held for prefetch).  One wave-wide load moves 1 KB (16 rows x
+//    64 B, or 4 rows x 256 B when a stage spans four k-steps) into contiguous
+//    LDS; which 16-byte piece a lane fetches is XOR-swizzled by row so the
+//    operand reads are free of bank conflicts.
 //    Each wave reads the next step's MFMA operands from LDS between the
 //    current step's MFMAs.
 //  * verify-sized row counts (R > 64) use 8 waves (two per SIMD, so one
