@@ -38,6 +38,7 @@ vc_status check_heads(int B, int Hq, int Hkv, int D) {
   REQ(B >= 0 && Hq > 0 && Hkv > 0, "B, Hq, Hkv must be positive (B may be 0)");
   REQ(Hq % Hkv == 0, "Hq (%d) must be a multiple of Hkv (%d)", Hq, Hkv);
   REQ(Hq / Hkv <= 16, "at most 16 query heads per KV head (got %d)", Hq / Hkv);
+  REQ((int64_t)B * Hkv <= 65535, "at most 65535 (request, KV head) slices per call (got %lld)", (long long)B * Hkv);
   if (D != 64 && D != 128) return fail(VC_ENOTSUP, "head_dim %d not compiled (64 or 128)", D);
   return VC_OK;
 }
@@ -273,6 +274,7 @@ vc_status vc_compact_kv(int32_t B, int32_t Hkv, int32_t D, int32_t dtype, const 
   if (D != 64 && D != 128) return fail(VC_ENOTSUP, "head_dim %d not compiled (64 or 128)", D);
   REQ(cap % 32 == 0, "cap (%lld) must be a multiple of 32", (long long)cap);
   REQ(cap / 32 <= 0x7fffffff, "cap too large");
+  REQ((int64_t)B * Hkv <= 65535, "at most 65535 (request, KV head) slices per call");
   if (B == 0 || cap == 0) return VC_OK;
   REQ(idx_stride >= 1, "idx_stride must be >= 1");
   REQ(src_k && src_v && idx && n_kept && dst_k && dst_v, "null pointer");
@@ -291,6 +293,7 @@ vc_status vc_quantize_int4(int32_t B, int32_t Hkv, int32_t D, const void *src_k,
   if (D != 128) return fail(VC_ENOTSUP, "the int4 cache is compiled for head_dim 128 (got %d)", D);
   REQ(cap % 32 == 0, "cap (%lld) must be a multiple of 32", (long long)cap);
   REQ(n_groups <= 65535, "at most 65535 groups per call (got %d)", n_groups);
+  REQ((int64_t)B * Hkv <= 65535, "at most 65535 (request, KV head) slices per call");
   if (B == 0 || n_groups == 0) return VC_OK;
   REQ(src_k && src_v && src_start && dst_start && k_codes && k_scale && k_zero && v_codes && v_scale && v_zero,
       "null pointer");
@@ -324,6 +327,7 @@ vc_status vc_quantize_int4_packed(int32_t B, int32_t Hkv, int32_t D, const void 
   if (D != 128) return fail(VC_ENOTSUP, "the int4 cache is compiled for head_dim 128 (got %d)", D);
   REQ(cap % 32 == 0, "cap (%lld) must be a multiple of 32", (long long)cap);
   REQ(n_groups <= 65535, "at most 65535 groups per call (got %d)", n_groups);
+  REQ((int64_t)B * Hkv <= 65535, "at most 65535 (request, KV head) slices per call");
   if (B == 0 || n_groups == 0) return VC_OK;
   REQ(src_k && src_v && src_start && dst_start && packed, "null pointer");
   REQ(aligned16(packed) && aligned16(src_k) && aligned16(src_v), "source and packed buffers must be 16-byte aligned");
@@ -352,6 +356,7 @@ vc_status vc_csm_round(int32_t B, int32_t Hkv, int32_t D, int32_t n_in, int32_t 
                        void *stream) {
   REQ(n_out, "null n_out");
   REQ(B >= 0 && Hkv >= 1 && n_in >= 0 && n_sink >= 0 && n_recent >= 0, "bad CSM shape");
+  REQ((int64_t)B * Hkv <= 65535, "at most 65535 (request, KV head) slices per call");
   if (D != 128) return fail(VC_ENOTSUP, "the CSM round is compiled for head_dim 128 (got %d)", D);
   REQ(chunk >= 2 && chunk <= 128, "chunk must lie in 2..128 (got %d)", chunk);
   REQ(r >= 0.f && r <= 1.f, "r must lie in [0, 1]");

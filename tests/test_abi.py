@@ -82,6 +82,9 @@ def test_validation_rejects_before_launch(L):
     acc.B, acc.M, acc.V = 1, 0, 10
     assert L.vc_accept(ctypes.byref(acc), None) == vcb.VC_EINVAL
     assert L.vc_status_string(2) == b"VC_ENOTSUP"
+    # (request, KV head) slices index a grid dimension capped at 65535
+    assert L.vc_draft_attn(ctypes.byref(_draft(B=40000, Hq=4, Hkv=2)), None) == vcb.VC_EINVAL
+    assert b"65535" in L.vc_last_error()
     # packed int4: bf16 queries and head_dim 128 only; the cache lives in k alone
     assert L.vc_draft_attn(ctypes.byref(_draft(fmt=2, dtype=1)), None) == vcb.VC_ENOTSUP
     assert L.vc_draft_attn(ctypes.byref(_draft(fmt=2, D=64)), None) == vcb.VC_ENOTSUP
