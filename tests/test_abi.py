@@ -135,3 +135,28 @@ def test_compact_kv_validation_is_host_only(L):
     assert L.vc_compact_kv(*args(idx=None)) == vcb.VC_EINVAL
     assert L.vc_compact_kv(*args(stride=0)) == vcb.VC_EINVAL
     assert L.vc_compact_kv(*args(B=0, sk=None)) == vcb.VC_OK
+
+
+def test_empty_batches_return_before_any_gpu_call(L):
+    # an empty batch (B = 0, R = 0 or no groups) is a valid call that enqueues
+    # nothing: NULL tensors are accepted and no HIP call is made, which is why
+    # these succeed on a machine without a GPU
+    d = _draft(B=0)
+    assert L.vc_draft_attn(ctypes.byref(d), None) == vcb.VC_OK
+    assert L.vc_draft_workspace_size(ctypes.byref(d)) == 0
+    v = vcb.VerifyArgs()
+    v.B, v.Hq, v.Hkv, v.D, v.M, v.scale, v.ccap = 0, 40, 8, 128, 33, 0.088, 131072
+    assert L.vc_verify_attn(ctypes.byref(v), None) == vcb.VC_OK
+    acc = vcb.AcceptArgs()
+    acc.B, acc.M, acc.V = 0, 33, 32768
+    assert L.vc_accept(ctypes.byref(acc), None) == vcb.VC_OK
+    assert L.vc_argmax(0, 32768, 1, None, None, 1, None) == vcb.VC_OK
+    assert L.vc_lm_head(0, 5120, 32768, None, None, None, None) == vcb.VC_OK
+    assert L.vc_commit_rows(0, 8, 128, 33, 0, 1024, 0, None, None, None, None, None, None, None, 0,
+                            None) == vcb.VC_OK
+    assert L.vc_quantize_int4(0, 8, 128, None, None, 64, None, 1, 64, None, None, None, None, None, None, None,
+                              None) == vcb.VC_OK
+    assert L.vc_quantize_int4_packed(2, 8, 128, None, None, 64, None, 0, 64, None, None, None) == vcb.VC_OK
+    # a non-empty call with the same NULL tensors is rejected
+    assert L.vc_argmax(4, 32768, 1, None, None, 1, None) == vcb.VC_EINVAL
+    assert L.vc_quantize_int4_packed(2, 8, 128, None, None, 64, None, 1, 64, None, None, None) == vcb.VC_EINVAL
