@@ -46,6 +46,37 @@ vc_status hipfail(hipError_t e, const char *what) {
     if (e_ != hipSuccess) return hipfail(e_, #x); \
   } while (0)
 
+// Streams and events of a new object; on failure the caller destroys the
+// partly built object (handles not yet created are null).
+vc_status stagger_init(vc_stagger *s, void *const *slots, int32_t nslots, size_t slot_bytes, int32_t max_layers) {
+  s->slots.assign(slots, slots + nslots);
+  s->slot_bytes = slot_bytes;
+  s->slot_free.assign(nslots, nullptr);
+  s->copy_start.assign(max_layers, nullptr);
+  s->copied.assign(max_layers, nullptr);
+  s->copy_recorded.assign(max_layers, 0);
+  HIPCHK(hipStreamCreateWithFlags(&s->h2d, hipStreamNonBlocking));
+  HIPCHK(hipStreamCreateWithFlags(&s->d2h, hipStreamNonBlocking));
+  for (auto &e : s->slot_free) HIPCHK(hipEventCreateWithFlags(&e, hipEventDisableTiming));
+  for (int l = 0; l < max_layers; ++l) {
+    HIPCHK(hipEventCreate(&s->copy_start[l]));
+    HIPCHK(hipEventCreate(&s->copied[l]));
+  }
+  return VC_OK;
+}
+
+// `waiter` runs its later work only after what `producer` holds now (a
+// one-off event, destroyed again on every path).
+vc_status stream_waits_for(hipStream_t waiter, hipStream_t producer) {
+  hipEvent_t ev;
+  HIPCHK(hipEventCreateWithFlags(&ev, hipEventDisableTiming));
+  hipError_t e = hipEventRecord(ev, producer);
+  if (e == hipSuccess) e = hipStreamWaitEvent(waiter, ev, 0);
+  (void)hipEventDestroy(ev);
+  if (e != hipSuccess) return hipfail(e, "ordering a copy stream after the caller's stream");
+  return VC_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -56,18 +87,10 @@ vc_status vc_stagger_create(vc_stagger **out, void *const *slots, int32_t nslots
   for (int i = 0; i < nslots; ++i)
     if (!slots[i]) return vc::set_error(VC_EINVAL, "null staging slot");
   vc_stagger *s = new vc_stagger;
-  s->slots.assign(slots, slots + nslots);
-  s->slot_bytes = slot_bytes;
-  HIPCHK(hipStreamCreateWithFlags(&s->h2d, hipStreamNonBlocking));
-  HIPCHK(hipStreamCreateWithFlags(&s->d2h, hipStreamNonBlocking));
-  s->slot_free.resize(nslots);
-  for (auto &e : s->slot_free) HIPCHK(hipEventCreateWithFlags(&e, hipEventDisableTiming));
-  s->copy_start.resize(max_layers);
-  s->copied.resize(max_layers);
-  s->copy_recorded.assign(max_layers, 0);
-  for (int l = 0; l < max_layers; ++l) {
-    HIPCHK(hipEventCreate(&s->copy_start[l]));
-    HIPCHK(hipEventCreate(&s->copied[l]));
+  const vc_status st = stagger_init(s, slots, nslots, slot_bytes, max_layers);
+  if (st != VC_OK) {
+    vc_stagger_destroy(s);   // frees what was created; the error message stays the init failure's
+    return st;
   }
   *out = s;
   return VC_OK;
@@ -101,23 +124,15 @@ vc_status vc_stagger_release(vc_stagger *s, int32_t layer, void *stream) {
 
 vc_status vc_stagger_writeback(vc_stagger *s, void *host_dst, const void *dev_src, size_t bytes, void *after) {
   if (!s || !host_dst || !dev_src) return vc::set_error(VC_EINVAL, "bad writeback arguments");
-  hipEvent_t ev;
-  HIPCHK(hipEventCreateWithFlags(&ev, hipEventDisableTiming));
-  HIPCHK(hipEventRecord(ev, (hipStream_t)after));
-  HIPCHK(hipStreamWaitEvent(s->d2h, ev, 0));
-  HIPCHK(hipEventDestroy(ev));
+  const vc_status st = stream_waits_for(s->d2h, (hipStream_t)after);
+  if (st != VC_OK) return st;
   HIPCHK(hipMemcpyAsync(host_dst, dev_src, bytes, hipMemcpyDeviceToHost, s->d2h));
   return VC_OK;
 }
 
 vc_status vc_stagger_after(vc_stagger *s, void *stream) {
   if (!s) return vc::set_error(VC_EINVAL, "null stagger");
-  hipEvent_t ev;
-  HIPCHK(hipEventCreateWithFlags(&ev, hipEventDisableTiming));
-  HIPCHK(hipEventRecord(ev, (hipStream_t)stream));
-  HIPCHK(hipStreamWaitEvent(s->h2d, ev, 0));
-  HIPCHK(hipEventDestroy(ev));
-  return VC_OK;
+  return stream_waits_for(s->h2d, (hipStream_t)stream);
 }
 
 vc_status vc_stagger_sync(vc_stagger *s) {
@@ -136,11 +151,13 @@ vc_status vc_stagger_copy_ms(vc_stagger *s, int32_t layer, float *ms) {
 
 vc_status vc_stagger_destroy(vc_stagger *s) {
   if (!s) return VC_OK;
+  // only handles that exist are passed on, so no HIP error is left behind
+  // for a later call to pick up
   if (s->h2d) (void)hipStreamSynchronize(s->h2d);
   if (s->d2h) (void)hipStreamSynchronize(s->d2h);
-  for (auto e : s->slot_free) (void)hipEventDestroy(e);
-  for (auto e : s->copy_start) (void)hipEventDestroy(e);
-  for (auto e : s->copied) (void)hipEventDestroy(e);
+  for (auto *v : {&s->slot_free, &s->copy_start, &s->copied})
+    for (auto e : *v)
+      if (e) (void)hipEventDestroy(e);
   if (s->h2d) (void)hipStreamDestroy(s->h2d);
   if (s->d2h) (void)hipStreamDestroy(s->d2h);
   delete s;

@@ -160,3 +160,21 @@ def test_empty_batches_return_before_any_gpu_call(L):
     # a non-empty call with the same NULL tensors is rejected
     assert L.vc_argmax(4, 32768, 1, None, None, 1, None) == vcb.VC_EINVAL
     assert L.vc_quantize_int4_packed(2, 8, 128, None, None, 64, None, 1, 64, None, None, None) == vcb.VC_EINVAL
+
+
+def test_stagger_create_failure_leaves_nothing_behind(L):
+    # without a usable device the first stream creation fails: the call
+    # reports that HIP error (not one from the cleanup), frees the partly
+    # built object and leaves the output handle untouched
+    h = ctypes.c_void_p(0)
+    slots = (ctypes.c_void_p * 2)(1 << 20, 2 << 20)
+    r = L.vc_stagger_create(ctypes.byref(h), slots, 2, 1024, 4)
+    if r == vcb.VC_OK:
+        assert L.vc_stagger_destroy(h) == vcb.VC_OK
+        pytest.skip("a GPU is present: creation succeeded")
+    assert r == vcb.VC_EHIP
+    assert b"hipStreamCreateWithFlags" in L.vc_last_error()
+    assert h.value is None
+    # argument errors come before any HIP call
+    assert L.vc_stagger_create(ctypes.byref(h), slots, 0, 1024, 4) == vcb.VC_EINVAL
+    assert L.vc_stagger_destroy(None) == vcb.VC_OK
