@@ -89,3 +89,42 @@ def test_fp32_mode(G):
 
 def test_fp32_prefill():
     _check(1, 130, 4, 2, 64, 0, [0], dtype="fp32", seed=14)
+
+
+def test_sixteen_query_heads_per_kv_head():
+    # G = 16 (the largest grouping): 33 block rows -> 528 packed rows, three row groups
+    _check(1, 33, 32, 2, 128, 1280, [1201], seed=15, qstd=2.0)
+    # 12 rows -> 192 packed rows, one row group split 32 + 16 per SIMD
+    _check(2, 12, 16, 1, 128, 640, [640, 77], seed=16, qstd=2.0)
+
+
+def test_prefill_of_1024_rows():
+    # the largest block: a 1024-token causal prefill, then 1024 rows after a short context
+    _check(1, 1024, 4, 2, 128, 0, [0], seed=17, qstd=2.0)
+    _check(1, 1024, 2, 1, 64, 192, [130], seed=18, qstd=2.0)
+
+
+@pytest.mark.parametrize("M,G", [(20, 5), (33, 5), (45, 5)])
+def test_capacity_beyond_32bit_offsets(M, G):
+    # A capacity of 2^23 tokens puts the V channel rows of one head 16 MiB
+    # apart, 2 GiB in all: beyond the 32-bit offsets of the ping-pong kernel,
+    # so the four-wave kernel serves every row count here (R = 100, 165 and
+    # 225: 32- and 48-row waves, one and two row groups).  Only the first
+    # 3000 context tokens are valid, so the oracle reads a small cache.
+    import torch
+    import lossless_speculative_decoding_vc_amd as vc
+    B, Hkv, D, cl, small, big = 1, 1, 128, 3000, 3008, 1 << 23
+    Hq = G * Hkv
+    dev, ref = _inputs(B, M, Hq, Hkv, D, small, "bf16", 40 + M, 2.0)
+    ck = torch.zeros((B, Hkv, big, D), dtype=torch.bfloat16, device="cuda")
+    cv = torch.zeros((B, Hkv, D, big), dtype=torch.bfloat16, device="cuda")
+    ck[:, :, :small] = dev["ctx_k"]
+    cv[..., :small] = dev["ctx_v"]
+    cl_arr = np.array([cl], np.int32)
+    lse = torch.empty((B, M, Hq), dtype=torch.float32, device="cuda")
+    out = vc.verify_attn(dev["q"], ck, cv, to_dev(cl_arr), dev["blk_k"], dev["blk_v"], out_lse=lse)
+    torch.cuda.synchronize()
+    del ck, cv
+    o_ref, lse_ref = A.verify_attn(ref["q"], ref["ctx_k"], ref["ctx_v"], cl_arr, ref["blk_k"], ref["blk_v"])
+    assert_close(bf16_dev_to_f64(out), o_ref, TOL["bf16"], "out")
+    assert_close(lse.cpu().numpy(), lse_ref, TOL["bf16"] * 0.1, "lse")
