@@ -68,7 +68,8 @@ typedef struct vc_draft_args {
   float   scale;                  /* softmax scale, normally 1/sqrt(D)             */
   int32_t num_splits;             /* token splits per (b, KV head); 0 = automatic  */
   int64_t cap;                    /* main capacity per (b, KV head); multiple of 64 */
-  int64_t tcap;                   /* tail capacity (0 when no tail)                */
+  int64_t tcap;                   /* tail capacity (0 when no tail); cap + tcap    */
+                                  /* <= 2^30                                       */
   const void    *q;               /* [B][Hq][D]                                    */
   const int32_t *main_len;        /* [B][Hkv] valid main tokens                    */
   const void    *k;               /* DENSE [B][Hkv][cap][D]; INT4 u8 [B][Hkv][cap][D/2]:
@@ -114,11 +115,12 @@ size_t    vc_draft_workspace_size(const vc_draft_args *a);
  *   o[b][i][h] = sum_t softmax_t(scale * q.k_t) v_t.
  * With ctx_len = 0 and the prompt as the block this is causal prefill.     */
 typedef struct vc_verify_args {
-  int32_t B, Hq, Hkv, D, M;       /* D in {64, 128}; M >= 1; Hq % Hkv == 0         */
+  int32_t B, Hq, Hkv, D, M;       /* D in {64, 128}; M >= 1; Hq % Hkv == 0;        */
+                                  /* M*Hq/Hkv <= 65535*64, B*M*Hq < 2^31           */
   int32_t dtype;                  /* vc_dtype of every tensor below                */
   float   scale;
   int32_t num_splits;             /* key splits per (b, KV head); 0 = automatic    */
-  int64_t ccap;                   /* context capacity; multiple of 64              */
+  int64_t ccap;                   /* context capacity; multiple of 64, <= 2^30     */
   const void    *q;               /* [B][M][Hq][D]                                 */
   const void    *ctx_k;           /* [B][Hkv][ccap][D]                             */
   const void    *ctx_v;           /* [B][Hkv][D][ccap]                             */

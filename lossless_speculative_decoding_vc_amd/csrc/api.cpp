@@ -2,6 +2,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdarg>
+#include <cstdint>
 #include <cstdio>
 #include <string>
 
@@ -21,6 +22,8 @@ vc_status fail(vc_status s, const char *fmt, ...) {
   g_err = buf;
   return s;
 }
+
+constexpr int64_t kMaxTokens = int64_t(1) << 30;   // per (request, KV head) slot
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -54,6 +57,8 @@ vc_status check_draft_shape(const vc_draft_args *a) {
   if (i4 && a->D != 128) return fail(VC_ENOTSUP, "int4 main segment is compiled for head_dim 128");
   REQ(a->cap >= 0 && a->cap % 64 == 0, "cap (%lld) must be a non-negative multiple of 64", (long long)a->cap);
   REQ(a->tcap >= 0, "tcap must be non-negative");
+  // token indices inside the kernels are 32-bit
+  REQ(a->cap + a->tcap <= kMaxTokens, "cap + tcap (%lld) above 2^30 tokens", (long long)(a->cap + a->tcap));
   return VC_OK;
 }
 
@@ -96,6 +101,11 @@ vc_status check_verify_shape(const vc_verify_args *a) {
   REQ(a->dtype == VC_BF16 || a->dtype == VC_FP32, "unknown dtype %d", a->dtype);
   REQ(a->M >= 1, "M must be >= 1");
   REQ(a->ccap >= 0 && a->ccap % 64 == 0, "ccap (%lld) must be a non-negative multiple of 64", (long long)a->ccap);
+  REQ(a->ccap <= kMaxTokens, "ccap (%lld) above 2^30 tokens", (long long)a->ccap);
+  // packed rows M*G index row groups of at least 64 on a grid dimension capped at 65535
+  REQ((int64_t)a->M * (a->Hq / a->Hkv) <= 65535 * 64, "M * Hq/Hkv (%lld) above 65535 * 64",
+      (long long)a->M * (a->Hq / a->Hkv));
+  REQ((int64_t)a->B * a->M * a->Hq <= INT32_MAX, "B * M * Hq above 2^31 - 1");
   return VC_OK;
 }
 

@@ -82,6 +82,15 @@ def test_validation_rejects_before_launch(L):
     acc.B, acc.M, acc.V = 1, 0, 10
     assert L.vc_accept(ctypes.byref(acc), None) == vcb.VC_EINVAL
     assert L.vc_status_string(2) == b"VC_ENOTSUP"
+    # token indices inside the kernels are 32-bit: capacities are bounded
+    assert L.vc_draft_attn(ctypes.byref(_draft(cap=1 << 30, tcap=64)), None) == vcb.VC_EINVAL
+    assert b"2^30" in L.vc_last_error()
+    v2 = vcb.VerifyArgs()
+    v2.B, v2.Hq, v2.Hkv, v2.D, v2.M, v2.scale, v2.ccap = 1, 16, 1, 128, 33, 0.088, (1 << 30) + 64
+    assert L.vc_verify_attn(ctypes.byref(v2), None) == vcb.VC_EINVAL
+    v2.ccap, v2.M = 64, 65535 * 4 + 1   # 16 * M packed rows need more than 65535 row groups of 64
+    assert L.vc_verify_attn(ctypes.byref(v2), None) == vcb.VC_EINVAL
+    assert b"65535 * 64" in L.vc_last_error()
     # (request, KV head) slices index a grid dimension capped at 65535
     assert L.vc_draft_attn(ctypes.byref(_draft(B=40000, Hq=4, Hkv=2)), None) == vcb.VC_EINVAL
     assert b"65535" in L.vc_last_error()
