@@ -283,7 +283,7 @@ vc_status vc_compact_kv(int32_t B, int32_t Hkv, int32_t D, int32_t dtype, const 
   REQ(dtype == VC_BF16 || dtype == VC_FP32, "unknown dtype %d", dtype);
   if (D != 64 && D != 128) return fail(VC_ENOTSUP, "head_dim %d not compiled (64 or 128)", D);
   REQ(cap % 32 == 0, "cap (%lld) must be a multiple of 32", (long long)cap);
-  REQ(cap / 32 <= 0x7fffffff, "cap too large");
+  REQ(cap <= kMaxTokens, "cap (%lld) above 2^30 tokens", (long long)cap);
   REQ((int64_t)B * Hkv <= 65535, "at most 65535 (request, KV head) slices per call");
   if (B == 0 || cap == 0) return VC_OK;
   REQ(idx_stride >= 1, "idx_stride must be >= 1");
@@ -300,6 +300,7 @@ vc_status vc_quantize_int4(int32_t B, int32_t Hkv, int32_t D, const void *src_k,
                            const int32_t *dst_start, void *k_codes, void *k_scale, void *k_zero, void *v_codes,
                            void *v_scale, void *v_zero, void *stream) {
   REQ(B >= 0 && Hkv >= 1 && n_groups >= 0 && src_cap >= 0 && cap >= 0, "bad quantize shape");
+  REQ(cap <= kMaxTokens && src_cap <= kMaxTokens, "cap or src_cap above 2^30 tokens");
   if (D != 128) return fail(VC_ENOTSUP, "the int4 cache is compiled for head_dim 128 (got %d)", D);
   REQ(cap % 32 == 0, "cap (%lld) must be a multiple of 32", (long long)cap);
   REQ(n_groups <= 65535, "at most 65535 groups per call (got %d)", n_groups);
@@ -334,6 +335,7 @@ vc_status vc_quantize_int4_packed(int32_t B, int32_t Hkv, int32_t D, const void 
                                   int64_t src_cap, const int32_t *src_start, int32_t n_groups, int64_t cap,
                                   const int32_t *dst_start, void *packed, void *stream) {
   REQ(B >= 0 && Hkv >= 1 && n_groups >= 0 && src_cap >= 0 && cap >= 0, "bad quantize shape");
+  REQ(cap <= kMaxTokens && src_cap <= kMaxTokens, "cap or src_cap above 2^30 tokens");
   if (D != 128) return fail(VC_ENOTSUP, "the int4 cache is compiled for head_dim 128 (got %d)", D);
   REQ(cap % 32 == 0, "cap (%lld) must be a multiple of 32", (long long)cap);
   REQ(n_groups <= 65535, "at most 65535 groups per call (got %d)", n_groups);
