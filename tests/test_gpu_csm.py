@@ -139,3 +139,64 @@ def test_merged_cache_feeds_draft_attention():
                                                                    deg[b, h, :n_in], 4, 16, chunk, r)
     o_ref, _ = A.draft_attn(bf16_to_f64(qbits), k_ref, v_ref, ml, degree=d_ref)
     assert_close(bf16_dev_to_f64(out), o_ref, TOL["bf16"], "draft over the merged cache")
+
+
+def _survivors_and_unmerged(info, n):
+    """Vectorised form of the two helpers above for long sequences: the
+    surviving positions and, for each, whether it absorbed no token."""
+    gone = np.zeros(n, bool)
+    absorbed = np.zeros(n, np.int64)
+    for c in info:
+        m = np.asarray(c["merged"], bool)
+        if not m.any():
+            continue
+        gone[c["start"] + 2 * np.nonzero(m)[0]] = True
+        cnt = np.bincount(np.asarray(c["match"])[m], minlength=(c["end"] - c["start"]) // 2)
+        absorbed[c["start"] + 2 * np.arange(len(cnt)) + 1] += cnt
+    pos = np.nonzero(~gone)[0]
+    return pos, absorbed[pos] == 0
+
+
+def test_full_size_round_sampled_slices():
+    # The launch configuration of the 128K cohort round: 16 requests x 8 KV
+    # heads, 131072 tokens, 4 sinks, 1024 recent tokens, chunks of 64, r = 1,
+    # no input degrees.  Two slices hold planted keys and are checked against
+    # the oracle; every slice keeps the same number of tokens and its degrees
+    # (token counts) add up to the input length.
+    import torch
+    import lossless_speculative_decoding_vc_amd as vc
+    B, Hkv, n, sink, recent, chunk, r = 16, 8, 131072, 4, 1024, 64, 1.0
+    cap_out = n // 2 + 1024
+    dev = "cuda"
+    K = S.torch_normal((B, Hkv, n, D), 61, dev, torch.bfloat16, 1.0)
+    V = S.torch_normal((B, Hkv, n // 32, D, 32), 62, dev, torch.bfloat16, 1.0)
+    samples = [(0, 0), (11, 5)]
+    planted = {}
+    for i, (b, h) in enumerate(samples):
+        k, v, _ = S.csm_planted(1, 1, n, D, sink, recent, chunk, _plant(r), 63 + i)
+        kb, vb = S.f32_to_bf16_bits(k[0, 0]), S.f32_to_bf16_bits(v[0, 0])
+        planted[(b, h)] = (kb, vb)
+        K[b, h] = to_dev_bf16(kb)
+        V[b, h] = to_dev_bf16(blocked32(vb))
+    ok = torch.zeros((B, Hkv, cap_out, D), dtype=torch.bfloat16, device=dev)
+    ov = torch.zeros((B, Hkv, cap_out // 32, D, 32), dtype=torch.bfloat16, device=dev)
+    od = torch.zeros((B, Hkv, cap_out), dtype=torch.float32, device=dev)
+    n_out = vc.csm_round(K, V, n, sink, recent, chunk, r, ok, ov, od)
+    torch.cuda.synchronize()
+    del K, V
+    assert n_out == C.survivors(n, sink, recent, chunk, r)
+    deg_all = od[:, :, :n_out].double().sum(-1).cpu().numpy()
+    np.testing.assert_array_equal(deg_all, np.full((B, Hkv), float(n)))
+    for (b, h), (kb, vb) in planted.items():
+        k2, v2, d2, info = C.csm_round(bf16_to_f64(kb), bf16_to_f64(vb), np.ones(n), sink, recent, chunk, r)
+        assert len(k2) == n_out
+        got_d = od[b, h, :n_out].cpu().numpy()
+        np.testing.assert_array_equal(got_d, d2.astype(np.float32))
+        got_k = ok[b, h, :n_out].contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+        got_v = (ov[b, h].contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+                 .transpose(0, 2, 1).reshape(cap_out, D)[:n_out])
+        pos, unmerged = _survivors_and_unmerged(info, n)
+        np.testing.assert_array_equal(got_k[unmerged], kb[pos[unmerged]])
+        np.testing.assert_array_equal(got_v[unmerged], vb[pos[unmerged]])
+        assert_close(bf16_to_f64(got_k), k2, 1e-2, "centroid keys")
+        assert_close(bf16_to_f64(got_v), v2, 1e-2, "centroid values")
