@@ -43,6 +43,8 @@ CPU oracle timed on a bounded sample of the same workload.
                  interleaved 5120-byte block per 32 tokens)
   csm128k        one Chunked Soft Matching round (vc_csm_round, r = 1, chunks of
                  64) over the cohort's 131072-token caches (16 x 8 KV heads)
+  compact128k    eviction compaction of the cohort's 131072-token caches (16 x 8 KV
+                 heads) to 32768 kept tokens (vc_compact_kv)
   draft_cohort   one layer-step of the staggered batch's drafting cohort (16 requests,
                  40 q / 8 KV heads, 32768 tokens + degrees + 32 tail tokens), alone
   lmhead_verify  the verifying cohort's LM head fused with argmax + acceptance
@@ -77,8 +79,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=1)
     ap.add_argument("--workload", default="stagger128k",
                     choices=["stagger128k", "verify32k", "verify128k", "verify1m", "draft128k", "draft128k_int4",
-                             "draft1m_int4", "draft128k_int4p", "draft1m_int4p", "draft_cohort", "long1m", "tiny", "quant128k_int4", "quant128k_int4p", "csm128k", "lmhead_verify", "lmhead_draft",
-                             "copy1g"])
+                             "draft1m_int4", "draft128k_int4p", "draft1m_int4p", "draft_cohort", "long1m", "tiny", "quant128k_int4", "quant128k_int4p", "csm128k", "compact128k", "lmhead_verify",
+                             "lmhead_draft", "copy1g"])
     ap.add_argument("--layers", type=int, default=None,
                     help="model layers per round (default 64 for stagger128k, 40 for long1m)")
     ap.add_argument("--distinct-layers", type=int, default=16,
@@ -121,6 +123,7 @@ KERNEL_OF = {
     "quant128k_int4": "vc_quantize_int4: quantize_int4",
     "quant128k_int4p": "vc_quantize_int4_packed: quantize_int4",
     "csm128k": "vc_csm_round: csm_round_kernel",
+    "compact128k": "vc_compact_kv: compact_kv",
     "lmhead_verify": "vc_lm_head_accept: lm_argmax + argmax_partials + accept_rows",
     "lmhead_draft": "vc_lm_head_argmax: lm_argmax + argmax_partials",
     "copy1g": "torch copy_ (1 GiB device to device)",
@@ -666,6 +669,26 @@ def kernel_alone(args):
             n_keep.append(vc.csm_round(K, Vb, cap, 4, 1024, 64, 1.0, ok, ov, od))
         flops = 0.0
         nbytes = B * Hkv * cap * D * 2 * 2 + B * Hkv * (cap // 2 + 514) * (D * 2 * 2 + 4)
+    elif args.workload == "compact128k":
+        # eviction compaction of the cohort's caches: 16 requests x 8 KV heads, a 131072-token full cache (V
+        # channel-major) -> the 32768 kept tokens (a sorted uniform random subset per request, the same for its
+        # heads) in the draft layout; the algorithmic bytes are the kept rows read and written
+        B, Hkv, D, n, kept = 16, 8, 128, 131072, 32768
+        K = _bf16_randn((B, Hkv, n, D), 17, dev)
+        Vt = _bf16_randn((B, Hkv, D, n), 18, dev)
+        g = torch.Generator(device=dev)
+        g.manual_seed(19)
+        idx = torch.stack([torch.randperm(n, generator=g, device=dev)[:kept].sort().values for _ in range(B)])
+        idx = idx.to(torch.int32).contiguous()
+        nk = torch.full((B,), kept, dtype=torch.int32, device=dev)
+        dk = torch.empty((B, Hkv, kept, D), dtype=torch.bfloat16, device=dev)
+        dv = torch.empty((B, Hkv, kept // 32, D, 32), dtype=torch.bfloat16, device=dev)
+        dl = torch.empty((B, Hkv), dtype=torch.int32, device=dev)
+
+        def call(i):
+            vc.compact_kv(K, Vt, idx, nk, dk, dv, dst_len=dl)
+        flops = 0.0
+        nbytes = B * Hkv * kept * D * 2 * 4 + B * kept * 4
     elif args.workload == "quant128k_int4p":
         # the same int4 cache built in the packed layout (one 5120-byte block per 32 tokens)
         B, Hkv, D, cap = 32, 8, 128, 131072

@@ -85,3 +85,29 @@ def test_draft_over_compacted_cache_is_masked_full_attention():
                             bias=np.concatenate([mask, np.zeros(len(extra_k))]))
             ref[b, h] = o
     assert_close(bf16_dev_to_f64(out), ref, TOL["bf16"], "draft over compacted cache")
+
+
+def test_full_size_sampled_slices_bit_exact():
+    # The launch configuration of the 128K cohort's compaction: 16 requests x
+    # 8 KV heads, a 131072-token full cache, 32768 kept tokens per request (a
+    # sorted random subset, as the bench times it).  Three sampled slices are
+    # compared with the oracle bit for bit.
+    import torch
+    import lossless_speculative_decoding_vc_amd as vc
+    B, Hkv, D, n, kept = 16, 8, 128, 131072, 32768
+    dev = "cuda"
+    K = S.torch_normal((B, Hkv, n, D), 81, dev, torch.bfloat16, 1.0)
+    Vt = S.torch_normal((B, Hkv, D, n), 82, dev, torch.bfloat16, 1.0)
+    rng = np.random.default_rng(83)
+    idx = np.stack([np.sort(rng.choice(n, kept, replace=False)) for _ in range(B)]).astype(np.int32)
+    dk = torch.empty((B, Hkv, kept, D), dtype=torch.bfloat16, device=dev)
+    dv = torch.empty((B, Hkv, kept // 32, D, 32), dtype=torch.bfloat16, device=dev)
+    dl = torch.empty((B, Hkv), dtype=torch.int32, device=dev)
+    vc.compact_kv(K, Vt, to_dev(idx), to_dev(np.full(B, kept, np.int32)), dk, dv, dst_len=dl)
+    torch.cuda.synchronize()
+    assert np.all(dl.cpu().numpy() == kept)
+    host = lambda t: t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+    for b, h in [(0, 0), (9, 4), (15, 7)]:
+        ref_k, ref_v = compact_kv(host(K[b, h]), host(Vt[b, h].t()), idx[b])
+        np.testing.assert_array_equal(host(dk[b, h]), ref_k)
+        np.testing.assert_array_equal(host(dv[b, h]).transpose(0, 2, 1).reshape(kept, D), ref_v)
