@@ -25,3 +25,27 @@ def test_workload_names_and_layer_defaults():
         assert bench.parse().layers == layers
     sys.argv = ["bench.py", "--workload", "long1m", "--layers", "8"]
     assert bench.parse().layers == 8
+
+
+def test_every_kernel_leg_names_its_kernel():
+    # each single-kernel workload reports the entry point and kernels it times
+    import argparse
+    sys.path.insert(0, ROOT)
+    import bench
+    captured = {}
+    orig = argparse.ArgumentParser.parse_args
+
+    def grab(self, *a, **k):
+        for act in self._actions:
+            if act.dest == "workload":
+                captured["choices"] = list(act.choices)
+        return orig(self, *a, **k)
+    sys.argv = ["bench.py"]
+    argparse.ArgumentParser.parse_args = grab
+    try:
+        bench.parse()
+    finally:
+        argparse.ArgumentParser.parse_args = orig
+    rounds = {"stagger128k", "long1m", "tiny"}
+    legs = [w for w in captured["choices"] if w not in rounds]
+    assert legs and all(w in bench.KERNEL_OF for w in legs), set(legs) - set(bench.KERNEL_OF)
