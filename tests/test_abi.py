@@ -187,3 +187,38 @@ def test_stagger_create_failure_leaves_nothing_behind(L):
     # argument errors come before any HIP call
     assert L.vc_stagger_create(ctypes.byref(h), slots, 0, 1024, 4) == vcb.VC_EINVAL
     assert L.vc_stagger_destroy(None) == vcb.VC_OK
+
+
+def test_csm_and_commit_validation_is_host_only(L):
+    from oracle import csm as C
+    fake = ctypes.c_void_p(1 << 20)
+    n = ctypes.c_int32(-1)
+    base = dict(B=2, Hkv=2, D=128, n_in=300, sink=4, recent=16, chunk=64, r=1.0, ik=fake, iv=fake, ideg=None,
+                cap_in=320, ok=fake, ov=fake, odeg=fake, cap_out=320)
+
+    def csm(**kw):
+        a = {**base, **kw}
+        return L.vc_csm_round(a["B"], a["Hkv"], a["D"], a["n_in"], a["sink"], a["recent"], a["chunk"], a["r"],
+                              a["ik"], a["iv"], a["ideg"], a["cap_in"], a["ok"], a["ov"], a["odeg"], a["cap_out"],
+                              ctypes.byref(n), None)
+    assert csm(D=64) == vcb.VC_ENOTSUP
+    assert csm(chunk=1) == vcb.VC_EINVAL
+    assert csm(r=1.5) == vcb.VC_EINVAL
+    assert csm(sink=200, recent=200) == vcb.VC_EINVAL
+    assert csm(cap_out=64) == vcb.VC_EINVAL       # the round keeps more tokens than that
+    assert csm(ik=None) == vcb.VC_EINVAL
+    # an empty batch still reports how many tokens the round keeps, as the oracle counts them
+    assert csm(B=0, ik=None, iv=None, ok=None, ov=None, odeg=None) == vcb.VC_OK
+    assert n.value == C.survivors(300, 4, 16, 64, 1.0)
+
+    def commit(**kw):
+        a = dict(B=2, Hkv=2, D=128, M=9, dtype=0, cap=1024, blocked=0, bk=fake, bv=fake, no=fake, dk=fake, dv=fake,
+                 ln=fake, deg=None, dhs=0)
+        a.update(kw)
+        return L.vc_commit_rows(a["B"], a["Hkv"], a["D"], a["M"], a["dtype"], a["cap"], a["blocked"], a["bk"],
+                                a["bv"], a["no"], a["dk"], a["dv"], a["ln"], a["deg"], a["dhs"], None)
+    assert commit(dtype=7) == vcb.VC_EINVAL
+    assert commit(blocked=1, cap=1000) == vcb.VC_EINVAL
+    assert commit(deg=fake, dhs=5) == vcb.VC_EINVAL
+    assert commit(ln=None) == vcb.VC_EINVAL
+    assert commit(B=0, bk=None, bv=None, no=None, dk=None, dv=None, ln=None) == vcb.VC_OK
