@@ -222,3 +222,27 @@ def test_csm_and_commit_validation_is_host_only(L):
     assert commit(deg=fake, dhs=5) == vcb.VC_EINVAL
     assert commit(ln=None) == vcb.VC_EINVAL
     assert commit(B=0, bk=None, bv=None, no=None, dk=None, dv=None, ln=None) == vcb.VC_OK
+
+
+def test_csm_survivor_count_matches_oracle_on_many_shapes(L):
+    # the library's survivor count (host integer arithmetic, reported even for
+    # an empty batch) equals the oracle's over a seeded sweep of shapes,
+    # including r at 0 and 1, chunks of 2 and 128, and no middle segment
+    import numpy as np
+    from oracle import csm as C
+    rng = np.random.default_rng(5)
+    n = ctypes.c_int32(-1)
+    cases = [(40, 20, 20, 2, 1.0), (40, 0, 0, 128, 0.0), (1, 0, 0, 64, 1.0), (131072, 4, 1024, 64, 1.0)]
+    for _ in range(200):
+        n_in = int(rng.integers(1, 5000))
+        sink = int(rng.integers(0, 40))
+        recent = int(rng.integers(0, 200))
+        if sink + recent > n_in:
+            continue
+        cases.append((n_in, sink, recent, int(rng.integers(2, 129)), float(np.float32(rng.random()))))
+    for n_in, sink, recent, chunk, r in cases:
+        cap = (n_in + 31) // 32 * 32
+        st = L.vc_csm_round(0, 2, 128, n_in, sink, recent, chunk, r, None, None, None, cap, None, None, None, cap,
+                            ctypes.byref(n), None)
+        assert st == vcb.VC_OK, (n_in, sink, recent, chunk, r, L.vc_last_error())
+        assert n.value == C.survivors(n_in, sink, recent, chunk, r), (n_in, sink, recent, chunk, r)
