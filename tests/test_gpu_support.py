@@ -172,3 +172,35 @@ def test_stagger_slot_reuse_under_forced_delays(delayed):
         torch.cuda.synchronize()
         assert torch.equal(outs[l], direct), l
     stg.close()
+
+
+def test_stagger_after_and_writeback_wait_for_the_compute_stream():
+    # The compute stream spins for a few milliseconds and then writes; the
+    # copy streams are told to wait for it.  The host-to-device copy into the
+    # slot must land after that write (the slot ends with the host bytes), and
+    # the write-back must read the buffer after it (the host gets the written
+    # bytes).  Without the waits the copies would run first.
+    import torch
+    import lossless_speculative_decoding_vc_amd as vc
+    n = 1 << 20
+    slot = torch.zeros(n, dtype=torch.uint8, device="cuda")
+    src = torch.full((n,), 7, dtype=torch.uint8, pin_memory=True)
+    dev_buf = torch.zeros(n, dtype=torch.uint8, device="cuda")
+    back = torch.zeros(n, dtype=torch.uint8, pin_memory=True)
+    stg = vc.Stagger([slot], n, 1)
+    try:
+        comp = torch.cuda.Stream()
+        torch.cuda.synchronize()
+        with torch.cuda.stream(comp):
+            torch.cuda._sleep(20_000_000)   # a few milliseconds of spinning, then it exits
+            slot.fill_(3)
+            dev_buf.fill_(9)
+        stg.after(comp)
+        stg.stream_layer(0, src, n)
+        stg.writeback(back, dev_buf, n, comp)
+        stg.sync()
+        torch.cuda.synchronize()
+        assert bool((slot == 7).all()), "the copy into the slot ran before the compute stream's write"
+        assert bool((back == 9).all()), "the write-back read the buffer before the compute stream wrote it"
+    finally:
+        stg.close()
