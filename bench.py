@@ -206,6 +206,9 @@ class Cohort:
 
 
 def run_stagger(args, t_start):
+    """Rounds of the staggered batch, each enqueued natively by ``vc_stagger_round``: the drafting cohort's 32
+    steps over 64 layers on one stream, the verifying cohort's 64 layers (each after its layer's copy into the
+    two-slot ring) and its LM head + acceptance + commit on another, the copy engines streaming throughout."""
     import torch
     import lossless_speculative_decoding_vc_amd as vc
     c = Cfg()
@@ -215,13 +218,6 @@ def run_stagger(args, t_start):
     W = _bf16_randn((c.V, c.Dm), 3, dev, std=0.02)   # LM head, vocab-major
     X = Cohort(c, "A", L, NLD, W, seed=4)
     Y = Cohort(c, "B", L, NLD, W, seed=40)
-    for co in (X, Y):
-        co.dws = torch.empty(max(vc.draft_workspace_size(
-            B=c.B, Hq=c.Hq, Hkv=c.Hkv, D=c.D, dtype=0, fmt=0, scale=c.D ** -0.5, cap=c.cap, tcap=c.k), 16),
-            dtype=torch.uint8, device=dev)
-        co.vws = torch.empty(max(vc.verify_workspace_size(
-            B=c.B, Hq=c.Hq, Hkv=c.Hkv, D=c.D, M=c.M, dtype=0, scale=c.D ** -0.5, ccap=c.N), 16),
-            dtype=torch.uint8, device=dev)
     # full cache: two 8 GiB HBM staging slots fed from two pinned 8 GiB host
     # buffers (layers rotate over them; content does not change the traffic)
     kv_half = c.B * c.Hkv * c.N * c.D * 2          # bytes of K (and of V) per layer
@@ -235,100 +231,62 @@ def run_stagger(args, t_start):
         p.copy_(slots[0])
     blk_bytes = c.B * c.Hkv * c.M * c.D * 2
     host_commit = torch.empty((L, 2, blk_bytes), dtype=torch.uint8, pin_memory=True)
+    for co in (X, Y):
+        co.dws = vc.new_workspace(vc.draft_workspace_size(
+            B=c.B, Hq=c.Hq, Hkv=c.Hkv, D=c.D, dtype=0, fmt=0, scale=c.D ** -0.5, cap=c.cap, tcap=c.k), dev)
+        co.vws = vc.new_workspace(vc.verify_workspace_size(
+            B=c.B, Hq=c.Hq, Hkv=c.Hkv, D=c.D, M=c.M, dtype=0, scale=c.D ** -0.5, ccap=c.N), dev)
+        # the per-layer calls of both roles, checked once (structs of raw pointers into the cohort's buffers)
+        co.dargs = [vc.draft_args(co.dq[l % NLD], co.K[l % NLD], co.Vt[l % NLD], co.len[l], degree=co.deg[l % NLD],
+                                  tail_k=co.tail_k, tail_v=co.tail_v, tail_len=co.taillen[1], out=co.dout,
+                                  workspace=co.dws) for l in range(L)]
+        co.vargs = [vc.verify_args(co.vq[l % NLD], None, None, co.ctx_len, co.bk[l % NLD], co.bv[l % NLD], co.vout,
+                                   workspace=co.vws, ccap=c.N) for l in range(L)]
+        co.commit = [dict(dst_k=co.K[l % NLD], dst_v=co.Vt[l % NLD], length=co.len[l], degree=co.deg[l % NLD],
+                          v_blocked=True, host_k=host_commit[l, 0], host_v=host_commit[l, 1]) for l in range(L)]
+        co.am = torch.empty((c.B, c.M), dtype=torch.int32, device=dev)
+        co.n_acc = torch.empty(c.B, dtype=torch.int32, device=dev)
+        co.toks = torch.empty((c.B, c.M), dtype=torch.int32, device=dev)
+        co.n_out = torch.empty(c.B, dtype=torch.int32, device=dev)
     stg = vc.Stagger(slots, slot_bytes, L)
     ver_s = torch.cuda.Stream()
     dr_s = torch.cuda.Stream()
+    host_kv = [pool[l % 2] for l in range(L)]
     torch.cuda.synchronize()
     setup_s = time.time() - t_start
     log(f"setup done in {setup_s:.1f} s")
+    timers = {"draft": [], "verify": []}
 
-    def slot_views(ptr):
-        base = slots[0] if ptr == slots[0].data_ptr() else slots[1]
-        kk = base[:kv_half].view(torch.bfloat16).view(c.B, c.Hkv, c.N, c.D)
-        vv = base[kv_half:].view(torch.bfloat16).view(c.B, c.Hkv, c.D, c.N)
-        return kk, vv
-
-    def enqueue_draft_step(Yc, i, timers):
-        for l in range(L):
-            j = l % NLD
-            ev = None
-            if timers is not None and l % 8 == 0:
-                ev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-                ev[0].record(dr_s)
-            vc.draft_attn(Yc.dq[j], Yc.K[j], Yc.Vt[j], Yc.len[l], degree=Yc.deg[j],
-                          tail_k=Yc.tail_k, tail_v=Yc.tail_v, tail_len=Yc.taillen[i + 1],
-                          out=Yc.dout, workspace=Yc.dws, stream=dr_s)
-            if ev is not None:
-                ev[1].record(dr_s)
-                timers["draft"].append((ev, l))
-        vc.lm_head_argmax(Yc.hd[i], W, out=Yc.drafts.view(-1)[i:], out_stride=c.k, workspace=Yc.lws_d,
-                          stream=dr_s)
-
-    def run_round(Xc, Yc, mode, timers=None):
+    def run_round(Xc, Yc, mode, timed=False):
         """Cohort Xc verifies, Yc drafts.  Returns verified tokens."""
-        nsteps_per_layer = [0] * L
-        if mode == "bulk":
-            for i in range(c.k):
-                enqueue_draft_step(Yc, i, timers)
-            stg.after(dr_s)
-            ver_s.wait_stream(dr_s)
-        else:
-            # spread the k draft steps over the verify layers
-            for i in range(c.k):
-                nsteps_per_layer[(i * L) // c.k] += 1
-        stg.stream_layer(0, pool[0], slot_bytes)
-        if L > 1:
-            stg.stream_layer(1, pool[1], slot_bytes)
-        step = 0
-        for l in range(L):
-            j = l % NLD
-            ptr = stg.acquire(l, ver_s)
-            kk, vv = slot_views(ptr)
-            ev = None
-            if timers is not None:
-                ev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-                ev[0].record(ver_s)
-            vc.verify_attn(Xc.vq[j], kk, vv, Xc.ctx_len, Xc.bk[j], Xc.bv[j], out=Xc.vout,
-                           workspace=Xc.vws, stream=ver_s)
-            if ev is not None:
-                ev[1].record(ver_s)
-                timers["verify"].append(ev)
-            stg.release(l, ver_s)
-            if l + 2 < L:
-                stg.stream_layer(l + 2, pool[l % 2], slot_bytes)
-            for _ in range(nsteps_per_layer[l]):
-                enqueue_draft_step(Yc, step, timers)
-                step += 1
-        # verify LM head fused with the greedy argmax and the acceptance, then commit
-        am, n_acc, toks, n_out = vc.lm_head_accept(Xc.hv, W, Xc.drafts, workspace=Xc.lws_v, stream=ver_s)
-        for l in range(L):
-            j = l % NLD
-            vc.commit_rows(Xc.bk[j], Xc.bv[j], n_out, Xc.K[j], Xc.Vt[j], Xc.len[l], degree=Xc.deg[j],
-                           v_blocked=True, stream=ver_s)
-            stg.writeback(host_commit[l, 0], Xc.bk[j], blk_bytes, ver_s)
-            stg.writeback(host_commit[l, 1], Xc.bv[j], blk_bytes, ver_s)
+        stg.round(L, mode, W, draft=Yc.dargs, step_tail_len=Yc.taillen[1:c.k + 1], draft_hidden=Yc.hd,
+                  drafts=Yc.drafts, draft_lm_ws=Yc.lws_d, verify=Xc.vargs, host_kv=host_kv, kv_bytes=slot_bytes,
+                  v_offset=kv_half, verify_hidden=Xc.hv, verify_drafts=Xc.drafts, argmax=Xc.am, accept_len=Xc.n_acc,
+                  out_tokens=Xc.toks, n_out=Xc.n_out, verify_lm_ws=Xc.lws_v, commit=Xc.commit,
+                  time_kernels=timed, draft_stream=dr_s, verify_stream=ver_s)
         torch.cuda.synchronize()
         stg.sync()
-        n_acc_h = n_acc.cpu().numpy()
-        n_out_h = n_out.cpu().numpy()
-        ok = bool(np.array_equal(n_acc_h, Xc.planted_n))
+        if timed:
+            d_ms, v_ms = stg.round_times()
+            timers["draft"] += [ms / L for ms in d_ms]   # per call: a step is L back-to-back draft calls
+            timers["verify"] += v_ms
+        ok = bool(np.array_equal(Xc.n_acc.cpu().numpy(), Xc.planted_n))
         # the drafting cohort's argmax must reproduce its planted drafts
         ok_d = bool(np.array_equal(Yc.drafts.cpu().numpy(), Yc.planted_d))
-        return int(n_out_h.sum()), ok and ok_d
+        return int(Xc.n_out.sum().item()), ok and ok_d
 
     cohorts = [X, Y]
     for w in range(args.warmup):
         tw = time.time()
-        run_round(cohorts[w % 2], cohorts[(w + 1) % 2], "stagger")
+        run_round(cohorts[w % 2], cohorts[(w + 1) % 2], vc.ROUND_STAGGERED)
         log(f"warmup round {w} done in {time.time() - tw:.2f} s")
-    timers = {"draft": [], "verify": []}
     torch.cuda.synchronize()
     t0 = time.time()
     verified, parity_ok = 0, True
     for s in range(args.steps):
         r = args.warmup + s
         tr = time.time()
-        v, ok = run_round(cohorts[r % 2], cohorts[(r + 1) % 2], "stagger", timers)
+        v, ok = run_round(cohorts[r % 2], cohorts[(r + 1) % 2], vc.ROUND_STAGGERED, timed=True)
         verified += v
         parity_ok &= ok
         log(f"timed round {s} done in {time.time() - tr:.2f} s, verified {v}, parity {ok}")
@@ -339,14 +297,14 @@ def run_stagger(args, t_start):
     if not args.no_bulk:
         r = args.warmup + args.steps
         tb = time.time()
-        _, ok = run_round(cohorts[r % 2], cohorts[(r + 1) % 2], "bulk")
+        _, ok = run_round(cohorts[r % 2], cohorts[(r + 1) % 2], vc.ROUND_BULK)
         bulk_s = time.time() - tb
         parity_ok &= ok
         log(f"bulk-synchronous round done in {bulk_s:.2f} s")
 
     step_s = (t1 - t0) / args.steps
-    d_ms = np.array([e[0].elapsed_time(e[1]) for e, _ in timers["draft"]])
-    v_ms = np.array([e[0].elapsed_time(e[1]) for e in timers["verify"]])
+    d_ms = np.array(timers["draft"])
+    v_ms = np.array(timers["verify"])
     mean_len = float(torch.stack([co.len.float().mean() for co in cohorts]).mean())
     # algorithmic bytes of one draft call: compressed K+V (+ tail) + degrees + q + out
     d_bytes = (c.B * c.Hkv * (mean_len + c.k / 2) * c.D * 2 * 2 + c.B * mean_len * 4
@@ -356,6 +314,8 @@ def run_stagger(args, t_start):
     d_avg = float(np.mean(d_ms)) * 1e-3
     v_avg = float(np.mean(v_ms)) * 1e-3
     pcie = slot_bytes / (np.mean(copy_ms) * 1e-3) / 1e9
+    # the round moves 64 layers x 8.59 GB of full cache over the link: the ceiling of verified tokens/s
+    pcie_ceiling = verified / args.steps / (L * slot_bytes / (pcie * 1e9))
     res = {
         "value": verified / (t1 - t0),
         "ms_per_step": step_s * 1e3,
@@ -367,9 +327,12 @@ def run_stagger(args, t_start):
         "verify_tflops": v_flops / v_avg / 1e12,
         "verify_gbs": v_bytes / v_avg / 1e9,
         "pcie_h2d_gbs": pcie,
+        "pcie_ceiling_tokens_per_s": pcie_ceiling,
         "bulk_sync_s": bulk_s,
         "verified_per_round": verified / args.steps,
         "d_bytes": d_bytes, "v_bytes": v_bytes, "v_flops": v_flops,
+        "timed_calls": {"draft": len(d_ms) * L, "verify": len(v_ms),
+                        "how": "draft: one event pair per step around its back-to-back draft calls; verify: per call"},
     }
     stg.close()
     return res
@@ -463,12 +426,12 @@ def run_long1m(args, t_start):
     taillen = [torch.full((B,), i, dtype=torch.int32, device=dev) for i in range(k + 1)]
     ml = torch.full((B, Hkv), N, dtype=torch.int32, device=dev)
     dout = torch.empty((B, Hq, D), dtype=torch.bfloat16, device=dev)
-    dws = torch.empty(1 << 26, dtype=torch.uint8, device=dev)
+    dws = vc.new_workspace(1 << 26, dev)
     vq = [_bf16_randn((B, M, Hq, D), 340 + i, dev) for i in range(NLD)]
     bk = _bf16_randn((B, Hkv, M, D), 350, dev)
     bv = _bf16_randn((B, Hkv, D, M), 351, dev)
     vout = torch.empty((B, M, Hq, D), dtype=torch.bfloat16, device=dev)
-    vws = torch.empty(1 << 26, dtype=torch.uint8, device=dev)
+    vws = vc.new_workspace(1 << 26, dev)
     ctx_len = torch.full((B,), N, dtype=torch.int32, device=dev)
     W = _bf16_randn((V, Dm), 352, dev, std=0.02)   # LM head, vocab-major
     lws_d = vc.lm_head_argmax_workspace(B, V, dev)
@@ -605,7 +568,7 @@ def kernel_alone(args):
                      bv=_bf16_randn((B, Hkv, D, M), 50 + i, dev)) for i in range(nset)]
         cl = torch.full((B,), N, dtype=torch.int32, device=dev)
         out = torch.empty((B, M, Hq, D), dtype=torch.bfloat16, device=dev)
-        ws = torch.empty(1 << 26, dtype=torch.uint8, device=dev)
+        ws = vc.new_workspace(1 << 26, dev)
 
         def call(i):
             st = sets[i % nset]
@@ -738,7 +701,7 @@ def kernel_alone(args):
         q = _bf16_randn((B, Hq, D), 3, dev)
         ml = torch.full((B, Hkv), cap, dtype=torch.int32, device=dev)
         out = torch.empty((B, Hq, D), dtype=torch.bfloat16, device=dev)
-        ws = torch.empty(1 << 26, dtype=torch.uint8, device=dev)
+        ws = vc.new_workspace(1 << 26, dev)
 
         if packed:   # the same codes and parameters, one interleaved 5120-byte block per 32 tokens
             nb = cap // 32
@@ -774,7 +737,7 @@ def kernel_alone(args):
         tl = torch.full((B,), c.k, dtype=torch.int32, device=dev)
         ml = torch.full((B, Hkv), c.Lc, dtype=torch.int32, device=dev)
         out = torch.empty((B, Hq, D), dtype=torch.bfloat16, device=dev)
-        ws = torch.empty(1 << 26, dtype=torch.uint8, device=dev)
+        ws = vc.new_workspace(1 << 26, dev)
 
         def call(i):
             st = sets[i % len(sets)]
@@ -792,7 +755,7 @@ def kernel_alone(args):
         deg = S.torch_randint((B, 1, cap), 1, 5, 4, dev, torch.int32).float()
         ml = torch.full((B, Hkv), cap, dtype=torch.int32, device=dev)
         out = torch.empty((B, Hq, D), dtype=torch.bfloat16, device=dev)
-        ws = torch.empty(1 << 26, dtype=torch.uint8, device=dev)
+        ws = vc.new_workspace(1 << 26, dev)
 
         def call(i):
             vc.draft_attn(q, K, Vt, ml, degree=deg, out=out, workspace=ws, num_splits=args.splits)
@@ -998,6 +961,9 @@ def main():
                    "mfma_frac": r["verify_tflops"] / MFMA_BF16_PEAK_TFLOPS, "hbm_gbs": r["verify_gbs"],
                    "hbm_frac": r["verify_gbs"] / HBM_PEAK_GBS, "flops_per_launch": r["v_flops"]},
         "pcie_h2d_gbs": r["pcie_h2d_gbs"],
+        "pcie_ceiling_tokens_per_s": r["pcie_ceiling_tokens_per_s"],
+        "frac_of_pcie_ceiling": r["value"] / r["pcie_ceiling_tokens_per_s"],
+        "timed_calls": r["timed_calls"],
         "measured_peaks": dict(peaks, draft_frac_of_copy=r["draft_gbs"] / peaks["hbm_device_copy_gbs"],
                                verify_frac_of_gemm=r["verify_tflops"] / peaks["bf16_gemm_tflops"],
                                pcie_frac_of_pinned_copy=r["pcie_h2d_gbs"] / peaks["pcie_h2d_pinned_gbs"]),

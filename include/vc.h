@@ -304,7 +304,7 @@ vc_status vc_quantize_int4_packed(int32_t B, int32_t Hkv, int32_t D, const void 
  * D = 128; 2 <= chunk <= 128; 0 <= r <= 1; caps multiples of 32; K buffers
  * 16-byte aligned; in and out must not overlap.                              */
 vc_status vc_csm_round(int32_t B, int32_t Hkv, int32_t D, int32_t n_in, int32_t n_sink, int32_t n_recent,
-                       int32_t chunk, float r, const void *in_k, const void *in_v, const float *in_deg,
+                       int32_t chunk, double r, const void *in_k, const void *in_v, const float *in_deg,
                        int64_t cap_in, void *out_k, void *out_v, float *out_deg, int64_t cap_out, int32_t *n_out,
                        void *stream);
 
@@ -341,6 +341,98 @@ vc_status vc_stagger_after(vc_stagger *s, void *stream);   /* copy stream waits 
 vc_status vc_stagger_sync(vc_stagger *s);
 vc_status vc_stagger_copy_ms(vc_stagger *s, int32_t layer, float *ms);
 vc_status vc_stagger_destroy(vc_stagger *s);
+
+/* ------------------------------------------------------------------------ */
+/* One round of the staggered schedule ("Innovazioni Chiave del Sistema",
+ * P1: the runtime staggers requests so that while some draft from HBM the
+ * others verify against a full cache brought over PCIe; the two cohorts
+ * swap roles every round).  In one call the library enqueues, on the
+ * caller's two compute streams and the stagger object's copy streams:
+ *   drafting cohort (draft_stream): `steps` draft steps; step i runs the
+ *     draft attention of every layer (draft[l], with tail_len replaced by
+ *     step_tail_len[i] when given), then the LM head fused with the argmax
+ *     over draft_hidden[i], writing draft column i of drafts [Bd][steps];
+ *   verifying cohort (verify_stream): per layer l, the full cache is
+ *     streamed from host_kv[l] into the slot ring (K at the slot's start, V
+ *     at v_offset), verify[l] runs against it (its ctx_k/ctx_v are ignored),
+ *     and the slot is released for layer l + nslots; then the LM head fused
+ *     with the argmax and the acceptance over verify_hidden [Bv][M][Dm]
+ *     against verify_drafts [Bv][M-1] ("Algoritmo Principale", steps 2-3);
+ *     then per layer the commit of the verified rows: vc_commit_rows of
+ *     verify[l]'s block into commit[l] and the write-back of the block's K
+ *     and V rows to commit[l].host_k / host_v.
+ * mode VC_ROUND_STAGGERED spreads the draft steps over the verify layers
+ * (step i is enqueued after layer floor(i * layers / steps)) and the copies
+ * run while the drafting cohort computes; VC_ROUND_BULK is the
+ * bulk-synchronous comparison: every draft step first, and the copy and
+ * verify streams wait for them.  Both modes run the same kernels on the same
+ * inputs, so their outputs are identical bit for bit.
+ * Every argument of every call is validated before anything is enqueued; on
+ * VC_EINVAL nothing was enqueued (VC_EHIP: a launch failed part-way; the
+ * caller synchronizes and discards the round).  The call returns without
+ * synchronizing; vc_stagger_sync and the caller's streams tell completion.
+ * `before_verify` (optional) is called on the host just before layer l's
+ * verify is enqueued, with the verify stream (e.g. to insert markers or a
+ * bounded stall).  Workspaces: each cohort's draft[l].workspace,
+ * verify[l].workspace and LM-head workspaces as their entry points require;
+ * the draft calls of one round may share one workspace (they run in order
+ * on draft_stream), and so may the verify calls.                            */
+#define VC_ROUND_STAGGERED 0
+#define VC_ROUND_BULK 1
+
+typedef struct vc_round_commit {
+  void    *dst_k, *dst_v;         /* the layer's cache the rows go to (vc_commit_rows) */
+  int32_t *len;                   /* [Bv][Hkv], advanced by n_out                    */
+  float   *degree;                /* optional merge degrees (appended rows get 1)    */
+  int64_t  degree_h_stride;       /* 0 or cap                                        */
+  int64_t  cap;
+  int32_t  dst_v_blocked;         /* 1: a compressed main segment, 0: a full cache   */
+  void    *host_k, *host_v;       /* optional pinned destinations of the block rows  */
+} vc_round_commit;
+
+typedef void (*vc_round_hook)(void *ctx, int32_t layer, void *verify_stream);
+
+typedef struct vc_round_desc {
+  int32_t layers;                 /* 1 .. the stagger object's max_layers            */
+  int32_t steps;                  /* draft steps (0: no drafting cohort)             */
+  int32_t mode;                   /* VC_ROUND_STAGGERED or VC_ROUND_BULK             */
+  /* LM head of the model, vocab-major [V][Dm] bf16 */
+  const void *lm_w;
+  int32_t Dm, V;
+  /* drafting cohort */
+  const vc_draft_args *draft;     /* [layers]                                        */
+  const int32_t *const *step_tail_len; /* optional [steps] device [Bd]               */
+  const void *const *draft_hidden;     /* [steps] device [Bd][Dm] bf16               */
+  int32_t *drafts;                /* device [Bd][steps]                              */
+  void   *draft_lm_ws;            /* vc_lm_head_argmax_workspace_size(Bd, V)         */
+  size_t  draft_lm_ws_bytes;
+  /* verifying cohort (verify == NULL: none) */
+  const vc_verify_args *verify;   /* [layers]                                        */
+  const void *const *host_kv;     /* [layers] pinned host: the layer's full K then V */
+  size_t  kv_bytes;               /* bytes streamed per layer (<= slot bytes)        */
+  size_t  v_offset;               /* offset of V in the slot, multiple of 16         */
+  const void    *verify_hidden;   /* device [Bv][M][Dm] bf16                         */
+  const int32_t *verify_drafts;   /* device [Bv][M-1]                                */
+  int32_t *argmax, *accept_len, *out_tokens, *n_out;   /* as vc_lm_head_accept       */
+  void   *verify_lm_ws;           /* vc_lm_head_argmax_workspace_size(Bv * M, V)     */
+  size_t  verify_lm_ws_bytes;
+  const vc_round_commit *commit;  /* optional [layers]                               */
+  vc_round_hook before_verify;    /* optional                                        */
+  void   *hook_ctx;
+  int32_t time_kernels;           /* 1: time each draft step's run of draft
+                                     attention calls and every verify call with
+                                     events on their streams (vc_stagger_round_times) */
+} vc_round_desc;
+
+vc_status vc_stagger_round(vc_stagger *s, const vc_round_desc *d, void *draft_stream, void *verify_stream);
+
+/* Durations (ms) of the last timed round, valid once its streams have
+ * completed: draft_ms[i] spans draft step i's `layers` back-to-back draft
+ * attention calls (the LM head excluded), verify_ms[l] layer l's verify
+ * call.  *n_draft and *n_verify are set to the counts; the arrays (host, may
+ * be NULL to query the counts) must hold at least that many entries.        */
+vc_status vc_stagger_round_times(vc_stagger *s, float *draft_ms, int32_t *n_draft, float *verify_ms,
+                                 int32_t *n_verify);
 
 /* ------------------------------------------------------------------------ */
 const char *vc_status_string(vc_status s);

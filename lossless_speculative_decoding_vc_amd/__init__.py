@@ -16,7 +16,8 @@ import torch
 __all__ = [
     "VcError", "lib", "library_path", "draft_attn", "verify_attn", "accept",
     "draft_workspace_size", "verify_workspace_size", "declared_symbols",
-    "argmax", "lm_head", "commit_rows", "quantize_int4", "csm_round", "Stagger",
+    "argmax", "lm_head", "commit_rows", "quantize_int4", "csm_round", "Stagger", "new_workspace",
+    "draft_args", "verify_args", "ROUND_STAGGERED", "ROUND_BULK",
     "VC_BF16", "VC_FP32", "VC_KV_DENSE", "VC_KV_INT4", "VC_KV_INT4_PACKED",
 ]
 
@@ -70,6 +71,30 @@ class AcceptArgs(ctypes.Structure):
                 ("out_tokens", _p), ("n_out", _p)]
 
 
+class RoundCommit(ctypes.Structure):
+    _fields_ = [("dst_k", _p), ("dst_v", _p), ("len", _p), ("degree", _p), ("degree_h_stride", _i64),
+                ("cap", _i64), ("dst_v_blocked", _i32), ("host_k", _p), ("host_v", _p)]
+
+
+ROUND_HOOK = ctypes.CFUNCTYPE(None, _p, _i32, _p)
+
+
+class RoundDesc(ctypes.Structure):
+    _fields_ = [("layers", _i32), ("steps", _i32), ("mode", _i32),
+                ("lm_w", _p), ("Dm", _i32), ("V", _i32),
+                ("draft", ctypes.POINTER(DraftArgs)), ("step_tail_len", ctypes.POINTER(_p)),
+                ("draft_hidden", ctypes.POINTER(_p)), ("drafts", _p), ("draft_lm_ws", _p),
+                ("draft_lm_ws_bytes", ctypes.c_size_t),
+                ("verify", ctypes.POINTER(VerifyArgs)), ("host_kv", ctypes.POINTER(_p)),
+                ("kv_bytes", ctypes.c_size_t), ("v_offset", ctypes.c_size_t),
+                ("verify_hidden", _p), ("verify_drafts", _p), ("argmax", _p), ("accept_len", _p),
+                ("out_tokens", _p), ("n_out", _p), ("verify_lm_ws", _p), ("verify_lm_ws_bytes", ctypes.c_size_t),
+                ("commit", ctypes.POINTER(RoundCommit)), ("before_verify", ROUND_HOOK), ("hook_ctx", _p),
+                ("time_kernels", _i32)]
+
+
+ROUND_STAGGERED, ROUND_BULK = 0, 1
+
 _lib = None
 
 
@@ -109,7 +134,7 @@ def lib():
         L.vc_compact_kv.restype = ctypes.c_int
         L.vc_quantize_int4_packed.argtypes = [_i32, _i32, _i32, _p, _p, _i64, _p, _i32, _i64, _p, _p, _p]
         L.vc_quantize_int4_packed.restype = ctypes.c_int
-        L.vc_csm_round.argtypes = [_i32, _i32, _i32, _i32, _i32, _i32, _i32, ctypes.c_float, _p, _p, _p, _i64,
+        L.vc_csm_round.argtypes = [_i32, _i32, _i32, _i32, _i32, _i32, _i32, ctypes.c_double, _p, _p, _p, _i64,
                                    _p, _p, _p, _i64, ctypes.POINTER(_i32), _p]
         L.vc_csm_round.restype = ctypes.c_int
         L.vc_stagger_create.argtypes = [ctypes.POINTER(_p), ctypes.POINTER(_p), _i32, ctypes.c_size_t, _i32]
@@ -121,9 +146,11 @@ def lib():
         L.vc_stagger_sync.argtypes = [_p]
         L.vc_stagger_copy_ms.argtypes = [_p, _i32, ctypes.POINTER(ctypes.c_float)]
         L.vc_stagger_destroy.argtypes = [_p]
+        L.vc_stagger_round.argtypes = [_p, ctypes.POINTER(RoundDesc), _p, _p]
+        L.vc_stagger_round_times.argtypes = [_p, _p, ctypes.POINTER(_i32), _p, ctypes.POINTER(_i32)]
         for n in ("vc_stagger_create", "vc_stagger_stream_layer", "vc_stagger_acquire", "vc_stagger_release",
                   "vc_stagger_writeback", "vc_stagger_after", "vc_stagger_sync", "vc_stagger_copy_ms",
-                  "vc_stagger_destroy"):
+                  "vc_stagger_destroy", "vc_stagger_round", "vc_stagger_round_times"):
             getattr(L, n).restype = ctypes.c_int
         L.vc_last_error.restype = ctypes.c_char_p
         L.vc_status_string.restype = ctypes.c_char_p
@@ -178,6 +205,34 @@ def _dev(t, name, dtype=None):
         raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
 
 
+def _want(t, name, shape, dtypes):
+    """Shape and dtype of a tensor against the layout the C ABI reads: the
+    kernels see raw pointers, so a short or mistyped buffer must be refused
+    here, before anything is enqueued."""
+    if t is None:
+        return
+    if tuple(t.shape) != tuple(int(x) for x in shape):
+        raise ValueError(f"{name} must be {list(int(x) for x in shape)}, got {list(t.shape)}")
+    if dtypes is not None and t.dtype not in dtypes:
+        raise ValueError(f"{name} must be {' or '.join(str(d) for d in dtypes)}, got {t.dtype}")
+
+
+_HALF = None   # binary16 carriers (float16 or int16), filled on first use
+
+
+def _half():
+    global _HALF
+    if _HALF is None:
+        _HALF = (torch.float16, torch.int16)
+    return _HALF
+
+
+def new_workspace(nbytes, device):
+    """A workspace for the split / tiled entry points (uint8, at least
+    ``nbytes`` bytes; its contents need no initialisation)."""
+    return torch.empty(max(int(nbytes), 16), dtype=torch.uint8, device=device)
+
+
 def _vc_dtype(t):
     if t.dtype == torch.bfloat16:
         return VC_BF16
@@ -218,30 +273,109 @@ def draft_attn(q, k, v, main_len, degree=None, tail_k=None, tail_v=None, tail_le
     ``tail_k [B][Hkv][tcap][D]``, ``tail_v [B][Hkv][D][tcap]``, ``tail_len``
     int32 ``[B]``.  Returns ``out [B][Hq][D]`` (and fills ``out_lse``).
     """
+    if out is None:
+        out = torch.empty_like(q)
+    a = draft_args(q, k, v, main_len, degree, tail_k, tail_v, tail_len, out, out_lse, scale, num_splits,
+                   workspace, fmt, k_scale, k_zero, v_scale, v_zero)
+    _check(lib().vc_draft_attn(ctypes.byref(a), _stream(stream)))
+    return out
+
+
+def draft_args(q, k, v, main_len, degree=None, tail_k=None, tail_v=None, tail_len=None, out=None, out_lse=None,
+               scale=None, num_splits=0, workspace=None, fmt=VC_KV_DENSE, k_scale=None, k_zero=None, v_scale=None,
+               v_zero=None):
+    """The checked ``vc_draft_args`` of one draft call (the arguments of
+    :func:`draft_attn`; ``out`` is required), with a workspace attached when
+    the call is split (a new zeroed one unless ``workspace`` is big enough).
+    The struct holds raw pointers: keep the tensors alive while it is used."""
+    if out is None:
+        raise ValueError("out is required")
+    _check_draft_shapes(q, k, v, main_len, degree, tail_k, tail_v, tail_len, out, out_lse, fmt,
+                        k_scale, k_zero, v_scale, v_zero)
     for t, n in ((q, "q"), (k, "k"), (v, "v"), (tail_k, "tail_k"), (tail_v, "tail_v"),
                  (out, "out"), (degree, "degree"), (out_lse, "out_lse"), (k_scale, "k_scale"),
                  (k_zero, "k_zero"), (v_scale, "v_scale"), (v_zero, "v_zero")):
         _dev(t, n)
     _dev(main_len, "main_len", torch.int32)
     _dev(tail_len, "tail_len", torch.int32)
-    B, Hq, D = q.shape
     Hkv = k.shape[1]
-    cap = k.shape[2]
-    if fmt == VC_KV_INT4_PACKED:   # k is [B][Hkv][cap/32][5120] uint8
-        if k.dim() != 4 or k.shape[3] != INT4_PACKED_BLOCK:
-            raise ValueError("a packed int4 cache is [B][Hkv][cap/32][5120] uint8")
-        cap = k.shape[2] * 32
-    if out is None:
-        out = torch.empty_like(q)
+    cap = k.shape[2] * 32 if fmt == VC_KV_INT4_PACKED else k.shape[2]
     a = _draft_struct(q, k, v, main_len, degree, tail_k, tail_v, tail_len, out, out_lse,
                       scale, num_splits, fmt, k_scale, k_zero, v_scale, v_zero, Hkv, cap)
     need = lib().vc_draft_workspace_size(ctypes.byref(a))
     if need:
         if workspace is None or workspace.numel() * workspace.element_size() < need:
-            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+            workspace = new_workspace(need, q.device)
         a.workspace, a.workspace_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
-    _check(lib().vc_draft_attn(ctypes.byref(a), _stream(stream)))
-    return out
+    a._keep = workspace
+    return a
+
+
+def _check_draft_shapes(q, k, v, main_len, degree, tail_k, tail_v, tail_len, out, out_lse, fmt,
+                        k_scale, k_zero, v_scale, v_zero):
+    """Every tensor of a draft call against the layouts of ``vc_draft_args``."""
+    if q.dim() != 3:
+        raise ValueError(f"q must be [B][Hq][D], got {list(q.shape)}")
+    B, Hq, D = q.shape
+    act = (torch.bfloat16, torch.float32)
+    _want(q, "q", (B, Hq, D), act)
+    if k.dim() < 2 or k.shape[0] != B:
+        raise ValueError(f"k must start with [B={B}][Hkv], got {list(k.shape)}")
+    Hkv = k.shape[1]
+    if Hkv < 1 or Hq % Hkv:
+        raise ValueError(f"Hq ({Hq}) must be a multiple of the KV heads of k ({Hkv})")
+    u8 = (torch.uint8,)
+    if fmt == VC_KV_INT4_PACKED:
+        if k.dim() != 4:
+            raise ValueError("a packed int4 cache is [B][Hkv][cap/32][5120] uint8")
+        cap = k.shape[2] * 32
+        _want(k, "k", (B, Hkv, cap // 32, INT4_PACKED_BLOCK), u8)
+        if any(t is not None for t in (v, k_scale, k_zero, v_scale, v_zero)):
+            raise ValueError("a packed int4 cache lives in k alone: v and the scales/zeros must be None")
+    elif fmt == VC_KV_INT4:
+        if k.dim() != 4:
+            raise ValueError("int4 k codes are [B][Hkv][cap][D/2] uint8")
+        cap = k.shape[2]
+        _want(k, "k", (B, Hkv, cap, D // 2), u8)
+        _want(v, "v", (B, Hkv, cap // 32, D, 16), u8)
+        for t, n in ((k_scale, "k_scale"), (k_zero, "k_zero")):
+            if t is None:
+                raise ValueError(f"{n} is required for an int4 cache")
+            _want(t, n, (B, Hkv, cap // 32, D), _half())
+        for t, n in ((v_scale, "v_scale"), (v_zero, "v_zero")):
+            if t is None:
+                raise ValueError(f"{n} is required for an int4 cache")
+            _want(t, n, (B, Hkv, cap // 32, D // 32, 32), _half())
+    elif fmt == VC_KV_DENSE:
+        if k.dim() != 4:
+            raise ValueError("k must be [B][Hkv][cap][D]")
+        cap = k.shape[2]
+        _want(k, "k", (B, Hkv, cap, D), (q.dtype,))
+        if v is None:
+            raise ValueError("v is required for a dense cache")
+        _want(v, "v", (B, Hkv, cap // 32, D, 32), (q.dtype,))
+        if any(t is not None for t in (k_scale, k_zero, v_scale, v_zero)):
+            raise ValueError("scales/zeros belong to an int4 cache only")
+    else:
+        raise ValueError(f"unknown kv format {fmt}")
+    if main_len is None:
+        raise ValueError("main_len is required")
+    _want(main_len, "main_len", (B, Hkv), (torch.int32,))
+    if degree is not None:
+        if degree.dim() != 3 or degree.shape[1] not in (1, Hkv):
+            raise ValueError(f"degree must be [B][1 or Hkv][cap], got {list(degree.shape)}")
+        _want(degree, "degree", (B, degree.shape[1], cap), (torch.float32,))
+    if (tail_k is None) != (tail_v is None) or (tail_len is not None and tail_k is None):
+        raise ValueError("tail_k, tail_v (and tail_len) go together")
+    if tail_k is not None:
+        if tail_k.dim() != 4:
+            raise ValueError("tail_k must be [B][Hkv][tcap][D]")
+        tcap = tail_k.shape[2]
+        _want(tail_k, "tail_k", (B, Hkv, tcap, D), (q.dtype,))
+        _want(tail_v, "tail_v", (B, Hkv, D, tcap), (q.dtype,))
+        _want(tail_len, "tail_len", (B,), (torch.int32,))
+    _want(out, "out", (B, Hq, D), (q.dtype,))
+    _want(out_lse, "out_lse", (B, Hq), (torch.float32,))
 
 
 def draft_workspace_size(**kw):
@@ -259,29 +393,75 @@ def verify_attn(q, ctx_k, ctx_v, ctx_len, blk_k, blk_v, out=None, out_lse=None, 
     ``ctx_len`` int32 ``[B]``; ``blk_k [B][Hkv][M][D]``, ``blk_v [B][Hkv][D][M]``.
     Returns ``out [B][M][Hq][D]``.
     """
+    if out is None:
+        out = torch.empty_like(q)
+    a = verify_args(q, ctx_k, ctx_v, ctx_len, blk_k, blk_v, out, out_lse, scale, num_splits, workspace)
+    _check(lib().vc_verify_attn(ctypes.byref(a), _stream(stream)))
+    return out
+
+
+def verify_args(q, ctx_k, ctx_v, ctx_len, blk_k, blk_v, out, out_lse=None, scale=None, num_splits=0,
+                workspace=None, ccap=None):
+    """The checked ``vc_verify_args`` of one verify call (the arguments of
+    :func:`verify_attn`; ``out`` is required).  With ``ctx_k = ctx_v = None``
+    and ``ccap`` given, the context comes from elsewhere (the staging slot of
+    :meth:`Stagger.round`).  The struct holds raw pointers: keep the tensors
+    alive while it is used."""
+    if out is None:
+        raise ValueError("out is required")
+    _check_verify_shapes(q, ctx_k, ctx_v, ctx_len, blk_k, blk_v, out, out_lse)
     for t, n in ((q, "q"), (ctx_k, "ctx_k"), (ctx_v, "ctx_v"), (blk_k, "blk_k"),
                  (blk_v, "blk_v"), (out, "out"), (out_lse, "out_lse")):
         _dev(t, n)
     _dev(ctx_len, "ctx_len", torch.int32)
     B, M, Hq, D = q.shape
     Hkv = blk_k.shape[1]
-    if out is None:
-        out = torch.empty_like(q)
     a = VerifyArgs()
     a.B, a.Hq, a.Hkv, a.D, a.M = B, Hq, Hkv, D, M
     a.dtype = _vc_dtype(q)
     a.scale = D ** -0.5 if scale is None else scale
     a.num_splits = num_splits
-    a.ccap = 0 if ctx_k is None else ctx_k.shape[2]
+    if ctx_k is not None:
+        a.ccap = ctx_k.shape[2]
+    else:
+        a.ccap = 0 if ccap is None else int(ccap)
     a.q, a.ctx_k, a.ctx_v, a.ctx_len = _ptr(q), _ptr(ctx_k), _ptr(ctx_v), _ptr(ctx_len)
     a.blk_k, a.blk_v, a.out, a.out_lse = _ptr(blk_k), _ptr(blk_v), _ptr(out), _ptr(out_lse)
     need = lib().vc_verify_workspace_size(ctypes.byref(a))
     if need:
         if workspace is None or workspace.numel() * workspace.element_size() < need:
-            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+            workspace = new_workspace(need, q.device)
         a.workspace, a.workspace_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
-    _check(lib().vc_verify_attn(ctypes.byref(a), _stream(stream)))
-    return out
+    a._keep = workspace
+    return a
+
+
+def _check_verify_shapes(q, ctx_k, ctx_v, ctx_len, blk_k, blk_v, out, out_lse):
+    """Every tensor of a verify call against the layouts of ``vc_verify_args``."""
+    if q.dim() != 4:
+        raise ValueError(f"q must be [B][M][Hq][D], got {list(q.shape)}")
+    B, M, Hq, D = q.shape
+    _want(q, "q", (B, M, Hq, D), (torch.bfloat16, torch.float32))
+    if blk_k is None or blk_v is None or ctx_len is None:
+        raise ValueError("blk_k, blk_v and ctx_len are required")
+    if blk_k.dim() != 4:
+        raise ValueError("blk_k must be [B][Hkv][M][D]")
+    Hkv = blk_k.shape[1]
+    if Hkv < 1 or Hq % Hkv:
+        raise ValueError(f"Hq ({Hq}) must be a multiple of the KV heads of blk_k ({Hkv})")
+    _want(blk_k, "blk_k", (B, Hkv, M, D), (q.dtype,))
+    _want(blk_v, "blk_v", (B, Hkv, D, M), (q.dtype,))
+    _want(ctx_len, "ctx_len", (B,), (torch.int32,))
+    if (ctx_k is None) != (ctx_v is None):
+        raise ValueError("ctx_k and ctx_v go together")
+    if ctx_k is not None:
+        if ctx_k.dim() != 4:
+            raise ValueError("ctx_k must be [B][Hkv][ccap][D]")
+        ccap = ctx_k.shape[2]
+        _want(ctx_k, "ctx_k", (B, Hkv, ccap, D), (q.dtype,))
+        _want(ctx_v, "ctx_v", (B, Hkv, D, ccap), (q.dtype,))
+    _want(out, "out", (B, M, Hq, D), (q.dtype,))
+    _want(out_lse, "out_lse", (B, M, Hq), (torch.float32,))
 
 
 def verify_workspace_size(**kw):
@@ -350,8 +530,7 @@ def lm_head(h, w, logits=None, stream=None):
 
 def lm_head_argmax_workspace(R, V, device):
     """Workspace tensor (uint8) for :func:`lm_head_argmax` over R rows."""
-    n = lib().vc_lm_head_argmax_workspace_size(R, V)
-    return torch.empty(max(n, 16), dtype=torch.uint8, device=device)
+    return new_workspace(lib().vc_lm_head_argmax_workspace_size(R, V), device)
 
 
 def lm_head_argmax(h, w, out=None, out_stride=1, workspace=None, stream=None):
@@ -417,12 +596,30 @@ def commit_rows(blk_k, blk_v, n_out, dst_k, dst_v, length, degree=None, v_blocke
     ``[B][Hkv][cap/32][D][32]`` (a compressed main segment), ``length`` int32
     ``[B][Hkv]`` (updated in place).
     """
+    if blk_k.dim() != 4 or dst_k.dim() != 4:
+        raise ValueError("blk_k must be [B][Hkv][M][D] and dst_k [B][Hkv][cap][D]")
+    B, Hkv, M, D = blk_k.shape
+    cap = dst_k.shape[2]
+    act = (torch.bfloat16, torch.float32)
+    _want(blk_k, "blk_k", (B, Hkv, M, D), act)
+    _want(blk_v, "blk_v", (B, Hkv, D, M), (blk_k.dtype,))
+    _want(dst_k, "dst_k", (B, Hkv, cap, D), (blk_k.dtype,))
+    if v_blocked:
+        if cap % 32:
+            raise ValueError("a blocked V cache needs cap % 32 == 0")
+        _want(dst_v, "dst_v", (B, Hkv, cap // 32, D, 32), (blk_k.dtype,))
+    else:
+        _want(dst_v, "dst_v", (B, Hkv, D, cap), (blk_k.dtype,))
+    _want(n_out, "n_out", (B,), (torch.int32,))
+    _want(length, "length", (B, Hkv), (torch.int32,))
+    if degree is not None:
+        if degree.dim() != 3 or degree.shape[1] not in (1, Hkv):
+            raise ValueError(f"degree must be [B][1 or Hkv][cap], got {list(degree.shape)}")
+        _want(degree, "degree", (B, degree.shape[1], cap), (torch.float32,))
     for t, n in ((blk_k, "blk_k"), (blk_v, "blk_v"), (dst_k, "dst_k"), (dst_v, "dst_v"), (degree, "degree")):
         _dev(t, n)
     _dev(n_out, "n_out", torch.int32)
     _dev(length, "length", torch.int32)
-    B, Hkv, M, D = blk_k.shape
-    cap = dst_k.shape[2]
     hstride = 0 if degree is None or degree.shape[1] == 1 else cap
     _check(lib().vc_commit_rows(B, Hkv, D, M, _vc_dtype(blk_k), cap, 1 if v_blocked else 0, _ptr(blk_k), _ptr(blk_v), _ptr(n_out),
                                 _ptr(dst_k), _ptr(dst_v), _ptr(length), _ptr(degree), hstride, _stream(stream)))
@@ -549,6 +746,147 @@ class Stagger:
 
     def sync(self):
         _check(lib().vc_stagger_sync(self.h))
+
+    def round(self, layers, mode, lm_w, draft=None, step_tail_len=None, draft_hidden=None, drafts=None,
+              draft_lm_ws=None, verify=None, host_kv=None, kv_bytes=0, v_offset=0, verify_hidden=None,
+              verify_drafts=None, argmax=None, accept_len=None, out_tokens=None, n_out=None, verify_lm_ws=None,
+              commit=None, before_verify=None, time_kernels=False, draft_stream=None, verify_stream=None):
+        """One round of the staggered schedule (``vc_stagger_round``), enqueued
+        natively on ``draft_stream`` / ``verify_stream`` and the copy streams.
+
+        ``draft``: list over layers of :func:`draft_args` structs (the drafting
+        cohort; None for none), ``step_tail_len``: list over the draft steps of
+        int32 ``[Bd]`` tail lengths, ``draft_hidden``: list over the steps of
+        bf16 ``[Bd][Dm]`` rows, ``drafts`` int32 ``[Bd][steps]``.  ``verify``:
+        list over layers of :func:`verify_args` structs built with ``ccap``
+        (the context comes from the slot), ``host_kv``: list of pinned uint8
+        tensors (the layer's full K then V; V at ``v_offset``),
+        ``verify_hidden`` bf16 ``[Bv][M][Dm]``, ``verify_drafts`` int32
+        ``[Bv][M-1]`` and the acceptance outputs of :func:`lm_head_accept`.
+        ``commit``: list over layers of dicts (``dst_k, dst_v, length, degree,
+        v_blocked, host_k, host_v``).  ``before_verify(layer, stream_ptr)`` is
+        called on the host before each verify is enqueued.  ``time_kernels``
+        times each draft step's run of draft attention calls and every verify
+        call (:meth:`round_times`).  ``lm_w`` is the
+        vocab-major ``[V][Dm]`` LM head.  Returns without synchronizing."""
+        d = RoundDesc()
+        keep = []
+        d.layers, d.mode, d.time_kernels = int(layers), int(mode), 1 if time_kernels else 0
+        _dev(lm_w, "lm_w", torch.bfloat16)
+        d.lm_w, d.V, d.Dm = _ptr(lm_w), lm_w.shape[0], lm_w.shape[1]
+        steps = 0
+        if draft is not None:
+            if len(draft) != layers or draft_hidden is None or drafts is None:
+                raise ValueError("draft needs one struct per layer, draft_hidden and drafts")
+            steps = len(draft_hidden)
+            arr = (DraftArgs * layers)(*draft)
+            keep.append(arr)
+            d.draft = ctypes.cast(arr, ctypes.POINTER(DraftArgs))
+            Bd = draft[0].B
+            _dev(drafts, "drafts", torch.int32)
+            _want(drafts, "drafts", (Bd, steps), (torch.int32,))
+            for i, h in enumerate(draft_hidden):
+                _dev(h, f"draft_hidden[{i}]", torch.bfloat16)
+                _want(h, f"draft_hidden[{i}]", (Bd, d.Dm), (torch.bfloat16,))
+            hid = (_p * steps)(*[h.data_ptr() for h in draft_hidden])
+            keep.append(hid)
+            d.draft_hidden = ctypes.cast(hid, ctypes.POINTER(_p))
+            if step_tail_len is not None:
+                if len(step_tail_len) != steps:
+                    raise ValueError("step_tail_len needs one tensor per draft step")
+                for i, t in enumerate(step_tail_len):
+                    _dev(t, f"step_tail_len[{i}]", torch.int32)
+                    _want(t, f"step_tail_len[{i}]", (Bd,), (torch.int32,))
+                tl = (_p * steps)(*[t.data_ptr() for t in step_tail_len])
+                keep.append(tl)
+                d.step_tail_len = ctypes.cast(tl, ctypes.POINTER(_p))
+            d.drafts = _ptr(drafts)
+            if draft_lm_ws is None:
+                draft_lm_ws = lm_head_argmax_workspace(Bd, d.V, drafts.device)
+            keep.append(draft_lm_ws)
+            d.draft_lm_ws, d.draft_lm_ws_bytes = _ptr(draft_lm_ws), draft_lm_ws.numel()
+        d.steps = steps
+        if verify is not None:
+            if len(verify) != layers or host_kv is None or len(host_kv) != layers:
+                raise ValueError("verify and host_kv need one entry per layer")
+            arr = (VerifyArgs * layers)(*verify)
+            keep.append(arr)
+            d.verify = ctypes.cast(arr, ctypes.POINTER(VerifyArgs))
+            for i, t in enumerate(host_kv):
+                if t.is_cuda or not t.is_pinned():
+                    raise ValueError(f"host_kv[{i}] must be pinned host memory")
+                if t.numel() * t.element_size() < kv_bytes:
+                    raise ValueError(f"host_kv[{i}] holds fewer than kv_bytes bytes")
+            hk = (_p * layers)(*[t.data_ptr() for t in host_kv])
+            keep.append(hk)
+            d.host_kv = ctypes.cast(hk, ctypes.POINTER(_p))
+            d.kv_bytes, d.v_offset = int(kv_bytes), int(v_offset)
+            Bv, M = verify[0].B, verify[0].M
+            _dev(verify_hidden, "verify_hidden", torch.bfloat16)
+            _want(verify_hidden, "verify_hidden", (Bv, M, d.Dm), (torch.bfloat16,))
+            _dev(verify_drafts, "verify_drafts", torch.int32)
+            _want(verify_drafts, "verify_drafts", (Bv, M - 1), (torch.int32,))
+            for t, n, shape in ((argmax, "argmax", (Bv, M)), (accept_len, "accept_len", (Bv,)),
+                                (out_tokens, "out_tokens", (Bv, M)), (n_out, "n_out", (Bv,))):
+                if t is None:
+                    raise ValueError(f"{n} is required")
+                _dev(t, n, torch.int32)
+                _want(t, n, shape, (torch.int32,))
+            d.verify_hidden, d.verify_drafts = _ptr(verify_hidden), _ptr(verify_drafts)
+            d.argmax, d.accept_len, d.out_tokens, d.n_out = map(_ptr, (argmax, accept_len, out_tokens, n_out))
+            if verify_lm_ws is None:
+                verify_lm_ws = lm_head_argmax_workspace(Bv * M, d.V, verify_hidden.device)
+            keep.append(verify_lm_ws)
+            d.verify_lm_ws, d.verify_lm_ws_bytes = _ptr(verify_lm_ws), verify_lm_ws.numel()
+            if commit is not None:
+                if len(commit) != layers:
+                    raise ValueError("commit needs one entry per layer")
+                cs = (RoundCommit * layers)()
+                for l, c in enumerate(commit):
+                    dk, dv, ln, deg = c["dst_k"], c["dst_v"], c["length"], c.get("degree")
+                    blocked = bool(c.get("v_blocked", False))
+                    vb = verify[l]
+                    Bc, Hkv, D = vb.B, vb.Hkv, vb.D
+                    cap = dk.shape[2]
+                    want_dt = torch.bfloat16 if vb.dtype == VC_BF16 else torch.float32
+                    _want(dk, f"commit[{l}].dst_k", (Bc, Hkv, cap, D), (want_dt,))
+                    _want(dv, f"commit[{l}].dst_v", (Bc, Hkv, cap // 32, D, 32) if blocked else (Bc, Hkv, D, cap),
+                          (want_dt,))
+                    _want(ln, f"commit[{l}].length", (Bc, Hkv), (torch.int32,))
+                    if deg is not None:
+                        if deg.dim() != 3 or deg.shape[1] not in (1, Hkv):
+                            raise ValueError(f"commit[{l}].degree must be [B][1 or Hkv][cap]")
+                        _want(deg, f"commit[{l}].degree", (Bc, deg.shape[1], cap), (torch.float32,))
+                    for t, n in ((dk, "dst_k"), (dv, "dst_v"), (ln, "length"), (deg, "degree")):
+                        _dev(t, f"commit[{l}].{n}")
+                    blk_bytes = Bc * Hkv * vb.M * D * (2 if vb.dtype == VC_BF16 else 4)
+                    for n in ("host_k", "host_v"):
+                        t = c.get(n)
+                        if t is not None and (t.is_cuda or not t.is_pinned()
+                                              or t.numel() * t.element_size() < blk_bytes):
+                            raise ValueError(f"commit[{l}].{n} must be pinned host memory of >= {blk_bytes} bytes")
+                    cs[l].dst_k, cs[l].dst_v, cs[l].len = _ptr(dk), _ptr(dv), _ptr(ln)
+                    cs[l].degree = _ptr(deg)
+                    cs[l].degree_h_stride = 0 if deg is None or deg.shape[1] == 1 else cap
+                    cs[l].cap, cs[l].dst_v_blocked = cap, 1 if blocked else 0
+                    cs[l].host_k, cs[l].host_v = _ptr(c.get("host_k")), _ptr(c.get("host_v"))
+                keep.append(cs)
+                d.commit = ctypes.cast(cs, ctypes.POINTER(RoundCommit))
+        if before_verify is not None:
+            hook = ROUND_HOOK(lambda ctx, layer, stream: before_verify(int(layer), stream))
+            keep.append(hook)
+            d.before_verify = hook
+        _check(lib().vc_stagger_round(self.h, ctypes.byref(d), _stream(draft_stream), _stream(verify_stream)))
+        return keep
+
+    def round_times(self):
+        """(draft_ms per step, verify_ms per layer) of the last timed round, once it completed."""
+        nd, nv = _i32(), _i32()
+        _check(lib().vc_stagger_round_times(self.h, None, ctypes.byref(nd), None, ctypes.byref(nv)))
+        dm = (ctypes.c_float * max(nd.value, 1))()
+        vm = (ctypes.c_float * max(nv.value, 1))()
+        _check(lib().vc_stagger_round_times(self.h, dm, ctypes.byref(nd), vm, ctypes.byref(nv)))
+        return list(dm)[:nd.value], list(vm)[:nv.value]
 
     def copy_ms(self, layer):
         ms = ctypes.c_float()

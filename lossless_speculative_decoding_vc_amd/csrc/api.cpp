@@ -126,6 +126,30 @@ vc_status check_verify(const vc_verify_args *a) {
 namespace vc {
 int lm_head(int R, int Dm, int V, const void *h, const void *w, float *logits, hipStream_t s, const char **err);
 vc_status set_error(vc_status s, const char *msg) { return fail(s, "%s", msg); }
+
+vc_status validate_draft_call(const vc_draft_args *a) {
+  vc_status st = check_draft(a);
+  if (st != VC_OK || a->B == 0) return st;
+  const SplitPlan pl = plan_draft(*a);
+  if (pl.ws_bytes) {
+    if (!a->workspace || a->workspace_bytes < pl.ws_bytes)
+      return fail(VC_EINVAL, "workspace of %zu bytes required (got %zu)", pl.ws_bytes, a->workspace_bytes);
+    if (!aligned16(a->workspace)) return fail(VC_EINVAL, "workspace must be 16-byte aligned");
+  }
+  return VC_OK;
+}
+
+vc_status validate_verify_call(const vc_verify_args *a) {
+  vc_status st = check_verify(a);
+  if (st != VC_OK || a->B == 0) return st;
+  const SplitPlan pl = plan_verify(*a);
+  if (pl.ws_bytes) {
+    if (!a->workspace || a->workspace_bytes < pl.ws_bytes)
+      return fail(VC_EINVAL, "workspace of %zu bytes required (got %zu)", pl.ws_bytes, a->workspace_bytes);
+    if (!aligned16(a->workspace)) return fail(VC_EINVAL, "workspace must be 16-byte aligned");
+  }
+  return VC_OK;
+}
 }  // namespace vc
 
 extern "C" {
@@ -157,29 +181,15 @@ size_t vc_verify_workspace_size(const vc_verify_args *a) {
 }
 
 vc_status vc_draft_attn(const vc_draft_args *a, void *stream) {
-  vc_status st = check_draft(a);
-  if (st != VC_OK) return st;
-  if (a->B == 0) return VC_OK;
-  const vc::SplitPlan pl = vc::plan_draft(*a);
-  if (pl.ws_bytes) {
-    if (!a->workspace || a->workspace_bytes < pl.ws_bytes)
-      return fail(VC_EINVAL, "workspace of %zu bytes required (got %zu)", pl.ws_bytes, a->workspace_bytes);
-    if (!aligned16(a->workspace)) return fail(VC_EINVAL, "workspace must be 16-byte aligned");
-  }
-  return hip_status(vc::launch_draft(*a, pl, (hipStream_t)stream), "vc_draft_attn launch");
+  vc_status st = vc::validate_draft_call(a);
+  if (st != VC_OK || a->B == 0) return st;
+  return hip_status(vc::launch_draft(*a, vc::plan_draft(*a), (hipStream_t)stream), "vc_draft_attn launch");
 }
 
 vc_status vc_verify_attn(const vc_verify_args *a, void *stream) {
-  vc_status st = check_verify(a);
-  if (st != VC_OK) return st;
-  if (a->B == 0) return VC_OK;
-  const vc::SplitPlan pl = vc::plan_verify(*a);
-  if (pl.ws_bytes) {
-    if (!a->workspace || a->workspace_bytes < pl.ws_bytes)
-      return fail(VC_EINVAL, "workspace of %zu bytes required (got %zu)", pl.ws_bytes, a->workspace_bytes);
-    if (!aligned16(a->workspace)) return fail(VC_EINVAL, "workspace must be 16-byte aligned");
-  }
-  return hip_status(vc::launch_verify(*a, pl, (hipStream_t)stream), "vc_verify_attn launch");
+  vc_status st = vc::validate_verify_call(a);
+  if (st != VC_OK || a->B == 0) return st;
+  return hip_status(vc::launch_verify(*a, vc::plan_verify(*a), (hipStream_t)stream), "vc_verify_attn launch");
 }
 
 vc_status vc_accept(const vc_accept_args *a, void *stream) {
@@ -219,7 +229,9 @@ size_t vc_lm_head_argmax_workspace_size(int32_t R, int32_t V) {
   return vc::lm_argmax_workspace(R, V);
 }
 
-namespace {
+}  // extern "C"
+
+namespace vc {
 vc_status check_lm_argmax(int32_t R, int32_t Dm, int32_t V, const void *h, const void *w, const void *out,
                           void *ws, size_t ws_bytes) {
   REQ(R >= 0 && V >= 1 && Dm >= 32, "R >= 0, V >= 1 and Dm >= 32 required");
@@ -232,12 +244,14 @@ vc_status check_lm_argmax(int32_t R, int32_t Dm, int32_t V, const void *h, const
       vc::lm_argmax_workspace(R, V));
   return VC_OK;
 }
-}  // namespace
+}  // namespace vc
+
+extern "C" {
 
 vc_status vc_lm_head_argmax(int32_t R, int32_t Dm, int32_t V, const void *h, const void *w, int32_t *out,
                             int32_t out_stride, void *workspace, size_t workspace_bytes, void *stream) {
   REQ(out_stride >= 1, "out_stride must be >= 1");
-  vc_status st = check_lm_argmax(R, Dm, V, h, w, out, workspace, workspace_bytes);
+  vc_status st = vc::check_lm_argmax(R, Dm, V, h, w, out, workspace, workspace_bytes);
   if (st != VC_OK || R == 0) return st;
   return hip_status(vc::launch_lm_argmax(R, Dm, V, h, w, out, out_stride, workspace, (hipStream_t)stream),
                     "vc_lm_head_argmax launch");
@@ -248,7 +262,7 @@ vc_status vc_lm_head_accept(int32_t B, int32_t M, int32_t Dm, int32_t V, const v
                             int32_t *n_out, void *workspace, size_t workspace_bytes, void *stream) {
   REQ(B >= 0 && M >= 1, "B >= 0 and M >= 1 required");
   REQ((int64_t)B * M <= 0x7fffffff, "B * M overflows");
-  vc_status st = check_lm_argmax(B * M, Dm, V, h, w, argmax, workspace, workspace_bytes);
+  vc_status st = vc::check_lm_argmax(B * M, Dm, V, h, w, argmax, workspace, workspace_bytes);
   if (st != VC_OK || B == 0) return st;
   REQ(accept_len && out_tokens && n_out, "null accept output");
   REQ(M == 1 || draft, "draft is required when M > 1");
@@ -259,10 +273,12 @@ vc_status vc_lm_head_accept(int32_t B, int32_t M, int32_t Dm, int32_t V, const v
                     "vc_lm_head_accept launch");
 }
 
-vc_status vc_commit_rows(int32_t B, int32_t Hkv, int32_t D, int32_t M, int32_t dtype, int64_t cap,
-                         int32_t dst_v_blocked, const void *blk_k, const void *blk_v, const int32_t *n_out,
-                         void *dst_k, void *dst_v,
-                         int32_t *len, float *degree, int64_t degree_h_stride, void *stream) {
+}  // extern "C"
+
+namespace vc {
+vc_status check_commit(int32_t B, int32_t Hkv, int32_t D, int32_t M, int32_t dtype, int64_t cap, int32_t dst_v_blocked,
+                       const void *blk_k, const void *blk_v, const int32_t *n_out, const void *dst_k,
+                       const void *dst_v, const int32_t *len, const float *degree, int64_t degree_h_stride) {
   REQ(B >= 0 && Hkv >= 1 && D >= 1 && M >= 1 && cap >= 0, "bad commit shape");
   REQ(dtype == VC_BF16 || dtype == VC_FP32, "unknown dtype %d", dtype);
   REQ(dst_v_blocked == 0 || dst_v_blocked == 1, "dst_v_blocked must be 0 or 1");
@@ -270,6 +286,19 @@ vc_status vc_commit_rows(int32_t B, int32_t Hkv, int32_t D, int32_t M, int32_t d
   if (B == 0) return VC_OK;
   REQ(blk_k && blk_v && n_out && dst_k && dst_v && len, "null pointer");
   REQ(!degree || degree_h_stride == 0 || degree_h_stride == cap, "degree_h_stride must be 0 or cap");
+  return VC_OK;
+}
+}  // namespace vc
+
+extern "C" {
+
+vc_status vc_commit_rows(int32_t B, int32_t Hkv, int32_t D, int32_t M, int32_t dtype, int64_t cap,
+                         int32_t dst_v_blocked, const void *blk_k, const void *blk_v, const int32_t *n_out,
+                         void *dst_k, void *dst_v,
+                         int32_t *len, float *degree, int64_t degree_h_stride, void *stream) {
+  vc_status st = vc::check_commit(B, Hkv, D, M, dtype, cap, dst_v_blocked, blk_k, blk_v, n_out, dst_k, dst_v, len,
+                                  degree, degree_h_stride);
+  if (st != VC_OK || B == 0) return st;
   const int64_t deg_b = degree_h_stride ? degree_h_stride * Hkv : cap;
   return hip_status(vc::launch_commit(B, Hkv, D, M, dtype == VC_BF16 ? 2 : 4, cap, dst_v_blocked, blk_k, blk_v, n_out, dst_k,
                                       dst_v, len, degree, deg_b, degree_h_stride, (hipStream_t)stream),
@@ -363,7 +392,7 @@ vc_status vc_quantize_int4_packed(int32_t B, int32_t Hkv, int32_t D, const void 
 }
 
 vc_status vc_csm_round(int32_t B, int32_t Hkv, int32_t D, int32_t n_in, int32_t n_sink, int32_t n_recent,
-                       int32_t chunk, float r, const void *in_k, const void *in_v, const float *in_deg,
+                       int32_t chunk, double r, const void *in_k, const void *in_v, const float *in_deg,
                        int64_t cap_in, void *out_k, void *out_v, float *out_deg, int64_t cap_out, int32_t *n_out,
                        void *stream) {
   REQ(n_out, "null n_out");

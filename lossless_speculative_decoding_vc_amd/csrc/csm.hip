@@ -83,8 +83,8 @@ __global__ __launch_bounds__(256) void csm_round_kernel(CsmParams p) {
   const int64_t s0 = (int64_t)p.n_sink + (int64_t)c * p.chunk;
   const int L = (int)min((int64_t)p.chunk, p.n_in - p.n_recent - s0);
   const int nA = (L + 1) / 2, nB = L / 2;
-  const int m = nB > 0 ? (int)floor((double)p.r * nA) : 0;
-  const int m_full = (int)floor((double)p.r * ((p.chunk + 1) / 2));
+  const int m = nB > 0 ? (int)floor(p.r * nA) : 0;
+  const int m_full = (int)floor(p.r * ((p.chunk + 1) / 2));
   const int64_t base = (int64_t)p.n_sink + (int64_t)c * (p.chunk - m_full);   // earlier chunks are full
 
   // stage the chunk: every load of a thread is issued before any of them is
@@ -341,7 +341,7 @@ __global__ __launch_bounds__(256) void csm_round_kernel(CsmParams p) {
 
 }  // namespace
 
-int csm_survivors(int n_in, int n_sink, int n_recent, int chunk, float r) {
+int csm_survivors(int n_in, int n_sink, int n_recent, int chunk, double r) {
   int out = n_in;
   for (int s = n_sink; s < n_in - n_recent; s += chunk) {
     const int L = min(chunk, n_in - n_recent - s);

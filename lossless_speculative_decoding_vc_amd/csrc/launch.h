@@ -17,6 +17,17 @@ struct SplitPlan {
 SplitPlan plan_draft(const vc_draft_args &a);
 SplitPlan plan_verify(const vc_verify_args &a);
 
+// Host-side validation of one call, as the entry point does it before any
+// launch (used by the round scheduler to check a whole round up front).
+vc_status validate_draft_call(const vc_draft_args *a);
+vc_status validate_verify_call(const vc_verify_args *a);
+vc_status check_lm_argmax(int32_t R, int32_t Dm, int32_t V, const void *h, const void *w, const void *out,
+                          void *ws, size_t ws_bytes);
+vc_status check_commit(int32_t B, int32_t Hkv, int32_t D, int32_t M, int32_t dtype, int64_t cap, int32_t dst_v_blocked,
+                       const void *blk_k, const void *blk_v, const int32_t *n_out, const void *dst_k,
+                       const void *dst_v, const int32_t *len, const float *degree, int64_t degree_h_stride);
+vc_status set_error(vc_status s, const char *msg);
+
 hipError_t launch_accept(const vc_accept_args &a, hipStream_t s);
 hipError_t launch_argmax(int rows, int V, int dtype, const void *logits, int *out, int out_stride,
                          hipStream_t s);
@@ -57,14 +68,14 @@ hipError_t launch_quantize_int4(const QuantParams &p, int n_groups, hipStream_t 
 // One Chunked Soft Matching round (see csm.hip).
 struct CsmParams {
   int n_in, n_sink, n_recent, chunk, n_out;
-  float r;
+  double r;   // merge count floor(r * |A|) is taken in double, as the caller wrote r
   int64_t cap_in, cap_out;
   const uint16_t *in_k, *in_v;
   const float *in_deg;
   uint16_t *out_k, *out_v;
   float *out_deg;
 };
-int csm_survivors(int n_in, int n_sink, int n_recent, int chunk, float r);
+int csm_survivors(int n_in, int n_sink, int n_recent, int chunk, double r);
 hipError_t launch_csm_round(const CsmParams &p, int BH, hipStream_t s);
 
 // Merge `splits` partials (o normalised per split, lse in log2 units) of

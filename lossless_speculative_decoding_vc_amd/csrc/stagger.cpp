@@ -19,20 +19,7 @@
 #include <string>
 #include <vector>
 
-#include "../../include/vc.h"
-
-struct vc_stagger {
-  std::vector<void *> slots;
-  size_t slot_bytes = 0;
-  hipStream_t h2d = nullptr, d2h = nullptr;
-  std::vector<hipEvent_t> slot_free;             // per slot
-  std::vector<hipEvent_t> copy_start, copied;    // per layer
-  std::vector<char> copy_recorded;
-};
-
-namespace vc {
-vc_status set_error(vc_status s, const char *msg);
-}
+#include "stagger_impl.h"
 
 namespace {
 
@@ -52,9 +39,12 @@ vc_status stagger_init(vc_stagger *s, void *const *slots, int32_t nslots, size_t
   s->slots.assign(slots, slots + nslots);
   s->slot_bytes = slot_bytes;
   s->slot_free.assign(nslots, nullptr);
+  s->holder.assign(nslots, -1);
+  s->released.assign(nslots, 1);
   s->copy_start.assign(max_layers, nullptr);
   s->copied.assign(max_layers, nullptr);
   s->copy_recorded.assign(max_layers, 0);
+  s->copy_timed.assign(max_layers, 0);
   HIPCHK(hipStreamCreateWithFlags(&s->h2d, hipStreamNonBlocking));
   HIPCHK(hipStreamCreateWithFlags(&s->d2h, hipStreamNonBlocking));
   for (auto &e : s->slot_free) HIPCHK(hipEventCreateWithFlags(&e, hipEventDisableTiming));
@@ -100,25 +90,44 @@ vc_status vc_stagger_stream_layer(vc_stagger *s, int32_t layer, const void *host
   if (!s || layer < 0 || layer >= (int)s->copied.size() || !host_src || bytes > s->slot_bytes)
     return vc::set_error(VC_EINVAL, "bad stream_layer arguments");
   const int slot = layer % (int)s->slots.size();
+  // the slot's previous layer must have been released, or the copy would
+  // overwrite a slot that verify may still read
+  if (!s->released[slot]) {
+    std::string m = "stream_layer(" + std::to_string(layer) + "): slot " + std::to_string(slot) +
+                    " still holds layer " + std::to_string(s->holder[slot]) + ", which was not released";
+    return vc::set_error(VC_EINVAL, m.c_str());
+  }
   HIPCHK(hipStreamWaitEvent(s->h2d, s->slot_free[slot], 0));
   HIPCHK(hipEventRecord(s->copy_start[layer], s->h2d));
   HIPCHK(hipMemcpyAsync(s->slots[slot], host_src, bytes, hipMemcpyHostToDevice, s->h2d));
   HIPCHK(hipEventRecord(s->copied[layer], s->h2d));
   s->copy_recorded[layer] = 1;
+  s->copy_timed[layer] = 1;
+  s->holder[slot] = layer;
+  s->released[slot] = 0;
   return VC_OK;
 }
 
 vc_status vc_stagger_acquire(vc_stagger *s, int32_t layer, void *stream, void **slot) {
-  if (!s || layer < 0 || layer >= (int)s->copied.size() || !slot || !s->copy_recorded[layer])
-    return vc::set_error(VC_EINVAL, "acquire of a layer that was not streamed");
+  if (!s || layer < 0 || layer >= (int)s->copied.size() || !slot)
+    return vc::set_error(VC_EINVAL, "bad acquire arguments");
+  const int sl = layer % (int)s->slots.size();
+  if (!s->copy_recorded[layer] || s->holder[sl] != layer)
+    return vc::set_error(VC_EINVAL, "acquire of a layer that is not streamed into its slot (not streamed, or "
+                                    "already released)");
   HIPCHK(hipStreamWaitEvent((hipStream_t)stream, s->copied[layer], 0));
-  *slot = s->slots[layer % (int)s->slots.size()];
+  *slot = s->slots[sl];
   return VC_OK;
 }
 
 vc_status vc_stagger_release(vc_stagger *s, int32_t layer, void *stream) {
   if (!s || layer < 0 || layer >= (int)s->copied.size()) return vc::set_error(VC_EINVAL, "bad release");
-  HIPCHK(hipEventRecord(s->slot_free[layer % (int)s->slots.size()], (hipStream_t)stream));
+  const int sl = layer % (int)s->slots.size();
+  if (s->holder[sl] != layer || s->released[sl])
+    return vc::set_error(VC_EINVAL, "release of a layer that does not hold its slot");
+  HIPCHK(hipEventRecord(s->slot_free[sl], (hipStream_t)stream));
+  s->released[sl] = 1;
+  s->copy_recorded[layer] = 0;   // the slot may be refilled: a later acquire needs a new copy
   return VC_OK;
 }
 
@@ -143,7 +152,7 @@ vc_status vc_stagger_sync(vc_stagger *s) {
 }
 
 vc_status vc_stagger_copy_ms(vc_stagger *s, int32_t layer, float *ms) {
-  if (!s || layer < 0 || layer >= (int)s->copied.size() || !ms || !s->copy_recorded[layer])
+  if (!s || layer < 0 || layer >= (int)s->copied.size() || !ms || !s->copy_timed[layer])
     return vc::set_error(VC_EINVAL, "no copy recorded for this layer");
   HIPCHK(hipEventElapsedTime(ms, s->copy_start[layer], s->copied[layer]));
   return VC_OK;
@@ -155,7 +164,7 @@ vc_status vc_stagger_destroy(vc_stagger *s) {
   // for a later call to pick up
   if (s->h2d) (void)hipStreamSynchronize(s->h2d);
   if (s->d2h) (void)hipStreamSynchronize(s->d2h);
-  for (auto *v : {&s->slot_free, &s->copy_start, &s->copied})
+  for (auto *v : {&s->slot_free, &s->copy_start, &s->copied, &s->round_ev})
     for (auto e : *v)
       if (e) (void)hipEventDestroy(e);
   if (s->h2d) (void)hipStreamDestroy(s->h2d);

@@ -108,6 +108,7 @@ def test_workspace_plan_is_host_only(L):
     # c3 draft shape: 32 x 8 KV heads, 32768 compressed tokens -> split partials
     a = _draft(B=32, Hq=32, Hkv=8, cap=32768)
     ws = L.vc_draft_workspace_size(ctypes.byref(a))
+    # one partial row (D values and a log-sum-exp) per split and query head
     assert ws > 0 and ws % (32 * 32 * 129 * 4) == 0
     # fp32 mode runs unsplit
     assert L.vc_draft_workspace_size(ctypes.byref(_draft(dtype=1))) == 0
@@ -118,7 +119,8 @@ def test_lm_head_argmax_validation_is_host_only(L):
     # workspace are rejected before any GPU work
     fake = ctypes.c_void_p(1 << 20)   # aligned, never dereferenced on these paths
     ws_need = L.vc_lm_head_argmax_workspace_size(528, 32768)
-    assert ws_need == 528 * 128 * 8   # one (max, index) pair per row and 256-entry vocabulary tile
+    # one (max, index) pair per row and 256-entry (128-entry for drafting rows) vocabulary tile
+    assert ws_need == 528 * 128 * 8
     assert L.vc_lm_head_argmax_workspace_size(16, 32768) == 16 * 256 * 8
     assert L.vc_lm_head_argmax(4, 48, 100, fake, fake, fake, 1, fake, 1 << 20, None) == vcb.VC_ENOTSUP
     assert L.vc_lm_head_argmax(4, 64, 100, fake, fake, fake, 1, fake, 8, None) == vcb.VC_EINVAL
@@ -232,14 +234,17 @@ def test_csm_survivor_count_matches_oracle_on_many_shapes(L):
     from oracle import csm as C
     rng = np.random.default_rng(5)
     n = ctypes.c_int32(-1)
-    cases = [(40, 20, 20, 2, 1.0), (40, 0, 0, 128, 0.0), (1, 0, 0, 64, 1.0), (131072, 4, 1024, 64, 1.0)]
+    cases = [(40, 20, 20, 2, 1.0), (40, 0, 0, 128, 0.0), (1, 0, 0, 64, 1.0), (131072, 4, 1024, 64, 1.0),
+             # ratios of a decaying schedule that float32 would round down: floor(0.7 * 10) = 7 needs r in double
+             (4 + 6 * 20 + 8, 4, 8, 20, 0.7), (4 + 3 * 40 + 8, 4, 8, 40, 0.9), (100, 0, 0, 20, 0.7),
+             (1000, 4, 64, 64, 1.0 - 3 * 0.1)]
     for _ in range(200):
         n_in = int(rng.integers(1, 5000))
         sink = int(rng.integers(0, 40))
         recent = int(rng.integers(0, 200))
         if sink + recent > n_in:
             continue
-        cases.append((n_in, sink, recent, int(rng.integers(2, 129)), float(np.float32(rng.random()))))
+        cases.append((n_in, sink, recent, int(rng.integers(2, 129)), float(rng.random())))
     for n_in, sink, recent, chunk, r in cases:
         cap = (n_in + 31) // 32 * 32
         st = L.vc_csm_round(0, 2, 128, n_in, sink, recent, chunk, r, None, None, None, cap, None, None, None, cap,

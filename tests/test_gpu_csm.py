@@ -20,7 +20,7 @@ D = 128
 
 
 def _plant(r):
-    return lambda L: int(np.floor(np.float64(np.float32(r)) * ((L + 1) // 2)))
+    return lambda L: int(np.floor(r * ((L + 1) // 2)))
 
 
 def _run(kbits, vbits, deg, n_in, sink, recent, chunk, r, cap_out):
@@ -56,13 +56,17 @@ def _case(B, Hkv, n_in, sink, recent, chunk, r, seed, with_deg=True):
 
 @pytest.mark.parametrize("n_in,sink,recent,chunk,r", [(4 + 5 * 64 + 23 + 16, 4, 16, 64, 1.0),
                                                       (300, 0, 32, 64, 0.5), (260, 8, 8, 128, 0.75),
-                                                      (200, 4, 4, 16, 0.25)])
+                                                      (200, 4, 4, 16, 0.25),
+                                                      # ratios a float32 would round below the exact count:
+                                                      # floor(0.7 * 10) = 7, floor(0.9 * 20) = 18
+                                                      (4 + 6 * 20 + 11 + 8, 4, 8, 20, 0.7),
+                                                      (4 + 3 * 40 + 8, 4, 8, 40, 0.9)])
 def test_planted_round_matches_oracle(n_in, sink, recent, chunk, r):
     B, Hkv = 2, 2
     kb, vb, deg, cap_in = _case(B, Hkv, n_in, sink, recent, chunk, r, seed=51)
     cap_out = cap_in
     n_out, ok, ov, od, _ = _run(kb, vb, deg, n_in, sink, recent, chunk, r, cap_out)
-    rr = float(np.float32(r))
+    rr = r   # the caller's ratio, unrounded: the merge count is floor(r * |A|) in double
     assert n_out == C.survivors(n_in, sink, recent, chunk, rr)
     for b in range(B):
         for h in range(Hkv):

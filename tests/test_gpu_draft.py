@@ -173,3 +173,27 @@ def test_int4_packed_main_segment(splits):
     got, ref = _int4_check(2, 16, 4, 512, [[512, 480, 96, 1], [200, 511, 32, 256]], 0, None, None, seed=32,
                            packed=True)
     assert rel_l2(got, ref) <= 2e-2
+
+
+def test_split_calls_share_one_workspace():
+    # One workspace serves draft calls of different shapes and split counts
+    # (2 .. 64 splits, 1 .. 16 query heads per KV head) back to back: every
+    # call writes its partials before its merge reads them.
+    import torch
+    import lossless_speculative_decoding_vc_amd as vc
+    ws = vc.new_workspace(1 << 24, "cuda")
+    cases = [(3, 12, 3, 2048, [[2048, 1999, 1500], [700, 64, 1], [0, 33, 2047]], 40, [40, 7, 1], 64),
+             (2, 32, 2, 4096, [[4096, 4000], [37, 2500]], 0, None, 2),
+             (1, 16, 1, 4096, [[4093]], 16, [16], 33),
+             (2, 8, 8, 1024, [[1024] * 8, [1, 2, 3, 4, 5, 6, 7, 1000]], 0, None, 0)]
+    for i, (B, Hq, Hkv, cap, ml, tcap, tl, splits) in enumerate(cases):
+        dev, ref, mlen, tlen, deg = _case(B, Hq, Hkv, 128, cap, ml, tcap, tl, "bf16", "shared", 90 + i, 3.0)
+        lse = torch.empty((B, Hq), dtype=torch.float32, device="cuda")
+        out = vc.draft_attn(dev["q"], dev["k"], dev["v"], to_dev(mlen), degree=to_dev(deg),
+                            tail_k=dev["tail_k"], tail_v=dev["tail_v"],
+                            tail_len=None if tlen is None else to_dev(tlen), out_lse=lse, num_splits=splits,
+                            workspace=ws)
+        torch.cuda.synchronize()
+        o_ref, lse_ref = A.draft_attn(ref["q"], ref["k"], ref["v"], mlen, deg, ref["tail_k"], ref["tail_v"], tlen)
+        assert_close(bf16_dev_to_f64(out), o_ref, TOL["bf16"], f"out, case {i}")
+        assert_close(lse.cpu().numpy(), lse_ref, TOL["bf16"] * 0.1, f"lse, case {i}")

@@ -38,7 +38,7 @@ def test_round_steps_replay_from_a_graph():
     al = torch.empty(B, dtype=torch.int32, device=dev)
     toks = torch.empty((B, M), dtype=torch.int32, device=dev)
     nout = torch.empty(B, dtype=torch.int32, device=dev)
-    ws = torch.empty(1 << 24, dtype=torch.uint8, device=dev)
+    ws = vc.new_workspace(1 << 24, dev)
     ws_lm_d = vc.lm_head_argmax_workspace(B, V, dev)
     ws_lm_v = vc.lm_head_argmax_workspace(B * M, V, dev)
 
