@@ -5,11 +5,13 @@
 // attention over the union of the ranges is
 //   o = sum_s 2^(lse_s - L) o_s,   L = log2 sum_s 2^lse_s,
 // the standard flash-decoding reduction.  One workgroup per output row with
-// up to 16 waves: wave w takes the splits w, w + nw, ... eight at a time (all
-// eight partial rows in flight), every lane its D/64 channels, and the waves'
-// sums meet in LDS.  Spreading one row over several waves keeps the loads of
-// a many-split, few-row merge (one long request) in flight instead of
-// walking the splits one batch after another.
+// up to 16 waves: wave w takes the splits w, w + nw, ... eight at a time, and
+// every lane its D/64 channels.  Each batch of eight issues all its loads at
+// once (eight log-sum-exps and eight partial rows) and folds them into a
+// running maximum and rescaled sums, so a merge of up to eight splits costs
+// one round trip to memory; the waves' (max, sum, row) triples meet in LDS.
+// Spreading one row over several waves keeps the loads of a many-split,
+// few-row merge (one long request) in flight.
 #include "common.h"
 #include "launch.h"
 
@@ -31,57 +33,80 @@ __global__ __launch_bounds__(kMaxCombineWaves * 64) void combine_splits(const fl
   const int nw = blockDim.x >> 6;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
 
-  // reference: the largest split lse of the row
-  float mx = kNegInf;
-  for (int s = threadIdx.x; s < splits; s += blockDim.x) mx = fmaxf(mx, part_lse[(size_t)s * rows + row]);
-  mx = wave_max(mx);
-  if (lane == 0) red_m[wave] = mx;
-  __syncthreads();
-  mx = red_m[0];
-  for (int w = 1; w < nw; ++w) mx = fmaxf(mx, red_m[w]);
-  const float mu = (mx == kNegInf) ? 0.f : mx;
-
+  float m = kNegInf;   // running reference (base 2) of this wave's sums
   float acc[kPer];
 #pragma unroll
   for (int e = 0; e < kPer; ++e) acc[e] = 0.f;
   float wsum = 0.f;
   for (int s0 = wave; s0 < splits; s0 += 8 * nw) {
-    float w[8], v[8][kPer];
+    float l[8], v[8][kPer];
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       const int s = s0 + u * nw;
       const bool ok = s < splits;
       const int sc = ok ? s : s0;
-      w[u] = ok ? fast_exp2(part_lse[(size_t)sc * rows + row] - mu) : 0.f;
+      l[u] = ok ? part_lse[(size_t)sc * rows + row] : kNegInf;
       const float *po = part_o + ((size_t)sc * rows + row) * D + lane * kPer;
 #pragma unroll
-      for (int e = 0; e < kPer; ++e) v[u][e] = ok ? po[e] : 0.f;
+      for (int e = 0; e < kPer; ++e) v[u][e] = po[e];
     }
+    float mb = m;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) mb = fmaxf(mb, l[u]);
+    const float mu = (mb == kNegInf) ? 0.f : mb;
+    const float alpha = fast_exp2(m - mu);   // 0 while nothing was summed (m = -inf)
+    wsum *= alpha;
+#pragma unroll
+    for (int e = 0; e < kPer; ++e) acc[e] *= alpha;
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
-      wsum += w[u];
+      const float w = fast_exp2(l[u] - mu);   // 0 for an empty split or past the end
+      wsum += w;
 #pragma unroll
-      for (int e = 0; e < kPer; ++e) acc[e] += w[u] * v[u][e];
+      for (int e = 0; e < kPer; ++e) acc[e] += w * v[u][e];
     }
+    m = mb;
+  }
+  if (nw == 1) {
+    const float inv = 1.f / wsum;   // wsum == 0 only for an empty key set -> NaN output
+#pragma unroll
+    for (int e = 0; e < kPer; ++e) {
+      const float x = acc[e] * inv;
+      if constexpr (kBf16) reinterpret_cast<uint16_t *>(out)[(size_t)row * D + lane * kPer + e] = f32_to_bf16(x);
+      else reinterpret_cast<float *>(out)[(size_t)row * D + lane * kPer + e] = x;
+    }
+    if (out_lse && lane == 0) out_lse[row] = (wsum > 0.f) ? (m + fast_log2(wsum)) * kLn2 : kNegInf;
+    return;
   }
 #pragma unroll
   for (int e = 0; e < kPer; ++e) red_o[wave][lane * kPer + e] = acc[e];
-  if (lane == 0) red_w[wave] = wsum;
+  if (lane == 0) {
+    red_w[wave] = wsum;
+    red_m[wave] = m;
+  }
   __syncthreads();
   if (wave != 0) return;
-  for (int w = 1; w < nw; ++w) {
+  float M = kNegInf;
+  for (int w = 0; w < nw; ++w) M = fmaxf(M, red_m[w]);
+  const float Mu = (M == kNegInf) ? 0.f : M;
+  float tot = 0.f;
+  float o[kPer];
 #pragma unroll
-    for (int e = 0; e < kPer; ++e) acc[e] += red_o[w][lane * kPer + e];
-    wsum += red_w[w];
+  for (int e = 0; e < kPer; ++e) o[e] = 0.f;
+  for (int w = 0; w < nw; ++w) {
+    const float f = fast_exp2(red_m[w] - Mu);
+    tot += f * red_w[w];
+#pragma unroll
+    for (int e = 0; e < kPer; ++e) o[e] += f * red_o[w][lane * kPer + e];
   }
-  const float inv = 1.f / wsum;   // wsum == 0 only for an empty key set -> NaN output
+  const float inv = 1.f / tot;
 #pragma unroll
   for (int e = 0; e < kPer; ++e) {
-    const float v = acc[e] * inv;
-    if constexpr (kBf16) reinterpret_cast<uint16_t *>(out)[(size_t)row * D + lane * kPer + e] = f32_to_bf16(v);
-    else reinterpret_cast<float *>(out)[(size_t)row * D + lane * kPer + e] = v;
+    const float x = o[e] * inv;
+    if constexpr (kBf16) reinterpret_cast<uint16_t *>(out)[(size_t)row * D + lane * kPer + e] = f32_to_bf16(x);
+    else reinterpret_cast<float *>(out)[(size_t)row * D + lane * kPer + e] = x;
   }
-  if (out_lse && lane == 0) out_lse[row] = (wsum > 0.f) ? (mx + fast_log2(wsum)) * kLn2 : kNegInf;
+  if (out_lse && lane == 0) out_lse[row] = (tot > 0.f) ? (M + fast_log2(tot)) * kLn2 : kNegInf;
 }
 
 }  // namespace
