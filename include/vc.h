@@ -106,6 +106,20 @@ typedef struct vc_draft_args {
 vc_status vc_draft_attn(const vc_draft_args *a, void *stream);
 size_t    vc_draft_workspace_size(const vc_draft_args *a);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * call as vc_draft_attn, with a->workspace ignored.  The split partials live
+ * in a static device array of vc_draft_noalloc_max_scratch() bytes (16 MiB),
+ * one per GPU, held until the process ends; this call allocates nothing.  A
+ * call whose vc_draft_workspace_size() exceeds the array fails with
+ * VC_EINVAL before anything is enqueued.  Every call on one GPU shares that
+ * GPU's array and the array keeps the last call's partials: calls that
+ * overlap in time on one GPU (e.g. on two streams) race and must not be
+ * made.  Nothing in it needs clearing: a call writes its partials before it
+ * reads them.                                                              */
+vc_status vc_draft_attn_noalloc(const vc_draft_args *a, void *stream);
+size_t    vc_draft_noalloc_max_scratch(void);
+
 /* ------------------------------------------------------------------------ */
 /* Verify block attention ("Algoritmo Principale", step 2: one forward pass
  * with the full cache checks every drafted token in parallel).  Each request

@@ -112,6 +112,9 @@ def lib():
             fn = getattr(L, name)
             fn.argtypes = argt
             fn.restype = ctypes.c_int
+        L.vc_draft_attn_noalloc.argtypes = [ctypes.POINTER(DraftArgs), _p]
+        L.vc_draft_attn_noalloc.restype = ctypes.c_int
+        L.vc_draft_noalloc_max_scratch.restype = ctypes.c_size_t
         L.vc_draft_workspace_size.argtypes = [ctypes.POINTER(DraftArgs)]
         L.vc_draft_workspace_size.restype = ctypes.c_size_t
         L.vc_verify_workspace_size.argtypes = [ctypes.POINTER(VerifyArgs)]
@@ -278,6 +281,30 @@ def draft_attn(q, k, v, main_len, degree=None, tail_k=None, tail_v=None, tail_le
     a = draft_args(q, k, v, main_len, degree, tail_k, tail_v, tail_len, out, out_lse, scale, num_splits,
                    workspace, fmt, k_scale, k_zero, v_scale, v_zero)
     _check(lib().vc_draft_attn(ctypes.byref(a), _stream(stream)))
+    return out
+
+
+def draft_attn_noalloc(q, k, v, main_len, degree=None, tail_k=None, tail_v=None, tail_len=None, out=None,
+                       out_lse=None, scale=None, num_splits=0, fmt=VC_KV_DENSE, k_scale=None, k_zero=None,
+                       v_scale=None, v_zero=None, stream=None):
+    """:func:`draft_attn` through ``vc_draft_attn_noalloc``: the split
+    partials live in the library's static per-GPU array, so the library
+    allocates nothing (``out`` is required: this wrapper allocates nothing
+    either)."""
+    if out is None:
+        raise ValueError("out is required")
+    _check_draft_shapes(q, k, v, main_len, degree, tail_k, tail_v, tail_len, out, out_lse, fmt,
+                        k_scale, k_zero, v_scale, v_zero)
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (tail_k, "tail_k"), (tail_v, "tail_v"),
+                 (out, "out"), (degree, "degree"), (out_lse, "out_lse"), (k_scale, "k_scale"),
+                 (k_zero, "k_zero"), (v_scale, "v_scale"), (v_zero, "v_zero")):
+        _dev(t, n)
+    _dev(main_len, "main_len", torch.int32)
+    _dev(tail_len, "tail_len", torch.int32)
+    cap = k.shape[2] * 32 if fmt == VC_KV_INT4_PACKED else k.shape[2]
+    a = _draft_struct(q, k, v, main_len, degree, tail_k, tail_v, tail_len, out, out_lse,
+                      scale, num_splits, fmt, k_scale, k_zero, v_scale, v_zero, k.shape[1], cap)
+    _check(lib().vc_draft_attn_noalloc(ctypes.byref(a), _stream(stream)))
     return out
 
 
