@@ -27,9 +27,22 @@ notes):
   (lower A index first on equal similarity) merge into the token they point
   at, chunk by chunk;
 * similarity = cosine of the key vectors as cached;
-* one round per call with a given r (the decaying schedule is the caller's);
-  a last chunk shorter than ``chunk`` is processed the same way;
+* one round per call with a given r; a last chunk shorter than ``chunk`` is
+  processed the same way;
 * survivors (unmerged A tokens and every B token) keep ascending position.
+
+The rounds compose into the inference pipeline of item 2 and the progressive
+schedule of item 3 (:func:`schedule_ratio`, :func:`centroid_run`), read as:
+
+* after the prefill, one round when the cache holds more tokens than the
+  budget; during decoding the cache grows by one token (degree 1) per step
+  and every ``every``-th step one round runs when it is over the budget;
+* round j (counting the rounds run so far, prefill round included) merges
+  with ``r_j = r_init - j * delta_r``, kept within [0, 1]; a round reduces
+  its middle segment by at most half, since only A tokens (every other token
+  of a chunk) can merge away ("Limitazioni": at most half per step);
+* degrees carry over from round to round (a centroid's degree counts every
+  token it ever absorbed).
 
 Parity: pinned by invariants a wrong index, weight or sign would break --
 conservation of total degree and of the degree-weighted key and value sums,
@@ -108,3 +121,46 @@ def survivors(n, n_sink, n_recent, chunk, r):
     for (s, e) in chunk_plan(n, n_sink, n_recent, chunk):
         out -= int(np.floor(r * ((e - s + 1) // 2))) if e - s > 1 else 0
     return out
+
+
+def schedule_ratio(j, r_init, delta_r):
+    """Ratio of clustering round ``j`` (0-based): ``r_init - j * delta_r``
+    ("Scheduling Progressivo"), kept within [0, 1]."""
+    return min(1.0, max(0.0, r_init - j * delta_r))
+
+
+def centroid_run(k0, v0, k_new, v_new, budget, every, r_init, delta_r, n_sink, n_recent, chunk):
+    """The CentroidKV pipeline over one KV head ("Pipeline di Inferenza",
+    "Scheduling Progressivo"): the prefill cache ``k0, v0 [n0][D]`` (degree
+    1), a round after the prefill if ``n0 > budget``, then one decode token
+    per step (``k_new, v_new [steps][D]``, degree 1) and a round after every
+    ``every``-th step while the cache holds more than ``budget`` tokens.
+
+    Returns ``(k, v, deg, rounds)``; ``rounds`` lists per round a dict with
+    the decode step it ran after (0 = prefill), its index ``j``, ratio ``r``,
+    token counts ``n_in`` / ``n_out`` and the round's per-chunk decisions.
+    """
+    if every < 1:
+        raise ValueError("every must be >= 1")
+    k = np.asarray(k0, np.float64).copy()
+    v = np.asarray(v0, np.float64).copy()
+    deg = np.ones(len(k))
+    rounds = []
+
+    def cluster(step):
+        nonlocal k, v, deg
+        j = len(rounds)
+        r = schedule_ratio(j, r_init, delta_r)
+        n_in = len(k)
+        k, v, deg, info = csm_round(k, v, deg, n_sink, n_recent, chunk, r)
+        rounds.append(dict(step=step, j=j, r=r, n_in=n_in, n_out=len(k), info=info))
+
+    if len(k) > budget:
+        cluster(0)
+    for t in range(len(k_new)):
+        k = np.concatenate([k, np.asarray(k_new[t], np.float64)[None]])
+        v = np.concatenate([v, np.asarray(v_new[t], np.float64)[None]])
+        deg = np.concatenate([deg, [1.0]])
+        if (t + 1) % every == 0 and len(k) > budget:
+            cluster(t + 1)
+    return k, v, deg, rounds
