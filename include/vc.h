@@ -306,10 +306,11 @@ vc_status vc_quantize_int4_packed(int32_t B, int32_t Hkv, int32_t D, const void 
  *   a cluster's key and value are the degree-weighted means of its members
  *   (fp32, rounded to bf16), its degree the sum; unmerged tokens are copied
  *   bit-exactly; survivors keep ascending position.
- * The decaying ratio schedule r = r_init - j * delta_r is the caller's (one
- * call per round).  The survivor count, the same for every (b, KV head), is
- * returned in *n_out (host) before launch; output tokens past it are not
- * written.
+ * One call is one round (the schedule that decides when rounds run and with
+ * which r is vc_csm_round_due / vc_csm_schedule_ratio below).  The survivor
+ * count, the same for every (b, KV head), is returned in *n_out (host)
+ * before launch, and written to out_len[b][h] (device, optional) by the
+ * launch; output tokens past it are not written.
  *   in_k [B][Hkv][cap_in][D], in_v [B][Hkv][cap_in/32][D][32]   bf16
  *   in_deg [B][Hkv][cap_in] fp32 (NULL: every degree 1)
  *   out_k [B][Hkv][cap_out][D], out_v [B][Hkv][cap_out/32][D][32]   bf16
@@ -320,7 +321,23 @@ vc_status vc_quantize_int4_packed(int32_t B, int32_t Hkv, int32_t D, const void 
 vc_status vc_csm_round(int32_t B, int32_t Hkv, int32_t D, int32_t n_in, int32_t n_sink, int32_t n_recent,
                        int32_t chunk, double r, const void *in_k, const void *in_v, const float *in_deg,
                        int64_t cap_in, void *out_k, void *out_v, float *out_deg, int64_t cap_out, int32_t *n_out,
-                       void *stream);
+                       int32_t *out_len, void *stream);
+
+/* The CentroidKV schedule around vc_csm_round ("Riassunto Tecnico:
+ * CentroidKV", "Componenti Chiave" item 2 "Pipeline di Inferenza": a first
+ * round after the prefill when the cache exceeds the budget, then a round
+ * every `every` decode steps to keep it within the budget; item 3 "Scheduling
+ * Progressivo": the ratio decays linearly over rounds).  Host-only.
+ *   vc_csm_round_due: 1 when a round is due after decode step `decode_step`
+ *     (0 = right after the prefill; a check every `every` steps after that)
+ *     for a cache of n_tokens, i.e. n_tokens > budget; 0 otherwise; -1 for
+ *     every < 1 or a negative step.
+ *   vc_csm_schedule_ratio: r_j = r_init - j * delta_r for round j (0-based,
+ *     counting the rounds run so far), kept within [0, 1].
+ * A round removes at most half of its middle segment (only one of the two
+ * alternating sets merges away).                                            */
+int32_t vc_csm_round_due(int64_t n_tokens, int64_t budget, int32_t decode_step, int32_t every);
+double  vc_csm_schedule_ratio(double r_init, double delta_r, int32_t round);
 
 /* ------------------------------------------------------------------------ */
 /* Cross-resource staggering ("Innovazioni Chiave del Sistema", P1): while

@@ -138,7 +138,11 @@ def lib():
         L.vc_quantize_int4_packed.argtypes = [_i32, _i32, _i32, _p, _p, _i64, _p, _i32, _i64, _p, _p, _p]
         L.vc_quantize_int4_packed.restype = ctypes.c_int
         L.vc_csm_round.argtypes = [_i32, _i32, _i32, _i32, _i32, _i32, _i32, ctypes.c_double, _p, _p, _p, _i64,
-                                   _p, _p, _p, _i64, ctypes.POINTER(_i32), _p]
+                                   _p, _p, _p, _i64, ctypes.POINTER(_i32), _p, _p]
+        L.vc_csm_round_due.argtypes = [_i64, _i64, _i32, _i32]
+        L.vc_csm_round_due.restype = _i32
+        L.vc_csm_schedule_ratio.argtypes = [ctypes.c_double, ctypes.c_double, _i32]
+        L.vc_csm_schedule_ratio.restype = ctypes.c_double
         L.vc_csm_round.restype = ctypes.c_int
         L.vc_stagger_create.argtypes = [ctypes.POINTER(_p), ctypes.POINTER(_p), _i32, ctypes.c_size_t, _i32]
         L.vc_stagger_stream_layer.argtypes = [_p, _i32, _p, ctypes.c_size_t]
@@ -723,12 +727,14 @@ def quantize_int4_packed(src_k, src_v, src_start, n_groups, dst_start, packed, s
                                          int(n_groups), cap, _ptr(dst_start), _ptr(packed), _stream(stream)))
 
 
-def csm_round(in_k, in_v, n_in, n_sink, n_recent, chunk, r, out_k, out_v, out_deg, in_deg=None, stream=None):
+def csm_round(in_k, in_v, n_in, n_sink, n_recent, chunk, r, out_k, out_v, out_deg, in_deg=None, out_len=None,
+              stream=None):
     """One Chunked Soft Matching round (``vc_csm_round``); returns the survivor count.
 
     ``in_k [B][Hkv][cap_in][D]``, ``in_v [B][Hkv][cap_in/32][D][32]`` bf16,
     ``in_deg [B][Hkv][cap_in]`` float32 or None; outputs in the same layouts with
-    ``cap_out``; ``out_deg [B][Hkv][cap_out]`` float32.
+    ``cap_out``; ``out_deg [B][Hkv][cap_out]`` float32; ``out_len`` int32
+    ``[B][Hkv]`` (optional) receives the survivor count on the device.
     """
     _dev(in_k, "in_k", torch.bfloat16)
     _dev(in_v, "in_v", torch.bfloat16)
@@ -736,12 +742,33 @@ def csm_round(in_k, in_v, n_in, n_sink, n_recent, chunk, r, out_k, out_v, out_de
     _dev(out_v, "out_v", torch.bfloat16)
     _dev(out_deg, "out_deg", torch.float32)
     _dev(in_deg, "in_deg", torch.float32)
+    _dev(out_len, "out_len", torch.int32)
     B, Hkv, cap_in, D = in_k.shape
+    cap_out = out_k.shape[2]
+    _want(in_v, "in_v", (B, Hkv, cap_in // 32, D, 32), (torch.bfloat16,))
+    _want(in_deg, "in_deg", (B, Hkv, cap_in), (torch.float32,))
+    _want(out_k, "out_k", (B, Hkv, cap_out, D), (torch.bfloat16,))
+    _want(out_v, "out_v", (B, Hkv, cap_out // 32, D, 32), (torch.bfloat16,))
+    _want(out_deg, "out_deg", (B, Hkv, cap_out), (torch.float32,))
+    _want(out_len, "out_len", (B, Hkv), (torch.int32,))
     n_out = _i32()
     _check(lib().vc_csm_round(B, Hkv, D, int(n_in), int(n_sink), int(n_recent), int(chunk), float(r), _ptr(in_k),
                               _ptr(in_v), _ptr(in_deg), cap_in, _ptr(out_k), _ptr(out_v), _ptr(out_deg),
-                              out_k.shape[2], ctypes.byref(n_out), _stream(stream)))
+                              cap_out, ctypes.byref(n_out), _ptr(out_len), _stream(stream)))
     return n_out.value
+
+
+def csm_round_due(n_tokens, budget, decode_step, every):
+    """Whether the CentroidKV schedule runs a round now (``vc_csm_round_due``)."""
+    d = lib().vc_csm_round_due(int(n_tokens), int(budget), int(decode_step), int(every))
+    if d < 0:
+        raise ValueError("every must be >= 1 and decode_step >= 0")
+    return bool(d)
+
+
+def csm_schedule_ratio(r_init, delta_r, round_index):
+    """Ratio of clustering round ``round_index`` (``vc_csm_schedule_ratio``)."""
+    return lib().vc_csm_schedule_ratio(float(r_init), float(delta_r), int(round_index))
 
 
 class Stagger:

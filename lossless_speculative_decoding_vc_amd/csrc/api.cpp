@@ -394,7 +394,7 @@ vc_status vc_quantize_int4_packed(int32_t B, int32_t Hkv, int32_t D, const void 
 vc_status vc_csm_round(int32_t B, int32_t Hkv, int32_t D, int32_t n_in, int32_t n_sink, int32_t n_recent,
                        int32_t chunk, double r, const void *in_k, const void *in_v, const float *in_deg,
                        int64_t cap_in, void *out_k, void *out_v, float *out_deg, int64_t cap_out, int32_t *n_out,
-                       void *stream) {
+                       int32_t *out_len, void *stream) {
   REQ(n_out, "null n_out");
   REQ(B >= 0 && Hkv >= 1 && n_in >= 0 && n_sink >= 0 && n_recent >= 0, "bad CSM shape");
   REQ((int64_t)B * Hkv <= 65535, "at most 65535 (request, KV head) slices per call");
@@ -419,7 +419,19 @@ vc_status vc_csm_round(int32_t B, int32_t Hkv, int32_t D, int32_t n_in, int32_t 
   p.out_k = static_cast<uint16_t *>(out_k);
   p.out_v = static_cast<uint16_t *>(out_v);
   p.out_deg = out_deg;
+  p.out_len = out_len;
   return hip_status(vc::launch_csm_round(p, B * Hkv, (hipStream_t)stream), "vc_csm_round launch");
+}
+
+int32_t vc_csm_round_due(int64_t n_tokens, int64_t budget, int32_t decode_step, int32_t every) {
+  if (every < 1 || decode_step < 0) return -1;
+  if (decode_step > 0 && decode_step % every != 0) return 0;
+  return n_tokens > budget ? 1 : 0;
+}
+
+double vc_csm_schedule_ratio(double r_init, double delta_r, int32_t round) {
+  const double r = r_init - (double)round * delta_r;
+  return r < 0.0 ? 0.0 : (r > 1.0 ? 1.0 : r);
 }
 
 }  // extern "C"

@@ -66,6 +66,7 @@ __global__ __launch_bounds__(256) void csm_round_kernel(CsmParams p) {
   auto vidx = [](int64_t t, int d) { return (size_t)(t >> 5) * kD * 32 + (size_t)d * 32 + (t & 31); };
 
   if (c < 0 || c >= nchunks) {
+    if (c < 0 && tid == 0 && p.out_len) p.out_len[bh] = p.n_out;
     // pass-through of the sinks (to the front) or the recent tokens (to the end)
     const int n = c < 0 ? p.n_sink : p.n_recent;
     const int64_t src0 = c < 0 ? 0 : p.n_in - p.n_recent, dst0 = c < 0 ? 0 : p.n_out - p.n_recent;

@@ -74,6 +74,7 @@ struct CsmParams {
   const float *in_deg;
   uint16_t *out_k, *out_v;
   float *out_deg;
+  int32_t *out_len;   // optional [BH]: set to n_out (the drafter's main_len)
 };
 int csm_survivors(int n_in, int n_sink, int n_recent, int chunk, double r);
 hipError_t launch_csm_round(const CsmParams &p, int BH, hipStream_t s);

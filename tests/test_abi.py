@@ -202,7 +202,7 @@ def test_csm_and_commit_validation_is_host_only(L):
         a = {**base, **kw}
         return L.vc_csm_round(a["B"], a["Hkv"], a["D"], a["n_in"], a["sink"], a["recent"], a["chunk"], a["r"],
                               a["ik"], a["iv"], a["ideg"], a["cap_in"], a["ok"], a["ov"], a["odeg"], a["cap_out"],
-                              ctypes.byref(n), None)
+                              ctypes.byref(n), None, None)
     assert csm(D=64) == vcb.VC_ENOTSUP
     assert csm(chunk=1) == vcb.VC_EINVAL
     assert csm(r=1.5) == vcb.VC_EINVAL
@@ -248,6 +248,42 @@ def test_csm_survivor_count_matches_oracle_on_many_shapes(L):
     for n_in, sink, recent, chunk, r in cases:
         cap = (n_in + 31) // 32 * 32
         st = L.vc_csm_round(0, 2, 128, n_in, sink, recent, chunk, r, None, None, None, cap, None, None, None, cap,
-                            ctypes.byref(n), None)
+                            ctypes.byref(n), None, None)
         assert st == vcb.VC_OK, (n_in, sink, recent, chunk, r, L.vc_last_error())
         assert n.value == C.survivors(n_in, sink, recent, chunk, r), (n_in, sink, recent, chunk, r)
+
+
+def test_centroid_schedule_functions_match_the_oracle(L):
+    # the library's CentroidKV schedule (when a round runs, with which ratio)
+    # drives the same sequence of rounds as the oracle's pipeline, on the
+    # hand-derived golden and on a longer run
+    import json
+    import numpy as np
+    from oracle import csm as C
+    for j in range(12):
+        for r_init, dr in ((1.0, 0.1), (0.75, 0.25), (0.5, 0.0), (1.2, 0.3)):
+            assert L.vc_csm_schedule_ratio(r_init, dr, j) == C.schedule_ratio(j, r_init, dr)
+    assert L.vc_csm_round_due(10, 5, 3, 0) == -1 and L.vc_csm_round_due(10, 5, -1, 4) == -1
+    g = json.load(open(os.path.join(ROOT, "tests", "golden", "centroid_schedule.json")))
+    for cfg, steps, n0 in ((g["config"], g["config"]["decode_steps"], g["config"]["n_prefill"]),
+                           (dict(n_sink=4, n_recent=32, chunk=32, budget=250, every=32, r_init=0.75, delta_r=0.125),
+                            160, 400)):
+        rng = np.random.default_rng(3)
+        k0, v0 = rng.standard_normal((n0, 8)), rng.standard_normal((n0, 8))
+        kn, vn = rng.standard_normal((steps, 8)), rng.standard_normal((steps, 8))
+        _, _, _, rounds = C.centroid_run(k0, v0, kn, vn, cfg["budget"], cfg["every"], cfg["r_init"], cfg["delta_r"],
+                                         cfg["n_sink"], cfg["n_recent"], cfg["chunk"])
+        # replay the schedule with the library's decisions and survivor counts
+        n, j, lib_rounds = n0, 0, []
+        for step in range(steps + 1):
+            if step > 0:
+                n += 1
+            if L.vc_csm_round_due(n, cfg["budget"], step, cfg["every"]) == 1:
+                r = L.vc_csm_schedule_ratio(cfg["r_init"], cfg["delta_r"], j)
+                cnt = ctypes.c_int32(-1)
+                cap = (n + 31) // 32 * 32
+                assert L.vc_csm_round(0, 1, 128, n, cfg["n_sink"], cfg["n_recent"], cfg["chunk"], r, None, None, None,
+                                      cap, None, None, None, cap, ctypes.byref(cnt), None, None) == vcb.VC_OK
+                lib_rounds.append((step, j, r, n, cnt.value))
+                n, j = cnt.value, j + 1
+        assert lib_rounds == [(rd["step"], rd["j"], rd["r"], rd["n_in"], rd["n_out"]) for rd in rounds]

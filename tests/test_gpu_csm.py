@@ -2,7 +2,9 @@
 oracle: on key sets with planted near-duplicates (every merge decision far
 from a tie) the survivor count and order, the degrees (exactly), the unmerged
 tokens (bit-exactly) and the centroids (bf16 tolerance) match; r = 0 copies;
-on plain random keys the degree and degree-weighted-sum invariants hold; and
+on plain random keys the degree and degree-weighted-sum invariants hold and
+every round is one of the valid results (matches and merged set within the
+fp32 cosine error of the exact ones, tests/csm_check.py); and
 the merged cache with its degrees feeds vc_draft_attn (attention over the
 oracle's merged cache with the log-degree term)."""
 import numpy as np
@@ -122,6 +124,24 @@ def test_random_keys_conserve_degree_and_weighted_sums():
             ws_in = (deg[b, h, :n_in, None] * bf16_to_f64(kb[b, h, :n_in])).sum(0)
             ws_out = (od[b, h, :n_out, None] * bf16_to_f64(ok[b, h, :n_out])).sum(0)
             np.testing.assert_allclose(ws_out, ws_in, rtol=0, atol=0.05 * np.abs(deg[b, h, :n_in]).sum() ** 0.5)
+
+
+@pytest.mark.parametrize("r,chunk", [(0.25, 64), (0.5, 64), (1.0, 37), (0.7, 20)])
+def test_random_keys_round_is_a_valid_round(r, chunk):
+    # generic keys: near-equal cosines may be ordered differently by the
+    # kernel's fp32 arithmetic, so the outputs are checked for being one of
+    # the correct results (tests/csm_check.py) rather than the oracle's
+    from .csm_check import check_round
+    B, Hkv, n_in = 2, 2, 600
+    k = S.normal_f32((B, Hkv, 608, D), 55, S.TID["k"])
+    v = S.normal_f32((B, Hkv, 608, D), 55, S.TID["v"])
+    kb, vb = S.f32_to_bf16_bits(k), S.f32_to_bf16_bits(v)
+    deg = S.degrees((B, Hkv, 608), 55)
+    n_out, ok, ov, od, _ = _run(kb, vb, deg, n_in, 4, 64, chunk, r, 608)
+    for b in range(B):
+        for h in range(Hkv):
+            check_round(kb[b, h, :n_in], vb[b, h, :n_in], deg[b, h, :n_in], 4, 64, chunk, r,
+                        ok[b, h, :n_out], ov[b, h, :n_out], od[b, h, :n_out])
 
 
 def test_merged_cache_feeds_draft_attention():
