@@ -394,12 +394,13 @@ def run_tiny(args):
 # ---------------------------------------------------------------------------
 # One request at 1M tokens (Mistral-24B layer shape), k = 40
 def run_long1m(args, t_start):
-    """Rounds of the 1M-token configuration: one request drafts k = 40 tokens over its int4 compressed cache
-    (packed blocks, resident in HBM) through every layer, then verifies the 41-row block layer by layer against
-    the full 1048576-token cache, each layer's 4 GiB streamed from pinned host memory through a two-slot ring
-    (the first two layers' copies overlap the drafting), then takes the LM head fused with the argmax and the
-    acceptance.  Acceptance is planted per round: full acceptance with the bonus, a first-position mismatch,
-    then n ~ U{24..40}."""
+    """Rounds of the 1M-token configuration, each enqueued natively by ``vc_stagger_round`` in its chained mode:
+    one request drafts k = 40 tokens over its int4 compressed cache (packed blocks, resident in HBM) through every
+    layer, then verifies the 41-row block layer by layer against the full 1048576-token cache, each layer's 4 GiB
+    streamed from pinned host memory through a six-slot ring whose first copies run during the drafting, then takes
+    the LM head fused with the argmax and the acceptance, and commits the verified rows to every layer's int4 cache
+    through its bf16 tail (full 32-token groups quantized on the device).  Acceptance is planted per round: full
+    acceptance with the bonus, a first-position mismatch, then n ~ U{24..40}."""
     import torch
     import lossless_speculative_decoding_vc_amd as vc
     import synthetic as S
@@ -407,8 +408,11 @@ def run_long1m(args, t_start):
     B, Hq, Hkv, D, N, k = 1, 32, 8, 128, 1048576, 40
     M, V, Dm = k + 1, 131072, 5120
     L, NLD = args.layers, min(args.distinct_layers, 4)
-    nb = N // 32
-    # int4 compressed caches (packed), NLD distinct layers
+    NSLOT = 6                     # 6 x 4 GiB staging ring: the link streams during the drafting
+    cap = N + 1024                # room for the verified tokens the rounds append
+    nb = cap // 32
+    tcap = 128                    # bf16 tail: < 32 committed rows + the k drafted ones
+    # int4 compressed caches (packed), NLD distinct buffers shared round-robin by the layers
     blks = []
     for i in range(NLD):
         blk = torch.empty((B, Hkv, nb, vc.INT4_PACKED_BLOCK), dtype=torch.uint8, device=dev)
@@ -421,11 +425,13 @@ def run_long1m(args, t_start):
             blk[..., 4352 + 512 * j:4608 + 512 * j] = (sc.float() * -7.5).half().view(torch.uint8)
         blks.append(blk)
     dq = [_bf16_randn((B, Hq, D), 320 + i, dev) for i in range(NLD)]
-    tail_k = _bf16_randn((B, Hkv, k, D), 330, dev)
-    tail_v = _bf16_randn((B, Hkv, D, k), 331, dev)
-    taillen = [torch.full((B,), i, dtype=torch.int32, device=dev) for i in range(k + 1)]
-    ml = torch.full((B, Hkv), N, dtype=torch.int32, device=dev)
-    dout = torch.empty((B, Hq, D), dtype=torch.bfloat16, device=dev)
+    # per layer: its int4 length, its bf16 tail (residual committed rows, then the drafted ones) and tail length
+    main_len = [torch.full((B, Hkv), N, dtype=torch.int32, device=dev) for _ in range(L)]
+    tail_k = [_bf16_randn((B, Hkv, tcap, D), 330, dev) for _ in range(L)]
+    tail_v = [_bf16_randn((B, Hkv, D, tcap), 331, dev) for _ in range(L)]
+    tail_len = [torch.zeros(B, dtype=torch.int32, device=dev) for _ in range(L)]
+    steps_tl = torch.arange(tcap + 1, dtype=torch.int32, device=dev)   # views [j:j+1] hold tail length j
+    douts = torch.empty((B, Hq, D), dtype=torch.bfloat16, device=dev)
     dws = vc.new_workspace(1 << 26, dev)
     vq = [_bf16_randn((B, M, Hq, D), 340 + i, dev) for i in range(NLD)]
     bk = _bf16_randn((B, Hkv, M, D), 350, dev)
@@ -437,26 +443,30 @@ def run_long1m(args, t_start):
     lws_d = vc.lm_head_argmax_workspace(B, V, dev)
     lws_v = vc.lm_head_argmax_workspace(B * M, V, dev)
     drafts = torch.zeros((B, k), dtype=torch.int32, device=dev)
+    am = torch.empty((B, M), dtype=torch.int32, device=dev)
+    n_acc = torch.empty(B, dtype=torch.int32, device=dev)
+    toks = torch.empty((B, M), dtype=torch.int32, device=dev)
+    n_out = torch.empty(B, dtype=torch.int32, device=dev)
     half = B * Hkv * N * D * 2
     slot_bytes = 2 * half   # 4 GiB: K then channel-major V
-    slots = [torch.empty(slot_bytes, dtype=torch.uint8, device=dev) for _ in range(2)]
+    slots = [torch.empty(slot_bytes, dtype=torch.uint8, device=dev) for _ in range(NSLOT)]
     g = torch.Generator(device=dev)
     g.manual_seed(353)
     slots[0].view(torch.bfloat16).normal_(0.0, 1.0, generator=g)
     pool = [torch.empty(slot_bytes, dtype=torch.uint8, pin_memory=True) for _ in range(2)]
     for pbuf in pool:
         pbuf.copy_(slots[0])
+    host_kv = [pool[l % 2] for l in range(L)]
     stg = vc.Stagger(slots, slot_bytes, L)
     ds, vs = torch.cuda.Stream(), torch.cuda.Stream()
+    verify = [vc.verify_args(vq[l % NLD], None, None, ctx_len, bk, bv, vout, workspace=vws, ccap=N)
+              for l in range(L)]
+    commit = [dict(int4=True, tail_k=tail_k[l], tail_v=tail_v[l], tail_len=tail_len[l], packed=blks[l % NLD],
+                   main_len=main_len[l]) for l in range(L)]
     torch.cuda.synchronize()
-    log(f"long1m setup done in {time.time() - t_start:.1f} s ({L} layers)")
-
-    def views(ptr):
-        base = slots[0] if ptr == slots[0].data_ptr() else slots[1]
-        return (base[:half].view(torch.bfloat16).view(B, Hkv, N, D),
-                base[half:].view(torch.bfloat16).view(B, Hkv, D, N))
-
+    log(f"long1m setup done in {time.time() - t_start:.1f} s ({L} layers, {NSLOT}-slot ring)")
     timers = {"draft": [], "verify": []}
+    resid = [0]   # committed rows waiting in every layer's tail (the same for all layers)
 
     def run_round(r, timed):
         force = {0: k} if r % 3 == 0 else ({0: 0} if r % 3 == 1 else {})
@@ -465,44 +475,29 @@ def run_long1m(args, t_start):
         dt_ = torch.from_numpy(d.astype(np.int64)).to(dev)
         hv = W[yt.reshape(-1)].contiguous().view(B, M, Dm)
         hd = [W[dt_[:, i]].contiguous() for i in range(k)]
+        rr = resid[0]
+        draft = [vc.draft_args(dq[l % NLD], blks[l % NLD], None, main_len[l], tail_k=tail_k[l], tail_v=tail_v[l],
+                               tail_len=steps_tl[rr + 1:rr + 2], out=douts, workspace=dws, fmt=vc.VC_KV_INT4_PACKED)
+                 for l in range(L)]
         torch.cuda.synchronize()
         t0 = time.time()
-        stg.stream_layer(0, pool[0], slot_bytes)
-        if L > 1:
-            stg.stream_layer(1, pool[1], slot_bytes)
-        for i in range(k):
-            for l in range(L):
-                ev = None
-                if timed and l == 0:
-                    ev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-                    ev[0].record(ds)
-                vc.draft_attn(dq[l % NLD], blks[l % NLD], None, ml, tail_k=tail_k, tail_v=tail_v,
-                              tail_len=taillen[i + 1], out=dout, workspace=dws, fmt=vc.VC_KV_INT4_PACKED, stream=ds)
-                if ev is not None:
-                    ev[1].record(ds)
-                    timers["draft"].append(ev)
-            vc.lm_head_argmax(hd[i], W, out=drafts.view(-1)[i:], out_stride=k, workspace=lws_d, stream=ds)
-        vs.wait_stream(ds)   # the block holds the drafted tokens
-        for l in range(L):
-            ptr = stg.acquire(l, vs)
-            kk, vv = views(ptr)
-            ev = None
-            if timed:
-                ev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-                ev[0].record(vs)
-            vc.verify_attn(vq[l % NLD], kk, vv, ctx_len, bk, bv, out=vout, workspace=vws, stream=vs)
-            if ev is not None:
-                ev[1].record(vs)
-                timers["verify"].append(ev)
-            stg.release(l, vs)
-            if l + 2 < L:
-                stg.stream_layer(l + 2, pool[l % 2], slot_bytes)
-        am, n_acc, toks, n_out = vc.lm_head_accept(hv, W, drafts, workspace=lws_v, stream=vs)
+        stg.round(L, vc.ROUND_CHAINED, W, draft=draft, step_tail_len=[steps_tl[rr + i + 1:rr + i + 2] for i in range(k)],
+                  draft_hidden=hd, drafts=drafts, draft_lm_ws=lws_d, verify=verify, host_kv=host_kv,
+                  kv_bytes=slot_bytes, v_offset=half, verify_hidden=hv, verify_drafts=drafts, argmax=am,
+                  accept_len=n_acc, out_tokens=toks, n_out=n_out, verify_lm_ws=lws_v, commit=commit,
+                  time_kernels=timed, draft_stream=ds, verify_stream=vs)
         torch.cuda.synchronize()
         stg.sync()
         dt = time.time() - t0
+        if timed:
+            d_ms, v_ms = stg.round_times()
+            timers["draft"] += [ms / L for ms in d_ms]
+            timers["verify"] += v_ms
+        n_out_h = int(n_out.cpu()[0])
+        resid[0] = (rr + n_out_h) % 32
         ok = bool(np.array_equal(n_acc.cpu().numpy(), n)) and bool(np.array_equal(drafts.cpu().numpy(), d))
-        return int(n_out.sum().item()), dt, ok, int(n[0])
+        ok &= all(int(t.cpu()[0]) == resid[0] for t in tail_len)
+        return n_out_h, dt, ok, int(n[0])
 
     for w in range(args.warmup):
         run_round(w, False)
@@ -515,15 +510,18 @@ def run_long1m(args, t_start):
         pattern.append(n0)
         log(f"long1m round {s_}: {dt:.2f} s, accepted {n0}, emitted {v}, parity {ok}")
     copy_ms = [stg.copy_ms(l) for l in range(L)]
+    grown = int(main_len[0].cpu().max()) - N
     stg.close()
-    d_us = float(np.mean([e[0].elapsed_time(e[1]) for e in timers["draft"]])) * 1e3
-    v_us = float(np.mean([e[0].elapsed_time(e[1]) for e in timers["verify"]])) * 1e3
+    d_us = float(np.mean(timers["draft"])) * 1e3
+    v_us = float(np.mean(timers["verify"])) * 1e3
     d_bytes = B * Hkv * N * 160 + B * Hkv * k / 2 * D * 4 + 2 * B * Hq * D * 2
     v_bytes = B * Hkv * (N + M) * D * 4 + 2 * B * M * Hq * D * 2
     v_flops = 4.0 * D * Hq * B * sum(N + i + 1 for i in range(M))
+    pcie = slot_bytes / (np.mean(copy_ms) * 1e-3) / 1e9
     return {"value": verified / total_s, "ms_per_step": total_s / args.steps * 1e3, "parity_ok": parity_ok,
-            "accepted_per_round": pattern, "layers": L,
-            "pcie_h2d_gbs": slot_bytes / (np.mean(copy_ms) * 1e-3) / 1e9,
+            "accepted_per_round": pattern, "layers": L, "slots": NSLOT,
+            "pcie_h2d_gbs": pcie, "round_floor_ms": L * slot_bytes / (pcie * 1e9) * 1e3,
+            "int4_tokens_appended": grown,
             "draft_avg_us": d_us, "draft_gbs": d_bytes / d_us / 1e3, "verify_avg_us": v_us,
             "verify_tflops": v_flops / v_us / 1e6, "verify_gbs": v_bytes / v_us / 1e3,
             "d_bytes": d_bytes, "v_flops": v_flops}
@@ -898,7 +896,9 @@ def main():
             "config": {"workload": "1M-token long context, Mistral-24B layer shape: one request, 32 q / 8 KV heads, "
                                    "head_dim 128; drafts k=40 over int4 (packed) compressed KV of 1048576 tokens in "
                                    "HBM, verifies the 41-row block against the full bf16 cache streamed per layer "
-                                   "(4 GiB) from pinned host memory; 5120x131072 LM head; planted acceptance",
+                                   "(4 GiB) from pinned host memory through a 6-slot ring; 5120x131072 LM head; "
+                                   "planted acceptance; verified rows committed to the int4 caches through bf16 "
+                                   "tails (full 32-token groups quantized on the device)",
                        "layers": r["layers"], "context": 1048576, "k": 40,
                        "step": "one round (k draft steps through every layer, then the verify pass)"},
             "roofline": {"bound": "hbm", "achieved": r["draft_gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -909,6 +909,8 @@ def main():
                        "mfma_frac": r["verify_tflops"] / MFMA_BF16_PEAK_TFLOPS, "hbm_gbs": r["verify_gbs"],
                        "hbm_frac": r["verify_gbs"] / HBM_PEAK_GBS, "flops_per_launch": r["v_flops"]},
             "pcie_h2d_gbs": r["pcie_h2d_gbs"], "accepted_per_round": r["accepted_per_round"],
+            "round_floor_ms": r["round_floor_ms"], "frac_of_pcie_floor": r["round_floor_ms"] / r["ms_per_step"],
+            "slots": r["slots"], "int4_tokens_appended": r["int4_tokens_appended"],
             "parity_planted_accept": r["parity_ok"],
         }
         print(json.dumps(out))

@@ -284,6 +284,28 @@ vc_status vc_quantize_int4(int32_t B, int32_t Hkv, int32_t D, const void *src_k,
                            const int32_t *dst_start, void *k_codes, void *k_scale, void *k_zero, void *v_codes,
                            void *v_scale, void *v_zero, void *stream);
 
+/* Commit of verified rows into a packed int4 cache through its bf16 tail
+ * ("Algoritmo Principale", step 3, with the quantizing drafter of "Supporto
+ * Architetturale"): int4 groups span 32 tokens, so verified rows wait in a
+ * bf16 tail -- the tail segment vc_draft_attn reads after the int4 main
+ * segment -- until a whole group is there.  Per request b and KV head h:
+ *   rows = tail[0 .. tail_len[b]) followed by the block's first n_out[b]
+ *   rows (at most M, and only as many as fit tcap); its full 32-token groups
+ *   are quantized (exactly as vc_quantize_int4_packed) into the packed cache
+ *   at token main_len[b][h], which advances by their tokens; the remaining
+ *   rows (< 32) move to the front of the tail and tail_len[b] becomes their
+ *   count.  When the cache has no room for all the groups of a (b, h) (or
+ *   main_len is not a multiple of 32) they are dropped and main_len stays.
+ *   blk_k [B][Hkv][M][D], blk_v [B][Hkv][D][M] bf16 (the verify block);
+ *   n_out [B] (device); tail_k [B][Hkv][tcap][D], tail_v [B][Hkv][D][tcap]
+ *   bf16; tail_len [B] (device, in/out); packed u8 [B][Hkv][cap/32][5120];
+ *   main_len [B][Hkv] (device, in/out).
+ * D = 128; cap % 32 == 0; tcap >= 32 (tcap >= 31 + M keeps every row);
+ * buffers 16-byte aligned.  Three launches on `stream`, no host round trip.  */
+vc_status vc_int4_commit(int32_t B, int32_t Hkv, int32_t D, int32_t M, const void *blk_k, const void *blk_v,
+                         const int32_t *n_out, void *tail_k, void *tail_v, int64_t tcap, int32_t *tail_len,
+                         void *packed, int64_t cap, int32_t *main_len, void *stream);
+
 /* The same quantization into the interleaved fmt = VC_KV_INT4_PACKED cache:
  * packed u8 [B][Hkv][cap/32][5120] (block layout as in vc_draft_args).
  * Arguments, decisions and errors as vc_quantize_int4.                      */
@@ -397,7 +419,11 @@ vc_status vc_stagger_destroy(vc_stagger *s);
  * run while the drafting cohort computes; VC_ROUND_BULK is the
  * bulk-synchronous comparison: every draft step first, and the copy and
  * verify streams wait for them.  Both modes run the same kernels on the same
- * inputs, so their outputs are identical bit for bit.
+ * inputs, so their outputs are identical bit for bit.  VC_ROUND_CHAINED is
+ * one cohort in both roles (a long context: "Supporto Architetturale"):
+ * the verify stream waits for the draft steps, since it verifies the drafts
+ * they write (verify_drafts may be drafts), while the copies of the first
+ * layers already stream during the drafting.
  * Every argument of every call is validated before anything is enqueued; on
  * VC_EINVAL nothing was enqueued (VC_EHIP: a launch failed part-way; the
  * caller synchronizes and discards the round).  The call returns without
@@ -410,14 +436,24 @@ vc_status vc_stagger_destroy(vc_stagger *s);
  * on draft_stream), and so may the verify calls.                            */
 #define VC_ROUND_STAGGERED 0
 #define VC_ROUND_BULK 1
+#define VC_ROUND_CHAINED 2
+
+#define VC_COMMIT_ROWS 0          /* vc_commit_rows into a dense cache               */
+#define VC_COMMIT_INT4_TAIL 1     /* vc_int4_commit into a packed int4 cache         */
 
 typedef struct vc_round_commit {
-  void    *dst_k, *dst_v;         /* the layer's cache the rows go to (vc_commit_rows) */
-  int32_t *len;                   /* [Bv][Hkv], advanced by n_out                    */
-  float   *degree;                /* optional merge degrees (appended rows get 1)    */
-  int64_t  degree_h_stride;       /* 0 or cap                                        */
-  int64_t  cap;
-  int32_t  dst_v_blocked;         /* 1: a compressed main segment, 0: a full cache   */
+  int32_t  kind;                  /* VC_COMMIT_ROWS or VC_COMMIT_INT4_TAIL           */
+  void    *dst_k, *dst_v;         /* ROWS: the layer's cache the rows go to          */
+  int32_t *len;                   /* ROWS: [Bv][Hkv], advanced by n_out              */
+  float   *degree;                /* ROWS: optional merge degrees (appended rows: 1) */
+  int64_t  degree_h_stride;       /* ROWS: 0 or cap                                  */
+  int64_t  cap;                   /* ROWS: dense capacity; INT4_TAIL: int4 capacity  */
+  int32_t  dst_v_blocked;         /* ROWS: 1 a compressed main segment, 0 full cache */
+  void    *tail_k, *tail_v;       /* INT4_TAIL: the bf16 tail and its capacity       */
+  int64_t  tcap;
+  int32_t *tail_len;              /* INT4_TAIL: [Bv] (in/out)                        */
+  void    *packed;                /* INT4_TAIL: [Bv][Hkv][cap/32][5120]              */
+  int32_t *main_len;              /* INT4_TAIL: [Bv][Hkv] (in/out)                   */
   void    *host_k, *host_v;       /* optional pinned destinations of the block rows  */
 } vc_round_commit;
 
@@ -426,7 +462,7 @@ typedef void (*vc_round_hook)(void *ctx, int32_t layer, void *verify_stream);
 typedef struct vc_round_desc {
   int32_t layers;                 /* 1 .. the stagger object's max_layers            */
   int32_t steps;                  /* draft steps (0: no drafting cohort)             */
-  int32_t mode;                   /* VC_ROUND_STAGGERED or VC_ROUND_BULK             */
+  int32_t mode;                   /* VC_ROUND_STAGGERED, _BULK or _CHAINED           */
   /* LM head of the model, vocab-major [V][Dm] bf16 */
   const void *lm_w;
   int32_t Dm, V;

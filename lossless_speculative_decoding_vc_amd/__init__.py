@@ -72,8 +72,9 @@ class AcceptArgs(ctypes.Structure):
 
 
 class RoundCommit(ctypes.Structure):
-    _fields_ = [("dst_k", _p), ("dst_v", _p), ("len", _p), ("degree", _p), ("degree_h_stride", _i64),
-                ("cap", _i64), ("dst_v_blocked", _i32), ("host_k", _p), ("host_v", _p)]
+    _fields_ = [("kind", _i32), ("dst_k", _p), ("dst_v", _p), ("len", _p), ("degree", _p), ("degree_h_stride", _i64),
+                ("cap", _i64), ("dst_v_blocked", _i32), ("tail_k", _p), ("tail_v", _p), ("tcap", _i64),
+                ("tail_len", _p), ("packed", _p), ("main_len", _p), ("host_k", _p), ("host_v", _p)]
 
 
 ROUND_HOOK = ctypes.CFUNCTYPE(None, _p, _i32, _p)
@@ -93,7 +94,8 @@ class RoundDesc(ctypes.Structure):
                 ("time_kernels", _i32)]
 
 
-ROUND_STAGGERED, ROUND_BULK = 0, 1
+ROUND_STAGGERED, ROUND_BULK, ROUND_CHAINED = 0, 1, 2
+COMMIT_ROWS, COMMIT_INT4_TAIL = 0, 1
 
 _lib = None
 
@@ -136,6 +138,8 @@ def lib():
         L.vc_compact_kv.argtypes = [_i32, _i32, _i32, _i32, _p, _p, _i64, _p, _i64, _p, _p, _p, _i64, _p, _p]
         L.vc_compact_kv.restype = ctypes.c_int
         L.vc_quantize_int4_packed.argtypes = [_i32, _i32, _i32, _p, _p, _i64, _p, _i32, _i64, _p, _p, _p]
+        L.vc_int4_commit.argtypes = [_i32, _i32, _i32, _i32, _p, _p, _p, _p, _p, _i64, _p, _p, _i64, _p, _p]
+        L.vc_int4_commit.restype = ctypes.c_int
         L.vc_quantize_int4_packed.restype = ctypes.c_int
         L.vc_csm_round.argtypes = [_i32, _i32, _i32, _i32, _i32, _i32, _i32, ctypes.c_double, _p, _p, _p, _i64,
                                    _p, _p, _p, _i64, ctypes.POINTER(_i32), _p, _p]
@@ -727,6 +731,33 @@ def quantize_int4_packed(src_k, src_v, src_start, n_groups, dst_start, packed, s
                                          int(n_groups), cap, _ptr(dst_start), _ptr(packed), _stream(stream)))
 
 
+def int4_commit(blk_k, blk_v, n_out, tail_k, tail_v, tail_len, packed, main_len, stream=None):
+    """Commit verified rows into a packed int4 cache through its bf16 tail
+    (``vc_int4_commit``): ``blk_k [B][Hkv][M][D]``, ``blk_v [B][Hkv][D][M]``,
+    ``n_out`` int32 ``[B]``, ``tail_k [B][Hkv][tcap][D]``, ``tail_v
+    [B][Hkv][D][tcap]`` (bf16), ``tail_len`` int32 ``[B]`` (in/out),
+    ``packed [B][Hkv][cap/32][5120]`` uint8, ``main_len`` int32 ``[B][Hkv]``
+    (in/out)."""
+    if blk_k.dim() != 4 or tail_k.dim() != 4 or packed.dim() != 4:
+        raise ValueError("blk_k, tail_k and packed are 4-dimensional")
+    B, Hkv, M, D = blk_k.shape
+    tcap = tail_k.shape[2]
+    bf = (torch.bfloat16,)
+    _want(blk_k, "blk_k", (B, Hkv, M, D), bf)
+    _want(blk_v, "blk_v", (B, Hkv, D, M), bf)
+    _want(n_out, "n_out", (B,), (torch.int32,))
+    _want(tail_k, "tail_k", (B, Hkv, tcap, D), bf)
+    _want(tail_v, "tail_v", (B, Hkv, D, tcap), bf)
+    _want(tail_len, "tail_len", (B,), (torch.int32,))
+    _want(packed, "packed", (B, Hkv, packed.shape[2], INT4_PACKED_BLOCK), (torch.uint8,))
+    _want(main_len, "main_len", (B, Hkv), (torch.int32,))
+    for t, n in ((blk_k, "blk_k"), (blk_v, "blk_v"), (n_out, "n_out"), (tail_k, "tail_k"), (tail_v, "tail_v"),
+                 (tail_len, "tail_len"), (packed, "packed"), (main_len, "main_len")):
+        _dev(t, n)
+    _check(lib().vc_int4_commit(B, Hkv, D, M, _ptr(blk_k), _ptr(blk_v), _ptr(n_out), _ptr(tail_k), _ptr(tail_v), tcap,
+                                _ptr(tail_len), _ptr(packed), packed.shape[2] * 32, _ptr(main_len), _stream(stream)))
+
+
 def csm_round(in_k, in_v, n_in, n_sink, n_recent, chunk, r, out_k, out_v, out_deg, in_deg=None, out_len=None,
               stream=None):
     """One Chunked Soft Matching round (``vc_csm_round``); returns the survivor count.
@@ -817,8 +848,11 @@ class Stagger:
         tensors (the layer's full K then V; V at ``v_offset``),
         ``verify_hidden`` bf16 ``[Bv][M][Dm]``, ``verify_drafts`` int32
         ``[Bv][M-1]`` and the acceptance outputs of :func:`lm_head_accept`.
-        ``commit``: list over layers of dicts (``dst_k, dst_v, length, degree,
-        v_blocked, host_k, host_v``).  ``before_verify(layer, stream_ptr)`` is
+        ``commit``: list over layers of dicts, either rows into a dense cache
+        (``dst_k, dst_v, length, degree, v_blocked``) or, with ``int4=True``,
+        rows into a packed int4 cache through its bf16 tail (``tail_k, tail_v,
+        tail_len, packed, main_len``, as :func:`int4_commit`); both may add
+        ``host_k, host_v`` (pinned write-back of the block rows).  ``before_verify(layer, stream_ptr)`` is
         called on the host before each verify is enqueued.  ``time_kernels``
         times each draft step's run of draft attention calls and every verify
         call (:meth:`round_times`).  ``lm_w`` is the
@@ -897,10 +931,33 @@ class Stagger:
                     raise ValueError("commit needs one entry per layer")
                 cs = (RoundCommit * layers)()
                 for l, c in enumerate(commit):
-                    dk, dv, ln, deg = c["dst_k"], c["dst_v"], c["length"], c.get("degree")
-                    blocked = bool(c.get("v_blocked", False))
                     vb = verify[l]
                     Bc, Hkv, D = vb.B, vb.Hkv, vb.D
+                    blk_bytes = Bc * Hkv * vb.M * D * (2 if vb.dtype == VC_BF16 else 4)
+                    for n in ("host_k", "host_v"):
+                        t = c.get(n)
+                        if t is not None and (t.is_cuda or not t.is_pinned()
+                                              or t.numel() * t.element_size() < blk_bytes):
+                            raise ValueError(f"commit[{l}].{n} must be pinned host memory of >= {blk_bytes} bytes")
+                    cs[l].host_k, cs[l].host_v = _ptr(c.get("host_k")), _ptr(c.get("host_v"))
+                    if c.get("int4"):
+                        tk, tv, tl, pk, ml = c["tail_k"], c["tail_v"], c["tail_len"], c["packed"], c["main_len"]
+                        tcap = tk.shape[2]
+                        bf = (torch.bfloat16,)
+                        _want(tk, f"commit[{l}].tail_k", (Bc, Hkv, tcap, D), bf)
+                        _want(tv, f"commit[{l}].tail_v", (Bc, Hkv, D, tcap), bf)
+                        _want(tl, f"commit[{l}].tail_len", (Bc,), (torch.int32,))
+                        _want(pk, f"commit[{l}].packed", (Bc, Hkv, pk.shape[2], INT4_PACKED_BLOCK), (torch.uint8,))
+                        _want(ml, f"commit[{l}].main_len", (Bc, Hkv), (torch.int32,))
+                        for t, n in ((tk, "tail_k"), (tv, "tail_v"), (tl, "tail_len"), (pk, "packed"), (ml, "main_len")):
+                            _dev(t, f"commit[{l}].{n}")
+                        cs[l].kind = COMMIT_INT4_TAIL
+                        cs[l].tail_k, cs[l].tail_v, cs[l].tcap = _ptr(tk), _ptr(tv), tcap
+                        cs[l].tail_len, cs[l].packed, cs[l].main_len = _ptr(tl), _ptr(pk), _ptr(ml)
+                        cs[l].cap = pk.shape[2] * 32
+                        continue
+                    dk, dv, ln, deg = c["dst_k"], c["dst_v"], c["length"], c.get("degree")
+                    blocked = bool(c.get("v_blocked", False))
                     cap = dk.shape[2]
                     want_dt = torch.bfloat16 if vb.dtype == VC_BF16 else torch.float32
                     _want(dk, f"commit[{l}].dst_k", (Bc, Hkv, cap, D), (want_dt,))
@@ -913,17 +970,11 @@ class Stagger:
                         _want(deg, f"commit[{l}].degree", (Bc, deg.shape[1], cap), (torch.float32,))
                     for t, n in ((dk, "dst_k"), (dv, "dst_v"), (ln, "length"), (deg, "degree")):
                         _dev(t, f"commit[{l}].{n}")
-                    blk_bytes = Bc * Hkv * vb.M * D * (2 if vb.dtype == VC_BF16 else 4)
-                    for n in ("host_k", "host_v"):
-                        t = c.get(n)
-                        if t is not None and (t.is_cuda or not t.is_pinned()
-                                              or t.numel() * t.element_size() < blk_bytes):
-                            raise ValueError(f"commit[{l}].{n} must be pinned host memory of >= {blk_bytes} bytes")
+                    cs[l].kind = COMMIT_ROWS
                     cs[l].dst_k, cs[l].dst_v, cs[l].len = _ptr(dk), _ptr(dv), _ptr(ln)
                     cs[l].degree = _ptr(deg)
                     cs[l].degree_h_stride = 0 if deg is None or deg.shape[1] == 1 else cap
                     cs[l].cap, cs[l].dst_v_blocked = cap, 1 if blocked else 0
-                    cs[l].host_k, cs[l].host_v = _ptr(c.get("host_k")), _ptr(c.get("host_v"))
                 keep.append(cs)
                 d.commit = ctypes.cast(cs, ctypes.POINTER(RoundCommit))
         if before_verify is not None:

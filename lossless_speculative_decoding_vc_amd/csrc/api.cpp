@@ -391,6 +391,39 @@ vc_status vc_quantize_int4_packed(int32_t B, int32_t Hkv, int32_t D, const void 
   return hip_status(vc::launch_quantize_int4(p, n_groups, (hipStream_t)stream), "vc_quantize_int4_packed launch");
 }
 
+}  // extern "C"
+
+namespace vc {
+vc_status check_int4_commit(int32_t B, int32_t Hkv, int32_t D, int32_t M, int32_t dtype, const void *blk_k,
+                            const void *blk_v, const int32_t *n_out, const void *tail_k, const void *tail_v,
+                            int64_t tcap, const int32_t *tail_len, const void *packed, int64_t cap,
+                            const int32_t *main_len) {
+  REQ(B >= 0 && Hkv >= 1 && M >= 1 && cap >= 0 && tcap >= 32, "bad int4 commit shape (tcap >= 32, M >= 1)");
+  if (D != 128 || dtype != VC_BF16) return fail(VC_ENOTSUP, "the int4 cache is compiled for bf16, head_dim 128");
+  REQ(cap % 32 == 0 && cap <= kMaxTokens && tcap <= kMaxTokens, "cap must be a multiple of 32; caps <= 2^30");
+  REQ(tcap / 32 <= 65535, "tcap above 65535 groups");
+  REQ((int64_t)B * Hkv <= 65535, "at most 65535 (request, KV head) slices per call");
+  if (B == 0) return VC_OK;
+  REQ(blk_k && blk_v && n_out && tail_k && tail_v && tail_len && packed && main_len, "null pointer");
+  REQ(aligned16(blk_k) && aligned16(blk_v) && aligned16(tail_k) && aligned16(tail_v) && aligned16(packed),
+      "K/V, tail and packed buffers must be 16-byte aligned");
+  return VC_OK;
+}
+}  // namespace vc
+
+extern "C" {
+
+vc_status vc_int4_commit(int32_t B, int32_t Hkv, int32_t D, int32_t M, const void *blk_k, const void *blk_v,
+                         const int32_t *n_out, void *tail_k, void *tail_v, int64_t tcap, int32_t *tail_len,
+                         void *packed, int64_t cap, int32_t *main_len, void *stream) {
+  vc_status st = vc::check_int4_commit(B, Hkv, D, M, VC_BF16, blk_k, blk_v, n_out, tail_k, tail_v, tcap, tail_len,
+                                       packed, cap, main_len);
+  if (st != VC_OK || B == 0) return st;
+  return hip_status(vc::launch_int4_commit(B, Hkv, M, blk_k, blk_v, n_out, tail_k, tail_v, tcap, tail_len, packed,
+                                           cap, main_len, (hipStream_t)stream),
+                    "vc_int4_commit launch");
+}
+
 vc_status vc_csm_round(int32_t B, int32_t Hkv, int32_t D, int32_t n_in, int32_t n_sink, int32_t n_recent,
                        int32_t chunk, double r, const void *in_k, const void *in_v, const float *in_deg,
                        int64_t cap_in, void *out_k, void *out_v, float *out_deg, int64_t cap_out, int32_t *n_out,

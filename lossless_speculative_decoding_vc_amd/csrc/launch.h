@@ -5,6 +5,8 @@
 
 #include "../../include/vc.h"
 
+#define VC_DEVICE_HOST_INLINE __host__ __device__ inline
+
 namespace vc {
 
 // Launch plan of a split attention call: `splits` partial results per
@@ -26,6 +28,10 @@ vc_status check_lm_argmax(int32_t R, int32_t Dm, int32_t V, const void *h, const
 vc_status check_commit(int32_t B, int32_t Hkv, int32_t D, int32_t M, int32_t dtype, int64_t cap, int32_t dst_v_blocked,
                        const void *blk_k, const void *blk_v, const int32_t *n_out, const void *dst_k,
                        const void *dst_v, const int32_t *len, const float *degree, int64_t degree_h_stride);
+vc_status check_int4_commit(int32_t B, int32_t Hkv, int32_t D, int32_t M, int32_t dtype, const void *blk_k,
+                            const void *blk_v, const int32_t *n_out, const void *tail_k, const void *tail_v,
+                            int64_t tcap, const int32_t *tail_len, const void *packed, int64_t cap,
+                            const int32_t *main_len);
 vc_status set_error(vc_status s, const char *msg);
 
 hipError_t launch_accept(const vc_accept_args &a, hipStream_t s);
@@ -62,7 +68,24 @@ struct QuantParams {
   uint8_t *k_codes, *v_codes;
   uint16_t *k_scale, *k_zero, *v_scale, *v_zero;
   int code_bs, par_bs;   // bytes per block: codes, scales/zeros
+  // tail mode (vc_int4_commit): when tail_len is set, slice bh quantizes the
+  // full groups of its bf16 tail after the append of n_add[b] rows, from
+  // token 0 of the tail to dst_start[bh]; the grid's group count is a bound
+  const int32_t *tail_len = nullptr, *n_add = nullptr;
+  int Hkv = 1, M = 0;
 };
+
+// Rows of a request's bf16 tail after appending n_out of a block of M rows:
+// the length clamped to [0, tcap], then at most M rows, at most up to tcap.
+VC_DEVICE_HOST_INLINE int tail_total(int tail_len, int n_out, int M, int64_t tcap) {
+  const int L = tail_len < 0 ? 0 : (tail_len > tcap ? (int)tcap : tail_len);
+  int n = n_out < 0 ? 0 : (n_out > M ? M : n_out);
+  if (n > tcap - L) n = (int)(tcap - L);
+  return L + n;
+}
+hipError_t launch_int4_commit(int B, int Hkv, int M, const void *blk_k, const void *blk_v, const int32_t *n_out,
+                              void *tail_k, void *tail_v, int64_t tcap, int32_t *tail_len, void *packed,
+                              int64_t cap, int32_t *main_len, hipStream_t s);
 hipError_t launch_quantize_int4(const QuantParams &p, int n_groups, hipStream_t s);
 
 // One Chunked Soft Matching round (see csm.hip).

@@ -89,8 +89,21 @@ __global__ __launch_bounds__(256) void quantize_int4(QuantParams p) {
   __shared__ uint8_t vcode[D][kGroup];
   const int grp = blockIdx.x, bh = blockIdx.y;
   const int tid = threadIdx.x;
-  const int s0 = p.src_start[bh], d0 = p.dst_start[bh];
-  const int64_t span = (int64_t)gridDim.x * kGroup;   // tokens of the whole call per (b, KV head)
+  int s0, d0;
+  int64_t span;   // tokens of the whole call per (b, KV head)
+  if (p.tail_len) {
+    // tail mode: the full groups of the slice's tail once n_add rows are appended
+    const int b = bh / p.Hkv;
+    const int g = tail_total(p.tail_len[b], p.n_add[b], p.M, p.src_cap) / kGroup;
+    if (grp >= g) return;
+    s0 = 0;
+    d0 = p.dst_start[bh];
+    span = (int64_t)g * kGroup;
+  } else {
+    s0 = p.src_start[bh];
+    d0 = p.dst_start[bh];
+    span = (int64_t)gridDim.x * kGroup;
+  }
   // every workgroup of a (b, KV head) sees the same starts, so a slice whose
   // call would leave the source or the cache is skipped as a whole
   if (s0 < 0 || d0 < 0 || (d0 % kGroup) != 0 || s0 + span > p.src_cap || d0 + span > p.cap) return;

@@ -45,7 +45,8 @@ vc_status validate(const vc_stagger *s, const vc_round_desc *d) {
   if (L < 1 || L > (int)s->copied.size())
     return bad("layers must lie in 1.." + std::to_string(s->copied.size()) + " (got " + std::to_string(L) + ")");
   if (k < 0) return bad("steps must be >= 0");
-  if (d->mode != VC_ROUND_STAGGERED && d->mode != VC_ROUND_BULK) return bad("unknown round mode");
+  if (d->mode != VC_ROUND_STAGGERED && d->mode != VC_ROUND_BULK && d->mode != VC_ROUND_CHAINED)
+    return bad("unknown round mode");
   if ((k > 0 || d->verify) && !d->lm_w) return bad("lm_w is required");
   if (k > 0) {
     if (!d->draft || !d->draft_hidden || !d->drafts) return bad("a drafting cohort needs draft, draft_hidden, drafts");
@@ -84,9 +85,17 @@ vc_status validate(const vc_stagger *s, const vc_round_desc *d) {
       if (st != VC_OK) return st;
       if (d->commit) {
         const vc_round_commit &c = d->commit[l];
-        st = with_layer(vc::check_commit(a.B, a.Hkv, a.D, a.M, a.dtype, c.cap, c.dst_v_blocked, a.blk_k, a.blk_v,
-                                         d->n_out, c.dst_k, c.dst_v, c.len, c.degree, c.degree_h_stride),
-                        "commit layer", l);
+        if (c.kind == VC_COMMIT_ROWS) {
+          st = with_layer(vc::check_commit(a.B, a.Hkv, a.D, a.M, a.dtype, c.cap, c.dst_v_blocked, a.blk_k, a.blk_v,
+                                           d->n_out, c.dst_k, c.dst_v, c.len, c.degree, c.degree_h_stride),
+                          "commit layer", l);
+        } else if (c.kind == VC_COMMIT_INT4_TAIL) {
+          st = with_layer(vc::check_int4_commit(a.B, a.Hkv, a.D, a.M, a.dtype, a.blk_k, a.blk_v, d->n_out, c.tail_k,
+                                                c.tail_v, c.tcap, c.tail_len, c.packed, c.cap, c.main_len),
+                          "int4 commit layer", l);
+        } else {
+          st = bad("unknown commit kind for layer " + std::to_string(l));
+        }
         if (st != VC_OK) return st;
       }
     }
@@ -164,17 +173,20 @@ extern "C" vc_status vc_stagger_round(vc_stagger *s, const vc_round_desc *d, voi
   RoundTimer vt{s, 0, tm.every ? k : 0};
 
   std::vector<int> steps_after(L, 0);   // staggered: draft steps enqueued after each verify layer
-  if (k > 0 && d->mode == VC_ROUND_BULK) {
+  const bool first = d->mode != VC_ROUND_STAGGERED;   // bulk and chained: every draft step first
+  if (k > 0 && first) {
+    for (int i = 0; i < (ns < L ? ns : L) && d->verify && d->mode == VC_ROUND_CHAINED; ++i)
+      CHK(vc_stagger_stream_layer(s, i, d->host_kv[i], d->kv_bytes));   // chained: copies overlap the drafting
     for (int i = 0; i < k; ++i) CHK(draft_step(d, i, draft_stream, tm));
-    CHK(vc_stagger_after(s, draft_stream));   // no copy overlaps the drafting
+    if (d->mode == VC_ROUND_BULK) CHK(vc_stagger_after(s, draft_stream));   // no copy overlaps the drafting
   } else {
     for (int i = 0; i < k; ++i) ++steps_after[(int)((int64_t)i * L / k)];
   }
   if (!d->verify) {
-    for (int i = 0; i < k && d->mode != VC_ROUND_BULK; ++i) CHK(draft_step(d, i, draft_stream, tm));
+    for (int i = 0; i < k && !first; ++i) CHK(draft_step(d, i, draft_stream, tm));
     return VC_OK;
   }
-  if (k > 0 && d->mode == VC_ROUND_BULK) {
+  if (k > 0 && first) {
     // the verify stream starts after the drafting cohort as well
     hipEvent_t ev;
     if (hipEventCreateWithFlags(&ev, hipEventDisableTiming) != hipSuccess)
@@ -184,7 +196,8 @@ extern "C" vc_status vc_stagger_round(vc_stagger *s, const vc_round_desc *d, voi
     (void)hipEventDestroy(ev);
     if (e != hipSuccess) return vc::set_error(VC_EHIP, hipGetErrorString(e));
   }
-  for (int l = 0; l < (ns < L ? ns : L); ++l) CHK(vc_stagger_stream_layer(s, l, d->host_kv[l], d->kv_bytes));
+  if (!(k > 0 && d->mode == VC_ROUND_CHAINED))
+    for (int l = 0; l < (ns < L ? ns : L); ++l) CHK(vc_stagger_stream_layer(s, l, d->host_kv[l], d->kv_bytes));
   int step = 0;
   for (int l = 0; l < L; ++l) {
     void *slot = nullptr;
@@ -208,8 +221,12 @@ extern "C" vc_status vc_stagger_round(vc_stagger *s, const vc_round_desc *d, voi
     for (int l = 0; l < L; ++l) {
       const vc_verify_args &a = d->verify[l];
       const vc_round_commit &c = d->commit[l];
-      CHK(vc_commit_rows(a.B, a.Hkv, a.D, a.M, a.dtype, c.cap, c.dst_v_blocked, a.blk_k, a.blk_v, d->n_out, c.dst_k,
-                         c.dst_v, c.len, c.degree, c.degree_h_stride, verify_stream));
+      if (c.kind == VC_COMMIT_ROWS)
+        CHK(vc_commit_rows(a.B, a.Hkv, a.D, a.M, a.dtype, c.cap, c.dst_v_blocked, a.blk_k, a.blk_v, d->n_out,
+                           c.dst_k, c.dst_v, c.len, c.degree, c.degree_h_stride, verify_stream));
+      else
+        CHK(vc_int4_commit(a.B, a.Hkv, a.D, a.M, a.blk_k, a.blk_v, d->n_out, c.tail_k, c.tail_v, c.tcap, c.tail_len,
+                           c.packed, c.cap, c.main_len, verify_stream));
       const size_t blk_bytes = (size_t)a.B * a.Hkv * a.M * a.D * elem_bytes(a.dtype);
       if (c.host_k) CHK(vc_stagger_writeback(s, c.host_k, a.blk_k, blk_bytes, verify_stream));
       if (c.host_v) CHK(vc_stagger_writeback(s, c.host_v, a.blk_v, blk_bytes, verify_stream));

@@ -30,7 +30,7 @@ def test_exports_every_declared_symbol(L):
 
 
 def _c_layout(struct, fields):
-    src = "#include <stdio.h>\n#include <stddef.h>\n#include \"vc_tiny.h\"\nint main(void){\n"
+    src = "#include <stdio.h>\n#include <stddef.h>\n#include \"vc_tiny.h\"\n#include \"vc.h\"\nint main(void){\n"
     src += f'printf("%zu\\n", sizeof({struct}));\n'
     for f in fields:
         src += f'printf("%zu\\n", offsetof({struct}, {f}));\n'
@@ -48,6 +48,8 @@ def _c_layout(struct, fields):
 @pytest.mark.parametrize("cls,cname", [(vcb.DraftArgs, "vc_draft_args"),
                                        (vcb.VerifyArgs, "vc_verify_args"),
                                        (vcb.AcceptArgs, "vc_accept_args"),
+                                       (vcb.RoundCommit, "vc_round_commit"),
+                                       (vcb.RoundDesc, "vc_round_desc"),
                                        ("TinyModelArgs", "vc_tiny_model"),
                                        ("TinyAttnArgs", "vc_tiny_attn")])
 def test_struct_layout_matches_header(cls, cname):

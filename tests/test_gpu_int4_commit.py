@@ -1,0 +1,220 @@
+"""GPU parity of the int4 cache kept current in the loop ("Algoritmo
+Principale" step 3 with the quantizing drafter of "Supporto Architetturale"):
+vc_int4_commit appends verified block rows to a request's bf16 tail, flushes
+every full 32-token group into the packed int4 cache and keeps the rest in the
+tail.  Over several commits of ragged sizes the flushed blocks are bit-exact
+against the oracle quantizer applied to the same 32 rows, the tail holds
+exactly the leftover rows, the lengths advance, and nothing else changes; a
+full cache drops its groups.  Then one chained round (one request drafting
+and verifying its own drafts, the copies of the first layers streaming during
+the drafting) with the int4 commit inside gives the same bits as the same
+calls made one by one, with the draft stream held back so a missing wait
+would show."""
+import numpy as np
+import pytest
+
+import synthetic as S
+from oracle import quant as Q
+from oracle.formats import bf16_to_f64
+
+from .helpers import to_dev, to_dev_bf16
+
+pytestmark = pytest.mark.gpu
+D = 128
+SENT = 0xA5
+
+
+def _bits(t):
+    import torch
+    return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def _packed_block(kb, vb):
+    """The oracle's packed 5120-byte block of 32 bf16 rows (token-major bits)."""
+    kc, ks, kz = Q.quantize_k(bf16_to_f64(kb))
+    vc_, vs, vz = Q.quantize_v(bf16_to_f64(vb))
+    parts = [S.pack_codes(kc).reshape(-1), S.pack_codes(vc_.T).reshape(-1)]
+    for a in (ks.reshape(-1), kz.reshape(-1), vs.T.reshape(-1), vz.T.reshape(-1)):
+        parts.append(np.ascontiguousarray(np.asarray(a).view(np.uint16).astype("<u2")).view(np.uint8))
+    return np.concatenate(parts)
+
+
+def test_commits_flush_full_groups_bit_exact():
+    import torch
+    import lossless_speculative_decoding_vc_amd as vc
+    dev = "cuda"
+    B, Hkv, M, tcap, cap = 2, 2, 9, 64, 256
+    main0 = np.array([[64, 64], [224, 224]], np.int32)   # request 1 has room for one more group only
+    tail0 = np.array([20, 25], np.int32)
+    packed = torch.full((B, Hkv, cap // 32, 5120), SENT, dtype=torch.uint8, device=dev)
+    main_len = to_dev(main0.copy())
+    tail_len = to_dev(tail0.copy())
+    tail_k_h = S.normal_bf16((B, Hkv, tcap, D), 90, 4, std=1.5)
+    tail_v_h = S.normal_bf16((B, Hkv, tcap, D), 90, 5, std=0.7)     # token-major on the host side
+    tail_k = to_dev_bf16(tail_k_h)
+    tail_v = to_dev_bf16(np.ascontiguousarray(np.swapaxes(tail_v_h, -1, -2)))
+    # host model of each (b, h): the rows waiting in the tail, the int4 length
+    rows_k = [[list(tail_k_h[b, h, :tail0[b]]) for h in range(Hkv)] for b in range(B)]
+    rows_v = [[list(tail_v_h[b, h, :tail0[b]]) for h in range(Hkv)] for b in range(B)]
+    mlen = main0.copy().tolist()
+    expect_blocks = {}
+    # request 0 commits ragged counts; request 1 flushes its one free group, then drops the next
+    for rnd, n_out in enumerate(([9, 9], [5, 9], [9, 9], [1, 9], [9, 9])):
+        bk = S.normal_bf16((B, Hkv, M, D), 91 + rnd, 6, std=1.5)
+        bv = S.normal_bf16((B, Hkv, M, D), 91 + rnd, 7, std=0.7)
+        vc.int4_commit(to_dev_bf16(bk), to_dev_bf16(np.ascontiguousarray(np.swapaxes(bv, -1, -2))),
+                       to_dev(np.asarray(n_out, np.int32)), tail_k, tail_v, tail_len, packed, main_len)
+        torch.cuda.synchronize()
+        for b in range(B):
+            for h in range(Hkv):
+                rows_k[b][h] += list(bk[b, h, :n_out[b]])
+                rows_v[b][h] += list(bv[b, h, :n_out[b]])
+                g = len(rows_k[b][h]) // 32
+                if g and mlen[b][h] + 32 * g <= cap:
+                    for j in range(g):
+                        blk = _packed_block(np.array(rows_k[b][h][32 * j:32 * j + 32]),
+                                            np.array(rows_v[b][h][32 * j:32 * j + 32]))
+                        expect_blocks[(b, h, mlen[b][h] // 32 + j)] = blk
+                    mlen[b][h] += 32 * g
+                rows_k[b][h] = rows_k[b][h][32 * g:]
+                rows_v[b][h] = rows_v[b][h][32 * g:]
+        np.testing.assert_array_equal(main_len.cpu().numpy(), np.array(mlen), err_msg=f"main_len after commit {rnd}")
+        np.testing.assert_array_equal(tail_len.cpu().numpy(), [len(rows_k[b][0]) for b in range(B)],
+                                      err_msg=f"tail_len after commit {rnd}")
+        got_tk, got_tv = _bits(tail_k), _bits(tail_v)
+        for b in range(B):
+            for h in range(Hkv):
+                r = len(rows_k[b][h])
+                if r:
+                    np.testing.assert_array_equal(got_tk[b, h, :r], np.array(rows_k[b][h]))
+                    np.testing.assert_array_equal(got_tv[b, h, :, :r].T, np.array(rows_v[b][h]))
+    got = packed.cpu().numpy()
+    assert len(expect_blocks) == 4
+    for b in range(B):
+        for h in range(Hkv):
+            for j in range(cap // 32):
+                if (b, h, j) in expect_blocks:
+                    np.testing.assert_array_equal(got[b, h, j], expect_blocks[(b, h, j)], err_msg=f"block {(b, h, j)}")
+                else:
+                    assert np.all(got[b, h, j] == SENT), f"block {(b, h, j)} written"
+    assert mlen[1] == [256, 256] and len(rows_k[1][0]) == 6   # request 1's second group was dropped
+
+
+def test_chained_round_with_int4_commit_equals_the_calls_one_by_one():
+    import torch
+    import lossless_speculative_decoding_vc_amd as vc
+    dev = "cuda"
+    B, Hq, Hkv, L, N, K, V, DM = 1, 8, 2, 3, 1024, 8, 512, 256
+    M, cap, tcap = K + 1, 2048, 64
+    y, d, n = S.planted_accept(B, K, V, cfg_seed=95, n_lo=3, n_hi=3)
+    hb, wb = S.lm_planted(V, DM, np.concatenate([y.reshape(-1), d.T.reshape(-1)]), 95)
+    W = to_dev_bf16(wb)
+    hv = to_dev_bf16(hb[:M].reshape(B, M, DM))
+    hd = [to_dev_bf16(hb[M + i:M + i + 1]) for i in range(K)]
+    # per layer: a packed int4 cache (codes U{0..15}, scales in [0.3, 0.5), zeros -7.5 scale), a bf16 tail
+    # holding a 10-row residual, a query, the verify block and the full cache in pinned host memory
+    g = torch.Generator(device=dev)
+    g.manual_seed(96)
+
+    def layer_state():
+        pk = S.torch_randint((B, Hkv, cap // 32, 5120), 0, 256, 97, dev, torch.int32).to(torch.uint8)
+        for j in range(2):
+            sc = (torch.rand((B, Hkv, cap // 32, 128), generator=g, device=dev) * 0.2 + 0.3).half()
+            pk[..., 4096 + 512 * j:4352 + 512 * j] = sc.view(torch.uint8)
+            pk[..., 4352 + 512 * j:4608 + 512 * j] = (sc.float() * -7.5).half().view(torch.uint8)
+        return dict(packed=pk, main_len=torch.full((B, Hkv), 1536, dtype=torch.int32, device=dev),
+                    tail_k=S.torch_normal((B, Hkv, tcap, D), 98, dev, torch.bfloat16),
+                    tail_v=S.torch_normal((B, Hkv, D, tcap), 99, dev, torch.bfloat16),
+                    tail_len=torch.full((B,), 10, dtype=torch.int32, device=dev))
+    init = [layer_state() for _ in range(L)]
+    dq = [S.torch_normal((B, Hq, D), 100 + l, dev, torch.bfloat16, 2.0) for l in range(L)]
+    vq = [S.torch_normal((B, M, Hq, D), 110 + l, dev, torch.bfloat16, 2.0) for l in range(L)]
+    bk = [S.torch_normal((B, Hkv, M, D), 120 + l, dev, torch.bfloat16) for l in range(L)]
+    bv = [S.torch_normal((B, Hkv, D, M), 130 + l, dev, torch.bfloat16) for l in range(L)]
+    half = B * Hkv * N * D * 2
+    fk = [S.torch_normal((B, Hkv, N, D), 140 + l, dev, torch.bfloat16) for l in range(L)]
+    fv = [S.torch_normal((B, Hkv, D, N), 150 + l, dev, torch.bfloat16) for l in range(L)]
+    host = []
+    for l in range(L):
+        h = torch.empty(2 * half, dtype=torch.uint8, pin_memory=True)
+        h[:half].copy_(fk[l].view(torch.uint8).reshape(-1).cpu())
+        h[half:].copy_(fv[l].view(torch.uint8).reshape(-1).cpu())
+        host.append(h)
+    cl = torch.full((B,), N, dtype=torch.int32, device=dev)
+    tl_steps = torch.arange(64, dtype=torch.int32, device=dev)   # tail length r + i + 1 at step i is a view
+
+    def fresh():
+        st = [{k: v.clone() for k, v in s.items()} for s in init]
+        out = dict(dout=[torch.empty((B, Hq, D), dtype=torch.bfloat16, device=dev) for _ in range(L)],
+                   vout=[torch.empty((B, M, Hq, D), dtype=torch.bfloat16, device=dev) for _ in range(L)],
+                   drafts=torch.full((B, K), -1, dtype=torch.int32, device=dev),
+                   am=torch.full((B, M), -1, dtype=torch.int32, device=dev),
+                   al=torch.full((B,), -1, dtype=torch.int32, device=dev),
+                   toks=torch.full((B, M), -1, dtype=torch.int32, device=dev),
+                   nout=torch.full((B,), -1, dtype=torch.int32, device=dev))
+        return st, out
+
+    def outputs(st, out):
+        res = {k: (_bits(v) if v.dtype == torch.bfloat16 else v.cpu().numpy()) for k, v in out.items() if k not in
+               ("dout", "vout")}
+        res["dout"] = [_bits(t) for t in out["dout"]]
+        res["vout"] = [_bits(t) for t in out["vout"]]
+        for key in ("packed", "main_len", "tail_len"):
+            res[key] = [s[key].cpu().numpy() for s in st]
+        res["tail_k"] = [_bits(s["tail_k"]) for s in st]
+        return res
+
+    r0 = 10
+    # 1. the calls one by one, in the order the round's streams impose
+    st, out = fresh()
+    for i in range(K):
+        for l in range(L):
+            vc.draft_attn(dq[l], st[l]["packed"], None, st[l]["main_len"], tail_k=st[l]["tail_k"],
+                          tail_v=st[l]["tail_v"], tail_len=tl_steps[r0 + i + 1:r0 + i + 2], out=out["dout"][l],
+                          fmt=vc.VC_KV_INT4_PACKED)
+        vc.lm_head_argmax(hd[i], W, out=out["drafts"].view(-1)[i:], out_stride=K)
+    for l in range(L):
+        vc.verify_attn(vq[l], fk[l], fv[l], cl, bk[l], bv[l], out=out["vout"][l])
+    vc.lm_head_accept(hv, W, out["drafts"], argmax=out["am"], accept_len=out["al"], out_tokens=out["toks"],
+                      n_out=out["nout"])
+    for l in range(L):
+        vc.int4_commit(bk[l], bv[l], out["nout"], st[l]["tail_k"], st[l]["tail_v"], st[l]["tail_len"],
+                       st[l]["packed"], st[l]["main_len"])
+    torch.cuda.synchronize()
+    ref = outputs(st, out)
+    np.testing.assert_array_equal(ref["drafts"], d)
+    np.testing.assert_array_equal(ref["al"], n)
+    # 2. the chained round, the draft stream held back by a spin first
+    st, out = fresh()
+    slots = [torch.empty(2 * half, dtype=torch.uint8, device=dev) for _ in range(2)]
+    stg = vc.Stagger(slots, 2 * half, L)
+    ds, vs = torch.cuda.Stream(), torch.cuda.Stream()
+    try:
+        draft = [vc.draft_args(dq[l], st[l]["packed"], None, st[l]["main_len"], tail_k=st[l]["tail_k"],
+                               tail_v=st[l]["tail_v"], tail_len=tl_steps[r0 + 1:r0 + 2], out=out["dout"][l],
+                               fmt=vc.VC_KV_INT4_PACKED) for l in range(L)]
+        verify = [vc.verify_args(vq[l], None, None, cl, bk[l], bv[l], out["vout"][l], ccap=N) for l in range(L)]
+        commit = [dict(int4=True, **{k: st[l][k] for k in ("tail_k", "tail_v", "tail_len", "packed", "main_len")})
+                  for l in range(L)]
+        torch.cuda.synchronize()
+        with torch.cuda.stream(ds):
+            torch.cuda._sleep(20_000_000)   # a few milliseconds of spinning, then it exits
+        stg.round(L, vc.ROUND_CHAINED, W, draft=draft,
+                  step_tail_len=[tl_steps[r0 + i + 1:r0 + i + 2] for i in range(K)], draft_hidden=hd,
+                  drafts=out["drafts"], verify=verify, host_kv=host, kv_bytes=2 * half, v_offset=half,
+                  verify_hidden=hv, verify_drafts=out["drafts"], argmax=out["am"], accept_len=out["al"],
+                  out_tokens=out["toks"], n_out=out["nout"], commit=commit, draft_stream=ds, verify_stream=vs)
+        torch.cuda.synchronize()
+        stg.sync()
+    finally:
+        stg.close()
+    got = outputs(st, out)
+    for key in ref:
+        a, b_ = ref[key], got[key]
+        if isinstance(a, list):
+            for i, (x, z) in enumerate(zip(a, b_)):
+                np.testing.assert_array_equal(x, z, err_msg=f"{key}[{i}]")
+        else:
+            np.testing.assert_array_equal(a, b_, err_msg=key)
+    # n = 3 accepted: 4 rows join the 10-row residual, no group is full yet
+    assert got["tail_len"][0].tolist() == [14] and got["main_len"][0].tolist() == [[1536, 1536]]
