@@ -60,7 +60,13 @@ typedef enum { VC_KV_DENSE = 0, VC_KV_INT4 = 1, VC_KV_INT4_PACKED = 2 } vc_kv_fo
  *   V_hat[t][d] = cv[t][d] * v_scale[t/32][d/32][t%32] + v_zero[t/32][d/32][t%32]
  * (one K group = one channel over 32 tokens, one V group = one token over 32
  * channels; codes 0..15, scales/zeros binary16).  Everything int4 is laid out
- * in 32-token blocks, so one block's codes and parameters are contiguous.  */
+ * in 32-token blocks, so one block's codes and parameters are contiguous.
+ * Range of the int4 path: its MFMA operands are fp16 (q * k_scale with q
+ * brought to [0.5, 1) by a power of two, and p * v_scale with p <= 2^8), so
+ * every k_scale and v_scale must lie below 2^9 (reconstructions within about
+ * +-7000); larger scales overflow to inf and the output is NaN.  Nothing checks
+ * this on the device: a cache built by vc_quantize_int4 from values that
+ * large must not be drafted over.                                          */
 typedef struct vc_draft_args {
   int32_t B, Hq, Hkv, D;          /* D in {64, 128}; Hq % Hkv == 0, Hq/Hkv <= 16   */
   int32_t dtype;                  /* vc_dtype of q, dense K/V, tail K/V and out    */
@@ -180,13 +186,6 @@ vc_status vc_accept(const vc_accept_args *a, void *stream);
 vc_status vc_argmax(int32_t R, int32_t V, int32_t logit_dtype, const void *logits,
                     int32_t *out, int32_t out_stride, void *stream);
 
-/* Logits of hidden rows: logits[R][V] (fp32) = h[R][Dm] (bf16) x W[Dm][V]
- * (bf16), row-major.  A plain library GEMM (rocBLAS, fp32 accumulate) on
- * `stream`; the rocBLAS handle is created on first use and kept for the
- * process (it owns rocBLAS's own workspace).                                */
-vc_status vc_lm_head(int32_t R, int32_t Dm, int32_t V, const void *h, const void *w,
-                     float *logits, void *stream);
-
 /* LM head fused with the greedy choice ("Algoritmo Principale", steps 1
  * and 3: the drafter and the verifier keep only the argmax of each logit
  * row): out[r * out_stride] = lowest index of the maximum over v of
@@ -194,9 +193,9 @@ vc_status vc_lm_head(int32_t R, int32_t Dm, int32_t V, const void *h, const void
  * computed in fp32 from bf16 products (MFMA) without writing the logits.
  *   h [R][Dm] bf16, w [V][Dm] bf16 (vocab-major: a linear layer's weight),
  *   both 16-byte aligned; Dm % 32 == 0; out int32 (device).
- * NaN logits never win (a row of NaN gives 0).  The summation order differs
- * from vc_lm_head + vc_argmax, so at a near tie (logits equal to fp32
- * rounding) the two may pick different maxima.  workspace: device buffer of
+ * NaN logits never win (a row of NaN gives 0).  The summation order is the
+ * kernel's own, so at a near tie (logits equal to fp32 rounding) another
+ * GEMM followed by vc_argmax may pick a different maximum.  workspace: device buffer of
  * at least vc_lm_head_argmax_workspace_size(R, V) bytes (per-tile maxima),
  * 16-byte aligned, owned by the caller and not read across calls.
  * VC_EINVAL on bad shapes, null or misaligned pointers or a short
@@ -276,7 +275,9 @@ vc_status vc_compact_kv(int32_t B, int32_t Hkv, int32_t D, int32_t dtype, const 
  *         vc_draft_args with capacity cap (a multiple of 32); only the
  *         written groups' bytes change.
  * D = 128; n_groups <= 65535; inputs finite with |x| <= 65504; src_k, src_v
- * and the code buffers 16-byte aligned.  Appending
+ * and the code buffers 16-byte aligned.  vc_draft_attn reads the result only
+ * while every scale stays below 2^9, i.e. groups spanning less than about
+ * 7680 (see the range note of vc_draft_args).  Appending
  * verified tokens to an int4 cache (flushing full 32-token groups of the bf16
  * tail) and building the cache from a full bf16 cache are both this call.    */
 vc_status vc_quantize_int4(int32_t B, int32_t Hkv, int32_t D, const void *src_k, const void *src_v,

@@ -16,7 +16,7 @@ import torch
 __all__ = [
     "VcError", "lib", "library_path", "draft_attn", "verify_attn", "accept",
     "draft_workspace_size", "verify_workspace_size", "declared_symbols",
-    "argmax", "lm_head", "commit_rows", "quantize_int4", "csm_round", "Stagger", "new_workspace",
+    "argmax", "commit_rows", "quantize_int4", "csm_round", "Stagger", "new_workspace",
     "draft_args", "verify_args", "ROUND_STAGGERED", "ROUND_BULK",
     "VC_BF16", "VC_FP32", "VC_KV_DENSE", "VC_KV_INT4", "VC_KV_INT4_PACKED",
 ]
@@ -123,8 +123,6 @@ def lib():
         L.vc_verify_workspace_size.restype = ctypes.c_size_t
         L.vc_argmax.argtypes = [_i32, _i32, _i32, _p, _p, _i32, _p]
         L.vc_argmax.restype = ctypes.c_int
-        L.vc_lm_head.argtypes = [_i32, _i32, _i32, _p, _p, _p, _p]
-        L.vc_lm_head.restype = ctypes.c_int
         L.vc_lm_head_argmax_workspace_size.argtypes = [_i32, _i32]
         L.vc_lm_head_argmax_workspace_size.restype = ctypes.c_size_t
         L.vc_lm_head_argmax.argtypes = [_i32, _i32, _i32, _p, _p, _p, _i32, _p, ctypes.c_size_t, _p]
@@ -548,19 +546,6 @@ def argmax(logits, out=None, out_stride=1, stream=None):
     _check_out(out, R, out_stride)
     _check(lib().vc_argmax(R, V, _vc_dtype(logits), _ptr(logits), _ptr(out), out_stride, _stream(stream)))
     return out
-
-
-def lm_head(h, w, logits=None, stream=None):
-    """``logits [R][V] (fp32) = h [R][Dm] (bf16) @ w [Dm][V] (bf16)`` (``vc_lm_head``)."""
-    _dev(h, "h", torch.bfloat16)
-    _dev(w, "w", torch.bfloat16)
-    R, Dm = h.shape
-    V = w.shape[1]
-    if logits is None:
-        logits = torch.empty((R, V), dtype=torch.float32, device=h.device)
-    _dev(logits, "logits", torch.float32)
-    _check(lib().vc_lm_head(R, Dm, V, _ptr(h), _ptr(w), _ptr(logits), _stream(stream)))
-    return logits
 
 
 def lm_head_argmax_workspace(R, V, device):

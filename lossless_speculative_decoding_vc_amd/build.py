@@ -24,7 +24,7 @@ CFLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-ffp-contract=fast",
 ]
-LDLIBS = ["-lrocblas"]
+LDLIBS = []
 
 
 def hipcc():

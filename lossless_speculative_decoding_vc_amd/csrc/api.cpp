@@ -124,7 +124,6 @@ vc_status check_verify(const vc_verify_args *a) {
 }  // namespace
 
 namespace vc {
-int lm_head(int R, int Dm, int V, const void *h, const void *w, float *logits, hipStream_t s, const char **err);
 vc_status set_error(vc_status s, const char *msg) { return fail(s, "%s", msg); }
 
 vc_status validate_draft_call(const vc_draft_args *a) {
@@ -212,16 +211,6 @@ vc_status vc_argmax(int32_t R, int32_t V, int32_t logit_dtype, const void *logit
   REQ(aligned16(logits), "logits must be 16-byte aligned");
   return hip_status(vc::launch_argmax(R, V, logit_dtype, logits, out, out_stride, (hipStream_t)stream),
                     "vc_argmax launch");
-}
-
-vc_status vc_lm_head(int32_t R, int32_t Dm, int32_t V, const void *h, const void *w, float *logits,
-                     void *stream) {
-  REQ(R >= 0 && Dm >= 1 && V >= 1, "R >= 0, Dm >= 1, V >= 1 required");
-  if (R == 0) return VC_OK;
-  REQ(h && w && logits, "null pointer");
-  const char *err = nullptr;
-  if (vc::lm_head(R, Dm, V, h, w, logits, (hipStream_t)stream, &err)) return fail(VC_EHIP, "vc_lm_head: %s", err);
-  return VC_OK;
 }
 
 size_t vc_lm_head_argmax_workspace_size(int32_t R, int32_t V) {

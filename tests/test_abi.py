@@ -164,7 +164,6 @@ def test_empty_batches_return_before_any_gpu_call(L):
     acc.B, acc.M, acc.V = 0, 33, 32768
     assert L.vc_accept(ctypes.byref(acc), None) == vcb.VC_OK
     assert L.vc_argmax(0, 32768, 1, None, None, 1, None) == vcb.VC_OK
-    assert L.vc_lm_head(0, 5120, 32768, None, None, None, None) == vcb.VC_OK
     assert L.vc_commit_rows(0, 8, 128, 33, 0, 1024, 0, None, None, None, None, None, None, None, 0,
                             None) == vcb.VC_OK
     assert L.vc_quantize_int4(0, 8, 128, None, None, 64, None, 1, 64, None, None, None, None, None, None, None,
