@@ -806,7 +806,28 @@ def measured_peaks():
 
 
 # ---------------------------------------------------------------------------
+def host_cpu():
+    """The host's CPU model and logical CPU count (from /proc/cpuinfo)."""
+    try:
+        names = [ln.split(":", 1)[1].strip() for ln in open("/proc/cpuinfo") if ln.startswith("model name")]
+    except OSError:
+        names = []
+    return {"model": names[0] if names else "unknown", "logical_cpus": len(names) or os.cpu_count()}
+
+
 def cpu_baseline(verified_per_round, layers):
+    """The oracle on its bounded sample with the BLAS threads it gets by
+    default, and again on a smaller sample with one BLAS thread."""
+    from threadpoolctl import threadpool_limits
+    full = cpu_baseline_sample(verified_per_round, layers, reps=2, n_rows=None)
+    with threadpool_limits(limits=1):
+        one = cpu_baseline_sample(verified_per_round, layers, reps=1, n_rows=11)
+    full["single_thread"] = {k: one[k] for k in ("value", "unit", "cores", "sample")}
+    full["host_cpu"] = host_cpu()
+    return full
+
+
+def cpu_baseline_sample(verified_per_round, layers, reps, n_rows):
     """The oracle (fp64 numpy) on a bounded sample of the round, extrapolated."""
     t_sample = time.time()
     from threadpoolctl import threadpool_info
@@ -819,9 +840,8 @@ def cpu_baseline(verified_per_round, layers):
     Vc = rng.standard_normal((c.N, D), dtype=np.float32).astype(np.float64)
     bk = rng.standard_normal((c.M, D))
     bv = rng.standard_normal((c.M, D))
-    reps = 2                  # two query sets over the same keys
-    q = rng.standard_normal((reps, c.M, G, D))
-    rows = list(range(c.M))   # all 33 block rows (about 10 s on 16 host threads in all)
+    q = rng.standard_normal((reps, c.M, G, D))   # reps query sets over the same keys
+    rows = list(range(c.M)) if n_rows is None else [round(i * (c.M - 1) / (n_rows - 1)) for i in range(n_rows)]
     t = time.time()
     for rep in range(reps):
         for i in rows:
