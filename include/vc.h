@@ -178,6 +178,15 @@ typedef struct vc_accept_args {
 
 vc_status vc_accept(const vc_accept_args *a, void *stream);
 
+/* The next round's first input ("Algoritmo Principale", step 3: decoding
+ * resumes from the last emitted token): dst[b * dst_stride] =
+ * out_tokens[b][n_out[b] - 1] for out_tokens [B][M] and n_out [B] as
+ * vc_accept writes them (n_out clamped to [1, M]); int32, device.  Lets a
+ * round's inputs be chained on the device without a host round trip.
+ * VC_EINVAL on B < 0, M < 1, dst_stride < 1 or null pointers.               */
+vc_status vc_next_input(int32_t B, int32_t M, const int32_t *out_tokens, const int32_t *n_out, int32_t *dst,
+                        int64_t dst_stride, void *stream);
+
 /* ------------------------------------------------------------------------ */
 /* Greedy token choice of the drafter (the draft step's argmax): for each of
  * R rows of logits[R][V], out[r * out_stride] = lowest index of the row

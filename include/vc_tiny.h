@@ -57,7 +57,12 @@ typedef enum { VC_TINY_VERIFY = 0, VC_TINY_DRAFT = 1 } vc_tiny_mode;
  *   (main_k[l] [Hkv][cap][D], main_v[l] [Hkv][D][cap], main_len device
  *   [Hkv]) and a tail; the forward writes the row's K/V into the tail at
  *   index tail_pos (tail_k[l] [Hkv][tcap][D], tail_v[l] [Hkv][D][tcap]) and
- *   attends with tail length tail_pos + 1 (tail_len, device [1], is set).  */
+ *   attends with tail length tail_pos + 1 (tail_len, device [1], is set).
+ * Positions: row r sits at pos0 + r, or at pos_base[0] + pos0 + r when
+ *   pos_base is set (a device value such as the committed length, so that a
+ *   captured round can be replayed as the sequence grows).  With pos_base the
+ *   host cannot check the RoPE table's range: the caller keeps positions
+ *   below rope_rows (the forward clamps them into the table).             */
 typedef struct vc_tiny_attn {
   int32_t mode;
   int64_t cap;                                   /* ctx capacity (VERIFY) / main capacity (DRAFT) */
@@ -69,6 +74,7 @@ typedef struct vc_tiny_attn {
   int64_t tcap;                                  /* DRAFT tail capacity                           */
   int32_t tail_pos;                              /* DRAFT: tail index of this row                 */
   int32_t *tail_len;                             /* DRAFT: device [1], set to tail_pos + 1        */
+  const int32_t *pos_base;                       /* optional device [1]: see below                */
 } vc_tiny_attn;
 
 /* Host-side RoPE table: cos/sin[p][i] of p * base^(-2i/D), computed in double
@@ -94,6 +100,24 @@ vc_status vc_tiny_forward(const vc_tiny_model *m, int32_t R, const int32_t *toke
 vc_status vc_gather_rows(int32_t Hkv, int32_t D, int32_t n, const int32_t *idx, const float *src_k,
                          const float *src_v, int64_t src_cap, float *dst_k, float *dst_v, int64_t dst_cap,
                          int32_t *dst_len, void *stream);
+
+/* The tiny loop's eviction compressor ("Riassunto Tecnico: CentroidKV",
+ * "Componenti Chiave", item 2: attention sinks and recent tokens are kept):
+ * of a cache of T committed tokens keep the first `sinks` positions, the
+ * last `recent`, and every multiple of `stride` in between; every position
+ * when T <= sinks + recent.  vc_evict_kept_count returns how many positions
+ * that keeps (-1 on negative arguments or stride < 1); it grows with T.     */
+int32_t   vc_evict_kept_count(int32_t T, int32_t sinks, int32_t recent, int32_t stride);
+
+/* vc_gather_rows over the kept positions of the eviction rule at the
+ * committed length T = src_len[0] (device), computed on the device: the
+ * compacted cache gets the kept rows in ascending order and dst_len[h] the
+ * kept count, so a round can be captured once and replayed.  T is clamped
+ * to [0, src_cap].  VC_EINVAL unless dst_cap % 32 == 0 and dst_cap holds the
+ * kept rows of a full source cache (vc_evict_kept_count(src_cap, ...)).     */
+vc_status vc_gather_evict(int32_t Hkv, int32_t D, const int32_t *src_len, int32_t sinks, int32_t recent,
+                          int32_t stride, const float *src_k, const float *src_v, int64_t src_cap, float *dst_k,
+                          float *dst_v, int64_t dst_cap, int32_t *dst_len, void *stream);
 
 #ifdef __cplusplus
 }

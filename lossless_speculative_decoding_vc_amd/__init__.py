@@ -123,6 +123,8 @@ def lib():
         L.vc_verify_workspace_size.restype = ctypes.c_size_t
         L.vc_argmax.argtypes = [_i32, _i32, _i32, _p, _p, _i32, _p]
         L.vc_argmax.restype = ctypes.c_int
+        L.vc_next_input.argtypes = [_i32, _i32, _p, _p, _p, _i64, _p]
+        L.vc_next_input.restype = ctypes.c_int
         L.vc_lm_head_argmax_workspace_size.argtypes = [_i32, _i32]
         L.vc_lm_head_argmax_workspace_size.restype = ctypes.c_size_t
         L.vc_lm_head_argmax.argtypes = [_i32, _i32, _i32, _p, _p, _p, _i32, _p, ctypes.c_size_t, _p]
@@ -545,6 +547,22 @@ def argmax(logits, out=None, out_stride=1, stream=None):
     _dev(out, "out", torch.int32)
     _check_out(out, R, out_stride)
     _check(lib().vc_argmax(R, V, _vc_dtype(logits), _ptr(logits), _ptr(out), out_stride, _stream(stream)))
+    return out
+
+
+def next_input(out_tokens, n_out, out, out_stride=1, stream=None):
+    """The next round's first input token of each request (``vc_next_input``):
+    ``out[b * out_stride] = out_tokens[b][n_out[b] - 1]`` for ``out_tokens
+    [B][M]`` and ``n_out [B]`` as :func:`accept` writes them."""
+    _dev(out_tokens, "out_tokens", torch.int32)
+    _dev(n_out, "n_out", torch.int32)
+    _dev(out, "out", torch.int32)
+    if out_tokens.dim() != 2:
+        raise ValueError("out_tokens must be [B][M]")
+    B, M = out_tokens.shape
+    _want(n_out, "n_out", (B,), (torch.int32,))
+    _check_out(out, B, out_stride)
+    _check(lib().vc_next_input(B, M, _ptr(out_tokens), _ptr(n_out), _ptr(out), out_stride, _stream(stream)))
     return out
 
 

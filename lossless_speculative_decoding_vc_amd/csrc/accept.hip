@@ -99,7 +99,23 @@ __global__ __launch_bounds__(64) void accept_rows(const int *__restrict__ draft,
   if (lane == 0) { accept_len[b] = n; n_out[b] = n + 1; }
 }
 
+__global__ __launch_bounds__(64) void next_input(int B, int M, const int *__restrict__ out_tokens,
+                                                 const int *__restrict__ n_out, int *__restrict__ dst,
+                                                 int64_t dst_stride) {
+  const int b = blockIdx.x * 64 + threadIdx.x;
+  if (b >= B) return;
+  int n = n_out[b];
+  n = n < 1 ? 1 : (n > M ? M : n);
+  dst[b * dst_stride] = out_tokens[(size_t)b * M + n - 1];
+}
+
 }  // namespace
+
+hipError_t launch_next_input(int B, int M, const int32_t *out_tokens, const int32_t *n_out, int32_t *dst,
+                             int64_t dst_stride, hipStream_t s) {
+  next_input<<<(B + 63) / 64, 64, 0, s>>>(B, M, out_tokens, n_out, dst, dst_stride);
+  return hipGetLastError();
+}
 
 hipError_t launch_argmax(int rows, int V, int dtype, const void *logits, int *out, int out_stride,
                          hipStream_t s) {

@@ -202,6 +202,15 @@ vc_status vc_accept(const vc_accept_args *a, void *stream) {
   return hip_status(vc::launch_accept(*a, (hipStream_t)stream), "vc_accept launch");
 }
 
+vc_status vc_next_input(int32_t B, int32_t M, const int32_t *out_tokens, const int32_t *n_out, int32_t *dst,
+                        int64_t dst_stride, void *stream) {
+  REQ(B >= 0 && M >= 1 && dst_stride >= 1, "B >= 0, M >= 1 and dst_stride >= 1 required");
+  if (B == 0) return VC_OK;
+  REQ(out_tokens && n_out && dst, "null pointer");
+  return hip_status(vc::launch_next_input(B, M, out_tokens, n_out, dst, dst_stride, (hipStream_t)stream),
+                    "vc_next_input launch");
+}
+
 vc_status vc_argmax(int32_t R, int32_t V, int32_t logit_dtype, const void *logits, int32_t *out,
                     int32_t out_stride, void *stream) {
   REQ(R >= 0 && V >= 1 && out_stride >= 1, "R >= 0, V >= 1, out_stride >= 1 required");

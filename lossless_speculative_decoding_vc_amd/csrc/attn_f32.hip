@@ -1,18 +1,24 @@
 // fp32 attention for the small fp32 mode (draft and verify share it).
 //
-// One wave per (request, block row, query head).  The key sequence is two
-// segments: A (compressed main segment, or the full-cache context) followed
-// by B (draft tail, or the verify block keys 0..i).  Segment A may carry
-// merge degrees whose logarithm is added to the score ("Riassunto Tecnico:
-// CentroidKV", "Componenti Chiave", item 4).  Keys are processed 64 at a
-// time: lane = key for the scores, lane = channel for the weighted sum, with
-// an online (running-max) softmax in base 2.  Used for the tiny fp32 decoder,
-// where every tensor is a few hundred KB; it is not a bandwidth kernel.
+// One 1024-thread workgroup per (request, block row, query head).  The key
+// sequence is two segments: A (compressed main segment, or the full-cache
+// context) followed by B (draft tail, or the verify block keys 0..i).
+// Segment A may carry merge degrees whose logarithm is added to the score
+// ("Riassunto Tecnico: CentroidKV", "Componenti Chiave", item 4).  Keys are
+// processed 1024 at a time: thread = key for the scores (its key row read with
+// 16-byte loads), a running maximum and sum shared by the workgroup (online
+// softmax in base 2), then each wave accumulates the weighted values of its
+// 64 keys with lane = channel, 32 value loads in flight together; the 16
+// waves' sums are added in wave order at the end.  Used for the tiny fp32
+// decoder, whose caches hold a few thousand tokens: the workgroup size only
+// shortens the chain of dependent loads (one chunk covers most contexts).
 #include "common.h"
 #include "launch.h"
 
 namespace vc {
 namespace {
+
+constexpr int kAT = 1024;   // threads per workgroup = keys per chunk
 
 struct F32Params {
   int Hq, Hkv, G, M, D;
@@ -33,17 +39,19 @@ struct F32Params {
   float *out_lse;                    // [B][M][Hq]
 };
 
-__global__ __launch_bounds__(64) void attn_f32(F32Params p) {
+__global__ __launch_bounds__(kAT) void attn_f32(F32Params p) {
   const int b = blockIdx.y;
   const int i = blockIdx.x / p.Hq;
   const int h = blockIdx.x % p.Hq;
   const int kvh = h / p.G;
-  const int lane = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int D = p.D;
-  __shared__ float qs[128];
-  __shared__ float ps[64];
+  __shared__ __attribute__((aligned(16))) float qs[128];
+  __shared__ float ps[kAT];
+  __shared__ float red_m[kAT / 64], red_s[kAT / 64];
+  __shared__ float acc_w[kAT / 64][128];
   const float *qrow = p.q + (((size_t)b * p.M + i) * p.Hq + h) * D;
-  for (int d = lane; d < D; d += 64) qs[d] = qrow[d];
+  if (tid < D) qs[tid] = qrow[tid];
   __syncthreads();
 
   int la = p.alen[p.alen_per_head ? b * p.Hkv + kvh : b];
@@ -59,49 +67,78 @@ __global__ __launch_bounds__(64) void attn_f32(F32Params p) {
   const float *bk = p.bk ? p.bk + bh * p.bcap * D : nullptr;
   const float *bv = p.bv ? p.bv + bh * D * p.bcap : nullptr;
   const float *dg = p.deg ? p.deg + b * p.deg_b_stride + kvh * p.deg_h_stride : nullptr;
+  const f32x4 *q4 = reinterpret_cast<const f32x4 *>(qs);
 
   float m_run = kNegInf, l_run = 0.f;
   float acc[2] = {0.f, 0.f};
-  for (int t0 = 0; t0 < total; t0 += 64) {
-    const int t = t0 + lane;
+  for (int t0 = 0; t0 < total; t0 += kAT) {
+    const int t = t0 + tid;
     float s = kNegInf;
     if (t < total) {
-      const float *kr = (t < la) ? ak + (size_t)t * D : bk + (size_t)(t - la) * D;
+      const f32x4 *kr = reinterpret_cast<const f32x4 *>((t < la) ? ak + (size_t)t * D : bk + (size_t)(t - la) * D);
       float dot = 0.f;
-      for (int d = 0; d < D; ++d) dot = fmaf(qs[d], kr[d], dot);
+      for (int d4 = 0; d4 < D / 4; ++d4) {
+        const f32x4 kv = kr[d4], qv = q4[d4];
+        dot = fmaf(qv[0], kv[0], dot);
+        dot = fmaf(qv[1], kv[1], dot);
+        dot = fmaf(qv[2], kv[2], dot);
+        dot = fmaf(qv[3], kv[3], dot);
+      }
       s = dot * p.qk_scale;
       if (dg && t < la) s += fast_log2(dg[t]);
     }
-    const float cmax = wave_max(s);
+    const float wm = wave_max(s);
+    if (lane == 0) red_m[wv] = wm;
+    __syncthreads();
+    float cmax = red_m[0];
+    for (int ww = 1; ww < kAT / 64; ++ww) cmax = fmaxf(cmax, red_m[ww]);
     const float m_new = fmaxf(m_run, cmax);
     const float alpha = fast_exp2(m_run - m_new);
     const float pr = (t < total) ? fast_exp2(s - m_new) : 0.f;
-    l_run = l_run * alpha + wave_sum(pr);
-    m_run = m_new;
-    ps[lane] = pr;
+    const float ws = wave_sum(pr);
+    if (lane == 0) red_s[wv] = ws;
+    ps[tid] = pr;
     __syncthreads();
-    const int n = min(64, total - t0);
+    float csum = red_s[0];
+    for (int ww = 1; ww < kAT / 64; ++ww) csum += red_s[ww];
+    l_run = l_run * alpha + csum;
+    m_run = m_new;
+    const int j0 = t0 + wv * 64;
+    const int n = min(64, total - j0);   // this wave's keys (may be <= 0)
     for (int e = 0; e < 2; ++e) {
       const int d = lane + 64 * e;
       if (d >= D) break;
       float a2 = acc[e] * alpha;
-      for (int j = 0; j < n; ++j) {
-        const int tt = t0 + j;
-        const float v = (tt < la) ? av[p.av_blocked ? (size_t)(tt >> 5) * D * 32 + d * 32 + (tt & 31)
-                                                   : (size_t)d * p.acap + tt]
-                                  : bv[(size_t)d * p.bcap + (tt - la)];
-        a2 = fmaf(ps[j], v, a2);
+#pragma unroll 1
+      for (int jh = 0; jh < n; jh += 32) {
+        float v[32];
+#pragma unroll
+        for (int j = 0; j < 32; ++j) {
+          const int tt = j0 + jh + j;
+          v[j] = jh + j >= n ? 0.f
+                             : (tt < la) ? av[p.av_blocked ? (size_t)(tt >> 5) * D * 32 + d * 32 + (tt & 31)
+                                                           : (size_t)d * p.acap + tt]
+                                         : bv[(size_t)d * p.bcap + (tt - la)];
+        }
+#pragma unroll
+        for (int j = 0; j < 32; ++j) a2 = fmaf(ps[wv * 64 + jh + j], v[j], a2);
       }
       acc[e] = a2;
     }
     __syncthreads();
   }
-  float *orow = p.out + (((size_t)b * p.M + i) * p.Hq + h) * D;
   for (int e = 0; e < 2; ++e) {
     const int d = lane + 64 * e;
-    if (d < D) orow[d] = acc[e] / l_run;
+    if (d < D) acc_w[wv][d] = acc[e];
   }
-  if (p.out_lse && lane == 0)
+  __syncthreads();
+  float *orow = p.out + (((size_t)b * p.M + i) * p.Hq + h) * D;
+  if (tid < D) {
+    float o = acc_w[0][tid];
+    for (int ww = 1; ww < kAT / 64; ++ww) o += acc_w[ww][tid];
+    orow[tid] = o / l_run;
+  }
+  if (p.out_lse && tid == 0)
     p.out_lse[((size_t)b * p.M + i) * p.Hq + h] = (l_run > 0.f) ? (m_run + fast_log2(l_run)) * kLn2 : kNegInf;
 }
 
@@ -121,7 +158,7 @@ hipError_t launch_draft_f32(const vc_draft_args &a, hipStream_t s) {
   p.blen = a.tail_len; p.causal = 0;
   if (!a.tail_len) p.bk = p.bv = nullptr;
   p.out = (float *)a.out; p.out_lse = a.out_lse;
-  attn_f32<<<dim3(a.Hq, a.B), 64, 0, s>>>(p);
+  attn_f32<<<dim3(a.Hq, a.B), kAT, 0, s>>>(p);
   return hipGetLastError();
 }
 
@@ -135,7 +172,7 @@ hipError_t launch_verify_f32(const vc_verify_args &a, hipStream_t s) {
   p.bk = (const float *)a.blk_k; p.bv = (const float *)a.blk_v; p.bcap = a.M;
   p.blen = nullptr; p.causal = 1;
   p.out = (float *)a.out; p.out_lse = a.out_lse;
-  attn_f32<<<dim3(a.M * a.Hq, a.B), 64, 0, s>>>(p);
+  attn_f32<<<dim3(a.M * a.Hq, a.B), kAT, 0, s>>>(p);
   return hipGetLastError();
 }
 

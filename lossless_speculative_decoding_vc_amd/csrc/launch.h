@@ -38,6 +38,8 @@ hipError_t launch_accept(const vc_accept_args &a, hipStream_t s);
 hipError_t launch_argmax(int rows, int V, int dtype, const void *logits, int *out, int out_stride,
                          hipStream_t s);
 // Acceptance over precomputed argmax rows (argmax [B][M], draft [B][M-1]).
+hipError_t launch_next_input(int B, int M, const int32_t *out_tokens, const int32_t *n_out, int32_t *dst,
+                             int64_t dst_stride, hipStream_t s);
 hipError_t launch_accept_rows(int B, int M, const int32_t *draft, const int32_t *argmax, int32_t *accept_len,
                               int32_t *out_tokens, int32_t *n_out, hipStream_t s);
 // LM head fused with the argmax (see lmhead_argmax.hip).

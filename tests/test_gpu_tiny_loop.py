@@ -1,7 +1,9 @@
 """End-to-end GPU draft-then-verify loop on the tiny fp32 decoder, compared
 with the oracle run step by step: identical output tokens (== full-KV greedy
 decoding), identical drafts and accept lengths in every round, and the
-identity compressor accepting every draft plus the bonus token."""
+identity compressor accepting every draft plus the bonus token.  Every round
+replays a HIP graph captured after the prefill; replayed rounds equal rounds
+enqueued one by one, record for record."""
 import numpy as np
 import pytest
 
@@ -10,10 +12,11 @@ from oracle import tiny
 pytestmark = pytest.mark.gpu
 
 
-def _gpu_loop(arrays, prompt, n_new, k, compressor, recent=128):
+def _gpu_loop(arrays, prompt, n_new, k, compressor, recent=128, graph=True):
     from lossless_speculative_decoding_vc_amd.tiny_loop import TinyDecoder, TinyVeriCache
     model = TinyDecoder(arrays, max_pos=len(prompt) + n_new + k + 64)
-    loop = TinyVeriCache(model, max_tokens=len(prompt) + n_new + k, k=k, compressor=compressor, recent=recent)
+    loop = TinyVeriCache(model, max_tokens=len(prompt) + n_new + k, k=k, compressor=compressor, recent=recent,
+                         graph=graph)
     return loop.generate(prompt, n_new)
 
 
@@ -49,3 +52,23 @@ def test_identity_compressor_full_acceptance(tiny_setup):
     toks, rounds = _gpu_loop(arrays, p, 30, 6, "identity")
     assert toks == tiny.greedy_decode(W, p, 30)
     assert all(r[2] == 6 and len(r[3]) == 7 for r in rounds)    # every draft + the bonus
+
+
+def test_graph_replays_equal_rounds_enqueued_one_by_one(tiny_setup):
+    spec, arrays, W, prompt = tiny_setup
+    p = prompt[:300]
+    eager = _gpu_loop(arrays, p, 40, 4, "evict", recent=32, graph=False)
+    replayed = _gpu_loop(arrays, p, 40, 4, "evict", recent=32, graph=True)
+    assert len(replayed[1]) >= 3          # the graph was replayed several times
+    assert replayed == eager
+    ref, ref_rounds = tiny.vericache_decode(W, p, 40, 4, lambda T: tiny.kept_positions(T, 4, 32, 8))
+    assert replayed[0] == ref
+    assert [r[2] for r in replayed[1]] == [r.n for r in ref_rounds]
+
+
+def test_greedy_k0_matches_oracle(tiny_setup):
+    spec, arrays, W, prompt = tiny_setup
+    p = prompt[:256]
+    toks, rounds = _gpu_loop(arrays, p, 20, 0, "evict", recent=32)
+    assert toks == tiny.greedy_decode(W, p, 20)
+    assert all(r[2] == 0 and len(r[3]) == 1 for r in rounds)
