@@ -392,7 +392,9 @@ double  vc_csm_schedule_ratio(double r_init, double delta_r, int32_t round);
  *   vc_stagger_copy_ms          duration of layer l's last host-to-device
  *                               copy (valid after vc_stagger_sync).
  * Slots are caller-owned device buffers; host sources must be pinned
- * (hipHostMalloc) for the copies to run on the DMA engines.               */
+ * (hipHostMalloc) for the host-to-device copies to run on the copy (SDMA)
+ * engines.  The runtime carries out the device-to-host write-backs, small
+ * here, as blit kernels on the compute units.                              */
 typedef struct vc_stagger vc_stagger;
 vc_status vc_stagger_create(vc_stagger **out, void *const *slots, int32_t nslots, size_t slot_bytes,
                             int32_t max_layers);
