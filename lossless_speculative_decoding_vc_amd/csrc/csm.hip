@@ -22,9 +22,11 @@
 // a 40 KB LDS footprint, up to 128 an 89 KB one.  A chunk's keys and values
 // are staged in LDS (bf16).  The |A| x |B| key dot products run on MFMA
 // (exact bf16 products, fp32 sums) and are divided by the fp32 norms; each A
-// token's argmax and rank come from eight lanes and a shuffle reduction.
-// Each survivor is written once: unmerged tokens bit-exactly, clusters as the
-// fp32 degree-weighted mean rounded to bf16, V through an LDS tile
+// token's argmax and rank come from eight lanes and a shuffle reduction; a B
+// token's members are one ballot (a bit mask over the A tokens).  Each
+// survivor is written once, by one wave with lane = channel pair, so member
+// loops never diverge within a wave: unmerged tokens bit-exactly, clusters as
+// the fp32 degree-weighted mean rounded to bf16, V through an LDS tile
 // [channel][survivor] so the blocked writes coalesce.  Every chunk before the
 // last is full, so a chunk's output offset follows from its index alone.
 #include "common.h"
@@ -47,13 +49,15 @@ VC_DEVICE float dot8(const u32x4 &a, const u32x4 &b, float acc) {
 template <int kMaxChunk>
 __global__ __launch_bounds__(256) void csm_round_kernel(CsmParams p) {
   __shared__ __attribute__((aligned(16))) uint16_t ks[kMaxChunk][kD + 8];   // rows padded by 16 B: lanes reading different rows spread over the banks
-  __shared__ __attribute__((aligned(16))) uint16_t vs[kD][kMaxChunk];   // channel-major, as in the source
+  // channel-major, as in the source; rows padded by 8 bytes so that lanes reading one token of 64 different
+  // channels spread over the banks
+  __shared__ __attribute__((aligned(16))) uint16_t vs[kD][kMaxChunk + 4];
   __shared__ float nrm[kMaxChunk], dg[kMaxChunk];
-  __shared__ float sim[kMaxChunk / 2][kMaxChunk / 2];
+  __shared__ __attribute__((aligned(16))) float sim[kMaxChunk / 2][kMaxChunk / 2];
   __shared__ float score[kMaxChunk / 2];
   __shared__ int match[kMaxChunk / 2], mergedA[kMaxChunk / 2];
-  __shared__ int surv[kMaxChunk], nmem[kMaxChunk / 2];
-  __shared__ uint8_t mem[kMaxChunk / 2][kMaxChunk / 2];
+  __shared__ int surv[kMaxChunk];
+  __shared__ unsigned long long amask[kMaxChunk / 2];   // B token j: bit i set iff A token i merges into it
   const int bh = blockIdx.y, tid = threadIdx.x;
   const int nchunks = (int)gridDim.x - 2;
   const int c = (int)blockIdx.x - 1;   // -1: sinks, nchunks: recent tokens
@@ -131,14 +135,21 @@ __global__ __launch_bounds__(256) void csm_round_kernel(CsmParams p) {
   }
   for (int t = tid; t < L; t += 256) dg[t] = idg ? idg[s0 + t] : 1.f;
   __syncthreads();
-  for (int t = tid; t < L; t += 256) {
+  // key norms: four lanes per token, each summing a quarter of the channels,
+  // the quarters added in a fixed order
+  for (int t0 = 0; t0 < L; t0 += 64) {
+    const int t = t0 + (tid >> 2), qq = tid & 3;
     float acc = 0.f;
-#pragma unroll 4
-    for (int q = 0; q < kD / 8; ++q) {
-      const u32x4 w = *reinterpret_cast<const u32x4 *>(&ks[t][8 * q]);
-      acc = dot8(w, w, acc);
+    if (t < L) {
+#pragma unroll
+      for (int q = 4 * qq; q < 4 * qq + 4; ++q) {
+        const u32x4 w = *reinterpret_cast<const u32x4 *>(&ks[t][8 * q]);
+        acc = dot8(w, w, acc);
+      }
     }
-    nrm[t] = sqrtf(acc);
+    const float a1 = acc + __shfl_xor(acc, 1, 64);
+    const float a2 = a1 + __shfl_xor(a1, 2, 64);
+    if (t < L && qq == 0) nrm[t] = sqrtf(a2);
   }
   __syncthreads();
   // cosines of A token i (position 2i) with B token j (position 2j+1): the
@@ -202,8 +213,8 @@ __global__ __launch_bounds__(256) void csm_round_kernel(CsmParams p) {
   }
   __syncthreads();
   // survivors (B tokens and unmerged A tokens) in position order: surv[k] is
-  // the chunk position of output slot base + k; mem[j] lists, in ascending
-  // order, the A tokens merged into B token j
+  // the chunk position of output slot base + k; amask[j] holds the A tokens
+  // merged into B token j
   {
     // merge flags of the A tokens as bit masks (A token i = bit i), one 64-bit
     // word per 64 A tokens, so survivor slots are popcounts
@@ -227,96 +238,101 @@ __global__ __launch_bounds__(256) void csm_round_kernel(CsmParams p) {
         surv[t - below] = t;
       }
     }
-    if (tid < nB) {
-      int n = 0;
-#pragma unroll
-      for (int i = 0; i < kMaxChunk / 2; ++i)
-        if (i < nA && mergedA[i] && match[i] == tid) mem[tid][n++] = (uint8_t)i;
-      nmem[tid] = n;
+    // members of each B token as a bit mask over the A tokens (ascending bit = ascending position): one
+    // ballot per B token, the B tokens dealt round-robin to the four waves
+    {
+      const int wave = tid >> 6, lane = tid & 63;
+      const bool mg = lane < nA && mergedA[lane];
+      const int mt = lane < nA ? match[lane] : -1;
+      for (int j = wave; j < nB; j += 4) {
+        const unsigned long long bal = __ballot(mg && mt == j);
+        if (lane == 0) amask[j] = bal;
+      }
     }
   }
   __syncthreads();
   const int ns = L - m;
-  // Output: survivor k (chunk position surv[k]) goes to slot base + k; its
-  // members are itself and, for a B token, the A tokens merged into it (the
-  // first kRegMem read into registers, any further ones from LDS).
-  constexpr int kRegMem = 8;
-  auto members = [&](int t, int (&mb)[kRegMem], float (&wm)[kRegMem], int &nm) __attribute__((always_inline)) {
-    nm = (t & 1) ? nmem[t >> 1] : 0;
-    float w = dg[t];
-#pragma unroll
-    for (int u = 0; u < kRegMem; ++u) {
-      mb[u] = u < nm ? 2 * mem[t >> 1][u] : t;
-      wm[u] = u < nm ? dg[mb[u]] : 0.f;
-      w += wm[u];
-    }
-    for (int u = kRegMem; u < nm; ++u) w += dg[2 * mem[t >> 1][u]];
-    return w;
-  };
-  // K rows and degrees: four lanes share a token row (32 channels each,
-  // 16-byte stores)
-  for (int k0 = 0; k0 < ns; k0 += 64) {
-    const int k = k0 + (tid & 63), quarter = tid >> 6;
-    if (k >= ns) continue;
+  // Output: survivor k (chunk position surv[k]) goes to slot base + k.  A
+  // cluster (a B token with merged A tokens) is its own degree-weighted value
+  // plus its members' in ascending position, times the inverse total degree;
+  // other survivors are copied bit-exactly.  Per survivor first (one thread
+  // each): its member mask, total degree and inverse.
+  // (held in the similarity matrix's space, no longer read)
+  static_assert(sizeof(sim) >= kMaxChunk * (sizeof(unsigned long long) + sizeof(float)), "per-survivor data fits");
+  unsigned long long *smask = reinterpret_cast<unsigned long long *>(&sim[0][0]);
+  float *sinv = reinterpret_cast<float *>(smask + kMaxChunk);
+  for (int k = tid; k < ns; k += 256) {
     const int t = surv[k];
-    int mb[kRegMem], nm;
-    float wm[kRegMem];
-    const float w = members(t, mb, wm, nm), inv = 1.f / w;
-    if (quarter == 0) odg[base + k] = w;
-#pragma unroll
-    for (int q = 4 * quarter; q < 4 * quarter + 4; ++q) {
-      uint16_t *dst = ok + (size_t)(base + k) * kD + 8 * q;
-      if (nm == 0) {
-        *reinterpret_cast<u32x4 *>(dst) = *reinterpret_cast<const u32x4 *>(&ks[t][8 * q]);
-        continue;
-      }
-      float acc[8];
-#pragma unroll
-      for (int e2 = 0; e2 < 8; ++e2) acc[e2] = dg[t] * bf16_to_f32(ks[t][8 * q + e2]);
-#pragma unroll
-      for (int u = 0; u < kRegMem; ++u)
-        if (u < nm)
-#pragma unroll
-          for (int e2 = 0; e2 < 8; ++e2) acc[e2] = fmaf(wm[u], bf16_to_f32(ks[mb[u]][8 * q + e2]), acc[e2]);
-      for (int u = kRegMem; u < nm; ++u) {
-        const int a2 = 2 * mem[t >> 1][u];
-#pragma unroll
-        for (int e2 = 0; e2 < 8; ++e2) acc[e2] = fmaf(dg[a2], bf16_to_f32(ks[a2][8 * q + e2]), acc[e2]);
-      }
-      u32x4 kw;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) kw[j] = pack_bf16x2(acc[2 * j] * inv, acc[2 * j + 1] * inv);
-      *reinterpret_cast<u32x4 *>(dst) = kw;
+    const unsigned long long mk = (t & 1) ? amask[t >> 1] : 0ull;
+    float w = dg[t];
+    for (unsigned long long b = mk; b; b &= b - 1) w += dg[2 * __builtin_ctzll(b)];
+    smask[k] = mk;
+    sinv[k] = 1.f / w;
+    odg[base + k] = w;
+  }
+  __syncthreads();
+  // K rows: 16 lanes per survivor (16-byte pieces), 16 survivors at a time
+  for (int k = tid >> 4; k < ns; k += 16) {
+    const int t = surv[k], q = tid & 15;
+    const unsigned long long mk = smask[k];
+    const u32x4 xt = *reinterpret_cast<const u32x4 *>(&ks[t][8 * q]);
+    u32x4 *dst = reinterpret_cast<u32x4 *>(ok + (size_t)(base + k) * kD + 8 * q);
+    if (!mk) {
+      *dst = xt;
+      continue;
     }
+    const float inv = sinv[k], dt = dg[t];
+    float acc[8];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      acc[2 * j] = dt * bf16_lo(xt[j]);
+      acc[2 * j + 1] = dt * bf16_hi(xt[j]);
+    }
+    for (unsigned long long b = mk; b; b &= b - 1) {
+      const int a2 = 2 * __builtin_ctzll(b);
+      const u32x4 xa = *reinterpret_cast<const u32x4 *>(&ks[a2][8 * q]);
+      const float wa = dg[a2];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        acc[2 * j] = fmaf(wa, bf16_lo(xa[j]), acc[2 * j]);
+        acc[2 * j + 1] = fmaf(wa, bf16_hi(xa[j]), acc[2 * j + 1]);
+      }
+    }
+    u32x4 kw;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) kw[j] = pack_bf16x2(acc[2 * j] * inv, acc[2 * j + 1] * inv);
+    *dst = kw;
   }
   __syncthreads();
   // V: the output tile [channel][survivor] is formed in LDS (over the key
-  // buffer, no longer read), then leaves in pieces of four consecutive tokens
-  // (8 bytes, never straddling a 32-token block) when the first output slot
-  // is a multiple of 4, else element by element.
-  static_assert(sizeof(ks) >= sizeof(uint16_t) * kD * kMaxChunk, "V tile fits over the key buffer");
-  uint16_t (*vo)[kMaxChunk] = reinterpret_cast<uint16_t (*)[kMaxChunk]>(&ks[0][0]);
-  for (int k0 = 0; k0 < ns; k0 += 64) {
-    const int k = k0 + (tid & 63), quarter = tid >> 6;
-    if (k >= ns) continue;
-    const int t = surv[k];
-    int mb[kRegMem], nm;
-    float wm[kRegMem];
-    const float inv = 1.f / members(t, mb, wm, nm);
-    for (int d = 32 * quarter; d < 32 * quarter + 32; ++d) {
-      uint16_t val = vs[d][t];
-      if (nm > 0) {
-        float acc = dg[t] * bf16_to_f32(val);
-#pragma unroll
-        for (int u = 0; u < kRegMem; ++u)
-          if (u < nm) acc = fmaf(wm[u], bf16_to_f32(vs[d][mb[u]]), acc);
-        for (int u = kRegMem; u < nm; ++u) {
-          const int a2 = 2 * mem[t >> 1][u];
-          acc = fmaf(dg[a2], bf16_to_f32(vs[d][a2]), acc);
+  // buffer, no longer read), each wave on whole survivors (uniform member
+  // loops within a wave); it then leaves in pieces of four consecutive tokens (8 bytes, never straddling a
+  // 32-token block) when the first output slot is a multiple of 4, else
+  // element by element.
+  static_assert(sizeof(ks) >= sizeof(uint16_t) * kD * (kMaxChunk + 4), "V tile fits over the key buffer");
+  uint16_t (*vo)[kMaxChunk + 4] = reinterpret_cast<uint16_t (*)[kMaxChunk + 4]>(&ks[0][0]);
+  {
+    // lane = channel pair (d, d + 64), wave w takes survivors w, w + 4, ...
+    const int lane = tid & 63;
+    for (int k = tid >> 6; k < ns; k += 4) {
+      const int t = surv[k];
+      const unsigned long long mk = smask[k];
+      uint16_t v0 = vs[lane][t], v1 = vs[lane + 64][t];
+      if (mk) {
+        const float dt = dg[t];
+        float acc0 = dt * bf16_to_f32(v0), acc1 = dt * bf16_to_f32(v1);
+        for (unsigned long long b = mk; b; b &= b - 1) {
+          const int a2 = 2 * __builtin_ctzll(b);
+          const float wa = dg[a2];
+          acc0 = fmaf(wa, bf16_to_f32(vs[lane][a2]), acc0);
+          acc1 = fmaf(wa, bf16_to_f32(vs[lane + 64][a2]), acc1);
         }
-        val = f32_to_bf16(acc * inv);
+        const float inv = sinv[k];
+        v0 = f32_to_bf16(acc0 * inv);
+        v1 = f32_to_bf16(acc1 * inv);
       }
-      vo[d][k] = val;
+      vo[lane][k] = v0;
+      vo[lane + 64][k] = v1;
     }
   }
   __syncthreads();
