@@ -21,7 +21,7 @@
 // head) that copy the sinks and the recent tokens; chunks up to 64 tokens use
 // a 40 KB LDS footprint, up to 128 an 89 KB one.  A chunk's keys and values
 // are staged in LDS (bf16).  The |A| x |B| key dot products run on MFMA
-// (exact bf16 products, fp32 sums) and are divided by the fp32 norms; each A
+// (exact bf16 products, fp32 sums) and scaled by the inverse fp32 norms; each A
 // token's argmax and rank come from eight lanes and a shuffle reduction; a B
 // token's members are one ballot (a bit mask over the A tokens).  Each
 // survivor is written once, by one wave with lane = channel pair, so member
@@ -149,13 +149,13 @@ __global__ __launch_bounds__(256) void csm_round_kernel(CsmParams p) {
     }
     const float a1 = acc + __shfl_xor(acc, 1, 64);
     const float a2 = a1 + __shfl_xor(a1, 2, 64);
-    if (t < L && qq == 0) nrm[t] = sqrtf(a2);
+    if (t < L && qq == 0) nrm[t] = 1.f / sqrtf(a2);   // the inverse norm
   }
   __syncthreads();
   // cosines of A token i (position 2i) with B token j (position 2j+1): the
   // dot products as 16x16 tiles of v_mfma_f32_16x16x32_bf16 (bf16 products
-  // are exact in its fp32 accumulation), one tile per wave in turn; rows past
-  // nA / nB read row 0 and are not stored
+  // are exact in its fp32 accumulation) times the two inverse norms, one tile
+  // per wave in turn; rows past nA / nB read row 0 and are not stored
   {
     const int wave = tid >> 6, lane = tid & 63, col = lane & 15, grp = lane >> 4;
     const int tA = (nA + 15) / 16, tB = (nB + 15) / 16;
@@ -174,7 +174,7 @@ __global__ __launch_bounds__(256) void csm_round_kernel(CsmParams p) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int ii = 16 * ti + 4 * grp + i, jj = 16 * tj + col;
-        if (ii < nA && jj < nB) sim[ii][jj] = acc[i] / (nrm[2 * ii] * nrm[2 * jj + 1]);
+        if (ii < nA && jj < nB) sim[ii][jj] = acc[i] * (nrm[2 * ii] * nrm[2 * jj + 1]);
       }
     }
   }
