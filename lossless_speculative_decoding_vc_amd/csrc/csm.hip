@@ -52,7 +52,7 @@ __global__ __launch_bounds__(256) void csm_round_kernel(CsmParams p) {
   // channel-major, as in the source; rows padded by 8 bytes so that lanes reading one token of 64 different
   // channels spread over the banks
   __shared__ __attribute__((aligned(16))) uint16_t vs[kD][kMaxChunk + 4];
-  __shared__ float nrm[kMaxChunk], dg[kMaxChunk];
+  __shared__ float dg[kMaxChunk];
   __shared__ __attribute__((aligned(16))) float sim[kMaxChunk / 2][kMaxChunk / 2];
   __shared__ float score[kMaxChunk / 2];
   __shared__ int match[kMaxChunk / 2], mergedA[kMaxChunk / 2];
@@ -135,27 +135,13 @@ __global__ __launch_bounds__(256) void csm_round_kernel(CsmParams p) {
   }
   for (int t = tid; t < L; t += 256) dg[t] = idg ? idg[s0 + t] : 1.f;
   __syncthreads();
-  // key norms: four lanes per token, each summing a quarter of the channels,
-  // the quarters added in a fixed order
-  for (int t0 = 0; t0 < L; t0 += 64) {
-    const int t = t0 + (tid >> 2), qq = tid & 3;
-    float acc = 0.f;
-    if (t < L) {
-#pragma unroll
-      for (int q = 4 * qq; q < 4 * qq + 4; ++q) {
-        const u32x4 w = *reinterpret_cast<const u32x4 *>(&ks[t][8 * q]);
-        acc = dot8(w, w, acc);
-      }
-    }
-    const float a1 = acc + __shfl_xor(acc, 1, 64);
-    const float a2 = a1 + __shfl_xor(a1, 2, 64);
-    if (t < L && qq == 0) nrm[t] = 1.f / sqrtf(a2);   // the inverse norm
-  }
-  __syncthreads();
   // cosines of A token i (position 2i) with B token j (position 2j+1): the
   // dot products as 16x16 tiles of v_mfma_f32_16x16x32_bf16 (bf16 products
   // are exact in its fp32 accumulation) times the two inverse norms, one tile
-  // per wave in turn; rows past nA / nB read row 0 and are not stored
+  // per wave in turn; rows past nA / nB read row 0 and are not stored.  The
+  // norms come from the same operand registers: lane (col, grp) holds a
+  // quarter of row col's channels over the four k-steps, the four quarters
+  // meet by two shuffles (in a fixed order).
   {
     const int wave = tid >> 6, lane = tid & 63, col = lane & 15, grp = lane >> 4;
     const int tA = (nA + 15) / 16, tB = (nB + 15) / 16;
@@ -164,17 +150,26 @@ __global__ __launch_bounds__(256) void csm_round_kernel(CsmParams p) {
       const int ia = 16 * ti + col, jb = 16 * tj + col;
       const int ra = ia < nA ? 2 * ia : 0, rb = jb < nB ? 2 * jb + 1 : 0;
       f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+      float na = 0.f, nb = 0.f;
 #pragma unroll
       for (int k = 0; k < kD / 32; ++k) {
         const u32x4 a = *reinterpret_cast<const u32x4 *>(&ks[ra][32 * k + 8 * grp]);
         const u32x4 b = *reinterpret_cast<const u32x4 *>(&ks[rb][32 * k + 8 * grp]);
         acc = mfma16x16x32(as_bf16x8(a), as_bf16x8(b), acc);
+        na = dot8(a, a, na);
+        nb = dot8(b, b, nb);
       }
+      na += __shfl_xor(na, 16, 64);
+      na += __shfl_xor(na, 32, 64);
+      nb += __shfl_xor(nb, 16, 64);
+      nb += __shfl_xor(nb, 32, 64);
+      const float rna = 1.f / sqrtf(na), rnb = 1.f / sqrtf(nb);   // rows ia and jb
       // lane holds S[16 ti + 4 grp + i][16 tj + col]
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int ii = 16 * ti + 4 * grp + i, jj = 16 * tj + col;
-        if (ii < nA && jj < nB) sim[ii][jj] = acc[i] * (nrm[2 * ii] * nrm[2 * jj + 1]);
+        const float ra_i = __shfl(rna, 4 * grp + i, 64);   // inverse norm of A row 4 grp + i of the tile
+        if (ii < nA && jj < nB) sim[ii][jj] = acc[i] * (ra_i * rnb);
       }
     }
   }
@@ -214,40 +209,26 @@ __global__ __launch_bounds__(256) void csm_round_kernel(CsmParams p) {
   __syncthreads();
   // survivors (B tokens and unmerged A tokens) in position order: surv[k] is
   // the chunk position of output slot base + k; amask[j] holds the A tokens
-  // merged into B token j
+  // merged into B token j.  Every wave takes the merge flags of all A tokens
+  // (at most 64) as one ballot, so a survivor's slot is a popcount.
   {
-    // merge flags of the A tokens as bit masks (A token i = bit i), one 64-bit
-    // word per 64 A tokens, so survivor slots are popcounts
-    __shared__ unsigned long long mmask[kMaxChunk / 128 + 1];
-    if (tid < 64 * ((nA + 63) / 64)) {
-      const unsigned long long bal = __ballot(tid < nA && mergedA[tid]);
-      if ((tid & 63) == 0) mmask[tid >> 6] = bal;
-    }
-    __syncthreads();
+    const int wave = tid >> 6, lane = tid & 63;
+    const bool mg = lane < nA && mergedA[lane];
+    const unsigned long long mm = __ballot(mg);
     if (tid < L) {
       const int t = tid;
-      if ((t & 1) || !mergedA[t >> 1]) {
+      if ((t & 1) || !((mm >> (t >> 1)) & 1ull)) {
         const int na_below = (t + 1) >> 1;   // A tokens at positions below t
-        int below = 0;
-#pragma unroll
-        for (int w = 0; w * 64 < kMaxChunk / 2; ++w) {
-          const int bits = min(64, max(0, na_below - 64 * w));
-          const unsigned long long msk = bits >= 64 ? ~0ull : ((1ull << bits) - 1);
-          below += __popcll(mmask[w] & msk);
-        }
-        surv[t - below] = t;
+        const unsigned long long msk = na_below >= 64 ? ~0ull : ((1ull << na_below) - 1);
+        surv[t - __popcll(mm & msk)] = t;
       }
     }
     // members of each B token as a bit mask over the A tokens (ascending bit = ascending position): one
     // ballot per B token, the B tokens dealt round-robin to the four waves
-    {
-      const int wave = tid >> 6, lane = tid & 63;
-      const bool mg = lane < nA && mergedA[lane];
-      const int mt = lane < nA ? match[lane] : -1;
-      for (int j = wave; j < nB; j += 4) {
-        const unsigned long long bal = __ballot(mg && mt == j);
-        if (lane == 0) amask[j] = bal;
-      }
+    const int mt = lane < nA ? match[lane] : -1;
+    for (int j = wave; j < nB; j += 4) {
+      const unsigned long long bal = __ballot(mg && mt == j);
+      if (lane == 0) amask[j] = bal;
     }
   }
   __syncthreads();
@@ -255,34 +236,28 @@ __global__ __launch_bounds__(256) void csm_round_kernel(CsmParams p) {
   // Output: survivor k (chunk position surv[k]) goes to slot base + k.  A
   // cluster (a B token with merged A tokens) is its own degree-weighted value
   // plus its members' in ascending position, times the inverse total degree;
-  // other survivors are copied bit-exactly.  Per survivor first (one thread
-  // each): its member mask, total degree and inverse.
-  // (held in the similarity matrix's space, no longer read)
+  // other survivors are copied bit-exactly.  The K rows go first, 16 lanes per
+  // survivor (16-byte pieces), 16 survivors at a time; lane 0 of a survivor
+  // also keeps its member mask and inverse degree for the V pass (in the
+  // similarity matrix's space, no longer read) and writes its degree.
   static_assert(sizeof(sim) >= kMaxChunk * (sizeof(unsigned long long) + sizeof(float)), "per-survivor data fits");
   unsigned long long *smask = reinterpret_cast<unsigned long long *>(&sim[0][0]);
   float *sinv = reinterpret_cast<float *>(smask + kMaxChunk);
-  for (int k = tid; k < ns; k += 256) {
-    const int t = surv[k];
-    const unsigned long long mk = (t & 1) ? amask[t >> 1] : 0ull;
-    float w = dg[t];
-    for (unsigned long long b = mk; b; b &= b - 1) w += dg[2 * __builtin_ctzll(b)];
-    smask[k] = mk;
-    sinv[k] = 1.f / w;
-    odg[base + k] = w;
-  }
-  __syncthreads();
-  // K rows: 16 lanes per survivor (16-byte pieces), 16 survivors at a time
   for (int k = tid >> 4; k < ns; k += 16) {
     const int t = surv[k], q = tid & 15;
-    const unsigned long long mk = smask[k];
+    const unsigned long long mk = (t & 1) ? amask[t >> 1] : 0ull;
     const u32x4 xt = *reinterpret_cast<const u32x4 *>(&ks[t][8 * q]);
     u32x4 *dst = reinterpret_cast<u32x4 *>(ok + (size_t)(base + k) * kD + 8 * q);
+    const float dt = dg[t];
     if (!mk) {
       *dst = xt;
+      if (q == 0) {
+        smask[k] = 0ull;
+        odg[base + k] = dt;
+      }
       continue;
     }
-    const float inv = sinv[k], dt = dg[t];
-    float acc[8];
+    float w = dt, acc[8];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       acc[2 * j] = dt * bf16_lo(xt[j]);
@@ -292,16 +267,23 @@ __global__ __launch_bounds__(256) void csm_round_kernel(CsmParams p) {
       const int a2 = 2 * __builtin_ctzll(b);
       const u32x4 xa = *reinterpret_cast<const u32x4 *>(&ks[a2][8 * q]);
       const float wa = dg[a2];
+      w += wa;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         acc[2 * j] = fmaf(wa, bf16_lo(xa[j]), acc[2 * j]);
         acc[2 * j + 1] = fmaf(wa, bf16_hi(xa[j]), acc[2 * j + 1]);
       }
     }
+    const float inv = 1.f / w;
     u32x4 kw;
 #pragma unroll
     for (int j = 0; j < 4; ++j) kw[j] = pack_bf16x2(acc[2 * j] * inv, acc[2 * j + 1] * inv);
     *dst = kw;
+    if (q == 0) {
+      smask[k] = mk;
+      sinv[k] = inv;
+      odg[base + k] = w;
+    }
   }
   __syncthreads();
   // V: the output tile [channel][survivor] is formed in LDS (over the key
