@@ -100,6 +100,7 @@ struct CsmParams {
   uint16_t *out_k, *out_v;
   float *out_deg;
   int32_t *out_len;   // optional [BH]: set to n_out (the drafter's main_len)
+  int row = 0, BH = 0;   // set by launch_csm_round: workgroups per (b, KV head) and the slice count
 };
 int csm_survivors(int n_in, int n_sink, int n_recent, int chunk, double r);
 hipError_t launch_csm_round(const CsmParams &p, int BH, hipStream_t s);
