@@ -75,6 +75,7 @@ struct QuantParams {
   // token 0 of the tail to dst_start[bh]; the grid's group count is a bound
   const int32_t *tail_len = nullptr, *n_add = nullptr;
   int Hkv = 1, M = 0;
+  int n_groups = 0;   // set by launch_quantize_int4: groups per (b, KV head) in the grid
 };
 
 // Rows of a request's bf16 tail after appending n_out of a block of M rows:
