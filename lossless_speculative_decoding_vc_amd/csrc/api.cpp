@@ -436,7 +436,9 @@ vc_status vc_csm_round(int32_t B, int32_t Hkv, int32_t D, int32_t n_in, int32_t 
   REQ(n_in <= cap_in && cap_in % 32 == 0 && cap_out % 32 == 0, "n_in <= cap_in; caps multiples of 32");
   const int out = vc::csm_survivors(n_in, n_sink, n_recent, chunk, r);
   REQ(out <= cap_out, "the round keeps %d tokens; cap_out is %lld", out, (long long)cap_out);
-  REQ((int64_t)(n_in - n_sink - n_recent + chunk - 1) / chunk + 2 <= 2147483647, "too many chunks");
+  // one 256-thread workgroup per chunk on the x dimension of the grid, whose work-item count is 32-bit
+  REQ((int64_t)(n_in - n_sink - n_recent + chunk - 1) / chunk + 2 <= (1 << 24) - 1,
+      "too many chunks: at most 2^24 - 3 per (request, KV head)");
   *n_out = out;
   if (B == 0) return VC_OK;
   REQ(in_k && in_v && out_k && out_v && out_deg, "null pointer");

@@ -58,6 +58,20 @@ VC_DEVICE float wave_sum(float v) {
   return v;
 }
 
+// The hardware hands workgroups to the eight XCDs round-robin by linear
+// index (x fastest).  xcd_order remaps a 2-D grid so that each XCD runs a
+// contiguous range of (x, y) in row-major order: neighbouring blocks of x,
+// which share cache lines at their boundaries, then go through one L2.
+VC_DEVICE void xcd_order(int &x, int &y) {
+  const int64_t nx = gridDim.x, total = nx * gridDim.y;
+  const int64_t L = (int64_t)blockIdx.y * nx + blockIdx.x;
+  const int64_t xcd = L % 8, q = L / 8;
+  const int64_t base_n = total / 8, extra = total % 8;   // XCD xcd runs base_n + (xcd < extra) workgroups
+  const int64_t v = xcd * base_n + (xcd < extra ? xcd : extra) + q;
+  y = (int)(v / nx);
+  x = (int)(v % nx);
+}
+
 VC_DEVICE f32x4 mfma16x16x32(const bf16x8 &a, const bf16x8 &b, const f32x4 &c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }

@@ -58,21 +58,13 @@ __global__ __launch_bounds__(256) void csm_round_kernel(CsmParams p) {
   __shared__ int match[kMaxChunk / 2], mergedA[kMaxChunk / 2];
   __shared__ int surv[kMaxChunk];
   __shared__ unsigned long long amask[kMaxChunk / 2];   // B token j: bit i set iff A token i merges into it
-  // Workgroups go to the eight XCDs round-robin by their linear index; the
-  // index is remapped so that each XCD runs a contiguous run of chunks, and
-  // the 32-token V blocks two neighbouring chunks share are fetched and
-  // written through one L2.
+  // each XCD runs a contiguous run of chunks, so the 32-token V blocks two
+  // neighbouring chunks share are fetched and written through one L2
   const int tid = threadIdx.x;
-  const int nchunks = p.row - 2;
+  const int nchunks = (int)gridDim.x - 2;
   int bh, c;
-  {
-    const int64_t L = blockIdx.x, total = (int64_t)p.row * p.BH;
-    const int64_t x = L % 8, q = L / 8;
-    const int64_t base_n = total / 8, extra = total % 8;   // XCD x runs base_n + (x < extra) workgroups
-    const int64_t v = x * base_n + min(x, extra) + q;
-    bh = (int)(v / p.row);
-    c = (int)(v % p.row) - 1;   // -1: sinks, nchunks: recent tokens
-  }
+  xcd_order(c, bh);
+  c -= 1;   // -1: sinks, nchunks: recent tokens
   const uint16_t *ik = p.in_k + (size_t)bh * p.cap_in * kD;
   const uint16_t *iv = p.in_v + (size_t)bh * p.cap_in * kD;
   const float *idg = p.in_deg ? p.in_deg + (size_t)bh * p.cap_in : nullptr;
@@ -365,12 +357,8 @@ hipError_t launch_csm_round(const CsmParams &p, int BH, hipStream_t s) {
   const int mid = p.n_in - p.n_recent - p.n_sink;
   const int nchunks = mid > 0 ? (mid + p.chunk - 1) / p.chunk : 0;
   if (BH == 0) return hipSuccess;
-  CsmParams q = p;
-  q.row = nchunks + 2;
-  q.BH = BH;
-  const unsigned grid = (unsigned)((int64_t)q.row * BH);
-  if (p.chunk <= 64) csm_round_kernel<64><<<grid, 256, 0, s>>>(q);
-  else csm_round_kernel<128><<<grid, 256, 0, s>>>(q);
+  if (p.chunk <= 64) csm_round_kernel<64><<<dim3(nchunks + 2, BH), 256, 0, s>>>(p);
+  else csm_round_kernel<128><<<dim3(nchunks + 2, BH), 256, 0, s>>>(p);
   return hipGetLastError();
 }
 

@@ -75,7 +75,6 @@ struct QuantParams {
   // token 0 of the tail to dst_start[bh]; the grid's group count is a bound
   const int32_t *tail_len = nullptr, *n_add = nullptr;
   int Hkv = 1, M = 0;
-  int n_groups = 0;   // set by launch_quantize_int4: groups per (b, KV head) in the grid
 };
 
 // Rows of a request's bf16 tail after appending n_out of a block of M rows:
@@ -101,7 +100,6 @@ struct CsmParams {
   uint16_t *out_k, *out_v;
   float *out_deg;
   int32_t *out_len;   // optional [BH]: set to n_out (the drafter's main_len)
-  int row = 0, BH = 0;   // set by launch_csm_round: workgroups per (b, KV head) and the slice count
 };
 int csm_survivors(int n_in, int n_sink, int n_recent, int chunk, double r);
 hipError_t launch_csm_round(const CsmParams &p, int BH, hipStream_t s);

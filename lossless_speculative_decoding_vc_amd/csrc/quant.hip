@@ -87,18 +87,10 @@ __global__ __launch_bounds__(256) void quantize_int4(QuantParams p) {
   __shared__ __attribute__((aligned(16))) uint16_t vtile[D][kGroup];   // [channel][token]
   __shared__ uint8_t kcode[kGroup][D];
   __shared__ uint8_t vcode[D][kGroup];
-  // Workgroups go to the eight XCDs round-robin by their linear index; the
-  // index is remapped so that each XCD runs a contiguous run of groups, and
-  // the two groups whose V runs share a 128-byte line read it through one L2.
+  // each XCD runs a contiguous run of groups, so the two groups whose V runs
+  // share a 128-byte line read it through one L2
   int grp, bh;
-  {
-    const int64_t L = blockIdx.x, total = (int64_t)p.n_groups * p.BH;
-    const int64_t x = L % 8, q = L / 8;
-    const int64_t base_n = total / 8, extra = total % 8;   // XCD x runs base_n + (x < extra) workgroups
-    const int64_t v = x * base_n + min(x, extra) + q;
-    bh = (int)(v / p.n_groups);
-    grp = (int)(v % p.n_groups);
-  }
+  xcd_order(grp, bh);
   const int tid = threadIdx.x;
   int s0, d0;
   int64_t span;   // tokens of the whole call per (b, KV head)
@@ -113,7 +105,7 @@ __global__ __launch_bounds__(256) void quantize_int4(QuantParams p) {
   } else {
     s0 = p.src_start[bh];
     d0 = p.dst_start[bh];
-    span = (int64_t)p.n_groups * kGroup;
+    span = (int64_t)gridDim.x * kGroup;
   }
   // every workgroup of a (b, KV head) sees the same starts, so a slice whose
   // call would leave the source or the cache is skipped as a whole
@@ -195,9 +187,7 @@ __global__ __launch_bounds__(256) void quantize_int4(QuantParams p) {
 
 hipError_t launch_quantize_int4(const QuantParams &p, int n_groups, hipStream_t s) {
   if (n_groups == 0 || p.BH == 0) return hipSuccess;
-  QuantParams q = p;
-  q.n_groups = n_groups;
-  quantize_int4<128><<<(unsigned)((int64_t)n_groups * p.BH), 256, 0, s>>>(q);
+  quantize_int4<128><<<dim3(n_groups, p.BH), 256, 0, s>>>(p);
   return hipGetLastError();
 }
 
