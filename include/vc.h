@@ -435,7 +435,9 @@ vc_status vc_stagger_destroy(vc_stagger *s);
  * one cohort in both roles (a long context: "Supporto Architetturale"):
  * the verify stream waits for the draft steps, since it verifies the drafts
  * they write (verify_drafts may be drafts), while the copies of the first
- * layers already stream during the drafting.
+ * layers already stream during the drafting; with `fetch` the compressed
+ * cache itself comes over the link first (remote prefix caching) and each
+ * layer's first draft call waits for its part.
  * Every argument of every call is validated before anything is enqueued; on
  * VC_EINVAL nothing was enqueued (VC_EHIP: a launch failed part-way; the
  * caller synchronizes and discards the round).  The call returns without
@@ -471,6 +473,19 @@ typedef struct vc_round_commit {
 
 typedef void (*vc_round_hook)(void *ctx, int32_t layer, void *verify_stream);
 
+/* A copy a chained round starts before any other: the compressed cache of a
+ * request whose prefix is held in host memory ("Supporto Architetturale",
+ * remote prefix caching: the drafter needs only the compressed cache, so it
+ * starts once that has arrived while the full cache is still on its way).
+ * `bytes` from pinned host memory to a device buffer; the first draft step's
+ * call for `layer` waits for every fetch of that layer.                     */
+typedef struct vc_round_fetch {
+  const void *host_src;           /* pinned host                                     */
+  void       *dev_dst;            /* device, e.g. the layer's packed int4 cache      */
+  size_t      bytes;
+  int32_t     layer;              /* 0 .. layers-1                                   */
+} vc_round_fetch;
+
 typedef struct vc_round_desc {
   int32_t layers;                 /* 1 .. the stagger object's max_layers            */
   int32_t steps;                  /* draft steps (0: no drafting cohort)             */
@@ -501,6 +516,10 @@ typedef struct vc_round_desc {
   int32_t time_kernels;           /* 1: time each draft step's run of draft
                                      attention calls and every verify call with
                                      events on their streams (vc_stagger_round_times) */
+  const vc_round_fetch *fetch;    /* optional [n_fetch], VC_ROUND_CHAINED with steps
+                                     > 0 only: enqueued in order on the copy stream
+                                     ahead of the layer copies                       */
+  int32_t n_fetch;
 } vc_round_desc;
 
 vc_status vc_stagger_round(vc_stagger *s, const vc_round_desc *d, void *draft_stream, void *verify_stream);

@@ -80,6 +80,10 @@ class RoundCommit(ctypes.Structure):
 ROUND_HOOK = ctypes.CFUNCTYPE(None, _p, _i32, _p)
 
 
+class RoundFetch(ctypes.Structure):
+    _fields_ = [("host_src", _p), ("dev_dst", _p), ("bytes", ctypes.c_size_t), ("layer", _i32)]
+
+
 class RoundDesc(ctypes.Structure):
     _fields_ = [("layers", _i32), ("steps", _i32), ("mode", _i32),
                 ("lm_w", _p), ("Dm", _i32), ("V", _i32),
@@ -91,7 +95,7 @@ class RoundDesc(ctypes.Structure):
                 ("verify_hidden", _p), ("verify_drafts", _p), ("argmax", _p), ("accept_len", _p),
                 ("out_tokens", _p), ("n_out", _p), ("verify_lm_ws", _p), ("verify_lm_ws_bytes", ctypes.c_size_t),
                 ("commit", ctypes.POINTER(RoundCommit)), ("before_verify", ROUND_HOOK), ("hook_ctx", _p),
-                ("time_kernels", _i32)]
+                ("time_kernels", _i32), ("fetch", ctypes.POINTER(RoundFetch)), ("n_fetch", _i32)]
 
 
 ROUND_STAGGERED, ROUND_BULK, ROUND_CHAINED = 0, 1, 2
@@ -838,7 +842,8 @@ class Stagger:
     def round(self, layers, mode, lm_w, draft=None, step_tail_len=None, draft_hidden=None, drafts=None,
               draft_lm_ws=None, verify=None, host_kv=None, kv_bytes=0, v_offset=0, verify_hidden=None,
               verify_drafts=None, argmax=None, accept_len=None, out_tokens=None, n_out=None, verify_lm_ws=None,
-              commit=None, before_verify=None, time_kernels=False, draft_stream=None, verify_stream=None):
+              commit=None, before_verify=None, time_kernels=False, draft_stream=None, verify_stream=None,
+              fetch=None):
         """One round of the staggered schedule (``vc_stagger_round``), enqueued
         natively on ``draft_stream`` / ``verify_stream`` and the copy streams.
 
@@ -859,7 +864,11 @@ class Stagger:
         called on the host before each verify is enqueued.  ``time_kernels``
         times each draft step's run of draft attention calls and every verify
         call (:meth:`round_times`).  ``lm_w`` is the
-        vocab-major ``[V][Dm]`` LM head.  Returns without synchronizing."""
+        vocab-major ``[V][Dm]`` LM head.  ``fetch`` (chained mode): list of
+        ``(host_src, dev_dst, layer)`` -- pinned host tensor, device tensor of
+        the same byte size (a layer's compressed cache) -- copied over the link
+        ahead of everything else, each layer's first draft call waiting for its
+        copies (remote prefix caching).  Returns without synchronizing."""
         d = RoundDesc()
         keep = []
         d.layers, d.mode, d.time_kernels = int(layers), int(mode), 1 if time_kernels else 0
@@ -980,6 +989,18 @@ class Stagger:
                     cs[l].cap, cs[l].dst_v_blocked = cap, 1 if blocked else 0
                 keep.append(cs)
                 d.commit = ctypes.cast(cs, ctypes.POINTER(RoundCommit))
+        if fetch:
+            fs = (RoundFetch * len(fetch))()
+            for j, (hsrc, ddst, layer) in enumerate(fetch):
+                if hsrc.is_cuda or not hsrc.is_pinned():
+                    raise ValueError(f"fetch[{j}] source must be pinned host memory")
+                _dev(ddst, f"fetch[{j}] destination")
+                nb = hsrc.numel() * hsrc.element_size()
+                if ddst.numel() * ddst.element_size() != nb:
+                    raise ValueError(f"fetch[{j}]: source and destination sizes differ")
+                fs[j].host_src, fs[j].dev_dst, fs[j].bytes, fs[j].layer = hsrc.data_ptr(), ddst.data_ptr(), nb, int(layer)
+            keep.append(fs)
+            d.fetch, d.n_fetch = ctypes.cast(fs, ctypes.POINTER(RoundFetch)), len(fetch)
         if before_verify is not None:
             hook = ROUND_HOOK(lambda ctx, layer, stream: before_verify(int(layer), stream))
             keep.append(hook)

@@ -67,6 +67,17 @@ vc_status validate(const vc_stagger *s, const vc_round_desc *d) {
       if (st != VC_OK) return st;
     }
   }
+  if (d->n_fetch < 0) return bad("n_fetch must be >= 0");
+  if (d->n_fetch > 0) {
+    if (d->mode != VC_ROUND_CHAINED || k == 0) return bad("fetches need the chained mode with draft steps");
+    if (!d->fetch) return bad("null fetch list");
+    for (int j = 0; j < d->n_fetch; ++j) {
+      const vc_round_fetch &f = d->fetch[j];
+      if (!f.host_src || !f.dev_dst || f.bytes == 0 || f.layer < 0 || f.layer >= L)
+        return bad("fetch " + std::to_string(j) + ": null pointer, no bytes or layer outside 0.." +
+                   std::to_string(L - 1));
+    }
+  }
   if (d->verify) {
     if (!d->host_kv) return bad("a verifying cohort needs host_kv");
     if (d->kv_bytes > s->slot_bytes || d->v_offset >= d->kv_bytes || d->v_offset % 16)
@@ -131,10 +142,14 @@ struct RoundTimer {
   }
 };
 
-vc_status draft_step(const vc_round_desc *d, int i, void *ds, RoundTimer &tm) {
+vc_status draft_step(const vc_round_desc *d, int i, void *ds, RoundTimer &tm, const vc_stagger *s) {
   // one event pair around the step's back-to-back draft attention calls
   CHK(tm.begin((hipStream_t)ds, tm.every > 0));
   for (int l = 0; l < d->layers; ++l) {
+    if (i == 0)   // the first use of each layer's compressed cache waits for its fetches
+      for (int j = 0; j < d->n_fetch; ++j)
+        if (d->fetch[j].layer == l && hipStreamWaitEvent((hipStream_t)ds, s->fetch_ev[j], 0) != hipSuccess)
+          return vc::set_error(VC_EHIP, "waiting for a fetch");
     vc_draft_args a = d->draft[l];
     if (d->step_tail_len) a.tail_len = d->step_tail_len[i];
     CHK(vc_draft_attn(&a, ds));
@@ -174,16 +189,31 @@ extern "C" vc_status vc_stagger_round(vc_stagger *s, const vc_round_desc *d, voi
 
   std::vector<int> steps_after(L, 0);   // staggered: draft steps enqueued after each verify layer
   const bool first = d->mode != VC_ROUND_STAGGERED;   // bulk and chained: every draft step first
+  if (d->n_fetch > 0) {
+    // the compressed cache first, each copy followed by its completion event
+    while ((int)s->fetch_ev.size() < d->n_fetch) {
+      hipEvent_t e;
+      if (hipEventCreateWithFlags(&e, hipEventDisableTiming) != hipSuccess)
+        return vc::set_error(VC_EHIP, "creating fetch events");
+      s->fetch_ev.push_back(e);
+    }
+    for (int j = 0; j < d->n_fetch; ++j) {
+      const vc_round_fetch &f = d->fetch[j];
+      if (hipMemcpyAsync(f.dev_dst, f.host_src, f.bytes, hipMemcpyHostToDevice, s->h2d) != hipSuccess ||
+          hipEventRecord(s->fetch_ev[j], s->h2d) != hipSuccess)
+        return vc::set_error(VC_EHIP, "enqueueing a fetch");
+    }
+  }
   if (k > 0 && first) {
     for (int i = 0; i < (ns < L ? ns : L) && d->verify && d->mode == VC_ROUND_CHAINED; ++i)
       CHK(vc_stagger_stream_layer(s, i, d->host_kv[i], d->kv_bytes));   // chained: copies overlap the drafting
-    for (int i = 0; i < k; ++i) CHK(draft_step(d, i, draft_stream, tm));
+    for (int i = 0; i < k; ++i) CHK(draft_step(d, i, draft_stream, tm, s));
     if (d->mode == VC_ROUND_BULK) CHK(vc_stagger_after(s, draft_stream));   // no copy overlaps the drafting
   } else {
     for (int i = 0; i < k; ++i) ++steps_after[(int)((int64_t)i * L / k)];
   }
   if (!d->verify) {
-    for (int i = 0; i < k && !first; ++i) CHK(draft_step(d, i, draft_stream, tm));
+    for (int i = 0; i < k && !first; ++i) CHK(draft_step(d, i, draft_stream, tm, s));
     return VC_OK;
   }
   if (k > 0 && first) {
@@ -211,7 +241,7 @@ extern "C" vc_status vc_stagger_round(vc_stagger *s, const vc_round_desc *d, voi
     CHK(vt.end((hipStream_t)verify_stream, tm.every > 0));
     CHK(vc_stagger_release(s, l, verify_stream));
     if (l + ns < L) CHK(vc_stagger_stream_layer(s, l + ns, d->host_kv[l + ns], d->kv_bytes));
-    for (int c = 0; c < steps_after[l]; ++c) CHK(draft_step(d, step++, draft_stream, tm));
+    for (int c = 0; c < steps_after[l]; ++c) CHK(draft_step(d, step++, draft_stream, tm, s));
   }
   const vc_verify_args &v0 = d->verify[0];
   CHK(vc_lm_head_accept(v0.B, v0.M, d->Dm, d->V, d->verify_hidden, d->lm_w, d->verify_drafts, d->argmax,

@@ -164,7 +164,7 @@ vc_status vc_stagger_destroy(vc_stagger *s) {
   // for a later call to pick up
   if (s->h2d) (void)hipStreamSynchronize(s->h2d);
   if (s->d2h) (void)hipStreamSynchronize(s->d2h);
-  for (auto *v : {&s->slot_free, &s->copy_start, &s->copied, &s->round_ev})
+  for (auto *v : {&s->slot_free, &s->copy_start, &s->copied, &s->round_ev, &s->fetch_ev})
     for (auto e : *v)
       if (e) (void)hipEventDestroy(e);
   if (s->h2d) (void)hipStreamDestroy(s->h2d);

@@ -22,6 +22,8 @@ struct vc_stagger {
   // event pairs around the timed draft calls, then around every verify call
   std::vector<hipEvent_t> round_ev;
   int timed_drafts = 0, timed_verifies = 0;
+  // completion of a round's fetches (vc_round_desc::fetch), one event each
+  std::vector<hipEvent_t> fetch_ev;
 };
 
 namespace vc {

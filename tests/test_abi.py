@@ -50,6 +50,7 @@ def _c_layout(struct, fields):
                                        (vcb.AcceptArgs, "vc_accept_args"),
                                        (vcb.RoundCommit, "vc_round_commit"),
                                        (vcb.RoundDesc, "vc_round_desc"),
+                                       (vcb.RoundFetch, "vc_round_fetch"),
                                        ("TinyModelArgs", "vc_tiny_model"),
                                        ("TinyAttnArgs", "vc_tiny_attn")])
 def test_struct_layout_matches_header(cls, cname):

@@ -9,7 +9,9 @@ full cache drops its groups.  Then one chained round (one request drafting
 and verifying its own drafts, the copies of the first layers streaming during
 the drafting) with the int4 commit inside gives the same bits as the same
 calls made one by one, with the draft stream held back so a missing wait
-would show."""
+would show; and so does the same round with every layer's packed cache
+fetched from pinned host memory first (remote prefix caching, "Supporto
+Architetturale"), the device copies holding garbage until their fetch."""
 import numpy as np
 import pytest
 
@@ -184,37 +186,53 @@ def test_chained_round_with_int4_commit_equals_the_calls_one_by_one():
     ref = outputs(st, out)
     np.testing.assert_array_equal(ref["drafts"], d)
     np.testing.assert_array_equal(ref["al"], n)
-    # 2. the chained round, the draft stream held back by a spin first
-    st, out = fresh()
-    slots = [torch.empty(2 * half, dtype=torch.uint8, device=dev) for _ in range(2)]
-    stg = vc.Stagger(slots, 2 * half, L)
-    ds, vs = torch.cuda.Stream(), torch.cuda.Stream()
-    try:
-        draft = [vc.draft_args(dq[l], st[l]["packed"], None, st[l]["main_len"], tail_k=st[l]["tail_k"],
-                               tail_v=st[l]["tail_v"], tail_len=tl_steps[r0 + 1:r0 + 2], out=out["dout"][l],
-                               fmt=vc.VC_KV_INT4_PACKED) for l in range(L)]
-        verify = [vc.verify_args(vq[l], None, None, cl, bk[l], bv[l], out["vout"][l], ccap=N) for l in range(L)]
-        commit = [dict(int4=True, **{k: st[l][k] for k in ("tail_k", "tail_v", "tail_len", "packed", "main_len")})
-                  for l in range(L)]
-        torch.cuda.synchronize()
-        with torch.cuda.stream(ds):
-            torch.cuda._sleep(20_000_000)   # a few milliseconds of spinning, then it exits
-        stg.round(L, vc.ROUND_CHAINED, W, draft=draft,
-                  step_tail_len=[tl_steps[r0 + i + 1:r0 + i + 2] for i in range(K)], draft_hidden=hd,
-                  drafts=out["drafts"], verify=verify, host_kv=host, kv_bytes=2 * half, v_offset=half,
-                  verify_hidden=hv, verify_drafts=out["drafts"], argmax=out["am"], accept_len=out["al"],
-                  out_tokens=out["toks"], n_out=out["nout"], commit=commit, draft_stream=ds, verify_stream=vs)
-        torch.cuda.synchronize()
-        stg.sync()
-    finally:
-        stg.close()
-    got = outputs(st, out)
-    for key in ref:
-        a, b_ = ref[key], got[key]
-        if isinstance(a, list):
-            for i, (x, z) in enumerate(zip(a, b_)):
-                np.testing.assert_array_equal(x, z, err_msg=f"{key}[{i}]")
-        else:
-            np.testing.assert_array_equal(a, b_, err_msg=key)
+    # 2. the chained round, the draft stream held back by a spin first; 3. the
+    # same round with every layer's packed cache fetched from pinned host
+    # memory over the link first (remote prefix caching), the device copy
+    # holding garbage until then
+    def chained(remote):
+        st, out = fresh()
+        fetch = None
+        if remote:
+            fetch = []
+            for l in range(L):
+                h = torch.empty(st[l]["packed"].numel(), dtype=torch.uint8, pin_memory=True)
+                h.copy_(st[l]["packed"].reshape(-1).cpu())
+                st[l]["packed"].fill_(0xA5)
+                fetch.append((h, st[l]["packed"], l))
+        slots = [torch.empty(2 * half, dtype=torch.uint8, device=dev) for _ in range(2)]
+        stg = vc.Stagger(slots, 2 * half, L)
+        ds, vs = torch.cuda.Stream(), torch.cuda.Stream()
+        try:
+            draft = [vc.draft_args(dq[l], st[l]["packed"], None, st[l]["main_len"], tail_k=st[l]["tail_k"],
+                                   tail_v=st[l]["tail_v"], tail_len=tl_steps[r0 + 1:r0 + 2], out=out["dout"][l],
+                                   fmt=vc.VC_KV_INT4_PACKED) for l in range(L)]
+            verify = [vc.verify_args(vq[l], None, None, cl, bk[l], bv[l], out["vout"][l], ccap=N) for l in range(L)]
+            commit = [dict(int4=True, **{k: st[l][k] for k in ("tail_k", "tail_v", "tail_len", "packed", "main_len")})
+                      for l in range(L)]
+            torch.cuda.synchronize()
+            with torch.cuda.stream(ds):
+                torch.cuda._sleep(20_000_000)   # a few milliseconds of spinning, then it exits
+            stg.round(L, vc.ROUND_CHAINED, W, draft=draft,
+                      step_tail_len=[tl_steps[r0 + i + 1:r0 + i + 2] for i in range(K)], draft_hidden=hd,
+                      drafts=out["drafts"], verify=verify, host_kv=host, kv_bytes=2 * half, v_offset=half,
+                      verify_hidden=hv, verify_drafts=out["drafts"], argmax=out["am"], accept_len=out["al"],
+                      out_tokens=out["toks"], n_out=out["nout"], commit=commit, draft_stream=ds, verify_stream=vs,
+                      fetch=fetch)
+            torch.cuda.synchronize()
+            stg.sync()
+        finally:
+            stg.close()
+        return outputs(st, out)
+
+    for remote in (False, True):
+        got = chained(remote)
+        for key in ref:
+            a, b_ = ref[key], got[key]
+            if isinstance(a, list):
+                for i, (x, z) in enumerate(zip(a, b_)):
+                    np.testing.assert_array_equal(x, z, err_msg=f"{key}[{i}] (remote {remote})")
+            else:
+                np.testing.assert_array_equal(a, b_, err_msg=f"{key} (remote {remote})")
     # n = 3 accepted: 4 rows join the 10-row residual, no group is full yet
     assert got["tail_len"][0].tolist() == [14] and got["main_len"][0].tolist() == [[1536, 1536]]

@@ -247,6 +247,10 @@ def test_round_rejects_bad_descriptors_before_enqueueing(inp):
             stg.round(L + 1, vc.ROUND_STAGGERED, W)
         with pytest.raises(vc.VcError, match="mode"):
             stg.round(L, 7, W)
+        # fetches belong to a chained round with draft steps
+        h = torch.zeros(64, dtype=torch.uint8, pin_memory=True)
+        with pytest.raises(vc.VcError, match="chained"):
+            stg.round(L, vc.ROUND_STAGGERED, W, fetch=[(h, torch.zeros(64, dtype=torch.uint8, device=dev), 0)])
         # a slot still holding an unreleased layer refuses a new round
         stg.stream_layer(0, inp.host_kv[0], 2 * inp.half)
         with pytest.raises(vc.VcError, match="unreleased"):
