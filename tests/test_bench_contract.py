@@ -46,6 +46,6 @@ def test_every_kernel_leg_names_its_kernel():
         bench.parse()
     finally:
         argparse.ArgumentParser.parse_args = orig
-    rounds = {"stagger128k", "long1m", "tiny"}
+    rounds = {"stagger128k", "long1m", "remote1m", "tiny"}
     legs = [w for w in captured["choices"] if w not in rounds]
     assert legs and all(w in bench.KERNEL_OF for w in legs), set(legs) - set(bench.KERNEL_OF)
