@@ -6,12 +6,13 @@ Default workload -- the staggered mixed batch at Qwen-32B layer shape
 
 * cohort X (16 requests) VERIFIES a k = 32 block (M = 33 rows) against its
   full 131072-token cache, which is streamed layer by layer from pinned host
-  memory over PCIe into a ring of two 8 GiB HBM slots (``vc_stagger``), then
+  memory over PCIe into a ring of six 8 GiB HBM slots (``vc_stagger``), then
   takes the block rows through a 5120 x 32768 bf16 LM head fused with the
   greedy argmax and the acceptance (``vc_lm_head_accept``: no logits reach
   HBM), accepts up to the first mismatch (+ bonus) and commits the verified
   rows (device append + host write-back);
-* cohort Y (16 requests) meanwhile DRAFTS its next 32 tokens: per step and
+* cohort Y (16 requests) meanwhile DRAFTS its next 32 tokens, the steps back
+  to back on their own stream while the first layers stream in: per step and
   layer, decode attention over its 25%-compressed cache (32768 kept tokens
   with log-degree bias, plus the draft tail) in HBM, then per step the LM head
   fused with the argmax (``vc_lm_head_argmax``).
@@ -91,6 +92,7 @@ def parse():
     ap.add_argument("--iters", type=int, default=50, help="kernel-alone iterations")
     ap.add_argument("--splits", type=int, default=0, help="kernel-alone split count (0 = library default)")
     ap.add_argument("--sets", type=int, default=4, help="draft_cohort: rotating compressed caches")
+    ap.add_argument("--slots", type=int, default=6, help="stagger128k: 8 GiB HBM staging slots of the full cache")
     args = ap.parse_args()
     if args.layers is None:
         args.layers = 40 if args.workload in ("long1m", "remote1m") else 64
@@ -208,8 +210,8 @@ class Cohort:
 
 def run_stagger(args, t_start):
     """Rounds of the staggered batch, each enqueued natively by ``vc_stagger_round``: the drafting cohort's 32
-    steps over 64 layers on one stream, the verifying cohort's 64 layers (each after its layer's copy into the
-    two-slot ring) and its LM head + acceptance + commit on another, the copy engines streaming throughout."""
+    steps over 64 layers back to back on one stream, the verifying cohort's 64 layers (each after its layer's copy
+    into the slot ring) and its LM head + acceptance + commit on another, the copy engines streaming throughout."""
     import torch
     import lossless_speculative_decoding_vc_amd as vc
     c = Cfg()
@@ -219,11 +221,11 @@ def run_stagger(args, t_start):
     W = _bf16_randn((c.V, c.Dm), 3, dev, std=0.02)   # LM head, vocab-major
     X = Cohort(c, "A", L, NLD, W, seed=4)
     Y = Cohort(c, "B", L, NLD, W, seed=40)
-    # full cache: two 8 GiB HBM staging slots fed from two pinned 8 GiB host
+    # full cache: args.slots 8 GiB HBM staging slots fed from two pinned 8 GiB host
     # buffers (layers rotate over them; content does not change the traffic)
     kv_half = c.B * c.Hkv * c.N * c.D * 2          # bytes of K (and of V) per layer
     slot_bytes = 2 * kv_half
-    slots = [torch.empty(slot_bytes, dtype=torch.uint8, device=dev) for _ in range(2)]
+    slots = [torch.empty(slot_bytes, dtype=torch.uint8, device=dev) for _ in range(args.slots)]
     g = torch.Generator(device=dev)
     g.manual_seed(99)
     slots[0].view(torch.bfloat16).normal_(0.0, 1.0, generator=g)

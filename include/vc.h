@@ -426,11 +426,14 @@ vc_status vc_stagger_destroy(vc_stagger *s);
  *     then per layer the commit of the verified rows: vc_commit_rows of
  *     verify[l]'s block into commit[l] and the write-back of the block's K
  *     and V rows to commit[l].host_k / host_v.
- * mode VC_ROUND_STAGGERED spreads the draft steps over the verify layers
- * (step i is enqueued after layer floor(i * layers / steps)) and the copies
- * run while the drafting cohort computes; VC_ROUND_BULK is the
- * bulk-synchronous comparison: every draft step first, and the copy and
- * verify streams wait for them.  Both modes run the same kernels on the same
+ * mode VC_ROUND_STAGGERED enqueues the first nslots layer copies, then every
+ * draft step back to back on the draft stream, then the verify layers, with
+ * no wait between the two compute streams: the copies run while the drafting
+ * cohort computes.  The verify kernels that free the slots queue behind the
+ * draft kernels for the CUs, so the ring needs enough slots to keep the link
+ * busy through the drafting (six of 8 GiB at the 128K shape; two stall it).
+ * VC_ROUND_BULK is the bulk-synchronous comparison: every draft step first,
+ * and the copy and verify streams wait for them.  Both modes run the same kernels on the same
  * inputs, so their outputs are identical bit for bit.  VC_ROUND_CHAINED is
  * one cohort in both roles (a long context: "Supporto Architetturale"):
  * the verify stream waits for the draft steps, since it verifies the drafts

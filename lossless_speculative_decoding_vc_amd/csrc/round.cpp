@@ -9,14 +9,15 @@
 // the first mismatch (plus the bonus), restart from the last accepted token.
 //
 // vc_stagger_round checks every call of the round first and then enqueues
-// the whole round from the host in one pass: the drafting cohort's k steps
-// (every layer's draft attention, then the LM head fused with the argmax) on
-// the draft stream, the verifying cohort's layers on the verify stream, each
-// after its layer's host-to-device copy into the slot ring, then the fused LM
-// head + acceptance and the commit of the verified rows.  The draft stream
-// never waits for a copy, so the copy engines stream the next layers while
-// the drafting cohort computes; in the bulk-synchronous mode every draft step
-// comes first and the copy and verify streams wait for them.
+// the whole round from the host in one pass: the first layers' copies into
+// the slot ring, the drafting cohort's k steps back to back (every layer's
+// draft attention, then the LM head fused with the argmax) on the draft
+// stream, the verifying cohort's layers on the verify stream, each after its
+// layer's host-to-device copy, then the fused LM head + acceptance and the
+// commit of the verified rows.  The draft stream never waits for a copy, so
+// the copy engines stream the next layers while the drafting cohort
+// computes; in the bulk-synchronous mode every draft step comes first and the
+// copy and verify streams wait for them.
 #include <hip/hip_runtime.h>
 
 #include <cstdio>
@@ -187,8 +188,6 @@ extern "C" vc_status vc_stagger_round(vc_stagger *s, const vc_round_desc *d, voi
   }
   RoundTimer vt{s, 0, tm.every ? k : 0};
 
-  std::vector<int> steps_after(L, 0);   // staggered: draft steps enqueued after each verify layer
-  const bool first = d->mode != VC_ROUND_STAGGERED;   // bulk and chained: every draft step first
   if (d->n_fetch > 0) {
     // the compressed cache first, each copy followed by its completion event
     while ((int)s->fetch_ev.size() < d->n_fetch) {
@@ -204,19 +203,15 @@ extern "C" vc_status vc_stagger_round(vc_stagger *s, const vc_round_desc *d, voi
         return vc::set_error(VC_EHIP, "enqueueing a fetch");
     }
   }
-  if (k > 0 && first) {
-    for (int i = 0; i < (ns < L ? ns : L) && d->verify && d->mode == VC_ROUND_CHAINED; ++i)
-      CHK(vc_stagger_stream_layer(s, i, d->host_kv[i], d->kv_bytes));   // chained: copies overlap the drafting
-    for (int i = 0; i < k; ++i) CHK(draft_step(d, i, draft_stream, tm, s));
-    if (d->mode == VC_ROUND_BULK) CHK(vc_stagger_after(s, draft_stream));   // no copy overlaps the drafting
-  } else {
-    for (int i = 0; i < k; ++i) ++steps_after[(int)((int64_t)i * L / k)];
-  }
-  if (!d->verify) {
-    for (int i = 0; i < k && !first; ++i) CHK(draft_step(d, i, draft_stream, tm, s));
-    return VC_OK;
-  }
-  if (k > 0 && first) {
+  // the first layers' copies (staggered and chained: they overlap the drafting), then every draft step back
+  // to back on the draft stream
+  const bool early_copies = k > 0 && d->verify && d->mode != VC_ROUND_BULK;
+  for (int i = 0; early_copies && i < (ns < L ? ns : L); ++i)
+    CHK(vc_stagger_stream_layer(s, i, d->host_kv[i], d->kv_bytes));
+  for (int i = 0; i < k; ++i) CHK(draft_step(d, i, draft_stream, tm, s));
+  if (k > 0 && d->mode == VC_ROUND_BULK) CHK(vc_stagger_after(s, draft_stream));   // no copy overlaps the drafting
+  if (!d->verify) return VC_OK;
+  if (k > 0 && d->mode != VC_ROUND_STAGGERED) {
     // the verify stream starts after the drafting cohort as well
     hipEvent_t ev;
     if (hipEventCreateWithFlags(&ev, hipEventDisableTiming) != hipSuccess)
@@ -226,9 +221,8 @@ extern "C" vc_status vc_stagger_round(vc_stagger *s, const vc_round_desc *d, voi
     (void)hipEventDestroy(ev);
     if (e != hipSuccess) return vc::set_error(VC_EHIP, hipGetErrorString(e));
   }
-  if (!(k > 0 && d->mode == VC_ROUND_CHAINED))
+  if (!early_copies)
     for (int l = 0; l < (ns < L ? ns : L); ++l) CHK(vc_stagger_stream_layer(s, l, d->host_kv[l], d->kv_bytes));
-  int step = 0;
   for (int l = 0; l < L; ++l) {
     void *slot = nullptr;
     CHK(vc_stagger_acquire(s, l, verify_stream, &slot));
@@ -241,7 +235,6 @@ extern "C" vc_status vc_stagger_round(vc_stagger *s, const vc_round_desc *d, voi
     CHK(vt.end((hipStream_t)verify_stream, tm.every > 0));
     CHK(vc_stagger_release(s, l, verify_stream));
     if (l + ns < L) CHK(vc_stagger_stream_layer(s, l + ns, d->host_kv[l + ns], d->kv_bytes));
-    for (int c = 0; c < steps_after[l]; ++c) CHK(draft_step(d, step++, draft_stream, tm, s));
   }
   const vc_verify_args &v0 = d->verify[0];
   CHK(vc_lm_head_accept(v0.B, v0.M, d->Dm, d->V, d->verify_hidden, d->lm_w, d->verify_drafts, d->argmax,
