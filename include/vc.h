@@ -40,7 +40,9 @@
 extern "C" {
 #endif
 
-typedef enum { VC_OK = 0, VC_EINVAL = 1, VC_ENOTSUP = 2, VC_EHIP = 3 } vc_status;
+/* The last enumerator keeps the type int-sized and makes every non-negative
+ * int a valid value, so a caller may pass any such code to vc_status_string. */
+typedef enum { VC_OK = 0, VC_EINVAL = 1, VC_ENOTSUP = 2, VC_EHIP = 3, VC_STATUS_MAX_ = 0x7fffffff } vc_status;
 typedef enum { VC_BF16 = 0, VC_FP32 = 1 } vc_dtype;
 typedef enum { VC_KV_DENSE = 0, VC_KV_INT4 = 1, VC_KV_INT4_PACKED = 2 } vc_kv_format;
 
@@ -201,7 +203,7 @@ vc_status vc_argmax(int32_t R, int32_t V, int32_t logit_dtype, const void *logit
  *   logit[r][v] = sum_k h[r][k] * w[v][k]
  * computed in fp32 from bf16 products (MFMA) without writing the logits.
  *   h [R][Dm] bf16, w [V][Dm] bf16 (vocab-major: a linear layer's weight),
- *   both 16-byte aligned; Dm % 32 == 0; out int32 (device).
+ *   both 16-byte aligned; Dm % 32 == 0, Dm <= 2^20, V <= 2^30; out int32 (device).
  * NaN logits never win (a row of NaN gives 0).  The summation order is the
  * kernel's own, so at a near tie (logits equal to fp32 rounding) another
  * GEMM followed by vc_argmax may pick a different maximum.  workspace: device buffer of
@@ -348,7 +350,7 @@ vc_status vc_quantize_int4_packed(int32_t B, int32_t Hkv, int32_t D, const void 
  *   out_k [B][Hkv][cap_out][D], out_v [B][Hkv][cap_out/32][D][32]   bf16
  *   out_deg [B][Hkv][cap_out] fp32 (feed vc_draft_attn with
  *           degree_h_stride = cap_out; the drafter takes cap_out % 64 == 0)
- * D = 128; 2 <= chunk <= 128; 0 <= r <= 1; caps multiples of 32; K buffers
+ * D = 128; 2 <= chunk <= 128; 0 <= r <= 1; n_in <= 2^30; caps multiples of 32; K buffers
  * 16-byte aligned; in and out must not overlap.                              */
 vc_status vc_csm_round(int32_t B, int32_t Hkv, int32_t D, int32_t n_in, int32_t n_sink, int32_t n_recent,
                        int32_t chunk, double r, const void *in_k, const void *in_v, const float *in_deg,

@@ -159,6 +159,7 @@ const char *vc_status_string(vc_status s) {
     case VC_EINVAL: return "VC_EINVAL";
     case VC_ENOTSUP: return "VC_ENOTSUP";
     case VC_EHIP: return "VC_EHIP";
+    default: break;
   }
   return "unknown vc_status";
 }
@@ -235,6 +236,7 @@ vc_status check_lm_argmax(int32_t R, int32_t Dm, int32_t V, const void *h, const
   REQ(R >= 0 && V >= 1 && Dm >= 32, "R >= 0, V >= 1 and Dm >= 32 required");
   if (Dm % 32) return fail(VC_ENOTSUP, "Dm (%d) must be a multiple of 32", Dm);
   REQ(Dm <= (1 << 20), "Dm (%d) above 2^20", Dm);
+  REQ(V <= (1 << 30), "V (%d) above 2^30", V);
   if (R == 0) return VC_OK;
   REQ(h && w && out && ws, "null h, w, output or workspace");
   REQ(aligned16(h) && aligned16(w) && aligned16(ws), "h, w and workspace must be 16-byte aligned");
@@ -278,6 +280,7 @@ vc_status check_commit(int32_t B, int32_t Hkv, int32_t D, int32_t M, int32_t dty
                        const void *blk_k, const void *blk_v, const int32_t *n_out, const void *dst_k,
                        const void *dst_v, const int32_t *len, const float *degree, int64_t degree_h_stride) {
   REQ(B >= 0 && Hkv >= 1 && D >= 1 && M >= 1 && cap >= 0, "bad commit shape");
+  REQ((int64_t)B * Hkv <= 65535, "at most 65535 (request, KV head) slices per call");
   REQ(dtype == VC_BF16 || dtype == VC_FP32, "unknown dtype %d", dtype);
   REQ(dst_v_blocked == 0 || dst_v_blocked == 1, "dst_v_blocked must be 0 or 1");
   REQ(!dst_v_blocked || cap % 32 == 0, "a blocked V cache needs cap %% 32 == 0");
@@ -432,13 +435,15 @@ vc_status vc_csm_round(int32_t B, int32_t Hkv, int32_t D, int32_t n_in, int32_t 
   if (D != 128) return fail(VC_ENOTSUP, "the CSM round is compiled for head_dim 128 (got %d)", D);
   REQ(chunk >= 2 && chunk <= 128, "chunk must lie in 2..128 (got %d)", chunk);
   REQ(r >= 0.f && r <= 1.f, "r must lie in [0, 1]");
-  REQ(n_sink + n_recent <= n_in, "sinks + recent tokens (%d) exceed n_in (%d)", n_sink + n_recent, n_in);
+  REQ(n_in <= kMaxTokens, "n_in (%d) above 2^30 tokens", n_in);
+  REQ((int64_t)n_sink + n_recent <= n_in, "sinks + recent tokens (%lld) exceed n_in (%d)",
+      (long long)n_sink + n_recent, n_in);
   REQ(n_in <= cap_in && cap_in % 32 == 0 && cap_out % 32 == 0, "n_in <= cap_in; caps multiples of 32");
+  // one 256-thread workgroup per chunk on the x dimension of the grid, whose work-item count is 32-bit
+  REQ(((int64_t)n_in - n_sink - n_recent + chunk - 1) / chunk + 2 <= (1 << 24) - 1,
+      "too many chunks: at most 2^24 - 3 per (request, KV head)");
   const int out = vc::csm_survivors(n_in, n_sink, n_recent, chunk, r);
   REQ(out <= cap_out, "the round keeps %d tokens; cap_out is %lld", out, (long long)cap_out);
-  // one 256-thread workgroup per chunk on the x dimension of the grid, whose work-item count is 32-bit
-  REQ((int64_t)(n_in - n_sink - n_recent + chunk - 1) / chunk + 2 <= (1 << 24) - 1,
-      "too many chunks: at most 2^24 - 3 per (request, KV head)");
   *n_out = out;
   if (B == 0) return VC_OK;
   REQ(in_k && in_v && out_k && out_v && out_deg, "null pointer");

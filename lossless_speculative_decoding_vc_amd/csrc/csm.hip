@@ -346,8 +346,8 @@ __global__ __launch_bounds__(256) void csm_round_kernel(CsmParams p) {
 
 int csm_survivors(int n_in, int n_sink, int n_recent, int chunk, double r) {
   int out = n_in;
-  for (int s = n_sink; s < n_in - n_recent; s += chunk) {
-    const int L = min(chunk, n_in - n_recent - s);
+  for (int64_t s = n_sink; s < (int64_t)n_in - n_recent; s += chunk) {
+    const int L = (int)std::min<int64_t>(chunk, (int64_t)n_in - n_recent - s);
     if (L > 1) out -= (int)floor((double)r * ((L + 1) / 2));
   }
   return out;

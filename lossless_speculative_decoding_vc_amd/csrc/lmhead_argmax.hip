@@ -291,7 +291,7 @@ int vocab_tile(int R) { return R > 64 ? 16 * kBigNV * kBigWV : 16 * kSmallNV * k
 
 size_t lm_argmax_workspace(int R, int V) {
   const int bv = vocab_tile(R);
-  return (size_t)R * ((V + bv - 1) / bv) * sizeof(Best);
+  return (size_t)R * (((int64_t)V + bv - 1) / bv) * sizeof(Best);
 }
 
 hipError_t launch_lm_argmax(int R, int Dm, int V, const void *h, const void *w, int *out, int out_stride,

@@ -82,7 +82,6 @@ VC_DEVICE uint32_t pack8(const uint8_t *c) {
 template <int D>
 __global__ __launch_bounds__(256) void quantize_int4(QuantParams p) {
   static_assert(D == 128, "int4 cache is compiled for head_dim 128");
-  constexpr int NG = D / kGroup;
   __shared__ __attribute__((aligned(16))) uint16_t ktile[kGroup][D];   // [token][channel]
   __shared__ __attribute__((aligned(16))) uint16_t vtile[D][kGroup];   // [channel][token]
   __shared__ uint8_t kcode[kGroup][D];

@@ -207,14 +207,17 @@ __global__ __launch_bounds__(kPT) void proj(ProjParams p) {
 // Eviction rule of the tiny loop's compressor: the first `sinks` positions,
 // the last `recent`, and the multiples of `stride` in between (ascending);
 // everything when T <= sinks + recent.
+// The middle range [sinks, T - recent) is non-empty; sums are taken in 64
+// bits so that no argument in int32 range wraps, and every result is at most T.
 VC_DEVICE_HOST_INLINE int evict_mid(int T, int sinks, int recent, int stride, int *first) {
-  const int lo = sinks, hi = T - recent;   // the middle range [lo, hi), non-empty
-  *first = (lo + stride - 1) / stride;
-  const int last = (hi - 1) / stride;
-  return last >= *first ? last - *first + 1 : 0;
+  const int64_t lo = sinks, hi = (int64_t)T - recent;
+  const int64_t f = (lo + stride - 1) / stride, last = (hi - 1) / stride;
+  *first = (int)f;
+  return last >= f ? (int)(last - f + 1) : 0;
 }
+VC_DEVICE_HOST_INLINE bool evict_all(int T, int sinks, int recent) { return (int64_t)T <= (int64_t)sinks + recent; }
 VC_DEVICE_HOST_INLINE int evict_count(int T, int sinks, int recent, int stride) {
-  if (T <= sinks + recent) return T;
+  if (evict_all(T, sinks, recent)) return T;
   int first;
   return sinks + evict_mid(T, sinks, recent, stride, &first) + recent;
 }
@@ -236,7 +239,7 @@ __global__ __launch_bounds__(256) void gather_tile(int D, int n_list, const int3
     T = *src_len;
     T = T < 0 ? 0 : (T > scap ? (int)scap : T);
     n = evict_count(T, sinks, recent, stride);
-    if (T > sinks + recent) mid = evict_mid(T, sinks, recent, stride, &first);
+    if (!evict_all(T, sinks, recent)) mid = evict_mid(T, sinks, recent, stride, &first);
   }
   n = n > dcap ? (int)dcap : n;
   if (blockIdx.x == 0 && tid == 0) dlen[h] = n;
@@ -247,7 +250,7 @@ __global__ __launch_bounds__(256) void gather_tile(int D, int n_list, const int3
     int p = j;
     if (idx) {
       p = j < n ? idx[j] : 0;
-    } else if (T > sinks + recent) {
+    } else if (!evict_all(T, sinks, recent)) {
       p = j < sinks ? j : (j < sinks + mid ? (first + (j - sinks)) * stride : T - recent + (j - sinks - mid));
     }
     pos[tid] = p < 0 ? 0 : (p >= scap ? (int)scap - 1 : p);
@@ -343,7 +346,7 @@ vc_status vc_tiny_forward(const vc_tiny_model *m, int32_t R, const int32_t *toke
   if (m->d_model < 1 || m->d_model > 1024 || m->ffn < 1 || m->ffn > kMaxK || m->vocab < 1 ||
       (size_t)m->n_q_heads * m->head_dim > 1024)
     return set_error(VC_ENOTSUP, "tiny model too wide (d_model and Hq * head_dim <= 1024, ffn <= 4096)");
-  if (pos0 < 0 || (!at->pos_base && pos0 + R > m->rope_rows))
+  if (pos0 < 0 || (!at->pos_base && (int64_t)pos0 + R > m->rope_rows))
     return set_error(VC_EINVAL, "positions exceed the RoPE table");
   if (!workspace || workspace_bytes < vc_tiny_workspace_size(m, R)) return set_error(VC_EINVAL, "workspace too small");
   if (at->mode == VC_TINY_DRAFT && (R != 1 || at->tail_pos < 0 || at->tail_pos >= at->tcap || !at->tail_len))
