@@ -478,6 +478,13 @@ typedef struct vc_round_commit {
 
 typedef void (*vc_round_hook)(void *ctx, int32_t layer, void *verify_stream);
 
+/* What a timed round measures (vc_round_desc::time_kernels).
+ *   VC_TIME_DRAFT_STEPS: each draft step's run of `layers` draft attention
+ *     calls (their split merges included), and each layer's verify call.
+ *   VC_TIME_ATTENTION_KERNELS: each draft and verify attention kernel alone,
+ *     the split merge that follows it left outside the event pair.        */
+typedef enum { VC_TIME_NONE = 0, VC_TIME_DRAFT_STEPS = 1, VC_TIME_ATTENTION_KERNELS = 2 } vc_round_timing;
+
 /* A copy a chained round starts before any other: the compressed cache of a
  * request whose prefix is held in host memory ("Supporto Architetturale",
  * remote prefix caching: the drafter needs only the compressed cache, so it
@@ -518,9 +525,8 @@ typedef struct vc_round_desc {
   const vc_round_commit *commit;  /* optional [layers]                               */
   vc_round_hook before_verify;    /* optional                                        */
   void   *hook_ctx;
-  int32_t time_kernels;           /* 1: time each draft step's run of draft
-                                     attention calls and every verify call with
-                                     events on their streams (vc_stagger_round_times) */
+  int32_t time_kernels;           /* vc_round_timing: events on the compute streams
+                                     (vc_stagger_round_times)                        */
   const vc_round_fetch *fetch;    /* optional [n_fetch], VC_ROUND_CHAINED with steps
                                      > 0 only: enqueued in order on the copy stream
                                      ahead of the layer copies                       */
@@ -530,10 +536,13 @@ typedef struct vc_round_desc {
 vc_status vc_stagger_round(vc_stagger *s, const vc_round_desc *d, void *draft_stream, void *verify_stream);
 
 /* Durations (ms) of the last timed round, valid once its streams have
- * completed: draft_ms[i] spans draft step i's `layers` back-to-back draft
- * attention calls (the LM head excluded), verify_ms[l] layer l's verify
- * call.  *n_draft and *n_verify are set to the counts; the arrays (host, may
- * be NULL to query the counts) must hold at least that many entries.        */
+ * completed.  VC_TIME_DRAFT_STEPS: draft_ms[i] spans draft step i's `layers`
+ * back-to-back draft attention calls (the LM head excluded), verify_ms[l]
+ * layer l's verify call.  VC_TIME_ATTENTION_KERNELS: draft_ms[i * layers + l]
+ * is layer l's draft attention kernel in step i and verify_ms[l] layer l's
+ * verify attention kernel, each without its split merge.  *n_draft and
+ * *n_verify are set to the counts; the arrays (host, may be NULL to query
+ * the counts) must hold at least that many entries.                        */
 vc_status vc_stagger_round_times(vc_stagger *s, float *draft_ms, int32_t *n_draft, float *verify_ms,
                                  int32_t *n_verify);
 

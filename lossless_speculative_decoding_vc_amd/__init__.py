@@ -99,6 +99,7 @@ class RoundDesc(ctypes.Structure):
 
 
 ROUND_STAGGERED, ROUND_BULK, ROUND_CHAINED = 0, 1, 2
+TIME_NONE, TIME_DRAFT_STEPS, TIME_ATTENTION_KERNELS = 0, 1, 2   # vc_round_timing
 COMMIT_ROWS, COMMIT_INT4_TAIL = 0, 1
 
 _lib = None
@@ -862,8 +863,10 @@ class Stagger:
         tail_len, packed, main_len``, as :func:`int4_commit`); both may add
         ``host_k, host_v`` (pinned write-back of the block rows).  ``before_verify(layer, stream_ptr)`` is
         called on the host before each verify is enqueued.  ``time_kernels``
-        times each draft step's run of draft attention calls and every verify
-        call (:meth:`round_times`).  ``lm_w`` is the
+        (:data:`TIME_DRAFT_STEPS` or True: each draft step's run of draft
+        attention calls and every verify call; :data:`TIME_ATTENTION_KERNELS`:
+        every draft and verify attention kernel alone, split merges excluded)
+        records events read by :meth:`round_times`.  ``lm_w`` is the
         vocab-major ``[V][Dm]`` LM head.  ``fetch`` (chained mode): list of
         ``(host_src, dev_dst, layer)`` -- pinned host tensor, device tensor of
         the same byte size (a layer's compressed cache) -- copied over the link
@@ -871,7 +874,11 @@ class Stagger:
         copies (remote prefix caching).  Returns without synchronizing."""
         d = RoundDesc()
         keep = []
-        d.layers, d.mode, d.time_kernels = int(layers), int(mode), 1 if time_kernels else 0
+        if time_kernels is True or time_kernels is False:
+            time_kernels = TIME_DRAFT_STEPS if time_kernels else TIME_NONE
+        if time_kernels not in (TIME_NONE, TIME_DRAFT_STEPS, TIME_ATTENTION_KERNELS):
+            raise ValueError(f"unknown timing mode {time_kernels!r}")
+        d.layers, d.mode, d.time_kernels = int(layers), int(mode), int(time_kernels)
         _dev(lm_w, "lm_w", torch.bfloat16)
         d.lm_w, d.V, d.Dm = _ptr(lm_w), lm_w.shape[0], lm_w.shape[1]
         steps = 0
@@ -1009,7 +1016,9 @@ class Stagger:
         return keep
 
     def round_times(self):
-        """(draft_ms per step, verify_ms per layer) of the last timed round, once it completed."""
+        """(draft_ms, verify_ms) of the last timed round, once it completed:
+        per draft step and per verify layer (TIME_DRAFT_STEPS), or per draft
+        kernel, step-major, and per verify kernel (TIME_ATTENTION_KERNELS)."""
         nd, nv = _i32(), _i32()
         _check(lib().vc_stagger_round_times(self.h, None, ctypes.byref(nd), None, ctypes.byref(nv)))
         dm = (ctypes.c_float * max(nd.value, 1))()

@@ -721,8 +721,11 @@ SplitPlan plan_draft(const vc_draft_args &a) {
 
 hipError_t launch_draft_f32(const vc_draft_args &a, hipStream_t s);
 
-hipError_t launch_draft(const vc_draft_args &a, const SplitPlan &pl, hipStream_t s) {
-  if (a.dtype == VC_FP32) return launch_draft_f32(a, s);
+hipError_t launch_draft(const vc_draft_args &a, const SplitPlan &pl, hipStream_t s, hipEvent_t after_kernel) {
+  if (a.dtype == VC_FP32) {
+    const hipError_t e = launch_draft_f32(a, s);
+    return (e != hipSuccess || !after_kernel) ? e : hipEventRecord(after_kernel, s);
+  }
   DraftParams p;
   p.B = a.B; p.Hq = a.Hq; p.Hkv = a.Hkv; p.G = a.Hq / a.Hkv; p.splits = pl.splits;
   p.qk_scale = a.scale * kLog2e;
@@ -753,6 +756,7 @@ hipError_t launch_draft(const vc_draft_args &a, const SplitPlan &pl, hipStream_t
     draft_bf16_dense<64><<<grid, kDraftWaves * 64, 0, s>>>(p);
   }
   hipError_t e = hipGetLastError();
+  if (e == hipSuccess && after_kernel) e = hipEventRecord(after_kernel, s);
   if (e != hipSuccess || pl.splits == 1) return e;
   return launch_combine(p.part_o, p.part_lse, pl.splits, (int)rows, a.D, a.dtype, a.out, a.out_lse, s);
 }

@@ -52,8 +52,10 @@ hipError_t launch_commit(int B, int Hkv, int D, int M, int elem_bytes, int64_t c
 hipError_t launch_compact_kv(int B, int Hkv, int D, int elem_bytes, const void *src_k, const void *src_v,
                              int64_t src_cap, const int32_t *idx, int64_t idx_stride, const int32_t *n_kept,
                              void *dst_k, void *dst_v, int64_t cap, int32_t *dst_len, hipStream_t s);
-hipError_t launch_draft(const vc_draft_args &a, const SplitPlan &p, hipStream_t s);
-hipError_t launch_verify(const vc_verify_args &a, const SplitPlan &p, hipStream_t s);
+// after_kernel (optional): an event recorded once the attention kernel is
+// enqueued and before the split merge, so a caller can time the kernel alone.
+hipError_t launch_draft(const vc_draft_args &a, const SplitPlan &p, hipStream_t s, hipEvent_t after_kernel = nullptr);
+hipError_t launch_verify(const vc_verify_args &a, const SplitPlan &p, hipStream_t s, hipEvent_t after_kernel = nullptr);
 
 // The interleaved int4 block (fmt = VC_KV_INT4_PACKED, head_dim 128): byte
 // offsets of a 32-token block's six pieces and the block size.

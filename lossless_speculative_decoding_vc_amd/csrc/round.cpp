@@ -48,6 +48,8 @@ vc_status validate(const vc_stagger *s, const vc_round_desc *d) {
   if (k < 0) return bad("steps must be >= 0");
   if (d->mode != VC_ROUND_STAGGERED && d->mode != VC_ROUND_BULK && d->mode != VC_ROUND_CHAINED)
     return bad("unknown round mode");
+  if (d->time_kernels < VC_TIME_NONE || d->time_kernels > VC_TIME_ATTENTION_KERNELS)
+    return bad("unknown timing mode");
   if ((k > 0 || d->verify) && !d->lm_w) return bad("lm_w is required");
   if (k > 0) {
     if (!d->draft || !d->draft_hidden || !d->drafts) return bad("a drafting cohort needs draft, draft_hidden, drafts");
@@ -141,11 +143,37 @@ struct RoundTimer {
     ++next;
     return e == hipSuccess ? VC_OK : vc::set_error(VC_EHIP, "timing event");
   }
+  // the closing event of the current pair, for a launch to record itself
+  hipEvent_t take_end() { return s->round_ev[2 * next++ + 1]; }
 };
 
+// One draft attention call (validated with the round); with per-kernel
+// timing its kernel alone sits between an event pair, the split merge after.
+vc_status draft_call(const vc_draft_args &a, hipStream_t st, RoundTimer &tm) {
+  if (tm.every != VC_TIME_ATTENTION_KERNELS) return vc_draft_attn(&a, st);
+  CHK(tm.begin(st, true));
+  if (a.B == 0) return tm.end(st, true);
+  const hipError_t e = vc::launch_draft(a, vc::plan_draft(a), st, tm.take_end());
+  return e == hipSuccess ? VC_OK : vc::set_error(VC_EHIP, hipGetErrorString(e));
+}
+
+vc_status verify_call(const vc_verify_args &a, hipStream_t st, RoundTimer &tm) {
+  if (tm.every != VC_TIME_ATTENTION_KERNELS) {
+    CHK(tm.begin(st, tm.every > 0));
+    CHK(vc_verify_attn(&a, st));
+    return tm.end(st, tm.every > 0);
+  }
+  CHK(tm.begin(st, true));
+  if (a.B == 0) return tm.end(st, true);
+  const hipError_t e = vc::launch_verify(a, vc::plan_verify(a), st, tm.take_end());
+  return e == hipSuccess ? VC_OK : vc::set_error(VC_EHIP, hipGetErrorString(e));
+}
+
 vc_status draft_step(const vc_round_desc *d, int i, void *ds, RoundTimer &tm, const vc_stagger *s) {
-  // one event pair around the step's back-to-back draft attention calls
-  CHK(tm.begin((hipStream_t)ds, tm.every > 0));
+  // VC_TIME_DRAFT_STEPS: one event pair around the step's back-to-back draft
+  // attention calls; VC_TIME_ATTENTION_KERNELS: one pair per kernel
+  const bool step_pair = tm.every == VC_TIME_DRAFT_STEPS;
+  CHK(tm.begin((hipStream_t)ds, step_pair));
   for (int l = 0; l < d->layers; ++l) {
     if (i == 0)   // the first use of each layer's compressed cache waits for its fetches
       for (int j = 0; j < d->n_fetch; ++j)
@@ -153,9 +181,9 @@ vc_status draft_step(const vc_round_desc *d, int i, void *ds, RoundTimer &tm, co
           return vc::set_error(VC_EHIP, "waiting for a fetch");
     vc_draft_args a = d->draft[l];
     if (d->step_tail_len) a.tail_len = d->step_tail_len[i];
-    CHK(vc_draft_attn(&a, ds));
+    CHK(draft_call(a, (hipStream_t)ds, tm));
   }
-  CHK(tm.end((hipStream_t)ds, tm.every > 0));
+  CHK(tm.end((hipStream_t)ds, step_pair));
   return vc_lm_head_argmax(d->draft[0].B, d->Dm, d->V, d->draft_hidden[i], d->lm_w, d->drafts + i, d->steps,
                            d->draft_lm_ws, d->draft_lm_ws_bytes, ds);
 }
@@ -171,11 +199,12 @@ extern "C" vc_status vc_stagger_round(vc_stagger *s, const vc_round_desc *d, voi
   for (int sl = 0; sl < ns; ++sl)
     if (!s->released[sl]) return bad("a staging slot still holds an unreleased layer");
 
-  // timing events: one pair per draft step first, then one pair per verify layer
-  RoundTimer tm{s, d->time_kernels ? 1 : 0};
+  // timing events: the draft pairs first (one per step, or one per layer and
+  // step), then one pair per verify layer
+  RoundTimer tm{s, d->time_kernels};
   s->timed_drafts = s->timed_verifies = 0;
   if (tm.every) {
-    const int n_draft = k;
+    const int n_draft = tm.every == VC_TIME_ATTENTION_KERNELS ? k * L : k;
     const int n_ver = d->verify ? L : 0;
     const size_t need = 2 * (size_t)(n_draft + n_ver);
     while (s->round_ev.size() < need) {
@@ -186,7 +215,7 @@ extern "C" vc_status vc_stagger_round(vc_stagger *s, const vc_round_desc *d, voi
     s->timed_drafts = n_draft;
     s->timed_verifies = n_ver;
   }
-  RoundTimer vt{s, 0, tm.every ? k : 0};
+  RoundTimer vt{s, tm.every, tm.every ? s->timed_drafts : 0};
 
   if (d->n_fetch > 0) {
     // the compressed cache first, each copy followed by its completion event
@@ -230,9 +259,7 @@ extern "C" vc_status vc_stagger_round(vc_stagger *s, const vc_round_desc *d, voi
     vc_verify_args a = d->verify[l];
     a.ctx_k = slot;
     a.ctx_v = static_cast<char *>(slot) + d->v_offset;
-    CHK(vt.begin((hipStream_t)verify_stream, tm.every > 0));
-    CHK(vc_verify_attn(&a, verify_stream));
-    CHK(vt.end((hipStream_t)verify_stream, tm.every > 0));
+    CHK(verify_call(a, (hipStream_t)verify_stream, vt));
     CHK(vc_stagger_release(s, l, verify_stream));
     if (l + ns < L) CHK(vc_stagger_stream_layer(s, l + ns, d->host_kv[l + ns], d->kv_bytes));
   }

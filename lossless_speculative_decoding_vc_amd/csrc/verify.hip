@@ -877,8 +877,11 @@ SplitPlan plan_verify(const vc_verify_args &a) {
 
 hipError_t launch_verify_f32(const vc_verify_args &a, hipStream_t s);
 
-hipError_t launch_verify(const vc_verify_args &a, const SplitPlan &pl, hipStream_t s) {
-  if (a.dtype == VC_FP32) return launch_verify_f32(a, s);
+hipError_t launch_verify(const vc_verify_args &a, const SplitPlan &pl, hipStream_t s, hipEvent_t after_kernel) {
+  if (a.dtype == VC_FP32) {
+    const hipError_t e = launch_verify_f32(a, s);
+    return (e != hipSuccess || !after_kernel) ? e : hipEventRecord(after_kernel, s);
+  }
   VerifyParams p;
   p.B = a.B; p.Hq = a.Hq; p.Hkv = a.Hkv; p.G = a.Hq / a.Hkv; p.M = a.M; p.R = a.M * p.G;
   p.splits = pl.splits;
@@ -896,6 +899,7 @@ hipError_t launch_verify(const vc_verify_args &a, const SplitPlan &pl, hipStream
   if (a.D == 128) launch_verify_d<128>(p, sh, row_groups, s);
   else launch_verify_d<64>(p, sh, row_groups, s);
   hipError_t e = hipGetLastError();
+  if (e == hipSuccess && after_kernel) e = hipEventRecord(after_kernel, s);
   if (e != hipSuccess || pl.splits == 1) return e;
   return launch_combine(p.part_o, p.part_lse, pl.splits, (int)rows, a.D, a.dtype, a.out, a.out_lse, s);
 }

@@ -87,8 +87,9 @@ class Inputs:
             self.host_kv.append(h)
 
 
-def _run(inp, mode, delayed=()):
-    """One round on fresh device state; returns every output on the host."""
+def _run(inp, mode, delayed=(), timing=0):
+    """One round on fresh device state; returns every output on the host
+    (and, with a timing mode, the round's event times under "times")."""
     import torch
     import lossless_speculative_decoding_vc_amd as vc
     dev = "cuda"
@@ -147,9 +148,11 @@ def _run(inp, mode, delayed=()):
         stg.round(L, mode, W, draft=draft, step_tail_len=step_tl, draft_hidden=hd, drafts=drafts,
                   verify=verify, host_kv=inp.host_kv, kv_bytes=2 * inp.half, v_offset=inp.half,
                   verify_hidden=hv, verify_drafts=vdr, argmax=am, accept_len=al, out_tokens=toks, n_out=nout,
-                  commit=commit, before_verify=before_verify, draft_stream=ds, verify_stream=vs)
+                  commit=commit, before_verify=before_verify, draft_stream=ds, verify_stream=vs,
+                  time_kernels=timing)
         torch.cuda.synchronize()
         stg.sync()
+        times = stg.round_times() if timing else None
     finally:
         stg.close()
     assert sorted(stalls) == sorted(delayed)
@@ -158,6 +161,8 @@ def _run(inp, mode, delayed=()):
                n_out=nout.cpu().numpy(), xk=[_bits(t) for t in xk], xv=[_bits(t) for t in xv],
                xdeg=[t.cpu().numpy() for t in xdeg], xlen=[t.cpu().numpy() for t in xlen],
                hostk=[t.numpy().copy() for t in hostk], hostv=[t.numpy().copy() for t in hostv])
+    if timing:
+        out["times"] = times
     return out
 
 
@@ -193,6 +198,22 @@ def test_verify_stalls_change_nothing(inp, staggered, delayed):
     stalled = _run(inp, vc.ROUND_STAGGERED, delayed)
     for key in staggered:
         _equal(staggered[key], stalled[key], key)
+
+
+@pytest.mark.parametrize("timing", ["draft steps", "attention kernels"])
+def test_timed_rounds_change_nothing(inp, staggered, timing):
+    """Timing events (per draft step, or around each attention kernel with
+    its split merge outside the pair) leave every output bit-identical, and
+    give one positive duration per timed call."""
+    import lossless_speculative_decoding_vc_amd as vc
+    mode = vc.TIME_DRAFT_STEPS if timing == "draft steps" else vc.TIME_ATTENTION_KERNELS
+    timed = _run(inp, vc.ROUND_STAGGERED, timing=mode)
+    d_ms, v_ms = timed.pop("times")
+    for key in staggered:
+        _equal(staggered[key], timed[key], key)
+    assert len(d_ms) == (K if mode == vc.TIME_DRAFT_STEPS else K * L)
+    assert len(v_ms) == L
+    assert all(0.0 < t < 1000.0 for t in list(d_ms) + list(v_ms)), (d_ms, v_ms)
 
 
 def test_round_matches_the_oracle(inp, staggered):
@@ -247,6 +268,8 @@ def test_round_rejects_bad_descriptors_before_enqueueing(inp):
             stg.round(L + 1, vc.ROUND_STAGGERED, W)
         with pytest.raises(vc.VcError, match="mode"):
             stg.round(L, 7, W)
+        with pytest.raises(ValueError, match="timing"):
+            stg.round(L, vc.ROUND_STAGGERED, W, time_kernels=5)
         # fetches belong to a chained round with draft steps
         h = torch.zeros(64, dtype=torch.uint8, pin_memory=True)
         with pytest.raises(vc.VcError, match="chained"):
