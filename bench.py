@@ -37,9 +37,11 @@ CPU oracle timed on a bounded sample of the same workload.
   draft128k      batch-32 draft over a 25% compressed 128K context + degrees
   draft128k_int4 batch-32 draft over int4 K/V of all 131072 tokens
   draft1m_int4   the 1M-token configuration's int4 drafter
+  draft32k_int4  batch-32 draft over int4 K/V of 32768 tokens (the same 1.34 GB as
+                 the 1M drafter, spread over 256 (request, KV head) slices)
   quant128k_int4 building that int4 cache from bf16 K/V (vc_quantize_int4 over
                  batch 32 x 8 KV heads x 131072 tokens)
-  draft128k_int4p, draft1m_int4p, quant128k_int4p
+  draft128k_int4p, draft1m_int4p, draft32k_int4p, quant128k_int4p
                  the same int4 legs in the packed layout (VC_KV_INT4_PACKED: one
                  interleaved 5120-byte block per 32 tokens)
   csm128k        one Chunked Soft Matching round (vc_csm_round, r = 1, chunks of
@@ -80,8 +82,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=1)
     ap.add_argument("--workload", default="stagger128k",
                     choices=["stagger128k", "verify32k", "verify128k", "verify1m", "draft128k", "draft128k_int4",
-                             "draft1m_int4", "draft128k_int4p", "draft1m_int4p", "draft_cohort", "long1m", "remote1m",
-                             "tiny", "quant128k_int4", "quant128k_int4p", "csm128k", "compact128k", "lmhead_verify",
+                             "draft1m_int4", "draft128k_int4p", "draft1m_int4p", "draft32k_int4", "draft32k_int4p",
+                             "draft_cohort", "long1m", "remote1m", "tiny", "quant128k_int4", "quant128k_int4p", "csm128k", "compact128k", "lmhead_verify",
                              "lmhead_draft", "copy1g"])
     ap.add_argument("--layers", type=int, default=None,
                     help="model layers per round (default 64 for stagger128k, 40 for long1m)")
@@ -120,6 +122,8 @@ KERNEL_OF = {
     "draft_cohort": "vc_draft_attn: draft_bf16_dense + combine_splits",
     "draft128k_int4p": "vc_draft_attn (packed int4 blocks): draft_int4 + combine_splits",
     "draft1m_int4p": "vc_draft_attn (packed int4 blocks): draft_int4 + combine_splits",
+    "draft32k_int4": "vc_draft_attn: draft_int4 + combine_splits",
+    "draft32k_int4p": "vc_draft_attn (packed int4 blocks): draft_int4 + combine_splits",
     "verify1m": "vc_verify_attn: verify_pp + combine_splits",
     "verify32k": "vc_verify_attn: verify_pp + combine_splits",
     "verify128k": "vc_verify_attn: verify_pp + combine_splits",
@@ -741,10 +745,13 @@ def kernel_alone(args):
             vc.quantize_int4(K, Vt, zero, cap // 32, zero, **qd)
         flops = 0.0
         nbytes = B * Hkv * cap * D * 2 * 2 + B * Hkv * cap * 160
-    elif args.workload in ("draft128k_int4", "draft1m_int4", "draft128k_int4p", "draft1m_int4p"):
+    elif args.workload in ("draft128k_int4", "draft1m_int4", "draft128k_int4p", "draft1m_int4p", "draft32k_int4",
+                           "draft32k_int4p"):
         packed = args.workload.endswith("p")
         if args.workload.startswith("draft128k"):   # batch 32, int4 K/V over all 131072 tokens (4 of 16 bits = 25%)
             B, Hq, Hkv, D, cap = 32, 32, 8, 128, 131072
+        elif args.workload.startswith("draft32k"):   # batch 32, int4 K/V over 32768 tokens
+            B, Hq, Hkv, D, cap = 32, 32, 8, 128, 32768
         else:   # drafter of the 1M-token configuration: one request, int4 over 1048576 tokens
             B, Hq, Hkv, D, cap = 1, 32, 8, 128, 1048576
         import synthetic as S

@@ -293,11 +293,16 @@ __global__ __launch_bounds__(kDraftWaves * 64) void draft_bf16_dense(DraftParams
 //      S_t   = sum_d (q_d s_d) c_td + sum_d q_d z_d
 //      O_d  += sum_t (p_t s_tg) c_td + sum_t p_t z_tg
 //    with c read as an exact fp16 "magic" value (1024 + c or 64 + c, one
-//    v_perm + one OR per pair of codes) and the magic offsets removed by an
-//    extra MFMA against the constant -1024/-64 operand; the zero-point terms
-//    are MFMAs whose A operand repeats z along the rows.  All operands are
-//    fp16 (v_mfma_f32_16x16x32_f16) with fp32 accumulation; Q is brought
-//    into fp16 range with an exact per-head power-of-two scale.
+//    shift and four and-or per eight codes).  On the score side the magic
+//    offsets are removed by an extra MFMA against the constant -1024/-64
+//    operand and the zero-point term is an MFMA whose A operand repeats z
+//    along the rows.  On the value side both are the same for every channel
+//    of a 32-channel group (V's magic depends on the token's slot, its zero
+//    point on the token and group), so they collect in one running sum per
+//    head and group, W_g = sum_t p_t (z_tg - magic_t s_tg), by packed fp16
+//    dot products, added to the group's channels once after the loop.  All
+//    operands are fp16 (v_mfma_f32_16x16x32_f16) with fp32 accumulation; Q
+//    is brought into fp16 range with an exact per-head power-of-two scale.
 //  * chunks that reach the bf16 tail or the end of the sequence are
 //    dequantised element-wise after the main loop.
 constexpr int kI4Stages = 3;
@@ -318,17 +323,12 @@ VC_DEVICE uint32_t pk_mul_f16(uint32_t a, uint32_t b) {
 VC_DEVICE float sum_f16x2(uint32_t w, float acc) {
   return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, w), f16x2{(_Float16)1.0f, (_Float16)1.0f}, acc, false);
 }
+// acc + a.lo * b.lo + a.hi * b.hi (fp16 pairs, exact products, fp32 sum).
+VC_DEVICE float dot_f16x2(uint32_t a, uint32_t b, float acc) {
+  return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, a), __builtin_bit_cast(f16x2, b), acc, false);
+}
 VC_DEVICE uint32_t pack_f16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{lo, hi}), f16x2));
-}
-// (x & m) | c in one v_and_or_b32.  A three-operand instruction takes no
-// 32-bit literal here and at most one scalar operand, so the mask comes from
-// an SGPR and the magic from a VGPR; written out because the compiler splits
-// the expression into two two-operand instructions with literals.
-VC_DEVICE uint32_t and_or(uint32_t x, uint32_t m, uint32_t c) {
-  uint32_t r;
-  __asm__("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(x), "s"(m), "v"(c));
-  return r;
 }
 // One 32-bit word of eight 4-bit codes (code 2j in bits 4j..4j+3, code 2j+1
 // in bits 16+4j..16+4j+3) as four fp16 pairs in code order:
@@ -336,11 +336,15 @@ VC_DEVICE uint32_t and_or(uint32_t x, uint32_t m, uint32_t c) {
 //   (64 + c6, 64 + c7).
 // A code in bits 0..3 of a half lands in the low mantissa bits of an fp16
 // whose ulp is 1, one in bits 4..7 in those of an fp16 whose ulp is 1/16:
-// both exact.  One shift and four and-or per eight codes.
-VC_DEVICE u32x4 magic_codes(uint32_t w, uint32_t m1024, uint32_t m64) {
+// both exact.  One shift and four v_and_or_b32 per eight codes: a
+// three-operand instruction takes no 32-bit literal here and at most one
+// scalar operand, so the caller keeps the masks (lo = 0x000F000F,
+// hi = 0x00F000F0) in SGPRs and the magics in VGPRs, values the compiler
+// cannot fold into literals.  Plain C, not inline asm: the compiler must see
+// these writes to insert the wait states an MFMA reading them needs.
+VC_DEVICE u32x4 magic_codes(uint32_t w, uint32_t lo, uint32_t hi, uint32_t m1024, uint32_t m64) {
   const uint32_t w8 = w >> 8;
-  return u32x4{and_or(w, 0x000F000Fu, m1024), and_or(w, 0x00F000F0u, m64),
-               and_or(w8, 0x000F000Fu, m1024), and_or(w8, 0x00F000F0u, m64)};
+  return u32x4{(w & lo) | m1024, (w & hi) | m64, (w8 & lo) | m1024, (w8 & hi) | m64};
 }
 // The magic offsets of magic_codes, negated (fp16 pairs, same slot order).
 constexpr uint32_t kNegMagic1024 = 0xE400E400u, kNegMagic64 = 0xD400D400u;
@@ -436,6 +440,11 @@ __global__ __launch_bounds__(kDraftWaves * 64, 2) void draft_int4(DraftParams p)
   f32x4 o[DT];
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // W_g of this lane's head and tokens: what the zero points and the magic
+  // offsets add to every channel of V group g
+  float wz[NG];
+#pragma unroll
+  for (int g = 0; g < NG; ++g) wz[g] = 0.f;
 
   // Online softmax of one chunk's 8 scores per lane (token 8*grp + e).
   // Returns the probabilities relative to the lane's reference max.  Lazy
@@ -451,6 +460,8 @@ __global__ __launch_bounds__(kDraftWaves * 64, 2) void draft_int4(DraftParams p)
       l_run *= alpha;
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) o[dt] *= alpha;
+#pragma unroll
+      for (int g = 0; g < NG; ++g) wz[g] *= alpha;
       m_run = m_new;
     }
     const float m_use = (m_run == kNegInf) ? 0.f : m_run;
@@ -516,8 +527,9 @@ __global__ __launch_bounds__(kDraftWaves * 64, 2) void draft_int4(DraftParams p)
   };
   static_assert(kI4Stages <= 5, "wait_chunks_after covers up to 3 chunks in flight");
   const u32x4 negm = u32x4{kNegMagic1024, kNegMagic64, kNegMagic1024, kNegMagic64};
-  uint32_t m1024 = 0x64006400u, m64 = 0x54005400u;
+  uint32_t m1024 = 0x64006400u, m64 = 0x54005400u, mlo = 0x000F000Fu, mhi = 0x00F000F0u;
   __asm__ volatile("" : "+v"(m1024), "+v"(m64));   // the magics stay in VGPRs
+  __asm__ volatile("" : "+s"(mlo), "+s"(mhi));     // and the masks in SGPRs
 
   // One int4 chunk from its LDS stage; `masked` drops tokens at or past mlen.
   auto main_chunk = [&](const uint8_t *st, int c, bool masked) __attribute__((always_inline)) {
@@ -569,7 +581,7 @@ __global__ __launch_bounds__(kDraftWaves * 64, 2) void draft_int4(DraftParams p)
     for (int tau = 0; tau < 2; ++tau) {
       s[tau] = cst;
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) s[tau] = mfma_f16(magic_codes(kc[tau][ks], m1024, m64), qp[ks], s[tau]);
+      for (int ks = 0; ks < KS; ++ks) s[tau] = mfma_f16(magic_codes(kc[tau][ks], mlo, mhi, m1024, m64), qp[ks], s[tau]);
     }
     float sc[8], pr[8];
 #pragma unroll
@@ -578,7 +590,8 @@ __global__ __launch_bounds__(kDraftWaves * 64, 2) void draft_int4(DraftParams p)
       if (masked && c * kChunk + 8 * grp + e >= mlen) sc[e] = kNegInf;
     }
     softmax(sc, pr);
-    // O += codes . (p s) + z . p, per 32-channel group g of the V scales
+    // O += (magic + codes) . (p s) per 32-channel group g of the V scales;
+    // W_g += p . z - (p s) . magic, the part shared by the group's channels
     u32x4 pp;
 #pragma unroll
     for (int j = 0; j < 4; ++j) pp[j] = pack_f16x2(pr[2 * j], pr[2 * j + 1]);
@@ -593,9 +606,12 @@ __global__ __launch_bounds__(kDraftWaves * 64, 2) void draft_int4(DraftParams p)
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         const int dt = 2 * g + h;
-        o[dt] = mfma_f16(magic_codes(vc[dt], m1024, m64), pg, o[dt]);
-        o[dt] = mfma_f16(negm, pg, o[dt]);
-        o[dt] = mfma_f16(vzr[g], pp, o[dt]);
+        o[dt] = mfma_f16(magic_codes(vc[dt], mlo, mhi, m1024, m64), pg, o[dt]);
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        wz[g] = dot_f16x2(pp[j], vzr[g][j], wz[g]);
+        wz[g] = dot_f16x2(pg[j], negm[j], wz[g]);
       }
     }
   };
@@ -657,6 +673,15 @@ __global__ __launch_bounds__(kDraftWaves * 64, 2) void draft_int4(DraftParams p)
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) o[dt] = mfma_f16(va[dt], pp, o[dt]);
   }
+
+  // ---- W_g over the chunk's four token groups, onto every channel of g ----
+#pragma unroll
+  for (int g = 0; g < NG; ++g) {
+    wz[g] += __shfl_xor(wz[g], 16, 64);
+    wz[g] += __shfl_xor(wz[g], 32, 64);
+  }
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) o[dt] += wz[dt >> 1];
 
   // ---- merge the 4 waves through LDS (reusing the ring) ------------------
   l_run += __shfl_xor(l_run, 16, 64);

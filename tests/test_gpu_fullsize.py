@@ -188,6 +188,11 @@ def test_draft_int4_128k():
     _int4_case(32, 32, 8, 131072, 1600, [(0, 0, [0]), (20, 4, [1, 3]), (31, 7, [2])], qstd=2.0)
 
 
+def test_draft_int4_32k_batch32():
+    # batch 32, 32 q / 8 KV heads, int4 K/V over 32768 tokens: the bytes of the 1M drafter over 256 slices
+    _int4_case(32, 32, 8, 32768, 1650, [(0, 2, [0, 3]), (17, 5, [1]), (31, 0, [2])], qstd=2.0)
+
+
 def test_draft_int4_1m():
     # the drafter of the 1M-token configuration: one request, 32 q / 8 KV heads, int4 over 1048576 tokens
     _int4_case(1, 32, 8, 1048576, 1700, [(0, 1, [0, 3]), (0, 6, [2])], qstd=2.0)
