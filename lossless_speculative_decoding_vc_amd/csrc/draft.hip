@@ -175,6 +175,10 @@ __global__ __launch_bounds__(kDraftWaves * 64) void draft_bf16_dense(DraftParams
   f32x4 o[DT];
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // Columns past the G heads are MFMA padding: with no visible token their
+  // probabilities are 0, so their P operand columns are zeros (less
+  // switching in the matrix cores; nothing reads those columns).
+  const int lane_total = (col < G) ? total : 0;
 
   auto compute = [&](int c, const DraftChunk<D> &ch) __attribute__((always_inline)) {
     const int base = c * kChunk;
@@ -193,7 +197,7 @@ __global__ __launch_bounds__(kDraftWaves * 64) void draft_bf16_dense(DraftParams
       for (int i = 0; i < 4; ++i) {
         const int e = 4 * tau + i;
         float x = fmaf(s[tau][i], p.qk_scale, ch.lg[e]);
-        x = (base + 8 * grp + e < total) ? x : kNegInf;
+        x = (base + 8 * grp + e < lane_total) ? x : kNegInf;
         sc[e] = x;
         cmax = fmaxf(cmax, x);
       }
@@ -413,6 +417,10 @@ __global__ __launch_bounds__(kDraftWaves * 64, 2) void draft_int4(DraftParams p)
   qmax = fmaxf(qmax, __shfl_xor(qmax, 32, 64));
   const int qexp = (qmax > 0.f) ? __builtin_amdgcn_frexp_expf(qmax) : 0;
   const float qs = ldexpf(p.qk_scale, qexp);   // score scale of this lane's head (base 2)
+  // Columns past the G heads are MFMA padding: a score of -inf there makes
+  // their probabilities 0, so the value-side operands of those columns are
+  // zeros (less switching in the matrix cores; nothing reads those columns).
+  const float pad = (col < G) ? 0.f : kNegInf;
   u32x4 qh[KS];
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks)
@@ -586,7 +594,7 @@ __global__ __launch_bounds__(kDraftWaves * 64, 2) void draft_int4(DraftParams p)
     float sc[8], pr[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      sc[e] = DEG ? fmaf(s[e >> 2][e & 3], qs, lg[e]) : s[e >> 2][e & 3] * qs;
+      sc[e] = fmaf(s[e >> 2][e & 3], qs, DEG ? lg[e] + pad : pad);
       if (masked && c * kChunk + 8 * grp + e >= mlen) sc[e] = kNegInf;
     }
     softmax(sc, pr);
@@ -662,7 +670,7 @@ __global__ __launch_bounds__(kDraftWaves * 64, 2) void draft_int4(DraftParams p)
     }
     float sc[8], pr[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) sc[e] = (tb + 8 * grp + e < tlen) ? s[e >> 2][e & 3] * qs : kNegInf;
+    for (int e = 0; e < 8; ++e) sc[e] = (tb + 8 * grp + e < tlen) ? fmaf(s[e >> 2][e & 3], qs, pad) : kNegInf;
     softmax(sc, pr);
     u32x4 pp;
 #pragma unroll

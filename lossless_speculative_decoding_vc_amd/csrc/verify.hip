@@ -219,8 +219,12 @@ __global__ __launch_bounds__(W * 64) void verify_bf16(VerifyParams p) {
   f32x4 o[CT][DT];
 #pragma unroll
   for (int ct = 0; ct < CT; ++ct) {
-    m_run[ct] = kNegInf;
-    mq[ct] = 0.f;
+    // a padding row (r >= R) starts with a reference of +inf: its
+    // probabilities are 0, so its P operand columns are zeros (less switching
+    // in the matrix cores); padding rows are never stored
+    const bool real = r0 + 16 * ct + col < p.R;
+    m_run[ct] = real ? kNegInf : -kNegInf;
+    mq[ct] = real ? 0.f : -kNegInf;
     l_run[ct] = 0.f;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) o[ct][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -274,7 +278,8 @@ __global__ __launch_bounds__(W * 64) void verify_bf16(VerifyParams p) {
         cmax = fmaxf(cmax, __shfl_xor(cmax, 16, 64));
         cmax = fmaxf(cmax, __shfl_xor(cmax, 32, 64));
         const float m_new = fmaxf(m_run[ct], cmax);
-        const float alpha = (m_new == kNegInf) ? 1.f : fast_exp2((m_run[ct] - m_new) * qs);
+        // 1 when the reference does not move (also at -inf, and at +inf for padding rows)
+        const float alpha = (m_new == m_run[ct]) ? 1.f : fast_exp2((m_run[ct] - m_new) * qs);
         l_run[ct] *= alpha;
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) o[ct][dt] *= alpha;
@@ -545,8 +550,12 @@ VC_DEVICE void pp_rows(const VerifyParams &p, uint8_t *lds, const int wave, cons
   f32x4 o[CT][DT];
 #pragma unroll
   for (int ct = 0; ct < CT; ++ct) {
-    m_run[ct] = kNegInf;
-    mq[ct] = 0.f;
+    // a padding row (r >= R) starts with a reference of +inf: its
+    // probabilities are 0, so its P operand columns are zeros (less switching
+    // in the matrix cores); padding rows are never stored
+    const bool real = r0 + 16 * ct + col < p.R;
+    m_run[ct] = real ? kNegInf : -kNegInf;
+    mq[ct] = real ? 0.f : -kNegInf;
     l_run[ct] = 0.f;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) o[ct][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -600,7 +609,8 @@ VC_DEVICE void pp_rows(const VerifyParams &p, uint8_t *lds, const int wave, cons
         cmax = fmaxf(cmax, __shfl_xor(cmax, 16, 64));
         cmax = fmaxf(cmax, __shfl_xor(cmax, 32, 64));
         const float m_new = fmaxf(m_run[ct], cmax);
-        const float alpha = (m_new == kNegInf) ? 1.f : fast_exp2((m_run[ct] - m_new) * qs);
+        // 1 when the reference does not move (also at -inf, and at +inf for padding rows)
+        const float alpha = (m_new == m_run[ct]) ? 1.f : fast_exp2((m_run[ct] - m_new) * qs);
         l_run[ct] *= alpha;
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) o[ct][dt] *= alpha;
