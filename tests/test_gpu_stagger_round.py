@@ -87,9 +87,13 @@ class Inputs:
             self.host_kv.append(h)
 
 
-def _run(inp, mode, delayed=(), timing=0):
+def _run(inp, mode, delayed=(), timing=0, copy_delayed=()):
     """One round on fresh device state; returns every output on the host
-    (and, with a timing mode, the round's event times under "times")."""
+    (and, with a timing mode, the round's event times under "times").
+    ``delayed``: layers before whose verify the verify stream spins;
+    ``copy_delayed``: layers before whose verify the copy stream is made to
+    wait for a spinning side stream, delaying every layer copy enqueued
+    after that point."""
     import torch
     import lossless_speculative_decoding_vc_amd as vc
     dev = "cuda"
@@ -134,7 +138,7 @@ def _run(inp, mode, delayed=(), timing=0):
                    host_v=hostv[l]) for l in range(L)]
     slots = [torch.empty(2 * inp.half, dtype=torch.uint8, device=dev) for _ in range(2)]
     stg = vc.Stagger(slots, 2 * inp.half, L)
-    ds, vs = torch.cuda.Stream(), torch.cuda.Stream()
+    ds, vs, side = torch.cuda.Stream(), torch.cuda.Stream(), torch.cuda.Stream()
     stalls = []
 
     def before_verify(layer, stream):
@@ -142,6 +146,11 @@ def _run(inp, mode, delayed=(), timing=0):
             stalls.append(layer)
             with torch.cuda.stream(vs):
                 torch.cuda._sleep(20_000_000)   # a few milliseconds of spinning, then it exits
+        if layer in copy_delayed:
+            stalls.append(layer)
+            with torch.cuda.stream(side):
+                torch.cuda._sleep(20_000_000)
+            stg.after(side)   # later host-to-device copies wait for the spin
 
     torch.cuda.synchronize()
     try:
@@ -155,7 +164,7 @@ def _run(inp, mode, delayed=(), timing=0):
         times = stg.round_times() if timing else None
     finally:
         stg.close()
-    assert sorted(stalls) == sorted(delayed)
+    assert sorted(stalls) == sorted(list(delayed) + list(copy_delayed))
     out = dict(dout=[_bits(t) for t in dout], drafts=drafts.cpu().numpy(), vout=[_bits(t) for t in vout],
                argmax=am.cpu().numpy(), accept_len=al.cpu().numpy(), out_tokens=toks.cpu().numpy(),
                n_out=nout.cpu().numpy(), xk=[_bits(t) for t in xk], xv=[_bits(t) for t in xv],
@@ -196,6 +205,16 @@ def test_staggered_equals_bulk_synchronous(inp, staggered):
 def test_verify_stalls_change_nothing(inp, staggered, delayed):
     import lossless_speculative_decoding_vc_amd as vc
     stalled = _run(inp, vc.ROUND_STAGGERED, delayed)
+    for key in staggered:
+        _equal(staggered[key], stalled[key], key)
+
+
+@pytest.mark.parametrize("copy_delayed", [(0,), (1, 2)])
+def test_copy_stalls_change_nothing(inp, staggered, copy_delayed):
+    """The copy stream held back mid-round (the slots' refills arrive late):
+    verify still waits for each layer's copy, so nothing changes."""
+    import lossless_speculative_decoding_vc_amd as vc
+    stalled = _run(inp, vc.ROUND_STAGGERED, copy_delayed=copy_delayed)
     for key in staggered:
         _equal(staggered[key], stalled[key], key)
 
