@@ -124,9 +124,9 @@ KERNEL_OF = {
     "draft1m_int4p": "vc_draft_attn (packed int4 blocks): draft_int4 + combine_splits",
     "draft32k_int4": "vc_draft_attn: draft_int4 + combine_splits",
     "draft32k_int4p": "vc_draft_attn (packed int4 blocks): draft_int4 + combine_splits",
-    "verify1m": "vc_verify_attn: verify_pp + combine_splits",
-    "verify32k": "vc_verify_attn: verify_pp + combine_splits",
-    "verify128k": "vc_verify_attn: verify_pp + combine_splits",
+    "verify1m": "vc_verify_attn: verify_ts (token split) + combine_splits",
+    "verify32k": "vc_verify_attn: verify_pp (row split) + combine_splits",
+    "verify128k": "vc_verify_attn: verify_ts (token split) + combine_splits",
     "quant128k_int4": "vc_quantize_int4: quantize_int4",
     "quant128k_int4p": "vc_quantize_int4_packed: quantize_int4",
     "csm128k": "vc_csm_round: csm_round_kernel",

@@ -10,30 +10,35 @@
 //  * the M block rows times the G = Hq/Hkv query heads that share a KV head
 //    are packed into R = M*G query rows, so one pass over a KV head's keys
 //    serves all of them (the contraction that makes verify dense).
-//  * grid (splits, row groups, B*Hkv).  A row group is up to 256 packed
-//    rows and K/V leave HBM once per row group: up to 192 rows it is four
-//    waves (one per SIMD) of up to three 16-row column tiles each, beyond
-//    that eight waves of two tiles (two per SIMD).
+//  * grid (splits, row groups, B*Hkv); K/V leave HBM once per row group.
+//    Up to 64 packed rows: four waves (one per SIMD) of one 16-row column
+//    tile.  Up to 192 rows (token split, verify_ts): eight waves, the two
+//    waves of a SIMD hold the same 32 or 48 rows and take alternate
+//    32-token halves of every tile, so each reads only its half of the tile
+//    from LDS and the two carry equal work; their softmax states are merged
+//    through LDS at the end.  Up to 256 rows (row split, verify_pp): eight
+//    waves of two column tiles, the two waves of a SIMD on different rows.
 //  * the workgroup streams 64-token tiles of K (token-major) and V
-//    (channel-major) through a ring of 4 LDS stages filled by direct
-//    global->LDS loads (global_load_lds_dwordx4), two to three tiles in
-//    flight (64-96 KB per CU at head_dim 128) without holding any of them
-//    in registers.  Each wave-wide load lands as 1 KB of contiguous LDS, so
-//    bank conflicts are avoided by XOR-swizzling which 16-byte piece a lane
-//    fetches instead of padding rows.  Tiles that reach the block keys or
-//    the end of the key sequence are staged through registers after the
-//    main loop.
+//    (channel-major) through a ring of LDS stages (four, or five for the
+//    token split: 160 KB at head_dim 128) filled by direct global->LDS
+//    loads (global_load_lds_dwordx4), two to three tiles in flight without
+//    holding any of them in registers.  Each wave-wide load lands as 1 KB of
+//    contiguous LDS, so bank conflicts are avoided by XOR-swizzling which
+//    16-byte piece a lane fetches instead of padding rows.  Tiles that reach
+//    the block keys or the end of the key sequence are staged through
+//    registers after the main loop.
 //  * S^T = K Q^T and O^T = V^T P^T on v_mfma_f32_16x16x32_bf16; the token
 //    rows of the S^T tiles are permuted so each lane's scores are the 8
 //    consecutive tokens the PV MFMA consumes as its k-slots: P never leaves
 //    the registers it was computed in.
-//  * the main loop is software-pipelined by 32-token halves: the QK MFMAs
-//    of the next half overlap the probabilities of the current one, the PV
-//    MFMAs overlap the next half's maxima, and K/V operands are read from
-//    LDS a half-step ahead.
+//  * the two waves of a SIMD run a ping-pong: one issues an MFMA cluster
+//    (PV, then QK) while the other computes probabilities on the VALU,
+//    separated by workgroup barriers.
 //  * fp32 online softmax in base 2 with a lazily updated reference max per
 //    packed row (rescale only when a score exceeds it by more than 2^8);
 //    causal masking only in tiles that reach the block.
+#include <float.h>
+
 #include "common.h"
 #include "launch.h"
 
@@ -42,6 +47,7 @@ namespace {
 
 constexpr int kTile = 64;      // tokens per LDS tile
 constexpr int kStages = 4;     // LDS ring depth
+constexpr int kStagesTs = 5;   // LDS ring depth of the token-split schedule (160 KB at head_dim 128)
 constexpr float kSlack = 8.f;  // lazy-rescale threshold (base 2)
 
 struct VerifyParams {
@@ -458,9 +464,13 @@ __global__ __launch_bounds__(W * 64) void verify_bf16(VerifyParams p) {
   }
 }
 
-// The rows [r0, r0 + 16*CT) of one workgroup of verify_pp, run by one wave
-// of eight (two per SIMD); the two waves of a SIMD may hold different CT.
-template <int D, int CT>
+// The rows [r0, r0 + 16*CT) of one workgroup of eight waves (two per SIMD),
+// run by one wave.  Row split (verify_pp): the two waves of a SIMD hold
+// different rows, possibly different CT, and each takes both 32-token halves
+// of every tile.  Token split (verify_ts, kTokens): both waves of a SIMD hold
+// the same rows; wave w takes the first half of every tile and wave w+4 the
+// second, and their softmax states are merged at the end.
+template <int D, int CT, bool kTokens>
 VC_DEVICE void pp_rows(const VerifyParams &p, uint8_t *lds, const int wave, const int r0) {
   constexpr int W = 8;
   using L = Lds<D>;
@@ -485,11 +495,9 @@ VC_DEVICE void pp_rows(const VerifyParams &p, uint8_t *lds, const int wave, cons
 
   // Q^T operands: column = packed row r = i*G + g.
   bf16x8 qb[CT][KS];
-  int row_lim[CT];   // row r sees key j iff j < row_lim = cl + i + 1
 #pragma unroll
   for (int ct = 0; ct < CT; ++ct) {
     const int r = r0 + 16 * ct + col;
-    row_lim[ct] = cl + r / G + 1;
     if (r < p.R) {
       const int i = r / G, g = r % G;
       const uint16_t *qp = p.q + (((size_t)b * M + i) * p.Hq + kvh * G + g) * D;
@@ -523,39 +531,51 @@ VC_DEVICE void pp_rows(const VerifyParams &p, uint8_t *lds, const int wave, cons
   const int cf = max(c0, min(c1, cl / kTile));
   // Per-lane byte offsets of this wave's direct loads, relative to the
   // tile's first K row / first V column (scalar bases, so each load holds one
-  // 32-bit VGPR).  K blocks come first: W divides the K block count.
+  // 32-bit VGPR).  K blocks come first: W divides the K block count.  The
+  // wave's j-th K block lies W*kRowsPerBlock rows (a multiple of 32, so the
+  // same row permutation and swizzle) below its first, and its j-th V block
+  // 8*W channel rows below its first: one offset per kind, with the block's
+  // distance added to the scalar base.
   constexpr int kJobs = L::kBlocks / W, kKJobs = L::kKBlocks / W;
   static_assert(L::kBlocks % W == 0 && L::kKBlocks % W == 0, "even split of a tile's loads");
-  uint32_t doff[kJobs];
-#pragma unroll
-  for (int j = 0; j < kJobs; ++j) {
-    const int q = wave + j * W;
-    if (j < kKJobs) {
-      const int r = q * L::kRowsPerBlock + lane / L::kSlots;
-      doff[j] = (uint32_t)(ktok(r) * D + 8 * kswz<D>(r, lane % L::kSlots)) * 2u;
-    } else {
-      const int d = (q - L::kKBlocks) * 8 + lane / 8;
-      doff[j] = (uint32_t)((size_t)d * p.ccap + 8 * vswz(d, lane % 8)) * 2u;
-    }
+  static_assert((W * L::kRowsPerBlock) % 32 == 0, "K blocks of one wave share the row permutation");
+  uint32_t doff_k, doff_v;
+  {
+    const int r = wave * L::kRowsPerBlock + lane / L::kSlots;
+    doff_k = (uint32_t)(ktok(r) * D + 8 * kswz<D>(r, lane % L::kSlots)) * 2u;
+    const int d = wave * 8 + lane / 8;
+    doff_v = (uint32_t)((size_t)d * p.ccap + 8 * vswz(d, lane % 8)) * 2u;
   }
+  // LDS stage of tile c: a ring of kStages tiles (row split) or of
+  // kStagesTs (token split), counted from the split's first tile
+  auto stage_of = [&](int c) __attribute__((always_inline)) {
+    return kTokens ? (c - c0) % kStagesTs : (c & (kStages - 1));
+  };
   auto issue = [&](int c) __attribute__((always_inline)) {
-    const uint32_t st = lds_base + (uint32_t)((c & (kStages - 1)) * L::kStage);
+    const uint32_t st = lds_base + (uint32_t)(stage_of(c) * L::kStage);
     const uint16_t *kb = ckb + (size_t)c * kTile * D, *vb = cvb + (size_t)c * kTile;
 #pragma unroll
-    for (int j = 0; j < kJobs; ++j)
-      load_lds16_s(doff[j], j < kKJobs ? kb : vb, st + (uint32_t)((wave + j * W) * 1024));
+    for (int j = 0; j < kJobs; ++j) {
+      const uint32_t dst = st + (uint32_t)((wave + j * W) * 1024);
+      if (j < kKJobs) load_lds16_s(doff_k, kb + (size_t)j * W * L::kRowsPerBlock * D, dst);
+      else load_lds16_s(doff_v, vb + (size_t)(j - kKJobs) * 8 * W * p.ccap, dst);
+    }
   };
 
-  float m_run[CT], l_run[CT], mq[CT];   // mq = scaled reference (0 while it is -inf)
+  float m_run[CT], l_run[CT];
   f32x4 o[CT][DT];
 #pragma unroll
   for (int ct = 0; ct < CT; ++ct) {
-    // a padding row (r >= R) starts with a reference of +inf: its
-    // probabilities are 0, so its P operand columns are zeros (less switching
-    // in the matrix cores); padding rows are never stored
+    // A real row starts with the reference -FLT_MAX: every finite score
+    // reaches it, so the first tile with a finite score takes the reference
+    // over before any probability is formed, and the scaled reference is
+    // plain m_run * qs (finite) throughout.  Until then l and o are 0, so the
+    // rescale weight applied to them (exp2 of a non-positive number) does
+    // not matter.  A padding row (r >= R) starts with +inf: its
+    // probabilities are 0, so its P operand columns are zeros (less
+    // switching in the matrix cores); padding rows are never stored.
     const bool real = r0 + 16 * ct + col < p.R;
-    m_run[ct] = real ? kNegInf : -kNegInf;
-    mq[ct] = real ? 0.f : -kNegInf;
+    m_run[ct] = real ? -FLT_MAX : -kNegInf;
     l_run[ct] = 0.f;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) o[ct][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -567,13 +587,15 @@ VC_DEVICE void pp_rows(const VerifyParams &p, uint8_t *lds, const int wave, cons
   using KOps = u32x4[2][KS];
   using Scores = f32x4[CT][2];
   // K operands of half h (16 token rows per S^T tile, 32 channels per k-step).
-  auto load_k = [&](const uint8_t *kt, int h, KOps &ka) __attribute__((always_inline)) {
+  // (k-steps [ks0, ks1) only, when given)
+  auto load_k = [&](const uint8_t *kt, int h, KOps &ka, int ks0 = 0, int ks1 = D / 32) __attribute__((always_inline)) {
 #pragma unroll
     for (int t2 = 0; t2 < 2; ++t2) {
       const int kr = 16 * (2 * h + t2) + col;   // token 8*(col>>2) + 4*t2 + (col&3) of the half
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks)
-        ka[t2][ks] = *reinterpret_cast<const u32x4 *>(kt + kr * L::kKRow + 16 * kswz<D>(kr, 4 * ks + grp));
+        if (ks >= ks0 && ks < ks1)
+          ka[t2][ks] = *reinterpret_cast<const u32x4 *>(kt + kr * L::kKRow + 16 * kswz<D>(kr, 4 * ks + grp));
     }
   };
   auto qk = [&](const KOps &ka, Scores &sc) __attribute__((always_inline)) {
@@ -609,13 +631,12 @@ VC_DEVICE void pp_rows(const VerifyParams &p, uint8_t *lds, const int wave, cons
         cmax = fmaxf(cmax, __shfl_xor(cmax, 16, 64));
         cmax = fmaxf(cmax, __shfl_xor(cmax, 32, 64));
         const float m_new = fmaxf(m_run[ct], cmax);
-        // 1 when the reference does not move (also at -inf, and at +inf for padding rows)
+        // 1 when the reference does not move (also at +inf for padding rows)
         const float alpha = (m_new == m_run[ct]) ? 1.f : fast_exp2((m_run[ct] - m_new) * qs);
         l_run[ct] *= alpha;
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) o[ct][dt] *= alpha;
         m_run[ct] = m_new;
-        mq[ct] = (m_new == kNegInf) ? 0.f : m_new * qs;
       }
     }
   };
@@ -630,9 +651,10 @@ VC_DEVICE void pp_rows(const VerifyParams &p, uint8_t *lds, const int wave, cons
   auto exp_pack = [&](const Scores &sc, bf16x8 (&pb)[CT]) __attribute__((always_inline)) {
 #pragma unroll
     for (int ct = 0; ct < CT; ++ct) {
+      const float mq = m_run[ct] * qs;   // scaled reference (+inf for padding rows)
       float pr[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) pr[e] = fast_exp2(fmaf(sc[ct][e >> 2][e & 3], qs, -mq[ct]));
+      for (int e = 0; e < 8; ++e) pr[e] = fast_exp2(fmaf(sc[ct][e >> 2][e & 3], qs, -mq));
       const u32x4 w = u32x4{pack_bf16x2(pr[0], pr[1]), pack_bf16x2(pr[2], pr[3]),
                             pack_bf16x2(pr[4], pr[5]), pack_bf16x2(pr[6], pr[7])};
       l_run[ct] = sum_bf16x2(w[3], sum_bf16x2(w[2], sum_bf16x2(w[1], sum_bf16x2(w[0], l_run[ct]))));
@@ -655,7 +677,7 @@ VC_DEVICE void pp_rows(const VerifyParams &p, uint8_t *lds, const int wave, cons
 #pragma unroll
       for (int ct = 0; ct < CT; ++ct) o[ct][dt] = mfma16x16x32(as_bf16x8(va[dt]), pb[ct], o[ct][dt]);
   };
-  auto stage_ptr = [&](int c) __attribute__((always_inline)) { return lds + (c & (kStages - 1)) * L::kStage; };
+  auto stage_ptr = [&](int c) __attribute__((always_inline)) { return lds + stage_of(c) * L::kStage; };
 
   // Main loop over the full tiles as a two-group ping-pong.  Each 32-token
   // half n is an MFMA cluster M_n (O += PV of half n-1, then S_n = QK of
@@ -690,7 +712,75 @@ VC_DEVICE void pp_rows(const VerifyParams &p, uint8_t *lds, const int wave, cons
   // A wave whose rows are all past R (row-group padding) keeps to the
   // barrier and load schedule but skips its LDS reads and arithmetic.
   const bool active = r0 < p.R;
-  if (c0 < cf) {
+  if constexpr (kTokens) {
+    // Token split: a wave's tile t is two clusters, V_t (P of tile t) and
+    // M_t+1 (V operands and PV of tile t, then K operands and S of tile
+    // t+1); wave group 1 lags group 0 by one cluster.  The operands are read
+    // from LDS inside the MFMA cluster that consumes them, so none is held
+    // through the softmax (a wave holds up to 48 rows).  Ring of five
+    // stages: in global phase f (group g runs its cluster f - g), tile u is
+    // read from phase 2u to 2u+3 and waited for at the end of phase 2u-1;
+    // tile u is issued at the start of phase 2u-6 into the stage of tile
+    // u-5, last read in phase 2u-7.  Two tiles stay in flight behind the
+    // one waited for.
+    const int h = grp2;
+    if (c0 < cf) {
+      const int T = cf - c0;
+      for (int t = 0; t < min(3, T); ++t) issue(c0 + t);
+      wait_tiles_after(min(T - 1, 2));
+      __syncthreads();
+      KOps ka;
+      VOps va;
+      Scores sc;
+      bf16x8 pb[CT];
+      if (grp2 == 1) {   // phase 0 (group 1's cluster "V_-1")
+        if (3 < T) issue(c0 + 3);
+        bar();
+      }
+      // M_0: S of tile 0
+      if (grp2 == 0 && 3 < T) issue(c0 + 3);
+      __builtin_amdgcn_sched_barrier(0);
+      if (active) {
+        load_k(stage_ptr(c0), h, ka);
+        qk(ka, sc);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      if (grp2 == 1 && 1 < T) wait_tiles_after(min(2, T - 2));
+      bar();
+      for (int t = 0; t < T; ++t) {
+        // V_t
+        if (grp2 == 1 && t + 4 < T) issue(c0 + t + 4);
+        __builtin_amdgcn_sched_barrier(0);
+        if (active) {
+          update_max(sc);
+          exp_pack(sc, pb);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        if (grp2 == 0 && t + 1 < T) wait_tiles_after(min(2, T - 2 - t));
+        bar();
+        // M_t+1
+        if (grp2 == 0 && t + 4 < T) issue(c0 + t + 4);
+        __builtin_amdgcn_sched_barrier(0);
+        if (active) {
+          // the V operands and the first half of the K operands are read
+          // first (one LDS latency per cluster), the rest of K behind PV
+          const uint8_t *kn = stage_ptr(c0 + min(t + 1, T - 1));
+          load_v(stage_ptr(c0 + t), h, va);
+          load_k(kn, h, ka, 0, KS / 2);
+          __builtin_amdgcn_sched_barrier(0);
+          pv(va, pb);
+          __builtin_amdgcn_sched_barrier(0);
+          load_k(kn, h, ka, KS / 2, KS);
+          __builtin_amdgcn_sched_barrier(0);
+          if (t + 1 < T) qk(ka, sc);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        if (grp2 == 1 && t + 2 < T) wait_tiles_after(min(2, T - 3 - t));
+        bar();
+      }
+      if (grp2 == 0) bar();
+    }
+  } else if (c0 < cf) {
     const int T = cf - c0;
     for (int t = 0; t < min(3, T); ++t) issue(c0 + t);
     wait_tiles_after(min(T - 1, 2));
@@ -751,14 +841,16 @@ VC_DEVICE void pp_rows(const VerifyParams &p, uint8_t *lds, const int wave, cons
   }
 
   // Tiles with block keys or past the end: staged through registers, causal
-  // mask applied to the scores, not pipelined.
+  // mask applied to the scores, not pipelined (token split: each wave its
+  // own half of the tile).
   for (int it = cf; it < c1; ++it) {
     uint8_t *st = stage_ptr(it);
     __syncthreads();
     stage_slow<D>(st, it * kTile, cl, total, M, p.ccap, ckb, cvb, bkb, bvb, tid, kThreads);
     __syncthreads();
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
+    for (int hh = 0; hh < (kTokens ? 1 : 2); ++hh) {
+      const int h = kTokens ? grp2 : hh;
       KOps ka;
       Scores sc;
       bf16x8 pb[CT];
@@ -766,17 +858,59 @@ VC_DEVICE void pp_rows(const VerifyParams &p, uint8_t *lds, const int wave, cons
       qk(ka, sc);
       const int jb = it * kTile + 32 * h + 8 * grp;   // key index of score (t2, i): jb + 4*t2 + i
 #pragma unroll
-      for (int ct = 0; ct < CT; ++ct)
+      for (int ct = 0; ct < CT; ++ct) {
+        const int row_lim = cl + (r0 + 16 * ct + col) / G + 1;   // row r = i*G + g sees key j < cl + i + 1
 #pragma unroll
         for (int t2 = 0; t2 < 2; ++t2)
 #pragma unroll
           for (int i = 0; i < 4; ++i)
-            if (jb + 4 * t2 + i >= row_lim[ct]) sc[ct][t2][i] = kNegInf;
+            if (jb + 4 * t2 + i >= row_lim) sc[ct][t2][i] = kNegInf;
+      }
       VOps va;
       load_v(st, h, va);
       update_max(sc);
       exp_pack(sc, pb);
       pv(va, pb);
+    }
+  }
+
+  if constexpr (kTokens) {
+    // Merge the pair's states: wave w+4 leaves its reference, row sums and
+    // unnormalised outputs in LDS (lane-major, per component), wave w
+    // rescales both to the larger reference and stores the rows.
+    constexpr int kComp = DT * 4 + 2;
+    static_assert(4 * CT * kComp * 64 * 4 <= kStagesTs * L::kStage, "merge area fits the ring");
+    float *xs = reinterpret_cast<float *>(lds) + (size_t)(wave & 3) * CT * kComp * 64 + lane;
+    __syncthreads();   // every wave is done with the ring and the tail stages
+    if (grp2 == 1) {
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct) {
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) xs[(ct * kComp + 4 * dt + i) * 64] = o[ct][dt][i];
+        xs[(ct * kComp + DT * 4) * 64] = m_run[ct];
+        xs[(ct * kComp + DT * 4 + 1) * 64] = l_run[ct];
+      }
+    }
+    __syncthreads();
+    if (grp2 == 1) return;
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) {
+      const float mb = xs[(ct * kComp + DT * 4) * 64];
+      const float mm = fmaxf(m_run[ct], mb);
+      // weight of a state kept relative to reference m: 1 at the common
+      // reference (also for padding rows, +inf in both), exp2 of a
+      // non-positive number otherwise (a state still at -FLT_MAX has l = 0
+      // and o = 0)
+      const float wa = (m_run[ct] == mm) ? 1.f : fast_exp2((m_run[ct] - mm) * qs);
+      const float wb = (mb == mm) ? 1.f : fast_exp2((mb - mm) * qs);
+      l_run[ct] = l_run[ct] * wa + xs[(ct * kComp + DT * 4 + 1) * 64] * wb;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) o[ct][dt][i] = o[ct][dt][i] * wa + xs[(ct * kComp + 4 * dt + i) * 64] * wb;
+      m_run[ct] = mm;
     }
   }
 
@@ -822,41 +956,54 @@ __global__ __launch_bounds__(512) void verify_pp(VerifyParams p) {
   __shared__ __attribute__((aligned(1024))) uint8_t lds[kStages * Lds<D>::kStage];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int rg = blockIdx.y * 64 * (CTA + CTB);
-  if (wave < 4) pp_rows<D, CTA>(p, lds, wave, rg + 16 * CTA * wave);
-  else pp_rows<D, CTB>(p, lds, wave, rg + 64 * CTA + 16 * CTB * (wave - 4));
+  if (wave < 4) pp_rows<D, CTA, false>(p, lds, wave, rg + 16 * CTA * wave);
+  else pp_rows<D, CTB, false>(p, lds, wave, rg + 64 * CTA + 16 * CTB * (wave - 4));
+}
+
+// Eight waves, two per SIMD, in the token-split schedule of pp_rows: a row
+// group is 64*CT packed rows, 16*CT per SIMD, shared by its two waves.
+template <int D, int CT>
+__global__ __launch_bounds__(512) void verify_ts(VerifyParams p) {
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[kStagesTs * Lds<D>::kStage];
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  pp_rows<D, CT, true>(p, lds, wave, blockIdx.y * 64 * CT + 16 * CT * (wave & 3));
 }
 
 // Kernel and row split for R packed rows.  Up to 64 rows: verify_bf16 with
-// four waves of one 16-row column tile.  Beyond that the ping-pong kernel:
-// 128-row groups as 16 + 16 rows per SIMD, 192 as 32 + 16, 256 as 32 + 32
-// (two waves per SIMD cap a wave at 256 registers, i.e. 32 rows at head_dim
-// 128).  The ping-pong kernel addresses a V row through a 32-bit byte offset,
+// four waves of one 16-row column tile.  Up to 192 rows the token-split
+// kernel: 32 or 48 rows per SIMD, shared by its two waves.  Beyond that the
+// row-split ping-pong kernel with 256-row groups as 32 + 32 rows per SIMD
+// (two waves per SIMD cap a wave at 256 registers, i.e. 48 rows at head_dim
+// 128).  The ping-pong kernels address a V row through a 32-bit byte offset,
 // so a context capacity of 2^31 bytes per channel row and beyond uses
 // verify_bf16 with 48-row waves.
 struct VerifyShape {
-  bool pp;
-  int W, CT;      // verify_bf16
-  int CTA, CTB;   // verify_pp
-  int rows() const { return pp ? 64 * (CTA + CTB) : 16 * CT * W; }
+  enum Kind { kFour, kTokenSplit, kRowSplit } kind;
+  int CT;   // column tiles per wave (kFour, kTokenSplit)
+  int rows() const { return kind == kFour ? 64 * CT : kind == kTokenSplit ? 64 * CT : 256; }
 };
 VerifyShape verify_shape(int R, int64_t ccap) {
-  if (R <= 64) return {false, 4, 1, 0, 0};
-  if ((int64_t)2 * ccap * 128 >= ((int64_t)1 << 31)) return {false, 4, R <= 128 ? 2 : 3, 0, 0};
-  if (R <= 128) return {true, 0, 0, 1, 1};
-  if (R <= 192) return {true, 0, 0, 2, 1};
-  return {true, 0, 0, 2, 2};
+  if (R <= 64) return {VerifyShape::kFour, 1};
+  if ((int64_t)2 * ccap * 128 >= ((int64_t)1 << 31)) return {VerifyShape::kFour, R <= 128 ? 2 : 3};
+  if (R <= 128) return {VerifyShape::kTokenSplit, 2};
+  if (R <= 192) return {VerifyShape::kTokenSplit, 3};
+  return {VerifyShape::kRowSplit, 2};
 }
 
 template <int D>
 void launch_verify_d(const VerifyParams &p, VerifyShape sh, int row_groups, hipStream_t s) {
   dim3 grid(p.splits, row_groups, p.B * p.Hkv);
-  if (sh.pp) {
-    if (sh.CTA == 1) verify_pp<D, 1, 1><<<grid, 512, 0, s>>>(p);
-    else if (sh.CTB == 1) verify_pp<D, 2, 1><<<grid, 512, 0, s>>>(p);
-    else verify_pp<D, 2, 2><<<grid, 512, 0, s>>>(p);
-  } else if (sh.CT == 1) verify_bf16<D, 4, 1><<<grid, 256, 0, s>>>(p);
-  else if (sh.CT == 2) verify_bf16<D, 4, 2><<<grid, 256, 0, s>>>(p);
-  else verify_bf16<D, 4, 3><<<grid, 256, 0, s>>>(p);
+  switch (sh.kind) {
+    case VerifyShape::kTokenSplit:
+      if (sh.CT == 2) verify_ts<D, 2><<<grid, 512, 0, s>>>(p);
+      else verify_ts<D, 3><<<grid, 512, 0, s>>>(p);
+      break;
+    case VerifyShape::kRowSplit: verify_pp<D, 2, 2><<<grid, 512, 0, s>>>(p); break;
+    default:
+      if (sh.CT == 1) verify_bf16<D, 4, 1><<<grid, 256, 0, s>>>(p);
+      else if (sh.CT == 2) verify_bf16<D, 4, 2><<<grid, 256, 0, s>>>(p);
+      else verify_bf16<D, 4, 3><<<grid, 256, 0, s>>>(p);
+  }
 }
 
 }  // namespace
