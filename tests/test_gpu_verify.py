@@ -94,8 +94,26 @@ def test_fp32_prefill():
 def test_sixteen_query_heads_per_kv_head():
     # G = 16 (the largest grouping): 33 block rows -> 528 packed rows, three row groups
     _check(1, 33, 32, 2, 128, 1280, [1201], seed=15, qstd=2.0)
-    # 12 rows -> 192 packed rows, one row group split 32 + 16 per SIMD
+    # 12 rows -> 192 packed rows, one row group of 48 rows per SIMD (token split)
     _check(2, 12, 16, 1, 128, 640, [640, 77], seed=16, qstd=2.0)
+
+
+@pytest.mark.parametrize("M,G,splits", [(33, 5, 0), (20, 5, 3), (40, 4, 1)])
+def test_token_split_head_dim_64(M, G, splits):
+    # 165, 100 and 160 packed rows at head_dim 64: the token-split kernel with three and two column tiles
+    _check(2, M, G * 2, 2, 64, 1280, [1280, 700], seed=19 + M, splits=splits, qstd=2.0)
+
+
+def test_token_split_prefill_and_short_contexts():
+    # 160 packed rows with no context (every tile holds block keys), then contexts shorter than one tile
+    _check(1, 40, 8, 2, 128, 0, [0], seed=23, qstd=2.0)
+    _check(2, 33, 10, 2, 128, 64, [50, 0], seed=24, qstd=2.0)
+
+
+def test_token_split_one_tile_per_split():
+    # 11 tiles over 11 splits: every split holds a single tile (one full tile or the block's tail)
+    got, ref = _check(2, 33, 10, 2, 128, 640, [640, 576], seed=25, splits=11, qstd=3.0)
+    assert rel_l2(got, ref) <= 2e-2
 
 
 def test_prefill_of_1024_rows():
