@@ -624,15 +624,18 @@ __global__ __launch_bounds__(kDraftWaves * 64, 2) void draft_int4(DraftParams p)
     }
   };
 
-  for (int k = 0; k < min(kI4Stages - 1, nmine); ++k) issue(k);
-  for (int k = 0; k < nmine; ++k) {
+  auto step = [&](int k, bool masked) __attribute__((always_inline)) {
     wait_chunks_after(min(nmine - 1 - k, kI4Stages - 2));
     if (k + kI4Stages - 1 < nmine) issue(k + kI4Stages - 1);
-    const uint8_t *st = ring + (k % kI4Stages) * kI4Stage;
-    const int c = first + kDraftWaves * k;
-    if ((c + 1) * kChunk <= mlen) main_chunk(st, c, false);
-    else main_chunk(st, c, true);
-  }
+    main_chunk(ring + (k % kI4Stages) * kI4Stage, first + kDraftWaves * k, masked);
+  };
+  // Only the chunk that holds token mlen-1 can be partial, and it is the
+  // wave's last: whole chunks run in a loop of their own, so the loop holds a
+  // single copy of the chunk code and the accumulators stay in place.
+  const int nwhole = (nmine > 0 && (first + kDraftWaves * (nmine - 1) + 1) * kChunk > mlen) ? nmine - 1 : nmine;
+  for (int k = 0; k < min(kI4Stages - 1, nmine); ++k) issue(k);
+  for (int k = 0; k < nwhole; ++k) step(k, false);
+  for (int k = nwhole; k < nmine; ++k) step(k, true);
 
   // ---- bf16 tail chunks (tokens mlen + 32 j ...): loads clamped in range and
   // masked afterwards, so they issue back to back ---------------------------
