@@ -303,8 +303,9 @@ __global__ __launch_bounds__(kDraftWaves * 64) void draft_bf16_dense(DraftParams
 //    along the rows.  On the value side both are the same for every channel
 //    of a 32-channel group (V's magic depends on the token's slot, its zero
 //    point on the token and group), so they collect in one running sum per
-//    head and group, W_g = sum_t p_t (z_tg - magic_t s_tg), by packed fp16
-//    dot products, added to the group's channels once after the loop.  All
+//    head and group, W_g = sum_t p_t (z_tg - magic_t s_tg), by two MFMAs per
+//    group whose A operands (the zero points, the -magic constant) repeat
+//    along the rows, added to the group's channels once after the loop.  All
 //    operands are fp16 (v_mfma_f32_16x16x32_f16) with fp32 accumulation; Q
 //    is brought into fp16 range with an exact per-head power-of-two scale.
 //  * chunks that reach the bf16 tail or the end of the sequence are
@@ -326,10 +327,6 @@ VC_DEVICE uint32_t pk_mul_f16(uint32_t a, uint32_t b) {
 // cast applied to an ext_vector element would read element 0).
 VC_DEVICE float sum_f16x2(uint32_t w, float acc) {
   return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, w), f16x2{(_Float16)1.0f, (_Float16)1.0f}, acc, false);
-}
-// acc + a.lo * b.lo + a.hi * b.hi (fp16 pairs, exact products, fp32 sum).
-VC_DEVICE float dot_f16x2(uint32_t a, uint32_t b, float acc) {
-  return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, a), __builtin_bit_cast(f16x2, b), acc, false);
 }
 VC_DEVICE uint32_t pack_f16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{lo, hi}), f16x2));
@@ -357,13 +354,19 @@ constexpr uint32_t kNegMagic1024 = 0xE400E400u, kNegMagic64 = 0xD400D400u;
 VC_DEVICE void dma16(const void *gptr, uint32_t lds_addr) {
   __asm__ volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gptr), "s"(lds_addr) : "memory", "m0");
 }
+// The same load from a wave-uniform 64-bit base plus a 32-bit lane offset
+// (no per-lane 64-bit address arithmetic).
+VC_DEVICE void dma16_s(uint32_t voff, const void *sbase, uint32_t lds_addr) {
+  __asm__ volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "s"(lds_addr) : "memory", "m0");
+}
 
 template <int D, bool DEG, bool PACKED>
 __global__ __launch_bounds__(kDraftWaves * 64, 2) void draft_int4(DraftParams p) {
   constexpr int KS = D / 32, DT = D / 16, NG = D / 32;
   static_assert(D == 128, "int4 draft is compiled for head_dim 128");
   constexpr int kBlk = DEG ? 6 : 5;   // direct loads per chunk per wave
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[kDraftWaves * kI4Stages * kI4Stage];
+  constexpr int kStages = kI4Stages, kStage = kI4Stage;
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[kDraftWaves * kStages * kStage];
 
   const int bh = blockIdx.y;
   const int b = bh / p.Hkv, kvh = bh % p.Hkv;
@@ -448,19 +451,27 @@ __global__ __launch_bounds__(kDraftWaves * 64, 2) void draft_int4(DraftParams p)
   f32x4 o[DT];
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  // W_g of this lane's head and tokens: what the zero points and the magic
-  // offsets add to every channel of V group g
-  float wz[NG];
+  // W_g of this lane's head: what the zero points and the magic offsets add
+  // to every channel of V group g, accumulated by MFMAs whose A operand is
+  // the same in every row (so all four rows of a lane hold the same sum)
+  f32x4 wz[NG];
 #pragma unroll
-  for (int g = 0; g < NG; ++g) wz[g] = 0.f;
+  for (int g = 0; g < NG; ++g) wz[g] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // Online softmax of one chunk's 8 scores per lane (token 8*grp + e).
-  // Returns the probabilities relative to the lane's reference max.  Lazy
-  // reference: the lane groups exchange maxima and rescale only when some
-  // score in the wave exceeds it by more than kSlack.
-  auto softmax = [&](float (&sc)[8], float (&pr)[8]) __attribute__((always_inline)) {
-    float cmax = vmax(vmax(vmax(sc[0], sc[1]), vmax(sc[2], sc[3])), vmax(vmax(sc[4], sc[5]), vmax(sc[6], sc[7])));
-    if (__any(cmax - m_run > kSlack)) {   // false when both are -inf
+  // The lane's reference as the scores are taken relative to it: m_run,
+  // or 0 while it is -inf.
+  auto ref_use = [&]() __attribute__((always_inline)) { return (m_run == kNegInf) ? 0.f : m_run; };
+  // Online softmax of one chunk's 8 scores per lane (token 8*grp + e), given
+  // relative to m_use = ref_use() (the subtraction folded into the scores'
+  // FMA).  Returns the probabilities relative to the lane's reference max.
+  // Lazy reference: the lane groups exchange maxima and rescale only when
+  // some score in the wave exceeds it by more than kSlack.
+  auto softmax = [&](float (&x)[8], float (&pr)[8], float m_use) __attribute__((always_inline)) {
+    float cmax = vmax(vmax(vmax(x[0], x[1]), vmax(x[2], x[3])), vmax(vmax(x[4], x[5]), vmax(x[6], x[7])));
+    // m_run - m_use is 0, or -inf before the first finite score (then any
+    // finite score takes the reference over; all -inf gives NaN: no)
+    if (__any(cmax - (m_run - m_use) > kSlack)) {
+      cmax += m_use;   // the scores' own maximum
       cmax = fmaxf(cmax, __shfl_xor(cmax, 16, 64));
       cmax = fmaxf(cmax, __shfl_xor(cmax, 32, 64));
       const float m_new = fmaxf(m_run, cmax);
@@ -471,14 +482,16 @@ __global__ __launch_bounds__(kDraftWaves * 64, 2) void draft_int4(DraftParams p)
 #pragma unroll
       for (int g = 0; g < NG; ++g) wz[g] *= alpha;
       m_run = m_new;
-    }
-    const float m_use = (m_run == kNegInf) ? 0.f : m_run;
+      const float shift = ref_use() - m_use;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) pr[e] = fast_exp2(sc[e] - m_use);
+      for (int e = 0; e < 8; ++e) x[e] -= shift;
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) pr[e] = fast_exp2(x[e]);
   };
 
   // ---- main loop: whole int4 chunks through the wave's LDS ring ----------
-  uint8_t *ring = lds + wave * (kI4Stages * kI4Stage);
+  uint8_t *ring = lds + wave * (kStages * kStage);
   const uint32_t ring_addr = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t *)ring;
   const int first = c0 + wave;
   const int nmine = (cf > first) ? (cf - first + kDraftWaves - 1) / kDraftWaves : 0;
@@ -491,30 +504,33 @@ __global__ __launch_bounds__(kDraftWaves * 64, 2) void draft_int4(DraftParams p)
   //  block 5:    merge degrees (5120 + 4 t), lanes 0..7 only.
   // Every piece is a contiguous run of the 32-token-blocked int4 layout, so
   // each load uses whole cache lines.
+  // Lane byte offsets of the loads, the same for every chunk: K code rows
+  // 16 h + lane/4 (slot swizzled), and 16 bytes per lane for the rest.
+  uint32_t koff[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int t = 16 * h + (lane >> 2);
+    koff[h] = (uint32_t)(t * (D / 2) + 16 * ((lane & 3) ^ ((t >> 3) & 3)));
+  }
+  const uint32_t loff = 16u * (uint32_t)lane;
   auto issue = [&](int k) __attribute__((always_inline)) {
     const int c = first + kDraftWaves * k;
     const int base = c * kChunk;
-    const uint32_t st = ring_addr + (uint32_t)((k % kI4Stages) * kI4Stage);
+    const uint32_t st = ring_addr + (uint32_t)((k % kStages) * kStage);
     if constexpr (PACKED) {
       // the block's K codes, V codes and its four 256-byte parameter pieces
       // are one contiguous 5120-byte run
       const uint8_t *blk = pkb + (size_t)c * kPackedBlock;
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int t = 16 * h + (lane >> 2);
-        dma16(blk + t * (D / 2) + 16 * ((lane & 3) ^ ((t >> 3) & 3)), st + 1024 * h);
-      }
+      for (int h = 0; h < 2; ++h) dma16_s(koff[h], blk, st + 1024 * h);
 #pragma unroll
-      for (int h = 0; h < 2; ++h) dma16(blk + kPackedVCodes + 1024 * h + 16 * lane, st + 2048 + 1024 * h);
-      dma16(blk + kPackedKScale + 16 * lane, st + 4096);
+      for (int h = 0; h < 2; ++h) dma16_s(loff, blk + kPackedVCodes + 1024 * h, st + 2048 + 1024 * h);
+      dma16_s(loff, blk + kPackedKScale, st + 4096);
     } else {
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int t = 16 * h + (lane >> 2);
-        dma16(kqb + (size_t)(base + t) * (D / 2) + 16 * ((lane & 3) ^ ((t >> 3) & 3)), st + 1024 * h);
-      }
+      for (int h = 0; h < 2; ++h) dma16_s(koff[h], kqb + (size_t)base * (D / 2), st + 1024 * h);
 #pragma unroll
-      for (int h = 0; h < 2; ++h) dma16(vqb + (size_t)base * (D / 2) + 1024 * h + 16 * lane, st + 2048 + 1024 * h);
+      for (int h = 0; h < 2; ++h) dma16_s(loff, vqb + (size_t)base * (D / 2) + 1024 * h, st + 2048 + 1024 * h);
       const uint16_t *src;
       const int q = lane & 15;
       if (lane < 16) src = ksb + (size_t)(base / 32) * D + 8 * q;
@@ -524,19 +540,19 @@ __global__ __launch_bounds__(kDraftWaves * 64, 2) void draft_int4(DraftParams p)
       dma16(src, st + 4096);
     }
     if (DEG) {
-      if (lane < 8) dma16(db + base + 4 * lane, st + 5120);
+      if (lane < 8) dma16_s(loff, db + base, st + 5120);
     }
   };
-  auto wait_chunks_after = [&](int n) __attribute__((always_inline)) {   // n = 0..kI4Stages-2
+  auto wait_chunks_after = [&](int n) __attribute__((always_inline)) {   // n = 0..kStages-2
     if (n >= 3) __asm__ volatile("s_waitcnt vmcnt(%0)" ::"n"(3 * kBlk) : "memory");
     else if (n == 2) __asm__ volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * kBlk) : "memory");
     else if (n == 1) __asm__ volatile("s_waitcnt vmcnt(%0)" ::"n"(kBlk) : "memory");
     else __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
   };
-  static_assert(kI4Stages <= 5, "wait_chunks_after covers up to 3 chunks in flight");
-  const u32x4 negm = u32x4{kNegMagic1024, kNegMagic64, kNegMagic1024, kNegMagic64};
+  static_assert(kStages <= 5, "wait_chunks_after covers up to 3 chunks in flight");
+  u32x4 negm = u32x4{kNegMagic1024, kNegMagic64, kNegMagic1024, kNegMagic64};
   uint32_t m1024 = 0x64006400u, m64 = 0x54005400u, mlo = 0x000F000Fu, mhi = 0x00F000F0u;
-  __asm__ volatile("" : "+v"(m1024), "+v"(m64));   // the magics stay in VGPRs
+  __asm__ volatile("" : "+v"(m1024), "+v"(m64), "+v"(negm));   // the magics stay in VGPRs
   __asm__ volatile("" : "+s"(mlo), "+s"(mhi));     // and the masks in SGPRs
 
   // One int4 chunk from its LDS stage; `masked` drops tokens at or past mlen.
@@ -592,14 +608,17 @@ __global__ __launch_bounds__(kDraftWaves * 64, 2) void draft_int4(DraftParams p)
       for (int ks = 0; ks < KS; ++ks) s[tau] = mfma_f16(magic_codes(kc[tau][ks], mlo, mhi, m1024, m64), qp[ks], s[tau]);
     }
     float sc[8], pr[8];
+    const float m_use = ref_use(), bias = pad - m_use;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      sc[e] = fmaf(s[e >> 2][e & 3], qs, DEG ? lg[e] + pad : pad);
+      sc[e] = fmaf(s[e >> 2][e & 3], qs, DEG ? lg[e] + bias : bias);
       if (masked && c * kChunk + 8 * grp + e >= mlen) sc[e] = kNegInf;
     }
-    softmax(sc, pr);
+    softmax(sc, pr, m_use);
     // O += (magic + codes) . (p s) per 32-channel group g of the V scales;
-    // W_g += p . z - (p s) . magic, the part shared by the group's channels
+    // W_g += p . z - (p s) . magic, the part shared by the group's channels:
+    // the zero points (the same for every channel row of the group) and the
+    // constant -magic operand against P and P s, exact fp16 products in fp32
     u32x4 pp;
 #pragma unroll
     for (int j = 0; j < 4; ++j) pp[j] = pack_f16x2(pr[2 * j], pr[2 * j + 1]);
@@ -616,24 +635,21 @@ __global__ __launch_bounds__(kDraftWaves * 64, 2) void draft_int4(DraftParams p)
         const int dt = 2 * g + h;
         o[dt] = mfma_f16(magic_codes(vc[dt], mlo, mhi, m1024, m64), pg, o[dt]);
       }
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        wz[g] = dot_f16x2(pp[j], vzr[g][j], wz[g]);
-        wz[g] = dot_f16x2(pg[j], negm[j], wz[g]);
-      }
+      wz[g] = mfma_f16(vzr[g], pp, wz[g]);
+      wz[g] = mfma_f16(negm, pg, wz[g]);
     }
   };
 
   auto step = [&](int k, bool masked) __attribute__((always_inline)) {
-    wait_chunks_after(min(nmine - 1 - k, kI4Stages - 2));
-    if (k + kI4Stages - 1 < nmine) issue(k + kI4Stages - 1);
-    main_chunk(ring + (k % kI4Stages) * kI4Stage, first + kDraftWaves * k, masked);
+    wait_chunks_after(min(nmine - 1 - k, kStages - 2));
+    if (k + kStages - 1 < nmine) issue(k + kStages - 1);
+    main_chunk(ring + (k % kStages) * kStage, first + kDraftWaves * k, masked);
   };
   // Only the chunk that holds token mlen-1 can be partial, and it is the
   // wave's last: whole chunks run in a loop of their own, so the loop holds a
   // single copy of the chunk code and the accumulators stay in place.
   const int nwhole = (nmine > 0 && (first + kDraftWaves * (nmine - 1) + 1) * kChunk > mlen) ? nmine - 1 : nmine;
-  for (int k = 0; k < min(kI4Stages - 1, nmine); ++k) issue(k);
+  for (int k = 0; k < min(kStages - 1, nmine); ++k) issue(k);
   for (int k = 0; k < nwhole; ++k) step(k, false);
   for (int k = nwhole; k < nmine; ++k) step(k, true);
 
@@ -672,9 +688,10 @@ __global__ __launch_bounds__(kDraftWaves * 64, 2) void draft_int4(DraftParams p)
       for (int ks = 0; ks < KS; ++ks) s[tau] = mfma_f16(ka[tau][ks], qh[ks], s[tau]);
     }
     float sc[8], pr[8];
+    const float m_use = ref_use(), bias = pad - m_use;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) sc[e] = (tb + 8 * grp + e < tlen) ? fmaf(s[e >> 2][e & 3], qs, pad) : kNegInf;
-    softmax(sc, pr);
+    for (int e = 0; e < 8; ++e) sc[e] = (tb + 8 * grp + e < tlen) ? fmaf(s[e >> 2][e & 3], qs, bias) : kNegInf;
+    softmax(sc, pr, m_use);
     u32x4 pp;
 #pragma unroll
     for (int j = 0; j < 4; ++j) pp[j] = pack_f16x2(pr[2 * j], pr[2 * j + 1]);
@@ -685,12 +702,7 @@ __global__ __launch_bounds__(kDraftWaves * 64, 2) void draft_int4(DraftParams p)
     for (int dt = 0; dt < DT; ++dt) o[dt] = mfma_f16(va[dt], pp, o[dt]);
   }
 
-  // ---- W_g over the chunk's four token groups, onto every channel of g ----
-#pragma unroll
-  for (int g = 0; g < NG; ++g) {
-    wz[g] += __shfl_xor(wz[g], 16, 64);
-    wz[g] += __shfl_xor(wz[g], 32, 64);
-  }
+  // ---- W_g onto every channel of group g --------------------------------
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) o[dt] += wz[dt >> 1];
 
@@ -700,6 +712,8 @@ __global__ __launch_bounds__(kDraftWaves * 64, 2) void draft_int4(DraftParams p)
   __syncthreads();   // every wave is done with its ring
   float (*sm)[16] = reinterpret_cast<float (*)[16]>(lds);
   float (*sl)[16] = reinterpret_cast<float (*)[16]>(lds + kDraftWaves * 16 * sizeof(float));
+  static_assert(2 * kDraftWaves * 16 * sizeof(float) + kDraftWaves * D * 17 * sizeof(float) <= sizeof(lds),
+                "the merge area fits the ring");
   float (*so)[D][17] = reinterpret_cast<float (*)[D][17]>(lds + 2 * kDraftWaves * 16 * sizeof(float));
   if (grp == 0) { sm[wave][col] = m_run; sl[wave][col] = l_run; }
 #pragma unroll
