@@ -175,6 +175,15 @@ def test_int4_packed_main_segment(splits):
     assert rel_l2(got, ref) <= 2e-2
 
 
+@pytest.mark.parametrize("G", [1, 5, 8, 16])
+@pytest.mark.parametrize("packed", [False, True])
+def test_int4_head_groupings(G, packed):
+    # 1 to 16 query heads per KV head fill 1 to 16 of the 16 MFMA columns (the rest is padding); degrees, a
+    # partial last chunk, a tail and forced splits
+    _int4_check(2, 2 * G, 2, 512, [[512, 300], [33, 480]], 8, [8, 5], "shared", seed=40 + G, splits=3,
+                qstd=2.0, packed=packed)
+
+
 def test_split_calls_share_one_workspace():
     # One workspace serves draft calls of different shapes and split counts
     # (2 .. 64 splits, 1 .. 16 query heads per KV head) back to back: every
